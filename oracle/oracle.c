@@ -1,0 +1,345 @@
+/*
+ * DepthWeave-KV CPU oracle -- TEST INFRASTRUCTURE, not part of the product.
+ *
+ * Only the test suite, the smoke check and the benchmark's CPU-baseline leg
+ * may load this library.  It shares no code with the HIP library: its own
+ * fp16 codec, its own loops, no layout of the GPU cache.  It works on the
+ * logical (token-position ordered) cache that the seeded input generator
+ * produces.
+ *
+ * What it computes, and from which passage:
+ *
+ *  oracle_decode -- decode-time attention over the compressed cache.
+ *    Reconstruction: DepthWeave-KV paper (arXiv 2607.06523) §3 Method,
+ *    Eq. (1): X^_t = A_t B + g R_t for Z in {K, V}; A_t is the token's
+ *    coefficient vector at its routed rank (the first r_tier basis vectors),
+ *    B the depth window's shared basis, g R_t the gated sparse residual whose
+ *    gate is folded into the stored fp16 scale.  Attention: the textbook
+ *    softmax attention the zhichai.net summary recalls in Ch. 1.1 and whose
+ *    decode procedure Ch. 1.2 gives (query of the new token against every
+ *    cached key, weighted sum of the cached values).  Everything is done in
+ *    fp64: fp16 inputs are exact in fp64, so the only error is the final
+ *    rounding order of fp64 sums.
+ *
+ *  oracle_append -- encoding one new K or V vector into the compressed form
+ *    (paper §3 Method, second paragraph: coefficients by projection onto the
+ *    current basis; residual kept only on the routed channels, with low-bit
+ *    group quantisation).  The pages fix neither the precision nor the order
+ *    of operations; this oracle takes the reading that the encoder works in
+ *    IEEE fp32 in one fixed order (sequential fused multiply-adds, ascending
+ *    index), because the encoding makes integer decisions (which channels,
+ *    which codes) that must be identical on both sides:
+ *      1. c_i = fp16_rne( sum_j B[i][j] * x_j )            i < r
+ *      2. e_j = x_j - sum_i B[i][j] * c_i                  j < d
+ *      3. S   = the s channels of largest |e_j| (ties: smaller j first)
+ *      4. s16 = fp16_rne( max_{j in S} |e_j| / qmax )
+ *      5. v_j = clamp( rint(e_j / s16), -qmax, qmax )     (0 if s16 == 0)
+ *      6. stored scale = s16, or fp16_rne(gate * s16) when gate != 1
+ *    This file must be compiled with -ffp-contract=off (no implicit fusion).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ------------------------------------------------------------------ fp16 */
+
+/* IEEE binary16 bit pattern -> exact double. */
+double oracle_half_to_double(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int ex = (h >> 10) & 0x1f;
+    int man = h & 0x3ff;
+    double v;
+    if (ex == 0)
+        v = ldexp((double)man, -24);                  /* zero / subnormal */
+    else if (ex == 31)
+        v = man ? NAN : INFINITY;
+    else
+        v = ldexp((double)(man | 0x400), ex - 25);    /* 1.man * 2^(ex-15) */
+    return sign ? -v : v;
+}
+
+/* fp32 -> binary16, round to nearest, ties to even. */
+uint16_t oracle_float_to_half(float f)
+{
+    uint16_t sign = signbit(f) ? 0x8000 : 0;
+    if (isnan(f))
+        return sign | 0x7e00;
+    double v = fabs((double)f);
+    if (v >= 65520.0)                /* halfway to 2^16 and above round to inf */
+        return sign | 0x7c00;
+    if (v == 0.0)
+        return sign;
+    int ex;
+    frexp(v, &ex);
+    int e = ex - 1;                  /* floor(log2 v) */
+    if (e < -14)
+        e = -14;                     /* subnormal range shares the 2^-24 step */
+    double step = ldexp(1.0, e - 10);
+    double m = nearbyint(v / step);  /* exact quotient, rounded half-even */
+    double r = m * step;
+    if (r == 0.0)
+        return sign;
+    frexp(r, &ex);
+    e = ex - 1;
+    if (e < -14)
+        return sign | (uint16_t)(r / ldexp(1.0, -24));
+    uint16_t man = (uint16_t)(r / ldexp(1.0, e - 10) - 1024.0);
+    return sign | (uint16_t)((e + 15) << 10) | man;
+}
+
+static float h2f(uint16_t h) { return (float)oracle_half_to_double(h); }
+
+void oracle_half_to_double_array(const uint16_t *in, double *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = oracle_half_to_double(in[i]);
+}
+
+void oracle_float_to_half_array(const float *in, uint16_t *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = oracle_float_to_half(in[i]);
+}
+
+/* ---------------------------------------------------------------- decode */
+
+typedef struct oracle_shape {
+    int32_t batch, num_q_heads, num_kv_heads, head_dim, r_max, s_max;
+    int64_t n_max;                   /* token stride of the logical arrays */
+    int32_t num_tiers;
+    int32_t tier_rank[8];
+    int32_t tier_resid[8];
+} oracle_shape;
+
+/* Rebuild one cached vector (K or V) of token t in fp64 (Eq. (1)).
+ * basis: the window's basis already decoded to fp64, [r_max][d]. */
+static void reconstruct(const oracle_shape *sh, const double *basis /* [r_max][d] */,
+                        const uint16_t *coef /* [r_max] */, const uint8_t *idx, const int8_t *val,
+                        uint16_t scale, int tier, double *x /* [d] */)
+{
+    int d = sh->head_dim;
+    int r = sh->tier_rank[tier];
+    int s = sh->tier_resid[tier];
+    for (int j = 0; j < d; ++j)
+        x[j] = 0.0;
+    for (int i = 0; i < r; ++i) {
+        double c = oracle_half_to_double(coef[i]);
+        const double *bi = basis + (int64_t)i * d;
+        for (int j = 0; j < d; ++j)
+            x[j] += c * bi[j];
+    }
+    double g = oracle_half_to_double(scale);
+    for (int u = 0; u < s; ++u)
+        x[idx[u]] += g * (double)val[u];
+}
+
+/*
+ * out[b][g][:] for every query head g of the selected (b, KV head) pairs.
+ * Query head g reads KV head g / (H_q / H_kv) (contiguous grouping).
+ * pairs: NULL for all, else n_pairs (b, h) pairs.  Empty context -> zeros.
+ * Returns 0, or -1 on an invalid argument.
+ */
+int oracle_decode(const oracle_shape *sh, const int64_t *n_tokens, const uint8_t *tier,
+                  const uint16_t *basisK, const uint16_t *basisV,
+                  const uint16_t *coefK, const uint16_t *coefV,
+                  const uint8_t *idxK, const uint8_t *idxV,
+                  const int8_t *valK, const int8_t *valV,
+                  const uint16_t *scaleK, const uint16_t *scaleV,
+                  const uint16_t *q, double alpha, double *out,
+                  const int32_t *pairs, int n_pairs, int nthreads)
+{
+    const int B = sh->batch, Hq = sh->num_q_heads, Hkv = sh->num_kv_heads;
+    const int d = sh->head_dim, R = sh->r_max, S = sh->s_max;
+    const int64_t NM = sh->n_max;
+    if (Hkv <= 0 || Hq % Hkv != 0 || d <= 0 || d > 256 || R <= 0 || sh->num_tiers <= 0 ||
+        sh->num_tiers > 8)
+        return -1;
+    const int gq = Hq / Hkv;
+    int total = pairs ? n_pairs : B * Hkv;
+    int bad = 0;
+
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+#endif
+    for (int p = 0; p < total; ++p) {
+        int b = pairs ? pairs[2 * p] : p / Hkv;
+        int h = pairs ? pairs[2 * p + 1] : p % Hkv;
+        if (b < 0 || b >= B || h < 0 || h >= Hkv) {
+            bad = 1;
+            continue;
+        }
+        int64_t n = n_tokens[b];
+        double *o = out + ((int64_t)b * Hq + (int64_t)h * gq) * d;
+        for (int64_t i = 0; i < (int64_t)gq * d; ++i)
+            o[i] = 0.0;
+        if (n <= 0)
+            continue;
+        int64_t base = ((int64_t)b * Hkv + h) * NM;
+        double *bK = (double *)malloc(sizeof(double) * (size_t)R * d);
+        double *bV = (double *)malloc(sizeof(double) * (size_t)R * d);
+        oracle_half_to_double_array(basisK + (int64_t)h * R * d, bK, (int64_t)R * d);
+        oracle_half_to_double_array(basisV + (int64_t)h * R * d, bV, (int64_t)R * d);
+        double *z = (double *)malloc(sizeof(double) * (size_t)(gq * n));
+        double *x = (double *)malloc(sizeof(double) * (size_t)d);
+        double *qd = (double *)malloc(sizeof(double) * (size_t)(gq * d));
+        for (int g = 0; g < gq; ++g)
+            for (int j = 0; j < d; ++j)
+                qd[g * d + j] = oracle_half_to_double(q[((int64_t)b * Hq + h * gq + g) * d + j]);
+
+        /* logits z_t = alpha * q . K^_t */
+        for (int64_t t = 0; t < n; ++t) {
+            int64_t tt = base + t;
+            int k = tier[tt];
+            if (k >= sh->num_tiers) { bad = 1; k = 0; }
+            reconstruct(sh, bK, coefK + tt * R, idxK + tt * S, valK + tt * S, scaleK[tt], k, x);
+            for (int g = 0; g < gq; ++g) {
+                double acc = 0.0;
+                for (int j = 0; j < d; ++j)
+                    acc += qd[g * d + j] * x[j];
+                z[g * n + t] = alpha * acc;
+            }
+        }
+        /* softmax weights w_t = exp(z_t - max z), normalised at the end */
+        double *mx = (double *)malloc(sizeof(double) * gq);
+        double *den = (double *)malloc(sizeof(double) * gq);
+        for (int g = 0; g < gq; ++g) {
+            double m = -INFINITY;
+            for (int64_t t = 0; t < n; ++t)
+                if (z[g * n + t] > m) m = z[g * n + t];
+            mx[g] = m;
+            den[g] = 0.0;
+        }
+        for (int64_t t = 0; t < n; ++t) {
+            int64_t tt = base + t;
+            int k = tier[tt];
+            if (k >= sh->num_tiers) k = 0;
+            reconstruct(sh, bV, coefV + tt * R, idxV + tt * S, valV + tt * S, scaleV[tt], k, x);
+            for (int g = 0; g < gq; ++g) {
+                double w = exp(z[g * n + t] - mx[g]);
+                den[g] += w;
+                for (int j = 0; j < d; ++j)
+                    o[g * d + j] += w * x[j];
+            }
+        }
+        for (int g = 0; g < gq; ++g)
+            for (int j = 0; j < d; ++j)
+                o[g * d + j] /= den[g];
+        free(mx); free(den); free(z); free(x); free(qd); free(bK); free(bV);
+    }
+    return bad ? -1 : 0;
+}
+
+/* ---------------------------------------------------------------- append */
+
+/*
+ * Encode one fp16 vector x[d] against basis[r_max][d] at rank r with s
+ * residual channels and range qmax (7 for 4-bit, 127 for 8-bit codes).
+ * gate: fp16 bit pattern of the residual gate (0x3c00 = 1).
+ * Outputs: c_out[r] fp16 bits, idx_out[s] ascending, val_out[s], *scale_out
+ * fp16 bits (0 when s == 0).  Returns 0, or -1 on an invalid argument.
+ */
+/* Steps 1-2: fp16 coefficients c[r] and the fp32 residual e[d]. */
+static void project(int d, const uint16_t *basis, const uint16_t *x, int r, uint16_t *c16,
+                    float *e)
+{
+    float c[256];
+    for (int i = 0; i < r; ++i) {
+        float acc = 0.0f;
+        for (int j = 0; j < d; ++j)
+            acc = fmaf(h2f(basis[(int64_t)i * d + j]), h2f(x[j]), acc);
+        c16[i] = oracle_float_to_half(acc);
+        c[i] = h2f(c16[i]);
+    }
+    for (int j = 0; j < d; ++j) {
+        float acc = 0.0f;
+        for (int i = 0; i < r; ++i)
+            acc = fmaf(h2f(basis[(int64_t)i * d + j]), c[i], acc);
+        e[j] = h2f(x[j]) - acc;
+    }
+}
+
+/*
+ * Encode one fp16 vector x[d] against basis[r_max][d] at rank r with s
+ * residual channels and range qmax (7 for 4-bit, 127 for 8-bit codes).
+ * gate: fp16 bit pattern of the residual gate (0x3c00 = 1).
+ * Outputs: c_out[r] fp16 bits, idx_out[s] ascending, val_out[s], *scale_out
+ * fp16 bits (0 when s == 0).  Returns 0, or -1 on an invalid argument.
+ */
+int oracle_append(int d, int r_max, const uint16_t *basis, const uint16_t *x, int r, int s,
+                  int qmax, uint16_t gate, uint16_t *c_out, uint8_t *idx_out, int8_t *val_out,
+                  uint16_t *scale_out)
+{
+    if (d <= 0 || d > 256 || r < 0 || r > r_max || s < 0 || s > d || qmax <= 0)
+        return -1;
+    float e[256];
+    project(d, basis, x, r, c_out, e);
+    *scale_out = 0;
+    if (s == 0)
+        return 0;
+    /* 3. the s largest |e_j|; a strict '>' keeps the smaller j on ties */
+    char taken[256];
+    memset(taken, 0, sizeof taken);
+    int first = -1;
+    for (int u = 0; u < s; ++u) {
+        int best = -1;
+        for (int j = 0; j < d; ++j) {
+            if (taken[j]) continue;
+            if (best < 0 || fabsf(e[j]) > fabsf(e[best]))
+                best = j;
+        }
+        taken[best] = 1;
+        if (u == 0) first = best;
+    }
+    /* 4. one fp16 scale for the group of kept channels */
+    float amax = fabsf(e[first]);
+    uint16_t s16 = oracle_float_to_half(amax / (float)qmax);
+    float sf = h2f(s16);
+    /* 5. integer codes, stored in ascending channel order */
+    int u = 0;
+    for (int j = 0; j < d; ++j) {
+        if (!taken[j]) continue;
+        float v = 0.0f;
+        if (sf != 0.0f) {
+            v = rintf(e[j] / sf);
+            if (v > (float)qmax) v = (float)qmax;
+            if (v < -(float)qmax) v = -(float)qmax;
+        }
+        idx_out[u] = (uint8_t)j;
+        val_out[u] = (int8_t)v;
+        ++u;
+    }
+    /* 6. gate folded into the stored scale */
+    if (gate == 0x3c00)
+        *scale_out = s16;
+    else
+        *scale_out = oracle_float_to_half(h2f(gate) * sf);
+    return 0;
+}
+
+/* Residual vector e of step 2 (for the quantisation-bound checks). */
+int oracle_append_residual(int d, int r_max, const uint16_t *basis, const uint16_t *x, int r,
+                           float *e_out)
+{
+    if (d <= 0 || d > 256 || r < 0 || r > r_max)
+        return -1;
+    uint16_t c16[256];
+    project(d, basis, x, r, c16, e_out);
+    return 0;
+}
+
+int oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

@@ -1,0 +1,104 @@
+"""Plants plausible mistakes in a copy of the oracle (CPU only) and checks
+that the pins catch every one: a dropped or sign-flipped residual, swapped
+K/V bases, a wrong query-to-KV-head map, a missing softmax scale, an
+off-by-one rank, a transposed basis, a missing normalisation, a wrong
+exponential base, and in the encoder a wrong tie rule, a wrong rounding
+rule, a residual against unrounded coefficients, a wrong code range and a
+flipped residual sign."""
+import os
+import shutil
+import subprocess
+import tempfile
+
+import pytest
+
+import oracle
+from tests import test_oracle_append as TA
+from tests import test_oracle_decode as TD
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(os.path.dirname(HERE), "oracle", "oracle.c")
+
+DECODE_PINS = [
+    lambda: TD.test_identity_basis_equals_sdpa(1),
+    TD.test_random_basis_equals_sdpa_on_materialised_cache,
+    TD.test_full_rank_zero_residual_is_attention_on_BC,
+    TD.test_single_token_returns_its_value,
+    TD.test_two_tokens_logistic_weights,
+    TD.test_zero_query_gives_mean_value,
+    TD.test_constant_values_weights_sum_to_one,
+    TD.test_planted_needle_is_returned,
+]
+APPEND_PINS = [
+    lambda: TA.test_identity_basis_by_hand(4, 7, 0),
+    lambda: TA.test_identity_basis_by_hand(8, 127, 1),
+    TA.test_signed_permutation_basis_projects_exactly,
+    TA.test_residual_matches_projection_residual_in_fp64,
+    lambda: TA.test_kept_channels_are_best_subset_by_brute_force(0),
+    lambda: TA.test_quantisation_error_bound(7),
+    TA.test_ties_prefer_smaller_channel_and_zero_residual,
+    TA.test_codes_round_half_to_even,
+]
+
+MUTANTS = {
+    "drop_residual": ("x[idx[u]] += g * (double)val[u];", "(void)g;", DECODE_PINS),
+    "residual_sign": ("x[idx[u]] += g * (double)val[u];", "x[idx[u]] -= g * (double)val[u];", DECODE_PINS),
+    "kv_basis_swap": ("reconstruct(sh, bV,", "reconstruct(sh, bK,", DECODE_PINS),
+    "head_map": ("q[((int64_t)b * Hq + h * gq + g) * d + j]", "q[((int64_t)b * Hq + g * Hkv + h) * d + j]",
+                 DECODE_PINS),
+    "no_softmax_scale": ("z[g * n + t] = alpha * acc;", "z[g * n + t] = acc;", DECODE_PINS),
+    "rank_off_by_one": ("int r = sh->tier_rank[tier];", "int r = sh->tier_rank[tier] - 1;", DECODE_PINS),
+    "basis_transposed": ("x[j] += c * bi[j];", "x[j] += c * basis[(int64_t)j * sh->r_max + i];", DECODE_PINS),
+    "no_normalisation": ("o[g * d + j] /= den[g];", "o[g * d + j] /= 1.0;", DECODE_PINS),
+    "exp2_weights": ("double w = exp(z[g * n + t] - mx[g]);", "double w = exp2(z[g * n + t] - mx[g]);",
+                     DECODE_PINS),
+    "tie_to_larger": ("fabsf(e[j]) > fabsf(e[best])", "fabsf(e[j]) >= fabsf(e[best])", APPEND_PINS),
+    "round_half_away": ("v = rintf(e[j] / sf);", "v = roundf(e[j] / sf);", APPEND_PINS),
+    "unrounded_coef": ("c[i] = h2f(c16[i]);", "c[i] = acc;", APPEND_PINS),
+    "wrong_code_range": ("amax / (float)qmax", "amax / (float)(qmax + 1)", APPEND_PINS),
+    "residual_flipped": ("e[j] = h2f(x[j]) - acc;", "e[j] = acc - h2f(x[j]);", APPEND_PINS),
+}
+
+
+@pytest.fixture(scope="module")
+def workdir():
+    d = tempfile.mkdtemp(prefix="oracle_mutants_")
+    yield d
+    shutil.rmtree(d, ignore_errors=True)
+
+
+def test_unmutated_copy_passes_all_pins(workdir):
+    so = os.path.join(workdir, "clean.so")
+    subprocess.run(["gcc", "-std=c11", "-O1", "-fPIC", "-shared", "-ffp-contract=off", SRC, "-o", so,
+                    "-lm"], check=True)
+    saved = oracle._lib
+    oracle._lib = oracle._load(so)
+    try:
+        for pin in DECODE_PINS + APPEND_PINS:
+            pin()
+    finally:
+        oracle._lib = saved
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(name, workdir):
+    old, new, pins = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name} not unique"
+    path = os.path.join(workdir, f"{name}.c")
+    open(path, "w").write(src.replace(old, new))
+    so = os.path.join(workdir, f"{name}.so")
+    subprocess.run(["gcc", "-std=c11", "-O1", "-fPIC", "-shared", "-ffp-contract=off", path, "-o", so,
+                    "-lm"], check=True)
+    saved = oracle._lib
+    oracle._lib = oracle._load(so)
+    caught = []
+    try:
+        for pin in pins:
+            try:
+                pin()
+            except (AssertionError, ValueError):
+                caught.append(pin)
+    finally:
+        oracle._lib = saved
+    assert caught, f"no pin caught mutant {name}"
