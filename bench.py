@@ -1,0 +1,259 @@
+#!/usr/bin/env python3
+"""Decode benchmark of compressed-KV attention (DepthWeave-KV) on one MI355X.
+
+A step is one decode token for every sequence: for each layer, decode
+attention over the whole compressed cache, then the append of the new
+token's K/V (the attend-then-append order of the decode procedure).  Inputs
+(cache, queries, new tokens) are resident in HBM before timing; steps are
+replayed from HIP graphs captured in chunks.  Prints one JSON line.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+from concurrent.futures import ProcessPoolExecutor
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workload as w  # noqa: E402
+from workload.gen import gen_append_inputs, gen_layer, gen_query, make_bases, max_tier_counts  # noqa: E402
+
+METRIC = "decode tokens/s + achieved HBM GB/s (% of peak), compressed-KV attn at 64K"
+PEAK_HBM_GBPS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+DECODE_SRC = os.path.join(ROOT, "compressed_kv_cache_dwkv_amd", "csrc", "decode.hip")
+
+
+def parse_args():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=None, help="timed steps (default: the workload's)")
+    p.add_argument("--warmup", type=int, default=8)
+    p.add_argument("--config", type=int, default=2, help="workload index 0-4 (2 = 64K headline)")
+    p.add_argument("--chunk", type=int, default=16, help="steps per captured graph")
+    p.add_argument("--splits", type=int, default=0, help="decode workgroups per KV head (0 = auto)")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample budget")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-graph", action="store_true", help="launch eagerly instead of graph replay")
+    p.add_argument("--kernel-reps", type=int, default=3)
+    return p.parse_args()
+
+
+def _gen_layer_job(args):
+    ci, layer = args
+    return gen_layer(w.get_config(ci), layer)
+
+
+def algorithmic_layer_bytes(cfg, counts: np.ndarray) -> int:
+    """Bytes the method must move for one layer's decode: every cached token at
+    its tier's size (fp16 coefficients at the routed rank, residual indices,
+    packed codes, scale; K and V), both bases of every KV head, q and out."""
+    per_tok = np.array([w.compressed_bytes_per_token(r, s, cfg.resid_bits)
+                        for r, s in zip(cfg.tier_rank, cfg.resid_per_tier)])
+    tok = float((counts.reshape(-1, cfg.num_tiers) * per_tok[None, :]).sum())
+    bases = 2 * cfg.num_kv_heads * cfg.r_max * cfg.head_dim * 2 * counts.shape[0]
+    qo = cfg.batch * cfg.num_q_heads * cfg.head_dim * (2 + 4)
+    return int(tok + bases + qo)
+
+
+def stored_traffic(workload: str):
+    """HBM bytes per decode launch measured by rocprofv3 counters, if the
+    summary in profiles/ was taken on the current decode kernel source."""
+    path = os.path.join(PROFILES, f"decode_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    sha = hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()
+    if rec.get("decode_source_sha256") != sha:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(cfg, layers, bases, appends, budget_s: float):
+    import oracle
+    threads = oracle.max_threads()
+    t0 = time.perf_counter()
+    done = 0
+    for layer in range(cfg.num_layers):
+        m = layer // cfg.layers_per_group
+        q = gen_query(cfg, layer)
+        oracle.decode(cfg, layers[layer], bases["K"][m], bases["V"][m], q, threads=threads)
+        a = appends[0][layer]
+        oracle.append_layer(cfg, bases["K"][m], bases["V"][m], a["k"], a["v"], a["tier"])
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    step_s = dt / done * cfg.num_layers
+    used = min(threads, cfg.batch * cfg.num_kv_heads)
+    return {
+        "value": cfg.batch / step_s, "unit": "tokens/s", "cores": used, "kind": "oracle",
+        "sample": f"{done} of {cfg.num_layers} layers of one step (decode over all "
+                  f"{cfg.n_tokens} tokens x {cfg.batch * cfg.num_kv_heads} KV heads + append), "
+                  f"{dt:.1f} s, scaled to a full step",
+    }
+
+
+def main():
+    args = parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}), flush=True)
+        sys.exit(2)
+    cfg = w.get_config(args.config)
+    K = args.steps if args.steps is not None else cfg.bench_steps
+    W = args.warmup
+    L, B, H = cfg.num_layers, cfg.batch, cfg.num_kv_heads
+
+    # ---- synthetic inputs (host), before the GPU is touched
+    t0 = time.perf_counter()
+    workers = min(16, len(os.sched_getaffinity(0)))
+    with ProcessPoolExecutor(max_workers=workers) as ex:
+        layers = list(ex.map(_gen_layer_job, [(args.config, l) for l in range(L)]))
+    bases = make_bases(cfg)
+    appends = [[gen_append_inputs(cfg, l, s, bases) for l in range(L)] for s in range(W + K)]
+    queries = np.stack([gen_query(cfg, l) for l in range(L)])
+    print(f"bench: generated {cfg.name} in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
+
+    import torch
+    from compressed_kv_cache_dwkv_amd import dwkv_append, dwkv_decode_attn
+    from compressed_kv_cache_dwkv_amd.cache import CompressedKVCache
+
+    torch.cuda.set_device(0)
+    cap = [int(c) + W + K + 8 for c in max_tier_counts(cfg)]
+    cache = CompressedKVCache(L, cfg.layers_per_group, cfg.num_q_heads, H, cfg.head_dim, cfg.r_max,
+                              cfg.tier_rank, cfg.resid_per_tier, cfg.resid_bits, B, cap,
+                              cfg.n_tokens + W + K + 8, decode_splits=args.splits)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    for m in range(cfg.num_groups):
+        cache.set_basis(m, dev(bases["K"][m]), dev(bases["V"][m]))
+    for l in range(L):
+        cache.import_layer(l, {k: dev(v) for k, v in layers[l].items() if k != "n_tokens"},
+                           [int(x) for x in layers[l]["n_tokens"]])
+    torch.cuda.synchronize()
+    assert cache.check_errors() == 0, "cache import overflowed"
+    q_dev = dev(queries)                                                 # [L][B][Hq][d]
+    out_dev = torch.empty((L, B, cfg.num_q_heads, cfg.head_dim), dtype=torch.float32, device="cuda")
+    k_dev = dev(np.stack([[appends[s][l]["k"] for l in range(L)] for s in range(W + K)]))
+    v_dev = dev(np.stack([[appends[s][l]["v"] for l in range(L)] for s in range(W + K)]))
+    t_dev = dev(np.stack([[appends[s][l]["tier"] for l in range(L)] for s in range(W + K)]))
+    ws = cache.workspace(B)
+    h = cache.handle
+    scale = 1.0 / math.sqrt(cfg.head_dim)
+    print(f"bench: cache resident ({cache.arena.numel() / 1e9:.2f} GB arena)", file=sys.stderr, flush=True)
+
+    def step(s):
+        for l in range(L):
+            dwkv_decode_attn(h, l, q_dev[l], out_dev[l], ws, scale)
+            dwkv_append(h, l, k_dev[s, l], v_dev[s, l], t_dev[s, l])
+
+    for s in range(W):
+        step(s)
+    torch.cuda.synchronize()
+
+    graphs = []
+    if not args.no_graph:
+        for c0 in range(W, W + K, args.chunk):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for s in range(c0, min(c0 + args.chunk, W + K)):
+                    step(s)
+            graphs.append(g)
+        torch.cuda.synchronize()
+
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    if graphs:
+        for g in graphs:
+            g.replay()
+    else:
+        for s in range(W, W + K):
+            step(s)
+    end.record()
+    torch.cuda.synchronize()
+    elapsed_ms = start.elapsed_time(end)
+    errs = cache.check_errors()
+    assert errs == 0, f"device error word {errs}"
+    ms_per_step = elapsed_ms / K
+    tok_s = B * K / (elapsed_ms / 1e3)
+
+    # ---- decode-kernel duration (events on the launch stream, queued behind a spin)
+    counts = np.stack([cache.read_counts(l, B) for l in range(L)])     # [L][B][H][T]
+    layer_bytes = [algorithmic_layer_bytes(cfg, counts[l]) for l in range(L)]
+    step_bytes = sum(layer_bytes)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(L * args.kernel_reps)]
+    torch.cuda._sleep(int(3e8))
+    i = 0
+    for _ in range(args.kernel_reps):
+        for l in range(L):
+            ev[i][0].record()
+            dwkv_decode_attn(h, l, q_dev[l], out_dev[l], ws, scale)
+            ev[i][1].record()
+            i += 1
+    torch.cuda.synchronize()
+    durs = np.array([a.elapsed_time(b) for a, b in ev]).reshape(args.kernel_reps, L)   # ms
+    mean_launch_ms = float(durs.mean())
+    bytes_per_launch = float(np.mean(layer_bytes))
+    achieved = bytes_per_launch / (mean_launch_ms * 1e-3) / 1e9
+    traffic = stored_traffic(cfg.name)
+
+    dense = w.dense_kv_bytes(L, H, cfg.head_dim, cfg.n_tokens + W + K, batch=B)
+    res = {
+        "metric": METRIC,
+        "value": tok_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": cfg.name, "batch": B, "context": cfg.n_tokens, "layers": L,
+            "q_heads": cfg.num_q_heads, "kv_heads": H, "head_dim": cfg.head_dim,
+            "layers_per_basis": cfg.layers_per_group, "r_max": cfg.r_max,
+            "tier_rank": list(cfg.tier_rank), "tier_mix": list(cfg.tier_prob),
+            "resid_channels": cfg.resid_channels, "resid_bits": cfg.resid_bits,
+            "storage": "fp16 coefficients, uint8 channel indices, packed codes, fp16 scales",
+            "graph_replay": bool(graphs),
+        },
+        "step_GBps": step_bytes / (ms_per_step * 1e-3) / 1e9,
+        "step_frac_of_peak": step_bytes / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+        "roofline": {
+            "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
+            "kernel": "decode_kernel", "algorithmic_bytes_per_launch": bytes_per_launch,
+            "mean_launch_us": mean_launch_ms * 1e3,
+        },
+        "memory": {
+            "compressed_bytes": step_bytes, "dense_fp16_bytes": dense,
+            "reduction_vs_fp16": dense / step_bytes,
+        },
+        "paper_context": {"decode_tok_s_64k": 72.8, "kv_memory_reduction": 8.3,
+                          "note": "end-to-end generation on unstated hardware and model; not comparable"},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(cfg, layers, bases, appends, args.cpu_seconds)
+    else:
+        res["cpu_baseline"] = None
+    cache.close()
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

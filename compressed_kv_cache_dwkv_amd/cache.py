@@ -1,0 +1,99 @@
+"""Device-memory plumbing around one libdwkv cache: torch owns the arena and
+the decode workspaces; every operation is a call into libdwkv."""
+from __future__ import annotations
+
+import math
+from typing import Dict, Optional, Sequence
+
+import torch
+
+from . import (dwkv_append, dwkv_arena_bytes, dwkv_check_errors, dwkv_clear_errors, dwkv_create,
+               dwkv_decode_attn, dwkv_destroy, dwkv_export_layer, dwkv_import_layer,
+               dwkv_read_counts, dwkv_reset, dwkv_set_basis, dwkv_workspace_bytes, make_config)
+
+
+class CompressedKVCache:
+    """One compressed cache (all layers) on one GPU.
+
+    tier_capacity: token slots per (layer, sequence, KV head) for each tier;
+    max_tokens: positions per (layer, sequence, KV head)."""
+
+    def __init__(self, num_layers: int, layers_per_group: int, num_q_heads: int, num_kv_heads: int,
+                 head_dim: int, r_max: int, tier_rank: Sequence[int], tier_resid: Sequence[int],
+                 resid_bits: int, max_batch: int, tier_capacity: Sequence[int], max_tokens: int,
+                 decode_splits: int = 0, device: str = "cuda"):
+        self.cfg = make_config(num_layers, layers_per_group, num_q_heads, num_kv_heads, head_dim,
+                               r_max, tier_rank, tier_resid, resid_bits, max_batch, tier_capacity,
+                               max_tokens, decode_splits)
+        self.device = torch.device(device)
+        self.num_layers, self.num_q_heads, self.num_kv_heads = num_layers, num_q_heads, num_kv_heads
+        self.head_dim, self.r_max, self.num_tiers = head_dim, r_max, len(tier_rank)
+        self.s_max = max(tier_resid) if len(tier_resid) else 0
+        self.max_batch = max_batch
+        self.arena = torch.empty(dwkv_arena_bytes(self.cfg), dtype=torch.uint8, device=self.device)
+        self.handle = dwkv_create(self.cfg, self.arena)
+        self._ws: Dict[int, torch.Tensor] = {}
+        dwkv_reset(self.handle)
+
+    # ------------------------------------------------------------------ setup
+    def workspace(self, batch: int) -> torch.Tensor:
+        ws = self._ws.get(batch)
+        if ws is None:
+            ws = torch.zeros(dwkv_workspace_bytes(self.cfg, batch), dtype=torch.uint8, device=self.device)
+            self._ws[batch] = ws
+        return ws
+
+    def set_basis(self, group: int, basisK: torch.Tensor, basisV: torch.Tensor) -> None:
+        dwkv_set_basis(self.handle, group, basisK, basisV)
+
+    def import_layer(self, layer: int, lay: Dict[str, torch.Tensor], n_tokens: Sequence[int]) -> None:
+        dwkv_import_layer(self.handle, layer, lay, n_tokens)
+
+    def export_layer(self, layer: int, batch: int, n_max: int):
+        B, H, R, S = batch, self.num_kv_heads, self.r_max, max(self.s_max, 1)
+        dev = self.device
+        dst = {"tier": torch.zeros((B, H, n_max), dtype=torch.uint8, device=dev)}
+        for z in "KV":
+            dst["coef" + z] = torch.zeros((B, H, n_max, R), dtype=torch.float16, device=dev)
+            dst["idx" + z] = torch.zeros((B, H, n_max, S), dtype=torch.uint8, device=dev)
+            dst["val" + z] = torch.zeros((B, H, n_max, S), dtype=torch.int8, device=dev)
+            dst["scale" + z] = torch.zeros((B, H, n_max), dtype=torch.float16, device=dev)
+        counts = torch.zeros((B, H, self.num_tiers), dtype=torch.int32, device=dev)
+        slots = torch.zeros((B, H, n_max), dtype=torch.int32, device=dev)
+        dwkv_export_layer(self.handle, layer, dst, counts, slots)
+        return dst, counts, slots
+
+    def read_counts(self, layer: int, batch: int):
+        return dwkv_read_counts(self.handle, layer, batch, self.num_kv_heads, self.num_tiers)
+
+    # ------------------------------------------------------------------ hot path
+    def decode(self, layer: int, q: torch.Tensor, out: Optional[torch.Tensor] = None,
+               softmax_scale: Optional[float] = None) -> torch.Tensor:
+        B = q.shape[0]
+        if out is None:
+            out = torch.empty((B, self.num_q_heads, self.head_dim), dtype=torch.float32, device=self.device)
+        dwkv_decode_attn(self.handle, layer, q, out, self.workspace(B),
+                         softmax_scale if softmax_scale is not None else 1.0 / math.sqrt(self.head_dim))
+        return out
+
+    def append(self, layer: int, k: torch.Tensor, v: torch.Tensor, tier: torch.Tensor,
+               gateK: Optional[torch.Tensor] = None, gateV: Optional[torch.Tensor] = None) -> None:
+        dwkv_append(self.handle, layer, k, v, tier, gateK, gateV)
+
+    # ------------------------------------------------------------------ errors
+    def check_errors(self) -> int:
+        return dwkv_check_errors(self.handle)
+
+    def clear_errors(self) -> None:
+        dwkv_clear_errors(self.handle)
+
+    def close(self) -> None:
+        if self.handle is not None:
+            dwkv_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,190 @@
+// Bulk load of a layer from its logical (position-ordered) form into the
+// tier-grouped arena, and the inverse read-back.  Not on the decode hot
+// path: they stand in for the prefill that builds the cache, and let tests
+// read appended tokens back.
+#include <hip/hip_runtime.h>
+
+#include "device.h"
+#include "kernels.h"
+#include "layout.h"
+
+namespace dwkv {
+
+namespace {
+
+constexpr int kBlock = 256;
+constexpr int kWaves = kBlock / kWave;
+
+// One workgroup per KV head of sequence b.  Tokens are visited in position
+// order, 256 at a time; each tier's slots are handed out in that order, so a
+// tier region keeps its tokens sorted by position.
+__global__ __launch_bounds__(kBlock) void import_kernel(Layout ly, uint8_t *arena, int layer,
+                                                        dwkv_logical_layer src, int b, int64_t n)
+{
+    const int h = blockIdx.x;
+    const int tid = threadIdx.x, wave = tid / kWave;
+    __shared__ int s_base[kMaxTiers];
+    __shared__ int s_cnt[kWaves][kMaxTiers];
+    if (tid < kMaxTiers) s_base[tid] = 0;
+    uint8_t *blk = head_block_ptr(ly, arena, layer, b, h);
+    int32_t *pmap = posmap_ptr(ly, arena, layer, b, h);
+    uint32_t *err = err_ptr(ly, arena);
+    const int64_t row0 = ((int64_t)b * ly.Hkv + h) * src.n_max;
+    const uint8_t *tier_in = static_cast<const uint8_t *>(src.tier) + row0;
+    __syncthreads();
+
+    for (int64_t c0 = 0; c0 < n; c0 += kBlock) {
+        const int64_t t = c0 + tid;
+        bool valid = t < n;
+        int k = valid ? tier_in[t] : 0;
+        if (valid && k >= ly.T) {
+            atomicOr(err, DWKV_DEVERR_BAD_TIER);
+            valid = false;
+        }
+        int rank_in_wave = 0;
+        for (int kk = 0; kk < ly.T; ++kk) {
+            uint64_t m = __ballot(valid && k == kk);
+            if (valid && k == kk) rank_in_wave = __popcll(m & lanemask_lt());
+            if (lane_id() == 0) s_cnt[wave][kk] = __popcll(m);
+        }
+        __syncthreads();
+        if (valid) {
+            int slot = s_base[k] + rank_in_wave;
+            for (int w = 0; w < wave; ++w) slot += s_cnt[w][k];
+            if (slot >= ly.cap[k]) {
+                atomicOr(err, DWKV_DEVERR_TIER_FULL);
+            } else {
+                const int r = ly.rank[k], s = ly.resid[k], vb = ly.vbytes[k];
+                const int64_t tr = row0 + t;
+                const uint16_t *ck = static_cast<const uint16_t *>(src.coefK) + tr * ly.R;
+                const uint16_t *cv = static_cast<const uint16_t *>(src.coefV) + tr * ly.R;
+                uint16_t *dk = reinterpret_cast<uint16_t *>(blk + ly.f_coefK[k]) + (int64_t)slot * r;
+                uint16_t *dv = reinterpret_cast<uint16_t *>(blk + ly.f_coefV[k]) + (int64_t)slot * r;
+                for (int i = 0; i < r; ++i) {
+                    dk[i] = ck[i];
+                    dv[i] = cv[i];
+                }
+                if (s > 0) {
+                    for (int z = 0; z < 2; ++z) {
+                        const uint8_t *ix = static_cast<const uint8_t *>(z ? src.idxV : src.idxK) +
+                                            tr * ly.s_max;
+                        const int8_t *vx = static_cast<const int8_t *>(z ? src.valV : src.valK) +
+                                           tr * ly.s_max;
+                        const uint16_t *sx = static_cast<const uint16_t *>(z ? src.scaleV : src.scaleK);
+                        uint8_t *di = blk + (z ? ly.f_idxV[k] : ly.f_idxK[k]) + (int64_t)slot * s;
+                        uint8_t *dvl = blk + (z ? ly.f_valV[k] : ly.f_valK[k]) + (int64_t)slot * vb;
+                        uint16_t *ds = reinterpret_cast<uint16_t *>(blk + (z ? ly.f_scaleV[k] : ly.f_scaleK[k]));
+                        for (int u = 0; u < s; ++u) di[u] = ix[u];
+                        if (ly.bits == 8) {
+                            for (int u = 0; u < s; ++u) dvl[u] = static_cast<uint8_t>(vx[u]);
+                        } else {
+                            for (int u = 0; u < vb; ++u) {
+                                int lo = vx[2 * u] & 0xF;
+                                int hi = (2 * u + 1 < s) ? (vx[2 * u + 1] & 0xF) : 0;
+                                dvl[u] = static_cast<uint8_t>(lo | (hi << 4));
+                            }
+                        }
+                        ds[slot] = sx[tr];
+                    }
+                }
+                pmap[t] = (k << 28) | slot;
+            }
+        }
+        __syncthreads();
+        if (tid < ly.T) {
+            int add = 0;
+            for (int w = 0; w < kWaves; ++w) add += s_cnt[w][tid];
+            s_base[tid] += add;
+        }
+        __syncthreads();
+    }
+    if (tid < ly.T) {
+        int64_t c = s_base[tid];
+        counts_ptr(ly, arena, layer, b, h)[tid] = (int32_t)(c < ly.cap[tid] ? c : ly.cap[tid]);
+    }
+}
+
+// One workgroup per (sequence, KV head): every position of the layer written
+// back in logical form through the position map.
+__global__ __launch_bounds__(kBlock) void export_kernel(Layout ly, uint8_t *arena, int layer,
+                                                        dwkv_logical_layer dst, int32_t *counts,
+                                                        int32_t *slots)
+{
+    const int b = blockIdx.x / ly.Hkv, h = blockIdx.x % ly.Hkv;
+    const int tid = threadIdx.x;
+    uint8_t *blk = head_block_ptr(ly, arena, layer, b, h);
+    const int32_t *pmap = posmap_ptr(ly, arena, layer, b, h);
+    const int32_t *cnt = counts_ptr(ly, arena, layer, b, h);
+    int64_t n = 0;
+    for (int k = 0; k < ly.T; ++k) n += cnt[k];
+    if (tid < ly.T) counts[((int64_t)b * ly.Hkv + h) * ly.T + tid] = cnt[tid];
+    if (n > dst.n_max) n = dst.n_max;
+    const int64_t row0 = ((int64_t)b * ly.Hkv + h) * dst.n_max;
+    for (int64_t t = tid; t < n; t += kBlock) {
+        const int pm = pmap[t];
+        const int k = pm >> 28, slot = pm & 0x0FFFFFFF;
+        const int r = ly.rank[k], s = ly.resid[k], vb = ly.vbytes[k];
+        const int64_t tr = row0 + t;
+        static_cast<uint8_t *>(dst.tier)[tr] = static_cast<uint8_t>(k);
+        if (slots) slots[tr] = slot;
+        const uint16_t *sk = reinterpret_cast<const uint16_t *>(blk + ly.f_coefK[k]) + (int64_t)slot * r;
+        const uint16_t *sv = reinterpret_cast<const uint16_t *>(blk + ly.f_coefV[k]) + (int64_t)slot * r;
+        uint16_t *ck = static_cast<uint16_t *>(dst.coefK) + tr * ly.R;
+        uint16_t *cv = static_cast<uint16_t *>(dst.coefV) + tr * ly.R;
+        for (int i = 0; i < ly.R; ++i) {
+            ck[i] = i < r ? sk[i] : 0;
+            cv[i] = i < r ? sv[i] : 0;
+        }
+        if (ly.s_max == 0) continue;
+        for (int z = 0; z < 2; ++z) {
+            uint8_t *ix = static_cast<uint8_t *>(z ? dst.idxV : dst.idxK) + tr * ly.s_max;
+            int8_t *vx = static_cast<int8_t *>(z ? dst.valV : dst.valK) + tr * ly.s_max;
+            uint16_t *sx = static_cast<uint16_t *>(z ? dst.scaleV : dst.scaleK);
+            const uint8_t *si = blk + (z ? ly.f_idxV[k] : ly.f_idxK[k]) + (int64_t)slot * s;
+            const uint8_t *svl = blk + (z ? ly.f_valV[k] : ly.f_valK[k]) + (int64_t)slot * vb;
+            for (int u = 0; u < ly.s_max; ++u) {
+                ix[u] = u < s ? si[u] : 0;
+                vx[u] = u < s ? static_cast<int8_t>(unpack_code(svl, u, ly.bits)) : 0;
+            }
+            sx[tr] = s > 0 ? reinterpret_cast<const uint16_t *>(blk + (z ? ly.f_scaleV[k] : ly.f_scaleK[k]))[slot] : 0;
+        }
+    }
+}
+
+__global__ void fill_u32_kernel(uint32_t *p, uint32_t value, int64_t count)
+{
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < count;
+         i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = value;
+}
+
+}  // namespace
+
+hipError_t launch_import(const Layout &ly, uint8_t *arena, int layer,
+                         const dwkv_logical_layer &src, int b, int64_t n, hipStream_t stream)
+{
+    hipLaunchKernelGGL(import_kernel, dim3(ly.Hkv), dim3(kBlock), 0, stream, ly, arena, layer, src,
+                       b, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_export(const Layout &ly, uint8_t *arena, int layer,
+                         const dwkv_logical_layer &dst, int32_t *counts, int32_t *slots,
+                         int batch, hipStream_t stream)
+{
+    hipLaunchKernelGGL(export_kernel, dim3(batch * ly.Hkv), dim3(kBlock), 0, stream, ly, arena,
+                       layer, dst, counts, slots);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_u32(uint32_t *p, uint32_t value, int64_t count, hipStream_t stream)
+{
+    if (count <= 0) return hipSuccess;
+    int64_t blocks = (count + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p, value,
+                       count);
+    return hipGetLastError();
+}
+
+}  // namespace dwkv

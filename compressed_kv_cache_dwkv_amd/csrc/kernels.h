@@ -1,0 +1,42 @@
+// Launchers of the HIP kernels (one translation unit per kernel family).
+// Each returns the hipError_t of its launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "layout.h"
+
+namespace dwkv {
+
+// Decode workspace carve-up for `batch` sequences and `splits` workgroups per
+// (sequence, KV head): arrival counters, then per (b, query head, split) the
+// running max, the normaliser and the unnormalised output vector.
+struct DecodeWorkspace {
+    uint32_t *arrive;   // [B][Hkv]
+    float *pm;          // [B][Hq][S]
+    float *pl;          // [B][Hq][S]
+    float *po;          // [B][Hq][S][d]
+};
+
+size_t decode_workspace_bytes(const Layout &ly, int batch, int splits);
+DecodeWorkspace carve_workspace(const Layout &ly, void *ws, int batch, int splits);
+
+hipError_t launch_decode(const Layout &ly, uint8_t *arena, int layer, const void *q, int batch,
+                         float softmax_scale, float *out, const DecodeWorkspace &ws, int splits,
+                         hipStream_t stream);
+
+hipError_t launch_append(const Layout &ly, uint8_t *arena, int layer, const void *k,
+                         const void *v, const void *tier, const void *gateK, const void *gateV,
+                         int batch, hipStream_t stream);
+
+// Loads sequence b (n tokens) of `layer` from its logical form.
+hipError_t launch_import(const Layout &ly, uint8_t *arena, int layer,
+                         const dwkv_logical_layer &src, int b, int64_t n, hipStream_t stream);
+
+hipError_t launch_export(const Layout &ly, uint8_t *arena, int layer,
+                         const dwkv_logical_layer &dst, int32_t *counts, int32_t *slots,
+                         int batch, hipStream_t stream);
+
+hipError_t launch_fill_u32(uint32_t *p, uint32_t value, int64_t count, hipStream_t stream);
+
+}  // namespace dwkv

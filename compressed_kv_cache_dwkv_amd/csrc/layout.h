@@ -1,0 +1,96 @@
+// Arena layout of a DepthWeave-KV compressed cache on the GPU.
+//
+// Decode attention is a sum over all cached tokens with no positional mask
+// (every cached token precedes the decoding query), so tokens need not be
+// stored in position order.  The arena keeps them grouped by rank tier: for
+// every (layer, sequence, KV head) a contiguous block, and inside it one
+// region per tier whose tokens all have the same coefficient rank r_k and the
+// same residual channel count s_k.  A tier region is a structure of arrays,
+// each array 16-byte aligned and unpadded per token:
+//
+//   coefK [cap][r_k] fp16   coefV [cap][r_k] fp16
+//   idxK  [cap][s_k] u8     idxV  [cap][s_k] u8       (ascending channels)
+//   valK  [cap][vb_k] u8    valV  [cap][vb_k] u8      (codes; 4-bit codes two
+//                                                      per byte, element 2u in
+//                                                      the low nibble of byte u)
+//   scaleK [cap] fp16       scaleV [cap] fp16         (absent when s_k == 0)
+//
+// so a run of tokens of one tier is a few contiguous streams and every byte a
+// decode step reads is a byte the method needs.  Besides the blocks the arena
+// holds the sticky error word, token counts per (layer, sequence, KV head,
+// tier), a position map per (layer, sequence, KV head) giving each position's
+// (tier << 28 | slot), and the shared bases per (depth window, Z, KV head)
+// as r_max rows of head_dim fp16 values.
+#pragma once
+
+#include <stdint.h>
+
+#include "dwkv.h"
+
+#if defined(__HIPCC__)
+#define DWKV_HD __host__ __device__ __forceinline__
+#else
+#define DWKV_HD inline
+#endif
+
+namespace dwkv {
+
+constexpr int kMaxTiers = DWKV_MAX_TIERS;
+constexpr int kMaxHeadDim = 128;
+constexpr int kMaxRank = 128;
+constexpr int kMaxResid = 16;
+constexpr int kMaxGroupQ = 8;
+
+struct Layout {
+    int32_t L, G, Hq, Hkv, d, R, T, bits, Bmax, gq, s_max, qmax, num_groups;
+    int32_t rank[kMaxTiers];
+    int32_t resid[kMaxTiers];
+    int32_t vbytes[kMaxTiers];   // packed code bytes per token
+    int32_t weight[kMaxTiers];   // algorithmic bytes per token (K and V)
+    int64_t cap[kMaxTiers];
+    int64_t max_tokens;
+    int64_t off_err, off_counts, off_posmap, off_basis, off_seg;
+    int64_t basis_elems;         // Hkv * R * d  (one Z of one window)
+    int64_t head_block;          // bytes of one (layer, b, h) block
+    int64_t f_coefK[kMaxTiers], f_coefV[kMaxTiers];
+    int64_t f_idxK[kMaxTiers], f_idxV[kMaxTiers];
+    int64_t f_valK[kMaxTiers], f_valV[kMaxTiers];
+    int64_t f_scaleK[kMaxTiers], f_scaleV[kMaxTiers];
+    int64_t total;
+};
+
+DWKV_HD int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+DWKV_HD uint8_t *head_block_ptr(const Layout &ly, uint8_t *arena, int layer, int b, int h)
+{
+    return arena + ly.off_seg + (((int64_t)layer * ly.Bmax + b) * ly.Hkv + h) * ly.head_block;
+}
+
+DWKV_HD int32_t *counts_ptr(const Layout &ly, uint8_t *arena, int layer, int b, int h)
+{
+    return reinterpret_cast<int32_t *>(arena + ly.off_counts) +
+           (((int64_t)layer * ly.Bmax + b) * ly.Hkv + h) * ly.T;
+}
+
+DWKV_HD int32_t *posmap_ptr(const Layout &ly, uint8_t *arena, int layer, int b, int h)
+{
+    return reinterpret_cast<int32_t *>(arena + ly.off_posmap) +
+           (((int64_t)layer * ly.Bmax + b) * ly.Hkv + h) * ly.max_tokens;
+}
+
+DWKV_HD uint32_t *err_ptr(const Layout &ly, uint8_t *arena)
+{
+    return reinterpret_cast<uint32_t *>(arena + ly.off_err);
+}
+
+// Basis of window m for Z (0 = K, 1 = V), KV head h: R rows of d fp16.
+DWKV_HD uint16_t *basis_ptr(const Layout &ly, uint8_t *arena, int m, int z, int h)
+{
+    return reinterpret_cast<uint16_t *>(arena + ly.off_basis) +
+           ((int64_t)m * 2 + z) * ly.basis_elems + (int64_t)h * ly.R * ly.d;
+}
+
+// Host-side construction and validation; returns DWKV_OK or an error code.
+int build_layout(const dwkv_config *cfg, Layout *ly);
+
+}  // namespace dwkv

@@ -173,17 +173,18 @@ def append_residual(basis: np.ndarray, x: np.ndarray, r: int) -> np.ndarray:
 
 
 def append_layer(cfg, basisK: np.ndarray, basisV: np.ndarray, k: np.ndarray, v: np.ndarray,
-                 tier: np.ndarray, gate: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+                 tier: np.ndarray, gateK: Optional[np.ndarray] = None,
+                 gateV: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
     """Encode the new token of every (b, KV head) of one layer.
 
-    k, v: fp16 [B][H_kv][d]; tier: uint8 [B][H_kv]; gate: optional fp16
-    [B][H_kv].  Returns logical-token arrays: coef{K,V} [B][H_kv][r_max] fp16
+    k, v: fp16 [B][H_kv][d]; tier: uint8 [B][H_kv]; gateK, gateV: optional
+    fp16 [B][H_kv] (None = a gate of 1).  Returns logical-token arrays: coef{K,V} [B][H_kv][r_max] fp16
     (zero beyond the rank), idx/val{K,V} [B][H_kv][s_max], scale{K,V} [B][H_kv]."""
     B, H, d = k.shape
     R, S = cfg.r_max, cfg.s_max
     res = cfg.resid_per_tier
     out = {}
-    for z, x, bas in (("K", k, basisK), ("V", v, basisV)):
+    for z, x, bas, gate in (("K", k, basisK, gateK), ("V", v, basisV, gateV)):
         coef = np.zeros((B, H, R), np.float16)
         idx = np.zeros((B, H, S), np.uint8)
         val = np.zeros((B, H, S), np.int8)

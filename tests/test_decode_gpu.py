@@ -1,0 +1,156 @@
+"""GPU decode parity against the CPU oracle (needs an MI355X).
+
+Tolerance: per (sequence, query head) max_j |o_gpu - o_ref| / max_j |o_ref|
+<= 2e-3, the bound the workload specification fixes for outputs relative to
+the fp32-or-better oracle; row-max normalisation keeps an all-zero output
+from passing when outputs are small."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import workload as w
+from workload import gen as wg
+from workload.gen import gen_layer, gen_query, make_bases
+from tests.helpers import tiny_config
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+
+
+@pytest.fixture(scope="module")
+def G():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from tests import gpu_util
+    return gpu_util
+
+
+def _run(G, cfg, layers=(0,), splits=0, peak=1.0, identity=False, all_top=False, n=None,
+         needle=False, pairs=None, scale=None, ragged=None, variant_seed=0):
+    bases = make_bases(cfg, identity=identity, variant_seed=variant_seed)
+    n = cfg.n_tokens if n is None else n
+    cache = G.make_cache(cfg, splits=splits, n=n)
+    worst = 0.0
+    try:
+        G.load_bases(cache, bases, groups=sorted({l // cfg.layers_per_group for l in layers}))
+        for layer in layers:
+            lay = gen_layer(cfg, layer, n=n, all_top=all_top, variant_seed=variant_seed)
+            if ragged is not None:
+                lay["n_tokens"][:] = ragged
+            q = gen_query(cfg, layer, peak=peak, variant_seed=variant_seed)
+            m = layer // cfg.layers_per_group
+            if needle and n > 0:
+                wg.plant_needles(cfg, lay, bases["K"][m], q, wg.needle_positions(n))
+            G.load_layer(cache, layer, lay)
+            got = G.decode_np(cache, layer, q, scale)
+            ref = oracle.decode(cfg, lay, bases["K"][m], bases["V"][m], q, alpha=scale, pairs=pairs)
+            if pairs is not None:
+                rows = [(b, h * cfg.group_q + g) for b, h in pairs for g in range(cfg.group_q)]
+                got = np.stack([got[b, g] for b, g in rows])
+                ref = np.stack([ref[b, g] for b, g in rows])
+            assert np.isfinite(got).all()
+            if n == 0 or (ragged is not None and max(ragged) == 0):
+                assert not got.any()
+                continue
+            err = G.norm_err(got, ref)
+            if ragged is not None:
+                err = err[np.asarray(ragged) > 0] if err.ndim == 2 else err
+            worst = max(worst, float(err.max()))
+            assert err.max() <= TOL, f"layer {layer}: max normalised error {err.max():.3e}"
+        assert cache.check_errors() == 0
+    finally:
+        cache.close()
+    return worst
+
+
+# ---------------------------------------------------------------- tiny reference workload
+@pytest.mark.parametrize("splits", [0, 1, 2, 3, 7, 64])
+def test_tiny_reference_all_layers(G, splits):
+    cfg = w.get_config(0)
+    _run(G, cfg, layers=(0, 1), splits=splits)
+
+
+@pytest.mark.parametrize("variant", ["peaked", "needle", "all_top", "s0", "identity", "scale"])
+def test_tiny_reference_variants(G, variant):
+    cfg = w.get_config(0)
+    kw = {}
+    if variant == "peaked":
+        kw["peak"] = 16.0
+    elif variant == "needle":
+        kw["needle"] = True
+    elif variant == "all_top":
+        kw["all_top"] = True
+    elif variant == "s0":
+        cfg = cfg.with_(tier_resid=(0, 0, 0, 0))
+    elif variant == "identity":
+        cfg = cfg.with_(r_max=64, tier_rank=(4, 8, 16, 64))
+        kw["identity"] = True
+    elif variant == "scale":
+        kw["scale"] = 0.3
+    _run(G, cfg, layers=(0, 1), splits=5, **kw)
+
+
+@pytest.mark.parametrize("n", [0, 1, 2, 63, 64, 65, 1000])
+def test_small_and_ragged_contexts(G, n):
+    cfg = tiny_config(batch=3, num_q_heads=8, num_kv_heads=2, head_dim=64, r_max=32,
+                      tier_rank=(4, 8, 16, 32), tier_prob=(0.4, 0.3, 0.2, 0.1), resid_channels=4,
+                      resid_bits=4, n_tokens=max(n, 1))
+    ragged = [n, max(n // 3, 0), 0 if n else 0]
+    _run(G, cfg, layers=(0,), splits=4, n=max(n, 1), ragged=ragged)
+
+
+@pytest.mark.parametrize("gq,d,bits", [(1, 64, 8), (2, 128, 4), (8, 128, 4), (4, 64, 8)])
+def test_group_sizes_and_head_dims(G, gq, d, bits):
+    cfg = tiny_config(batch=2, num_kv_heads=2, num_q_heads=2 * gq, head_dim=d, r_max=64,
+                      tier_rank=(8, 16, 32, 64), tier_prob=(0.55, 0.25, 0.12, 0.08),
+                      resid_channels=8 if bits == 4 else 5, resid_bits=bits, n_tokens=3000)
+    _run(G, cfg, layers=(0, 1), splits=9, peak=4.0)
+
+
+def test_wide_basis_identity_d128(G):
+    """B = I with r_max = d = 128: the cache stores K and V directly."""
+    cfg = tiny_config(batch=1, num_kv_heads=2, num_q_heads=8, head_dim=128, r_max=128,
+                      tier_rank=(32, 64, 128), tier_prob=(0.5, 0.3, 0.2), resid_channels=8,
+                      resid_bits=4, n_tokens=2000)
+    _run(G, cfg, layers=(0,), splits=6, identity=True, peak=8.0)
+
+
+# ---------------------------------------------------------------- full-size workloads
+# Every layer of these workloads is decoded in the launch configuration the
+# benchmark uses (automatic split count); the oracle checks sampled
+# (sequence, KV head) pairs of sampled layers.
+@pytest.mark.parametrize("ci,layers,pairs", [
+    (1, (0, 31), None),
+    (2, (0, 17), [(0, 0), (0, 5)]),
+    (3, (3,), [(0, 0), (7, 3), (15, 7)]),
+    (4, (0, 79), [(0, 0), (0, 7)]),
+])
+def test_full_size_workloads_sampled(G, ci, layers, pairs):
+    cfg = w.get_config(ci)
+    _run(G, cfg, layers=layers, pairs=pairs)
+
+
+def test_full_size_64k_peaked_and_needle(G):
+    cfg = w.get_config(2)
+    _run(G, cfg, layers=(9,), pairs=[(0, 1), (0, 6)], peak=16.0)
+    _run(G, cfg, layers=(9,), pairs=[(0, 2)], needle=True)
+
+
+def test_repeat_launch_is_bitwise_deterministic(G):
+    cfg = w.get_config(1)
+    bases = make_bases(cfg)
+    cache = G.make_cache(cfg)
+    try:
+        G.load_bases(cache, bases, groups=[0])
+        lay = gen_layer(cfg, 2)
+        G.load_layer(cache, 2, lay)
+        q = gen_query(cfg, 2)
+        a = G.decode_np(cache, 2, q)
+        for _ in range(3):
+            assert np.array_equal(G.decode_np(cache, 2, q), a)
+    finally:
+        cache.close()

@@ -240,3 +240,17 @@ def plant_needles(cfg: Config, lay: Dict[str, np.ndarray], basisK16: np.ndarray,
                     lay["val" + z][b, h, t] = 0
                     lay["scale" + z][b, h, t] = 0
     return lay
+
+
+def max_tier_counts(cfg: Config, n: Optional[int] = None, all_top: bool = False,
+                    variant_seed: int = 0) -> np.ndarray:
+    """Largest number of tokens any (layer, sequence, KV head) of the workload
+    holds in each tier (used to size tier capacities)."""
+    n = cfg.n_tokens if n is None else int(n)
+    seed = _seed_of(cfg, variant_seed)
+    mx = np.zeros(cfg.num_tiers, np.int64)
+    for m in range(cfg.num_groups):
+        tier = _tiers(cfg, m * cfg.layers_per_group, n, seed, all_top)
+        for k in range(cfg.num_tiers):
+            mx[k] = max(mx[k], int((tier == k).sum(axis=-1).max()) if n > 0 else 0)
+    return mx
