@@ -17,6 +17,11 @@ from typing import Dict, Optional, Sequence
 
 import numpy as np
 
+# torch first: it loads the HIP runtime (libamdhip64.so.7) whose device memory
+# and streams the callers hand over; libdwkv.so must bind to that same
+# runtime instance rather than load a second copy from the ROCm install.
+import torch  # noqa: F401
+
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdwkv.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "dwkv.h")
@@ -86,16 +91,23 @@ for _name, _args in _SIGS.items():
     _f.restype = ctypes.c_int
 _lib.dwkv_strerror.argtypes = [_I]
 _lib.dwkv_strerror.restype = ctypes.c_char_p
+_lib.dwkv_last_hip_error.argtypes = []
+_lib.dwkv_last_hip_error.restype = ctypes.c_char_p
 
 
 class DwkvError(RuntimeError):
     def __init__(self, code: int, where: str):
-        super().__init__(f"{where}: {dwkv_strerror(code)} ({code})")
+        detail = f" [{dwkv_last_hip_error()}]" if code == DWKV_ERR_HIP else ""
+        super().__init__(f"{where}: {dwkv_strerror(code)} ({code}){detail}")
         self.code = code
 
 
 def dwkv_strerror(code: int) -> str:
     return _lib.dwkv_strerror(int(code)).decode()
+
+
+def dwkv_last_hip_error() -> str:
+    return _lib.dwkv_last_hip_error().decode()
 
 
 def _check(code: int, where: str) -> None:

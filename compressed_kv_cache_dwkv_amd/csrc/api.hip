@@ -2,6 +2,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <cstdio>
 #include <cstring>
 #include <new>
 
@@ -138,7 +139,14 @@ DecodeWorkspace carve_workspace(const Layout &ly, void *ws, int batch, int split
 
 using dwkv::Layout;
 
-static int hip_status(hipError_t e) { return e == hipSuccess ? DWKV_OK : DWKV_ERR_HIP; }
+static thread_local char g_hip_detail[160];
+
+static int hip_status(hipError_t e)
+{
+    if (e == hipSuccess) return DWKV_OK;
+    std::snprintf(g_hip_detail, sizeof g_hip_detail, "%s (%d)", hipGetErrorString(e), (int)e);
+    return DWKV_ERR_HIP;
+}
 
 static bool valid_handle(const dwkv_handle *h) { return h && h->arena; }
 
@@ -228,7 +236,7 @@ int dwkv_import_layer(dwkv_handle *h, int layer, const dwkv_logical_layer *src,
     hipStream_t s = static_cast<hipStream_t>(stream);
     for (int b = 0; b < batch; ++b) {
         hipError_t e = dwkv::launch_import(ly, h->arena, layer, *src, b, n_tokens[b], s);
-        if (e != hipSuccess) return DWKV_ERR_HIP;
+        if (e != hipSuccess) return hip_status(e);
     }
     return DWKV_OK;
 }
@@ -302,7 +310,7 @@ int dwkv_check_errors(dwkv_handle *h, void *stream, uint32_t *bits)
     hipError_t e = hipStreamSynchronize(s);
     if (e == hipSuccess)
         e = hipMemcpy(&word, dwkv::err_ptr(h->ly, h->arena), 4, hipMemcpyDeviceToHost);
-    if (e != hipSuccess) return DWKV_ERR_HIP;
+    if (e != hipSuccess) return hip_status(e);
     if (bits) *bits = word;
     return word ? DWKV_ERR_DEVICE : DWKV_OK;
 }
@@ -313,6 +321,8 @@ int dwkv_clear_errors(dwkv_handle *h, void *stream)
     hipStream_t s = static_cast<hipStream_t>(stream);
     return hip_status(dwkv::launch_fill_u32(dwkv::err_ptr(h->ly, h->arena), 0u, 1, s));
 }
+
+const char *dwkv_last_hip_error(void) { return g_hip_detail; }
 
 const char *dwkv_strerror(int code)
 {

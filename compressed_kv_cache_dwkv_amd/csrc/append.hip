@@ -168,6 +168,7 @@ hipError_t launch_append(const Layout &ly, uint8_t *arena, int layer, const void
                          const void *v, const void *tier, const void *gateK, const void *gateV,
                          int batch, hipStream_t stream)
 {
+    (void)hipGetLastError();  // drop errors left by earlier, unrelated calls
     hipLaunchKernelGGL(append_kernel, dim3(batch * ly.Hkv), dim3(2 * kWave), 0, stream, ly, arena,
                        layer, static_cast<const uint16_t *>(k), static_cast<const uint16_t *>(v),
                        static_cast<const uint8_t *>(tier), static_cast<const uint16_t *>(gateK),

@@ -247,6 +247,7 @@ hipError_t launch_decode(const Layout &ly, uint8_t *arena, int layer, const void
     const dim3 grid(splits, ly.Hkv, batch);
     const float qs = softmax_scale * kLog2e;
     const uint16_t *qq = static_cast<const uint16_t *>(q);
+    (void)hipGetLastError();  // drop errors left by earlier, unrelated calls
     switch (ly.gq) {
     case 1: hipLaunchKernelGGL(decode_kernel<1>, grid, dim3(kBlock), 0, stream, ly, arena, layer, qq, out, ws, splits, qs); break;
     case 2: hipLaunchKernelGGL(decode_kernel<2>, grid, dim3(kBlock), 0, stream, ly, arena, layer, qq, out, ws, splits, qs); break;

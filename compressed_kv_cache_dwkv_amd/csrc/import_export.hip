@@ -163,6 +163,7 @@ __global__ void fill_u32_kernel(uint32_t *p, uint32_t value, int64_t count)
 hipError_t launch_import(const Layout &ly, uint8_t *arena, int layer,
                          const dwkv_logical_layer &src, int b, int64_t n, hipStream_t stream)
 {
+    (void)hipGetLastError();  // drop errors left by earlier, unrelated calls
     hipLaunchKernelGGL(import_kernel, dim3(ly.Hkv), dim3(kBlock), 0, stream, ly, arena, layer, src,
                        b, n);
     return hipGetLastError();
@@ -172,6 +173,7 @@ hipError_t launch_export(const Layout &ly, uint8_t *arena, int layer,
                          const dwkv_logical_layer &dst, int32_t *counts, int32_t *slots,
                          int batch, hipStream_t stream)
 {
+    (void)hipGetLastError();  // drop errors left by earlier, unrelated calls
     hipLaunchKernelGGL(export_kernel, dim3(batch * ly.Hkv), dim3(kBlock), 0, stream, ly, arena,
                        layer, dst, counts, slots);
     return hipGetLastError();
@@ -182,6 +184,7 @@ hipError_t launch_fill_u32(uint32_t *p, uint32_t value, int64_t count, hipStream
     if (count <= 0) return hipSuccess;
     int64_t blocks = (count + 255) / 256;
     if (blocks > 4096) blocks = 4096;
+    (void)hipGetLastError();  // drop errors left by earlier, unrelated calls
     hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p, value,
                        count);
     return hipGetLastError();

@@ -217,6 +217,10 @@ int dwkv_clear_errors(dwkv_handle *h, void *stream);
 /* Static text for an error code. */
 const char *dwkv_strerror(int code);
 
+/* Text of the HIP error behind the calling thread's last DWKV_ERR_HIP
+ * ("" if none); valid until the thread's next failing call. */
+const char *dwkv_last_hip_error(void);
+
 #ifdef __cplusplus
 }
 #endif

@@ -132,3 +132,10 @@ def test_strerror():
     for code in range(-6, 0):
         assert d.dwkv_strerror(code) != "unknown error"
     assert d.dwkv_strerror(-99) == "unknown error"
+
+
+def test_single_hip_runtime_in_process():
+    """The binding must share torch's HIP runtime: one libamdhip64 mapped."""
+    maps = open("/proc/self/maps").read()
+    libs = {l.split()[-1] for l in maps.splitlines() if "libamdhip64" in l}
+    assert len(libs) == 1, libs
