@@ -44,6 +44,7 @@ DWKV_ERR_DEVICE = -6
 DWKV_DEVERR_TIER_FULL = 1
 DWKV_DEVERR_POS_FULL = 2
 DWKV_DEVERR_BAD_TIER = 4
+DWKV_DEVERR_BAD_INDEX = 8
 
 
 class dwkv_config(ctypes.Structure):

@@ -35,7 +35,7 @@ int build_layout(const dwkv_config *c, Layout *ly)
     if (c->r_max % 4 != 0 || c->r_max > kMaxRank) return DWKV_ERR_UNSUPPORTED;
     if (c->resid_bits != 4 && c->resid_bits != 8) return DWKV_ERR_UNSUPPORTED;
     if (c->max_tokens >= (int64_t(1) << 31)) return DWKV_ERR_UNSUPPORTED;
-    if (c->decode_splits > 1024) return DWKV_ERR_UNSUPPORTED;
+    if (c->decode_splits > kMaxSplits) return DWKV_ERR_UNSUPPORTED;
     int prev = 0, smax = 0;
     for (int k = 0; k < c->num_tiers; ++k) {
         int r = c->tier_rank[k], s = c->tier_resid[k];
@@ -64,13 +64,13 @@ int build_layout(const dwkv_config *c, Layout *ly)
 
     int64_t blk = 0;
     for (int k = 0; k < c->num_tiers; ++k) {
-        const int64_t cap = c->tier_capacity[k];
+        const int64_t cap = align_up(c->tier_capacity[k], 16);  // whole 16-token blocks
         const int r = c->tier_rank[k], s = c->tier_resid[k];
         const int vb = (s * c->resid_bits + 7) / 8;
         ly->rank[k] = r;
         ly->resid[k] = s;
         ly->vbytes[k] = vb;
-        ly->cap[k] = cap;
+        ly->cap[k] = c->tier_capacity[k];
         ly->weight[k] = 4 * r + (s > 0 ? 2 * (s + vb + 2) : 0);
         blk = align_up(blk, 256);
         ly->f_coefK[k] = blk; blk = align_up(blk + cap * r * 2, 16);
@@ -95,19 +95,21 @@ int build_layout(const dwkv_config *c, Layout *ly)
     return DWKV_OK;
 }
 
-// Workgroups per (sequence, KV head) for decode: enough to put several on
-// each of the 256 compute units when few heads are active, never so many
-// that a workgroup streams less than ~32 KiB of its largest possible share.
+// Workgroups per (sequence, KV head) for decode.  A decode workgroup fills
+// one compute unit (8 waves, more than half the LDS), so the grid aims at
+// one workgroup per compute unit of the 256, while leaving each workgroup at
+// least 1024 token slots (16 tiles of 64) of its head.
 static int plan_splits(const dwkv_config &c, const Layout &ly)
 {
     if (c.decode_splits > 0) return c.decode_splits;
-    int64_t wcap = 0;
-    for (int k = 0; k < ly.T; ++k) wcap += ly.cap[k] * ly.weight[k];
-    int64_t by_bytes = (wcap + 32767) / 32768;
-    int64_t by_fill = (2048 + (int64_t)ly.Hkv - 1) / ly.Hkv;
-    int64_t s = by_bytes < by_fill ? by_bytes : by_fill;
+    int64_t slots = 0;
+    for (int k = 0; k < ly.T; ++k) slots += ly.cap[k];
+    const int64_t heads = (int64_t)ly.Bmax * ly.Hkv;
+    int64_t s = (256 + heads - 1) / heads;
+    const int64_t by_tokens = slots / 1024;
+    if (s > by_tokens) s = by_tokens;
     if (s < 1) s = 1;
-    if (s > 512) s = 512;
+    if (s > kMaxSplits) s = kMaxSplits;
     return (int)s;
 }
 

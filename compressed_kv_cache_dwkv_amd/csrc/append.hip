@@ -79,14 +79,13 @@ __global__ __launch_bounds__(2 * kWave) void append_kernel(Layout ly, uint8_t *a
     __syncthreads();
 
     // 1. coefficients c_i = fp16(sum_j B[i][j] x_j), sequential in j
-    uint16_t *cdst = reinterpret_cast<uint16_t *>(blk + (z ? ly.f_coefV[k] : ly.f_coefK[k])) +
-                     (int64_t)slot * r;
+    uint16_t *cdst = reinterpret_cast<uint16_t *>(blk + (z ? ly.f_coefV[k] : ly.f_coefK[k]));
     for (int i = lane; i < r; i += kWave) {
         const uint16_t *bi = B + (int64_t)i * d;
         float acc = 0.0f;
         for (int j = 0; j < d; ++j) acc = __builtin_fmaf(h2f(bi[j]), s_x[z][j], acc);
         const uint16_t c16 = f2h(acc);
-        cdst[i] = c16;
+        cdst[z ? coefV_index(r, slot, i) : (int64_t)slot * r + i] = c16;
         s_c[z][i] = h2f(c16);
     }
     __syncthreads();

@@ -59,10 +59,10 @@ __global__ __launch_bounds__(kBlock) void import_kernel(Layout ly, uint8_t *aren
                 const uint16_t *ck = static_cast<const uint16_t *>(src.coefK) + tr * ly.R;
                 const uint16_t *cv = static_cast<const uint16_t *>(src.coefV) + tr * ly.R;
                 uint16_t *dk = reinterpret_cast<uint16_t *>(blk + ly.f_coefK[k]) + (int64_t)slot * r;
-                uint16_t *dv = reinterpret_cast<uint16_t *>(blk + ly.f_coefV[k]) + (int64_t)slot * r;
+                uint16_t *dv = reinterpret_cast<uint16_t *>(blk + ly.f_coefV[k]);
                 for (int i = 0; i < r; ++i) {
                     dk[i] = ck[i];
-                    dv[i] = cv[i];
+                    dv[coefV_index(r, slot, i)] = cv[i];
                 }
                 if (s > 0) {
                     for (int z = 0; z < 2; ++z) {
@@ -74,7 +74,14 @@ __global__ __launch_bounds__(kBlock) void import_kernel(Layout ly, uint8_t *aren
                         uint8_t *di = blk + (z ? ly.f_idxV[k] : ly.f_idxK[k]) + (int64_t)slot * s;
                         uint8_t *dvl = blk + (z ? ly.f_valV[k] : ly.f_valK[k]) + (int64_t)slot * vb;
                         uint16_t *ds = reinterpret_cast<uint16_t *>(blk + (z ? ly.f_scaleV[k] : ly.f_scaleK[k]));
-                        for (int u = 0; u < s; ++u) di[u] = ix[u];
+                        for (int u = 0; u < s; ++u) {
+                            int j = ix[u];
+                            if (j >= ly.d) {   // decode trusts indices < head_dim
+                                atomicOr(err, DWKV_DEVERR_BAD_INDEX);
+                                j = ly.d - 1;
+                            }
+                            di[u] = static_cast<uint8_t>(j);
+                        }
                         if (ly.bits == 8) {
                             for (int u = 0; u < s; ++u) dvl[u] = static_cast<uint8_t>(vx[u]);
                         } else {
@@ -128,12 +135,12 @@ __global__ __launch_bounds__(kBlock) void export_kernel(Layout ly, uint8_t *aren
         static_cast<uint8_t *>(dst.tier)[tr] = static_cast<uint8_t>(k);
         if (slots) slots[tr] = slot;
         const uint16_t *sk = reinterpret_cast<const uint16_t *>(blk + ly.f_coefK[k]) + (int64_t)slot * r;
-        const uint16_t *sv = reinterpret_cast<const uint16_t *>(blk + ly.f_coefV[k]) + (int64_t)slot * r;
+        const uint16_t *sv = reinterpret_cast<const uint16_t *>(blk + ly.f_coefV[k]);
         uint16_t *ck = static_cast<uint16_t *>(dst.coefK) + tr * ly.R;
         uint16_t *cv = static_cast<uint16_t *>(dst.coefV) + tr * ly.R;
         for (int i = 0; i < ly.R; ++i) {
             ck[i] = i < r ? sk[i] : 0;
-            cv[i] = i < r ? sv[i] : 0;
+            cv[i] = i < r ? sv[coefV_index(r, slot, i)] : 0;
         }
         if (ly.s_max == 0) continue;
         for (int z = 0; z < 2; ++z) {

@@ -8,7 +8,9 @@
 // same residual channel count s_k.  A tier region is a structure of arrays,
 // each array 16-byte aligned and unpadded per token:
 //
-//   coefK [cap][r_k] fp16   coefV [cap][r_k] fp16
+//   coefK [cap][r_k] fp16                             (token-major rows)
+//   coefV [cap/16][r_k][16] fp16                      (16-token blocks, channel-
+//                                                      major inside a block)
 //   idxK  [cap][s_k] u8     idxV  [cap][s_k] u8       (ascending channels)
 //   valK  [cap][vb_k] u8    valV  [cap][vb_k] u8      (codes; 4-bit codes two
 //                                                      per byte, element 2u in
@@ -16,7 +18,11 @@
 //   scaleK [cap] fp16       scaleV [cap] fp16         (absent when s_k == 0)
 //
 // so a run of tokens of one tier is a few contiguous streams and every byte a
-// decode step reads is a byte the method needs.  Besides the blocks the arena
+// decode step reads is a byte the method needs.  K coefficients are rows of
+// a token x channel matrix and V coefficients columns of 16 tokens: both
+// then load directly as operands of 16x16x16 matrix-core products (scores
+// contract over channels, value sums over tokens).  Capacities are rounded
+// up to whole 16-token blocks.  Besides the blocks the arena
 // holds the sticky error word, token counts per (layer, sequence, KV head,
 // tier), a position map per (layer, sequence, KV head) giving each position's
 // (tier << 28 | slot), and the shared bases per (depth window, Z, KV head)
@@ -40,6 +46,7 @@ constexpr int kMaxHeadDim = 128;
 constexpr int kMaxRank = 128;
 constexpr int kMaxResid = 16;
 constexpr int kMaxGroupQ = 8;
+constexpr int kMaxSplits = 256;   // decode workgroups per (sequence, KV head)
 
 struct Layout {
     int32_t L, G, Hq, Hkv, d, R, T, bits, Bmax, gq, s_max, qmax, num_groups;
@@ -88,6 +95,13 @@ DWKV_HD uint16_t *basis_ptr(const Layout &ly, uint8_t *arena, int m, int z, int 
 {
     return reinterpret_cast<uint16_t *>(arena + ly.off_basis) +
            ((int64_t)m * 2 + z) * ly.basis_elems + (int64_t)h * ly.R * ly.d;
+}
+
+// Element (slot, i) of a tier's V coefficients, in fp16 units from the array
+// start: 16-token blocks, each r channel rows of 16 tokens.
+DWKV_HD int64_t coefV_index(int r, int64_t slot, int i)
+{
+    return ((slot >> 4) * r + i) * 16 + (slot & 15);
 }
 
 // Host-side construction and validation; returns DWKV_OK or an error code.

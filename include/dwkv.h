@@ -64,6 +64,8 @@ extern "C" {
 #define DWKV_DEVERR_TIER_FULL 1u  /* a token did not fit its tier's capacity      */
 #define DWKV_DEVERR_POS_FULL 2u   /* a position beyond max_tokens                 */
 #define DWKV_DEVERR_BAD_TIER 4u   /* a tier index >= num_tiers in device input    */
+#define DWKV_DEVERR_BAD_INDEX 8u  /* a residual channel index >= head_dim on import
+                                     (stored as head_dim - 1)                     */
 
 /*
  * Static shape of one cache.  Supported: head_dim 64 or 128; r_max a multiple
@@ -146,7 +148,8 @@ int dwkv_set_basis(dwkv_handle *h, int group, const void *basisK, const void *ba
  * see dwkv_logical_layer) holding n_tokens[b] tokens for sequence b < batch
  * (n_tokens: host int64 [batch]).  Tokens keep their position order inside
  * each tier.  Host-checked: n_tokens[b] <= min(n_max, max_tokens).
- * Device-checked (error word): tier indices and per-tier capacity.
+ * Device-checked (error word): tier indices, residual channel indices and
+ * per-tier capacity.
  */
 int dwkv_import_layer(dwkv_handle *h, int layer, const dwkv_logical_layer *src,
                       const int64_t *n_tokens, int batch, void *stream);

@@ -20,11 +20,11 @@ def to_dev(lay: Dict[str, np.ndarray]) -> Dict[str, torch.Tensor]:
 
 
 def make_cache(cfg: Config, capacity=None, extra: int = 16, splits: int = 0,
-               max_tokens: Optional[int] = None, n: Optional[int] = None):
+               max_tokens: Optional[int] = None, n: Optional[int] = None, all_top: bool = False):
     from compressed_kv_cache_dwkv_amd.cache import CompressedKVCache
     n = cfg.n_tokens if n is None else n
     if capacity is None:
-        capacity = [int(c) + extra for c in max_tier_counts(cfg, n)]
+        capacity = [int(c) + extra for c in max_tier_counts(cfg, n, all_top=all_top)]
     return CompressedKVCache(
         cfg.num_layers, cfg.layers_per_group, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim,
         cfg.r_max, cfg.tier_rank, cfg.resid_per_tier, cfg.resid_bits, cfg.batch, capacity,

@@ -39,6 +39,7 @@ def test_every_declared_symbol_is_exported():
     ("num_layers", 0, d.DWKV_ERR_INVALID_ARG),
     ("max_batch", 0, d.DWKV_ERR_INVALID_ARG),
     ("decode_splits", -1, d.DWKV_ERR_INVALID_ARG),
+    ("decode_splits", 257, d.DWKV_ERR_UNSUPPORTED),
 ])
 def test_config_validation(field, value, code):
     cfg = _cfg()

@@ -33,7 +33,7 @@ def _run(G, cfg, layers=(0,), splits=0, peak=1.0, identity=False, all_top=False,
          needle=False, pairs=None, scale=None, ragged=None, variant_seed=0):
     bases = make_bases(cfg, identity=identity, variant_seed=variant_seed)
     n = cfg.n_tokens if n is None else n
-    cache = G.make_cache(cfg, splits=splits, n=n)
+    cache = G.make_cache(cfg, splits=splits, n=n, all_top=all_top)
     worst = 0.0
     try:
         G.load_bases(cache, bases, groups=sorted({l // cfg.layers_per_group for l in layers}))
@@ -46,6 +46,7 @@ def _run(G, cfg, layers=(0,), splits=0, peak=1.0, identity=False, all_top=False,
             if needle and n > 0:
                 wg.plant_needles(cfg, lay, bases["K"][m], q, wg.needle_positions(n))
             G.load_layer(cache, layer, lay)
+            assert cache.check_errors() == 0, "import overflowed the cache"
             got = G.decode_np(cache, layer, q, scale)
             ref = oracle.decode(cfg, lay, bases["K"][m], bases["V"][m], q, alpha=scale, pairs=pairs)
             if pairs is not None:
