@@ -69,20 +69,24 @@ int build_layout(const dwkv_config *c, Layout *ly)
         const int vb = (s * c->resid_bits + 7) / 8;
         ly->rank[k] = r;
         ly->resid[k] = s;
+        const int is = (s + 3) & ~3, vs = (vb + 3) & ~3;
         ly->vbytes[k] = vb;
+        ly->istride[k] = is;
+        ly->vstride[k] = vs;
         ly->cap[k] = c->tier_capacity[k];
-        ly->weight[k] = 4 * r + (s > 0 ? 2 * (s + vb + 2) : 0);
+        ly->weight[k] = 4 * r + (s > 0 ? 2 * (is + vs + 2) : 0);
         blk = align_up(blk, 256);
         ly->f_coefK[k] = blk; blk = align_up(blk + cap * r * 2, 16);
         ly->f_coefV[k] = blk; blk = align_up(blk + cap * r * 2, 16);
-        ly->f_idxK[k] = blk;  blk = align_up(blk + cap * s, 16);
-        ly->f_idxV[k] = blk;  blk = align_up(blk + cap * s, 16);
-        ly->f_valK[k] = blk;  blk = align_up(blk + cap * vb, 16);
-        ly->f_valV[k] = blk;  blk = align_up(blk + cap * vb, 16);
+        ly->f_idxK[k] = blk;  blk = align_up(blk + cap * is, 16);
+        ly->f_idxV[k] = blk;  blk = align_up(blk + cap * is, 16);
+        ly->f_valK[k] = blk;  blk = align_up(blk + cap * vs, 16);
+        ly->f_valV[k] = blk;  blk = align_up(blk + cap * vs, 16);
         ly->f_scaleK[k] = blk; blk = align_up(blk + (s > 0 ? cap * 2 : 0), 16);
         ly->f_scaleV[k] = blk; blk = align_up(blk + (s > 0 ? cap * 2 : 0), 16);
     }
-    ly->head_block = align_up(blk, 256);
+    // 16 spare bytes: fixed-width residual reads may run past the last token
+    ly->head_block = align_up(blk + 16, 256);
     const int64_t heads = (int64_t)ly->L * ly->Bmax * ly->Hkv;
     int64_t off = 0;
     ly->off_err = off;      off = align_up(off + 4, 256);

@@ -136,8 +136,8 @@ __global__ __launch_bounds__(2 * kWave) void append_kernel(Layout ly, uint8_t *a
         }
         __syncthreads();
         const int vb = ly.vbytes[k];
-        uint8_t *idst = blk + (z ? ly.f_idxV[k] : ly.f_idxK[k]) + (int64_t)slot * s;
-        uint8_t *vdst = blk + (z ? ly.f_valV[k] : ly.f_valK[k]) + (int64_t)slot * vb;
+        uint8_t *idst = blk + (z ? ly.f_idxV[k] : ly.f_idxK[k]) + (int64_t)slot * ly.istride[k];
+        uint8_t *vdst = blk + (z ? ly.f_valV[k] : ly.f_valK[k]) + (int64_t)slot * ly.vstride[k];
         if (lane < s) idst[lane] = s_idx[z][lane];
         if (ly.bits == 8) {
             if (lane < s) vdst[lane] = static_cast<uint8_t>(s_code[z][lane]);

@@ -55,6 +55,7 @@ __global__ __launch_bounds__(kBlock) void import_kernel(Layout ly, uint8_t *aren
                 atomicOr(err, DWKV_DEVERR_TIER_FULL);
             } else {
                 const int r = ly.rank[k], s = ly.resid[k], vb = ly.vbytes[k];
+                const int is = ly.istride[k], vs = ly.vstride[k];
                 const int64_t tr = row0 + t;
                 const uint16_t *ck = static_cast<const uint16_t *>(src.coefK) + tr * ly.R;
                 const uint16_t *cv = static_cast<const uint16_t *>(src.coefV) + tr * ly.R;
@@ -71,8 +72,8 @@ __global__ __launch_bounds__(kBlock) void import_kernel(Layout ly, uint8_t *aren
                         const int8_t *vx = static_cast<const int8_t *>(z ? src.valV : src.valK) +
                                            tr * ly.s_max;
                         const uint16_t *sx = static_cast<const uint16_t *>(z ? src.scaleV : src.scaleK);
-                        uint8_t *di = blk + (z ? ly.f_idxV[k] : ly.f_idxK[k]) + (int64_t)slot * s;
-                        uint8_t *dvl = blk + (z ? ly.f_valV[k] : ly.f_valK[k]) + (int64_t)slot * vb;
+                        uint8_t *di = blk + (z ? ly.f_idxV[k] : ly.f_idxK[k]) + (int64_t)slot * is;
+                        uint8_t *dvl = blk + (z ? ly.f_valV[k] : ly.f_valK[k]) + (int64_t)slot * vs;
                         uint16_t *ds = reinterpret_cast<uint16_t *>(blk + (z ? ly.f_scaleV[k] : ly.f_scaleK[k]));
                         for (int u = 0; u < s; ++u) {
                             int j = ix[u];
@@ -130,7 +131,8 @@ __global__ __launch_bounds__(kBlock) void export_kernel(Layout ly, uint8_t *aren
     for (int64_t t = tid; t < n; t += kBlock) {
         const int pm = pmap[t];
         const int k = pm >> 28, slot = pm & 0x0FFFFFFF;
-        const int r = ly.rank[k], s = ly.resid[k], vb = ly.vbytes[k];
+        const int r = ly.rank[k], s = ly.resid[k];
+        const int is = ly.istride[k], vs = ly.vstride[k];
         const int64_t tr = row0 + t;
         static_cast<uint8_t *>(dst.tier)[tr] = static_cast<uint8_t>(k);
         if (slots) slots[tr] = slot;
@@ -147,8 +149,8 @@ __global__ __launch_bounds__(kBlock) void export_kernel(Layout ly, uint8_t *aren
             uint8_t *ix = static_cast<uint8_t *>(z ? dst.idxV : dst.idxK) + tr * ly.s_max;
             int8_t *vx = static_cast<int8_t *>(z ? dst.valV : dst.valK) + tr * ly.s_max;
             uint16_t *sx = static_cast<uint16_t *>(z ? dst.scaleV : dst.scaleK);
-            const uint8_t *si = blk + (z ? ly.f_idxV[k] : ly.f_idxK[k]) + (int64_t)slot * s;
-            const uint8_t *svl = blk + (z ? ly.f_valV[k] : ly.f_valK[k]) + (int64_t)slot * vb;
+            const uint8_t *si = blk + (z ? ly.f_idxV[k] : ly.f_idxK[k]) + (int64_t)slot * is;
+            const uint8_t *svl = blk + (z ? ly.f_valV[k] : ly.f_valK[k]) + (int64_t)slot * vs;
             for (int u = 0; u < ly.s_max; ++u) {
                 ix[u] = u < s ? si[u] : 0;
                 vx[u] = u < s ? static_cast<int8_t>(unpack_code(svl, u, ly.bits)) : 0;

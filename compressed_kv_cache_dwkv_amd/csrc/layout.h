@@ -11,14 +11,17 @@
 //   coefK [cap][r_k] fp16                             (token-major rows)
 //   coefV [cap/16][r_k][16] fp16                      (16-token blocks, channel-
 //                                                      major inside a block)
-//   idxK  [cap][s_k] u8     idxV  [cap][s_k] u8       (ascending channels)
-//   valK  [cap][vb_k] u8    valV  [cap][vb_k] u8      (codes; 4-bit codes two
+//   idxK  [cap][is_k] u8    idxV  [cap][is_k] u8      (ascending channels)
+//   valK  [cap][vs_k] u8    valV  [cap][vs_k] u8      (codes; 4-bit codes two
 //                                                      per byte, element 2u in
 //                                                      the low nibble of byte u)
 //   scaleK [cap] fp16       scaleV [cap] fp16         (absent when s_k == 0)
 //
-// so a run of tokens of one tier is a few contiguous streams and every byte a
-// decode step reads is a byte the method needs.  K coefficients are rows of
+// where is_k and vs_k are the s_k index bytes and s_k * bits / 8 code bytes
+// of a token rounded up to whole 4-byte words (no rounding for the usual
+// s_k = 4 or 8 with 8-bit, s_k = 8 with 4-bit codes), so a run of tokens of
+// one tier is a few contiguous streams and every byte a decode step reads is
+// a byte the method needs.  K coefficients are rows of
 // a token x channel matrix and V coefficients columns of 16 tokens: both
 // then load directly as operands of 16x16x16 matrix-core products (scores
 // contract over channels, value sums over tokens).  Capacities are rounded
@@ -44,7 +47,7 @@ namespace dwkv {
 constexpr int kMaxTiers = DWKV_MAX_TIERS;
 constexpr int kMaxHeadDim = 128;
 constexpr int kMaxRank = 128;
-constexpr int kMaxResid = 16;
+constexpr int kMaxResid = 8;
 constexpr int kMaxGroupQ = 8;
 constexpr int kMaxSplits = 256;   // decode workgroups per (sequence, KV head)
 
@@ -53,6 +56,8 @@ struct Layout {
     int32_t rank[kMaxTiers];
     int32_t resid[kMaxTiers];
     int32_t vbytes[kMaxTiers];   // packed code bytes per token
+    int32_t istride[kMaxTiers];  // stored index bytes per token (s rounded up to 4)
+    int32_t vstride[kMaxTiers];  // stored code bytes per token (vbytes rounded up to 4)
     int32_t weight[kMaxTiers];   // algorithmic bytes per token (K and V)
     int64_t cap[kMaxTiers];
     int64_t max_tokens;

@@ -51,7 +51,7 @@ def test_tier_table_validation():
     assert _rc_arena(_cfg(tier_rank=(8, 8, 32, 64))) == d.DWKV_ERR_INVALID_ARG      # not ascending
     assert _rc_arena(_cfg(tier_rank=(8, 16, 32, 72))) == d.DWKV_ERR_UNSUPPORTED     # above r_max
     assert _rc_arena(_cfg(tier_rank=(6, 16, 32, 64))) == d.DWKV_ERR_UNSUPPORTED     # not /4
-    assert _rc_arena(_cfg(tier_resid=(8, 8, 8, 17))) == d.DWKV_ERR_UNSUPPORTED
+    assert _rc_arena(_cfg(tier_resid=(8, 8, 8, 9))) == d.DWKV_ERR_UNSUPPORTED
     cfg = _cfg()
     cfg.num_tiers = 9
     assert _rc_arena(cfg) == d.DWKV_ERR_UNSUPPORTED
