@@ -75,6 +75,7 @@ int build_layout(const dwkv_config *c, Layout *ly)
         ly->vstride[k] = vs;
         ly->cap[k] = c->tier_capacity[k];
         ly->weight[k] = 4 * r + (s > 0 ? 2 * (is + vs + 2) : 0);
+        ly->inv_wblk[k] = 1.0 / (16.0 * ly->weight[k]);
         blk = align_up(blk, 256);
         ly->f_coefK[k] = blk; blk = align_up(blk + cap * r * 2, 16);
         ly->f_coefV[k] = blk; blk = align_up(blk + cap * r * 2, 16);

@@ -28,9 +28,13 @@
 //   * probabilities (fp16) times V coefficient columns accumulate the
 //     basis-space value sum on the matrix cores -- the score accumulator's
 //     register layout is exactly the probability operand's;
-//   * the V residual of each 16-token block is written densely (code x
-//     scale) into an LDS tile [channel][token] and multiplied by the same
-//     probabilities on the matrix cores; the written cells are then cleared.
+//   * the V residual of the tile is written densely (code x scale) into a
+//     per-wave LDS tile [channel][token] by the lane that owns the token and
+//     multiplied by the same probabilities on the matrix cores; the written
+//     cells are cleared afterwards.
+// Inner loops have compile-time trip counts and no branches, so that a
+// wave's LDS reads and matrix-core products stream back to back; only the
+// tile's shape (its rank class) and its residual presence are branched on.
 // The running max may trail the true max by up to 8 (a factor 256) before
 // the accumulators are rescaled, so rescaling is rare.  The last workgroup
 // of a (sequence, KV head) to finish merges all partials.
@@ -50,6 +54,10 @@ constexpr int kBlock = 512;               // 8 waves: one workgroup fills a comp
 constexpr int kWaves = kBlock / kWave;
 constexpr int kTile = 64;                 // most tokens in a tile
 constexpr int kSlots = 4;                 // 16x16 operand blocks per tile and Z (rank <= 64)
+constexpr int kEvStride = kTile + 4;      // fp16 per channel row of the V-residual tile (padded:
+                                          // the 16 lanes of an operand read hit distinct banks)
+constexpr int kEvRows = kMaxHeadDim + 1;  // channel rows plus one row that absorbs unused entries
+constexpr int kEvWave = (kEvRows * kEvStride + 7) / 8 * 8;   // fp16 per wave, 16-byte multiple
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kMaxLag = 8.0f;           // log2 units the running max may trail
 
@@ -77,6 +85,8 @@ __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlan
 // are irrelevant next to the >= 1 weight of the running max).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Orders LDS accesses of the lanes of one wave (a wave's LDS operations
+// execute in issue order, so this costs no instruction).
 __device__ __forceinline__ void wave_fence()
 {
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
@@ -87,54 +97,49 @@ __device__ __forceinline__ uint32_t ld32(const uint8_t *p)
     return *reinterpret_cast<const uint32_t *>(p);
 }
 
-// Index byte u (0..7) and code u of a token's residual record.
+// Index byte u (0..7) of a token's residual record.
 __device__ __forceinline__ int idx_at(uint32_t i0, uint32_t i1, int u)
 {
     return ((u < 4 ? i0 : i1) >> (8 * (u & 3))) & 0xFF;
 }
 
-template <int BITS>
-__device__ __forceinline__ float code_at(uint32_t c0, uint32_t c1, int u)
+// Signed code u of a token's record: `bits`-bit fields packed from bit 0 of
+// the 64-bit word (c1:c0).
+__device__ __forceinline__ float code_at(uint32_t c0, uint32_t c1, int u, int bits)
 {
-    if (BITS == 8) return (float)(int)(int8_t)((u < 4 ? c0 : c1) >> (8 * (u & 3)));
-    return (float)(((int)(c0 << (28 - 4 * u))) >> 28);
+    const int pos = u * bits;
+    // the builtin's result is typed unsigned: it must be read back as signed
+    return (float)(int)__builtin_amdgcn_sbfe((int)(pos < 32 ? c0 : c1), pos & 31, bits);
 }
 
 // Rotates a token's s <= 8 entries by `rot` positions.  Entries are stored
 // in ascending channel order; rotating by the lane number keeps the lanes of
 // a wave from visiting the same narrow band of channels at the same step.
-template <int BITS>
 __device__ __forceinline__ void rotate_entries(uint32_t &i0, uint32_t &i1, uint32_t &c0, uint32_t &c1,
-                                               int s, int rot)
+                                               int s, int bits, int rot)
 {
-    if (rot == 0) return;
-    const uint32_t iw = 8u * s, cw = (uint32_t)BITS * s;
+    const uint32_t iw = 8u * s, cw = (uint32_t)bits * s;
     const uint64_t imask = iw == 64 ? ~0ull : ((1ull << iw) - 1);
     const uint64_t cmask = cw == 64 ? ~0ull : ((1ull << cw) - 1);
     const uint64_t i64 = (((uint64_t)i1 << 32) | i0) & imask;
     const uint64_t c64 = (((uint64_t)c1 << 32) | c0) & cmask;
-    const uint32_t ri = 8u * rot, rc = (uint32_t)BITS * rot;
-    const uint64_t ni = ((i64 >> ri) | (i64 << (iw - ri))) & imask;
-    const uint64_t nc = ((c64 >> rc) | (c64 << (cw - rc))) & cmask;
+    const uint32_t ri = 8u * rot, rc = (uint32_t)bits * rot;
+    const uint64_t ni = rot ? ((i64 >> ri) | (i64 << (iw - ri))) & imask : i64;
+    const uint64_t nc = rot ? ((c64 >> rc) | (c64 << (cw - rc))) & cmask : c64;
     i0 = (uint32_t)ni;
     i1 = (uint32_t)(ni >> 32);
     c0 = (uint32_t)nc;
     c1 = (uint32_t)(nc >> 32);
 }
 
-// Copies n fp16 values (n a multiple of 8, source 16-byte aligned) into LDS.
-__device__ __forceinline__ void stage_basis(uint16_t *dst, const uint16_t *src, int n, int tid)
+// floor(x / w) for 0 <= x < 2^52, w > 0, given inv_w ~ 1 / w: the estimate
+// is off by at most one, which one exact integer check corrects.
+__device__ __forceinline__ int64_t div_floor(int64_t x, int64_t w, double inv_w)
 {
-    const uint4 *s4 = reinterpret_cast<const uint4 *>(src);
-    uint4 *d4 = reinterpret_cast<uint4 *>(dst);
-    for (int i = tid; i < n / 8; i += kBlock) d4[i] = s4[i];
-}
-
-// ceil(x / w) for 0 <= x < 2^53, w > 0 (exact: the quotient's distance to an
-// integer is a multiple of 1/w, far above double rounding)
-__device__ __forceinline__ int64_t ceil_div(int64_t x, int64_t w)
-{
-    return x <= 0 ? 0 : (int64_t)ceil((double)x / (double)w);
+    int64_t q = (int64_t)((double)x * inv_w);
+    if (q * w > x) --q;
+    else if ((q + 1) * w <= x) ++q;
+    return q;
 }
 
 // Where a tile lies, uniform over the wave.
@@ -144,7 +149,7 @@ struct Tile {
     int r, s;         // rank and residual channels of the tier
     int kbr;          // 16-channel blocks of the rank (1, 2, 4, 8)
     int nv;           // valid tokens (<= 16 * slots / kbr)
-    int64_t blk0;     // first 16-token block
+    int blk0;         // first 16-token block
 };
 
 // Loads of one tile in flight: coefficient operand slots (slot i is m-block
@@ -153,13 +158,12 @@ template <int NS>
 struct TileData {
     half4_t ka[NS], va[NS];
     uint32_t ki0, ki1, kc0, kc1, vi0, vi1, vc0, vc1;
-    uint16_t ksc, vsc;
+    uint32_t ksc, vsc;          // fp16 scale in the low half
 };
 
 // Per-tier block ranges of this workgroup (uniform values).
 struct Ranges {
-    int T;
-    int64_t b0[kMaxTiers], b1[kMaxTiers];
+    int b0[kMaxTiers], b1[kMaxTiers];
     int cnt[kMaxTiers], nt[kMaxTiers], kbr[kMaxTiers];
 };
 
@@ -175,7 +179,7 @@ __device__ __forceinline__ Tile locate(const Ranges &rg, const Layout &ly, int i
     int rem = it;
 #pragma unroll
     for (int kk = 0; kk < kMaxTiers; ++kk) {
-        if (kk < rg.T && !t.valid) {
+        if (kk < ly.T && !t.valid) {
             if (rem < rg.nt[kk]) {
                 const int kbr = rg.kbr[kk], mbs = NS / kbr;
                 t.valid = 1;
@@ -183,10 +187,10 @@ __device__ __forceinline__ Tile locate(const Ranges &rg, const Layout &ly, int i
                 t.r = ly.rank[kk];
                 t.s = ly.resid[kk];
                 t.kbr = kbr;
-                t.blk0 = rg.b0[kk] + (int64_t)rem * mbs;
-                int nv = (int)(rg.b1[kk] - t.blk0) * 16;
+                t.blk0 = rg.b0[kk] + rem * mbs;
+                int nv = (rg.b1[kk] - t.blk0) * 16;
                 if (nv > 16 * mbs) nv = 16 * mbs;
-                const int left = (int)(rg.cnt[kk] - t.blk0 * 16);
+                const int left = rg.cnt[kk] - t.blk0 * 16;
                 t.nv = nv < left ? nv : left;
             } else {
                 rem -= rg.nt[kk];
@@ -208,7 +212,7 @@ __device__ __forceinline__ void issue_tile(const Tile &t, TileData<NS> &D, const
     const int k = t.k, r = t.r, kbr = t.kbr;
     const uint16_t *cK = reinterpret_cast<const uint16_t *>(blk + ly.f_coefK[k]);
     const uint16_t *cV = reinterpret_cast<const uint16_t *>(blk + ly.f_coefV[k]);
-    const int64_t tok0 = t.blk0 * 16;
+    const int64_t tok0 = (int64_t)t.blk0 * 16;
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
         const int mb = i / kbr, kb = i - mb * kbr;
@@ -217,7 +221,7 @@ __device__ __forceinline__ void issue_tile(const Tile &t, TileData<NS> &D, const
         const int64_t ko = use && tr < t.nv && 16 * kb + 4 * grp < r
                                ? (tok0 + tr) * r + 16 * kb + 4 * grp : 0;
         const int64_t vo = use && 16 * kb + c16 < r
-                               ? ((t.blk0 + mb) * r + 16 * kb + c16) * 16 + 4 * grp : 0;
+                               ? (((int64_t)t.blk0 + mb) * r + 16 * kb + c16) * 16 + 4 * grp : 0;
         D.ka[i] = *reinterpret_cast<const half4_t *>(cK + ko);
         D.va[i] = *reinterpret_cast<const half4_t *>(cV + vo);
     }
@@ -227,37 +231,39 @@ __device__ __forceinline__ void issue_tile(const Tile &t, TileData<NS> &D, const
     const uint8_t *vK = blk + ly.f_valK[k] + tt * ly.vstride[k];
     const uint8_t *iV = blk + ly.f_idxV[k] + tt * ly.istride[k];
     const uint8_t *vV = blk + ly.f_valV[k] + tt * ly.vstride[k];
+    // scales: the aligned 4-byte word holding this token's fp16
+    const int64_t sw = (tt & ~1ll) * 2;
     D.ki0 = ld32(iK);
     D.ki1 = ld32(iK + 4);
     D.kc0 = ld32(vK);
     D.kc1 = ld32(vK + 4);
-    D.ksc = reinterpret_cast<const uint16_t *>(blk + ly.f_scaleK[k])[tt];
+    D.ksc = ld32(blk + ly.f_scaleK[k] + sw) >> (16 * (tt & 1));
     D.vi0 = ld32(iV);
     D.vi1 = ld32(iV + 4);
     D.vc0 = ld32(vV);
     D.vc1 = ld32(vV + 4);
-    D.vsc = reinterpret_cast<const uint16_t *>(blk + ly.f_scaleV[k])[tt];
+    D.vsc = ld32(blk + ly.f_scaleV[k] + sw) >> (16 * (tt & 1));
 }
 
 // Per-wave state of the online softmax and the value sums.
-template <int KB>
+template <int KB, int D>
 struct WaveAcc {
     float4_t O[KB];                      // basis-space value sums [head row][channel]
-    float4_t Ores[kMaxHeadDim / 16];     // residual value mass [head row][channel]
+    float4_t Ores[D / 16];               // residual value mass [head row][channel]
     float m_run;                         // running max of head (lane % 16) % 8
     float l_part;                        // this lane's share of that head's normaliser
 };
 
-template <int GQ, int BITS, int KB, int KBR>
-__device__ __forceinline__ void process_tile(const Tile &t, const TileData<kSlots * (KB / 4)> &D,
-                                             const half4_t (&qb)[KB], WaveAcc<KB> &A,
+template <int GQ, int KB, int D, int KBR>
+__device__ __forceinline__ void process_tile(const Tile &t, const TileData<kSlots * (KB / 4)> &Dt,
+                                             const half4_t (&qb)[KB], WaveAcc<KB, D> &A,
                                              const float (*s_qt)[GQ < 4 ? 4 : GQ], float *sR,
-                                             _Float16 *ev, uint32_t *srec, int d, int lane)
+                                             _Float16 *ev, int bits, int lane)
 {
     constexpr int NS = kSlots * (KB / 4);
     constexpr int MBS = NS / KBR;                   // 16-token blocks in the tile
     constexpr int GP = GQ < 4 ? 4 : GQ;
-    constexpr int ND = kMaxHeadDim / 16;
+    constexpr int ND = D / 16;
     const int c16 = lane & 15, grp = lane >> 4;
     const int r = t.r, s = t.s, nv = t.nv;
 
@@ -266,52 +272,60 @@ __device__ __forceinline__ void process_tile(const Tile &t, const TileData<kSlot
 #pragma unroll
     for (int mb = 0; mb < MBS; ++mb) {
         Sc[mb] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
-        if (16 * mb < nv) {
-            const bool tv = 16 * mb + c16 < nv;
+        const bool tv = 16 * mb + c16 < nv;
 #pragma unroll
-            for (int kb = 0; kb < KBR; ++kb) {
-                half4_t a = D.ka[mb * KBR + kb];
-                if (!(tv && 16 * kb + 4 * grp < r)) a = half4_t{0, 0, 0, 0};
-                Sc[mb] = mma16(a, qb[kb], Sc[mb]);
-            }
+        for (int kb = 0; kb < KBR; ++kb) {
+            half4_t a = Dt.ka[mb * KBR + kb];
+            if (!(tv && 16 * kb + 4 * grp < r)) a = half4_t{0, 0, 0, 0};
+            Sc[mb] = mma16(a, qb[kb], Sc[mb]);
         }
     }
 
-    // ---- K residual: one token per lane, q gathered from LDS
+    // ---- residuals, one token per lane: K logit terms (q gathered from
+    //      LDS) and the V residual's cells of the dense LDS tile
+    const bool tok = lane < nv;
+    int vcell[kMaxResid];
     if (s > 0) {
-        uint32_t i0 = D.ki0, i1 = D.ki1, c0 = D.kc0, c1 = D.kc1;
-        rotate_entries<BITS>(i0, i1, c0, c1, s, lane % s);
+        uint32_t i0 = Dt.ki0, i1 = Dt.ki1, c0 = Dt.kc0, c1 = Dt.kc1;
+        rotate_entries(i0, i1, c0, c1, s, bits, lane % s);
         float rk[GP];
 #pragma unroll
         for (int g = 0; g < GP; ++g) rk[g] = 0.0f;
 #pragma unroll
         for (int u = 0; u < kMaxResid; ++u) {
-            if (u < s) {
-                const int j = idx_at(i0, i1, u);
-                const float cv = code_at<BITS>(c0, c1, u);
-                const float4_t q0 = *reinterpret_cast<const float4_t *>(&s_qt[j][0]);
+            const bool on = u < s;
+            const int j = on ? idx_at(i0, i1, u) : 0;
+            const float cv = on ? code_at(c0, c1, u, bits) : 0.0f;
+            const float4_t q0 = *reinterpret_cast<const float4_t *>(&s_qt[j][0]);
 #pragma unroll
-                for (int g = 0; g < 4; ++g) rk[g] += cv * q0[g];
-                if constexpr (GP == 8) {
-                    const float4_t q1 = *reinterpret_cast<const float4_t *>(&s_qt[j][4]);
+            for (int g = 0; g < 4; ++g) rk[g] += cv * q0[g];
+            if constexpr (GP == 8) {
+                const float4_t q1 = *reinterpret_cast<const float4_t *>(&s_qt[j][4]);
 #pragma unroll
-                    for (int g = 0; g < 4; ++g) rk[4 + g] += cv * q1[g];
-                }
+                for (int g = 0; g < 4; ++g) rk[4 + g] += cv * q1[g];
             }
         }
-        const float sc = lane < nv ? h2f(D.ksc) : 0.0f;
+        const float sck = tok ? h2f((uint16_t)Dt.ksc) : 0.0f;
 #pragma unroll
-        for (int g = 0; g < GQ; ++g) sR[g * kTile + lane] = rk[g] * sc;
+        for (int g = 0; g < GQ; ++g) sR[g * kTile + lane] = rk[g] * sck;
+        const float scv = h2f((uint16_t)Dt.vsc);
+#pragma unroll
+        for (int u = 0; u < kMaxResid; ++u) {
+            const bool on = tok && u < s;
+            vcell[u] = (on ? idx_at(Dt.vi0, Dt.vi1, u) : kMaxHeadDim) * kEvStride + lane;
+            ev[vcell[u]] = (_Float16)(on ? code_at(Dt.vc0, Dt.vc1, u, bits) * scv : 0.0f);
+        }
         wave_fence();
     }
 
     // ---- logits, tile max, lazy rescale, probabilities
     float z[MBS][4];
     float tmax = -INFINITY;
+    const int rrow = (c16 & 7) < GQ ? (c16 & 7) : 0;
 #pragma unroll
     for (int mb = 0; mb < MBS; ++mb) {
         float4_t rr = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
-        if (s > 0) rr = *reinterpret_cast<const float4_t *>(&sR[(c16 & 7) * kTile + 16 * mb + 4 * grp]);
+        if (s > 0) rr = *reinterpret_cast<const float4_t *>(&sR[rrow * kTile + 16 * mb + 4 * grp]);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const float zz = Sc[mb][j] + row_swap8(Sc[mb][j]) + rr[j];
@@ -350,141 +364,114 @@ __device__ __forceinline__ void process_tile(const Tile &t, const TileData<kSlot
     // ---- values: probabilities x V coefficient columns (16-token blocks)
 #pragma unroll
     for (int mb = 0; mb < MBS; ++mb) {
-        if (16 * mb < nv) {
-            const bool partial = 16 * mb + 16 > nv;
 #pragma unroll
-            for (int nb = 0; nb < KBR; ++nb) {
-                half4_t bv = D.va[mb * KBR + nb];
-                if (16 * nb + c16 >= r) bv = half4_t{0, 0, 0, 0};
-                if (partial) {
+        for (int nb = 0; nb < KBR; ++nb) {
+            half4_t bv = Dt.va[mb * KBR + nb];
 #pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        if (16 * mb + 4 * grp + j >= nv) bv[j] = 0;
-                }
-                A.O[nb] = mma16(P[mb], bv, A.O[nb]);
-            }
+            for (int j = 0; j < 4; ++j)
+                if (16 * nb + c16 >= r || 16 * mb + 4 * grp + j >= nv) bv[j] = 0;
+            A.O[nb] = mma16(P[mb], bv, A.O[nb]);
         }
     }
 
-    // ---- V residual mass: per 16-token block, a dense LDS tile of
-    //      code x scale [channel][token] times the probabilities; four lanes
-    //      per token (records handed over through LDS), lane taking entries
-    //      rot and rot + 4 of its token; the written cells are cleared after.
+    // ---- V residual mass: the dense tile times the probabilities, then the
+    //      written cells are cleared (after the reads: same wave, in order)
     if (s > 0) {
-        uint32_t *rec = srec + lane * 5;
-        rec[0] = D.vi0;
-        rec[1] = D.vi1;
-        rec[2] = D.vc0;
-        rec[3] = D.vc1;
-        rec[4] = lane < nv ? D.vsc : 0u;
-        wave_fence();
-        const int rot = lane & 3, tcol = lane >> 2;
 #pragma unroll
         for (int mb = 0; mb < MBS; ++mb) {
-            if (16 * mb < nv) {
-                const uint32_t *rr = srec + (16 * mb + tcol) * 5;
-                const uint32_t i0 = rr[0], i1 = rr[1], c0 = rr[2], c1 = rr[3];
-                const float sc = h2f((uint16_t)rr[4]);
-                const bool tv = 16 * mb + tcol < nv;
-                // entry rot lands in the low byte (nibble) of the first word,
-                // entry rot + 4 in that of the second
-                const uint32_t i0s = __builtin_amdgcn_alignbit(i1, i0, 8u * rot);
-                const uint32_t i1s = rot ? (i1 >> (8u * rot)) : i1;
-                uint32_t c0s, c1s;
-                if (BITS == 8) {
-                    c0s = __builtin_amdgcn_alignbit(c1, c0, 8u * rot);
-                    c1s = rot ? (c1 >> (8u * rot)) : c1;
-                } else {
-                    c0s = c0 >> (4u * rot);
-                    c1s = c0s >> 16;
-                }
-                int js[2];
 #pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    js[e] = -1;
-                    if (tv && 4 * e + rot < s) {
-                        const uint32_t iw = e == 0 ? i0s : i1s;
-                        const uint32_t cw = e == 0 ? c0s : c1s;
-                        js[e] = (int)(iw & 0xFF);
-                        const float code = BITS == 8 ? (float)(int)(int8_t)(cw & 0xFF)
-                                                     : (float)(((int)(cw << 28)) >> 28);
-                        ev[js[e] * 16 + tcol] = (_Float16)(code * sc);
-                    }
-                }
-                wave_fence();
-#pragma unroll
-                for (int nb = 0; nb < ND; ++nb) {
-                    if (16 * nb < d) {
-                        const half4_t bv = *reinterpret_cast<const half4_t *>(&ev[(16 * nb + c16) * 16 + 4 * grp]);
-                        A.Ores[nb] = mma16(P[mb], bv, A.Ores[nb]);
-                    }
-                }
-                wave_fence();
-#pragma unroll
-                for (int e = 0; e < 2; ++e)
-                    if (js[e] >= 0) ev[js[e] * 16 + tcol] = (_Float16)0.0f;
-                wave_fence();
+            for (int nb = 0; nb < ND; ++nb) {
+                const half4_t bv =
+                    *reinterpret_cast<const half4_t *>(&ev[(16 * nb + c16) * kEvStride + 16 * mb + 4 * grp]);
+                A.Ores[nb] = mma16(P[mb], bv, A.Ores[nb]);
             }
         }
+        wave_fence();
+#pragma unroll
+        for (int u = 0; u < kMaxResid; ++u) ev[vcell[u]] = (_Float16)0.0f;
     }
 }
 
-template <int GQ, int BITS, int KB>
-__device__ __forceinline__ void process_any(const Tile &t, const TileData<kSlots * (KB / 4)> &D,
-                                            const half4_t (&qb)[KB], WaveAcc<KB> &A,
+template <int GQ, int KB, int D>
+__device__ __forceinline__ void process_any(const Tile &t, const TileData<kSlots * (KB / 4)> &Dt,
+                                            const half4_t (&qb)[KB], WaveAcc<KB, D> &A,
                                             const float (*s_qt)[GQ < 4 ? 4 : GQ], float *sR,
-                                            _Float16 *ev, uint32_t *srec, int d, int lane)
+                                            _Float16 *ev, int bits, int lane)
 {
     switch (t.kbr) {
-    case 1: process_tile<GQ, BITS, KB, 1>(t, D, qb, A, s_qt, sR, ev, srec, d, lane); break;
-    case 2: process_tile<GQ, BITS, KB, 2>(t, D, qb, A, s_qt, sR, ev, srec, d, lane); break;
-    case 4: process_tile<GQ, BITS, KB, 4>(t, D, qb, A, s_qt, sR, ev, srec, d, lane); break;
+    case 1: process_tile<GQ, KB, D, 1>(t, Dt, qb, A, s_qt, sR, ev, bits, lane); break;
+    case 2: process_tile<GQ, KB, D, 2>(t, Dt, qb, A, s_qt, sR, ev, bits, lane); break;
+    case 4: process_tile<GQ, KB, D, 4>(t, Dt, qb, A, s_qt, sR, ev, bits, lane); break;
     default:
-        if constexpr (KB == 8) process_tile<GQ, BITS, KB, 8>(t, D, qb, A, s_qt, sR, ev, srec, d, lane);
+        if constexpr (KB == 8) process_tile<GQ, KB, D, 8>(t, Dt, qb, A, s_qt, sR, ev, bits, lane);
         break;
     }
 }
 
-template <int GQ, int BITS, int KB>
+template <int GQ, int KB, int D>
 __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *arena, int layer,
                                                            const uint16_t *q, float *out,
-                                                           DecodeWorkspace ws, int S, float qscale)
+                                                           DecodeWorkspace ws, int S, double invS,
+                                                           float qscale)
 {
     constexpr int GP = GQ < 4 ? 4 : GQ;           // query heads padded for 16-byte gathers
     constexpr int NS = kSlots * (KB / 4);          // operand slots per tile and Z
-    constexpr int ND = kMaxHeadDim / 16;           // channel blocks of the residual mass
+    constexpr int ND = D / 16;                     // channel blocks of the head
+    constexpr int RMAX = 16 * KB;                  // largest rank this instance handles
     const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
+    const int tid = threadIdx.x, wave = uni(tid / kWave), lane = lane_id();
     const int c16 = lane & 15, grp = lane >> 4;
-    const int d = ly.d, R = ly.R;
+    const int R = ly.R, bits = ly.bits;
     const int g0 = h * GQ;
 
-    __shared__ __attribute__((aligned(16))) float s_qt[kMaxHeadDim][GP];        // q, base-2 units
-    __shared__ float s_qp[GQ][kMaxRank];                                        // merged basis sums
-    __shared__ float s_res[GQ][kMaxHeadDim];                                    // merged residual mass
-    __shared__ __attribute__((aligned(16))) float s_rk[kWaves][8][kTile];       // K-residual logits
-    __shared__ __attribute__((aligned(16))) _Float16 s_ev[kWaves][kMaxHeadDim][16];   // V residual block
-    __shared__ uint32_t s_rec[kWaves][kTile * 5];                               // V residual records
-    __shared__ float s_m[kWaves][GQ], s_l[kWaves][GQ], s_f[kWaves][GQ];
+    __shared__ __attribute__((aligned(16))) _Float16 s_ev[kWaves * kEvWave];   // V-residual tiles
+    __shared__ __attribute__((aligned(16))) float s_qt[D][GP];                 // q, base-2 units
+    __shared__ __attribute__((aligned(16))) float s_rk[kWaves][GQ][kTile];     // K-residual logits
+    __shared__ float s_m[kWaves][GQ], s_l[kWaves][GQ];
     __shared__ float s_M[GQ], s_L[GQ];
-    __shared__ __attribute__((aligned(16))) uint16_t s_bas[kMaxRank * kMaxHeadDim];   // B_V
     __shared__ int s_last;
 
+    // ---- loads that depend on nothing go out first: the query (operand
+    //      layout), the basis rows for q' = B_K q, this wave's B_V operand
+    const uint16_t *BK = basis_ptr(ly, arena, layer / ly.G, 0, h);
+    const uint16_t *BV = basis_ptr(ly, arena, layer / ly.G, 1, h);
+    const int gq = c16 & 7;
+    const uint16_t *qrow = q + ((int64_t)b * ly.Hq + g0 + (gq < GQ ? gq : 0)) * D;
+    half4_t bq[ND];
+#pragma unroll
+    for (int kb = 0; kb < ND; ++kb) bq[kb] = *reinterpret_cast<const half4_t *>(qrow + 16 * kb + 4 * grp);
+    half4_t ak[KB][ND];
+#pragma unroll
+    for (int mb = 0; mb < KB; ++mb) {
+        const int row = 16 * mb + c16 < R ? 16 * mb + c16 : R - 1;
+#pragma unroll
+        for (int kb = 0; kb < ND; ++kb)
+            ak[mb][kb] = *reinterpret_cast<const half4_t *>(BK + (int64_t)row * D + 16 * kb + 4 * grp);
+    }
+    uint16_t bvr[RMAX / 4];
+    {
+        const int col = 16 * (wave < ND ? wave : 0) + c16;
+#pragma unroll
+        for (int kb = 0; kb < RMAX / 4; ++kb) {
+            const int row = 4 * kb + grp < R ? 4 * kb + grp : R - 1;
+            bvr[kb] = BV[(int64_t)row * D + col];
+        }
+    }
+
     // ---- this workgroup's byte-balanced run of 16-token blocks, per tier
-    //      (computed by every wave from scalar loads: no barrier needed)
+    //      (every wave computes it from scalar loads: no barrier needed)
     const uint8_t *blk = head_block_ptr(ly, arena, layer, b, h);
     Ranges rg;
     {
         const int32_t *cnt = counts_ptr(ly, arena, layer, b, h);
-        rg.T = ly.T;
         int64_t W = 0;
 #pragma unroll
         for (int k = 0; k < kMaxTiers; ++k) {
             rg.cnt[k] = k < ly.T ? uni(cnt[k]) : 0;
             W += (int64_t)((rg.cnt[k] + 15) >> 4) * 16 * (k < ly.T ? ly.weight[k] : 0);
         }
-        const int64_t lo = (int64_t)floor((double)W * split / S);
-        const int64_t hi = (int64_t)floor((double)W * (split + 1) / S);
+        const int64_t lo = div_floor(W * split, S, invS);
+        const int64_t hi = div_floor(W * (split + 1), S, invS);
         int64_t wk = 0;
 #pragma unroll
         for (int k = 0; k < kMaxTiers; ++k) {
@@ -493,35 +480,40 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
             rg.kbr[k] = 1;
             if (k < ly.T) {
                 const int64_t nb = (rg.cnt[k] + 15) >> 4, wb = 16 * (int64_t)ly.weight[k];
-                int64_t b0 = ceil_div(lo - wk, wb), b1 = ceil_div(hi - wk, wb);
+                const int64_t x0 = lo - wk, x1 = hi - wk;
+                int64_t b0 = x0 <= 0 ? 0 : div_floor(x0 + wb - 1, wb, ly.inv_wblk[k]);
+                int64_t b1 = x1 <= 0 ? 0 : div_floor(x1 + wb - 1, wb, ly.inv_wblk[k]);
                 b0 = b0 < nb ? b0 : nb;
                 b1 = b1 < nb ? b1 : nb;
                 wk += nb * wb;
                 const int r = ly.rank[k];
                 const int kbr = r <= 16 ? 1 : r <= 32 ? 2 : r <= 64 ? 4 : 8;
                 const int mbs = NS / kbr;
-                rg.b0[k] = b0;
-                rg.b1[k] = b1;
+                rg.b0[k] = uni((int)b0);
+                rg.b1[k] = uni((int)b1);
                 rg.kbr[k] = kbr;
-                rg.nt[k] = (int)((b1 - b0 + mbs - 1) / mbs);
+                rg.nt[k] = uni((int)((b1 - b0 + mbs - 1) / mbs));
             }
         }
     }
 
-    // ---- first tile's loads go out before anything else
+    // ---- first tile's loads
     TileData<NS> DA, DB;
     int it = wave;
     Tile ta = locate<NS>(rg, ly, it);
     issue_tile<NS>(ta, DA, blk, ly, lane);
 
-    // ---- query in base-2 logit units (LDS, for residual gathers), B_V staged
-    for (int i = tid; i < kMaxHeadDim * GP; i += kBlock) {
+    // ---- query in base-2 logit units (LDS, for residual gathers); this
+    //      wave's V-residual tile cleared
+    for (int i = tid; i < D * GP; i += kBlock) {
         const int j = i / GP, g = i % GP;
-        s_qt[j][g] = (g < GQ && j < d) ? qscale * h2f(q[((int64_t)b * ly.Hq + g0 + g) * d + j]) : 0.0f;
+        s_qt[j][g] = g < GQ ? qscale * h2f(q[((int64_t)b * ly.Hq + g0 + g) * D + j]) : 0.0f;
     }
-    for (int i = tid; i < kWaves * 8 * kTile; i += kBlock) (&s_rk[0][0][0])[i] = 0.0f;
-    for (int i = tid; i < kWaves * kMaxHeadDim * 16; i += kBlock) (&s_ev[0][0][0])[i] = (_Float16)0.0f;
-    stage_basis(s_bas, basis_ptr(ly, arena, layer / ly.G, 1, h), R * d, tid);
+    _Float16 *ev = s_ev + wave * kEvWave;
+    {
+        uint4 *e4 = reinterpret_cast<uint4 *>(ev);
+        for (int i = lane; i < kEvWave / 8; i += kWave) e4[i] = uint4{0u, 0u, 0u, 0u};
+    }
 
     // ---- score operand qb: q' = B_K q on the matrix cores, straight into
     //      operand layout.  Column c16 carries query head c16 % 8 -- as
@@ -529,45 +521,26 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
     //      above -- so that the fp16 products reproduce q' to ~2^-22.
     //      Products of fp16 inputs are exact and sums fp32: q' is fp32-accurate.
     half4_t qb[KB];
-    {
-        const uint16_t *BK = basis_ptr(ly, arena, layer / ly.G, 0, h);
-        const int gq = c16 & 7;
-        const uint16_t *qrow = q + ((int64_t)b * ly.Hq + g0 + (gq < GQ ? gq : 0)) * d;
-        half4_t bq[kMaxHeadDim / 16];
 #pragma unroll
-        for (int kb = 0; kb < kMaxHeadDim / 16; ++kb)
-            bq[kb] = (gq < GQ && 16 * kb < d) ? *reinterpret_cast<const half4_t *>(qrow + 16 * kb + 4 * grp)
-                                              : half4_t{0, 0, 0, 0};
+    for (int mb = 0; mb < KB; ++mb) {
+        float4_t acc = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int mb = 0; mb < KB; ++mb) {
-            float4_t acc = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
-            if (16 * mb < R) {
-                const uint16_t *brow = BK + (int64_t)(16 * mb + c16 < R ? 16 * mb + c16 : 0) * d;
-                half4_t a[kMaxHeadDim / 16];
+        for (int kb = 0; kb < ND; ++kb) {
+            const half4_t bb = gq < GQ ? bq[kb] : half4_t{0, 0, 0, 0};
+            acc = mma16(ak[mb][kb], bb, acc);
+        }
 #pragma unroll
-                for (int kb = 0; kb < kMaxHeadDim / 16; ++kb)
-                    a[kb] = 16 * kb < d ? *reinterpret_cast<const half4_t *>(brow + 16 * kb + 4 * grp)
-                                        : half4_t{0, 0, 0, 0};
-#pragma unroll
-                for (int kb = 0; kb < kMaxHeadDim / 16; ++kb) {
-                    half4_t aa = a[kb];
-                    if (16 * mb + c16 >= R) aa = half4_t{0, 0, 0, 0};
-                    acc = mma16(aa, bq[kb], acc);
-                }
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float v = qscale * acc[j];
-                const _Float16 hi = (_Float16)v;
-                const _Float16 lo = (_Float16)(v - (float)hi);
-                qb[mb][j] = (c16 < 8) ? hi : lo;
-            }
+        for (int j = 0; j < 4; ++j) {
+            const float v = 16 * mb + 4 * grp + j < R ? qscale * acc[j] : 0.0f;
+            const _Float16 hi = (_Float16)v;
+            const _Float16 lo = (_Float16)(v - (float)hi);
+            qb[mb][j] = (c16 < 8) ? hi : lo;
         }
     }
     __syncthreads();
 
     // ---- main loop: two-deep pipeline over this wave's tiles
-    WaveAcc<KB> A;
+    WaveAcc<KB, D> A;
 #pragma unroll
     for (int nb = 0; nb < KB; ++nb) A.O[nb] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -575,21 +548,20 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
     A.m_run = -INFINITY;
     A.l_part = 0.0f;
     float *sR = &s_rk[wave][0][0];
-    _Float16 *ev = &s_ev[wave][0][0];
-    uint32_t *srec = &s_rec[wave][0];
     while (ta.valid) {
         it += kWaves;
         Tile tb = locate<NS>(rg, ly, it);
         issue_tile<NS>(tb, DB, blk, ly, lane);
-        process_any<GQ, BITS, KB>(ta, DA, qb, A, s_qt, sR, ev, srec, d, lane);
+        process_any<GQ, KB, D>(ta, DA, qb, A, s_qt, sR, ev, bits, lane);
         if (!tb.valid) break;
         it += kWaves;
         ta = locate<NS>(rg, ly, it);
         issue_tile<NS>(ta, DA, blk, ly, lane);
-        process_any<GQ, BITS, KB>(tb, DB, qb, A, s_qt, sR, ev, srec, d, lane);
+        process_any<GQ, KB, D>(tb, DB, qb, A, s_qt, sR, ev, bits, lane);
     }
 
-    // ---- merge the waves of this workgroup
+    // ---- merge the waves of this workgroup: each wave leaves its unscaled
+    //      sums in its own (now idle) V-residual tile, then one barrier
     float l_part = A.l_part;
     l_part += __shfl_xor(l_part, 16, kWave);
     l_part += __shfl_xor(l_part, 32, kWave);
@@ -597,57 +569,63 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
         s_m[wave][lane] = A.m_run;
         s_l[wave][lane] = l_part;
     }
+    {
+        float *part = reinterpret_cast<float *>(ev);            // [GQ][RMAX + D]
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int row = 4 * grp + j;
+            if (row < GQ) {
+#pragma unroll
+                for (int nb = 0; nb < KB; ++nb) part[row * (RMAX + D) + 16 * nb + c16] = A.O[nb][j];
+#pragma unroll
+                for (int nb = 0; nb < ND; ++nb) part[row * (RMAX + D) + RMAX + 16 * nb + c16] = A.Ores[nb][j];
+            }
+        }
+    }
     __syncthreads();
+    // weights 2^(m_w - M) in a fixed wave order (bitwise reproducible);
+    // merged sums go to the K-residual area, idle now
+    float *s_qp = &s_rk[0][0][0];                                // [GQ][RMAX + D]
+    for (int i = tid; i < GQ * (RMAX + D); i += kBlock) {
+        const int g = i / (RMAX + D);
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w][g]);
+        float acc = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const float f = M == -INFINITY ? 0.0f : exp2f(s_m[w][g] - M);
+            acc += f * reinterpret_cast<const float *>(s_ev + w * kEvWave)[i];
+        }
+        s_qp[i] = acc;
+    }
     if (tid < GQ) {
         const int g = tid;
         float M = -INFINITY;
         for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w][g]);
         float L = 0.0f;
-        for (int w = 0; w < kWaves; ++w) {
-            const float f = M == -INFINITY ? 0.0f : exp2f(s_m[w][g] - M);
-            s_f[w][g] = f;
-            L += f * s_l[w][g];
-        }
+        for (int w = 0; w < kWaves; ++w) L += (M == -INFINITY ? 0.0f : exp2f(s_m[w][g] - M)) * s_l[w][g];
         s_M[g] = M;
         s_L[g] = L;
     }
-    for (int i = tid; i < GQ * kMaxRank; i += kBlock) (&s_qp[0][0])[i] = 0.0f;
-    for (int i = tid; i < GQ * kMaxHeadDim; i += kBlock) (&s_res[0][0])[i] = 0.0f;
     __syncthreads();
-    // waves add their rescaled sums in a fixed order (bitwise reproducible)
-    for (int w = 0; w < kWaves; ++w) {
-        if (wave == w) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int row = 4 * grp + j;
-                if (row < GQ) {
-                    const float f = s_f[wave][row];
-#pragma unroll
-                    for (int nb = 0; nb < KB; ++nb)
-                        if (16 * nb < R) s_qp[row][16 * nb + c16] += f * A.O[nb][j];
-#pragma unroll
-                    for (int nb = 0; nb < ND; ++nb)
-                        if (16 * nb < d) s_res[row][16 * nb + c16] += f * A.Ores[nb][j];
-                }
-            }
-        }
-        __syncthreads();
-    }
     // one back-projection through B_V plus the residual mass, on the matrix
     // cores in fp32: wave w forms output channels 16w..16w+15 as
     // out^T[j][g] = res[g][j] + sum_i B_V[i][j] a[g][i]
-    if (16 * wave < d) {
+    if (wave < ND) {
         float4_t acc;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[j] = c16 < GQ ? s_res[c16][16 * wave + 4 * grp + j] : 0.0f;
-        for (int kb = 0; kb < R / 4; ++kb) {
+        for (int j = 0; j < 4; ++j)
+            acc[j] = c16 < GQ ? s_qp[c16 * (RMAX + D) + RMAX + 16 * wave + 4 * grp + j] : 0.0f;
+#pragma unroll
+        for (int kb = 0; kb < RMAX / 4; ++kb) {
             const int i = 4 * kb + grp;
-            const float a = h2f(s_bas[i * d + 16 * wave + c16]);
-            const float bb = c16 < GQ ? s_qp[c16][i] : 0.0f;
+            const float a = i < R ? h2f(bvr[kb]) : 0.0f;
+            const float bb = c16 < GQ && i < R ? s_qp[c16 * (RMAX + D) + i] : 0.0f;
             acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bb, acc, 0, 0, 0);
         }
         if (c16 < GQ) {
-            float *po = ws.po + (((int64_t)b * ly.Hq + g0 + c16) * S + split) * d + 16 * wave + 4 * grp;
+            float *po = ws.po + (((int64_t)b * ly.Hq + g0 + c16) * S + split) * D + 16 * wave + 4 * grp;
 #pragma unroll
             for (int j = 0; j < 4; ++j) __hip_atomic_store(po + j, acc[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
@@ -659,7 +637,7 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
                            __HIP_MEMORY_SCOPE_AGENT);
     }
 
-    // ---- a3: the last workgroup of this (sequence, KV head) merges the splits.
+    // ---- the last workgroup of this (sequence, KV head) merges the splits.
     // Partials travel as agent-scope (cross-XCD coherent) relaxed stores and
     // loads; every store has completed (vmcnt 0) before the workgroup's
     // arrival is counted, so no cache-wide write-back or invalidate is needed.
@@ -672,10 +650,10 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
     }
     __syncthreads();
     if (!s_last) return;
-    // weights 2^(m_s - M) of every split, through LDS (reusing the basis
-    // buffer: [GQ][S] weights, [GQ][S] normalisers, then the reduction area)
-    static_assert(kMaxSplits * 2 * 8 * 4 + kBlock * 16 <= kMaxRank * kMaxHeadDim * 2, "merge scratch");
-    float *s_w = reinterpret_cast<float *>(s_bas);
+    // weights 2^(m_s - M) of every split, through LDS (the V-residual tiles:
+    // [GQ][S] weights, [GQ][S] normalisers, then the reduction area)
+    static_assert((2 * kMaxSplits * 8 + kBlock * 4) * 4 <= kWaves * kEvWave * 2, "merge scratch");
+    float *s_w = reinterpret_cast<float *>(s_ev);
     float *s_pl = s_w + GQ * S;
     for (int i = tid; i < GQ * S; i += kBlock) {
         const int g = i / S, sp = i % S;
@@ -703,51 +681,62 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
     }
     // each thread: 4 adjacent outputs of one head over an interleaved subset
     // of the splits, many independent loads in flight
-    const int quads = GQ * d / 4;
-    const int parts = kBlock / quads;
+    constexpr int quads = GQ * D / 4;
+    constexpr int parts = kBlock / quads;
     float4_t accm = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
     const int qd = tid % quads, part = tid / quads;
-    const int gq = (4 * qd) / d, j4 = (4 * qd) % d;
+    const int hq = (4 * qd) / D, j4 = (4 * qd) % D;
     if (part < parts) {
-        const float *po = ws.po + ((int64_t)b * ly.Hq + g0 + gq) * S * d + j4;
+        const float *po = ws.po + ((int64_t)b * ly.Hq + g0 + hq) * S * D + j4;
 #pragma unroll 8
         for (int sp = part; sp < S; sp += parts) {
             float4_t v;
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                v[j] = __hip_atomic_load(po + (int64_t)sp * d + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            accm += s_w[gq * S + sp] * v;
+                v[j] = __hip_atomic_load(po + (int64_t)sp * D + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            accm += s_w[hq * S + sp] * v;
         }
     }
     __syncthreads();
-    float4_t *s_red = reinterpret_cast<float4_t *>(s_bas) + kMaxSplits * 2 * 8 / 4;   // [parts][quads]
+    float4_t *s_red = reinterpret_cast<float4_t *>(s_ev) + kMaxSplits * 2 * 8 / 4;   // [parts][quads]
     if (part < parts) s_red[part * quads + qd] = accm;
     __syncthreads();
     if (tid < quads) {
         float4_t o = s_red[tid];
         for (int p2 = 1; p2 < parts; ++p2) o += s_red[p2 * quads + tid];
-        const float L = s_L[gq];
+        const float L = s_L[hq];
         const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-        *reinterpret_cast<float4_t *>(out + ((int64_t)b * ly.Hq + g0 + gq) * d + j4) = o * inv;
+        *reinterpret_cast<float4_t *>(out + ((int64_t)b * ly.Hq + g0 + hq) * D + j4) = o * inv;
     }
     if (tid == 0) __hip_atomic_store(&ws.arrive[b * ly.Hkv + h], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int GQ>
+template <int GQ, int D>
 hipError_t launch_gq(const Layout &ly, uint8_t *arena, int layer, const uint16_t *q, int batch,
                      float qs, float *out, const DecodeWorkspace &ws, int splits, hipStream_t stream)
 {
     const dim3 grid(splits, ly.Hkv, batch);
-#define DWKV_LAUNCH(BITS, KB)                                                                      \
-    hipLaunchKernelGGL((decode_kernel<GQ, BITS, KB>), grid, dim3(kBlock), 0, stream, ly, arena,   \
-                       layer, q, out, ws, splits, qs)
-    if (ly.R <= 64) {
-        if (ly.bits == 4) DWKV_LAUNCH(4, 4); else DWKV_LAUNCH(8, 4);
-    } else {
-        if (ly.bits == 4) DWKV_LAUNCH(4, 8); else DWKV_LAUNCH(8, 8);
-    }
-#undef DWKV_LAUNCH
+    const double inv = 1.0 / splits;
+    if (ly.R <= 64)
+        hipLaunchKernelGGL((decode_kernel<GQ, 4, D>), grid, dim3(kBlock), 0, stream, ly, arena, layer, q, out,
+                           ws, splits, inv, qs);
+    else
+        hipLaunchKernelGGL((decode_kernel<GQ, 8, D>), grid, dim3(kBlock), 0, stream, ly, arena, layer, q, out,
+                           ws, splits, inv, qs);
     return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const Layout &ly, uint8_t *arena, int layer, const uint16_t *q, int batch,
+                    float qs, float *out, const DecodeWorkspace &ws, int splits, hipStream_t stream)
+{
+    switch (ly.gq) {
+    case 1: return launch_gq<1, D>(ly, arena, layer, q, batch, qs, out, ws, splits, stream);
+    case 2: return launch_gq<2, D>(ly, arena, layer, q, batch, qs, out, ws, splits, stream);
+    case 4: return launch_gq<4, D>(ly, arena, layer, q, batch, qs, out, ws, splits, stream);
+    case 8: return launch_gq<8, D>(ly, arena, layer, q, batch, qs, out, ws, splits, stream);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace
@@ -759,13 +748,9 @@ hipError_t launch_decode(const Layout &ly, uint8_t *arena, int layer, const void
     const float qs = softmax_scale * kLog2e;
     const uint16_t *qq = static_cast<const uint16_t *>(q);
     (void)hipGetLastError();  // drop errors left by earlier, unrelated calls
-    switch (ly.gq) {
-    case 1: return launch_gq<1>(ly, arena, layer, qq, batch, qs, out, ws, splits, stream);
-    case 2: return launch_gq<2>(ly, arena, layer, qq, batch, qs, out, ws, splits, stream);
-    case 4: return launch_gq<4>(ly, arena, layer, qq, batch, qs, out, ws, splits, stream);
-    case 8: return launch_gq<8>(ly, arena, layer, qq, batch, qs, out, ws, splits, stream);
-    default: return hipErrorInvalidValue;
-    }
+    if (ly.d == 64) return launch_d<64>(ly, arena, layer, qq, batch, qs, out, ws, splits, stream);
+    if (ly.d == 128) return launch_d<128>(ly, arena, layer, qq, batch, qs, out, ws, splits, stream);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace dwkv
