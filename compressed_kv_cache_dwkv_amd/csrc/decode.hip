@@ -418,6 +418,7 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
     constexpr int NS = kSlots * (KB / 4);          // operand slots per tile and Z
     constexpr int ND = D / 16;                     // channel blocks of the head
     constexpr int RMAX = 16 * KB;                  // largest rank this instance handles
+    static_assert(KB <= kWaves, "one wave per block of q'");
     const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, wave = uni(tid / kWave), lane = lane_id();
     const int c16 = lane & 15, grp = lane >> 4;
@@ -426,74 +427,67 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
 
     __shared__ __attribute__((aligned(16))) _Float16 s_ev[kWaves * kEvWave];   // V-residual tiles
     __shared__ __attribute__((aligned(16))) float s_qt[D][GP];                 // q, base-2 units
-    __shared__ __attribute__((aligned(16))) float s_rk[kWaves][GQ][kTile];     // K-residual logits
+    constexpr int RK = GQ < 2 ? 2 : GQ;            // rows of the K-residual area (>= 4 KiB)
+    __shared__ __attribute__((aligned(16))) float s_rk[kWaves][RK][kTile];     // K-residual logits
     __shared__ float s_m[kWaves][GQ], s_l[kWaves][GQ];
     __shared__ float s_M[GQ], s_L[GQ];
     __shared__ int s_last;
+    static_assert(KB * kWave * 8 <= sizeof(s_rk) && GQ * (RMAX + D) * 4 <= sizeof(s_rk), "K-residual area reuse");
 
-    // ---- loads that depend on nothing go out first: the query (operand
-    //      layout), the basis rows for q' = B_K q, this wave's B_V operand
-    const uint16_t *BK = basis_ptr(ly, arena, layer / ly.G, 0, h);
-    const uint16_t *BV = basis_ptr(ly, arena, layer / ly.G, 1, h);
+    // ---- token counts first (one lane per tier), then the query in
+    //      operand layout and, for waves 0..KB-1, one 16-row block of B_K
+    const int T = ly.T;
+    const int kl = lane < T ? lane : 0;
+    const int cnt_l = lane < T ? counts_ptr(ly, arena, layer, b, h)[kl] : 0;
     const int gq = c16 & 7;
     const uint16_t *qrow = q + ((int64_t)b * ly.Hq + g0 + (gq < GQ ? gq : 0)) * D;
-    half4_t bq[ND];
+    half4_t bq[ND], ak[ND];
 #pragma unroll
     for (int kb = 0; kb < ND; ++kb) bq[kb] = *reinterpret_cast<const half4_t *>(qrow + 16 * kb + 4 * grp);
-    half4_t ak[KB][ND];
-#pragma unroll
-    for (int mb = 0; mb < KB; ++mb) {
-        const int row = 16 * mb + c16 < R ? 16 * mb + c16 : R - 1;
+    if (wave < KB) {
+        const uint16_t *BK = basis_ptr(ly, arena, layer / ly.G, 0, h);
+        const int row = 16 * wave + c16 < R ? 16 * wave + c16 : R - 1;
 #pragma unroll
         for (int kb = 0; kb < ND; ++kb)
-            ak[mb][kb] = *reinterpret_cast<const half4_t *>(BK + (int64_t)row * D + 16 * kb + 4 * grp);
-    }
-    uint16_t bvr[RMAX / 4];
-    {
-        const int col = 16 * (wave < ND ? wave : 0) + c16;
-#pragma unroll
-        for (int kb = 0; kb < RMAX / 4; ++kb) {
-            const int row = 4 * kb + grp < R ? 4 * kb + grp : R - 1;
-            bvr[kb] = BV[(int64_t)row * D + col];
-        }
+            ak[kb] = *reinterpret_cast<const half4_t *>(BK + (int64_t)row * D + 16 * kb + 4 * grp);
     }
 
-    // ---- this workgroup's byte-balanced run of 16-token blocks, per tier
-    //      (every wave computes it from scalar loads: no barrier needed)
+    // ---- this workgroup's byte-balanced run of 16-token blocks: lane k
+    //      works out tier k's range, then every value is read into scalars
     const uint8_t *blk = head_block_ptr(ly, arena, layer, b, h);
     Ranges rg;
     {
-        const int32_t *cnt = counts_ptr(ly, arena, layer, b, h);
-        int64_t W = 0;
+        const bool on = lane < T;
+        const int r_l = ly.rank[kl];
+        const int64_t wb_l = 16 * (int64_t)ly.weight[kl];
+        const int64_t nb_l = on ? (cnt_l + 15) >> 4 : 0;
+        const int64_t wt_l = nb_l * wb_l;                     // bytes of tier k's blocks
+        int64_t W = 0, wk_l = 0;                               // total; bytes of tiers before k
 #pragma unroll
         for (int k = 0; k < kMaxTiers; ++k) {
-            rg.cnt[k] = k < ly.T ? uni(cnt[k]) : 0;
-            W += (int64_t)((rg.cnt[k] + 15) >> 4) * 16 * (k < ly.T ? ly.weight[k] : 0);
+            const uint32_t lo32 = __builtin_amdgcn_readlane((uint32_t)wt_l, k);
+            const uint32_t hi32 = __builtin_amdgcn_readlane((uint32_t)(wt_l >> 32), k);
+            const int64_t wt = (int64_t)(((uint64_t)hi32 << 32) | lo32);
+            if (lane > k) wk_l += wt;
+            W += wt;
         }
         const int64_t lo = div_floor(W * split, S, invS);
         const int64_t hi = div_floor(W * (split + 1), S, invS);
-        int64_t wk = 0;
+        const int64_t x0 = lo - wk_l, x1 = hi - wk_l;
+        int64_t b0 = x0 <= 0 || !on ? 0 : div_floor(x0 + wb_l - 1, wb_l, ly.inv_wblk[kl]);
+        int64_t b1 = x1 <= 0 || !on ? 0 : div_floor(x1 + wb_l - 1, wb_l, ly.inv_wblk[kl]);
+        b0 = b0 < nb_l ? b0 : nb_l;
+        b1 = b1 < nb_l ? b1 : nb_l;
+        const int lkbr = (r_l > 16) + (r_l > 32) + (r_l > 64);     // log2 of 16-channel blocks
+        const int lmbs = (NS == 8 ? 3 : 2) - lkbr;                 // log2 of 16-token blocks per tile
+        const int nt_l = (int)((b1 - b0 + (1 << lmbs) - 1) >> lmbs);
 #pragma unroll
         for (int k = 0; k < kMaxTiers; ++k) {
-            rg.b0[k] = rg.b1[k] = 0;
-            rg.nt[k] = 0;
-            rg.kbr[k] = 1;
-            if (k < ly.T) {
-                const int64_t nb = (rg.cnt[k] + 15) >> 4, wb = 16 * (int64_t)ly.weight[k];
-                const int64_t x0 = lo - wk, x1 = hi - wk;
-                int64_t b0 = x0 <= 0 ? 0 : div_floor(x0 + wb - 1, wb, ly.inv_wblk[k]);
-                int64_t b1 = x1 <= 0 ? 0 : div_floor(x1 + wb - 1, wb, ly.inv_wblk[k]);
-                b0 = b0 < nb ? b0 : nb;
-                b1 = b1 < nb ? b1 : nb;
-                wk += nb * wb;
-                const int r = ly.rank[k];
-                const int kbr = r <= 16 ? 1 : r <= 32 ? 2 : r <= 64 ? 4 : 8;
-                const int mbs = NS / kbr;
-                rg.b0[k] = uni((int)b0);
-                rg.b1[k] = uni((int)b1);
-                rg.kbr[k] = kbr;
-                rg.nt[k] = uni((int)((b1 - b0 + mbs - 1) / mbs));
-            }
+            rg.cnt[k] = __builtin_amdgcn_readlane(cnt_l, k);
+            rg.b0[k] = __builtin_amdgcn_readlane((int)b0, k);
+            rg.b1[k] = __builtin_amdgcn_readlane((int)b1, k);
+            rg.nt[k] = k < T ? __builtin_amdgcn_readlane(nt_l, k) : 0;
+            rg.kbr[k] = 1 << __builtin_amdgcn_readlane(lkbr, k);
         }
     }
 
@@ -516,27 +510,30 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
     }
 
     // ---- score operand qb: q' = B_K q on the matrix cores, straight into
-    //      operand layout.  Column c16 carries query head c16 % 8 -- as
-    //      fp16(q') for c16 < 8 and as the remainder fp16(q' - fp16(q'))
-    //      above -- so that the fp16 products reproduce q' to ~2^-22.
-    //      Products of fp16 inputs are exact and sums fp32: q' is fp32-accurate.
-    half4_t qb[KB];
-#pragma unroll
-    for (int mb = 0; mb < KB; ++mb) {
+    //      operand layout (wave mb forms block mb, shared through LDS).
+    //      Column c16 carries query head c16 % 8 -- as fp16(q') for c16 < 8
+    //      and as the remainder fp16(q' - fp16(q')) above -- so that the fp16
+    //      products reproduce q' to ~2^-22.  Products of fp16 inputs are
+    //      exact and sums fp32: q' is fp32-accurate.
+    half4_t *s_qb = reinterpret_cast<half4_t *>(&s_rk[0][0][0]);   // [KB][64], before the loop
+    if (wave < KB) {
         float4_t acc = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int kb = 0; kb < ND; ++kb) {
-            const half4_t bb = gq < GQ ? bq[kb] : half4_t{0, 0, 0, 0};
-            acc = mma16(ak[mb][kb], bb, acc);
-        }
+        for (int kb = 0; kb < ND; ++kb) acc = mma16(ak[kb], gq < GQ ? bq[kb] : half4_t{0, 0, 0, 0}, acc);
+        half4_t v;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const float v = 16 * mb + 4 * grp + j < R ? qscale * acc[j] : 0.0f;
-            const _Float16 hi = (_Float16)v;
-            const _Float16 lo = (_Float16)(v - (float)hi);
-            qb[mb][j] = (c16 < 8) ? hi : lo;
+            const float x = 16 * wave + 4 * grp + j < R ? qscale * acc[j] : 0.0f;
+            const _Float16 xh = (_Float16)x;
+            const _Float16 xl = (_Float16)(x - (float)xh);
+            v[j] = c16 < 8 ? xh : xl;
         }
+        s_qb[wave * kWave + lane] = v;
     }
+    __syncthreads();
+    half4_t qb[KB];
+#pragma unroll
+    for (int mb = 0; mb < KB; ++mb) qb[mb] = s_qb[mb * kWave + lane];
     __syncthreads();
 
     // ---- main loop: two-deep pipeline over this wave's tiles
@@ -558,6 +555,19 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
         ta = locate<NS>(rg, ly, it);
         issue_tile<NS>(ta, DA, blk, ly, lane);
         process_any<GQ, KB, D>(tb, DB, qb, A, s_qt, sR, ev, bits, lane);
+    }
+
+    // ---- this wave's B_V operand for the back-projection (in flight
+    //      while the waves merge)
+    uint16_t bvr[RMAX / 4];
+    {
+        const uint16_t *BV = basis_ptr(ly, arena, layer / ly.G, 1, h);
+        const int col = 16 * (wave < ND ? wave : 0) + c16;
+#pragma unroll
+        for (int kb = 0; kb < RMAX / 4; ++kb) {
+            const int row = 4 * kb + grp < R ? 4 * kb + grp : R - 1;
+            bvr[kb] = BV[(int64_t)row * D + col];
+        }
     }
 
     // ---- merge the waves of this workgroup: each wave leaves its unscaled
@@ -594,7 +604,7 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
         float acc = 0.0f;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
-            const float f = M == -INFINITY ? 0.0f : exp2f(s_m[w][g] - M);
+            const float f = M == -INFINITY ? 0.0f : fast_exp2(s_m[w][g] - M);
             acc += f * reinterpret_cast<const float *>(s_ev + w * kEvWave)[i];
         }
         s_qp[i] = acc;
