@@ -88,6 +88,24 @@ int build_layout(const dwkv_config *c, Layout *ly)
     }
     // 16 spare bytes: fixed-width residual reads may run past the last token
     ly->head_block = align_up(blk + 16, 256);
+    if (ly->head_block > INT32_MAX) return DWKV_ERR_UNSUPPORTED;   // offsets are 32-bit
+    for (int k = 0; k < c->num_tiers; ++k) {
+        TierDesc &t = ly->tier[k];
+        t.coefK = (int32_t)ly->f_coefK[k];
+        t.coefV = (int32_t)ly->f_coefV[k];
+        t.idxK = (int32_t)ly->f_idxK[k];
+        t.idxV = (int32_t)ly->f_idxV[k];
+        t.valK = (int32_t)ly->f_valK[k];
+        t.valV = (int32_t)ly->f_valV[k];
+        t.scaleK = (int32_t)ly->f_scaleK[k];
+        t.scaleV = (int32_t)ly->f_scaleV[k];
+        t.rank = ly->rank[k];
+        t.resid = ly->resid[k];
+        t.istride = ly->istride[k];
+        t.vstride = ly->vstride[k];
+        t.weight = ly->weight[k];
+        t.pad0 = t.pad1 = t.pad2 = 0;
+    }
     const int64_t heads = (int64_t)ly->L * ly->Bmax * ly->Hkv;
     int64_t off = 0;
     ly->off_err = off;      off = align_up(off + 4, 256);

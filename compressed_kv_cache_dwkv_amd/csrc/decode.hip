@@ -62,6 +62,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kMaxLag = 8.0f;           // log2 units the running max may trail
 
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float4_t mma16(half4_t a, half4_t b, float4_t c)
@@ -69,6 +70,21 @@ __device__ __forceinline__ float4_t mma16(half4_t a, half4_t b, float4_t c)
     // D[m][n] += sum_k A[m][k] B[k][n]; lane l supplies A[l%16][4(l/16)+j],
     // B[4(l/16)+j][l%16] and holds D[4(l/16)+j][l%16], j = 0..3.
     return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+
+// The same with 32-deep operands (two 4-deep pieces per lane).  Whatever
+// order the hardware gives the 8 values of a lane in the contraction, A
+// and B use the same one, so pairing two 16-deep operand pieces of A with
+// the matching pieces of B sums exactly the products of the two 16-deep
+// steps.
+__device__ __forceinline__ float4_t mma32(half8_t a, half8_t b, float4_t c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ half8_t cat(half4_t a, half4_t b)
+{
+    return half8_t{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
 // Value from the lane 8 positions away inside each row of 16 lanes.
@@ -161,88 +177,95 @@ struct TileData {
     uint32_t ksc, vsc;          // fp16 scale in the low half
 };
 
-// Per-tier block ranges of this workgroup (uniform values).
+// This workgroup's block ranges, lane k holding tier k's values.
 struct Ranges {
-    int b0[kMaxTiers], b1[kMaxTiers];
-    int cnt[kMaxTiers], nt[kMaxTiers], kbr[kMaxTiers];
+    int b0, b1;       // first and end 16-token block of the workgroup's run
+    int cnt;          // tokens in the tier
+    int nt;           // tiles of the run (low 28 bits) | log2(16-channel blocks) << 28
+};
+
+// A wave's position: its tiles are numbers wave, wave + 8, ... counted
+// through the tiers in order, so the position only moves forward.
+struct Cursor {
+    int k;            // tier
+    int rem;          // tile number within the tier's run
 };
 
 template <int NS>
-__device__ __forceinline__ Tile locate(const Ranges &rg, const Layout &ly, int it)
+__device__ __forceinline__ Tile locate(const Ranges &rg, Cursor &cur, const Layout &ly)
 {
-    Tile t;
-    t.valid = 0;
-    t.k = 0;
-    t.r = t.s = t.nv = 0;
-    t.kbr = 1;
-    t.blk0 = 0;
-    int rem = it;
-#pragma unroll
-    for (int kk = 0; kk < kMaxTiers; ++kk) {
-        if (kk < ly.T && !t.valid) {
-            if (rem < rg.nt[kk]) {
-                const int kbr = rg.kbr[kk], mbs = NS / kbr;
-                t.valid = 1;
-                t.k = kk;
-                t.r = ly.rank[kk];
-                t.s = ly.resid[kk];
-                t.kbr = kbr;
-                t.blk0 = rg.b0[kk] + rem * mbs;
-                int nv = (rg.b1[kk] - t.blk0) * 16;
-                if (nv > 16 * mbs) nv = 16 * mbs;
-                const int left = rg.cnt[kk] - t.blk0 * 16;
-                t.nv = nv < left ? nv : left;
-            } else {
-                rem -= rg.nt[kk];
-            }
-        }
+    int k = cur.k, rem = cur.rem;
+    while (k < ly.T) {
+        const int nt = __builtin_amdgcn_readlane(rg.nt, k) & 0x0FFFFFFF;
+        if (rem < nt) break;
+        rem -= nt;
+        ++k;
     }
+    cur.k = k;
+    cur.rem = rem;
+    Tile t;
+    t.valid = k < ly.T;
+    t.k = t.valid ? k : 0;
+    const int lkbr = (int)((uint32_t)__builtin_amdgcn_readlane(rg.nt, t.k) >> 28);
+    const int mbs = NS >> lkbr;
+    t.kbr = 1 << lkbr;
+    t.r = ly.tier[t.k].rank;
+    t.s = ly.tier[t.k].resid;
+    const int blk0 = __builtin_amdgcn_readlane(rg.b0, t.k) + rem * mbs;
+    int nv = (__builtin_amdgcn_readlane(rg.b1, t.k) - blk0) * 16;
+    nv = nv < 16 * mbs ? nv : 16 * mbs;
+    const int left = __builtin_amdgcn_readlane(rg.cnt, t.k) - blk0 * 16;
+    t.nv = t.valid ? (nv < left ? nv : left) : 0;
+    t.blk0 = t.valid ? blk0 : 0;
     return t;
 }
 
 // Issues every load of a tile: always the same number of load instructions
 // (slots the tile does not use read a harmless in-block address), so the
 // compiler's wait counts stay exact and the next tile's loads are never
-// waited for while the current tile is computed.
+// waited for while the current tile is computed.  Addresses are a
+// wave-uniform base at the tile's first token plus 32-bit lane offsets.
 template <int NS>
 __device__ __forceinline__ void issue_tile(const Tile &t, TileData<NS> &D, const uint8_t *blk,
                                            const Layout &ly, int lane)
 {
     const int c16 = lane & 15, grp = lane >> 4;
-    const int k = t.k, r = t.r, kbr = t.kbr;
-    const uint16_t *cK = reinterpret_cast<const uint16_t *>(blk + ly.f_coefK[k]);
-    const uint16_t *cV = reinterpret_cast<const uint16_t *>(blk + ly.f_coefV[k]);
+    const TierDesc &td = ly.tier[t.k];
+    const int r = t.r, kbr = t.kbr, nv = t.nv;
     const int64_t tok0 = (int64_t)t.blk0 * 16;
+    // K rows and V 16-token blocks both start r fp16 per token in
+    const uint8_t *cK = blk + td.coefK + tok0 * r * 2;
+    const uint8_t *cV = blk + td.coefV + tok0 * r * 2;
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
         const int mb = i / kbr, kb = i - mb * kbr;
-        const bool use = t.valid && 16 * mb < t.nv;
+        const bool use = 16 * mb < nv;
         const int tr = 16 * mb + c16;
-        const int64_t ko = use && tr < t.nv && 16 * kb + 4 * grp < r
-                               ? (tok0 + tr) * r + 16 * kb + 4 * grp : 0;
-        const int64_t vo = use && 16 * kb + c16 < r
-                               ? (((int64_t)t.blk0 + mb) * r + 16 * kb + c16) * 16 + 4 * grp : 0;
+        const uint32_t ko = use && tr < nv && 16 * kb + 4 * grp < r
+                                ? (uint32_t)(tr * r + 16 * kb + 4 * grp) * 2u : 0u;
+        const uint32_t vo = use && 16 * kb + c16 < r
+                                ? (uint32_t)((mb * r + 16 * kb + c16) * 16 + 4 * grp) * 2u : 0u;
         D.ka[i] = *reinterpret_cast<const half4_t *>(cK + ko);
         D.va[i] = *reinterpret_cast<const half4_t *>(cV + vo);
     }
-    const bool tv = t.valid && t.s > 0 && lane < t.nv;
-    const int64_t tt = tv ? tok0 + lane : 0;
-    const uint8_t *iK = blk + ly.f_idxK[k] + tt * ly.istride[k];
-    const uint8_t *vK = blk + ly.f_valK[k] + tt * ly.vstride[k];
-    const uint8_t *iV = blk + ly.f_idxV[k] + tt * ly.istride[k];
-    const uint8_t *vV = blk + ly.f_valV[k] + tt * ly.vstride[k];
-    // scales: the aligned 4-byte word holding this token's fp16
-    const int64_t sw = (tt & ~1ll) * 2;
-    D.ki0 = ld32(iK);
-    D.ki1 = ld32(iK + 4);
-    D.kc0 = ld32(vK);
-    D.kc1 = ld32(vK + 4);
-    D.ksc = ld32(blk + ly.f_scaleK[k] + sw) >> (16 * (tt & 1));
-    D.vi0 = ld32(iV);
-    D.vi1 = ld32(iV + 4);
-    D.vc0 = ld32(vV);
-    D.vc1 = ld32(vV + 4);
-    D.vsc = ld32(blk + ly.f_scaleV[k] + sw) >> (16 * (tt & 1));
+    const uint32_t tl = t.s > 0 && lane < nv ? (uint32_t)lane : 0u;
+    const uint32_t io = tl * (uint32_t)td.istride, vo = tl * (uint32_t)td.vstride;
+    const uint8_t *iK = blk + td.idxK + tok0 * td.istride;
+    const uint8_t *vK = blk + td.valK + tok0 * td.vstride;
+    const uint8_t *iV = blk + td.idxV + tok0 * td.istride;
+    const uint8_t *vV = blk + td.valV + tok0 * td.vstride;
+    // scales: the aligned 4-byte word holding this token's fp16 (tok0 is even)
+    const uint32_t so = (tl & ~1u) * 2u, sh = 16u * (tl & 1u);
+    D.ki0 = ld32(iK + io);
+    D.ki1 = ld32(iK + io + 4);
+    D.kc0 = ld32(vK + vo);
+    D.kc1 = ld32(vK + vo + 4);
+    D.ksc = ld32(blk + td.scaleK + tok0 * 2 + so) >> sh;
+    D.vi0 = ld32(iV + io);
+    D.vi1 = ld32(iV + io + 4);
+    D.vc0 = ld32(vV + vo);
+    D.vc1 = ld32(vV + vo + 4);
+    D.vsc = ld32(blk + td.scaleV + tok0 * 2 + so) >> sh;
 }
 
 // Per-wave state of the online softmax and the value sums.
@@ -284,7 +307,6 @@ __device__ __forceinline__ void process_tile(const Tile &t, const TileData<kSlot
     // ---- residuals, one token per lane: K logit terms (q gathered from
     //      LDS) and the V residual's cells of the dense LDS tile
     const bool tok = lane < nv;
-    int vcell[kMaxResid];
     if (s > 0) {
         uint32_t i0 = Dt.ki0, i1 = Dt.ki1, c0 = Dt.kc0, c1 = Dt.kc1;
         rotate_entries(i0, i1, c0, c1, s, bits, lane % s);
@@ -312,8 +334,8 @@ __device__ __forceinline__ void process_tile(const Tile &t, const TileData<kSlot
 #pragma unroll
         for (int u = 0; u < kMaxResid; ++u) {
             const bool on = tok && u < s;
-            vcell[u] = (on ? idx_at(Dt.vi0, Dt.vi1, u) : kMaxHeadDim) * kEvStride + lane;
-            ev[vcell[u]] = (_Float16)(on ? code_at(Dt.vc0, Dt.vc1, u, bits) * scv : 0.0f);
+            ev[(on ? idx_at(Dt.vi0, Dt.vi1, u) : kMaxHeadDim) * kEvStride + lane] =
+                (_Float16)(on ? code_at(Dt.vc0, Dt.vc1, u, bits) * scv : 0.0f);
         }
         wave_fence();
     }
@@ -361,34 +383,49 @@ __device__ __forceinline__ void process_tile(const Tile &t, const TileData<kSlot
         }
     }
 
-    // ---- values: probabilities x V coefficient columns (16-token blocks)
+    // ---- values: probabilities x V coefficient columns, two 16-token
+    //      blocks per product where the tile has them
 #pragma unroll
-    for (int mb = 0; mb < MBS; ++mb) {
+    for (int nb = 0; nb < KBR; ++nb) {
+        half4_t bv[MBS];
 #pragma unroll
-        for (int nb = 0; nb < KBR; ++nb) {
-            half4_t bv = Dt.va[mb * KBR + nb];
+        for (int mb = 0; mb < MBS; ++mb) {
+            bv[mb] = Dt.va[mb * KBR + nb];
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                if (16 * nb + c16 >= r || 16 * mb + 4 * grp + j >= nv) bv[j] = 0;
-            A.O[nb] = mma16(P[mb], bv, A.O[nb]);
+                if (16 * nb + c16 >= r || 16 * mb + 4 * grp + j >= nv) bv[mb][j] = 0;
+        }
+        if constexpr (MBS == 1) {
+            A.O[nb] = mma16(P[0], bv[0], A.O[nb]);
+        } else {
+#pragma unroll
+            for (int p = 0; p < MBS / 2; ++p)
+                A.O[nb] = mma32(cat(P[2 * p], P[2 * p + 1]), cat(bv[2 * p], bv[2 * p + 1]), A.O[nb]);
         }
     }
 
     // ---- V residual mass: the dense tile times the probabilities, then the
     //      written cells are cleared (after the reads: same wave, in order)
     if (s > 0) {
+        const _Float16 *evr = ev + c16 * kEvStride + 4 * grp;
 #pragma unroll
-        for (int mb = 0; mb < MBS; ++mb) {
+        for (int nb = 0; nb < ND; ++nb) {
+            if constexpr (MBS == 1) {
+                const half4_t e0 = *reinterpret_cast<const half4_t *>(evr + 16 * nb * kEvStride);
+                A.Ores[nb] = mma16(P[0], e0, A.Ores[nb]);
+            } else {
 #pragma unroll
-            for (int nb = 0; nb < ND; ++nb) {
-                const half4_t bv =
-                    *reinterpret_cast<const half4_t *>(&ev[(16 * nb + c16) * kEvStride + 16 * mb + 4 * grp]);
-                A.Ores[nb] = mma16(P[mb], bv, A.Ores[nb]);
+                for (int p = 0; p < MBS / 2; ++p) {
+                    const half4_t e0 = *reinterpret_cast<const half4_t *>(evr + 16 * nb * kEvStride + 32 * p);
+                    const half4_t e1 = *reinterpret_cast<const half4_t *>(evr + 16 * nb * kEvStride + 32 * p + 16);
+                    A.Ores[nb] = mma32(cat(P[2 * p], P[2 * p + 1]), cat(e0, e1), A.Ores[nb]);
+                }
             }
         }
         wave_fence();
 #pragma unroll
-        for (int u = 0; u < kMaxResid; ++u) ev[vcell[u]] = (_Float16)0.0f;
+        for (int u = 0; u < kMaxResid; ++u)
+            ev[((tok && u < s) ? idx_at(Dt.vi0, Dt.vi1, u) : kMaxHeadDim) * kEvStride + lane] = (_Float16)0.0f;
     }
 }
 
@@ -453,7 +490,7 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
     }
 
     // ---- this workgroup's byte-balanced run of 16-token blocks: lane k
-    //      works out tier k's range, then every value is read into scalars
+    //      works out and keeps tier k's range
     const uint8_t *blk = head_block_ptr(ly, arena, layer, b, h);
     Ranges rg;
     {
@@ -481,20 +518,16 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
         const int lkbr = (r_l > 16) + (r_l > 32) + (r_l > 64);     // log2 of 16-channel blocks
         const int lmbs = (NS == 8 ? 3 : 2) - lkbr;                 // log2 of 16-token blocks per tile
         const int nt_l = (int)((b1 - b0 + (1 << lmbs) - 1) >> lmbs);
-#pragma unroll
-        for (int k = 0; k < kMaxTiers; ++k) {
-            rg.cnt[k] = __builtin_amdgcn_readlane(cnt_l, k);
-            rg.b0[k] = __builtin_amdgcn_readlane((int)b0, k);
-            rg.b1[k] = __builtin_amdgcn_readlane((int)b1, k);
-            rg.nt[k] = k < T ? __builtin_amdgcn_readlane(nt_l, k) : 0;
-            rg.kbr[k] = 1 << __builtin_amdgcn_readlane(lkbr, k);
-        }
+        rg.b0 = (int)b0;
+        rg.b1 = (int)b1;
+        rg.cnt = cnt_l;
+        rg.nt = nt_l | (lkbr << 28);
     }
 
     // ---- first tile's loads
     TileData<NS> DA, DB;
-    int it = wave;
-    Tile ta = locate<NS>(rg, ly, it);
+    Cursor cur{0, wave};
+    Tile ta = locate<NS>(rg, cur, ly);
     issue_tile<NS>(ta, DA, blk, ly, lane);
 
     // ---- query in base-2 logit units (LDS, for residual gathers); this
@@ -546,13 +579,13 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
     A.l_part = 0.0f;
     float *sR = &s_rk[wave][0][0];
     while (ta.valid) {
-        it += kWaves;
-        Tile tb = locate<NS>(rg, ly, it);
+        cur.rem += kWaves;
+        Tile tb = locate<NS>(rg, cur, ly);
         issue_tile<NS>(tb, DB, blk, ly, lane);
         process_any<GQ, KB, D>(ta, DA, qb, A, s_qt, sR, ev, bits, lane);
         if (!tb.valid) break;
-        it += kWaves;
-        ta = locate<NS>(rg, ly, it);
+        cur.rem += kWaves;
+        ta = locate<NS>(rg, cur, ly);
         issue_tile<NS>(ta, DA, blk, ly, lane);
         process_any<GQ, KB, D>(tb, DB, qb, A, s_qt, sR, ev, bits, lane);
     }

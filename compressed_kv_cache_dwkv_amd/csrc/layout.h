@@ -51,6 +51,13 @@ constexpr int kMaxResid = 8;
 constexpr int kMaxGroupQ = 8;
 constexpr int kMaxSplits = 256;   // decode workgroups per (sequence, KV head)
 
+// One tier as the decode kernel sees it: array offsets in bytes from the
+// start of a (layer, sequence, KV head) block, and the tier's shape.
+struct TierDesc {
+    int32_t coefK, coefV, idxK, idxV, valK, valV, scaleK, scaleV;
+    int32_t rank, resid, istride, vstride, weight, pad0, pad1, pad2;
+};
+
 struct Layout {
     int32_t L, G, Hq, Hkv, d, R, T, bits, Bmax, gq, s_max, qmax, num_groups;
     int32_t rank[kMaxTiers];
@@ -70,6 +77,7 @@ struct Layout {
     int64_t f_valK[kMaxTiers], f_valV[kMaxTiers];
     int64_t f_scaleK[kMaxTiers], f_scaleV[kMaxTiers];
     int64_t total;
+    TierDesc tier[kMaxTiers];    // the same tiers, packed per tier (head blocks < 2 GiB)
 };
 
 DWKV_HD int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
