@@ -19,6 +19,13 @@ struct dwkv_handle {
 
 namespace dwkv {
 
+// Decode work of a token beyond its bytes, in byte equivalents: a token's
+// residual gathers and softmax cost about as much time as streaming this
+// many bytes (measured on the 64K-token Llama-3-8B shape).  Splits balance
+// bytes plus this share, so tiers with few bytes per token are not
+// under-provisioned.
+constexpr int kTokenCost = 48;
+
 int build_layout(const dwkv_config *c, Layout *ly)
 {
     if (!c || !ly) return DWKV_ERR_INVALID_ARG;
@@ -75,7 +82,8 @@ int build_layout(const dwkv_config *c, Layout *ly)
         ly->vstride[k] = vs;
         ly->cap[k] = c->tier_capacity[k];
         ly->weight[k] = 4 * r + (s > 0 ? 2 * (is + vs + 2) : 0);
-        ly->inv_wblk[k] = 1.0 / (16.0 * ly->weight[k]);
+        ly->cost[k] = ly->weight[k] + kTokenCost;
+        ly->inv_cblk[k] = 1.0 / (16.0 * ly->cost[k]);
         blk = align_up(blk, 256);
         ly->f_coefK[k] = blk; blk = align_up(blk + cap * r * 2, 16);
         ly->f_coefV[k] = blk; blk = align_up(blk + cap * r * 2, 16);

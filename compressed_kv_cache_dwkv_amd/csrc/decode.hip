@@ -12,8 +12,8 @@
 // B_V is applied once per workgroup at the end.
 //
 // Work split (split-K "flash decode"): grid = (splits, KV heads, sequences),
-// one 8-wave workgroup per compute unit.  A workgroup takes a byte-balanced
-// run of 16-token blocks of the tier regions of its (sequence, KV head) and
+// one 8-wave workgroup per compute unit.  A workgroup takes a work-balanced
+// (bytes plus a fixed per-token share) run of 16-token blocks of the tier regions of its (sequence, KV head) and
 // cuts it into tiles of about 2 KiB of coefficients per K and V (64 tokens
 // at rank <= 16, 32 at rank 32, 16 at rank 64 or more); wave w takes tiles
 // w, w + 8, ...  Each wave keeps its own online softmax (base-2 logits) and
@@ -489,14 +489,14 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
             ak[kb] = *reinterpret_cast<const half4_t *>(BK + (int64_t)row * D + 16 * kb + 4 * grp);
     }
 
-    // ---- this workgroup's byte-balanced run of 16-token blocks: lane k
+    // ---- this workgroup's work-balanced run of 16-token blocks: lane k
     //      works out and keeps tier k's range
     const uint8_t *blk = head_block_ptr(ly, arena, layer, b, h);
     Ranges rg;
     {
         const bool on = lane < T;
         const int r_l = ly.rank[kl];
-        const int64_t wb_l = 16 * (int64_t)ly.weight[kl];
+        const int64_t wb_l = 16 * (int64_t)ly.cost[kl];
         const int64_t nb_l = on ? (cnt_l + 15) >> 4 : 0;
         const int64_t wt_l = nb_l * wb_l;                     // bytes of tier k's blocks
         int64_t W = 0, wk_l = 0;                               // total; bytes of tiers before k
@@ -511,8 +511,8 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
         const int64_t lo = div_floor(W * split, S, invS);
         const int64_t hi = div_floor(W * (split + 1), S, invS);
         const int64_t x0 = lo - wk_l, x1 = hi - wk_l;
-        int64_t b0 = x0 <= 0 || !on ? 0 : div_floor(x0 + wb_l - 1, wb_l, ly.inv_wblk[kl]);
-        int64_t b1 = x1 <= 0 || !on ? 0 : div_floor(x1 + wb_l - 1, wb_l, ly.inv_wblk[kl]);
+        int64_t b0 = x0 <= 0 || !on ? 0 : div_floor(x0 + wb_l - 1, wb_l, ly.inv_cblk[kl]);
+        int64_t b1 = x1 <= 0 || !on ? 0 : div_floor(x1 + wb_l - 1, wb_l, ly.inv_cblk[kl]);
         b0 = b0 < nb_l ? b0 : nb_l;
         b1 = b1 < nb_l ? b1 : nb_l;
         const int lkbr = (r_l > 16) + (r_l > 32) + (r_l > 64);     // log2 of 16-channel blocks
@@ -693,9 +693,28 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
     }
     __syncthreads();
     if (!s_last) return;
-    // weights 2^(m_s - M) of every split, through LDS (the V-residual tiles:
-    // [GQ][S] weights, [GQ][S] normalisers, then the reduction area)
+    // Each thread owns 4 adjacent outputs of one head and an interleaved
+    // subset of the splits.  Its first 8 partial vectors are requested
+    // together with every split's max and normaliser, so the merge waits
+    // for memory once; weights 2^(m_s - M) then come from LDS (the
+    // V-residual tiles: [GQ][S] weights, [GQ][S] normalisers, reduction area).
+    constexpr int quads = GQ * D / 4;
+    constexpr int parts = kBlock / quads;
+    constexpr int kFirst = 8;
+    static_assert(kBlock % quads == 0, "merge layout");
     static_assert((2 * kMaxSplits * 8 + kBlock * 4) * 4 <= kWaves * kEvWave * 2, "merge scratch");
+    const int qd = tid % quads, part = tid / quads;
+    const int hq = (4 * qd) / D, j4 = (4 * qd) % D;
+    const float *pob = ws.po + ((int64_t)b * ly.Hq + g0 + hq) * S * D + j4;
+    float4_t pc[kFirst];
+#pragma unroll
+    for (int c = 0; c < kFirst; ++c) {
+        const int sp = part + c * parts;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            pc[c][j] = sp < S ? __hip_atomic_load(pob + (int64_t)sp * D + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                              : 0.0f;
+    }
     float *s_w = reinterpret_cast<float *>(s_ev);
     float *s_pl = s_w + GQ * S;
     for (int i = tid; i < GQ * S; i += kBlock) {
@@ -714,7 +733,7 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
     __syncthreads();
     for (int i = tid; i < GQ * S; i += kBlock) {
         const float M = s_M[i / S];
-        s_w[i] = M == -INFINITY ? 0.0f : exp2f(s_w[i] - M);
+        s_w[i] = M == -INFINITY ? 0.0f : fast_exp2(s_w[i] - M);
     }
     __syncthreads();
     if (tid < GQ) {
@@ -722,27 +741,22 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
         for (int i = 0; i < S; ++i) L += s_w[tid * S + i] * s_pl[tid * S + i];
         s_L[tid] = L;
     }
-    // each thread: 4 adjacent outputs of one head over an interleaved subset
-    // of the splits, many independent loads in flight
-    constexpr int quads = GQ * D / 4;
-    constexpr int parts = kBlock / quads;
     float4_t accm = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    const int qd = tid % quads, part = tid / quads;
-    const int hq = (4 * qd) / D, j4 = (4 * qd) % D;
-    if (part < parts) {
-        const float *po = ws.po + ((int64_t)b * ly.Hq + g0 + hq) * S * D + j4;
-#pragma unroll 8
-        for (int sp = part; sp < S; sp += parts) {
-            float4_t v;
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                v[j] = __hip_atomic_load(po + (int64_t)sp * D + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            accm += s_w[hq * S + sp] * v;
-        }
+    for (int c = 0; c < kFirst; ++c) {
+        const int sp = part + c * parts;
+        if (sp < S) accm += s_w[hq * S + sp] * pc[c];
+    }
+    for (int sp = part + kFirst * parts; sp < S; sp += parts) {
+        float4_t v;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            v[j] = __hip_atomic_load(pob + (int64_t)sp * D + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        accm += s_w[hq * S + sp] * v;
     }
     __syncthreads();
     float4_t *s_red = reinterpret_cast<float4_t *>(s_ev) + kMaxSplits * 2 * 8 / 4;   // [parts][quads]
-    if (part < parts) s_red[part * quads + qd] = accm;
+    s_red[part * quads + qd] = accm;
     __syncthreads();
     if (tid < quads) {
         float4_t o = s_red[tid];

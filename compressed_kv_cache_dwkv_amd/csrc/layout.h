@@ -66,7 +66,9 @@ struct Layout {
     int32_t istride[kMaxTiers];  // stored index bytes per token (s rounded up to 4)
     int32_t vstride[kMaxTiers];  // stored code bytes per token (vbytes rounded up to 4)
     int32_t weight[kMaxTiers];   // algorithmic bytes per token (K and V)
-    double inv_wblk[kMaxTiers];  // 1 / (16 * weight): reciprocal of a 16-token block's bytes
+    int32_t cost[kMaxTiers];     // decode work per token in byte equivalents: weight plus a
+                                 // fixed per-token share (residuals, softmax)
+    double inv_cblk[kMaxTiers];  // 1 / (16 * cost): reciprocal of a 16-token block's cost
     int64_t cap[kMaxTiers];
     int64_t max_tokens;
     int64_t off_err, off_counts, off_posmap, off_basis, off_seg;
