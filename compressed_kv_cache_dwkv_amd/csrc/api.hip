@@ -25,6 +25,7 @@ namespace dwkv {
 // bytes plus this share, so tiers with few bytes per token are not
 // under-provisioned.
 constexpr int kTokenCost = 48;
+constexpr int64_t kArenaTail = 8192;
 
 int build_layout(const dwkv_config *c, Layout *ly)
 {
@@ -122,7 +123,9 @@ int build_layout(const dwkv_config *c, Layout *ly)
     ly->basis_elems = (int64_t)ly->Hkv * ly->R * ly->d;
     ly->off_basis = off;    off = align_up(off + (int64_t)ly->num_groups * 2 * ly->basis_elems * 2, 256);
     ly->off_seg = off;      off = off + heads * ly->head_block;
-    ly->total = align_up(off, 256);
+    // spare tail: the decode kernel's fixed-shape tile loads may read up to
+    // a few KiB past the last token of the last head block
+    ly->total = align_up(off + kArenaTail, 256);
     return DWKV_OK;
 }
 

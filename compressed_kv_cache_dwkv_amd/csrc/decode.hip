@@ -220,35 +220,36 @@ __device__ __forceinline__ Tile locate(const Ranges &rg, Cursor &cur, const Layo
     return t;
 }
 
-// Issues every load of a tile: always the same number of load instructions
-// (slots the tile does not use read a harmless in-block address), so the
-// compiler's wait counts stay exact and the next tile's loads are never
-// waited for while the current tile is computed.  Addresses are a
-// wave-uniform base at the tile's first token plus 32-bit lane offsets.
+// Issues every load of a tile: always the same number of load instructions,
+// so the compiler's wait counts stay exact and the next tile's loads are
+// never waited for while the current tile is computed.  Addresses are a
+// wave-uniform base per operand slot plus one 32-bit lane offset per tile.
+// Slots and lanes past the tile's valid tokens or its rank still read
+// inside the arena (which ends in a spare tail for this) and their values
+// are zeroed where they are used.
 template <int NS>
 __device__ __forceinline__ void issue_tile(const Tile &t, TileData<NS> &D, const uint8_t *blk,
                                            const Layout &ly, int lane)
 {
     const int c16 = lane & 15, grp = lane >> 4;
     const TierDesc &td = ly.tier[t.k];
-    const int r = t.r, kbr = t.kbr, nv = t.nv;
+    const int r = t.r, kbr = t.kbr;
     const int64_t tok0 = (int64_t)t.blk0 * 16;
-    // K rows and V 16-token blocks both start r fp16 per token in
+    // K: token rows of r fp16; V: 16-token blocks of r rows x 16 tokens --
+    // both start r fp16 per token into their arrays
     const uint8_t *cK = blk + td.coefK + tok0 * r * 2;
     const uint8_t *cV = blk + td.coefV + tok0 * r * 2;
+    const uint32_t kl = (uint32_t)(c16 * r + 4 * grp) * 2u;     // token c16, channels 4grp..
+    const uint32_t vl = (uint32_t)(c16 * 16 + 4 * grp) * 2u;    // channel c16, tokens 4grp..
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
         const int mb = i / kbr, kb = i - mb * kbr;
-        const bool use = 16 * mb < nv;
-        const int tr = 16 * mb + c16;
-        const uint32_t ko = use && tr < nv && 16 * kb + 4 * grp < r
-                                ? (uint32_t)(tr * r + 16 * kb + 4 * grp) * 2u : 0u;
-        const uint32_t vo = use && 16 * kb + c16 < r
-                                ? (uint32_t)((mb * r + 16 * kb + c16) * 16 + 4 * grp) * 2u : 0u;
-        D.ka[i] = *reinterpret_cast<const half4_t *>(cK + ko);
-        D.va[i] = *reinterpret_cast<const half4_t *>(cV + vo);
+        D.ka[i] = *reinterpret_cast<const half4_t *>(cK + (16 * mb * r + 16 * kb) * 2 + kl);
+        D.va[i] = *reinterpret_cast<const half4_t *>(cV + (mb * r + 16 * kb) * 32 + vl);
     }
-    const uint32_t tl = t.s > 0 && lane < nv ? (uint32_t)lane : 0u;
+    // residual records of token `lane` (token 0's for lanes past the tile:
+    // their indices must stay valid)
+    const uint32_t tl = lane < t.nv ? (uint32_t)lane : 0u;
     const uint32_t io = tl * (uint32_t)td.istride, vo = tl * (uint32_t)td.vstride;
     const uint8_t *iK = blk + td.idxK + tok0 * td.istride;
     const uint8_t *vK = blk + td.valK + tok0 * td.vstride;
@@ -273,9 +274,16 @@ template <int KB, int D>
 struct WaveAcc {
     float4_t O[KB];                      // basis-space value sums [head row][channel]
     float4_t Ores[D / 16];               // residual value mass [head row][channel]
+    float4_t Ol;                         // normalisers: column 0 holds sum_t p per head row
     float m_run;                         // running max of head (lane % 16) % 8
-    float l_part;                        // this lane's share of that head's normaliser
 };
+
+// Bit masks keeping the first s entries of a token's record words (index
+// bytes; `bits`-bit codes), uniform over the wave.
+__device__ __forceinline__ uint32_t low_bits(int n)
+{
+    return n >= 32 ? 0xFFFFFFFFu : n <= 0 ? 0u : (1u << n) - 1u;
+}
 
 template <int GQ, int KB, int D, int KBR>
 __device__ __forceinline__ void process_tile(const Tile &t, const TileData<kSlots * (KB / 4)> &Dt,
@@ -289,13 +297,14 @@ __device__ __forceinline__ void process_tile(const Tile &t, const TileData<kSlot
     constexpr int ND = D / 16;
     const int c16 = lane & 15, grp = lane >> 4;
     const int r = t.r, s = t.s, nv = t.nv;
+    const bool full = nv == 16 * MBS;               // uniform: no token masks needed
 
     // ---- scores: K coefficient rows x (q'_hi, q'_lo)
     float4_t Sc[MBS];
 #pragma unroll
     for (int mb = 0; mb < MBS; ++mb) {
         Sc[mb] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
-        const bool tv = 16 * mb + c16 < nv;
+        const bool tv = full || 16 * mb + c16 < nv;
 #pragma unroll
         for (int kb = 0; kb < KBR; ++kb) {
             half4_t a = Dt.ka[mb * KBR + kb];
@@ -304,20 +313,24 @@ __device__ __forceinline__ void process_tile(const Tile &t, const TileData<kSlot
         }
     }
 
-    // ---- residuals, one token per lane: K logit terms (q gathered from
-    //      LDS) and the V residual's cells of the dense LDS tile
-    const bool tok = lane < nv;
+    // ---- residuals, one token per lane.  Entries past s are given index
+    //      128 (a zero row of q, the spare row of the V-residual tile) and
+    //      code 0, a whole record word at a time.  K: logit terms from q
+    //      gathered in LDS.  V: the token's cells of the dense LDS tile.
+    uint32_t vi0 = 0, vi1 = 0;
     if (s > 0) {
-        uint32_t i0 = Dt.ki0, i1 = Dt.ki1, c0 = Dt.kc0, c1 = Dt.kc1;
-        rotate_entries(i0, i1, c0, c1, s, bits, lane % s);
+        const uint32_t im0 = low_bits(8 * s), im1 = low_bits(8 * s - 32);
+        const uint32_t cm0 = low_bits(bits * s), cm1 = low_bits(bits * s - 32);
+        const uint32_t ki0 = (Dt.ki0 & im0) | (0x80808080u & ~im0);
+        const uint32_t ki1 = (Dt.ki1 & im1) | (0x80808080u & ~im1);
+        const uint32_t kc0 = Dt.kc0 & cm0, kc1 = Dt.kc1 & cm1;
         float rk[GP];
 #pragma unroll
         for (int g = 0; g < GP; ++g) rk[g] = 0.0f;
 #pragma unroll
         for (int u = 0; u < kMaxResid; ++u) {
-            const bool on = u < s;
-            const int j = on ? idx_at(i0, i1, u) : 0;
-            const float cv = on ? code_at(c0, c1, u, bits) : 0.0f;
+            const int j = idx_at(ki0, ki1, u);
+            const float cv = code_at(kc0, kc1, u, bits);
             const float4_t q0 = *reinterpret_cast<const float4_t *>(&s_qt[j][0]);
 #pragma unroll
             for (int g = 0; g < 4; ++g) rk[g] += cv * q0[g];
@@ -327,15 +340,20 @@ __device__ __forceinline__ void process_tile(const Tile &t, const TileData<kSlot
                 for (int g = 0; g < 4; ++g) rk[4 + g] += cv * q1[g];
             }
         }
-        const float sck = tok ? h2f((uint16_t)Dt.ksc) : 0.0f;
+        const float sck = lane < nv ? h2f((uint16_t)Dt.ksc) : 0.0f;
 #pragma unroll
         for (int g = 0; g < GQ; ++g) sR[g * kTile + lane] = rk[g] * sck;
-        const float scv = h2f((uint16_t)Dt.vsc);
+        // V cells (lanes past the tile write finite values of token 0 into
+        // their own columns, which meet probability 0)
+        vi0 = (Dt.vi0 & im0) | (0x80808080u & ~im0);
+        vi1 = (Dt.vi1 & im1) | (0x80808080u & ~im1);
+        const uint32_t vc0 = Dt.vc0 & cm0, vc1 = Dt.vc1 & cm1;
+        const _Float16 scv = __builtin_bit_cast(_Float16, (uint16_t)Dt.vsc);
 #pragma unroll
         for (int u = 0; u < kMaxResid; ++u) {
-            const bool on = tok && u < s;
-            ev[(on ? idx_at(Dt.vi0, Dt.vi1, u) : kMaxHeadDim) * kEvStride + lane] =
-                (_Float16)(on ? code_at(Dt.vc0, Dt.vc1, u, bits) * scv : 0.0f);
+            const int pos = u * bits;
+            const int code = (int)__builtin_amdgcn_sbfe((int)(pos < 32 ? vc0 : vc1), pos & 31, bits);
+            ev[idx_at(vi0, vi1, u) * kEvStride + lane] = (_Float16)(int16_t)code * scv;
         }
         wave_fence();
     }
@@ -349,19 +367,25 @@ __device__ __forceinline__ void process_tile(const Tile &t, const TileData<kSlot
         float4_t rr = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
         if (s > 0) rr = *reinterpret_cast<const float4_t *>(&sR[rrow * kTile + 16 * mb + 4 * grp]);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const float zz = Sc[mb][j] + row_swap8(Sc[mb][j]) + rr[j];
-            z[mb][j] = (16 * mb + 4 * grp + j < nv) ? zz : -INFINITY;
-            tmax = fmaxf(tmax, z[mb][j]);
-        }
+        for (int j = 0; j < 4; ++j) z[mb][j] = Sc[mb][j] + row_swap8(Sc[mb][j]) + rr[j];
     }
+    if (!full) {
+#pragma unroll
+        for (int mb = 0; mb < MBS; ++mb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (16 * mb + 4 * grp + j >= nv) z[mb][j] = -INFINITY;
+    }
+#pragma unroll
+    for (int mb = 0; mb < MBS; ++mb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) tmax = fmaxf(tmax, z[mb][j]);
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
     const bool need = tmax > A.m_run + kMaxLag;
     if (__any(need)) {
         const float new_m = need ? tmax : A.m_run;
         const float f = fast_exp2(A.m_run - new_m);
-        A.l_part *= f;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const float fh = __shfl(f, 4 * grp + j, kWave);
@@ -369,31 +393,34 @@ __device__ __forceinline__ void process_tile(const Tile &t, const TileData<kSlot
             for (int nb = 0; nb < KB; ++nb) A.O[nb][j] *= fh;
 #pragma unroll
             for (int nb = 0; nb < ND; ++nb) A.Ores[nb][j] *= fh;
+            A.Ol[j] *= fh;
         }
         A.m_run = new_m;
     }
     half4_t P[MBS];
 #pragma unroll
-    for (int mb = 0; mb < MBS; ++mb) {
+    for (int mb = 0; mb < MBS; ++mb)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const _Float16 ph = (_Float16)fast_exp2(z[mb][j] - A.m_run);
-            P[mb][j] = ph;
-            A.l_part += (float)ph;
-        }
-    }
+        for (int j = 0; j < 4; ++j) P[mb][j] = (_Float16)fast_exp2(z[mb][j] - A.m_run);
 
     // ---- values: probabilities x V coefficient columns, two 16-token
-    //      blocks per product where the tile has them
+    //      blocks per product where the tile has them; the normaliser is
+    //      the same product with a column of ones (fp32 sums of the fp16
+    //      probabilities the values use)
+    const _Float16 one = c16 == 0 ? (_Float16)1.0f : (_Float16)0.0f;
+    const half4_t ones = half4_t{one, one, one, one};
 #pragma unroll
     for (int nb = 0; nb < KBR; ++nb) {
         half4_t bv[MBS];
+        const bool cv = 16 * nb + c16 < r;
 #pragma unroll
         for (int mb = 0; mb < MBS; ++mb) {
-            bv[mb] = Dt.va[mb * KBR + nb];
+            bv[mb] = cv ? Dt.va[mb * KBR + nb] : half4_t{0, 0, 0, 0};
+            if (!full) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                if (16 * nb + c16 >= r || 16 * mb + 4 * grp + j >= nv) bv[mb][j] = 0;
+                for (int j = 0; j < 4; ++j)
+                    if (16 * mb + 4 * grp + j >= nv) bv[mb][j] = 0;
+            }
         }
         if constexpr (MBS == 1) {
             A.O[nb] = mma16(P[0], bv[0], A.O[nb]);
@@ -402,6 +429,12 @@ __device__ __forceinline__ void process_tile(const Tile &t, const TileData<kSlot
             for (int p = 0; p < MBS / 2; ++p)
                 A.O[nb] = mma32(cat(P[2 * p], P[2 * p + 1]), cat(bv[2 * p], bv[2 * p + 1]), A.O[nb]);
         }
+    }
+    if constexpr (MBS == 1) {
+        A.Ol = mma16(P[0], ones, A.Ol);
+    } else {
+#pragma unroll
+        for (int p = 0; p < MBS / 2; ++p) A.Ol = mma32(cat(P[2 * p], P[2 * p + 1]), cat(ones, ones), A.Ol);
     }
 
     // ---- V residual mass: the dense tile times the probabilities, then the
@@ -424,8 +457,7 @@ __device__ __forceinline__ void process_tile(const Tile &t, const TileData<kSlot
         }
         wave_fence();
 #pragma unroll
-        for (int u = 0; u < kMaxResid; ++u)
-            ev[((tok && u < s) ? idx_at(Dt.vi0, Dt.vi1, u) : kMaxHeadDim) * kEvStride + lane] = (_Float16)0.0f;
+        for (int u = 0; u < kMaxResid; ++u) ev[idx_at(vi0, vi1, u) * kEvStride + lane] = (_Float16)0.0f;
     }
 }
 
@@ -463,7 +495,8 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
     const int g0 = h * GQ;
 
     __shared__ __attribute__((aligned(16))) _Float16 s_ev[kWaves * kEvWave];   // V-residual tiles
-    __shared__ __attribute__((aligned(16))) float s_qt[D][GP];                 // q, base-2 units
+    __shared__ __attribute__((aligned(16))) float s_qt[kMaxHeadDim + 1][GP];   // q, base-2 units; zero rows
+                                                                                // from D on (row 128: unused entries)
     constexpr int RK = GQ < 2 ? 2 : GQ;            // rows of the K-residual area (>= 4 KiB)
     __shared__ __attribute__((aligned(16))) float s_rk[kWaves][RK][kTile];     // K-residual logits
     __shared__ float s_m[kWaves][GQ], s_l[kWaves][GQ];
@@ -532,9 +565,9 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
 
     // ---- query in base-2 logit units (LDS, for residual gathers); this
     //      wave's V-residual tile cleared
-    for (int i = tid; i < D * GP; i += kBlock) {
+    for (int i = tid; i < (kMaxHeadDim + 1) * GP; i += kBlock) {
         const int j = i / GP, g = i % GP;
-        s_qt[j][g] = g < GQ ? qscale * h2f(q[((int64_t)b * ly.Hq + g0 + g) * D + j]) : 0.0f;
+        s_qt[j][g] = g < GQ && j < D ? qscale * h2f(q[((int64_t)b * ly.Hq + g0 + g) * D + j]) : 0.0f;
     }
     _Float16 *ev = s_ev + wave * kEvWave;
     {
@@ -575,8 +608,8 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
     for (int nb = 0; nb < KB; ++nb) A.O[nb] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int nb = 0; nb < ND; ++nb) A.Ores[nb] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    A.Ol = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
     A.m_run = -INFINITY;
-    A.l_part = 0.0f;
     float *sR = &s_rk[wave][0][0];
     while (ta.valid) {
         cur.rem += kWaves;
@@ -605,12 +638,11 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
 
     // ---- merge the waves of this workgroup: each wave leaves its unscaled
     //      sums in its own (now idle) V-residual tile, then one barrier
-    float l_part = A.l_part;
-    l_part += __shfl_xor(l_part, 16, kWave);
-    l_part += __shfl_xor(l_part, 32, kWave);
-    if (lane < GQ) {
-        s_m[wave][lane] = A.m_run;
-        s_l[wave][lane] = l_part;
+    if (lane < GQ) s_m[wave][lane] = A.m_run;
+    if (c16 == 0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (4 * grp + j < GQ) s_l[wave][4 * grp + j] = A.Ol[j];
     }
     {
         float *part = reinterpret_cast<float *>(ev);            // [GQ][RMAX + D]
