@@ -36,7 +36,7 @@
 // wave's LDS reads and matrix-core products stream back to back; only the
 // tile's shape (its rank class) and its residual presence are branched on.
 // The running max may trail the true max by up to 8 (a factor 256) before
-// the accumulators are rescaled, so rescaling is rare.  The last workgroup
+// it moves, so probabilities stay well inside fp16.  The last workgroup
 // of a (sequence, KV head) to finish merges all partials.
 #include <hip/hip_runtime.h>
 
@@ -382,8 +382,11 @@ __device__ __forceinline__ void process_tile(const Tile &t, const TileData<kSlot
         for (int j = 0; j < 4; ++j) tmax = fmaxf(tmax, z[mb][j]);
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+    // (applied every tile with factor 1 when the max holds: a branch here
+    // makes the compiler shuttle every accumulator between two register
+    // ranges on the common path)
     const bool need = tmax > A.m_run + kMaxLag;
-    if (__any(need)) {
+    {
         const float new_m = need ? tmax : A.m_run;
         const float f = fast_exp2(A.m_run - new_m);
 #pragma unroll
@@ -757,22 +760,22 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
                                     __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();
-    if (tid < GQ) {
+    // wave g reduces head g: max, weights, normaliser
+    if (wave < GQ) {
+        const int g = wave;
         float M = -INFINITY;
-        for (int i = 0; i < S; ++i) M = fmaxf(M, s_w[tid * S + i]);
-        s_M[tid] = M;
-    }
-    __syncthreads();
-    for (int i = tid; i < GQ * S; i += kBlock) {
-        const float M = s_M[i / S];
-        s_w[i] = M == -INFINITY ? 0.0f : fast_exp2(s_w[i] - M);
-    }
-    __syncthreads();
-    if (tid < GQ) {
+        for (int sp = lane; sp < S; sp += kWave) M = fmaxf(M, s_w[g * S + sp]);
+        M = wave_max(M);
         float L = 0.0f;
-        for (int i = 0; i < S; ++i) L += s_w[tid * S + i] * s_pl[tid * S + i];
-        s_L[tid] = L;
+        for (int sp = lane; sp < S; sp += kWave) {
+            const float wgt = M == -INFINITY ? 0.0f : fast_exp2(s_w[g * S + sp] - M);
+            s_w[g * S + sp] = wgt;
+            L += wgt * s_pl[g * S + sp];
+        }
+        L = wave_sum(L);
+        if (lane == 0) s_L[g] = L;
     }
+    __syncthreads();
     float4_t accm = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int c = 0; c < kFirst; ++c) {
