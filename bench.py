@@ -45,7 +45,7 @@ def parse_args():
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample budget")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-graph", action="store_true", help="launch eagerly instead of graph replay")
-    p.add_argument("--kernel-reps", type=int, default=3)
+    p.add_argument("--kernel-reps", type=int, default=10)
     return p.parse_args()
 
 
@@ -188,22 +188,26 @@ def main():
     ms_per_step = elapsed_ms / K
     tok_s = B * K / (elapsed_ms / 1e3)
 
-    # ---- decode-kernel duration (events on the launch stream, queued behind a spin)
+    # ---- decode-kernel duration: every layer's launch back to back in one
+    #      graph, replayed; events on the launch stream around the replays
     counts = np.stack([cache.read_counts(l, B) for l in range(L)])     # [L][B][H][T]
     layer_bytes = [algorithmic_layer_bytes(cfg, counts[l]) for l in range(L)]
     step_bytes = sum(layer_bytes)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(L * args.kernel_reps)]
-    torch.cuda._sleep(int(3e8))
-    i = 0
-    for _ in range(args.kernel_reps):
+    kg = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(kg):
         for l in range(L):
-            ev[i][0].record()
             dwkv_decode_attn(h, l, q_dev[l], out_dev[l], ws, scale)
-            ev[i][1].record()
-            i += 1
+    kg.replay()
     torch.cuda.synchronize()
-    durs = np.array([a.elapsed_time(b) for a, b in ev]).reshape(args.kernel_reps, L)   # ms
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.kernel_reps)]
+    torch.cuda._sleep(int(3e8))
+    for a, b in ev:
+        a.record()
+        kg.replay()
+        b.record()
+    torch.cuda.synchronize()
+    durs = np.array([a.elapsed_time(b) for a, b in ev]) / L                              # ms per launch
     mean_launch_ms = float(durs.mean())
     bytes_per_launch = float(np.mean(layer_bytes))
     achieved = bytes_per_launch / (mean_launch_ms * 1e-3) / 1e9

@@ -101,13 +101,6 @@ __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlan
 // are irrelevant next to the >= 1 weight of the running max).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Orders LDS accesses of the lanes of one wave (a wave's LDS operations
-// execute in issue order, so this costs no instruction).
-__device__ __forceinline__ void wave_fence()
-{
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-}
-
 __device__ __forceinline__ uint32_t ld32(const uint8_t *p)
 {
     return *reinterpret_cast<const uint32_t *>(p);

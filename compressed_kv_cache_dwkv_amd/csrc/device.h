@@ -36,6 +36,13 @@ __device__ __forceinline__ float wave_max(float v)
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
+// Orders LDS accesses of the lanes of one wave (a wave's LDS operations
+// execute in issue order, so this costs no instruction).
+__device__ __forceinline__ void wave_fence()
+{
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+}
+
 __device__ __forceinline__ uint64_t lanemask_lt() { return (uint64_t(1) << lane_id()) - 1; }
 
 // Signed code u of a token's packed residual values (bits = 4 or 8).
