@@ -46,7 +46,63 @@ def parse_args():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-graph", action="store_true", help="launch eagerly instead of graph replay")
     p.add_argument("--kernel-reps", type=int, default=10)
+    p.add_argument("--copy-probe", action="store_true",
+                   help="also run a plain 512 MiB device copy (counter calibration)")
+    p.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                   help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this "
+                        "script with --copy-probe into profiles/ and exit")
     return p.parse_args()
+
+
+COPY_PROBE_BYTES = 512 << 20
+
+
+def _pmc_per_dispatch(run_dir: str, counter: str):
+    """{kernel name: [counter value per dispatch]} from a rocprofv3 csv run."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {run_dir}")
+    per = {}
+    for f in files:
+        for row in csv.DictReader(open(f)):
+            if row["Counter_Name"] != counter:
+                continue
+            key = (row["Kernel_Name"], row["Dispatch_Id"])
+            per[key] = per.get(key, 0.0) + float(row["Counter_Value"])
+    out = {}
+    for (name, _), v in per.items():
+        out.setdefault(name, []).append(v)
+    return out
+
+
+def pmc_summary(workload: str, fetch_dir: str, write_dir: str):
+    """HBM bytes per decode launch from FETCH_SIZE / WRITE_SIZE (KiB per
+    dispatch), each scaled by what the same counter reads for a plain copy
+    of COPY_PROBE_BYTES bytes in the same process."""
+    res = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        per = _pmc_per_dispatch(d, counter)
+        dec = [v for k, vs in per.items() if "decode_kernel" in k for v in vs]
+        cpy = [v for k, vs in per.items() if ("copyBuffer" in k or "copy" in k.lower()) and "decode" not in k
+               for v in vs]
+        cpy = [v for v in cpy if v * 1024 > COPY_PROBE_BYTES / 4]          # the probe, not small copies
+        if not dec or not cpy:
+            raise SystemExit(f"{counter}: decode dispatches {len(dec)}, copy-probe dispatches {len(cpy)}")
+        scale = COPY_PROBE_BYTES / (float(np.mean(cpy)) * 1024)
+        res[counter] = {"decode_kib_mean": float(np.mean(dec)), "decode_dispatches": len(dec),
+                        "copy_kib_mean": float(np.mean(cpy)), "copy_dispatches": len(cpy),
+                        "scale": scale, "bytes_per_launch": float(np.mean(dec)) * 1024 * scale}
+    total = res["FETCH_SIZE"]["bytes_per_launch"] + res["WRITE_SIZE"]["bytes_per_launch"]
+    rec = {"workload": workload, "kernel": "decode_kernel",
+           "decode_source_sha256": hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest(),
+           "hbm_bytes_per_launch": total, "counters": res,
+           "copy_probe_bytes": COPY_PROBE_BYTES}
+    os.makedirs(PROFILES, exist_ok=True)
+    path = os.path.join(PROFILES, f"decode_{workload}_traffic.json")
+    json.dump(rec, open(path, "w"), indent=1)
+    print(json.dumps(rec), flush=True)
 
 
 def _gen_layer_job(args):
@@ -111,6 +167,9 @@ def main():
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}), flush=True)
         sys.exit(2)
     cfg = w.get_config(args.config)
+    if args.pmc_summary:
+        pmc_summary(cfg.name, *args.pmc_summary)
+        return
     K = args.steps if args.steps is not None else cfg.bench_steps
     W = args.warmup
     L, B, H = cfg.num_layers, cfg.batch, cfg.num_kv_heads
@@ -251,6 +310,13 @@ def main():
         "paper_context": {"decode_tok_s_64k": 72.8, "kv_memory_reduction": 8.3,
                           "note": "end-to-end generation on unstated hardware and model; not comparable"},
     }
+    if args.copy_probe:
+        src = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, layers, bases, appends, args.cpu_seconds)
     else:
