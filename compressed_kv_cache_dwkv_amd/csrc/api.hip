@@ -19,12 +19,20 @@ struct dwkv_handle {
 
 namespace dwkv {
 
-// Decode work of a token beyond its bytes, in byte equivalents: a token's
-// residual gathers and softmax cost about as much time as streaming this
-// many bytes (measured on the 64K-token Llama-3-8B shape).  Splits balance
-// bytes plus this share, so tiers with few bytes per token are not
-// under-provisioned.
-constexpr int kTokenCost = 48;
+// Decode work of a token, in the unit splits are balanced on.  The decode
+// kernel cuts each tier into tiles of about 2 KiB of coefficients per K and
+// V (64 tokens at rank <= 16, 32 at rank 32, 16 at rank 64; twice that when
+// the basis is wider than 64).  Workgroup times on the 64K-token
+// Llama-3-8B shape fit a fixed cost per tile plus a small cost per token
+// (about 23:1 for a 64-token tile), whatever the rank: a token weighs its
+// share of a tile plus that per-token part.
+static int token_cost(int r, int r_max)
+{
+    const int slots = r_max <= 64 ? 4 : 8;                 // 16x16 operand blocks per tile
+    const int kbr = r <= 16 ? 1 : r <= 32 ? 2 : r <= 64 ? 4 : 8;
+    const int tokens_per_tile = 16 * (slots / kbr);
+    return 3072 / tokens_per_tile + 14;
+}
 constexpr int64_t kArenaTail = 8192;
 
 int build_layout(const dwkv_config *c, Layout *ly)
@@ -83,7 +91,7 @@ int build_layout(const dwkv_config *c, Layout *ly)
         ly->vstride[k] = vs;
         ly->cap[k] = c->tier_capacity[k];
         ly->weight[k] = 4 * r + (s > 0 ? 2 * (is + vs + 2) : 0);
-        ly->cost[k] = ly->weight[k] + kTokenCost;
+        ly->cost[k] = token_cost(r, c->r_max);
         ly->inv_cblk[k] = 1.0 / (16.0 * ly->cost[k]);
         blk = align_up(blk, 256);
         ly->f_coefK[k] = blk; blk = align_up(blk + cap * r * 2, 16);

@@ -13,7 +13,7 @@
 //
 // Work split (split-K "flash decode"): grid = (splits, KV heads, sequences),
 // one 8-wave workgroup per compute unit.  A workgroup takes a work-balanced
-// (bytes plus a fixed per-token share) run of 16-token blocks of the tier regions of its (sequence, KV head) and
+// (tile shares plus a little of the bytes) run of 16-token blocks of the tier regions of its (sequence, KV head) and
 // cuts it into tiles of about 2 KiB of coefficients per K and V (64 tokens
 // at rank <= 16, 32 at rank 32, 16 at rank 64 or more); wave w takes tiles
 // w, w + 8, ...  Each wave keeps its own online softmax (base-2 logits) and

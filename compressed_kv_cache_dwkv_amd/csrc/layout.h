@@ -66,8 +66,7 @@ struct Layout {
     int32_t istride[kMaxTiers];  // stored index bytes per token (s rounded up to 4)
     int32_t vstride[kMaxTiers];  // stored code bytes per token (vbytes rounded up to 4)
     int32_t weight[kMaxTiers];   // algorithmic bytes per token (K and V)
-    int32_t cost[kMaxTiers];     // decode work per token in byte equivalents: weight plus a
-                                 // fixed per-token share (residuals, softmax)
+    int32_t cost[kMaxTiers];     // decode work per token, the unit splits are balanced on
     double inv_cblk[kMaxTiers];  // 1 / (16 * cost): reciprocal of a 16-token block's cost
     int64_t cap[kMaxTiers];
     int64_t max_tokens;
