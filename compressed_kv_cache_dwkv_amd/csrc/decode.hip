@@ -121,24 +121,21 @@ __device__ __forceinline__ float code_at(uint32_t c0, uint32_t c1, int u, int bi
     return (float)(int)__builtin_amdgcn_sbfe((int)(pos < 32 ? c0 : c1), pos & 31, bits);
 }
 
-// Rotates a token's s <= 8 entries by `rot` positions.  Entries are stored
-// in ascending channel order; rotating by the lane number keeps the lanes of
-// a wave from visiting the same narrow band of channels at the same step.
-__device__ __forceinline__ void rotate_entries(uint32_t &i0, uint32_t &i1, uint32_t &c0, uint32_t &c1,
-                                               int s, int bits, int rot)
+// Partial results cross workgroups (and XCDs, whose L2s are not coherent
+// with each other) as agent-scope relaxed atomics, two floats per access.
+__device__ __forceinline__ void st_agent2(float *p, float x, float y)
 {
-    const uint32_t iw = 8u * s, cw = (uint32_t)bits * s;
-    const uint64_t imask = iw == 64 ? ~0ull : ((1ull << iw) - 1);
-    const uint64_t cmask = cw == 64 ? ~0ull : ((1ull << cw) - 1);
-    const uint64_t i64 = (((uint64_t)i1 << 32) | i0) & imask;
-    const uint64_t c64 = (((uint64_t)c1 << 32) | c0) & cmask;
-    const uint32_t ri = 8u * rot, rc = (uint32_t)bits * rot;
-    const uint64_t ni = rot ? ((i64 >> ri) | (i64 << (iw - ri))) & imask : i64;
-    const uint64_t nc = rot ? ((c64 >> rc) | (c64 << (cw - rc))) & cmask : c64;
-    i0 = (uint32_t)ni;
-    i1 = (uint32_t)(ni >> 32);
-    c0 = (uint32_t)nc;
-    c1 = (uint32_t)(nc >> 32);
+    const uint64_t v = ((uint64_t)__float_as_uint(y) << 32) | __float_as_uint(x);
+    __hip_atomic_store(reinterpret_cast<uint64_t *>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ float4_t ld_agent4(const float *p)
+{
+    uint64_t *q = reinterpret_cast<uint64_t *>(const_cast<float *>(p));
+    const uint64_t a = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t b = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return float4_t{__uint_as_float((uint32_t)a), __uint_as_float((uint32_t)(a >> 32)),
+                    __uint_as_float((uint32_t)b), __uint_as_float((uint32_t)(b >> 32))};
 }
 
 // floor(x / w) for 0 <= x < 2^52, w > 0, given inv_w ~ 1 / w: the estimate
@@ -697,8 +694,8 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
         }
         if (c16 < GQ) {
             float *po = ws.po + (((int64_t)b * ly.Hq + g0 + c16) * S + split) * D + 16 * wave + 4 * grp;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) __hip_atomic_store(po + j, acc[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            st_agent2(po, acc[0], acc[1]);
+            st_agent2(po + 2, acc[2], acc[3]);
         }
     }
     if (tid < GQ) {
@@ -738,10 +735,7 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
 #pragma unroll
     for (int c = 0; c < kFirst; ++c) {
         const int sp = part + c * parts;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            pc[c][j] = sp < S ? __hip_atomic_load(pob + (int64_t)sp * D + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                              : 0.0f;
+        pc[c] = sp < S ? ld_agent4(pob + (int64_t)sp * D) : float4_t{0.0f, 0.0f, 0.0f, 0.0f};
     }
     float *s_w = reinterpret_cast<float *>(s_ev);
     float *s_pl = s_w + GQ * S;
@@ -776,11 +770,7 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
         if (sp < S) accm += s_w[hq * S + sp] * pc[c];
     }
     for (int sp = part + kFirst * parts; sp < S; sp += parts) {
-        float4_t v;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            v[j] = __hip_atomic_load(pob + (int64_t)sp * D + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        accm += s_w[hq * S + sp] * v;
+        accm += s_w[hq * S + sp] * ld_agent4(pob + (int64_t)sp * D);
     }
     __syncthreads();
     float4_t *s_red = reinterpret_cast<float4_t *>(s_ev) + kMaxSplits * 2 * 8 / 4;   // [parts][quads]
