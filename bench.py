@@ -46,6 +46,8 @@ def parse_args():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-graph", action="store_true", help="launch eagerly instead of graph replay")
     p.add_argument("--kernel-reps", type=int, default=10)
+    p.add_argument("--separate", action="store_true",
+                   help="two launches per layer (dwkv_decode_attn, dwkv_append) instead of dwkv_decode_step")
     p.add_argument("--copy-probe", action="store_true",
                    help="also run a plain 512 MiB device copy (counter calibration)")
     p.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -113,13 +115,25 @@ def _gen_layer_job(args):
 def algorithmic_layer_bytes(cfg, counts: np.ndarray) -> int:
     """Bytes the method must move for one layer's decode: every cached token at
     its tier's size (fp16 coefficients at the routed rank, residual indices,
-    packed codes, scale; K and V), both bases of every KV head, q and out."""
+    packed codes, scale; K and V), both bases of every KV head (once: every
+    sequence shares them), q and out."""
     per_tok = np.array([w.compressed_bytes_per_token(r, s, cfg.resid_bits)
                         for r, s in zip(cfg.tier_rank, cfg.resid_per_tier)])
     tok = float((counts.reshape(-1, cfg.num_tiers) * per_tok[None, :]).sum())
-    bases = 2 * cfg.num_kv_heads * cfg.r_max * cfg.head_dim * 2 * counts.shape[0]
+    bases = 2 * cfg.num_kv_heads * cfg.r_max * cfg.head_dim * 2
     qo = cfg.batch * cfg.num_q_heads * cfg.head_dim * (2 + 4)
     return int(tok + bases + qo)
+
+
+def append_layer_bytes(cfg, tier: np.ndarray) -> int:
+    """Bytes one layer's append moves beyond the bases (which the decode in
+    the same launch reads): the new K and V and the tier per (b, KV head) in,
+    the encoded token, its tier count and its position-map entry out."""
+    per_tok = np.array([w.compressed_bytes_per_token(r, s, cfg.resid_bits)
+                        for r, s in zip(cfg.tier_rank, cfg.resid_per_tier)])
+    ins = tier.size * (2 * cfg.head_dim * 2 + 1)
+    outs = float(per_tok[tier.reshape(-1).astype(np.int64)].sum()) + tier.size * 8
+    return int(ins + outs)
 
 
 def stored_traffic(workload: str):
@@ -185,14 +199,15 @@ def main():
     print(f"bench: generated {cfg.name} in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
 
     import torch
-    from compressed_kv_cache_dwkv_amd import dwkv_append, dwkv_decode_attn
+    from compressed_kv_cache_dwkv_amd import dwkv_append, dwkv_decode_attn, dwkv_decode_step
     from compressed_kv_cache_dwkv_amd.cache import CompressedKVCache
 
     torch.cuda.set_device(0)
-    cap = [int(c) + W + K + 8 for c in max_tier_counts(cfg)]
+    extra = W + K + args.kernel_reps + 8        # appended tokens: steps and kernel timing
+    cap = [int(c) + extra for c in max_tier_counts(cfg)]
     cache = CompressedKVCache(L, cfg.layers_per_group, cfg.num_q_heads, H, cfg.head_dim, cfg.r_max,
                               cfg.tier_rank, cfg.resid_per_tier, cfg.resid_bits, B, cap,
-                              cfg.n_tokens + W + K + 8, decode_splits=args.splits)
+                              cfg.n_tokens + extra, decode_splits=args.splits)
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
     for m in range(cfg.num_groups):
         cache.set_basis(m, dev(bases["K"][m]), dev(bases["V"][m]))
@@ -211,10 +226,17 @@ def main():
     scale = 1.0 / math.sqrt(cfg.head_dim)
     print(f"bench: cache resident ({cache.arena.numel() / 1e9:.2f} GB arena)", file=sys.stderr, flush=True)
 
-    def step(s):
-        for l in range(L):
+    def layer_step(l, s):
+        if args.separate:
             dwkv_decode_attn(h, l, q_dev[l], out_dev[l], ws, scale)
             dwkv_append(h, l, k_dev[s, l], v_dev[s, l], t_dev[s, l])
+        else:
+            dwkv_decode_step(h, l, q_dev[l], out_dev[l], ws, k_dev[s, l], v_dev[s, l], t_dev[s, l],
+                             softmax_scale=scale)
+
+    def step(s):
+        for l in range(L):
+            layer_step(l, s)
 
     for s in range(W):
         step(s)
@@ -247,15 +269,22 @@ def main():
     ms_per_step = elapsed_ms / K
     tok_s = B * K / (elapsed_ms / 1e3)
 
-    # ---- decode-kernel duration: every layer's launch back to back in one
-    #      graph, replayed; events on the launch stream around the replays
+    # ---- decode-kernel duration: every layer's launch of the step (with
+    #      its append unless --separate) back to back in one graph, replayed;
+    #      events on the launch stream around the replays
     counts = np.stack([cache.read_counts(l, B) for l in range(L)])     # [L][B][H][T]
-    layer_bytes = [algorithmic_layer_bytes(cfg, counts[l]) for l in range(L)]
-    step_bytes = sum(layer_bytes)
+    app_bytes = [0 if args.separate else append_layer_bytes(cfg, appends[W + K - 1][l]["tier"])
+                 for l in range(L)]
+    layer_bytes = [algorithmic_layer_bytes(cfg, counts[l]) + app_bytes[l] for l in range(L)]
+    step_bytes = sum(algorithmic_layer_bytes(cfg, counts[l]) +
+                     append_layer_bytes(cfg, appends[W + K - 1][l]["tier"]) for l in range(L))
     kg = torch.cuda.CUDAGraph()
     with torch.cuda.graph(kg):
         for l in range(L):
-            dwkv_decode_attn(h, l, q_dev[l], out_dev[l], ws, scale)
+            if args.separate:
+                dwkv_decode_attn(h, l, q_dev[l], out_dev[l], ws, scale)
+            else:
+                layer_step(l, W + K - 1)
     kg.replay()
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -266,6 +295,7 @@ def main():
         kg.replay()
         b.record()
     torch.cuda.synchronize()
+    assert cache.check_errors() == 0, "kernel timing overflowed the cache"
     durs = np.array([a.elapsed_time(b) for a, b in ev]) / L                              # ms per launch
     mean_launch_ms = float(durs.mean())
     bytes_per_launch = float(np.mean(layer_bytes))
@@ -294,6 +324,7 @@ def main():
             "resid_channels": cfg.resid_channels, "resid_bits": cfg.resid_bits,
             "storage": "fp16 coefficients, uint8 channel indices, packed codes, fp16 scales",
             "graph_replay": bool(graphs),
+            "launches_per_layer": 2 if args.separate else 1,
         },
         "step_GBps": step_bytes / (ms_per_step * 1e-3) / 1e9,
         "step_frac_of_peak": step_bytes / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBPS,

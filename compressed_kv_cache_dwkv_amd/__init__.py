@@ -83,6 +83,7 @@ _SIGS = {
     "dwkv_workspace_bytes": [ctypes.POINTER(dwkv_config), _I, ctypes.POINTER(ctypes.c_size_t)],
     "dwkv_decode_attn": [_P, _I, _P, _I, ctypes.c_float, _P, _P, ctypes.c_size_t, _P],
     "dwkv_append": [_P, _I, _P, _P, _P, _P, _P, _I, _P],
+    "dwkv_decode_step": [_P, _I, _P, _I, ctypes.c_float, _P, _P, ctypes.c_size_t, _P, _P, _P, _P, _P, _P],
     "dwkv_check_errors": [_P, _P, ctypes.POINTER(ctypes.c_uint32)],
     "dwkv_clear_errors": [_P, _P],
 }
@@ -264,6 +265,28 @@ def dwkv_append(h, layer: int, k, v, tier, gateK=None, gateV=None, stream=None) 
                             _ptr(gateK, torch.float16, (B, H), name="gateK"),
                             _ptr(gateV, torch.float16, (B, H), name="gateV"), B, _stream(stream)),
            "dwkv_append")
+
+
+def dwkv_decode_step(h, layer: int, q, out, workspace, k, v, tier, gateK=None, gateV=None,
+                     softmax_scale: Optional[float] = None, stream=None) -> None:
+    """dwkv_decode_attn(q) then dwkv_append(k, v, tier, gates) in one launch.
+    q: fp16 [B][H_q][d]; out: fp32 [B][H_q][d]; k, v: fp16 [B][H_kv][d];
+    tier: uint8 [B][H_kv]; gates: fp16 [B][H_kv] or None."""
+    import torch
+    B, Hq, d = q.shape
+    H = k.shape[1] if k.dim() == 3 else -1
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    ws = workspace.numel() * workspace.element_size()
+    _check(_lib.dwkv_decode_step(h, layer, _ptr(q, torch.float16, name="q"), B, float(softmax_scale),
+                                 _ptr(out, torch.float32, (B, Hq, d), name="out"),
+                                 _ptr(workspace, name="workspace"), ws,
+                                 _ptr(k, torch.float16, (B, H, d), name="k"),
+                                 _ptr(v, torch.float16, (B, H, d), name="v"),
+                                 _ptr(tier, torch.uint8, (B, H), name="tier"),
+                                 _ptr(gateK, torch.float16, (B, H), name="gateK"),
+                                 _ptr(gateV, torch.float16, (B, H), name="gateV"), _stream(stream)),
+           "dwkv_decode_step")
 
 
 def dwkv_check_errors(h, stream=None) -> int:

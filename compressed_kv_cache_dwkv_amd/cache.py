@@ -8,7 +8,7 @@ from typing import Dict, Optional, Sequence
 import torch
 
 from . import (dwkv_append, dwkv_arena_bytes, dwkv_check_errors, dwkv_clear_errors, dwkv_create,
-               dwkv_decode_attn, dwkv_destroy, dwkv_export_layer, dwkv_import_layer,
+               dwkv_decode_attn, dwkv_decode_step, dwkv_destroy, dwkv_export_layer, dwkv_import_layer,
                dwkv_read_counts, dwkv_reset, dwkv_set_basis, dwkv_workspace_bytes, make_config)
 
 
@@ -79,6 +79,18 @@ class CompressedKVCache:
     def append(self, layer: int, k: torch.Tensor, v: torch.Tensor, tier: torch.Tensor,
                gateK: Optional[torch.Tensor] = None, gateV: Optional[torch.Tensor] = None) -> None:
         dwkv_append(self.handle, layer, k, v, tier, gateK, gateV)
+
+    def decode_step(self, layer: int, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                    tier: torch.Tensor, gateK: Optional[torch.Tensor] = None,
+                    gateV: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                    softmax_scale: Optional[float] = None) -> torch.Tensor:
+        """decode(q) over the cache as it stands, then append(k, v, tier), in one launch."""
+        B = q.shape[0]
+        if out is None:
+            out = torch.empty((B, self.num_q_heads, self.head_dim), dtype=torch.float32, device=self.device)
+        dwkv_decode_step(self.handle, layer, q, out, self.workspace(B), k, v, tier, gateK, gateV,
+                         softmax_scale if softmax_scale is not None else 1.0 / math.sqrt(self.head_dim))
+        return out
 
     # ------------------------------------------------------------------ errors
     def check_errors(self) -> int:

@@ -333,7 +333,28 @@ int dwkv_decode_attn(dwkv_handle *h, int layer, const void *q, int batch, float 
     hipStream_t s = static_cast<hipStream_t>(stream);
     dwkv::DecodeWorkspace ws = dwkv::carve_workspace(ly, workspace, batch, h->splits);
     return hip_status(
-        dwkv::launch_decode(ly, h->arena, layer, q, batch, softmax_scale, out, ws, h->splits, s));
+        dwkv::launch_decode(ly, h->arena, layer, q, batch, softmax_scale, out, ws, h->splits, nullptr, s));
+}
+
+int dwkv_decode_step(dwkv_handle *h, int layer, const void *q, int batch, float softmax_scale,
+                     float *out, void *workspace, size_t workspace_bytes, const void *k,
+                     const void *v, const void *tier, const void *gateK, const void *gateV,
+                     void *stream)
+{
+    if (!valid_handle(h) || !q || !out || !workspace || !k || !v || !tier) return DWKV_ERR_INVALID_ARG;
+    const Layout &ly = h->ly;
+    if (layer < 0 || layer >= ly.L || batch <= 0 || batch > ly.Bmax) return DWKV_ERR_INVALID_ARG;
+    if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale)) return DWKV_ERR_INVALID_ARG;
+    if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return DWKV_ERR_INVALID_ARG;
+    if (workspace_bytes < dwkv::decode_workspace_bytes(ly, batch, h->splits))
+        return DWKV_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    dwkv::DecodeWorkspace ws = dwkv::carve_workspace(ly, workspace, batch, h->splits);
+    const dwkv::AppendArgs ap{static_cast<const uint16_t *>(k), static_cast<const uint16_t *>(v),
+                              static_cast<const uint8_t *>(tier), static_cast<const uint16_t *>(gateK),
+                              static_cast<const uint16_t *>(gateV)};
+    return hip_status(
+        dwkv::launch_decode(ly, h->arena, layer, q, batch, softmax_scale, out, ws, h->splits, &ap, s));
 }
 
 int dwkv_append(dwkv_handle *h, int layer, const void *k, const void *v, const void *tier,

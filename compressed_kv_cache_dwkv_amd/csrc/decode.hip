@@ -42,6 +42,7 @@
 
 #include <cmath>
 
+#include "append_body.h"
 #include "device.h"
 #include "kernels.h"
 #include "layout.h"
@@ -60,6 +61,10 @@ constexpr int kEvRows = kMaxHeadDim + 1;  // channel rows plus one row that abso
 constexpr int kEvWave = (kEvRows * kEvStride + 7) / 8 * 8;   // fp16 per wave, 16-byte multiple
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kMaxLag = 8.0f;           // log2 units the running max may trail
+// The append's encoding, done by the first workgroup of each (sequence, KV
+// head) before its share of the tiles, in the units of the work balance
+// (per 16-token block: 16 x the tier's per-token cost).
+constexpr int64_t kEncodeUnits = 80000;
 
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
@@ -474,7 +479,7 @@ template <int GQ, int KB, int D>
 __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *arena, int layer,
                                                            const uint16_t *q, float *out,
                                                            DecodeWorkspace ws, int S, double invS,
-                                                           float qscale)
+                                                           float qscale, AppendArgs ap)
 {
     constexpr int GP = GQ < 4 ? 4 : GQ;           // query heads padded for 16-byte gathers
     constexpr int NS = kSlots * (KB / 4);          // operand slots per tile and Z
@@ -514,6 +519,14 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
         for (int kb = 0; kb < ND; ++kb)
             ak[kb] = *reinterpret_cast<const half4_t *>(BK + (int64_t)row * D + 16 * kb + 4 * grp);
     }
+    // With new tokens to append, waves 0 and 1 of the first workgroup of
+    // each (sequence, KV head) encode them while the workgroup waits for its
+    // first tiles; the token goes to its slot past the tier's counted tokens,
+    // which no tile of this launch uses, and the last workgroup publishes it.
+    const bool appending = ap.k != nullptr;
+    const bool encoder = appending && split == 0;
+    AppendRegs<D> app;
+    if (encoder && wave < 2) append_fetch<D>(app, ly, arena, layer, b, h, wave, lane, ap);
 
     // ---- this workgroup's work-balanced run of 16-token blocks: lane k
     //      works out and keeps tier k's range
@@ -534,8 +547,13 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
             if (lane > k) wk_l += wt;
             W += wt;
         }
-        const int64_t lo = div_floor(W * split, S, invS);
-        const int64_t hi = div_floor(W * (split + 1), S, invS);
+        // the encoding workgroup starts its share later: its boundaries
+        // move down by the encoding's cost in balance units
+        const int64_t E = appending ? kEncodeUnits : 0;
+        int64_t lo = div_floor((W + E) * split, S, invS) - E;
+        int64_t hi = div_floor((W + E) * (split + 1), S, invS) - E;
+        lo = lo > 0 ? lo : 0;
+        hi = hi > 0 ? hi : 0;
         const int64_t x0 = lo - wk_l, x1 = hi - wk_l;
         int64_t b0 = x0 <= 0 || !on ? 0 : div_floor(x0 + wb_l - 1, wb_l, ly.inv_cblk[kl]);
         int64_t b1 = x1 <= 0 || !on ? 0 : div_floor(x1 + wb_l - 1, wb_l, ly.inv_cblk[kl]);
@@ -563,7 +581,9 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
         s_qt[j][g] = g < GQ && j < D ? qscale * h2f(q[((int64_t)b * ly.Hq + g0 + g) * D + j]) : 0.0f;
     }
     _Float16 *ev = s_ev + wave * kEvWave;
-    {
+    constexpr int kAppendTiles = 4;                 // V-residual tiles the append scratch covers
+    static_assert(kAppendLdsBytes <= kAppendTiles * kEvWave * sizeof(_Float16), "append scratch");
+    if (!(encoder && wave < kAppendTiles)) {
         uint4 *e4 = reinterpret_cast<uint4 *>(ev);
         for (int i = lane; i < kEvWave / 8; i += kWave) e4[i] = uint4{0u, 0u, 0u, 0u};
     }
@@ -589,7 +609,20 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
         }
         s_qb[wave * kWave + lane] = v;
     }
+    if (encoder && wave < 2) {
+        int slot, n;
+        append_encode<D>(app, ly, arena, layer, b, h, wave, lane, ap, carve_append_lds(s_ev), slot, n);
+    }
     __syncthreads();
+    if (encoder && wave < 2) {
+        // both encodings are done: clear the V-residual tiles of waves 0..3
+        // the append scratch spanned
+#pragma unroll
+        for (int t = 0; t < kAppendTiles / 2; ++t) {
+            uint4 *e4 = reinterpret_cast<uint4 *>(s_ev + (wave + 2 * t) * kEvWave);
+            for (int i = lane; i < kEvWave / 8; i += kWave) e4[i] = uint4{0u, 0u, 0u, 0u};
+        }
+    }
     half4_t qb[KB];
 #pragma unroll
     for (int mb = 0; mb < KB; ++mb) qb[mb] = s_qb[mb * kWave + lane];
@@ -718,6 +751,15 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
     }
     __syncthreads();
     if (!s_last) return;
+    // every workgroup of this (sequence, KV head) has read the token counts:
+    // the appended token can be published (its tier from the same input and
+    // the counts this workgroup read, so admission matches the encoder's)
+    if (appending && wave == 0) {
+        const int k = __builtin_amdgcn_readfirstlane(ap.tier[b * ly.Hkv + h]);
+        int slot, n;
+        if (append_admit(ly, k, rg.cnt, slot, n) == 0 && lane == 0)
+            append_commit(ly, arena, layer, b, h, k, slot, n);
+    }
     // Each thread owns 4 adjacent outputs of one head and an interleaved
     // subset of the splits.  Its first 8 partial vectors are requested
     // together with every split's max and normaliser, so the merge waits
@@ -727,7 +769,7 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
     constexpr int parts = kBlock / quads;
     constexpr int kFirst = 8;
     static_assert(kBlock % quads == 0, "merge layout");
-    static_assert((2 * kMaxSplits * 8 + kBlock * 4) * 4 <= kWaves * kEvWave * 2, "merge scratch");
+    static_assert((2 * kMaxSplits * 8 + kBlock * 4) * 4 <= sizeof(s_ev), "merge scratch");
     const int qd = tid % quads, part = tid / quads;
     const int hq = (4 * qd) / D, j4 = (4 * qd) % D;
     const float *pob = ws.po + ((int64_t)b * ly.Hq + g0 + hq) * S * D + j4;
@@ -788,28 +830,30 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
 
 template <int GQ, int D>
 hipError_t launch_gq(const Layout &ly, uint8_t *arena, int layer, const uint16_t *q, int batch,
-                     float qs, float *out, const DecodeWorkspace &ws, int splits, hipStream_t stream)
+                     float qs, float *out, const DecodeWorkspace &ws, int splits, const AppendArgs &ap,
+                     hipStream_t stream)
 {
     const dim3 grid(splits, ly.Hkv, batch);
     const double inv = 1.0 / splits;
     if (ly.R <= 64)
         hipLaunchKernelGGL((decode_kernel<GQ, 4, D>), grid, dim3(kBlock), 0, stream, ly, arena, layer, q, out,
-                           ws, splits, inv, qs);
+                           ws, splits, inv, qs, ap);
     else
         hipLaunchKernelGGL((decode_kernel<GQ, 8, D>), grid, dim3(kBlock), 0, stream, ly, arena, layer, q, out,
-                           ws, splits, inv, qs);
+                           ws, splits, inv, qs, ap);
     return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_d(const Layout &ly, uint8_t *arena, int layer, const uint16_t *q, int batch,
-                    float qs, float *out, const DecodeWorkspace &ws, int splits, hipStream_t stream)
+                    float qs, float *out, const DecodeWorkspace &ws, int splits, const AppendArgs &ap,
+                    hipStream_t stream)
 {
     switch (ly.gq) {
-    case 1: return launch_gq<1, D>(ly, arena, layer, q, batch, qs, out, ws, splits, stream);
-    case 2: return launch_gq<2, D>(ly, arena, layer, q, batch, qs, out, ws, splits, stream);
-    case 4: return launch_gq<4, D>(ly, arena, layer, q, batch, qs, out, ws, splits, stream);
-    case 8: return launch_gq<8, D>(ly, arena, layer, q, batch, qs, out, ws, splits, stream);
+    case 1: return launch_gq<1, D>(ly, arena, layer, q, batch, qs, out, ws, splits, ap, stream);
+    case 2: return launch_gq<2, D>(ly, arena, layer, q, batch, qs, out, ws, splits, ap, stream);
+    case 4: return launch_gq<4, D>(ly, arena, layer, q, batch, qs, out, ws, splits, ap, stream);
+    case 8: return launch_gq<8, D>(ly, arena, layer, q, batch, qs, out, ws, splits, ap, stream);
     default: return hipErrorInvalidValue;
     }
 }
@@ -818,13 +862,15 @@ hipError_t launch_d(const Layout &ly, uint8_t *arena, int layer, const uint16_t 
 
 hipError_t launch_decode(const Layout &ly, uint8_t *arena, int layer, const void *q, int batch,
                          float softmax_scale, float *out, const DecodeWorkspace &ws, int splits,
-                         hipStream_t stream)
+                         const AppendArgs *ap, hipStream_t stream)
 {
     const float qs = softmax_scale * kLog2e;
     const uint16_t *qq = static_cast<const uint16_t *>(q);
+    const AppendArgs none{nullptr, nullptr, nullptr, nullptr, nullptr};
+    const AppendArgs &a = ap ? *ap : none;
     (void)hipGetLastError();  // drop errors left by earlier, unrelated calls
-    if (ly.d == 64) return launch_d<64>(ly, arena, layer, qq, batch, qs, out, ws, splits, stream);
-    if (ly.d == 128) return launch_d<128>(ly, arena, layer, qq, batch, qs, out, ws, splits, stream);
+    if (ly.d == 64) return launch_d<64>(ly, arena, layer, qq, batch, qs, out, ws, splits, a, stream);
+    if (ly.d == 128) return launch_d<128>(ly, arena, layer, qq, batch, qs, out, ws, splits, a, stream);
     return hipErrorInvalidValue;
 }
 

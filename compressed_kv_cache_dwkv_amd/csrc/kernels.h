@@ -18,12 +18,23 @@ struct DecodeWorkspace {
     float *po;          // [B][Hq][S][d]
 };
 
+// Inputs of one append call (device pointers).
+struct AppendArgs {
+    const uint16_t *k, *v;          // fp16 [B][Hkv][d]
+    const uint8_t *tier;            // [B][Hkv], the router's rank tier
+    const uint16_t *gateK, *gateV;  // fp16 [B][Hkv], or null for a gate of 1
+};
+
 size_t decode_workspace_bytes(const Layout &ly, int batch, int splits);
 DecodeWorkspace carve_workspace(const Layout &ly, void *ws, int batch, int splits);
 
+// Decode attention of one layer; with `ap` non-null the same launch also
+// appends the new tokens: the first workgroup of each (sequence, KV head)
+// encodes them into their slots, the last publishes them once every
+// workgroup of that head has read the token counts.
 hipError_t launch_decode(const Layout &ly, uint8_t *arena, int layer, const void *q, int batch,
                          float softmax_scale, float *out, const DecodeWorkspace &ws, int splits,
-                         hipStream_t stream);
+                         const AppendArgs *ap, hipStream_t stream);
 
 hipError_t launch_append(const Layout &ly, uint8_t *arena, int layer, const void *k,
                          const void *v, const void *tier, const void *gateK, const void *gateV,

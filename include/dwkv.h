@@ -210,6 +210,26 @@ int dwkv_decode_attn(dwkv_handle *h, int layer, const void *q, int batch, float 
 int dwkv_append(dwkv_handle *h, int layer, const void *k, const void *v, const void *tier,
                 const void *gateK, const void *gateV, int batch, void *stream);
 
+/*
+ * One whole decode step of a layer in a single launch: exactly
+ * dwkv_decode_attn(q) over the cache as it stands, then dwkv_append(k, v,
+ * tier, gates) -- the order of the zhichai.net summary's decode procedure
+ * (Ch. 1.2: attend over the cached keys and values, then append the new
+ * token's).  The cache afterwards is bit-identical to what the two calls
+ * made in sequence leave; the attention output equals theirs up to
+ * rounding (the tiles are split differently among workgroups, and each
+ * rounds its probabilities to fp16 against its own running max).  For each (b, KV
+ * head) the first decode workgroup encodes the new token into its slot past
+ * the tier's counted tokens before taking a smaller share of the tiles, and
+ * the workgroup that finishes last publishes it (tier count, position map)
+ * once every workgroup of that head has read the counts.  Arguments,
+ * layouts, errors and the workspace as for the two calls.
+ */
+int dwkv_decode_step(dwkv_handle *h, int layer, const void *q, int batch, float softmax_scale,
+                     float *out, void *workspace, size_t workspace_bytes, const void *k,
+                     const void *v, const void *tier, const void *gateK, const void *gateV,
+                     void *stream);
+
 /* Synchronises the stream; returns DWKV_ERR_DEVICE if the device error word
  * is set (its bits in *bits if non-NULL), else DWKV_OK. */
 int dwkv_check_errors(dwkv_handle *h, void *stream, uint32_t *bits);

@@ -68,3 +68,25 @@ def rel_err(a: np.ndarray, ref: np.ndarray) -> float:
     num = np.abs(a - ref).max(axis=-1)
     den = np.maximum(np.abs(ref).max(axis=-1), 1e-30)
     return float((num / den).max())
+
+
+def extend_layer(lay: dict, enc: dict, tier: np.ndarray, n: int) -> dict:
+    """The logical layer `lay` (n tokens per sequence) with the oracle's
+    encoding `enc` of one appended token per (b, KV head) at position n."""
+    out = {}
+    for key, v in lay.items():
+        if key == "n_tokens":
+            out[key] = v + 1
+            continue
+        shape = list(v.shape)
+        shape[2] += 1
+        nv = np.zeros(shape, v.dtype)
+        nv[:, :, :n] = v
+        out[key] = nv
+    out["tier"][:, :, n] = tier
+    for z in "KV":
+        out["coef" + z][:, :, n] = enc["coef" + z]
+        out["idx" + z][:, :, n] = enc["idx" + z]
+        out["val" + z][:, :, n] = enc["val" + z]
+        out["scale" + z][:, :, n] = enc["scale" + z]
+    return out

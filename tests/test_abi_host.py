@@ -97,6 +97,20 @@ def test_create_and_call_validation_without_gpu():
         assert L.dwkv_decode_attn(h, 0, None, 1, 0.1, out, wsp, ws, None) == d.DWKV_ERR_INVALID_ARG
         assert L.dwkv_decode_attn(h, 0, q, 1, 0.1, out, ctypes.c_void_p((1 << 43) + 8), ws,
                                   None) == d.DWKV_ERR_INVALID_ARG
+        # fused step: the decode checks plus the append inputs
+        kk = ctypes.c_void_p(1 << 44)
+        assert L.dwkv_decode_step(h, 0, q, 1, 0.1, out, wsp, ws, None, kk, kk, None, None,
+                                  None) == d.DWKV_ERR_INVALID_ARG
+        assert L.dwkv_decode_step(h, 0, q, 1, 0.1, out, wsp, ws, kk, kk, None, None, None,
+                                  None) == d.DWKV_ERR_INVALID_ARG
+        assert L.dwkv_decode_step(h, 32, q, 1, 0.1, out, wsp, ws, kk, kk, kk, None, None,
+                                  None) == d.DWKV_ERR_INVALID_ARG
+        assert L.dwkv_decode_step(h, 0, q, 1, 0.0, out, wsp, ws, kk, kk, kk, None, None,
+                                  None) == d.DWKV_ERR_INVALID_ARG
+        assert L.dwkv_decode_step(h, 0, q, 2, 0.1, out, wsp, ws - 1, kk, kk, kk, None, None,
+                                  None) == d.DWKV_ERR_WORKSPACE
+        assert L.dwkv_decode_step(h, 0, q, 1, 0.1, out, ctypes.c_void_p((1 << 43) + 8), ws, kk, kk, kk,
+                                  None, None, None) == d.DWKV_ERR_INVALID_ARG
         # append
         assert L.dwkv_append(h, 0, q, None, q, None, None, 1, None) == d.DWKV_ERR_INVALID_ARG
         assert L.dwkv_append(h, 40, q, q, q, None, None, 1, None) == d.DWKV_ERR_INVALID_ARG

@@ -9,7 +9,7 @@ import pytest
 import oracle
 import workload as w
 from workload.gen import gen_append_inputs, gen_layer, gen_query, make_bases
-from tests.helpers import tiny_config
+from tests.helpers import extend_layer, tiny_config
 
 pytestmark = pytest.mark.gpu
 
@@ -179,32 +179,12 @@ def test_attend_then_append_and_append_then_attend(G):
         got1 = G.decode_np(cache, 1, q)
         enc = oracle.append_layer(cfg, bases["K"][0], bases["V"][0], a["k"], a["v"], a["tier"])
         n = cfg.n_tokens
-        lay2 = wg_extend(lay, enc, a["tier"], n)
+        lay2 = extend_layer(lay, enc, a["tier"], n)
         ref1 = oracle.decode(cfg, lay2, bases["K"][0], bases["V"][0], q)
         assert G.norm_err(got1, ref1).max() <= 2e-3
         assert not np.allclose(ref0, ref1)
     finally:
         cache.close()
-
-
-def wg_extend(lay, enc, tier, n):
-    out = {}
-    for key, v in lay.items():
-        if key == "n_tokens":
-            out[key] = v + 1
-            continue
-        shape = list(v.shape)
-        shape[2] += 1
-        nv = np.zeros(shape, v.dtype)
-        nv[:, :, :n] = v
-        out[key] = nv
-    out["tier"][:, :, n] = tier
-    for z in "KV":
-        out["coef" + z][:, :, n] = enc["coef" + z]
-        out["idx" + z][:, :, n] = enc["idx" + z]
-        out["val" + z][:, :, n] = enc["val" + z]
-        out["scale" + z][:, :, n] = enc["scale" + z]
-    return out
 
 
 def test_full_tier_sets_device_error_and_drops_token(G):
