@@ -69,6 +69,14 @@ constexpr int64_t kEncodeUnits = 80000;
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// The fp16 values of v whose 16-bit lanes of (m0, m1) are ones; the others 0.
+__device__ __forceinline__ half4_t keep_h4(half4_t v, uint32_t m0, uint32_t m1)
+{
+    const u32x2_t b = __builtin_bit_cast(u32x2_t, v);
+    return __builtin_bit_cast(half4_t, u32x2_t{b[0] & m0, b[1] & m1});
+}
 
 __device__ __forceinline__ float4_t mma16(half4_t a, half4_t b, float4_t c)
 {
@@ -105,11 +113,6 @@ __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlan
 // 2^x on the transcendental unit (no denormal fix-up: results below 2^-126
 // are irrelevant next to the >= 1 weight of the running max).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-__device__ __forceinline__ uint32_t ld32(const uint8_t *p)
-{
-    return *reinterpret_cast<const uint32_t *>(p);
-}
 
 // Index byte u (0..7) of a token's residual record.
 __device__ __forceinline__ int idx_at(uint32_t i0, uint32_t i1, int u)
@@ -215,62 +218,75 @@ __device__ __forceinline__ Tile locate(const Ranges &rg, Cursor &cur, const Layo
     return t;
 }
 
+// Buffer resource over `bytes` bytes at p (a wave-uniform address).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const uint8_t *p, int64_t bytes)
+{
+    const uint64_t a = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    void *u = reinterpret_cast<void *>(((uint64_t)hi << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(u, (short)0, __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000);
+}
+
 // Issues every load of a tile: always the same number of load instructions,
 // so the compiler's wait counts stay exact and the next tile's loads are
-// never waited for while the current tile is computed.  Addresses are a
-// wave-uniform base per operand slot plus one 32-bit lane offset per tile.
-// Slots and lanes past the tile's valid tokens or its rank still read
-// inside the arena (which ends in a spare tail for this) and their values
-// are zeroed where they are used.
+// never waited for while the current tile is computed.  The loads are
+// buffer loads on the (layer, sequence, KV head) block: a 32-bit lane offset
+// plus a wave-uniform offset per operand slot, so a tile costs almost no
+// vector address arithmetic.  Slots and lanes past the tile's valid tokens
+// or its rank read other bytes of the block, or zeros past its end; their
+// values are zeroed where they are used.
 template <int NS>
-__device__ __forceinline__ void issue_tile(const Tile &t, TileData<NS> &D, const uint8_t *blk,
+__device__ __forceinline__ void issue_tile(const Tile &t, TileData<NS> &D, __amdgpu_buffer_rsrc_t rb,
                                            const Layout &ly, int lane)
 {
     const int c16 = lane & 15, grp = lane >> 4;
     const TierDesc &td = ly.tier[t.k];
     const int r = t.r, kbr = t.kbr;
-    const int64_t tok0 = (int64_t)t.blk0 * 16;
+    const uint32_t tok0 = (uint32_t)t.blk0 * 16u;
     // K: token rows of r fp16; V: 16-token blocks of r rows x 16 tokens --
     // both start r fp16 per token into their arrays
-    const uint8_t *cK = blk + td.coefK + tok0 * r * 2;
-    const uint8_t *cV = blk + td.coefV + tok0 * r * 2;
+    const uint32_t sK = (uint32_t)td.coefK + tok0 * (uint32_t)r * 2u;
+    const uint32_t sV = (uint32_t)td.coefV + tok0 * (uint32_t)r * 2u;
     const uint32_t kl = (uint32_t)(c16 * r + 4 * grp) * 2u;     // token c16, channels 4grp..
     const uint32_t vl = (uint32_t)(c16 * 16 + 4 * grp) * 2u;    // channel c16, tokens 4grp..
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
         const int mb = i / kbr, kb = i - mb * kbr;
-        D.ka[i] = *reinterpret_cast<const half4_t *>(cK + (16 * mb * r + 16 * kb) * 2 + kl);
-        D.va[i] = *reinterpret_cast<const half4_t *>(cV + (mb * r + 16 * kb) * 32 + vl);
+        D.ka[i] = __builtin_bit_cast(
+            half4_t, __builtin_amdgcn_raw_buffer_load_b64(rb, kl, sK + (uint32_t)(16 * mb * r + 16 * kb) * 2u, 0));
+        D.va[i] = __builtin_bit_cast(
+            half4_t, __builtin_amdgcn_raw_buffer_load_b64(rb, vl, sV + (uint32_t)(mb * r + 16 * kb) * 32u, 0));
     }
     // residual records of token `lane` (token 0's for lanes past the tile:
-    // their indices must stay valid)
+    // their indices must stay valid); a record's two words in one load
     const uint32_t tl = lane < t.nv ? (uint32_t)lane : 0u;
     const uint32_t io = tl * (uint32_t)td.istride, vo = tl * (uint32_t)td.vstride;
-    const uint8_t *iK = blk + td.idxK + tok0 * td.istride;
-    const uint8_t *vK = blk + td.valK + tok0 * td.vstride;
-    const uint8_t *iV = blk + td.idxV + tok0 * td.istride;
-    const uint8_t *vV = blk + td.valV + tok0 * td.vstride;
+    const u32x2_t ki = __builtin_amdgcn_raw_buffer_load_b64(rb, io, (uint32_t)td.idxK + tok0 * (uint32_t)td.istride, 0);
+    const u32x2_t kc = __builtin_amdgcn_raw_buffer_load_b64(rb, vo, (uint32_t)td.valK + tok0 * (uint32_t)td.vstride, 0);
+    const u32x2_t vi = __builtin_amdgcn_raw_buffer_load_b64(rb, io, (uint32_t)td.idxV + tok0 * (uint32_t)td.istride, 0);
+    const u32x2_t vc = __builtin_amdgcn_raw_buffer_load_b64(rb, vo, (uint32_t)td.valV + tok0 * (uint32_t)td.vstride, 0);
     // scales: the aligned 4-byte word holding this token's fp16 (tok0 is even)
     const uint32_t so = (tl & ~1u) * 2u, sh = 16u * (tl & 1u);
-    D.ki0 = ld32(iK + io);
-    D.ki1 = ld32(iK + io + 4);
-    D.kc0 = ld32(vK + vo);
-    D.kc1 = ld32(vK + vo + 4);
-    D.ksc = ld32(blk + td.scaleK + tok0 * 2 + so) >> sh;
-    D.vi0 = ld32(iV + io);
-    D.vi1 = ld32(iV + io + 4);
-    D.vc0 = ld32(vV + vo);
-    D.vc1 = ld32(vV + vo + 4);
-    D.vsc = ld32(blk + td.scaleV + tok0 * 2 + so) >> sh;
+    D.ksc = __builtin_amdgcn_raw_buffer_load_b32(rb, so, (uint32_t)td.scaleK + tok0 * 2u, 0) >> sh;
+    D.vsc = __builtin_amdgcn_raw_buffer_load_b32(rb, so, (uint32_t)td.scaleV + tok0 * 2u, 0) >> sh;
+    D.ki0 = ki[0];
+    D.ki1 = ki[1];
+    D.kc0 = kc[0];
+    D.kc1 = kc[1];
+    D.vi0 = vi[0];
+    D.vi1 = vi[1];
+    D.vc0 = vc[0];
+    D.vc1 = vc[1];
 }
 
 // Per-wave state of the online softmax and the value sums.
-template <int KB, int D>
+template <int GQ, int KB, int D>
 struct WaveAcc {
     float4_t O[KB];                      // basis-space value sums [head row][channel]
     float4_t Ores[D / 16];               // residual value mass [head row][channel]
     float4_t Ol;                         // normalisers: column 0 holds sum_t p per head row
-    float m_run;                         // running max of head (lane % 16) % 8
+    float m[GQ];                         // running max per head (the same in every lane)
 };
 
 // Bit masks keeping the first s entries of a token's record words (index
@@ -280,38 +296,81 @@ __device__ __forceinline__ uint32_t low_bits(int n)
     return n >= 32 ? 0xFFFFFFFFu : n <= 0 ? 0u : (1u << n) - 1u;
 }
 
+// fp16 probabilities of a wave's tile in LDS, [head][token] with the tokens
+// of each 32-token chunk ordered as the lanes of a 32-deep operand hold
+// them: token 16 h + 4 g + i of the chunk (h < 2, g < 4, i < 4) sits at
+// 8 g + 4 h + i, so one 16-byte read gives a lane its operand.  Row GQ stays
+// zero (the operand rows of padding heads).
+constexpr int kPStride = kTile + 8;        // fp16 per head row (16-byte multiple)
+__device__ __forceinline__ int p_slot(int t)
+{
+    return (t & ~31) | ((t & 12) << 1) | ((t & 16) >> 2) | (t & 3);
+}
+
+// Row h of the value products' A operand: 0 for the rows past the heads.
+template <int GQ>
+__device__ __forceinline__ const _Float16 *p_row(const _Float16 *sP, int c16)
+{
+    return sP + (c16 < GQ ? c16 : GQ) * kPStride;
+}
+
 template <int GQ, int KB, int D, int KBR>
 __device__ __forceinline__ void process_tile(const Tile &t, const TileData<kSlots * (KB / 4)> &Dt,
-                                             const half4_t (&qb)[KB], WaveAcc<KB, D> &A,
-                                             const float (*s_qt)[GQ < 4 ? 4 : GQ], float *sR,
+                                             const half4_t *qop, WaveAcc<GQ, KB, D> &A,
+                                             const float (*s_qt)[GQ < 4 ? 4 : GQ], _Float16 *sP,
                                              _Float16 *ev, int bits, int lane)
 {
     constexpr int NS = kSlots * (KB / 4);
     constexpr int MBS = NS / KBR;                   // 16-token blocks in the tile
     constexpr int GP = GQ < 4 ? 4 : GQ;
+    constexpr int NU = GP / 4;                      // score accumulators (4 heads each)
     constexpr int ND = D / 16;
     const int c16 = lane & 15, grp = lane >> 4;
     const int r = t.r, s = t.s, nv = t.nv;
     const bool full = nv == 16 * MBS;               // uniform: no token masks needed
+    const bool tok = lane < nv;                     // this lane's token is in the tile
 
-    // ---- scores: K coefficient rows x (q'_hi, q'_lo)
-    float4_t Sc[MBS];
+    // ---- scores, one token per lane: block mb's A rows 4 mb + j carry q' of
+    //      head 4 u + j (hi and lo parts), its B operand the tokens'
+    //      coefficients, so row 4 grp + j of accumulator u is (token lane,
+    //      head 4 u + j).  The q' pieces come from LDS (qop: this lane's
+    //      entry of the operand table).
+    float4_t Sc[NU];
 #pragma unroll
-    for (int mb = 0; mb < MBS; ++mb) {
-        Sc[mb] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
-        const bool tv = full || 16 * mb + c16 < nv;
+    for (int u = 0; u < NU; ++u) Sc[u] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    // (the B operand's columns are tokens and every product adds 0 x B into
+    // the other blocks' rows: channels past the rank and tokens past the
+    // tile must be zeros, not whatever the arena holds there)
 #pragma unroll
-        for (int kb = 0; kb < KBR; ++kb) {
-            half4_t a = Dt.ka[mb * KBR + kb];
-            if (!(tv && 16 * kb + 4 * grp < r)) a = half4_t{0, 0, 0, 0};
-            Sc[mb] = mma16(a, qb[kb], Sc[mb]);
+    for (int kb = 0; kb < KBR; ++kb) {
+        half4_t qa[NU][2];
+#pragma unroll
+        for (int u = 0; u < NU; ++u)
+#pragma unroll
+            for (int hl = 0; hl < 2; ++hl) qa[u][hl] = qop[kb * kWave + 4 * u + 8 * hl];
+        const bool chan = 16 * kb + 4 * grp < r;
+#pragma unroll
+        for (int mb = 0; mb < MBS; ++mb) {
+            const bool rows = (c16 >> 2) == mb;
+            const bool col = full || 16 * mb + c16 < nv;
+            half4_t bk = Dt.ka[mb * KBR + kb];
+            if (!(col && chan)) bk = half4_t{0, 0, 0, 0};
+#pragma unroll
+            for (int u = 0; u < NU; ++u)
+#pragma unroll
+                for (int hl = 0; hl < 2; ++hl)
+                    Sc[u] = mma16(rows ? qa[u][hl] : half4_t{0, 0, 0, 0}, bk, Sc[u]);
         }
     }
 
     // ---- residuals, one token per lane.  Entries past s are given index
     //      128 (a zero row of q, the spare row of the V-residual tile) and
     //      code 0, a whole record word at a time.  K: logit terms from q
-    //      gathered in LDS.  V: the token's cells of the dense LDS tile.
+    //      gathered in LDS, added to the lane's scores.  V: the token's
+    //      cells of the dense LDS tile.
+    float z[GP];
+#pragma unroll
+    for (int g = 0; g < GP; ++g) z[g] = Sc[g / 4][g % 4];
     uint32_t vi0 = 0, vi1 = 0;
     if (s > 0) {
         const uint32_t im0 = low_bits(8 * s), im1 = low_bits(8 * s - 32);
@@ -335,9 +394,9 @@ __device__ __forceinline__ void process_tile(const Tile &t, const TileData<kSlot
                 for (int g = 0; g < 4; ++g) rk[4 + g] += cv * q1[g];
             }
         }
-        const float sck = lane < nv ? h2f((uint16_t)Dt.ksc) : 0.0f;
+        const float sck = h2f((uint16_t)Dt.ksc);
 #pragma unroll
-        for (int g = 0; g < GQ; ++g) sR[g * kTile + lane] = rk[g] * sck;
+        for (int g = 0; g < GQ; ++g) z[g] += rk[g] * sck;
         // V cells (lanes past the tile write finite values of token 0 into
         // their own columns, which meet probability 0)
         vi0 = (Dt.vi0 & im0) | (0x80808080u & ~im0);
@@ -352,87 +411,103 @@ __device__ __forceinline__ void process_tile(const Tile &t, const TileData<kSlot
         }
         wave_fence();
     }
+    if (MBS < 4 || !full) {
+#pragma unroll
+        for (int g = 0; g < GQ; ++g) z[g] = tok ? z[g] : -INFINITY;
+    }
 
-    // ---- logits, tile max, lazy rescale, probabilities
-    float z[MBS][4];
-    float tmax = -INFINITY;
-    const int rrow = (c16 & 7) < GQ ? (c16 & 7) : 0;
+    // ---- lazy running max: only when a logit passes its head's max by more
+    //      than the lag are the max and every accumulator rescaled (rare)
+    bool over = false;
 #pragma unroll
-    for (int mb = 0; mb < MBS; ++mb) {
-        float4_t rr = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
-        if (s > 0) rr = *reinterpret_cast<const float4_t *>(&sR[rrow * kTile + 16 * mb + 4 * grp]);
+    for (int g = 0; g < GQ; ++g) over |= z[g] > A.m[g] + kMaxLag;
+    float f[GQ];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) z[mb][j] = Sc[mb][j] + row_swap8(Sc[mb][j]) + rr[j];
-    }
-    if (!full) {
+    for (int g = 0; g < GQ; ++g) f[g] = 1.0f;
+    if (__builtin_amdgcn_ballot_w64(over)) {
 #pragma unroll
-        for (int mb = 0; mb < MBS; ++mb)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                if (16 * mb + 4 * grp + j >= nv) z[mb][j] = -INFINITY;
-    }
-#pragma unroll
-    for (int mb = 0; mb < MBS; ++mb)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) tmax = fmaxf(tmax, z[mb][j]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
-    // (applied every tile with factor 1 when the max holds: a branch here
-    // makes the compiler shuttle every accumulator between two register
-    // ranges on the common path)
-    const bool need = tmax > A.m_run + kMaxLag;
-    {
-        const float new_m = need ? tmax : A.m_run;
-        const float f = fast_exp2(A.m_run - new_m);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const float fh = __shfl(f, 4 * grp + j, kWave);
-#pragma unroll
-            for (int nb = 0; nb < KB; ++nb) A.O[nb][j] *= fh;
-#pragma unroll
-            for (int nb = 0; nb < ND; ++nb) A.Ores[nb][j] *= fh;
-            A.Ol[j] *= fh;
+        for (int g = 0; g < GQ; ++g) {
+            const float tmax = wave_max(z[g]);
+            // the same in every lane: kept in a scalar register
+            const float nm = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(
+                                 int, tmax > A.m[g] + kMaxLag ? tmax : A.m[g])));
+            f[g] = fast_exp2(A.m[g] - nm);
+            A.m[g] = nm;
         }
-        A.m_run = new_m;
     }
-    half4_t P[MBS];
+    // (the factors are applied every tile, 1 when the max held: accumulators
+    // updated inside the branch make the compiler keep two copies of them)
 #pragma unroll
-    for (int mb = 0; mb < MBS; ++mb)
+    for (int j = 0; j < 4; ++j) {
+        float fh = 1.0f;                             // accumulator row 4 grp + j is head 4 grp + j
 #pragma unroll
-        for (int j = 0; j < 4; ++j) P[mb][j] = (_Float16)fast_exp2(z[mb][j] - A.m_run);
+        for (int g = j; g < GQ; g += 4) fh = 4 * grp + j == g ? f[g] : fh;
+#pragma unroll
+        for (int nb = 0; nb < KB; ++nb) A.O[nb][j] *= fh;
+#pragma unroll
+        for (int nb = 0; nb < ND; ++nb) A.Ores[nb][j] *= fh;
+        A.Ol[j] *= fh;
+    }
 
-    // ---- values: probabilities x V coefficient columns, two 16-token
-    //      blocks per product where the tile has them; the normaliser is
+    // ---- probabilities: to LDS in operand order, back as the A operand
+    //      (rows: heads; 32-deep: the chunk's tokens)
+    {
+        const int ps = p_slot(lane);
+#pragma unroll
+        for (int g = 0; g < GQ; ++g) sP[g * kPStride + ps] = (_Float16)fast_exp2(z[g] - A.m[g]);
+    }
+    wave_fence();
+    const _Float16 *prow = p_row<GQ>(sP, c16);
+    constexpr int NP = MBS == 1 ? 1 : MBS / 2;
+    half8_t PA[NP];
+    half4_t P1 = half4_t{0, 0, 0, 0};
+    if constexpr (MBS == 1) {
+        P1 = *reinterpret_cast<const half4_t *>(prow + 8 * grp);
+    } else {
+#pragma unroll
+        for (int p = 0; p < NP; ++p) PA[p] = *reinterpret_cast<const half8_t *>(prow + 32 * p + 8 * grp);
+    }
+
+    // ---- values: probabilities x V coefficient columns; the normaliser is
     //      the same product with a column of ones (fp32 sums of the fp16
     //      probabilities the values use)
     const _Float16 one = c16 == 0 ? (_Float16)1.0f : (_Float16)0.0f;
     const half4_t ones = half4_t{one, one, one, one};
+    // V coefficients of tokens past the tile are zeroed (they meet p = 0,
+    // but 0 x whatever the arena holds there need not be 0): whole-register
+    // masks, so the tile's registers stay registers
+    half4_t va[NS];
+#pragma unroll
+    for (int i = 0; i < NS; ++i) va[i] = Dt.va[i];
+    if (!full) {
+#pragma unroll
+        for (int mb = 0; mb < MBS; ++mb) {
+            const int t0 = 16 * mb + 4 * grp;
+            const uint32_t m0 = (t0 < nv ? 0xFFFFu : 0u) | (t0 + 1 < nv ? 0xFFFF0000u : 0u);
+            const uint32_t m1 = (t0 + 2 < nv ? 0xFFFFu : 0u) | (t0 + 3 < nv ? 0xFFFF0000u : 0u);
+#pragma unroll
+            for (int kb = 0; kb < KBR; ++kb) va[mb * KBR + kb] = keep_h4(va[mb * KBR + kb], m0, m1);
+        }
+    }
 #pragma unroll
     for (int nb = 0; nb < KBR; ++nb) {
         half4_t bv[MBS];
         const bool cv = 16 * nb + c16 < r;
 #pragma unroll
-        for (int mb = 0; mb < MBS; ++mb) {
-            bv[mb] = cv ? Dt.va[mb * KBR + nb] : half4_t{0, 0, 0, 0};
-            if (!full) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    if (16 * mb + 4 * grp + j >= nv) bv[mb][j] = 0;
-            }
-        }
+        for (int mb = 0; mb < MBS; ++mb) bv[mb] = cv ? va[mb * KBR + nb] : half4_t{0, 0, 0, 0};
         if constexpr (MBS == 1) {
-            A.O[nb] = mma16(P[0], bv[0], A.O[nb]);
+            A.O[nb] = mma16(P1, bv[0], A.O[nb]);
         } else {
 #pragma unroll
-            for (int p = 0; p < MBS / 2; ++p)
-                A.O[nb] = mma32(cat(P[2 * p], P[2 * p + 1]), cat(bv[2 * p], bv[2 * p + 1]), A.O[nb]);
+            for (int p = 0; p < NP; ++p)
+                A.O[nb] = mma32(PA[p], cat(bv[2 * p], bv[2 * p + 1]), A.O[nb]);
         }
     }
     if constexpr (MBS == 1) {
-        A.Ol = mma16(P[0], ones, A.Ol);
+        A.Ol = mma16(P1, ones, A.Ol);
     } else {
 #pragma unroll
-        for (int p = 0; p < MBS / 2; ++p) A.Ol = mma32(cat(P[2 * p], P[2 * p + 1]), cat(ones, ones), A.Ol);
+        for (int p = 0; p < NP; ++p) A.Ol = mma32(PA[p], cat(ones, ones), A.Ol);
     }
 
     // ---- V residual mass: the dense tile times the probabilities, then the
@@ -443,13 +518,13 @@ __device__ __forceinline__ void process_tile(const Tile &t, const TileData<kSlot
         for (int nb = 0; nb < ND; ++nb) {
             if constexpr (MBS == 1) {
                 const half4_t e0 = *reinterpret_cast<const half4_t *>(evr + 16 * nb * kEvStride);
-                A.Ores[nb] = mma16(P[0], e0, A.Ores[nb]);
+                A.Ores[nb] = mma16(P1, e0, A.Ores[nb]);
             } else {
 #pragma unroll
-                for (int p = 0; p < MBS / 2; ++p) {
+                for (int p = 0; p < NP; ++p) {
                     const half4_t e0 = *reinterpret_cast<const half4_t *>(evr + 16 * nb * kEvStride + 32 * p);
                     const half4_t e1 = *reinterpret_cast<const half4_t *>(evr + 16 * nb * kEvStride + 32 * p + 16);
-                    A.Ores[nb] = mma32(cat(P[2 * p], P[2 * p + 1]), cat(e0, e1), A.Ores[nb]);
+                    A.Ores[nb] = mma32(PA[p], cat(e0, e1), A.Ores[nb]);
                 }
             }
         }
@@ -461,16 +536,16 @@ __device__ __forceinline__ void process_tile(const Tile &t, const TileData<kSlot
 
 template <int GQ, int KB, int D>
 __device__ __forceinline__ void process_any(const Tile &t, const TileData<kSlots * (KB / 4)> &Dt,
-                                            const half4_t (&qb)[KB], WaveAcc<KB, D> &A,
-                                            const float (*s_qt)[GQ < 4 ? 4 : GQ], float *sR,
+                                            const half4_t *qop, WaveAcc<GQ, KB, D> &A,
+                                            const float (*s_qt)[GQ < 4 ? 4 : GQ], _Float16 *sP,
                                             _Float16 *ev, int bits, int lane)
 {
     switch (t.kbr) {
-    case 1: process_tile<GQ, KB, D, 1>(t, Dt, qb, A, s_qt, sR, ev, bits, lane); break;
-    case 2: process_tile<GQ, KB, D, 2>(t, Dt, qb, A, s_qt, sR, ev, bits, lane); break;
-    case 4: process_tile<GQ, KB, D, 4>(t, Dt, qb, A, s_qt, sR, ev, bits, lane); break;
+    case 1: process_tile<GQ, KB, D, 1>(t, Dt, qop, A, s_qt, sP, ev, bits, lane); break;
+    case 2: process_tile<GQ, KB, D, 2>(t, Dt, qop, A, s_qt, sP, ev, bits, lane); break;
+    case 4: process_tile<GQ, KB, D, 4>(t, Dt, qop, A, s_qt, sP, ev, bits, lane); break;
     default:
-        if constexpr (KB == 8) process_tile<GQ, KB, D, 8>(t, Dt, qb, A, s_qt, sR, ev, bits, lane);
+        if constexpr (KB == 8) process_tile<GQ, KB, D, 8>(t, Dt, qop, A, s_qt, sP, ev, bits, lane);
         break;
     }
 }
@@ -495,12 +570,16 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
     __shared__ __attribute__((aligned(16))) _Float16 s_ev[kWaves * kEvWave];   // V-residual tiles
     __shared__ __attribute__((aligned(16))) float s_qt[kMaxHeadDim + 1][GP];   // q, base-2 units; zero rows
                                                                                 // from D on (row 128: unused entries)
-    constexpr int RK = GQ < 2 ? 2 : GQ;            // rows of the K-residual area (>= 4 KiB)
-    __shared__ __attribute__((aligned(16))) float s_rk[kWaves][RK][kTile];     // K-residual logits
+    // per-wave area: the tile probabilities in the loop, the merged sums after
+    constexpr int kPBytes = (GQ + 1) * kPStride * 2;
+    constexpr int kQpBytes = (GQ * (RMAX + D) * 4 / kWaves + 15) / 16 * 16;
+    constexpr int kWvBytes = kPBytes > kQpBytes ? kPBytes : kQpBytes;
+    __shared__ __attribute__((aligned(16))) uint8_t s_wv[kWaves * kWvBytes];
+    __shared__ half4_t s_qb[KB * kWave];           // score operand q', [channel block][lane]
     __shared__ float s_m[kWaves][GQ], s_l[kWaves][GQ];
     __shared__ float s_M[GQ], s_L[GQ];
     __shared__ int s_last;
-    static_assert(KB * kWave * 8 <= sizeof(s_rk) && GQ * (RMAX + D) * 4 <= sizeof(s_rk), "K-residual area reuse");
+    static_assert(GQ * (RMAX + D) * 4 <= sizeof(s_wv) && kPBytes % 16 == 0, "per-wave area");
 
     // ---- token counts first (one lane per tier), then the query in
     //      operand layout and, for waves 0..KB-1, one 16-row block of B_K
@@ -531,6 +610,9 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
     // ---- this workgroup's work-balanced run of 16-token blocks: lane k
     //      works out and keeps tier k's range
     const uint8_t *blk = head_block_ptr(ly, arena, layer, b, h);
+    // buffer resource on the block (reads past its end return zeros), built
+    // from scalar registers so every load takes it directly
+    const __amdgpu_buffer_rsrc_t rb = block_rsrc(blk, ly.head_block);
     Ranges rg;
     {
         const bool on = lane < T;
@@ -572,7 +654,7 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
     TileData<NS> DA, DB;
     Cursor cur{0, wave};
     Tile ta = locate<NS>(rg, cur, ly);
-    issue_tile<NS>(ta, DA, blk, ly, lane);
+    issue_tile<NS>(ta, DA, rb, ly, lane);
 
     // ---- query in base-2 logit units (LDS, for residual gathers); this
     //      wave's V-residual tile cleared
@@ -594,7 +676,6 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
     //      and as the remainder fp16(q' - fp16(q')) above -- so that the fp16
     //      products reproduce q' to ~2^-22.  Products of fp16 inputs are
     //      exact and sums fp32: q' is fp32-accurate.
-    half4_t *s_qb = reinterpret_cast<half4_t *>(&s_rk[0][0][0]);   // [KB][64], before the loop
     if (wave < KB) {
         float4_t acc = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -623,30 +704,33 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
             for (int i = lane; i < kEvWave / 8; i += kWave) e4[i] = uint4{0u, 0u, 0u, 0u};
         }
     }
-    half4_t qb[KB];
-#pragma unroll
-    for (int mb = 0; mb < KB; ++mb) qb[mb] = s_qb[mb * kWave + lane];
-    __syncthreads();
+    if (encoder) __syncthreads();                  // waves 2, 3 write their tiles only after this
+    // the A operand of the scores for lane (c16, grp): q' (hi, lo) of head
+    // 4 u + c16 % 4, channels 16 kb + 4 grp + 0..3, at qop[64 kb + 4 u + 8 hl]
+    const half4_t *qop = s_qb + 16 * grp + (c16 & 3);
+    // this wave's probability rows; row GQ (the padding heads' operand) zero
+    _Float16 *sP = reinterpret_cast<_Float16 *>(s_wv + wave * kWvBytes);
+    if (lane < kPStride / 8) reinterpret_cast<uint4 *>(sP + GQ * kPStride)[lane] = uint4{0u, 0u, 0u, 0u};
 
     // ---- main loop: two-deep pipeline over this wave's tiles
-    WaveAcc<KB, D> A;
+    WaveAcc<GQ, KB, D> A;
 #pragma unroll
     for (int nb = 0; nb < KB; ++nb) A.O[nb] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int nb = 0; nb < ND; ++nb) A.Ores[nb] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
     A.Ol = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    A.m_run = -INFINITY;
-    float *sR = &s_rk[wave][0][0];
+#pragma unroll
+    for (int g = 0; g < GQ; ++g) A.m[g] = -INFINITY;
     while (ta.valid) {
         cur.rem += kWaves;
         Tile tb = locate<NS>(rg, cur, ly);
-        issue_tile<NS>(tb, DB, blk, ly, lane);
-        process_any<GQ, KB, D>(ta, DA, qb, A, s_qt, sR, ev, bits, lane);
+        issue_tile<NS>(tb, DB, rb, ly, lane);
+        process_any<GQ, KB, D>(ta, DA, qop, A, s_qt, sP, ev, bits, lane);
         if (!tb.valid) break;
         cur.rem += kWaves;
         ta = locate<NS>(rg, cur, ly);
-        issue_tile<NS>(ta, DA, blk, ly, lane);
-        process_any<GQ, KB, D>(tb, DB, qb, A, s_qt, sR, ev, bits, lane);
+        issue_tile<NS>(ta, DA, rb, ly, lane);
+        process_any<GQ, KB, D>(tb, DB, qop, A, s_qt, sP, ev, bits, lane);
     }
 
     // ---- this wave's B_V operand for the back-projection (in flight
@@ -664,7 +748,10 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
 
     // ---- merge the waves of this workgroup: each wave leaves its unscaled
     //      sums in its own (now idle) V-residual tile, then one barrier
-    if (lane < GQ) s_m[wave][lane] = A.m_run;
+    if (lane == 0) {
+#pragma unroll
+        for (int g = 0; g < GQ; ++g) s_m[wave][g] = A.m[g];
+    }
     if (c16 == 0) {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
@@ -686,7 +773,7 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
     __syncthreads();
     // weights 2^(m_w - M) in a fixed wave order (bitwise reproducible);
     // merged sums go to the K-residual area, idle now
-    float *s_qp = &s_rk[0][0][0];                                // [GQ][RMAX + D]
+    float *s_qp = reinterpret_cast<float *>(s_wv);                // [GQ][RMAX + D]
     for (int i = tid; i < GQ * (RMAX + D); i += kBlock) {
         const int g = i / (RMAX + D);
         float M = -INFINITY;
