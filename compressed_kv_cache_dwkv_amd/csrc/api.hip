@@ -23,15 +23,15 @@ namespace dwkv {
 // kernel cuts each tier into tiles of about 2 KiB of coefficients per K and
 // V (64 tokens at rank <= 16, 32 at rank 32, 16 at rank 64; twice that when
 // the basis is wider than 64).  Workgroup times on the 64K-token
-// Llama-3-8B shape fit a fixed cost per tile plus a small cost per token
-// (about 23:1 for a 64-token tile), whatever the rank: a token weighs its
-// share of a tile plus that per-token part.
+// Llama-3-8B shape are set by their tile count alone (about 0.45 us of a
+// compute unit per tile, whatever its rank and number of tokens): a token
+// weighs its share of a tile.
 static int token_cost(int r, int r_max)
 {
     const int slots = r_max <= 64 ? 4 : 8;                 // 16x16 operand blocks per tile
     const int kbr = r <= 16 ? 1 : r <= 32 ? 2 : r <= 64 ? 4 : 8;
     const int tokens_per_tile = 16 * (slots / kbr);
-    return 3072 / tokens_per_tile + 14;
+    return 9216 / tokens_per_tile;
 }
 constexpr int64_t kArenaTail = 8192;
 

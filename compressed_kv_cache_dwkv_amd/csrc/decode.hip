@@ -63,8 +63,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kMaxLag = 8.0f;           // log2 units the running max may trail
 // The append's encoding, done by the first workgroup of each (sequence, KV
 // head) before its share of the tiles, in the units of the work balance
-// (per 16-token block: 16 x the tier's per-token cost).
-constexpr int64_t kEncodeUnits = 80000;
+// (9216 per tile; measured: shares reduced by 20 to 30 tiles hide it).
+constexpr int64_t kEncodeUnits = 250000;
 
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
@@ -604,6 +604,9 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
     // which no tile of this launch uses, and the last workgroup publishes it.
     const bool appending = ap.k != nullptr;
     const bool encoder = appending && split == 0;
+    // the new token's tier, for the workgroup that publishes it (read now,
+    // with the counts, so publishing waits for no memory)
+    const int app_tier = appending ? __builtin_amdgcn_readfirstlane(ap.tier[b * ly.Hkv + h]) : 0;
     AppendRegs<D> app;
     if (encoder && wave < 2) append_fetch<D>(app, ly, arena, layer, b, h, wave, lane, ap);
 
@@ -842,10 +845,9 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
     // the appended token can be published (its tier from the same input and
     // the counts this workgroup read, so admission matches the encoder's)
     if (appending && wave == 0) {
-        const int k = __builtin_amdgcn_readfirstlane(ap.tier[b * ly.Hkv + h]);
         int slot, n;
-        if (append_admit(ly, k, rg.cnt, slot, n) == 0 && lane == 0)
-            append_commit(ly, arena, layer, b, h, k, slot, n);
+        if (append_admit(ly, app_tier, rg.cnt, slot, n) == 0 && lane == 0)
+            append_commit(ly, arena, layer, b, h, app_tier, slot, n);
     }
     // Each thread owns 4 adjacent outputs of one head and an interleaved
     // subset of the splits.  Its first 8 partial vectors are requested
