@@ -71,6 +71,15 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
+// A loaded operand kept in registers: without it the compiler turns the
+// per-block select of a shared operand into a masked reload for every block.
+__device__ __forceinline__ half4_t in_reg(half4_t v)
+{
+    u32x2_t b = __builtin_bit_cast(u32x2_t, v);
+    asm volatile("" : "+v"(b));
+    return __builtin_bit_cast(half4_t, b);
+}
+
 // The fp16 values of v whose 16-bit lanes of (m0, m1) are ones; the others 0.
 __device__ __forceinline__ half4_t keep_h4(half4_t v, uint32_t m0, uint32_t m1)
 {
@@ -347,7 +356,7 @@ __device__ __forceinline__ void process_tile(const Tile &t, const TileData<kSlot
 #pragma unroll
         for (int u = 0; u < NU; ++u)
 #pragma unroll
-            for (int hl = 0; hl < 2; ++hl) qa[u][hl] = qop[kb * kWave + 4 * u + 8 * hl];
+            for (int hl = 0; hl < 2; ++hl) qa[u][hl] = in_reg(qop[kb * kWave + 4 * u + 8 * hl]);
         const bool chan = 16 * kb + 4 * grp < r;
 #pragma unroll
         for (int mb = 0; mb < MBS; ++mb) {
