@@ -130,6 +130,7 @@ int build_layout(const dwkv_config *c, Layout *ly)
     ly->off_posmap = off;   off = align_up(off + heads * ly->max_tokens * 4, 256);
     ly->basis_elems = (int64_t)ly->Hkv * ly->R * ly->d;
     ly->off_basis = off;    off = align_up(off + (int64_t)ly->num_groups * 2 * ly->basis_elems * 2, 256);
+    ly->off_basisvt = off;  off = align_up(off + (int64_t)ly->num_groups * ly->basis_elems * 2, 256);
     ly->off_seg = off;      off = off + heads * ly->head_block;
     // spare tail: the decode kernel's fixed-shape tile loads may read up to
     // a few KiB past the last token of the last head block
@@ -254,6 +255,7 @@ int dwkv_set_basis(dwkv_handle *h, int group, const void *basisK, const void *ba
     if (e == hipSuccess)
         e = hipMemcpyAsync(dwkv::basis_ptr(ly, h->arena, group, 1, 0), basisV, bytes,
                            hipMemcpyDeviceToDevice, s);
+    if (e == hipSuccess) e = dwkv::launch_transpose_basis(ly, h->arena, group, s);
     return hip_status(e);
 }
 

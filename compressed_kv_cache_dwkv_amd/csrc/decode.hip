@@ -244,10 +244,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const uint8_t *p, i
 // plus a wave-uniform offset per operand slot, so a tile costs almost no
 // vector address arithmetic.  Slots and lanes past the tile's valid tokens
 // or its rank read other bytes of the block, or zeros past its end; their
-// values are zeroed where they are used.
+// values are zeroed where they are used.  A tile past the wave's last one
+// loads, in its K slots, the wave's operand of the back-projection instead
+// (slot i: channels 16 i + 4 grp.. of row `kbv` of the transposed V basis),
+// so that operand arrives while the last tile is computed.
 template <int NS>
 __device__ __forceinline__ void issue_tile(const Tile &t, TileData<NS> &D, __amdgpu_buffer_rsrc_t rb,
-                                           const Layout &ly, int lane)
+                                           __amdgpu_buffer_rsrc_t rbv, uint32_t kbv, const Layout &ly,
+                                           int lane)
 {
     const int c16 = lane & 15, grp = lane >> 4;
     const TierDesc &td = ly.tier[t.k];
@@ -257,13 +261,15 @@ __device__ __forceinline__ void issue_tile(const Tile &t, TileData<NS> &D, __amd
     // both start r fp16 per token into their arrays
     const uint32_t sK = (uint32_t)td.coefK + tok0 * (uint32_t)r * 2u;
     const uint32_t sV = (uint32_t)td.coefV + tok0 * (uint32_t)r * 2u;
-    const uint32_t kl = (uint32_t)(c16 * r + 4 * grp) * 2u;     // token c16, channels 4grp..
     const uint32_t vl = (uint32_t)(c16 * 16 + 4 * grp) * 2u;    // channel c16, tokens 4grp..
+    const bool v = t.valid;
+    const __amdgpu_buffer_rsrc_t rk = v ? rb : rbv;
+    const uint32_t kl = v ? (uint32_t)(c16 * r + 4 * grp) * 2u : kbv;   // token c16, channels 4grp..
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
         const int mb = i / kbr, kb = i - mb * kbr;
-        D.ka[i] = __builtin_bit_cast(
-            half4_t, __builtin_amdgcn_raw_buffer_load_b64(rb, kl, sK + (uint32_t)(16 * mb * r + 16 * kb) * 2u, 0));
+        const uint32_t ko = v ? sK + (uint32_t)(16 * mb * r + 16 * kb) * 2u : (uint32_t)i * 32u;
+        D.ka[i] = __builtin_bit_cast(half4_t, __builtin_amdgcn_raw_buffer_load_b64(rk, kl, ko, 0));
         D.va[i] = __builtin_bit_cast(
             half4_t, __builtin_amdgcn_raw_buffer_load_b64(rb, vl, sV + (uint32_t)(mb * r + 16 * kb) * 32u, 0));
     }
@@ -625,6 +631,10 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
     // buffer resource on the block (reads past its end return zeros), built
     // from scalar registers so every load takes it directly
     const __amdgpu_buffer_rsrc_t rb = block_rsrc(blk, ly.head_block);
+    // the transposed V basis (back-projection operand: row 16 w + c16 for wave w)
+    const __amdgpu_buffer_rsrc_t rbv = block_rsrc(
+        reinterpret_cast<const uint8_t *>(basis_vt_ptr(ly, arena, layer / ly.G, h)), (int64_t)R * D * 2);
+    const uint32_t kbv = (uint32_t)((16 * (wave < ND ? wave : 0) + c16) * R + 4 * grp) * 2u;
     Ranges rg;
     {
         const bool on = lane < T;
@@ -666,7 +676,7 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
     TileData<NS> DA, DB;
     Cursor cur{0, wave};
     Tile ta = locate<NS>(rg, cur, ly);
-    issue_tile<NS>(ta, DA, rb, ly, lane);
+    issue_tile<NS>(ta, DA, rb, rbv, kbv, ly, lane);
 
     // ---- query in base-2 logit units (LDS, for residual gathers); this
     //      wave's V-residual tile cleared
@@ -733,30 +743,25 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
     A.Ol = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int g = 0; g < GQ; ++g) A.m[g] = -INFINITY;
+    bool bv_in_b = false;                           // the tile past the last holds the B_V operand
     while (ta.valid) {
         cur.rem += kWaves;
         Tile tb = locate<NS>(rg, cur, ly);
-        issue_tile<NS>(tb, DB, rb, ly, lane);
+        issue_tile<NS>(tb, DB, rb, rbv, kbv, ly, lane);
         process_any<GQ, KB, D>(ta, DA, qop, A, s_qt, sP, ev, bits, lane);
-        if (!tb.valid) break;
+        if (!tb.valid) {
+            bv_in_b = true;
+            break;
+        }
         cur.rem += kWaves;
         ta = locate<NS>(rg, cur, ly);
-        issue_tile<NS>(ta, DA, rb, ly, lane);
+        issue_tile<NS>(ta, DA, rb, rbv, kbv, ly, lane);
         process_any<GQ, KB, D>(tb, DB, qop, A, s_qt, sP, ev, bits, lane);
     }
 
-    // ---- this wave's B_V operand for the back-projection (in flight
-    //      while the waves merge)
-    uint16_t bvr[RMAX / 4];
-    {
-        const uint16_t *BV = basis_ptr(ly, arena, layer / ly.G, 1, h);
-        const int col = 16 * (wave < ND ? wave : 0) + c16;
+    half4_t bvt[NS];
 #pragma unroll
-        for (int kb = 0; kb < RMAX / 4; ++kb) {
-            const int row = 4 * kb + grp < R ? 4 * kb + grp : R - 1;
-            bvr[kb] = BV[(int64_t)row * D + col];
-        }
-    }
+    for (int i = 0; i < NS; ++i) bvt[i] = bv_in_b ? DB.ka[i] : DA.ka[i];
 
     // ---- merge the waves of this workgroup: each wave leaves its unscaled
     //      sums in its own (now idle) V-residual tile, then one barrier
@@ -786,18 +791,19 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
     // weights 2^(m_w - M) in a fixed wave order (bitwise reproducible);
     // merged sums go to the K-residual area, idle now
     float *s_qp = reinterpret_cast<float *>(s_wv);                // [GQ][RMAX + D]
-    for (int i = tid; i < GQ * (RMAX + D); i += kBlock) {
-        const int g = i / (RMAX + D);
+    static_assert((RMAX + D) % 4 == 0 && (kEvWave * 2) % 16 == 0, "float4 merge");
+    for (int i4 = 4 * tid; i4 < GQ * (RMAX + D); i4 += 4 * kBlock) {
+        const int g = i4 / (RMAX + D);
         float M = -INFINITY;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w][g]);
-        float acc = 0.0f;
+        float4_t acc = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
             const float f = M == -INFINITY ? 0.0f : fast_exp2(s_m[w][g] - M);
-            acc += f * reinterpret_cast<const float *>(s_ev + w * kEvWave)[i];
+            acc += f * *reinterpret_cast<const float4_t *>(reinterpret_cast<const float *>(s_ev + w * kEvWave) + i4);
         }
-        s_qp[i] = acc;
+        *reinterpret_cast<float4_t *>(s_qp + i4) = acc;
     }
     if (tid < GQ) {
         const int g = tid;
@@ -810,24 +816,33 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
     }
     __syncthreads();
     // one back-projection through B_V plus the residual mass, on the matrix
-    // cores in fp32: wave w forms output channels 16w..16w+15 as
-    // out^T[j][g] = res[g][j] + sum_i B_V[i][j] a[g][i]
+    // cores: wave w forms output channels 16w..16w+15 as
+    // out[g][j] = res[g][j] + sum_i B_V[i][j] a[g][i], with B_V^T rows as the
+    // A operand (exact fp16) and a as fp16 hi and lo parts in columns g and
+    // 8 + g (products exact, sums fp32), the two halves added across lanes
     if (wave < ND) {
-        float4_t acc;
+        float4_t acc = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        const int g = c16 & 7;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            acc[j] = c16 < GQ ? s_qp[c16 * (RMAX + D) + RMAX + 16 * wave + 4 * grp + j] : 0.0f;
+        for (int kb = 0; kb < NS; ++kb) {
+            half4_t bb;
 #pragma unroll
-        for (int kb = 0; kb < RMAX / 4; ++kb) {
-            const int i = 4 * kb + grp;
-            const float a = i < R ? h2f(bvr[kb]) : 0.0f;
-            const float bb = c16 < GQ && i < R ? s_qp[c16 * (RMAX + D) + i] : 0.0f;
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bb, acc, 0, 0, 0);
+            for (int j = 0; j < 4; ++j) {
+                const int i = 16 * kb + 4 * grp + j;
+                const float x = g < GQ && i < R ? s_qp[g * (RMAX + D) + i] : 0.0f;
+                const _Float16 xh = (_Float16)x;
+                bb[j] = c16 < 8 ? xh : (_Float16)(x - (float)xh);
+            }
+            acc = mma16(bvt[kb], bb, acc);
         }
         if (c16 < GQ) {
             float *po = ws.po + (((int64_t)b * ly.Hq + g0 + c16) * S + split) * D + 16 * wave + 4 * grp;
-            st_agent2(po, acc[0], acc[1]);
-            st_agent2(po + 2, acc[2], acc[3]);
+            float o[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                o[j] = acc[j] + row_swap8(acc[j]) + s_qp[c16 * (RMAX + D) + RMAX + 16 * wave + 4 * grp + j];
+            st_agent2(po, o[0], o[1]);
+            st_agent2(po + 2, o[2], o[3]);
         }
     }
     if (tid < GQ) {

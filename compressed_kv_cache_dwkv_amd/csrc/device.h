@@ -20,18 +20,40 @@ __device__ __forceinline__ uint16_t f2h(float f)
     return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
 }
 
+// Value of another lane of the same row of 16 by a DPP move: quad_perm
+// [1,0,3,2] (0xB1) and [2,3,0,1] (0x4E), row_half_mirror (0x141), row_mirror
+// (0x140).  Each pairs every lane with one of the other half of its group.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Reductions over the 64 lanes of a (fully active) wave: within each row of
+// 16 by DPP moves, then across the four rows by reading one lane of each.
+// The result is the same in every lane.
 __device__ __forceinline__ float wave_sum(float v)
 {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
-    return v;
+    v += dpp_mov<0xB1>(v);
+    v += dpp_mov<0x4E>(v);
+    v += dpp_mov<0x141>(v);
+    v += dpp_mov<0x140>(v);
+    return (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0)) +
+            __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16))) +
+           (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32)) +
+            __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48)));
 }
 
 __device__ __forceinline__ float wave_max(float v)
 {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
-    return v;
+    v = fmaxf(v, dpp_mov<0xB1>(v));
+    v = fmaxf(v, dpp_mov<0x4E>(v));
+    v = fmaxf(v, dpp_mov<0x141>(v));
+    v = fmaxf(v, dpp_mov<0x140>(v));
+    return fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0)),
+                       __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16))),
+                 fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32)),
+                       __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48))));
 }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }

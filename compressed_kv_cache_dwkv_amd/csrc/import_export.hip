@@ -188,6 +188,31 @@ hipError_t launch_export(const Layout &ly, uint8_t *arena, int layer,
     return hipGetLastError();
 }
 
+namespace {
+
+// One thread per element of the window's V bases: dst[h][j][i] = src[h][i][j].
+__global__ void transpose_basis_kernel(Layout ly, uint8_t *arena, int m)
+{
+    const int64_t n = ly.basis_elems;
+    for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < n; e += (int64_t)gridDim.x * blockDim.x) {
+        const int h = (int)(e / ((int64_t)ly.R * ly.d));
+        const int64_t rem = e - (int64_t)h * ly.R * ly.d;
+        const int j = (int)(rem / ly.R), i = (int)(rem % ly.R);
+        basis_vt_ptr(ly, arena, m, h)[(int64_t)j * ly.R + i] = basis_ptr(ly, arena, m, 1, h)[(int64_t)i * ly.d + j];
+    }
+}
+
+}  // namespace
+
+hipError_t launch_transpose_basis(const Layout &ly, uint8_t *arena, int m, hipStream_t stream)
+{
+    (void)hipGetLastError();  // drop errors left by earlier, unrelated calls
+    const int64_t blocks = (ly.basis_elems + 255) / 256;
+    hipLaunchKernelGGL(transpose_basis_kernel, dim3((unsigned)(blocks < 1024 ? blocks : 1024)), dim3(256), 0, stream,
+                       ly, arena, m);
+    return hipGetLastError();
+}
+
 hipError_t launch_fill_u32(uint32_t *p, uint32_t value, int64_t count, hipStream_t stream)
 {
     if (count <= 0) return hipSuccess;

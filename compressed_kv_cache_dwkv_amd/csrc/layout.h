@@ -70,7 +70,7 @@ struct Layout {
     double inv_cblk[kMaxTiers];  // 1 / (16 * cost): reciprocal of a 16-token block's cost
     int64_t cap[kMaxTiers];
     int64_t max_tokens;
-    int64_t off_err, off_counts, off_posmap, off_basis, off_seg;
+    int64_t off_err, off_counts, off_posmap, off_basis, off_basisvt, off_seg;
     int64_t basis_elems;         // Hkv * R * d  (one Z of one window)
     int64_t head_block;          // bytes of one (layer, b, h) block
     int64_t f_coefK[kMaxTiers], f_coefV[kMaxTiers];
@@ -110,6 +110,15 @@ DWKV_HD uint16_t *basis_ptr(const Layout &ly, uint8_t *arena, int m, int z, int 
 {
     return reinterpret_cast<uint16_t *>(arena + ly.off_basis) +
            ((int64_t)m * 2 + z) * ly.basis_elems + (int64_t)h * ly.R * ly.d;
+}
+
+// Transposed V basis of window m, KV head h: d rows of R fp16 (row j holds
+// component j of every basis vector), the operand layout of the decode's
+// back-projection.
+DWKV_HD uint16_t *basis_vt_ptr(const Layout &ly, uint8_t *arena, int m, int h)
+{
+    return reinterpret_cast<uint16_t *>(arena + ly.off_basisvt) + (int64_t)m * ly.basis_elems +
+           (int64_t)h * ly.R * ly.d;
 }
 
 // Element (slot, i) of a tier's V coefficients, in fp16 units from the array
