@@ -600,7 +600,13 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
     //      operand layout and, for waves 0..KB-1, one 16-row block of B_K
     const int T = ly.T;
     const int kl = lane < T ? lane : 0;
-    const int cnt_l = lane < T ? counts_ptr(ly, arena, layer, b, h)[kl] : 0;
+    // every per-tier value of lane k's tier, requested together and without
+    // a branch, so the loads are in flight at once
+    const int cnt_raw = counts_ptr(ly, arena, layer, b, h)[kl];
+    const int r_l = ly.rank[kl];
+    const int cost_l = ly.cost[kl];
+    const double icb_l = ly.inv_cblk[kl];
+    const int cnt_l = lane < T ? cnt_raw : 0;
     const int gq = c16 & 7;
     const uint16_t *qrow = q + ((int64_t)b * ly.Hq + g0 + (gq < GQ ? gq : 0)) * D;
     half4_t bq[ND], ak[ND];
@@ -619,9 +625,9 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
     // which no tile of this launch uses, and the last workgroup publishes it.
     const bool appending = ap.k != nullptr;
     const bool encoder = appending && split == 0;
-    // the new token's tier, for the workgroup that publishes it (read now,
-    // with the counts, so publishing waits for no memory)
-    const int app_tier = appending ? __builtin_amdgcn_readfirstlane(ap.tier[b * ly.Hkv + h]) : 0;
+    // the new token's tier, for the workgroup that publishes it (requested
+    // now, with the counts, so publishing waits for no memory)
+    const int app_tier_v = appending ? ap.tier[b * ly.Hkv + h] : 0;
     AppendRegs<D> app;
     if (encoder && wave < 2) append_fetch<D>(app, ly, arena, layer, b, h, wave, lane, ap);
 
@@ -638,8 +644,7 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
     Ranges rg;
     {
         const bool on = lane < T;
-        const int r_l = ly.rank[kl];
-        const int64_t wb_l = 16 * (int64_t)ly.cost[kl];
+        const int64_t wb_l = 16 * (int64_t)cost_l;
         const int64_t nb_l = on ? (cnt_l + 15) >> 4 : 0;
         const int64_t wt_l = nb_l * wb_l;                     // bytes of tier k's blocks
         int64_t W = 0, wk_l = 0;                               // total; bytes of tiers before k
@@ -659,8 +664,8 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
         lo = lo > 0 ? lo : 0;
         hi = hi > 0 ? hi : 0;
         const int64_t x0 = lo - wk_l, x1 = hi - wk_l;
-        int64_t b0 = x0 <= 0 || !on ? 0 : div_floor(x0 + wb_l - 1, wb_l, ly.inv_cblk[kl]);
-        int64_t b1 = x1 <= 0 || !on ? 0 : div_floor(x1 + wb_l - 1, wb_l, ly.inv_cblk[kl]);
+        int64_t b0 = x0 <= 0 || !on ? 0 : div_floor(x0 + wb_l - 1, wb_l, icb_l);
+        int64_t b1 = x1 <= 0 || !on ? 0 : div_floor(x1 + wb_l - 1, wb_l, icb_l);
         b0 = b0 < nb_l ? b0 : nb_l;
         b1 = b1 < nb_l ? b1 : nb_l;
         const int lkbr = (r_l > 16) + (r_l > 32) + (r_l > 64);     // log2 of 16-channel blocks
@@ -869,6 +874,7 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
     // the appended token can be published (its tier from the same input and
     // the counts this workgroup read, so admission matches the encoder's)
     if (appending && wave == 0) {
+        const int app_tier = __builtin_amdgcn_readfirstlane(app_tier_v);
         int slot, n;
         if (append_admit(ly, app_tier, rg.cnt, slot, n) == 0 && lane == 0)
             append_commit(ly, arena, layer, b, h, app_tier, slot, n);
