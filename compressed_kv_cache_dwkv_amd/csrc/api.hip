@@ -30,7 +30,8 @@ static int token_cost(int r, int r_max)
 {
     const int slots = r_max <= 64 ? 4 : 8;                 // 16x16 operand blocks per tile
     const int kbr = r <= 16 ? 1 : r <= 32 ? 2 : r <= 64 ? 4 : 8;
-    const int tokens_per_tile = 16 * (slots / kbr);
+    const int blocks = slots / kbr;                        // 16-token blocks, at most 4 (one token per lane)
+    const int tokens_per_tile = 16 * (blocks < 4 ? blocks : 4);
     return 9216 / tokens_per_tile;
 }
 constexpr int64_t kArenaTail = 8192;

@@ -214,7 +214,7 @@ __device__ __forceinline__ Tile locate(const Ranges &rg, Cursor &cur, const Layo
     t.valid = k < ly.T;
     t.k = t.valid ? k : 0;
     const int lkbr = (int)((uint32_t)__builtin_amdgcn_readlane(rg.nt, t.k) >> 28);
-    const int mbs = NS >> lkbr;
+    const int mbs = lkbr == 0 && NS == 8 ? 4 : NS >> lkbr;     // 16-token blocks: at most 4
     t.kbr = 1 << lkbr;
     t.r = ly.tier[t.k].rank;
     t.s = ly.tier[t.k].resid;
@@ -336,7 +336,7 @@ __device__ __forceinline__ void process_tile(const Tile &t, const TileData<kSlot
                                              _Float16 *ev, int bits, int lane)
 {
     constexpr int NS = kSlots * (KB / 4);
-    constexpr int MBS = NS / KBR;                   // 16-token blocks in the tile
+    constexpr int MBS = NS / KBR < 4 ? NS / KBR : 4; // 16-token blocks in the tile (one token per lane)
     constexpr int GP = GQ < 4 ? 4 : GQ;
     constexpr int NU = GP / 4;                      // score accumulators (4 heads each)
     constexpr int ND = D / 16;
@@ -396,18 +396,19 @@ __device__ __forceinline__ void process_tile(const Tile &t, const TileData<kSlot
         float rk[GP];
 #pragma unroll
         for (int g = 0; g < GP; ++g) rk[g] = 0.0f;
+        // every gather requested before the first is used: one LDS round
+        // trip for the token's entries, not one per entry
+        float4_t qg[kMaxResid][GP / 4];
+#pragma unroll
+        for (int u = 0; u < kMaxResid; ++u)
+#pragma unroll
+            for (int p = 0; p < GP / 4; ++p)
+                qg[u][p] = *reinterpret_cast<const float4_t *>(&s_qt[idx_at(ki0, ki1, u)][4 * p]);
 #pragma unroll
         for (int u = 0; u < kMaxResid; ++u) {
-            const int j = idx_at(ki0, ki1, u);
             const float cv = code_at(kc0, kc1, u, bits);
-            const float4_t q0 = *reinterpret_cast<const float4_t *>(&s_qt[j][0]);
 #pragma unroll
-            for (int g = 0; g < 4; ++g) rk[g] += cv * q0[g];
-            if constexpr (GP == 8) {
-                const float4_t q1 = *reinterpret_cast<const float4_t *>(&s_qt[j][4]);
-#pragma unroll
-                for (int g = 0; g < 4; ++g) rk[4 + g] += cv * q1[g];
-            }
+            for (int g = 0; g < GP; ++g) rk[g] += cv * qg[u][g / 4][g % 4];
         }
         const float sck = h2f((uint16_t)Dt.ksc);
 #pragma unroll
@@ -669,7 +670,9 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
         b0 = b0 < nb_l ? b0 : nb_l;
         b1 = b1 < nb_l ? b1 : nb_l;
         const int lkbr = (r_l > 16) + (r_l > 32) + (r_l > 64);     // log2 of 16-channel blocks
-        const int lmbs = (NS == 8 ? 3 : 2) - lkbr;                 // log2 of 16-token blocks per tile
+        // log2 of 16-token blocks per tile: NS / (channel blocks), at most 4
+        // (one token per lane)
+        const int lmbs = lkbr == 0 ? 2 : (NS == 8 ? 3 : 2) - lkbr;
         const int nt_l = (int)((b1 - b0 + (1 << lmbs) - 1) >> lmbs);
         rg.b0 = (int)b0;
         rg.b1 = (int)b1;

@@ -120,6 +120,15 @@ def test_wide_basis_identity_d128(G):
     _run(G, cfg, layers=(0,), splits=6, identity=True, peak=8.0)
 
 
+def test_wide_basis_low_rank_tiers(G):
+    """r_max = 128 (the wide kernel, 8 operand slots per tile) with tiers of
+    rank 8 and 16: a tile of such a tier still holds at most 64 tokens."""
+    cfg = tiny_config(batch=2, num_kv_heads=2, num_q_heads=8, head_dim=128, r_max=128,
+                      tier_rank=(8, 16, 64, 128), tier_prob=(0.4, 0.3, 0.2, 0.1), resid_channels=8,
+                      resid_bits=4, n_tokens=2500)
+    _run(G, cfg, layers=(0, 1), splits=6, peak=4.0)
+
+
 # ---------------------------------------------------------------- full-size workloads
 # Every layer of these workloads is decoded in the launch configuration the
 # benchmark uses (automatic split count); the oracle checks sampled
