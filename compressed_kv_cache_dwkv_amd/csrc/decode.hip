@@ -80,6 +80,30 @@ __device__ __forceinline__ half4_t in_reg(half4_t v)
     return __builtin_bit_cast(half4_t, b);
 }
 
+// Ends a batch of LDS reads: the reads before it are all issued before
+// anything after it, so a batch costs one LDS round trip (left alone, the
+// compiler waits for each read before issuing the next).
+__device__ __forceinline__ void lds_batch_end() { asm volatile("" ::: "memory"); }
+
+// Eight loaded operands held in registers at once: the empty asm takes
+// them all, so their reads are issued together and waited for once.
+__device__ __forceinline__ void hold8(half8_t (&e)[4][2])
+{
+    asm volatile("" : "+v"(e[0][0]), "+v"(e[0][1]), "+v"(e[1][0]), "+v"(e[1][1]), "+v"(e[2][0]), "+v"(e[2][1]),
+                 "+v"(e[3][0]), "+v"(e[3][1]));
+}
+
+__device__ __forceinline__ void hold8(float4_t (&e)[8])
+{
+    asm volatile("" : "+v"(e[0]), "+v"(e[1]), "+v"(e[2]), "+v"(e[3]), "+v"(e[4]), "+v"(e[5]), "+v"(e[6]),
+                 "+v"(e[7]));
+}
+
+__device__ __forceinline__ void hold4(float4_t (&e)[4])
+{
+    asm volatile("" : "+v"(e[0]), "+v"(e[1]), "+v"(e[2]), "+v"(e[3]));
+}
+
 // The fp16 values of v whose 16-bit lanes of (m0, m1) are ones; the others 0.
 __device__ __forceinline__ half4_t keep_h4(half4_t v, uint32_t m0, uint32_t m1)
 {
@@ -171,6 +195,7 @@ struct Tile {
     int k;            // tier
     int r, s;         // rank and residual channels of the tier
     int kbr;          // 16-channel blocks of the rank (1, 2, 4, 8)
+    int lkbr;         // log2(kbr)
     int nv;           // valid tokens (<= 16 * slots / kbr)
     int blk0;         // first 16-token block
 };
@@ -216,6 +241,7 @@ __device__ __forceinline__ Tile locate(const Ranges &rg, Cursor &cur, const Layo
     const int lkbr = (int)((uint32_t)__builtin_amdgcn_readlane(rg.nt, t.k) >> 28);
     const int mbs = lkbr == 0 && NS == 8 ? 4 : NS >> lkbr;     // 16-token blocks: at most 4
     t.kbr = 1 << lkbr;
+    t.lkbr = lkbr;
     t.r = ly.tier[t.k].rank;
     t.s = ly.tier[t.k].resid;
     const int blk0 = __builtin_amdgcn_readlane(rg.b0, t.k) + rem * mbs;
@@ -267,7 +293,7 @@ __device__ __forceinline__ void issue_tile(const Tile &t, TileData<NS> &D, __amd
     const uint32_t kl = v ? (uint32_t)(c16 * r + 4 * grp) * 2u : kbv;   // token c16, channels 4grp..
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
-        const int mb = i / kbr, kb = i - mb * kbr;
+        const int mb = i >> t.lkbr, kb = i & (kbr - 1);
         const uint32_t ko = v ? sK + (uint32_t)(16 * mb * r + 16 * kb) * 2u : (uint32_t)i * 32u;
         D.ka[i] = __builtin_bit_cast(half4_t, __builtin_amdgcn_raw_buffer_load_b64(rk, kl, ko, 0));
         D.va[i] = __builtin_bit_cast(
@@ -298,9 +324,11 @@ __device__ __forceinline__ void issue_tile(const Tile &t, TileData<NS> &D, __amd
 // Per-wave state of the online softmax and the value sums.
 template <int GQ, int KB, int D>
 struct WaveAcc {
-    float4_t O[KB];                      // basis-space value sums [head row][channel]
+    // basis-space value sums, 16 / GP channel blocks per accumulator: row
+    // GP q + g, column c of accumulator a is head g, channel 16 (a 16 / GP + q) + c
+    float4_t O[KB * (GQ < 4 ? 4 : GQ) / 16];
     float4_t Ores[D / 16];               // residual value mass [head row][channel]
-    float4_t Ol;                         // normalisers: column 0 holds sum_t p per head row
+    float l[GQ];                         // this lane's share of the normalisers
     float m[GQ];                         // running max per head (the same in every lane)
 };
 
@@ -329,67 +357,75 @@ __device__ __forceinline__ const _Float16 *p_row(const _Float16 *sP, int c16)
     return sP + (c16 < GQ ? c16 : GQ) * kPStride;
 }
 
-template <int GQ, int KB, int D, int KBR>
+// One tile of a wave: every rank class runs the same instructions, the
+// slot -> (16-token block, 16-channel block) map coming from the tile at run
+// time, so the accumulators never pass through per-class code paths.
+template <int GQ, int KB, int D>
 __device__ __forceinline__ void process_tile(const Tile &t, const TileData<kSlots * (KB / 4)> &Dt,
-                                             const half4_t *qop, WaveAcc<GQ, KB, D> &A,
+                                             const half4_t *s_qb, WaveAcc<GQ, KB, D> &A,
                                              const float (*s_qt)[GQ < 4 ? 4 : GQ], _Float16 *sP,
                                              _Float16 *ev, int bits, int lane)
 {
     constexpr int NS = kSlots * (KB / 4);
-    constexpr int MBS = NS / KBR < 4 ? NS / KBR : 4; // 16-token blocks in the tile (one token per lane)
     constexpr int GP = GQ < 4 ? 4 : GQ;
     constexpr int NU = GP / 4;                      // score accumulators (4 heads each)
     constexpr int ND = D / 16;
+    constexpr int G4 = 16 / GP;                     // channel blocks per packed value accumulator
+    constexpr int NA = KB / G4;
     const int c16 = lane & 15, grp = lane >> 4;
-    const int r = t.r, s = t.s, nv = t.nv;
-    const bool full = nv == 16 * MBS;               // uniform: no token masks needed
+    const int r = t.r, s = t.s, nv = t.nv, kbr = t.kbr, lkbr = t.lkbr;
+    // the tile's 16-token blocks (one token per lane: at most 4)
+    const int mbs = (NS >> lkbr) < kTile / 16 ? NS >> lkbr : kTile / 16;
+    const bool full = nv == 16 * mbs;               // uniform: no token masks needed
     const bool tok = lane < nv;                     // this lane's token is in the tile
 
-    // ---- scores, one token per lane: block mb's A rows 4 mb + j carry q' of
-    //      head 4 u + j (hi and lo parts), its B operand the tokens'
-    //      coefficients, so row 4 grp + j of accumulator u is (token lane,
-    //      head 4 u + j).  The q' pieces come from LDS (qop: this lane's
-    //      entry of the operand table).
+    // ---- scores, one token per lane: for slot i (block mb, channel block
+    //      kb) the A rows 4 mb + j carry q' of head 4 u + j (hi and lo
+    //      parts, read from the q' table; other rows read its zero block),
+    //      the B operand the tokens' coefficients, so row 4 grp + j of
+    //      accumulator u is (token lane, head 4 u + j)
     float4_t Sc[NU];
 #pragma unroll
     for (int u = 0; u < NU; ++u) Sc[u] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
     // (the B operand's columns are tokens and every product adds 0 x B into
     // the other blocks' rows: channels past the rank and tokens past the
     // tile must be zeros, not whatever the arena holds there)
+    half4_t qa[NS][NU][2];
 #pragma unroll
-    for (int kb = 0; kb < KBR; ++kb) {
-        half4_t qa[NU][2];
+    for (int i = 0; i < NS; ++i) {
+        const int mb = i >> lkbr, kb = i & (kbr - 1);  // uniform
+        const bool rows = (c16 >> 2) == mb;
+        const half4_t *qp = s_qb + (rows ? kb : KB) * kWave + 16 * grp + (c16 & 3);
 #pragma unroll
         for (int u = 0; u < NU; ++u)
 #pragma unroll
-            for (int hl = 0; hl < 2; ++hl) qa[u][hl] = in_reg(qop[kb * kWave + 4 * u + 8 * hl]);
+            for (int hl = 0; hl < 2; ++hl) qa[i][u][hl] = qp[4 * u + 8 * hl];
+    }
+    lds_batch_end();
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+        const int mb = i >> lkbr, kb = i & (kbr - 1);  // uniform
+        const bool col = mb < kTile / 16 && (full || 16 * mb + c16 < nv);
         const bool chan = 16 * kb + 4 * grp < r;
+        half4_t bk = Dt.ka[i];
+        if (!(col && chan)) bk = half4_t{0, 0, 0, 0};
 #pragma unroll
-        for (int mb = 0; mb < MBS; ++mb) {
-            const bool rows = (c16 >> 2) == mb;
-            const bool col = full || 16 * mb + c16 < nv;
-            half4_t bk = Dt.ka[mb * KBR + kb];
-            if (!(col && chan)) bk = half4_t{0, 0, 0, 0};
+        for (int u = 0; u < NU; ++u)
 #pragma unroll
-            for (int u = 0; u < NU; ++u)
-#pragma unroll
-                for (int hl = 0; hl < 2; ++hl)
-                    Sc[u] = mma16(rows ? qa[u][hl] : half4_t{0, 0, 0, 0}, bk, Sc[u]);
-        }
+            for (int hl = 0; hl < 2; ++hl) Sc[u] = mma16(qa[i][u][hl], bk, Sc[u]);
     }
 
     // ---- residuals, one token per lane.  Entries past s are given index
     //      128 (a zero row of q, the spare row of the V-residual tile) and
-    //      code 0, a whole record word at a time.  K: logit terms from q
-    //      gathered in LDS, added to the lane's scores.  V: the token's
-    //      cells of the dense LDS tile.
+    //      code 0, a whole record word at a time (s = 0: every entry).  K:
+    //      logit terms from q gathered in LDS, added to the lane's scores.
+    //      V: the token's cells of the dense LDS tile.
     float z[GP];
 #pragma unroll
     for (int g = 0; g < GP; ++g) z[g] = Sc[g / 4][g % 4];
-    uint32_t vi0 = 0, vi1 = 0;
-    if (s > 0) {
-        const uint32_t im0 = low_bits(8 * s), im1 = low_bits(8 * s - 32);
-        const uint32_t cm0 = low_bits(bits * s), cm1 = low_bits(bits * s - 32);
+    const uint32_t im0 = low_bits(8 * s), im1 = low_bits(8 * s - 32);
+    const uint32_t cm0 = low_bits(bits * s), cm1 = low_bits(bits * s - 32);
+    {
         const uint32_t ki0 = (Dt.ki0 & im0) | (0x80808080u & ~im0);
         const uint32_t ki1 = (Dt.ki1 & im1) | (0x80808080u & ~im1);
         const uint32_t kc0 = Dt.kc0 & cm0, kc1 = Dt.kc1 & cm1;
@@ -404,33 +440,35 @@ __device__ __forceinline__ void process_tile(const Tile &t, const TileData<kSlot
 #pragma unroll
             for (int p = 0; p < GP / 4; ++p)
                 qg[u][p] = *reinterpret_cast<const float4_t *>(&s_qt[idx_at(ki0, ki1, u)][4 * p]);
+        lds_batch_end();
 #pragma unroll
         for (int u = 0; u < kMaxResid; ++u) {
             const float cv = code_at(kc0, kc1, u, bits);
 #pragma unroll
             for (int g = 0; g < GP; ++g) rk[g] += cv * qg[u][g / 4][g % 4];
         }
-        const float sck = h2f((uint16_t)Dt.ksc);
+        // (a tier without residuals has no scale array: its scale reads 0)
+        const float sck = s > 0 ? h2f((uint16_t)Dt.ksc) : 0.0f;
 #pragma unroll
         for (int g = 0; g < GQ; ++g) z[g] += rk[g] * sck;
-        // V cells (lanes past the tile write finite values of token 0 into
-        // their own columns, which meet probability 0)
-        vi0 = (Dt.vi0 & im0) | (0x80808080u & ~im0);
-        vi1 = (Dt.vi1 & im1) | (0x80808080u & ~im1);
+    }
+    // V cells (lanes past the tile write finite values of token 0 into
+    // their own columns, which meet probability 0)
+    const uint32_t vi0 = (Dt.vi0 & im0) | (0x80808080u & ~im0);
+    const uint32_t vi1 = (Dt.vi1 & im1) | (0x80808080u & ~im1);
+    {
         const uint32_t vc0 = Dt.vc0 & cm0, vc1 = Dt.vc1 & cm1;
-        const _Float16 scv = __builtin_bit_cast(_Float16, (uint16_t)Dt.vsc);
+        const _Float16 scv = s > 0 ? __builtin_bit_cast(_Float16, (uint16_t)Dt.vsc) : (_Float16)0.0f;
 #pragma unroll
         for (int u = 0; u < kMaxResid; ++u) {
             const int pos = u * bits;
             const int code = (int)__builtin_amdgcn_sbfe((int)(pos < 32 ? vc0 : vc1), pos & 31, bits);
             ev[idx_at(vi0, vi1, u) * kEvStride + lane] = (_Float16)(int16_t)code * scv;
         }
-        wave_fence();
     }
-    if (MBS < 4 || !full) {
+    wave_fence();
 #pragma unroll
-        for (int g = 0; g < GQ; ++g) z[g] = tok ? z[g] : -INFINITY;
-    }
+    for (int g = 0; g < GQ; ++g) z[g] = tok ? z[g] : -INFINITY;
 
     // ---- lazy running max: only when a logit passes its head's max by more
     //      than the lag are the max and every accumulator rescaled (rare)
@@ -441,6 +479,9 @@ __device__ __forceinline__ void process_tile(const Tile &t, const TileData<kSlot
 #pragma unroll
     for (int g = 0; g < GQ; ++g) f[g] = 1.0f;
     if (__builtin_amdgcn_ballot_w64(over)) {
+        // (kept a branch: without the barrier the compiler computes the
+        // reductions on every tile and selects their results)
+        asm volatile("" ::: "memory");
 #pragma unroll
         for (int g = 0; g < GQ; ++g) {
             const float tmax = wave_max(z[g]);
@@ -452,117 +493,108 @@ __device__ __forceinline__ void process_tile(const Tile &t, const TileData<kSlot
         }
     }
     // (the factors are applied every tile, 1 when the max held: accumulators
-    // updated inside the branch make the compiler keep two copies of them)
+    // updated inside the branch make the compiler keep two copies of them).
+    // Accumulator row 4 grp + j holds head (4 grp + j) % GP -- or nothing
+    // (rows past the heads are zero, any factor keeps them so).
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        float fh = 1.0f;                             // accumulator row 4 grp + j is head 4 grp + j
+        float fh = 1.0f;
+        if constexpr (GP == 4) {
+            if (j < GQ) fh = f[j];
+        } else {
+            fh = (grp & 1) ? f[4 + j] : f[j];
+        }
 #pragma unroll
-        for (int g = j; g < GQ; g += 4) fh = 4 * grp + j == g ? f[g] : fh;
-#pragma unroll
-        for (int nb = 0; nb < KB; ++nb) A.O[nb][j] *= fh;
+        for (int a = 0; a < NA; ++a) A.O[a][j] *= fh;
 #pragma unroll
         for (int nb = 0; nb < ND; ++nb) A.Ores[nb][j] *= fh;
-        A.Ol[j] *= fh;
     }
+#pragma unroll
+    for (int g = 0; g < GQ; ++g) A.l[g] *= f[g];
 
-    // ---- probabilities: to LDS in operand order, back as the A operand
-    //      (rows: heads; 32-deep: the chunk's tokens)
+    // ---- probabilities: to LDS in operand order; the lane's normaliser
+    //      terms are the same fp16 values
     {
         const int ps = p_slot(lane);
 #pragma unroll
-        for (int g = 0; g < GQ; ++g) sP[g * kPStride + ps] = (_Float16)fast_exp2(z[g] - A.m[g]);
+        for (int g = 0; g < GQ; ++g) {
+            const _Float16 ph = (_Float16)fast_exp2(z[g] - A.m[g]);
+            sP[g * kPStride + ps] = ph;
+            A.l[g] += (float)ph;
+        }
     }
     wave_fence();
-    const _Float16 *prow = p_row<GQ>(sP, c16);
-    constexpr int NP = MBS == 1 ? 1 : MBS / 2;
-    half8_t PA[NP];
-    half4_t P1 = half4_t{0, 0, 0, 0};
-    if constexpr (MBS == 1) {
-        P1 = *reinterpret_cast<const half4_t *>(prow + 8 * grp);
-    } else {
-#pragma unroll
-        for (int p = 0; p < NP; ++p) PA[p] = *reinterpret_cast<const half8_t *>(prow + 32 * p + 8 * grp);
-    }
 
-    // ---- values: probabilities x V coefficient columns; the normaliser is
-    //      the same product with a column of ones (fp32 sums of the fp16
-    //      probabilities the values use)
-    const _Float16 one = c16 == 0 ? (_Float16)1.0f : (_Float16)0.0f;
-    const half4_t ones = half4_t{one, one, one, one};
-    // V coefficients of tokens past the tile are zeroed (they meet p = 0,
-    // but 0 x whatever the arena holds there need not be 0): whole-register
-    // masks, so the tile's registers stay registers
+    // ---- values: P x V coefficients in basis space.  Slot i adds its
+    //      16 tokens x 16 channels into the packed accumulator of channel
+    //      block kb: rows GP (kb % G4) + g are head g, the A rows of the
+    //      lanes of other blocks read the zero row.  V coefficients of
+    //      tokens past the tile are zeroed (they meet p = 0, but 0 x whatever
+    //      the arena holds there need not be 0): whole-register masks.
+    const int rq = c16 / GP, rh = c16 % GP;         // this lane's A row: block group, head
     half4_t va[NS];
 #pragma unroll
     for (int i = 0; i < NS; ++i) va[i] = Dt.va[i];
     if (!full) {
 #pragma unroll
-        for (int mb = 0; mb < MBS; ++mb) {
-            const int t0 = 16 * mb + 4 * grp;
+        for (int i = 0; i < NS; ++i) {
+            const int t0 = 16 * (i >> lkbr) + 4 * grp;
             const uint32_t m0 = (t0 < nv ? 0xFFFFu : 0u) | (t0 + 1 < nv ? 0xFFFF0000u : 0u);
             const uint32_t m1 = (t0 + 2 < nv ? 0xFFFFu : 0u) | (t0 + 3 < nv ? 0xFFFF0000u : 0u);
-#pragma unroll
-            for (int kb = 0; kb < KBR; ++kb) va[mb * KBR + kb] = keep_h4(va[mb * KBR + kb], m0, m1);
+            va[i] = keep_h4(va[i], m0, m1);
         }
     }
+    half4_t pv[NS][NA];
 #pragma unroll
-    for (int nb = 0; nb < KBR; ++nb) {
-        half4_t bv[MBS];
-        const bool cv = 16 * nb + c16 < r;
+    for (int i = 0; i < NS; ++i) {
+        const int mb = i >> lkbr, kb = i & (kbr - 1);  // uniform
 #pragma unroll
-        for (int mb = 0; mb < MBS; ++mb) bv[mb] = cv ? va[mb * KBR + nb] : half4_t{0, 0, 0, 0};
-        if constexpr (MBS == 1) {
-            A.O[nb] = mma16(P1, bv[0], A.O[nb]);
-        } else {
-#pragma unroll
-            for (int p = 0; p < NP; ++p)
-                A.O[nb] = mma32(PA[p], cat(bv[2 * p], bv[2 * p + 1]), A.O[nb]);
+        for (int a = 0; a < NA; ++a) {
+            const bool on = mb < kTile / 16 && a * G4 + rq == kb && rh < GQ;
+            const _Float16 *pr = on ? sP + rh * kPStride + 32 * (mb >> 1) + 4 * (mb & 1) + 8 * grp
+                                    : sP + GQ * kPStride + 8 * grp;
+            pv[i][a] = *reinterpret_cast<const half4_t *>(pr);
         }
     }
-    if constexpr (MBS == 1) {
-        A.Ol = mma16(P1, ones, A.Ol);
-    } else {
+    lds_batch_end();
 #pragma unroll
-        for (int p = 0; p < NP; ++p) A.Ol = mma32(PA[p], cat(ones, ones), A.Ol);
+    for (int i = 0; i < NS; ++i) {
+        const int mb = i >> lkbr, kb = i & (kbr - 1);  // uniform
+        half4_t bv = va[i];
+        if (!(mb < kTile / 16 && 16 * kb + c16 < r)) bv = half4_t{0, 0, 0, 0};
+#pragma unroll
+        for (int a = 0; a < NA; ++a) A.O[a] = mma16(pv[i][a], bv, A.O[a]);
     }
 
-    // ---- V residual mass: the dense tile times the probabilities, then the
-    //      written cells are cleared (after the reads: same wave, in order)
-    if (s > 0) {
+    // ---- V residual mass: the dense tile times the probabilities (32-deep
+    //      chunks; tokens past the tile have p = 0), then the written cells
+    //      are cleared (after the reads: same wave, in order)
+    {
+        const _Float16 *prow = p_row<GQ>(sP, c16);
+        half8_t PA[kTile / 32];
+#pragma unroll
+        for (int p = 0; p < kTile / 32; ++p) PA[p] = *reinterpret_cast<const half8_t *>(prow + 32 * p + 8 * grp);
         const _Float16 *evr = ev + c16 * kEvStride + 4 * grp;
+        constexpr int NB = ND < 4 ? ND : 4;          // channel blocks per batch of reads
 #pragma unroll
-        for (int nb = 0; nb < ND; ++nb) {
-            if constexpr (MBS == 1) {
-                const half4_t e0 = *reinterpret_cast<const half4_t *>(evr + 16 * nb * kEvStride);
-                A.Ores[nb] = mma16(P1, e0, A.Ores[nb]);
-            } else {
+        for (int n0 = 0; n0 < ND; n0 += NB) {
+            half8_t E[NB][kTile / 32];
 #pragma unroll
-                for (int p = 0; p < NP; ++p) {
-                    const half4_t e0 = *reinterpret_cast<const half4_t *>(evr + 16 * nb * kEvStride + 32 * p);
-                    const half4_t e1 = *reinterpret_cast<const half4_t *>(evr + 16 * nb * kEvStride + 32 * p + 16);
-                    A.Ores[nb] = mma32(PA[p], cat(e0, e1), A.Ores[nb]);
+            for (int q = 0; q < NB; ++q)
+#pragma unroll
+                for (int p = 0; p < kTile / 32; ++p) {
+                    const _Float16 *e = evr + 16 * (n0 + q) * kEvStride + 32 * p;
+                    E[q][p] = cat(*reinterpret_cast<const half4_t *>(e), *reinterpret_cast<const half4_t *>(e + 16));
                 }
-            }
+            if constexpr (NB == 4 && kTile / 32 == 2) hold8(E);
+#pragma unroll
+            for (int q = 0; q < NB; ++q)
+#pragma unroll
+                for (int p = 0; p < kTile / 32; ++p) A.Ores[n0 + q] = mma32(PA[p], E[q][p], A.Ores[n0 + q]);
         }
         wave_fence();
 #pragma unroll
         for (int u = 0; u < kMaxResid; ++u) ev[idx_at(vi0, vi1, u) * kEvStride + lane] = (_Float16)0.0f;
-    }
-}
-
-template <int GQ, int KB, int D>
-__device__ __forceinline__ void process_any(const Tile &t, const TileData<kSlots * (KB / 4)> &Dt,
-                                            const half4_t *qop, WaveAcc<GQ, KB, D> &A,
-                                            const float (*s_qt)[GQ < 4 ? 4 : GQ], _Float16 *sP,
-                                            _Float16 *ev, int bits, int lane)
-{
-    switch (t.kbr) {
-    case 1: process_tile<GQ, KB, D, 1>(t, Dt, qop, A, s_qt, sP, ev, bits, lane); break;
-    case 2: process_tile<GQ, KB, D, 2>(t, Dt, qop, A, s_qt, sP, ev, bits, lane); break;
-    case 4: process_tile<GQ, KB, D, 4>(t, Dt, qop, A, s_qt, sP, ev, bits, lane); break;
-    default:
-        if constexpr (KB == 8) process_tile<GQ, KB, D, 8>(t, Dt, qop, A, s_qt, sP, ev, bits, lane);
-        break;
     }
 }
 
@@ -591,7 +623,7 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
     constexpr int kQpBytes = (GQ * (RMAX + D) * 4 / kWaves + 15) / 16 * 16;
     constexpr int kWvBytes = kPBytes > kQpBytes ? kPBytes : kQpBytes;
     __shared__ __attribute__((aligned(16))) uint8_t s_wv[kWaves * kWvBytes];
-    __shared__ half4_t s_qb[KB * kWave];           // score operand q', [channel block][lane]
+    __shared__ half4_t s_qb[(KB + 1) * kWave];     // score operand q', [channel block][lane]; block KB zero
     __shared__ float s_m[kWaves][GQ], s_l[kWaves][GQ];
     __shared__ float s_M[GQ], s_L[GQ];
     __shared__ int s_last;
@@ -720,6 +752,7 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
         }
         s_qb[wave * kWave + lane] = v;
     }
+    if (wave == KB % kWaves) s_qb[KB * kWave + lane] = half4_t{0, 0, 0, 0};
     if (encoder && wave < 2) {
         int slot, n;
         append_encode<D>(app, ly, arena, layer, b, h, wave, lane, ap, carve_append_lds(s_ev), slot, n);
@@ -735,28 +768,31 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
         }
     }
     if (encoder) __syncthreads();                  // waves 2, 3 write their tiles only after this
-    // the A operand of the scores for lane (c16, grp): q' (hi, lo) of head
-    // 4 u + c16 % 4, channels 16 kb + 4 grp + 0..3, at qop[64 kb + 4 u + 8 hl]
-    const half4_t *qop = s_qb + 16 * grp + (c16 & 3);
+    // (the A operand of the scores for lane (c16, grp): q' (hi, lo) of head
+    // 4 u + c16 % 4, channels 16 kb + 4 grp + 0..3, at s_qb[64 kb + 16 grp +
+    // c16 % 4 + 4 u + 8 hl])
     // this wave's probability rows; row GQ (the padding heads' operand) zero
     _Float16 *sP = reinterpret_cast<_Float16 *>(s_wv + wave * kWvBytes);
     if (lane < kPStride / 8) reinterpret_cast<uint4 *>(sP + GQ * kPStride)[lane] = uint4{0u, 0u, 0u, 0u};
 
     // ---- main loop: two-deep pipeline over this wave's tiles
     WaveAcc<GQ, KB, D> A;
+    constexpr int NA = KB * GP / 16;               // packed value accumulators
 #pragma unroll
-    for (int nb = 0; nb < KB; ++nb) A.O[nb] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int a = 0; a < NA; ++a) A.O[a] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int nb = 0; nb < ND; ++nb) A.Ores[nb] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    A.Ol = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int g = 0; g < GQ; ++g) A.m[g] = -INFINITY;
+    for (int g = 0; g < GQ; ++g) {
+        A.l[g] = 0.0f;
+        A.m[g] = -INFINITY;
+    }
     bool bv_in_b = false;                           // the tile past the last holds the B_V operand
     while (ta.valid) {
         cur.rem += kWaves;
         Tile tb = locate<NS>(rg, cur, ly);
         issue_tile<NS>(tb, DB, rb, rbv, kbv, ly, lane);
-        process_any<GQ, KB, D>(ta, DA, qop, A, s_qt, sP, ev, bits, lane);
+        process_tile<GQ, KB, D>(ta, DA, s_qb, A, s_qt, sP, ev, bits, lane);
         if (!tb.valid) {
             bv_in_b = true;
             break;
@@ -764,7 +800,7 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
         cur.rem += kWaves;
         ta = locate<NS>(rg, cur, ly);
         issue_tile<NS>(ta, DA, rb, rbv, kbv, ly, lane);
-        process_any<GQ, KB, D>(tb, DB, qop, A, s_qt, sP, ev, bits, lane);
+        process_tile<GQ, KB, D>(tb, DB, s_qb, A, s_qt, sP, ev, bits, lane);
     }
 
     half4_t bvt[NS];
@@ -773,23 +809,29 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
 
     // ---- merge the waves of this workgroup: each wave leaves its unscaled
     //      sums in its own (now idle) V-residual tile, then one barrier
-    if (lane == 0) {
+    {
+        float lw[GQ];
 #pragma unroll
-        for (int g = 0; g < GQ; ++g) s_m[wave][g] = A.m[g];
-    }
-    if (c16 == 0) {
+        for (int g = 0; g < GQ; ++g) lw[g] = wave_sum(A.l[g]);
+        if (lane == 0) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            if (4 * grp + j < GQ) s_l[wave][4 * grp + j] = A.Ol[j];
+            for (int g = 0; g < GQ; ++g) {
+                s_m[wave][g] = A.m[g];
+                s_l[wave][g] = lw[g];
+            }
+        }
     }
     {
         float *part = reinterpret_cast<float *>(ev);            // [GQ][RMAX + D]
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int row = 4 * grp + j;
-            if (row < GQ) {
+            const int g = row % GP, kq = row / GP;                // packed row: head, block in group
+            if (g < GQ) {
 #pragma unroll
-                for (int nb = 0; nb < KB; ++nb) part[row * (RMAX + D) + 16 * nb + c16] = A.O[nb][j];
+                for (int a = 0; a < NA; ++a) part[g * (RMAX + D) + 16 * (a * (16 / GP) + kq) + c16] = A.O[a][j];
+            }
+            if (row < GQ) {
 #pragma unroll
                 for (int nb = 0; nb < ND; ++nb) part[row * (RMAX + D) + RMAX + 16 * nb + c16] = A.Ores[nb][j];
             }
@@ -800,27 +842,35 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
     // merged sums go to the K-residual area, idle now
     float *s_qp = reinterpret_cast<float *>(s_wv);                // [GQ][RMAX + D]
     static_assert((RMAX + D) % 4 == 0 && (kEvWave * 2) % 16 == 0, "float4 merge");
+    static_assert(kWaves == 8, "one batch of eight wave parts");
     for (int i4 = 4 * tid; i4 < GQ * (RMAX + D); i4 += 4 * kBlock) {
         const int g = i4 / (RMAX + D);
-        float M = -INFINITY;
+        float4_t pw[kWaves];
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w][g]);
-        float4_t acc = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int w = 0; w < kWaves; ++w)
+            pw[w] = *reinterpret_cast<const float4_t *>(reinterpret_cast<const float *>(s_ev + w * kEvWave) + i4);
+        float mw[kWaves], lw[kWaves];
+        float M = -INFINITY;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
-            const float f = M == -INFINITY ? 0.0f : fast_exp2(s_m[w][g] - M);
-            acc += f * *reinterpret_cast<const float4_t *>(reinterpret_cast<const float *>(s_ev + w * kEvWave) + i4);
+            mw[w] = s_m[w][g];
+            lw[w] = s_l[w][g];
+            M = fmaxf(M, mw[w]);
+        }
+        hold8(pw);
+        float4_t acc = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        float L = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const float f = M == -INFINITY ? 0.0f : fast_exp2(mw[w] - M);
+            acc += f * pw[w];
+            L += f * lw[w];
         }
         *reinterpret_cast<float4_t *>(s_qp + i4) = acc;
-    }
-    if (tid < GQ) {
-        const int g = tid;
-        float M = -INFINITY;
-        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w][g]);
-        float L = 0.0f;
-        for (int w = 0; w < kWaves; ++w) L += (M == -INFINITY ? 0.0f : exp2f(s_m[w][g] - M)) * s_l[w][g];
-        s_M[g] = M;
-        s_L[g] = L;
+        if (i4 == g * (RMAX + D)) {
+            s_M[g] = M;
+            s_L[g] = L;
+        }
     }
     __syncthreads();
     // one back-projection through B_V plus the residual mass, on the matrix
@@ -831,13 +881,23 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
     if (wave < ND) {
         float4_t acc = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
         const int g = c16 & 7;
+        const int gr = g < GQ ? g : 0;
+        static_assert(NS == 4 || NS == 8, "back-projection batches");
+        float4_t av[NS];
+#pragma unroll
+        for (int kb = 0; kb < NS; ++kb)
+            av[kb] = *reinterpret_cast<const float4_t *>(&s_qp[gr * (RMAX + D) + 16 * kb + 4 * grp]);
+        const float4_t res =
+            *reinterpret_cast<const float4_t *>(&s_qp[gr * (RMAX + D) + RMAX + 16 * wave + 4 * grp]);
+#pragma unroll
+        for (int k0 = 0; k0 < NS; k0 += 4) hold4(*reinterpret_cast<float4_t (*)[4]>(&av[k0]));
 #pragma unroll
         for (int kb = 0; kb < NS; ++kb) {
             half4_t bb;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int i = 16 * kb + 4 * grp + j;
-                const float x = g < GQ && i < R ? s_qp[g * (RMAX + D) + i] : 0.0f;
+                const float x = g < GQ && i < R ? av[kb][j] : 0.0f;
                 const _Float16 xh = (_Float16)x;
                 bb[j] = c16 < 8 ? xh : (_Float16)(x - (float)xh);
             }
@@ -847,8 +907,7 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
             float *po = ws.po + (((int64_t)b * ly.Hq + g0 + c16) * S + split) * D + 16 * wave + 4 * grp;
             float o[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                o[j] = acc[j] + row_swap8(acc[j]) + s_qp[c16 * (RMAX + D) + RMAX + 16 * wave + 4 * grp + j];
+            for (int j = 0; j < 4; ++j) o[j] = acc[j] + row_swap8(acc[j]) + res[j];
             st_agent2(po, o[0], o[1]);
             st_agent2(po + 2, o[2], o[3]);
         }
