@@ -55,10 +55,14 @@ constexpr int kBlock = 512;               // 8 waves: one workgroup fills a comp
 constexpr int kWaves = kBlock / kWave;
 constexpr int kTile = 64;                 // most tokens in a tile
 constexpr int kSlots = 4;                 // 16x16 operand blocks per tile and Z (rank <= 64)
-constexpr int kEvStride = kTile + 4;      // fp16 per channel row of the V-residual tile (padded:
-                                          // the 16 lanes of an operand read hit distinct banks)
-constexpr int kEvRows = kMaxHeadDim + 1;  // channel rows plus one row that absorbs unused entries
-constexpr int kEvWave = (kEvRows * kEvStride + 7) / 8 * 8;   // fp16 per wave, 16-byte multiple
+// The per-wave V-residual tile: channel rows (plus one row that absorbs
+// unused entries) of fp16 cells, one column per token in 32-deep operand
+// order.  Rows are padded so that the 16 rows of an operand read hit
+// distinct banks: to 72 fp16 (16-byte reads) where the LDS holds it, else
+// (8 query heads per KV head) to 68 (8-byte reads).
+constexpr int kEvRows = kMaxHeadDim + 1;
+constexpr int ev_stride(int gq) { return gq > 4 ? kTile + 4 : kTile + 8; }
+constexpr int ev_wave(int gq) { return (kEvRows * ev_stride(gq) + 7) / 8 * 8; }   // fp16, 16-byte multiple
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kMaxLag = 8.0f;           // log2 units the running max may trail
 // The append's encoding, done by the first workgroup of each (sequence, KV
@@ -378,6 +382,10 @@ __device__ __forceinline__ void process_tile(const Tile &t, const TileData<kSlot
     const int mbs = (NS >> lkbr) < kTile / 16 ? NS >> lkbr : kTile / 16;
     const bool full = nv == 16 * mbs;               // uniform: no token masks needed
     const bool tok = lane < nv;                     // this lane's token is in the tile
+    // this lane's token column in the probability table and the V-residual
+    // tile (32-deep operand order: one 16-byte read per operand)
+    const int ps = p_slot(lane);
+    constexpr int EVS = ev_stride(GQ);
 
     // ---- scores, one token per lane: for slot i (block mb, channel block
     //      kb) the A rows 4 mb + j carry q' of head 4 u + j (hi and lo
@@ -452,18 +460,18 @@ __device__ __forceinline__ void process_tile(const Tile &t, const TileData<kSlot
 #pragma unroll
         for (int g = 0; g < GQ; ++g) z[g] += rk[g] * sck;
     }
-    // V cells (lanes past the tile write finite values of token 0 into
-    // their own columns, which meet probability 0)
+    // V cells of the lane's token (lanes past the tile leave their columns
+    // zero)
     const uint32_t vi0 = (Dt.vi0 & im0) | (0x80808080u & ~im0);
     const uint32_t vi1 = (Dt.vi1 & im1) | (0x80808080u & ~im1);
-    {
+    if (tok) {
         const uint32_t vc0 = Dt.vc0 & cm0, vc1 = Dt.vc1 & cm1;
         const _Float16 scv = s > 0 ? __builtin_bit_cast(_Float16, (uint16_t)Dt.vsc) : (_Float16)0.0f;
 #pragma unroll
         for (int u = 0; u < kMaxResid; ++u) {
             const int pos = u * bits;
             const int code = (int)__builtin_amdgcn_sbfe((int)(pos < 32 ? vc0 : vc1), pos & 31, bits);
-            ev[idx_at(vi0, vi1, u) * kEvStride + lane] = (_Float16)(int16_t)code * scv;
+            ev[idx_at(vi0, vi1, u) * EVS + ps] = (_Float16)(int16_t)code * scv;
         }
     }
     wave_fence();
@@ -515,7 +523,6 @@ __device__ __forceinline__ void process_tile(const Tile &t, const TileData<kSlot
     // ---- probabilities: to LDS in operand order; the lane's normaliser
     //      terms are the same fp16 values
     {
-        const int ps = p_slot(lane);
 #pragma unroll
         for (int g = 0; g < GQ; ++g) {
             const _Float16 ph = (_Float16)fast_exp2(z[g] - A.m[g]);
@@ -574,7 +581,7 @@ __device__ __forceinline__ void process_tile(const Tile &t, const TileData<kSlot
         half8_t PA[kTile / 32];
 #pragma unroll
         for (int p = 0; p < kTile / 32; ++p) PA[p] = *reinterpret_cast<const half8_t *>(prow + 32 * p + 8 * grp);
-        const _Float16 *evr = ev + c16 * kEvStride + 4 * grp;
+        const _Float16 *evr = ev + c16 * EVS + 8 * grp;
         constexpr int NB = ND < 4 ? ND : 4;          // channel blocks per batch of reads
 #pragma unroll
         for (int n0 = 0; n0 < ND; n0 += NB) {
@@ -583,8 +590,11 @@ __device__ __forceinline__ void process_tile(const Tile &t, const TileData<kSlot
             for (int q = 0; q < NB; ++q)
 #pragma unroll
                 for (int p = 0; p < kTile / 32; ++p) {
-                    const _Float16 *e = evr + 16 * (n0 + q) * kEvStride + 32 * p;
-                    E[q][p] = cat(*reinterpret_cast<const half4_t *>(e), *reinterpret_cast<const half4_t *>(e + 16));
+                    const _Float16 *e = evr + 16 * (n0 + q) * EVS + 32 * p;
+                    if constexpr (EVS % 8 == 0)
+                        E[q][p] = *reinterpret_cast<const half8_t *>(e);
+                    else
+                        E[q][p] = cat(*reinterpret_cast<const half4_t *>(e), *reinterpret_cast<const half4_t *>(e + 4));
                 }
             if constexpr (NB == 4 && kTile / 32 == 2) hold8(E);
 #pragma unroll
@@ -593,8 +603,10 @@ __device__ __forceinline__ void process_tile(const Tile &t, const TileData<kSlot
                 for (int p = 0; p < kTile / 32; ++p) A.Ores[n0 + q] = mma32(PA[p], E[q][p], A.Ores[n0 + q]);
         }
         wave_fence();
+        if (tok) {
 #pragma unroll
-        for (int u = 0; u < kMaxResid; ++u) ev[idx_at(vi0, vi1, u) * kEvStride + lane] = (_Float16)0.0f;
+            for (int u = 0; u < kMaxResid; ++u) ev[idx_at(vi0, vi1, u) * EVS + ps] = (_Float16)0.0f;
+        }
     }
 }
 
@@ -615,7 +627,8 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
     const int R = ly.R, bits = ly.bits;
     const int g0 = h * GQ;
 
-    __shared__ __attribute__((aligned(16))) _Float16 s_ev[kWaves * kEvWave];   // V-residual tiles
+    constexpr int EVW = ev_wave(GQ);
+    __shared__ __attribute__((aligned(16))) _Float16 s_ev[kWaves * EVW];   // V-residual tiles
     __shared__ __attribute__((aligned(16))) float s_qt[kMaxHeadDim + 1][GP];   // q, base-2 units; zero rows
                                                                                 // from D on (row 128: unused entries)
     // per-wave area: the tile probabilities in the loop, the merged sums after
@@ -724,12 +737,12 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
         const int j = i / GP, g = i % GP;
         s_qt[j][g] = g < GQ && j < D ? qscale * h2f(q[((int64_t)b * ly.Hq + g0 + g) * D + j]) : 0.0f;
     }
-    _Float16 *ev = s_ev + wave * kEvWave;
+    _Float16 *ev = s_ev + wave * EVW;
     constexpr int kAppendTiles = 4;                 // V-residual tiles the append scratch covers
-    static_assert(kAppendLdsBytes <= kAppendTiles * kEvWave * sizeof(_Float16), "append scratch");
+    static_assert(kAppendLdsBytes <= kAppendTiles * EVW * sizeof(_Float16), "append scratch");
     if (!(encoder && wave < kAppendTiles)) {
         uint4 *e4 = reinterpret_cast<uint4 *>(ev);
-        for (int i = lane; i < kEvWave / 8; i += kWave) e4[i] = uint4{0u, 0u, 0u, 0u};
+        for (int i = lane; i < EVW / 8; i += kWave) e4[i] = uint4{0u, 0u, 0u, 0u};
     }
 
     // ---- score operand qb: q' = B_K q on the matrix cores, straight into
@@ -763,8 +776,8 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
         // the append scratch spanned
 #pragma unroll
         for (int t = 0; t < kAppendTiles / 2; ++t) {
-            uint4 *e4 = reinterpret_cast<uint4 *>(s_ev + (wave + 2 * t) * kEvWave);
-            for (int i = lane; i < kEvWave / 8; i += kWave) e4[i] = uint4{0u, 0u, 0u, 0u};
+            uint4 *e4 = reinterpret_cast<uint4 *>(s_ev + (wave + 2 * t) * EVW);
+            for (int i = lane; i < EVW / 8; i += kWave) e4[i] = uint4{0u, 0u, 0u, 0u};
         }
     }
     if (encoder) __syncthreads();                  // waves 2, 3 write their tiles only after this
@@ -841,14 +854,14 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
     // weights 2^(m_w - M) in a fixed wave order (bitwise reproducible);
     // merged sums go to the K-residual area, idle now
     float *s_qp = reinterpret_cast<float *>(s_wv);                // [GQ][RMAX + D]
-    static_assert((RMAX + D) % 4 == 0 && (kEvWave * 2) % 16 == 0, "float4 merge");
+    static_assert((RMAX + D) % 4 == 0 && (EVW * 2) % 16 == 0, "float4 merge");
     static_assert(kWaves == 8, "one batch of eight wave parts");
     for (int i4 = 4 * tid; i4 < GQ * (RMAX + D); i4 += 4 * kBlock) {
         const int g = i4 / (RMAX + D);
         float4_t pw[kWaves];
 #pragma unroll
         for (int w = 0; w < kWaves; ++w)
-            pw[w] = *reinterpret_cast<const float4_t *>(reinterpret_cast<const float *>(s_ev + w * kEvWave) + i4);
+            pw[w] = *reinterpret_cast<const float4_t *>(reinterpret_cast<const float *>(s_ev + w * EVW) + i4);
         float mw[kWaves], lw[kWaves];
         float M = -INFINITY;
 #pragma unroll
