@@ -67,8 +67,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kMaxLag = 8.0f;           // log2 units the running max may trail
 // The append's encoding, done by the first workgroup of each (sequence, KV
 // head) before its share of the tiles, in the units of the work balance
-// (9216 per tile; measured: shares reduced by 20 to 30 tiles hide it).
-constexpr int64_t kEncodeUnits = 250000;
+// (9216 per tile; measured: a share about 22 tiles smaller hides it).
+constexpr int64_t kEncodeUnits = 200000;
 
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
@@ -671,9 +671,6 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
     // which no tile of this launch uses, and the last workgroup publishes it.
     const bool appending = ap.k != nullptr;
     const bool encoder = appending && split == 0;
-    // the new token's tier, for the workgroup that publishes it (requested
-    // now, with the counts, so publishing waits for no memory)
-    const int app_tier_v = appending ? ap.tier[b * ly.Hkv + h] : 0;
     AppendRegs<D> app;
     if (encoder && wave < 2) append_fetch<D>(app, ly, arena, layer, b, h, wave, lane, ap);
 
@@ -945,15 +942,9 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
     }
     __syncthreads();
     if (!s_last) return;
-    // every workgroup of this (sequence, KV head) has read the token counts:
-    // the appended token can be published (its tier from the same input and
-    // the counts this workgroup read, so admission matches the encoder's)
-    if (appending && wave == 0) {
-        const int app_tier = __builtin_amdgcn_readfirstlane(app_tier_v);
-        int slot, n;
-        if (append_admit(ly, app_tier, rg.cnt, slot, n) == 0 && lane == 0)
-            append_commit(ly, arena, layer, b, h, app_tier, slot, n);
-    }
+    // the appended token's tier (requested with the partials: publishing,
+    // after the merge, waits for no memory of its own)
+    const int app_tier_v = appending && wave == 0 ? ap.tier[b * ly.Hkv + h] : 0;
     // Each thread owns 4 adjacent outputs of one head and an interleaved
     // subset of the splits.  Its first 8 partial vectors are requested
     // together with every split's max and normaliser, so the merge waits
@@ -1018,6 +1009,15 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
         const float L = s_L[hq];
         const float inv = L > 0.0f ? 1.0f / L : 0.0f;
         *reinterpret_cast<float4_t *>(out + ((int64_t)b * ly.Hq + g0 + hq) * D + j4) = o * inv;
+    }
+    // every workgroup of this (sequence, KV head) has read the token counts:
+    // the appended token can be published (its tier from the same input and
+    // the counts this workgroup read, so admission matches the encoder's)
+    if (appending && wave == 0) {
+        const int app_tier = __builtin_amdgcn_readfirstlane(app_tier_v);
+        int slot, n;
+        if (append_admit(ly, app_tier, rg.cnt, slot, n) == 0 && lane == 0)
+            append_commit(ly, arena, layer, b, h, app_tier, slot, n);
     }
     if (tid == 0) __hip_atomic_store(&ws.arrive[b * ly.Hkv + h], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
