@@ -183,16 +183,6 @@ __device__ __forceinline__ float4_t ld_agent4(const float *p)
                     __uint_as_float((uint32_t)b), __uint_as_float((uint32_t)(b >> 32))};
 }
 
-// floor(x / w) for 0 <= x < 2^52, w > 0, given inv_w ~ 1 / w: the estimate
-// is off by at most one, which one exact integer check corrects.
-__device__ __forceinline__ int64_t div_floor(int64_t x, int64_t w, double inv_w)
-{
-    int64_t q = (int64_t)((double)x * inv_w);
-    if (q * w > x) --q;
-    else if ((q + 1) * w <= x) ++q;
-    return q;
-}
-
 // Where a tile lies, uniform over the wave.
 struct Tile {
     int valid;        // 0 once the wave has no more tiles
@@ -686,38 +676,36 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
     const uint32_t kbv = (uint32_t)((16 * (wave < ND ? wave : 0) + c16) * R + 4 * grp) * 2u;
     Ranges rg;
     {
+        // (fp32: every workgroup evaluates the same expressions for a shared
+        // boundary, so neighbours agree exactly; the first and last
+        // boundaries are exact, so the runs cover every block once)
         const bool on = lane < T;
-        const int64_t wb_l = 16 * (int64_t)cost_l;
-        const int64_t nb_l = on ? (cnt_l + 15) >> 4 : 0;
-        const int64_t wt_l = nb_l * wb_l;                     // bytes of tier k's blocks
-        int64_t W = 0, wk_l = 0;                               // total; bytes of tiers before k
+        const int nb_l = on ? (cnt_l + 15) >> 4 : 0;
+        const float wt_l = (float)nb_l * (16.0f * (float)cost_l);   // work of tier k's blocks
+        float W = 0.0f, wk_l = 0.0f;                               // total; work of the tiers before k
 #pragma unroll
         for (int k = 0; k < kMaxTiers; ++k) {
-            const uint32_t lo32 = __builtin_amdgcn_readlane((uint32_t)wt_l, k);
-            const uint32_t hi32 = __builtin_amdgcn_readlane((uint32_t)(wt_l >> 32), k);
-            const int64_t wt = (int64_t)(((uint64_t)hi32 << 32) | lo32);
+            const float wt = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wt_l), k));
             if (lane > k) wk_l += wt;
             W += wt;
         }
         // the encoding workgroup starts its share later: its boundaries
         // move down by the encoding's cost in balance units
-        const int64_t E = appending ? kEncodeUnits : 0;
-        int64_t lo = div_floor((W + E) * split, S, invS) - E;
-        int64_t hi = div_floor((W + E) * (split + 1), S, invS) - E;
-        lo = lo > 0 ? lo : 0;
-        hi = hi > 0 ? hi : 0;
-        const int64_t x0 = lo - wk_l, x1 = hi - wk_l;
-        int64_t b0 = x0 <= 0 || !on ? 0 : div_floor(x0 + wb_l - 1, wb_l, icb_l);
-        int64_t b1 = x1 <= 0 || !on ? 0 : div_floor(x1 + wb_l - 1, wb_l, icb_l);
-        b0 = b0 < nb_l ? b0 : nb_l;
-        b1 = b1 < nb_l ? b1 : nb_l;
+        const float E = appending ? (float)kEncodeUnits : 0.0f;
+        const float step = (W + E) * (float)invS;
+        const float icb = (float)icb_l;
+        const float x0 = fmaxf(floorf(step * (float)split) - E, 0.0f) - wk_l;
+        const float x1 = fmaxf(floorf(step * (float)(split + 1)) - E, 0.0f) - wk_l;
+        const int c0 = (int)fmaxf(ceilf(x0 * icb), 0.0f), c1 = (int)fmaxf(ceilf(x1 * icb), 0.0f);
+        const int b0 = split == 0 ? 0 : (c0 < nb_l ? c0 : nb_l);
+        const int b1 = split + 1 == S ? nb_l : (c1 < nb_l ? c1 : nb_l);
         const int lkbr = (r_l > 16) + (r_l > 32) + (r_l > 64);     // log2 of 16-channel blocks
         // log2 of 16-token blocks per tile: NS / (channel blocks), at most 4
         // (one token per lane)
         const int lmbs = lkbr == 0 ? 2 : (NS == 8 ? 3 : 2) - lkbr;
-        const int nt_l = (int)((b1 - b0 + (1 << lmbs) - 1) >> lmbs);
-        rg.b0 = (int)b0;
-        rg.b1 = (int)b1;
+        const int nt_l = (b1 - b0 + (1 << lmbs) - 1) >> lmbs;
+        rg.b0 = b0;
+        rg.b1 = b1;
         rg.cnt = cnt_l;
         rg.nt = nt_l | (lkbr << 28);
     }
