@@ -500,7 +500,11 @@ __device__ __forceinline__ void process_tile(const Tile &t, const TileData<kSlot
         if constexpr (GP == 4) {
             if (j < GQ) fh = f[j];
         } else {
-            fh = (grp & 1) ? f[4 + j] : f[j];
+            // (both factors pinned first: a select between two elements of
+            // f became an indexed load from scratch memory)
+            float fa = f[j], fb = f[4 + j];
+            asm volatile("" : "+v"(fa), "+v"(fb));
+            fh = (grp & 1) ? fb : fa;
         }
 #pragma unroll
         for (int a = 0; a < NA; ++a) A.O[a][j] *= fh;
