@@ -354,12 +354,13 @@ __device__ __forceinline__ const _Float16 *p_row(const _Float16 *sP, int c16)
 // One tile of a wave: every rank class runs the same instructions, the
 // slot -> (16-token block, 16-channel block) map coming from the tile at run
 // time, so the accumulators never pass through per-class code paths.
-template <int GQ, int KB, int D>
+template <int GQ, int KB, int D, int BITS>
 __device__ __forceinline__ void process_tile(const Tile &t, const TileData<kSlots * (KB / 4)> &Dt,
                                              const half4_t *s_qb, WaveAcc<GQ, KB, D> &A,
                                              const float (*s_qt)[GQ < 4 ? 4 : GQ], _Float16 *sP,
-                                             _Float16 *ev, int bits, int lane)
+                                             _Float16 *ev, int lane)
 {
+    constexpr int bits = BITS;                      // code width: fields at fixed positions
     constexpr int NS = kSlots * (KB / 4);
     constexpr int GP = GQ < 4 ? 4 : GQ;
     constexpr int NU = GP / 4;                      // score accumulators (4 heads each)
@@ -604,7 +605,7 @@ __device__ __forceinline__ void process_tile(const Tile &t, const TileData<kSlot
     }
 }
 
-template <int GQ, int KB, int D>
+template <int GQ, int KB, int D, int BITS>
 __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *arena, int layer,
                                                            const uint16_t *q, float *out,
                                                            DecodeWorkspace ws, int S, double invS,
@@ -618,7 +619,7 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
     const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, wave = uni(tid / kWave), lane = lane_id();
     const int c16 = lane & 15, grp = lane >> 4;
-    const int R = ly.R, bits = ly.bits;
+    const int R = ly.R;
     const int g0 = h * GQ;
 
     constexpr int EVW = ev_wave(GQ);
@@ -794,7 +795,7 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
         cur.rem += kWaves;
         Tile tb = locate<NS>(rg, cur, ly);
         issue_tile<NS>(tb, DB, rb, rbv, kbv, ly, lane);
-        process_tile<GQ, KB, D>(ta, DA, s_qb, A, s_qt, sP, ev, bits, lane);
+        process_tile<GQ, KB, D, BITS>(ta, DA, s_qb, A, s_qt, sP, ev, lane);
         if (!tb.valid) {
             bv_in_b = true;
             break;
@@ -802,7 +803,7 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
         cur.rem += kWaves;
         ta = locate<NS>(rg, cur, ly);
         issue_tile<NS>(ta, DA, rb, rbv, kbv, ly, lane);
-        process_tile<GQ, KB, D>(tb, DB, s_qb, A, s_qt, sP, ev, bits, lane);
+        process_tile<GQ, KB, D, BITS>(tb, DB, s_qb, A, s_qt, sP, ev, lane);
     }
 
     half4_t bvt[NS];
@@ -1021,11 +1022,18 @@ hipError_t launch_gq(const Layout &ly, uint8_t *arena, int layer, const uint16_t
 {
     const dim3 grid(splits, ly.Hkv, batch);
     const double inv = 1.0 / splits;
-    if (ly.R <= 64)
-        hipLaunchKernelGGL((decode_kernel<GQ, 4, D>), grid, dim3(kBlock), 0, stream, ly, arena, layer, q, out,
+    // (code widths 4 and 8, checked when the layout is built)
+    if (ly.R <= 64 && ly.bits == 4)
+        hipLaunchKernelGGL((decode_kernel<GQ, 4, D, 4>), grid, dim3(kBlock), 0, stream, ly, arena, layer, q, out,
+                           ws, splits, inv, qs, ap);
+    else if (ly.R <= 64)
+        hipLaunchKernelGGL((decode_kernel<GQ, 4, D, 8>), grid, dim3(kBlock), 0, stream, ly, arena, layer, q, out,
+                           ws, splits, inv, qs, ap);
+    else if (ly.bits == 4)
+        hipLaunchKernelGGL((decode_kernel<GQ, 8, D, 4>), grid, dim3(kBlock), 0, stream, ly, arena, layer, q, out,
                            ws, splits, inv, qs, ap);
     else
-        hipLaunchKernelGGL((decode_kernel<GQ, 8, D>), grid, dim3(kBlock), 0, stream, ly, arena, layer, q, out,
+        hipLaunchKernelGGL((decode_kernel<GQ, 8, D, 8>), grid, dim3(kBlock), 0, stream, ly, arena, layer, q, out,
                            ws, splits, inv, qs, ap);
     return hipGetLastError();
 }
