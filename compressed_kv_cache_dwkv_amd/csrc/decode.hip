@@ -653,6 +653,16 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
     half4_t bq[ND], ak[ND];
 #pragma unroll
     for (int kb = 0; kb < ND; ++kb) bq[kb] = *reinterpret_cast<const half4_t *>(qrow + 16 * kb + 4 * grp);
+    // this thread's entries of the residual-gather table, requested now with
+    // the counts (the table is written once the first tile is issued)
+    constexpr int kQtEntries = (kMaxHeadDim + 1) * GP;
+    constexpr int kQtPer = (kQtEntries + kBlock - 1) / kBlock;
+    uint16_t qt_h[kQtPer];
+#pragma unroll
+    for (int e = 0; e < kQtPer; ++e) {
+        const int i = tid + e * kBlock, j = i / GP, g = i % GP;
+        qt_h[e] = i < kQtEntries && g < GQ && j < D ? q[((int64_t)b * ly.Hq + g0 + g) * D + j] : (uint16_t)0;
+    }
     if (wave < KB) {
         const uint16_t *BK = basis_ptr(ly, arena, layer / ly.G, 0, h);
         const int row = 16 * wave + c16 < R ? 16 * wave + c16 : R - 1;
@@ -723,16 +733,26 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
 
     // ---- query in base-2 logit units (LDS, for residual gathers); this
     //      wave's V-residual tile cleared
-    for (int i = tid; i < (kMaxHeadDim + 1) * GP; i += kBlock) {
-        const int j = i / GP, g = i % GP;
-        s_qt[j][g] = g < GQ && j < D ? qscale * h2f(q[((int64_t)b * ly.Hq + g0 + g) * D + j]) : 0.0f;
+#pragma unroll
+    for (int e = 0; e < kQtPer; ++e) {
+        const int i = tid + e * kBlock;
+        if (i < kQtEntries) s_qt[i / GP][i % GP] = qscale * h2f(qt_h[e]);
     }
     _Float16 *ev = s_ev + wave * EVW;
     constexpr int kAppendTiles = 4;                 // V-residual tiles the append scratch covers
     static_assert(kAppendLdsBytes <= kAppendTiles * EVW * sizeof(_Float16), "append scratch");
     if (!(encoder && wave < kAppendTiles)) {
         uint4 *e4 = reinterpret_cast<uint4 *>(ev);
-        for (int i = lane; i < EVW / 8; i += kWave) e4[i] = uint4{0u, 0u, 0u, 0u};
+        if constexpr (ev_stride(GQ) % 8 == 0) {
+            // the cells the products read: channel rows 0..D-1, token columns
+            // 0..63 (the spare row only ever receives zeros; the padding is
+            // never read)
+            constexpr int RW = ev_stride(GQ) / 8;   // 16-byte pieces per row
+#pragma unroll 4
+            for (int i = lane; i < D * (kTile / 8); i += kWave) e4[(i >> 3) * RW + (i & 7)] = uint4{0u, 0u, 0u, 0u};
+        } else {
+            for (int i = lane; i < EVW / 8; i += kWave) e4[i] = uint4{0u, 0u, 0u, 0u};
+        }
     }
 
     // ---- score operand qb: q' = B_K q on the matrix cores, straight into
