@@ -67,8 +67,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kMaxLag = 8.0f;           // log2 units the running max may trail
 // The append's encoding, done by the first workgroup of each (sequence, KV
 // head) before its share of the tiles, in the units of the work balance
-// (9216 per tile; measured: a share about 22 tiles smaller hides it).
-constexpr int64_t kEncodeUnits = 200000;
+// (9216 per tile; measured: a share about 27 tiles smaller hides it).
+constexpr int64_t kEncodeUnits = 250000;
 
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
@@ -780,6 +780,11 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
         int slot, n;
         append_encode<D>(app, ly, arena, layer, b, h, wave, lane, ap, carve_append_lds(s_ev), slot, n);
     }
+    // the second tile's loads before the barrier (the loop's first step
+    // then only processes the first tile)
+    cur.rem += kWaves;
+    Tile tb = locate<NS>(rg, cur, ly);
+    issue_tile<NS>(tb, DB, rb, rbv, kbv, ly, lane);
     __syncthreads();
     if (encoder && wave < 2) {
         // both encodings are done: clear the V-residual tiles of waves 0..3
@@ -810,25 +815,35 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
         A.l[g] = 0.0f;
         A.m[g] = -INFINITY;
     }
-    bool bv_in_b = false;                           // the tile past the last holds the B_V operand
-    while (ta.valid) {
-        cur.rem += kWaves;
-        Tile tb = locate<NS>(rg, cur, ly);
-        issue_tile<NS>(tb, DB, rb, rbv, kbv, ly, lane);
-        process_tile<GQ, KB, D, BITS>(ta, DA, s_qb, A, s_qt, sP, ev, lane);
-        if (!tb.valid) {
-            bv_in_b = true;
-            break;
-        }
-        cur.rem += kWaves;
-        ta = locate<NS>(rg, cur, ly);
-        issue_tile<NS>(ta, DA, rb, rbv, kbv, ly, lane);
-        process_tile<GQ, KB, D, BITS>(tb, DB, s_qb, A, s_qt, sP, ev, lane);
-    }
-
+    // (the tile past a wave's last holds the B_V operand: copied out at the
+    // loop's exits, not selected between the buffers after it)
     half4_t bvt[NS];
+    if (ta.valid) {
+        process_tile<GQ, KB, D, BITS>(ta, DA, s_qb, A, s_qt, sP, ev, lane);
+        while (true) {
+            if (!tb.valid) {
 #pragma unroll
-    for (int i = 0; i < NS; ++i) bvt[i] = bv_in_b ? DB.ka[i] : DA.ka[i];
+                for (int i = 0; i < NS; ++i) bvt[i] = DB.ka[i];
+                break;
+            }
+            cur.rem += kWaves;
+            ta = locate<NS>(rg, cur, ly);
+            issue_tile<NS>(ta, DA, rb, rbv, kbv, ly, lane);
+            process_tile<GQ, KB, D, BITS>(tb, DB, s_qb, A, s_qt, sP, ev, lane);
+            if (!ta.valid) {
+#pragma unroll
+                for (int i = 0; i < NS; ++i) bvt[i] = DA.ka[i];
+                break;
+            }
+            cur.rem += kWaves;
+            tb = locate<NS>(rg, cur, ly);
+            issue_tile<NS>(tb, DB, rb, rbv, kbv, ly, lane);
+            process_tile<GQ, KB, D, BITS>(ta, DA, s_qb, A, s_qt, sP, ev, lane);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < NS; ++i) bvt[i] = DA.ka[i];
+    }
 
     // ---- merge the waves of this workgroup: each wave leaves its unscaled
     //      sums in its own (now idle) V-residual tile, then one barrier
