@@ -605,6 +605,19 @@ __device__ __forceinline__ void process_tile(const Tile &t, const TileData<kSlot
     }
 }
 
+// Publishes the appended token (tier count and position-map entry) from the
+// last workgroup of its (sequence, KV head): every workgroup of the head has
+// read the token counts by then.  The tier comes from the same input as the
+// encoder's and the counts are the ones this workgroup read, so admission
+// matches the encoder's.  Called by one wave; lane k of cnt_l holds tier k's count.
+__device__ __forceinline__ void publish_token(const Layout &ly, uint8_t *arena, int layer, int b, int h,
+                                              int tier_v, int cnt_l, int lane)
+{
+    const int tier = __builtin_amdgcn_readfirstlane(tier_v);
+    int slot, n;
+    if (append_admit(ly, tier, cnt_l, slot, n) == 0 && lane == 0) append_commit(ly, arena, layer, b, h, tier, slot, n);
+}
+
 template <int GQ, int KB, int D, int BITS>
 __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *arena, int layer,
                                                            const uint16_t *q, float *out,
@@ -970,9 +983,12 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
     }
     __syncthreads();
     if (!s_last) return;
-    // the appended token's tier (requested with the partials: publishing,
-    // after the merge, waits for no memory of its own)
-    const int app_tier_v = appending && wave == 0 ? ap.tier[b * ly.Hkv + h] : 0;
+    // The appended token is published by a wave with no head of its own to
+    // reduce (the last one, while the others reduce), else by wave 0 after
+    // the merge.  Its tier is requested with the partials, so publishing
+    // waits for no memory of its own.
+    constexpr int kPubWave = GQ < kWaves ? kWaves - 1 : 0;
+    const int app_tier_v = appending && wave == kPubWave ? ap.tier[b * ly.Hkv + h] : 0;
     // Each thread owns 4 adjacent outputs of one head and an interleaved
     // subset of the splits.  Its first 8 partial vectors are requested
     // together with every split's max and normaliser, so the merge waits
@@ -1016,6 +1032,8 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
         }
         L = wave_sum(L);
         if (lane == 0) s_L[g] = L;
+    } else if (appending && wave == kPubWave) {
+        publish_token(ly, arena, layer, b, h, app_tier_v, rg.cnt, lane);
     }
     __syncthreads();
     float4_t accm = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
@@ -1038,15 +1056,8 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
         const float inv = L > 0.0f ? 1.0f / L : 0.0f;
         *reinterpret_cast<float4_t *>(out + ((int64_t)b * ly.Hq + g0 + hq) * D + j4) = o * inv;
     }
-    // every workgroup of this (sequence, KV head) has read the token counts:
-    // the appended token can be published (its tier from the same input and
-    // the counts this workgroup read, so admission matches the encoder's)
-    if (appending && wave == 0) {
-        const int app_tier = __builtin_amdgcn_readfirstlane(app_tier_v);
-        int slot, n;
-        if (append_admit(ly, app_tier, rg.cnt, slot, n) == 0 && lane == 0)
-            append_commit(ly, arena, layer, b, h, app_tier, slot, n);
-    }
+    if (GQ == kWaves && appending && wave == kPubWave)
+        publish_token(ly, arena, layer, b, h, app_tier_v, rg.cnt, lane);
     if (tid == 0) __hip_atomic_store(&ws.arrive[b * ly.Hkv + h], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
