@@ -990,13 +990,14 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
     constexpr int kPubWave = GQ < kWaves ? kWaves - 1 : 0;
     const int app_tier_v = appending && wave == kPubWave ? ap.tier[b * ly.Hkv + h] : 0;
     // Each thread owns 4 adjacent outputs of one head and an interleaved
-    // subset of the splits.  Its first 8 partial vectors are requested
-    // together with every split's max and normaliser, so the merge waits
-    // for memory once; weights 2^(m_s - M) then come from LDS (the
-    // V-residual tiles: [GQ][S] weights, [GQ][S] normalisers, reduction area).
+    // subset of the splits.  Its partial vectors of the first 32 splits (at
+    // least 8) are requested together with every split's max and
+    // normaliser, so the merge waits for memory once up to 32 splits;
+    // weights 2^(m_s - M) then come from LDS (the V-residual tiles: [GQ][S]
+    // weights, [GQ][S] normalisers, reduction area).
     constexpr int quads = GQ * D / 4;
     constexpr int parts = kBlock / quads;
-    constexpr int kFirst = 8;
+    constexpr int kFirst = 32 / parts > 8 ? 32 / parts : 8;
     static_assert(kBlock % quads == 0, "merge layout");
     static_assert((2 * kMaxSplits * 8 + kBlock * 4) * 4 <= sizeof(s_ev), "merge scratch");
     const int qd = tid % quads, part = tid / quads;
