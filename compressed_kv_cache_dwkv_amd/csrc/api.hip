@@ -160,8 +160,8 @@ static int plan_splits(const dwkv_config &c, const Layout &ly)
 size_t decode_workspace_bytes(const Layout &ly, int batch, int splits)
 {
     const int64_t B = batch;
-    int64_t off = align_up(B * ly.Hkv * 4, 256);
-    off += 2 * align_up(B * ly.Hq * splits * 4, 256);
+    int64_t off = align_up(B * ly.Hkv * kArriveStride * 4, 256);
+    off += align_up(B * ly.Hkv * splits * kMlStride * 4, 256);
     off += align_up(B * ly.Hq * splits * (int64_t)ly.d * 4, 256);
     return (size_t)off;
 }
@@ -172,11 +172,10 @@ DecodeWorkspace carve_workspace(const Layout &ly, void *ws, int batch, int split
     uint8_t *p = static_cast<uint8_t *>(ws);
     DecodeWorkspace w;
     w.arrive = reinterpret_cast<uint32_t *>(p);
-    p += align_up(B * ly.Hkv * 4, 256);
+    p += align_up(B * ly.Hkv * kArriveStride * 4, 256);
     w.pm = reinterpret_cast<float *>(p);
-    p += align_up(B * ly.Hq * splits * 4, 256);
-    w.pl = reinterpret_cast<float *>(p);
-    p += align_up(B * ly.Hq * splits * 4, 256);
+    w.pl = w.pm + kMlNorm;
+    p += align_up(B * ly.Hkv * splits * kMlStride * 4, 256);
     w.po = reinterpret_cast<float *>(p);
     return w;
 }

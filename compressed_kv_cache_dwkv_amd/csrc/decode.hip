@@ -963,11 +963,11 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
             st_agent2(po + 2, o[2], o[3]);
         }
     }
+    static_assert(GQ <= kMlNorm, "maxima and normalisers share a line");
     if (tid < GQ) {
-        __hip_atomic_store(ws.pm + ((int64_t)b * ly.Hq + g0 + tid) * S + split, s_M[tid], __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(ws.pl + ((int64_t)b * ly.Hq + g0 + tid) * S + split, s_L[tid], __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+        const int64_t ml = (((int64_t)b * ly.Hkv + h) * S + split) * kMlStride + tid;
+        __hip_atomic_store(ws.pm + ml, s_M[tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(ws.pl + ml, s_L[tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 
     // ---- the last workgroup of this (sequence, KV head) merges the splits.
@@ -977,7 +977,7 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (tid == 0) {
-        const uint32_t prev = __hip_atomic_fetch_add(&ws.arrive[b * ly.Hkv + h], 1u, __ATOMIC_RELAXED,
+        const uint32_t prev = __hip_atomic_fetch_add(&ws.arrive[(b * ly.Hkv + h) * kArriveStride], 1u, __ATOMIC_RELAXED,
                                                      __HIP_MEMORY_SCOPE_AGENT);
         s_last = prev == (uint32_t)(S - 1);
     }
@@ -1013,9 +1013,10 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
     float *s_pl = s_w + GQ * S;
     for (int i = tid; i < GQ * S; i += kBlock) {
         const int g = i / S, sp = i % S;
-        s_w[i] = __hip_atomic_load(ws.pm + ((int64_t)b * ly.Hq + g0 + g) * S + sp, __ATOMIC_RELAXED,
+        const int64_t ml = (((int64_t)b * ly.Hkv + h) * S + sp) * kMlStride + g;
+        s_w[i] = __hip_atomic_load(ws.pm + ml, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
-        s_pl[i] = __hip_atomic_load(ws.pl + ((int64_t)b * ly.Hq + g0 + g) * S + sp, __ATOMIC_RELAXED,
+        s_pl[i] = __hip_atomic_load(ws.pl + ml, __ATOMIC_RELAXED,
                                     __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();
@@ -1059,7 +1060,7 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
     }
     if (GQ == kWaves && appending && wave == kPubWave)
         publish_token(ly, arena, layer, b, h, app_tier_v, rg.cnt, lane);
-    if (tid == 0) __hip_atomic_store(&ws.arrive[b * ly.Hkv + h], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) __hip_atomic_store(&ws.arrive[(b * ly.Hkv + h) * kArriveStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int GQ, int D>

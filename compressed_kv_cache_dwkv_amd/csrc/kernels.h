@@ -10,11 +10,17 @@ namespace dwkv {
 
 // Decode workspace carve-up for `batch` sequences and `splits` workgroups per
 // (sequence, KV head): arrival counters, then per (b, query head, split) the
-// running max, the normaliser and the unnormalised output vector.
+// running max, the normaliser and the unnormalised output vector.  Each
+// (sequence, KV head) counter, and the maxima and normalisers of each
+// (sequence, KV head, split), have a 128-byte line of their own, so the
+// stores and atomics of different workgroups do not queue on one line.
+constexpr int kArriveStride = 32;   // uint32 per arrival counter
+constexpr int kMlStride = 32;       // floats per split's maxima and normalisers
+constexpr int kMlNorm = 16;         // offset of the normalisers in that line
 struct DecodeWorkspace {
-    uint32_t *arrive;   // [B][Hkv]
-    float *pm;          // [B][Hq][S]
-    float *pl;          // [B][Hq][S]
+    uint32_t *arrive;   // [B][Hkv][kArriveStride], element 0 used
+    float *pm;          // [B][Hkv][S][kMlStride], query head g of the group at g
+    float *pl;          // pm + kMlNorm (same lines)
     float *po;          // [B][Hq][S][d]
 };
 
