@@ -702,13 +702,37 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
     const __amdgpu_buffer_rsrc_t rbv = block_rsrc(
         reinterpret_cast<const uint8_t *>(basis_vt_ptr(ly, arena, layer / ly.G, h)), (int64_t)R * D * 2);
     const uint32_t kbv = (uint32_t)((16 * (wave < ND ? wave : 0) + c16) * R + 4 * grp) * 2u;
+    // ---- a first tile that needs no token count, issued before the counts
+    //      arrive: tile (split, wave) of tier 0's first S * 8 tiles.  Its
+    //      valid tokens are known once the counts are (lanes past them are
+    //      masked as in any tile; a tile with none is skipped), and the
+    //      balanced runs below start after these tiles.
+    TileData<NS> DA, DB;
+    Tile ta;
+    {
+        const int r0 = ly.tier[0].rank;
+        const int lkbr0 = (r0 > 16) + (r0 > 32) + (r0 > 64);
+        const int mbs0 = lkbr0 == 0 && NS == 8 ? 4 : NS >> lkbr0;
+        ta.valid = 1;
+        ta.k = 0;
+        ta.r = r0;
+        ta.s = ly.tier[0].resid;
+        ta.kbr = 1 << lkbr0;
+        ta.lkbr = lkbr0;
+        ta.blk0 = (split * kWaves + wave) * mbs0;
+        ta.nv = 16 * mbs0;
+    }
+    issue_tile<NS>(ta, DA, rb, rbv, kbv, ly, lane);
+    const int static_blocks = S * kWaves * (ta.nv >> 4);   // tier 0's blocks the first tiles cover
     Ranges rg;
     {
         // (fp32: every workgroup evaluates the same expressions for a shared
         // boundary, so neighbours agree exactly; the first and last
         // boundaries are exact, so the runs cover every block once)
         const bool on = lane < T;
-        const int nb_l = on ? (cnt_l + 15) >> 4 : 0;
+        const int nall_l = on ? (cnt_l + 15) >> 4 : 0;                // 16-token blocks of tier k
+        const int bs_l = lane == 0 ? min(nall_l, static_blocks) : 0;  // of them, in the first tiles
+        const int nb_l = nall_l - bs_l;                                // balanced over the splits
         const float wt_l = (float)nb_l * (16.0f * (float)cost_l);   // work of tier k's blocks
         float W = 0.0f, wk_l = 0.0f;                               // total; work of the tiers before k
 #pragma unroll
@@ -732,17 +756,20 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
         // (one token per lane)
         const int lmbs = lkbr == 0 ? 2 : (NS == 8 ? 3 : 2) - lkbr;
         const int nt_l = (b1 - b0 + (1 << lmbs) - 1) >> lmbs;
-        rg.b0 = b0;
-        rg.b1 = b1;
+        rg.b0 = bs_l + b0;
+        rg.b1 = bs_l + b1;
         rg.cnt = cnt_l;
         rg.nt = nt_l | (lkbr << 28);
     }
 
-    // ---- first tile's loads
-    TileData<NS> DA, DB;
+    // ---- the first balanced tile's loads; the first tile's valid tokens
     Cursor cur{0, wave};
-    Tile ta = locate<NS>(rg, cur, ly);
-    issue_tile<NS>(ta, DA, rb, rbv, kbv, ly, lane);
+    Tile tb = locate<NS>(rg, cur, ly);
+    issue_tile<NS>(tb, DB, rb, rbv, kbv, ly, lane);
+    {
+        const int left = __builtin_amdgcn_readlane(cnt_l, 0) - 16 * ta.blk0;
+        ta.nv = left < 0 ? 0 : (left < ta.nv ? left : ta.nv);
+    }
 
     // ---- query in base-2 logit units (LDS, for residual gathers); this
     //      wave's V-residual tile cleared
@@ -793,11 +820,6 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
         int slot, n;
         append_encode<D>(app, ly, arena, layer, b, h, wave, lane, ap, carve_append_lds(s_ev), slot, n);
     }
-    // the second tile's loads before the barrier (the loop's first step
-    // then only processes the first tile)
-    cur.rem += kWaves;
-    Tile tb = locate<NS>(rg, cur, ly);
-    issue_tile<NS>(tb, DB, rb, rbv, kbv, ly, lane);
     __syncthreads();
     if (encoder && wave < 2) {
         // both encodings are done: clear the V-residual tiles of waves 0..3
@@ -831,31 +853,26 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
     // (the tile past a wave's last holds the B_V operand: copied out at the
     // loop's exits, not selected between the buffers after it)
     half4_t bvt[NS];
-    if (ta.valid) {
-        process_tile<GQ, KB, D, BITS>(ta, DA, s_qb, A, s_qt, sP, ev, lane);
-        while (true) {
-            if (!tb.valid) {
+    if (ta.nv > 0) process_tile<GQ, KB, D, BITS>(ta, DA, s_qb, A, s_qt, sP, ev, lane);
+    while (true) {
+        if (!tb.valid) {
 #pragma unroll
-                for (int i = 0; i < NS; ++i) bvt[i] = DB.ka[i];
-                break;
-            }
-            cur.rem += kWaves;
-            ta = locate<NS>(rg, cur, ly);
-            issue_tile<NS>(ta, DA, rb, rbv, kbv, ly, lane);
-            process_tile<GQ, KB, D, BITS>(tb, DB, s_qb, A, s_qt, sP, ev, lane);
-            if (!ta.valid) {
-#pragma unroll
-                for (int i = 0; i < NS; ++i) bvt[i] = DA.ka[i];
-                break;
-            }
-            cur.rem += kWaves;
-            tb = locate<NS>(rg, cur, ly);
-            issue_tile<NS>(tb, DB, rb, rbv, kbv, ly, lane);
-            process_tile<GQ, KB, D, BITS>(ta, DA, s_qb, A, s_qt, sP, ev, lane);
+            for (int i = 0; i < NS; ++i) bvt[i] = DB.ka[i];
+            break;
         }
-    } else {
+        cur.rem += kWaves;
+        ta = locate<NS>(rg, cur, ly);
+        issue_tile<NS>(ta, DA, rb, rbv, kbv, ly, lane);
+        process_tile<GQ, KB, D, BITS>(tb, DB, s_qb, A, s_qt, sP, ev, lane);
+        if (!ta.valid) {
 #pragma unroll
-        for (int i = 0; i < NS; ++i) bvt[i] = DA.ka[i];
+            for (int i = 0; i < NS; ++i) bvt[i] = DA.ka[i];
+            break;
+        }
+        cur.rem += kWaves;
+        tb = locate<NS>(rg, cur, ly);
+        issue_tile<NS>(tb, DB, rb, rbv, kbv, ly, lane);
+        process_tile<GQ, KB, D, BITS>(ta, DA, s_qb, A, s_qt, sP, ev, lane);
     }
 
     // ---- merge the waves of this workgroup: each wave leaves its unscaled
