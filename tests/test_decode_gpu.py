@@ -104,6 +104,23 @@ def test_small_and_ragged_contexts(G, n):
     _run(G, cfg, layers=(0,), splits=4, n=max(n, 1), ragged=ragged)
 
 
+@pytest.mark.parametrize("ranks,probs,ns", [
+    # tier 0 of rank 8: the fixed first tiles of 2 splits x 8 waves cover
+    # 16 x 64 = 1024 tier-0 tokens; the sequences hold about 0.85 n of them
+    ((8, 16, 32, 64), (0.85, 0.05, 0.05, 0.05), [1100, 1200, 1210, 3000]),
+    # tier 0 of rank 32: 32-token tiles, 512 tokens in the fixed tiles
+    ((32, 64), (0.8, 0.2), [500, 640, 660, 2000]),
+])
+def test_first_tiles_cover_part_or_all_of_tier0(G, ranks, probs, ns):
+    """Each wave's first tile is a fixed tile of tier 0; tier-0 counts below,
+    near and above the tokens those tiles cover (the balanced runs take the
+    rest)."""
+    cfg = tiny_config(batch=len(ns), num_kv_heads=2, num_q_heads=8, head_dim=128, r_max=64,
+                      tier_rank=ranks, tier_prob=probs, resid_channels=8, resid_bits=4,
+                      n_tokens=max(ns))
+    _run(G, cfg, layers=(0,), splits=2, peak=4.0, n=max(ns), ragged=ns)
+
+
 @pytest.mark.parametrize("gq,d,bits", [(1, 64, 8), (2, 128, 4), (8, 128, 4), (4, 64, 8)])
 def test_group_sizes_and_head_dims(G, gq, d, bits):
     cfg = tiny_config(batch=2, num_kv_heads=2, num_q_heads=2 * gq, head_dim=d, r_max=64,
