@@ -702,11 +702,14 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
     const __amdgpu_buffer_rsrc_t rbv = block_rsrc(
         reinterpret_cast<const uint8_t *>(basis_vt_ptr(ly, arena, layer / ly.G, h)), (int64_t)R * D * 2);
     const uint32_t kbv = (uint32_t)((16 * (wave < ND ? wave : 0) + c16) * R + 4 * grp) * 2u;
-    // ---- a first tile that needs no token count, issued before the counts
-    //      arrive: tile (split, wave) of tier 0's first S * 8 tiles.  Its
-    //      valid tokens are known once the counts are (lanes past them are
-    //      masked as in any tile; a tile with none is skipped), and the
-    //      balanced runs below start after these tiles.
+    // ---- a first tile whose place needs no token count: tile (split, wave)
+    //      of tier 0's first S * 8 tiles, its loads requested ahead of the
+    //      work-balanced ranges (which need the counts).  Its valid tokens are
+    //      known once the counts are (lanes past them are masked as in any
+    //      tile; a tile with none is skipped), and the balanced runs below
+    //      start after these tiles.  (Requesting it ahead of the counts
+    //      themselves was slower: 2048 waves' tile loads then queue in front
+    //      of the loads the prologue waits for.)
     TileData<NS> DA, DB;
     Tile ta;
     {
