@@ -53,6 +53,8 @@ def _load(path: str):
                                 ctypes.c_int, ctypes.c_uint16, P, P, P, P]
     L.oracle_append_residual.restype = ctypes.c_int
     L.oracle_append_residual.argtypes = [ctypes.c_int, ctypes.c_int, P, P, ctypes.c_int, P]
+    L.oracle_append_projection.restype = ctypes.c_int
+    L.oracle_append_projection.argtypes = [ctypes.c_int, ctypes.c_int, P, P, ctypes.c_int, P]
     L.oracle_max_threads.restype = ctypes.c_int
     return L
 
@@ -170,6 +172,18 @@ def append_residual(basis: np.ndarray, x: np.ndarray, r: int) -> np.ndarray:
     if lib().oracle_append_residual(d, r_max, _p(b), _p(xv), r, _p(e)) != 0:
         raise ValueError("oracle_append_residual rejected its arguments")
     return e
+
+
+def append_projection(basis: np.ndarray, x: np.ndarray, r: int) -> np.ndarray:
+    """fp32 sums of the encoder's step 1 (the coefficients before their fp16
+    rounding), fp32 [r]."""
+    b = _u16(basis)
+    xv = _u16(x)
+    r_max, d = b.shape
+    out = np.zeros(max(r, 1), np.float32)
+    if lib().oracle_append_projection(d, r_max, _p(b), _p(xv), r, _p(out)) != 0:
+        raise ValueError("oracle_append_projection rejected its arguments")
+    return out[:r]
 
 
 def append_layer(cfg, basisK: np.ndarray, basisV: np.ndarray, k: np.ndarray, v: np.ndarray,

@@ -246,20 +246,23 @@ int oracle_decode(const oracle_shape *sh, const int64_t *n_tokens, const uint8_t
  * Outputs: c_out[r] fp16 bits, idx_out[s] ascending, val_out[s], *scale_out
  * fp16 bits (0 when s == 0).  Returns 0, or -1 on an invalid argument.
  */
-/* Steps 1-2: fp16 coefficients c[r] and the fp32 residual e[d]. */
+/* Steps 1-2: fp16 coefficients c[r] (and, if sum is not NULL, the fp32
+ * projection sums they are rounded from) and the fp32 residual e[d]. */
 static void project(int d, const uint16_t *basis, const uint16_t *x, int r, uint16_t *c16,
-                    float *e)
+                    float *sum, float *e)
 {
     float c[256];
     for (int i = 0; i < r; ++i) {
-        float acc = 0.0f;
+        float acc = 0.0f;                                         /* step 1 */
         for (int j = 0; j < d; ++j)
             acc = fmaf(h2f(basis[(int64_t)i * d + j]), h2f(x[j]), acc);
+        if (sum)
+            sum[i] = acc;
         c16[i] = oracle_float_to_half(acc);
         c[i] = h2f(c16[i]);
     }
     for (int j = 0; j < d; ++j) {
-        float acc = 0.0f;
+        float acc = 0.0f;                                         /* step 2 */
         for (int i = 0; i < r; ++i)
             acc = fmaf(h2f(basis[(int64_t)i * d + j]), c[i], acc);
         e[j] = h2f(x[j]) - acc;
@@ -280,7 +283,7 @@ int oracle_append(int d, int r_max, const uint16_t *basis, const uint16_t *x, in
     if (d <= 0 || d > 256 || r < 0 || r > r_max || s < 0 || s > d || qmax <= 0)
         return -1;
     float e[256];
-    project(d, basis, x, r, c_out, e);
+    project(d, basis, x, r, c_out, NULL, e);
     *scale_out = 0;
     if (s == 0)
         return 0;
@@ -331,7 +334,20 @@ int oracle_append_residual(int d, int r_max, const uint16_t *basis, const uint16
     if (d <= 0 || d > 256 || r < 0 || r > r_max)
         return -1;
     uint16_t c16[256];
-    project(d, basis, x, r, c16, e_out);
+    project(d, basis, x, r, c16, NULL, e_out);
+    return 0;
+}
+
+/* The fp32 sums of step 1 before their fp16 rounding (for the checks of the
+ * fixed operation order). */
+int oracle_append_projection(int d, int r_max, const uint16_t *basis, const uint16_t *x, int r,
+                             float *sum_out)
+{
+    if (d <= 0 || d > 256 || r < 0 || r > r_max)
+        return -1;
+    uint16_t c16[256];
+    float e[256];
+    project(d, basis, x, r, c16, sum_out, e);
     return 0;
 }
 

@@ -3,8 +3,14 @@ that the pins catch every one: a dropped or sign-flipped residual, swapped
 K/V bases, a wrong query-to-KV-head map, a missing softmax scale, an
 off-by-one rank, a transposed basis, a missing normalisation, a wrong
 exponential base, and in the encoder a wrong tie rule, a wrong rounding
-rule, a residual against unrounded coefficients, a wrong code range and a
-flipped residual sign."""
+rule, a residual against unrounded coefficients, a wrong code range, a
+flipped residual sign, and in the encoder's fixed fp32 order a reversed
+summation order (step 1 or 2) and a wider (fp64) accumulator (step 1 or 2).
+
+A separate multiply and add in place of the fused multiply-add is not a
+mistake these pins could catch: every product in the encoder is of two fp16
+values, which binary32 holds exactly, so both forms round once and give the
+same bits (test_oracle_encoder_order.py proves the exactness)."""
 import os
 import shutil
 import subprocess
@@ -15,6 +21,7 @@ import pytest
 import oracle
 from tests import test_oracle_append as TA
 from tests import test_oracle_decode as TD
+from tests import test_oracle_encoder_order as TO
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(os.path.dirname(HERE), "oracle", "oracle.c")
@@ -38,7 +45,16 @@ APPEND_PINS = [
     lambda: TA.test_quantisation_error_bound(7),
     TA.test_ties_prefer_smaller_channel_and_zero_residual,
     TA.test_codes_round_half_to_even,
+    lambda: TO.test_encoder_steps_match_exact_fma_chain(1, 8),
+    lambda: TO.test_encoder_steps_match_exact_fma_chain(2, 64),
 ]
+
+_STEP1 = ("        float acc = 0.0f;                                         /* step 1 */\n"
+          "        for (int j = 0; j < d; ++j)\n"
+          "            acc = fmaf(h2f(basis[(int64_t)i * d + j]), h2f(x[j]), acc);\n")
+_STEP2 = ("        float acc = 0.0f;                                         /* step 2 */\n"
+          "        for (int i = 0; i < r; ++i)\n"
+          "            acc = fmaf(h2f(basis[(int64_t)i * d + j]), c[i], acc);\n")
 
 MUTANTS = {
     "drop_residual": ("x[idx[u]] += g * (double)val[u];", "(void)g;", DECODE_PINS),
@@ -57,6 +73,18 @@ MUTANTS = {
     "unrounded_coef": ("c[i] = h2f(c16[i]);", "c[i] = acc;", APPEND_PINS),
     "wrong_code_range": ("amax / (float)qmax", "amax / (float)(qmax + 1)", APPEND_PINS),
     "residual_flipped": ("e[j] = h2f(x[j]) - acc;", "e[j] = acc - h2f(x[j]);", APPEND_PINS),
+    "step1_descending": (_STEP1, _STEP1.replace("for (int j = 0; j < d; ++j)", "for (int j = d - 1; j >= 0; --j)"),
+                         APPEND_PINS),
+    "step2_descending": (_STEP2, _STEP2.replace("for (int i = 0; i < r; ++i)", "for (int i = r - 1; i >= 0; --i)"),
+                         APPEND_PINS),
+    "step1_fp64_accumulate": (_STEP1, "        double acc64 = 0.0;\n"
+                                      "        for (int j = 0; j < d; ++j)\n"
+                                      "            acc64 = fma(h2f(basis[(int64_t)i * d + j]), h2f(x[j]), acc64);\n"
+                                      "        float acc = (float)acc64;\n", APPEND_PINS),
+    "step2_fp64_accumulate": (_STEP2, "        double acc64 = 0.0;\n"
+                                      "        for (int i = 0; i < r; ++i)\n"
+                                      "            acc64 = fma(h2f(basis[(int64_t)i * d + j]), c[i], acc64);\n"
+                                      "        float acc = (float)acc64;\n", APPEND_PINS),
 }
 
 
