@@ -19,6 +19,7 @@ import os
 import sys
 import time
 from concurrent.futures import ProcessPoolExecutor
+from typing import Optional
 
 import numpy as np
 
@@ -112,28 +113,20 @@ def _gen_layer_job(args):
     return gen_layer(w.get_config(ci), layer)
 
 
-def algorithmic_layer_bytes(cfg, counts: np.ndarray) -> int:
-    """Bytes the method must move for one layer's decode: every cached token at
-    its tier's size (fp16 coefficients at the routed rank, residual indices,
-    packed codes, scale; K and V), both bases of every KV head (once: every
-    sequence shares them), q and out."""
+def algorithmic_layer_bytes(cfg, counts: np.ndarray, app_tier: Optional[np.ndarray] = None) -> int:
+    """Bytes one layer's decode step must move, the one accounting used for
+    every figure: every cached token at its tier's size (fp16 coefficients at
+    the routed rank; per K and V a residual block of channel indices, packed
+    codes and an fp16 scale), both bases of every KV head (once: every
+    sequence shares them), and -- with an append -- the appended token of each
+    (sequence, KV head) at its tier's size.  Queries, outputs, split partials
+    and padding are not counted."""
     per_tok = np.array([w.compressed_bytes_per_token(r, s, cfg.resid_bits)
                         for r, s in zip(cfg.tier_rank, cfg.resid_per_tier)])
     tok = float((counts.reshape(-1, cfg.num_tiers) * per_tok[None, :]).sum())
     bases = 2 * cfg.num_kv_heads * cfg.r_max * cfg.head_dim * 2
-    qo = cfg.batch * cfg.num_q_heads * cfg.head_dim * (2 + 4)
-    return int(tok + bases + qo)
-
-
-def append_layer_bytes(cfg, tier: np.ndarray) -> int:
-    """Bytes one layer's append moves beyond the bases (which the decode in
-    the same launch reads): the new K and V and the tier per (b, KV head) in,
-    the encoded token, its tier count and its position-map entry out."""
-    per_tok = np.array([w.compressed_bytes_per_token(r, s, cfg.resid_bits)
-                        for r, s in zip(cfg.tier_rank, cfg.resid_per_tier)])
-    ins = tier.size * (2 * cfg.head_dim * 2 + 1)
-    outs = float(per_tok[tier.reshape(-1).astype(np.int64)].sum()) + tier.size * 8
-    return int(ins + outs)
+    app = 0.0 if app_tier is None else float(per_tok[app_tier.reshape(-1).astype(np.int64)].sum())
+    return int(tok + bases + app)
 
 
 def stored_traffic(workload: str):
@@ -149,12 +142,21 @@ def stored_traffic(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(cfg, bases, appends, budget_s: float):
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_step_rate(cfg, bases, appends, budget_s: float, threads: int):
     """The oracle's decode + append, layer by layer over one step (each
     layer's synthetic input regenerated first, outside the timing), until
-    the budget is spent; scaled to a full step."""
+    the budget is spent; returns (seconds per full step, layers timed, s)."""
     import oracle
-    threads = oracle.max_threads()
     dt = 0.0
     done = 0
     for layer in range(cfg.num_layers):
@@ -169,13 +171,28 @@ def cpu_baseline(cfg, bases, appends, budget_s: float):
         done += 1
         if dt >= budget_s:
             break
-    step_s = dt / done * cfg.num_layers
+    return dt / done * cfg.num_layers, done, dt
+
+
+def cpu_baseline(cfg, bases, appends, budget_s: float):
+    """The oracle timed on this host's cores (all it may use, then one
+    thread), on a bounded sample of one step, scaled to a full step.  The
+    oracle runs one (sequence, KV head) per thread, so it uses at most
+    B x H_kv threads."""
+    import oracle
+    host = len(os.sched_getaffinity(0))
+    threads = min(oracle.max_threads(), host)
     used = min(threads, cfg.batch * cfg.num_kv_heads)
+    step_s, done, dt = _oracle_step_rate(cfg, bases, appends, budget_s, threads)
+    step_1, done_1, dt_1 = _oracle_step_rate(cfg, bases, appends, budget_s / 2, 1)
     return {
         "value": cfg.batch / step_s, "unit": "tokens/s", "cores": used, "kind": "oracle",
+        "host_cores": host, "cpu_model": _cpu_model(),
+        "value_1_thread": cfg.batch / step_1,
         "sample": f"{done} of {cfg.num_layers} layers of one step (decode over all "
-                  f"{cfg.n_tokens} tokens x {cfg.batch * cfg.num_kv_heads} KV heads + append), "
-                  f"{dt:.1f} s, scaled to a full step",
+                  f"{cfg.n_tokens} tokens x {cfg.batch * cfg.num_kv_heads} KV heads + append) "
+                  f"on {used} threads, {dt:.1f} s; 1 thread: {done_1} layers, {dt_1:.1f} s; "
+                  f"each scaled to a full step",
     }
 
 
@@ -283,12 +300,13 @@ def main():
     # ---- decode-kernel duration: every layer's launch of the step (with
     #      its append unless --separate) back to back in one graph, replayed;
     #      events on the launch stream around the replays
+    # (counts after the timed steps; the timed launches saw up to K fewer
+    # tokens per (layer, KV head): under 0.4% at 64K)
     counts = np.stack([cache.read_counts(l, B) for l in range(L)])     # [L][B][H][T]
-    app_bytes = [0 if args.separate else append_layer_bytes(cfg, appends[W + K - 1][l]["tier"])
-                 for l in range(L)]
-    layer_bytes = [algorithmic_layer_bytes(cfg, counts[l]) + app_bytes[l] for l in range(L)]
-    step_bytes = sum(algorithmic_layer_bytes(cfg, counts[l]) +
-                     append_layer_bytes(cfg, appends[W + K - 1][l]["tier"]) for l in range(L))
+    last = appends[W + K - 1]
+    layer_bytes = [algorithmic_layer_bytes(cfg, counts[l], None if args.separate else last[l]["tier"])
+                   for l in range(L)]
+    step_bytes = sum(algorithmic_layer_bytes(cfg, counts[l], last[l]["tier"]) for l in range(L))
     kg = torch.cuda.CUDAGraph()
     with torch.cuda.graph(kg):
         for l in range(L):
@@ -335,7 +353,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "fp16 MFMA operands, fp32 accumulate",
         "data": "synthetic",
         "config": {
             "workload": cfg.name, "batch": B, "context": cfg.n_tokens, "layers": L,
@@ -344,7 +362,7 @@ def main():
             "tier_rank": list(cfg.tier_rank), "tier_mix": list(cfg.tier_prob),
             "resid_channels": cfg.resid_channels, "resid_bits": cfg.resid_bits,
             "storage": "fp16 coefficients, uint8 channel indices, packed codes, fp16 scales",
-            "graph_replay": bool(graphs),
+            "graph_replay": bool(graphs), "decode_splits": cache.splits,
             "launches_per_layer": 2 if args.separate else 1,
         },
         "step_GBps": step_bytes / (ms_per_step * 1e-3) / 1e9,
@@ -352,6 +370,7 @@ def main():
         "roofline": {
             "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
             "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
+            "traffic_GBps": None if traffic is None else traffic / (mean_launch_ms * 1e-3) / 1e9,
             "kernel": "decode_kernel", "algorithmic_bytes_per_launch": bytes_per_launch,
             "mean_launch_us": mean_launch_ms * 1e3, "launch_time_from": launch_source,
             "one_step_graph_launch_us": graph_launch_ms * 1e3,

@@ -81,6 +81,7 @@ _SIGS = {
     "dwkv_export_layer": [_P, _I, ctypes.POINTER(dwkv_logical_layer), _P, _P, _I, _P],
     "dwkv_read_counts": [_P, _I, _I, _P, _P],
     "dwkv_workspace_bytes": [ctypes.POINTER(dwkv_config), _I, ctypes.POINTER(ctypes.c_size_t)],
+    "dwkv_decode_splits": [_P, ctypes.POINTER(_I)],
     "dwkv_decode_attn": [_P, _I, _P, _I, ctypes.c_float, _P, _P, ctypes.c_size_t, _P],
     "dwkv_append": [_P, _I, _P, _P, _P, _P, _P, _I, _P],
     "dwkv_decode_step": [_P, _I, _P, _I, ctypes.c_float, _P, _P, ctypes.c_size_t, _P, _P, _P, _P, _P, _P],
@@ -238,6 +239,13 @@ def dwkv_read_counts(h, layer: int, batch: int, num_kv_heads: int, num_tiers: in
 def dwkv_workspace_bytes(cfg: dwkv_config, batch: int) -> int:
     n = ctypes.c_size_t()
     _check(_lib.dwkv_workspace_bytes(ctypes.byref(cfg), batch, ctypes.byref(n)), "dwkv_workspace_bytes")
+    return n.value
+
+
+def dwkv_decode_splits(h) -> int:
+    """Workgroups per (sequence, KV head) of this handle's decode launches."""
+    n = ctypes.c_int()
+    _check(_lib.dwkv_decode_splits(h, ctypes.byref(n)), "dwkv_decode_splits")
     return n.value
 
 

@@ -8,7 +8,7 @@ from typing import Dict, Optional, Sequence
 import torch
 
 from . import (dwkv_append, dwkv_arena_bytes, dwkv_check_errors, dwkv_clear_errors, dwkv_create,
-               dwkv_decode_attn, dwkv_decode_step, dwkv_destroy, dwkv_export_layer, dwkv_import_layer,
+               dwkv_decode_attn, dwkv_decode_splits, dwkv_decode_step, dwkv_destroy, dwkv_export_layer, dwkv_import_layer,
                dwkv_read_counts, dwkv_reset, dwkv_set_basis, dwkv_workspace_bytes, make_config)
 
 
@@ -36,6 +36,11 @@ class CompressedKVCache:
         dwkv_reset(self.handle)
 
     # ------------------------------------------------------------------ setup
+    @property
+    def splits(self) -> int:
+        """Decode workgroups per (sequence, KV head)."""
+        return dwkv_decode_splits(self.handle)
+
     def workspace(self, batch: int) -> torch.Tensor:
         ws = self._ws.get(batch)
         if ws is None:

@@ -322,6 +322,13 @@ int dwkv_workspace_bytes(const dwkv_config *cfg, int batch, size_t *bytes)
     return DWKV_OK;
 }
 
+int dwkv_decode_splits(const dwkv_handle *h, int *splits)
+{
+    if (!valid_handle(h) || !splits) return DWKV_ERR_INVALID_ARG;
+    *splits = h->splits;
+    return DWKV_OK;
+}
+
 int dwkv_decode_attn(dwkv_handle *h, int layer, const void *q, int batch, float softmax_scale,
                      float *out, void *workspace, size_t workspace_bytes, void *stream)
 {

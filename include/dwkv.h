@@ -175,6 +175,13 @@ int dwkv_read_counts(dwkv_handle *h, int layer, int batch, int32_t *host_counts,
 int dwkv_workspace_bytes(const dwkv_config *cfg, int batch, size_t *bytes);
 
 /*
+ * Workgroups per (sequence, KV head) that dwkv_decode_attn and
+ * dwkv_decode_step launch with this handle (the config's decode_splits, or
+ * the count chosen from the capacities when that is 0).  Host only.
+ */
+int dwkv_decode_splits(const dwkv_handle *h, int *splits);
+
+/*
  * Decode attention of one layer (the hot path; paper §3 last paragraph, and
  * the decode procedure of the zhichai.net summary Ch. 1.2):
  *   out[b][g][:] = sum_t softmax_t(softmax_scale * q[b][g] . K^_t) V^_t

@@ -134,6 +134,29 @@ def test_create_and_call_validation_without_gpu():
     assert d._lib.dwkv_destroy(None) == d.DWKV_ERR_INVALID_ARG
 
 
+@pytest.mark.parametrize("ci,extra,expect", [(1, 282, 9), (2, 282, 32), (3, 82, 2), (4, 82, 32), (2, 6, 32),
+                                             (4, 6, 32)])
+def test_split_plan_of_the_workloads(ci, extra, expect):
+    """The split count the benchmark's caches get (capacities of the
+    workload plus its appended tokens) and the full-size step tests' (a few
+    spare slots) agree: 32 at 64K and 128K."""
+    from workload.gen import max_tier_counts
+    c = w.get_config(ci)
+    cap = [int(x) + extra for x in max_tier_counts(c)]
+    cfg = d.make_config(c.num_layers, c.layers_per_group, c.num_q_heads, c.num_kv_heads, c.head_dim,
+                        c.r_max, c.tier_rank, c.resid_per_tier, c.resid_bits, c.batch, cap,
+                        c.n_tokens + extra, 0)
+    h = ctypes.c_void_p()
+    need = d.dwkv_arena_bytes(cfg)
+    assert d._lib.dwkv_create(ctypes.byref(cfg), ctypes.c_void_p(1 << 40), need, ctypes.byref(h)) == d.DWKV_OK
+    try:
+        assert d.dwkv_decode_splits(h) == expect
+    finally:
+        d._lib.dwkv_destroy(h)
+    n = ctypes.c_int()
+    assert d._lib.dwkv_decode_splits(None, ctypes.byref(n)) == d.DWKV_ERR_INVALID_ARG
+
+
 def test_workspace_scales_with_batch_and_splits():
     a = d.dwkv_workspace_bytes(_cfg(decode_splits=4), 1)
     b = d.dwkv_workspace_bytes(_cfg(decode_splits=8), 1)

@@ -131,10 +131,97 @@ def test_append_paper_literal_tiers(G):
 
 
 def test_append_many_random_vectors(G):
-    """~16k encodings (64 sequences x 8 heads x 2 (K,V) x 16 steps)."""
-    cfg = w.get_config(1).with_(batch=64)
-    cache, _, _ = _append_steps(G, cfg, steps=16, n0=8)
+    """102,400 encodings (256 sequences x 8 heads x 2 (K,V) x 25 steps) of
+    the Llama-3-8B shape, each bit for bit."""
+    cfg = w.get_config(1).with_(batch=256)
+    cache, _, _ = _append_steps(G, cfg, steps=25, n0=8)
     cache.close()
+
+
+def _append_given(G, cfg, bases, k, v, tier, n0=4):
+    """One append of the given fp16 vectors k, v [B][H][d] and tiers, compared
+    bit for bit with the oracle's encoding."""
+    cache = G.make_cache(cfg, n=n0, extra=4)
+    try:
+        G.load_bases(cache, bases, groups=[0])
+        lay = gen_layer(cfg, 0, n=n0)
+        G.load_layer(cache, 0, lay)
+        before = cache.read_counts(0, cfg.batch)
+        cache.append(0, G.dev(k), G.dev(v), G.dev(tier))
+        enc = oracle.append_layer(cfg, bases["K"][0], bases["V"][0], k, v, tier)
+        exported, counts, slots = G.export_np(cache, 0, cfg.batch, n0 + 1)
+        _compare_token(cfg, exported, slots, before, n0, enc, tier)
+        assert cache.check_errors() == 0
+        return enc
+    finally:
+        cache.close()
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_append_planted_ties(G, bits):
+    """Identity bases and inputs drawn from a handful of values, so most
+    residual magnitudes tie with others: the kept channels must follow the
+    tie rule (larger |e| first, then the smaller channel) on the GPU too."""
+    d = 64
+    cfg = tiny_config(batch=48, num_q_heads=4, num_kv_heads=2, head_dim=d, r_max=d,
+                      tier_rank=(8, 16, 32, 64), tier_prob=(0.25, 0.25, 0.25, 0.25),
+                      resid_channels=8 if bits == 4 else 5, resid_bits=bits, n_tokens=4)
+    bases = make_bases(cfg, identity=True)
+    rng = np.random.default_rng(71 + bits)
+    vals = np.array([0.0, 0.25, -0.25, 0.5, -0.5, 1.0, -1.0], np.float16)
+    B, H = cfg.batch, cfg.num_kv_heads
+    k = vals[rng.integers(0, len(vals), size=(B, H, d))]
+    v = vals[rng.integers(0, len(vals), size=(B, H, d))]
+    tier = rng.integers(0, 3, size=(B, H)).astype(np.uint8)       # ranks 8..32: residual channels remain
+    enc = _append_given(G, cfg, bases, k, v, tier)
+    # the ties really are there: some kept channel ties with an unkept one
+    tied = 0
+    for b in range(B):
+        for h in range(H):
+            r = cfg.tier_rank[int(tier[b, h])]
+            e = np.abs(k[b, h].astype(np.float32))
+            e[:r] = 0.0                                      # B = I: e is x past the rank
+            kept = enc["idxK"][b, h, :cfg.resid_channels].astype(int)
+            low = e[kept].min()
+            tied += int((e[np.setdiff1d(np.arange(d), kept)] == low).any())
+    assert tied > B * H // 4
+
+
+def test_append_in_span_vectors_have_zero_scale(G):
+    """Vectors inside the span of the first r basis vectors of exact bases
+    (identity and signed-permutation): the residual is exactly zero, so the
+    scale and every code are 0 and the kept channels are 0..s-1."""
+    from tests.helpers import signed_permutation_basis
+    d, R = 128, 64
+    cfg = tiny_config(batch=16, num_q_heads=8, num_kv_heads=2, head_dim=d, r_max=R,
+                      tier_rank=(8, 16, 32, 64), tier_prob=(0.25, 0.25, 0.25, 0.25),
+                      resid_channels=8, resid_bits=4, n_tokens=4)
+    rng = np.random.default_rng(5)
+    B, H = cfg.batch, cfg.num_kv_heads
+    for kind in ("identity", "permutation"):
+        if kind == "identity":
+            bases = {"K": np.zeros((1, H, R, d), np.float16), "V": np.zeros((1, H, R, d), np.float16)}
+            for z in "KV":
+                bases[z][0, :] = np.eye(d, dtype=np.float16)[:R]
+        else:
+            bases = {"K": np.zeros((1, H, R, d), np.float16), "V": np.zeros((1, H, R, d), np.float16)}
+            for zi, z in enumerate("KV"):
+                for h in range(H):
+                    bases[z][0, h] = signed_permutation_basis(d, R, 10 * zi + h)[0]
+        tier = rng.integers(0, 4, size=(B, H)).astype(np.uint8)
+        k = np.zeros((B, H, d), np.float16)
+        v = np.zeros((B, H, d), np.float16)
+        for b in range(B):
+            for h in range(H):
+                r = cfg.tier_rank[int(tier[b, h])]
+                for x, z in ((k, "K"), (v, "V")):
+                    c = rng.standard_normal(r).astype(np.float16)
+                    x[b, h] = (c.astype(np.float32) @ bases[z][0, h, :r].astype(np.float32)).astype(np.float16)
+        enc = _append_given(G, cfg, bases, k, v, tier)
+        for z in "KV":
+            assert not enc["scale" + z].view(np.uint16).any()
+            assert not enc["val" + z].any()
+            assert (enc["idx" + z] == np.arange(8, dtype=np.uint8)).all()
 
 
 def test_identity_basis_append_is_hand_predictable(G):

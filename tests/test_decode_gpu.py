@@ -38,6 +38,7 @@ def _run(G, cfg, layers=(0,), splits=0, peak=1.0, identity=False, all_top=False,
     try:
         G.load_bases(cache, bases, groups=sorted({l // cfg.layers_per_group for l in layers}))
         for layer in layers:
+            print(f"decode test: {cfg.name} n={n} layer={layer} splits={cache.splits}", flush=True)
             lay = gen_layer(cfg, layer, n=n, all_top=all_top, variant_seed=variant_seed)
             if ragged is not None:
                 lay["n_tokens"][:] = ragged
@@ -147,14 +148,14 @@ def test_wide_basis_low_rank_tiers(G):
 
 
 # ---------------------------------------------------------------- full-size workloads
-# Every layer of these workloads is decoded in the launch configuration the
-# benchmark uses (automatic split count); the oracle checks sampled
-# (sequence, KV head) pairs of sampled layers.
+# Sampled layers of these workloads are decoded in the launch configuration
+# the benchmark uses (automatic split count); the oracle checks every
+# (sequence, KV head) pair of them.
 @pytest.mark.parametrize("ci,layers,pairs", [
     (1, (0, 31), None),
-    (2, (0, 17), [(0, 0), (0, 5)]),
-    (3, (3,), [(0, 0), (7, 3), (15, 7)]),
-    (4, (0, 79), [(0, 0), (0, 7)]),
+    (2, (0, 17), None),
+    (3, (3,), None),
+    (4, (0, 79), None),
 ])
 def test_full_size_workloads_sampled(G, ci, layers, pairs):
     cfg = w.get_config(ci)
@@ -163,8 +164,8 @@ def test_full_size_workloads_sampled(G, ci, layers, pairs):
 
 def test_full_size_64k_peaked_and_needle(G):
     cfg = w.get_config(2)
-    _run(G, cfg, layers=(9,), pairs=[(0, 1), (0, 6)], peak=16.0)
-    _run(G, cfg, layers=(9,), pairs=[(0, 2)], needle=True)
+    _run(G, cfg, layers=(9,), peak=16.0)
+    _run(G, cfg, layers=(9,), needle=True)
 
 
 def test_repeat_launch_is_bitwise_deterministic(G):
