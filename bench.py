@@ -54,6 +54,13 @@ def parse_args():
     p.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this "
                         "script with --copy-probe into profiles/ and exit")
+    p.add_argument("--trace-summary", metavar="TRACE_DIR",
+                   help="summarise a rocprofv3 --kernel-trace --stats run of this script into "
+                        "profiles/ and exit")
+    p.add_argument("--bench-json", metavar="FILE",
+                   help="with --trace-summary: the JSON line of a default run of the same build, "
+                        "quoted beside the trace; with --pmc-summary: the counter run's own JSON line "
+                        "(its algorithmic bytes per launch)")
     return p.parse_args()
 
 
@@ -80,7 +87,14 @@ def _pmc_per_dispatch(run_dir: str, counter: str):
     return out
 
 
-def pmc_summary(workload: str, fetch_dir: str, write_dir: str):
+def _json_line(path: str) -> dict:
+    """The last JSON object line of a file (a bench run's output, possibly
+    mixed with a profiler's messages)."""
+    lines = [l for l in open(path).read().splitlines() if l.startswith("{")]
+    return json.loads(lines[-1])
+
+
+def pmc_summary(workload: str, fetch_dir: str, write_dir: str, bench_json: Optional[str] = None):
     """HBM bytes per decode launch from FETCH_SIZE / WRITE_SIZE (KiB per
     dispatch), each scaled by what the same counter reads for a plain copy
     of COPY_PROBE_BYTES bytes in the same process."""
@@ -105,7 +119,111 @@ def pmc_summary(workload: str, fetch_dir: str, write_dir: str):
     os.makedirs(PROFILES, exist_ok=True)
     path = os.path.join(PROFILES, f"decode_{workload}_traffic.json")
     json.dump(rec, open(path, "w"), indent=1)
+    cfg = next(c for c in w.CONFIGS if c.name == workload)
+    ci = w.CONFIGS.index(cfg)
+    alg = None
+    if bench_json:     # the JSON line the counter run itself printed
+        alg = _json_line(bench_json)["roofline"]["algorithmic_bytes_per_launch"]
+        rec["algorithmic_bytes_per_launch"] = alg
+        json.dump(rec, open(path, "w"), indent=1)
+    f, wr = res["FETCH_SIZE"], res["WRITE_SIZE"]
+    lines = [
+        f"# decode_kernel HBM traffic, {workload}",
+        "",
+        "The kernel measured is the one-launch decode step (decode attention plus the append of the new",
+        "token), as `bench.py` launches it.",
+        "",
+        "Commands (run from /tmp with TMPDIR=/tmp on one MI355X), then the summary on any host:",
+        "",
+        "```",
+        f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d <fetch> -o run -- python3 <repo>/bench.py "
+        f"--config {ci} {PMC_RUN_ARGS}",
+        f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d <write> -o run -- python3 <repo>/bench.py "
+        f"--config {ci} {PMC_RUN_ARGS}",
+        f"python3 <repo>/bench.py --config {ci} --pmc-summary <fetch> <write> --bench-json <fetch run's JSON line>",
+        "```",
+        "",
+        "`--copy-probe` adds a plain 512 MiB device-to-device copy to the same process; each counter is",
+        "scaled by (512 MiB) / (what the counter reads for that copy).",
+        "",
+        "| counter | decode KiB / dispatch (mean) | dispatches | copy KiB / dispatch | scale | decode bytes / launch |",
+        "|---|---|---|---|---|---|",
+        f"| FETCH_SIZE | {f['decode_kib_mean']:.1f} | {f['decode_dispatches']} | {f['copy_kib_mean']:.1f} | "
+        f"{f['scale']:.4f} | {f['bytes_per_launch']:.0f} |",
+        f"| WRITE_SIZE | {wr['decode_kib_mean']:.1f} | {wr['decode_dispatches']} | {wr['copy_kib_mean']:.1f} | "
+        f"{wr['scale']:.4f} | {wr['bytes_per_launch']:.0f} |",
+        "",
+        f"HBM traffic per launch: {total:.0f} bytes"
+        + (f", {total / alg:.3f}x the {alg:.0f} algorithmic bytes (reads {f['bytes_per_launch'] / alg:.3f}x)."
+           if alg else "."),
+        "",
+        f"Decode source sha256: `{rec['decode_source_sha256']}` (bench.py reports `traffic` only while "
+        "decode.hip matches it).",
+    ]
+    open(os.path.join(PROFILES, f"decode_{workload}_traffic.md"), "w").write("\n".join(lines) + "\n")
     print(json.dumps(rec), flush=True)
+
+
+PMC_RUN_ARGS = "--steps 2 --warmup 1 --no-cpu-baseline --copy-probe --kernel-reps 1"
+TRACE_RUN_ARGS = "--steps 16 --warmup 2 --no-cpu-baseline"
+
+
+def trace_summary(cfg, ci: int, trace_dir: str, bench_json: Optional[str]):
+    """profiles/decode_<workload>_kernel_trace.md from a rocprofv3
+    --kernel-trace --stats run (its *_kernel_stats.csv)."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_stats.csv under {trace_dir}")
+    rows = []
+    for f in files:
+        rows += list(csv.DictReader(open(f)))
+    dec = [r for r in rows if "decode_kernel" in r["Name"]]
+    if not dec:
+        raise SystemExit("no decode_kernel in the trace")
+    bj = _json_line(bench_json) if bench_json else None
+    lines = [
+        f"# decode_kernel, {cfg.name} (batch {cfg.batch}, {cfg.num_layers} layers, {cfg.num_q_heads} q / "
+        f"{cfg.num_kv_heads} KV heads, d {cfg.head_dim}, {cfg.n_tokens} tokens)",
+        "",
+        "The kernel is the one-launch decode step (`dwkv_decode_step`: decode attention plus the append of the new",
+        "token), which is what `bench.py` launches per layer.",
+        "",
+        "Command (run from /tmp with TMPDIR=/tmp on one MI355X), then the summary on any host:",
+        "",
+        "```",
+        f"rocprofv3 --kernel-trace --stats --output-format csv -d <out> -o bench -- python3 <repo>/bench.py "
+        f"--config {ci} {TRACE_RUN_ARGS}",
+        f"python3 <repo>/bench.py --config {ci} --trace-summary <out> [--bench-json <default run's line>]",
+        "```",
+        "",
+        "Kernel statistics (durations in ns; graph replays of the warm-up and timed steps plus the replays of",
+        "the one-step timing graph):",
+        "",
+        "| kernel | calls | average ns | min ns | max ns | stddev ns |",
+        "|---|---|---|---|---|---|",
+    ]
+    for r in dec:
+        lines.append(f"| {r['Name']} | {r['Calls']} | {float(r['AverageNs']):.0f} | {float(r['MinNs']):.0f} | "
+                     f"{float(r['MaxNs']):.0f} | {float(r.get('StdDev', 0) or 0):.0f} |")
+    avg = sum(float(r["AverageNs"]) * int(r["Calls"]) for r in dec) / sum(int(r["Calls"]) for r in dec)
+    lines.append("")
+    if bj:
+        rf = bj["roofline"]
+        alg = rf["algorithmic_bytes_per_launch"]
+        lines += [
+            f"Algorithmic bytes per launch: {alg:.0f} -> {alg / avg:.0f} GB/s at the trace average "
+            f"({alg / avg / PEAK_HBM_GBPS * 100:.1f}% of {PEAK_HBM_GBPS:.0f} GB/s).",
+            "",
+            f"The same build's default `bench.py --config {ci}` run: {bj['value']:.1f} tokens/s, "
+            f"{rf['mean_launch_us']:.2f} us per launch over its timed region ({rf['achieved']:.0f} GB/s, "
+            f"{rf['frac'] * 100:.1f}% of peak), {rf['one_step_graph_launch_us']:.2f} us from replays of a graph",
+            "of one step's launches.  The trace's start-to-end durations of back-to-back kernels include each",
+            "kernel's end, which overlaps the next kernel's start.",
+        ]
+    open(os.path.join(PROFILES, f"decode_{cfg.name}_kernel_trace.md"), "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines), flush=True)
 
 
 def _gen_layer_job(args):
@@ -204,7 +322,10 @@ def main():
         sys.exit(2)
     cfg = w.get_config(args.config)
     if args.pmc_summary:
-        pmc_summary(cfg.name, *args.pmc_summary)
+        pmc_summary(cfg.name, *args.pmc_summary, bench_json=args.bench_json)
+        return
+    if args.trace_summary:
+        trace_summary(cfg, args.config, args.trace_summary, args.bench_json)
         return
     K = args.steps if args.steps is not None else cfg.bench_steps
     W = args.warmup
