@@ -45,6 +45,8 @@ DWKV_DEVERR_TIER_FULL = 1
 DWKV_DEVERR_POS_FULL = 2
 DWKV_DEVERR_BAD_TIER = 4
 DWKV_DEVERR_BAD_INDEX = 8
+DWKV_NOALLOC_SCRATCH_BYTES = 4 << 20
+DWKV_NOALLOC_MAX_PAIRS = 1024
 
 
 class dwkv_config(ctypes.Structure):
@@ -85,6 +87,7 @@ _SIGS = {
     "dwkv_decode_attn": [_P, _I, _P, _I, ctypes.c_float, _P, _P, ctypes.c_size_t, _P],
     "dwkv_append": [_P, _I, _P, _P, _P, _P, _P, _I, _P],
     "dwkv_decode_step": [_P, _I, _P, _I, ctypes.c_float, _P, _P, ctypes.c_size_t, _P, _P, _P, _P, _P, _P],
+    "dwkv_decode_step_noalloc": [_P, _I, _P, _I, ctypes.c_float, _P, _P, _P, _P, _P, _P, _P],
     "dwkv_check_errors": [_P, _P, ctypes.POINTER(ctypes.c_uint32)],
     "dwkv_clear_errors": [_P, _P],
 }
@@ -295,6 +298,26 @@ def dwkv_decode_step(h, layer: int, q, out, workspace, k, v, tier, gateK=None, g
                                  _ptr(gateK, torch.float16, (B, H), name="gateK"),
                                  _ptr(gateV, torch.float16, (B, H), name="gateV"), _stream(stream)),
            "dwkv_decode_step")
+
+
+def dwkv_decode_step_noalloc(h, layer: int, q, out, k, v, tier, gateK=None, gateV=None,
+                             softmax_scale: Optional[float] = None, stream=None) -> None:
+    """dwkv_decode_step with the library's static scratch array in place of a
+    caller workspace (no device allocation anywhere).  Arguments as
+    dwkv_decode_step without the workspace."""
+    import torch
+    B, Hq, d = q.shape
+    H = k.shape[1] if k.dim() == 3 else -1
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    _check(_lib.dwkv_decode_step_noalloc(h, layer, _ptr(q, torch.float16, name="q"), B, float(softmax_scale),
+                                         _ptr(out, torch.float32, (B, Hq, d), name="out"),
+                                         _ptr(k, torch.float16, (B, H, d), name="k"),
+                                         _ptr(v, torch.float16, (B, H, d), name="v"),
+                                         _ptr(tier, torch.uint8, (B, H), name="tier"),
+                                         _ptr(gateK, torch.float16, (B, H), name="gateK"),
+                                         _ptr(gateV, torch.float16, (B, H), name="gateV"), _stream(stream)),
+           "dwkv_decode_step_noalloc")
 
 
 def dwkv_check_errors(h, stream=None) -> int:

@@ -4,6 +4,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 
 #include "dwkv.h"
@@ -166,6 +167,33 @@ size_t decode_workspace_bytes(const Layout &ly, int batch, int splits)
     return (size_t)off;
 }
 
+// The decode workspace of dwkv_decode_step_noalloc: a fixed region of
+// arrival counters at the start (so that no call's partials ever overlap
+// another call's counters, whatever their batch), then the per-split maxima,
+// normalisers and output vectors as in a caller workspace.
+constexpr int64_t kScratchCounterBytes = (int64_t)DWKV_NOALLOC_MAX_PAIRS * kArriveStride * 4;
+
+static size_t noalloc_workspace_bytes(const Layout &ly, int batch, int splits)
+{
+    const int64_t B = batch;
+    int64_t off = kScratchCounterBytes;
+    off += align_up(B * ly.Hkv * splits * kMlStride * 4, 256);
+    off += align_up(B * ly.Hq * splits * (int64_t)ly.d * 4, 256);
+    return (size_t)off;
+}
+
+static DecodeWorkspace carve_noalloc(const Layout &ly, uint8_t *p, int batch, int splits)
+{
+    DecodeWorkspace w;
+    w.arrive = reinterpret_cast<uint32_t *>(p);
+    p += kScratchCounterBytes;
+    w.pm = reinterpret_cast<float *>(p);
+    w.pl = w.pm + kMlNorm;
+    p += align_up((int64_t)batch * ly.Hkv * splits * kMlStride * 4, 256);
+    w.po = reinterpret_cast<float *>(p);
+    return w;
+}
+
 DecodeWorkspace carve_workspace(const Layout &ly, void *ws, int batch, int splits)
 {
     const int64_t B = batch;
@@ -194,6 +222,43 @@ static int hip_status(hipError_t e)
 }
 
 static bool valid_handle(const dwkv_handle *h) { return h && h->arena; }
+
+// Scratch memory of dwkv_decode_step_noalloc.  Each GPU the library runs on
+// holds its own copy until the process ends.  In host code `scratch` names
+// a host-side stand-in, never device memory: kernels and copies take the
+// device address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) uint8_t scratch[DWKV_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];      // device address of `scratch` per device, once set up
+}  // namespace
+
+// The current device's scratch address, set up on the first call on that
+// device: the address is looked up, and the arrival counters are cleared by
+// a kernel queued on `stream` ahead of the caller's first decode (each
+// decode leaves them at zero for the next).
+static int noalloc_scratch(hipStream_t stream, uint8_t **out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e);
+    if (dev < 0 || dev >= kMaxDevices) return DWKV_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_status(e);
+        if (!ptr) return DWKV_ERR_HIP;
+        e = dwkv::launch_fill_u32(static_cast<uint32_t *>(ptr), 0u, dwkv::kScratchCounterBytes / 4, stream);
+        if (e != hipSuccess) return hip_status(e);
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = static_cast<uint8_t *>(g_scratch_ptr[dev]);
+    return DWKV_OK;
+}
+
 
 extern "C" {
 
@@ -359,6 +424,29 @@ int dwkv_decode_step(dwkv_handle *h, int layer, const void *q, int batch, float 
         return DWKV_ERR_WORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);
     dwkv::DecodeWorkspace ws = dwkv::carve_workspace(ly, workspace, batch, h->splits);
+    const dwkv::AppendArgs ap{static_cast<const uint16_t *>(k), static_cast<const uint16_t *>(v),
+                              static_cast<const uint8_t *>(tier), static_cast<const uint16_t *>(gateK),
+                              static_cast<const uint16_t *>(gateV)};
+    return hip_status(
+        dwkv::launch_decode(ly, h->arena, layer, q, batch, softmax_scale, out, ws, h->splits, &ap, s));
+}
+
+int dwkv_decode_step_noalloc(dwkv_handle *h, int layer, const void *q, int batch, float softmax_scale,
+                             float *out, const void *k, const void *v, const void *tier,
+                             const void *gateK, const void *gateV, void *stream)
+{
+    if (!valid_handle(h) || !q || !out || !k || !v || !tier) return DWKV_ERR_INVALID_ARG;
+    const Layout &ly = h->ly;
+    if (layer < 0 || layer >= ly.L || batch <= 0 || batch > ly.Bmax) return DWKV_ERR_INVALID_ARG;
+    if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale)) return DWKV_ERR_INVALID_ARG;
+    if ((int64_t)batch * ly.Hkv > DWKV_NOALLOC_MAX_PAIRS) return DWKV_ERR_WORKSPACE;
+    if (dwkv::noalloc_workspace_bytes(ly, batch, h->splits) > (size_t)DWKV_NOALLOC_SCRATCH_BYTES)
+        return DWKV_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint8_t *base = nullptr;
+    const int rc = noalloc_scratch(s, &base);
+    if (rc != DWKV_OK) return rc;
+    dwkv::DecodeWorkspace ws = dwkv::carve_noalloc(ly, base, batch, h->splits);
     const dwkv::AppendArgs ap{static_cast<const uint16_t *>(k), static_cast<const uint16_t *>(v),
                               static_cast<const uint8_t *>(tier), static_cast<const uint16_t *>(gateK),
                               static_cast<const uint16_t *>(gateV)};

@@ -237,6 +237,26 @@ int dwkv_decode_step(dwkv_handle *h, int layer, const void *q, int batch, float 
                      const void *v, const void *tier, const void *gateK, const void *gateV,
                      void *stream);
 
+/*
+ * dwkv_decode_step without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The split partials and arrival counters
+ * live in a static device array of DWKV_NOALLOC_SCRATCH_BYTES per GPU,
+ * which the library holds until the process ends; nothing is allocated or
+ * freed.  The first call on a device looks the array up and queues a
+ * kernel on `stream` that clears its counters; every call leaves them at
+ * zero for the next.  Every call on one GPU shares that GPU's array: calls
+ * that overlap on one GPU (other streams, other threads, other handles)
+ * race and give wrong results.  DWKV_ERR_WORKSPACE when batch * num_kv_heads
+ * exceeds DWKV_NOALLOC_MAX_PAIRS or the partials of batch sequences at the
+ * handle's split count exceed the array.  Otherwise as dwkv_decode_step.
+ */
+#define DWKV_NOALLOC_SCRATCH_BYTES (4 << 20)
+#define DWKV_NOALLOC_MAX_PAIRS 1024
+int dwkv_decode_step_noalloc(dwkv_handle *h, int layer, const void *q, int batch, float softmax_scale,
+                             float *out, const void *k, const void *v, const void *tier,
+                             const void *gateK, const void *gateV, void *stream);
+
 /* Synchronises the stream; returns DWKV_ERR_DEVICE if the device error word
  * is set (its bits in *bits if non-NULL), else DWKV_OK. */
 int dwkv_check_errors(dwkv_handle *h, void *stream, uint32_t *bits);

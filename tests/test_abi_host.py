@@ -157,6 +157,39 @@ def test_split_plan_of_the_workloads(ci, extra, expect):
     assert d._lib.dwkv_decode_splits(None, ctypes.byref(n)) == d.DWKV_ERR_INVALID_ARG
 
 
+def test_noalloc_step_rejects_what_its_scratch_cannot_hold():
+    """Host checks of dwkv_decode_step_noalloc, before any HIP call: more
+    (sequence, KV head) pairs than its counters, or partials larger than its
+    static array, give DWKV_ERR_WORKSPACE; bad arguments INVALID_ARG."""
+    L = d._lib
+    kk = ctypes.c_void_p(1 << 44)
+    big = _cfg(max_batch=200, decode_splits=8)           # 200 x 8 pairs > 1024
+    h = ctypes.c_void_p()
+    assert L.dwkv_create(ctypes.byref(big), ctypes.c_void_p(1 << 40), d.dwkv_arena_bytes(big),
+                         ctypes.byref(h)) == d.DWKV_OK
+    try:
+        assert L.dwkv_decode_step_noalloc(h, 0, kk, 129, 0.1, kk, kk, kk, kk, None, None,
+                                          None) == d.DWKV_ERR_WORKSPACE
+        assert L.dwkv_decode_step_noalloc(h, 0, kk, 201, 0.1, kk, kk, kk, kk, None, None,
+                                          None) == d.DWKV_ERR_INVALID_ARG
+        assert L.dwkv_decode_step_noalloc(h, 0, kk, 1, 0.1, kk, kk, None, kk, None, None,
+                                          None) == d.DWKV_ERR_INVALID_ARG
+        assert L.dwkv_decode_step_noalloc(h, 32, kk, 1, 0.1, kk, kk, kk, kk, None, None,
+                                          None) == d.DWKV_ERR_INVALID_ARG
+        assert L.dwkv_decode_step_noalloc(h, 0, kk, 1, 0.0, kk, kk, kk, kk, None, None,
+                                          None) == d.DWKV_ERR_INVALID_ARG
+    finally:
+        L.dwkv_destroy(h)
+    wide = _cfg(max_batch=16, decode_splits=256)          # 16 x 32 x 256 x 128 x 4 B of partials
+    assert L.dwkv_create(ctypes.byref(wide), ctypes.c_void_p(1 << 40), d.dwkv_arena_bytes(wide),
+                         ctypes.byref(h)) == d.DWKV_OK
+    try:
+        assert L.dwkv_decode_step_noalloc(h, 0, kk, 16, 0.1, kk, kk, kk, kk, None, None,
+                                          None) == d.DWKV_ERR_WORKSPACE
+    finally:
+        L.dwkv_destroy(h)
+
+
 def test_workspace_scales_with_batch_and_splits():
     a = d.dwkv_workspace_bytes(_cfg(decode_splits=4), 1)
     b = d.dwkv_workspace_bytes(_cfg(decode_splits=8), 1)
