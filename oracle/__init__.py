@@ -48,6 +48,12 @@ def _load(path: str):
     L.oracle_decode.restype = ctypes.c_int
     L.oracle_decode.argtypes = [ctypes.POINTER(_Shape), P, P, P, P, P, P, P, P, P, P, P, P,
                                 P, ctypes.c_double, P, P, ctypes.c_int, ctypes.c_int]
+    L.oracle_materialize.restype = ctypes.c_int
+    L.oracle_materialize.argtypes = [ctypes.POINTER(_Shape), P, P, P, P, P, P, P, P, P, P, P, P, P, P,
+                                     ctypes.c_int]
+    L.oracle_dense_decode.restype = ctypes.c_int
+    L.oracle_dense_decode.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int64,
+                                      P, P, P, P, ctypes.c_double, P, ctypes.c_int]
     L.oracle_append.restype = ctypes.c_int
     L.oracle_append.argtypes = [ctypes.c_int, ctypes.c_int, P, P, ctypes.c_int, ctypes.c_int,
                                 ctypes.c_int, ctypes.c_uint16, P, P, P, P]
@@ -141,6 +147,58 @@ def decode(cfg, lay: Dict[str, np.ndarray], basisK: np.ndarray, basisV: np.ndarr
         pa, npairs, int(threads))
     if rc != 0:
         raise ValueError("oracle_decode rejected its arguments")
+    return out
+
+
+def _shape(cfg, lay, tier_resid=None):
+    B, Hkv, n_max, R = lay["coefK"].shape
+    sh = _Shape()
+    sh.batch, sh.num_kv_heads, sh.head_dim = B, Hkv, cfg.head_dim
+    sh.num_q_heads = cfg.num_q_heads
+    sh.r_max, sh.s_max, sh.n_max = R, lay["idxK"].shape[3], n_max
+    sh.num_tiers = cfg.num_tiers
+    res = tuple(tier_resid) if tier_resid is not None else cfg.resid_per_tier
+    for k in range(cfg.num_tiers):
+        sh.tier_rank[k] = cfg.tier_rank[k]
+        sh.tier_resid[k] = res[k]
+    return sh
+
+
+def materialize(cfg, lay: Dict[str, np.ndarray], basisK: np.ndarray, basisV: np.ndarray,
+                threads: int = 0):
+    """(K^, V^) fp64 [B][H_kv][n_max][d]: Eq. (1) for every cached token in
+    position order, zero past each sequence's length."""
+    B, Hkv, n_max, R = lay["coefK"].shape
+    d = cfg.head_dim
+    sh = _shape(cfg, lay)
+    K = np.zeros((B, Hkv, n_max, d), np.float64)
+    V = np.zeros((B, Hkv, n_max, d), np.float64)
+    c = {k: np.ascontiguousarray(v) for k, v in lay.items()}
+    rc = lib().oracle_materialize(
+        ctypes.byref(sh), _p(np.ascontiguousarray(c["n_tokens"], np.int64)), _p(c["tier"]),
+        _p(_u16(basisK)), _p(_u16(basisV)), _p(_u16(c["coefK"])), _p(_u16(c["coefV"])),
+        _p(c["idxK"]), _p(c["idxV"]), _p(c["valK"]), _p(c["valV"]),
+        _p(_u16(c["scaleK"])), _p(_u16(c["scaleV"])), _p(K), _p(V), int(threads))
+    if rc != 0:
+        raise ValueError("oracle_materialize rejected its arguments")
+    return K, V
+
+
+def dense_decode(K: np.ndarray, V: np.ndarray, n_tokens, q: np.ndarray, alpha: Optional[float] = None,
+                 threads: int = 0) -> np.ndarray:
+    """Textbook attention [B][H_q][d] (fp64) over dense fp16 K, V
+    [B][H_kv][n_max][d] (token rows) for q fp16 [B][H_q][d]."""
+    B, Hkv, n_max, d = K.shape
+    Hq = q.shape[1]
+    if alpha is None:
+        alpha = 1.0 / np.sqrt(d)
+    out = np.zeros((B, Hq, d), np.float64)
+    n = np.ascontiguousarray(np.asarray(n_tokens, np.int64).reshape(B))
+    rc = lib().oracle_dense_decode(B, Hq, Hkv, d, n_max, _p(n), _p(_u16(np.ascontiguousarray(K))),
+                                   _p(_u16(np.ascontiguousarray(V))), _p(_u16(np.ascontiguousarray(q))),
+                                   float(alpha), _p(out), int(threads))
+    if rc != 0:
+        raise ValueError("oracle_dense_decode rejected its arguments")
     return out
 
 

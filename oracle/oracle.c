@@ -21,6 +21,12 @@
  *    fp64: fp16 inputs are exact in fp64, so the only error is the final
  *    rounding order of fp64 sums.
  *
+ *  oracle_materialize -- the Eq. (1) reconstruction of every cached token,
+ *    the explicit K^/V^ that a decode without the fused kernel writes out.
+ *
+ *  oracle_dense_decode -- textbook decode attention over a dense fp16 K/V
+ *    cache (the uncompressed baseline).
+ *
  *  oracle_append -- encoding one new K or V vector into the compressed form
  *    (paper §3 Method, second paragraph: coefficients by projection onto the
  *    current basis; residual kept only on the routed channels, with low-bit
@@ -235,6 +241,118 @@ int oracle_decode(const oracle_shape *sh, const int64_t *n_tokens, const uint8_t
         free(mx); free(den); free(z); free(x); free(qd); free(bK); free(bV);
     }
     return bad ? -1 : 0;
+}
+
+/* ------------------------------------------------------- materialisation */
+
+/*
+ * Kout, Vout[b][h][t][:] = the Eq. (1) reconstruction of token t (fp64) for
+ * t < n_tokens[b], zero beyond; arrays [B][H_kv][n_max][d].  Follows the
+ * paper's Eq. (1) (the basis combination of the token's coefficients plus
+ * its gated sparse residual), the step a decode without the fused kernel
+ * performs before attention (the topic page's Ch. 3.3: base lookup and
+ * residual dequantisation as launches of their own).
+ */
+int oracle_materialize(const oracle_shape *sh, const int64_t *n_tokens, const uint8_t *tier,
+                       const uint16_t *basisK, const uint16_t *basisV,
+                       const uint16_t *coefK, const uint16_t *coefV,
+                       const uint8_t *idxK, const uint8_t *idxV,
+                       const int8_t *valK, const int8_t *valV,
+                       const uint16_t *scaleK, const uint16_t *scaleV,
+                       double *Kout, double *Vout, int nthreads)
+{
+    const int B = sh->batch, Hkv = sh->num_kv_heads;
+    const int d = sh->head_dim, R = sh->r_max, S = sh->s_max;
+    const int64_t NM = sh->n_max;
+    if (Hkv <= 0 || d <= 0 || d > 256 || R <= 0 || sh->num_tiers <= 0 || sh->num_tiers > 8)
+        return -1;
+    int bad = 0;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+#endif
+    for (int p = 0; p < B * Hkv; ++p) {
+        int b = p / Hkv, h = p % Hkv;
+        int64_t base = ((int64_t)b * Hkv + h) * NM;
+        double *bK = (double *)malloc(sizeof(double) * (size_t)R * d);
+        double *bV = (double *)malloc(sizeof(double) * (size_t)R * d);
+        oracle_half_to_double_array(basisK + (int64_t)h * R * d, bK, (int64_t)R * d);
+        oracle_half_to_double_array(basisV + (int64_t)h * R * d, bV, (int64_t)R * d);
+        for (int64_t t = 0; t < NM; ++t) {
+            double *xk = Kout + (base + t) * d, *xv = Vout + (base + t) * d;
+            if (t >= n_tokens[b]) {
+                for (int j = 0; j < d; ++j)
+                    xk[j] = xv[j] = 0.0;
+                continue;
+            }
+            int64_t tt = base + t;
+            int k = tier[tt];
+            if (k >= sh->num_tiers) { bad = 1; k = 0; }
+            reconstruct(sh, bK, coefK + tt * R, idxK + tt * S, valK + tt * S, scaleK[tt], k, xk);
+            reconstruct(sh, bV, coefV + tt * R, idxV + tt * S, valV + tt * S, scaleV[tt], k, xv);
+        }
+        free(bK); free(bV);
+    }
+    return bad ? -1 : 0;
+}
+
+/* ------------------------------------------------------------ dense decode */
+
+/*
+ * Textbook decode attention over a dense fp16 cache (the uncompressed
+ * baseline the paper compares against, §4): out[b][g][:] =
+ * sum_t softmax_t(alpha q_g . K_t) V_t over t < n_tokens[b], query head g
+ * reading KV head g / (H_q / H_kv).  K, V fp16 [B][H_kv][n_max][d] token
+ * rows; q fp16 [B][H_q][d]; out fp64.  Empty context -> zeros.  Every sum
+ * in fp64.
+ */
+int oracle_dense_decode(int B, int Hq, int Hkv, int d, int64_t n_max, const int64_t *n_tokens,
+                        const uint16_t *K, const uint16_t *V, const uint16_t *q, double alpha,
+                        double *out, int nthreads)
+{
+    if (B <= 0 || Hkv <= 0 || Hq % Hkv != 0 || d <= 0 || d > 256)
+        return -1;
+    const int gq = Hq / Hkv;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1)
+#endif
+    for (int p = 0; p < B * Hq; ++p) {
+        int b = p / Hq, g = p % Hq, h = g / gq;
+        int64_t n = n_tokens[b];
+        double *o = out + (int64_t)p * d;
+        for (int j = 0; j < d; ++j)
+            o[j] = 0.0;
+        if (n <= 0)
+            continue;
+        const uint16_t *Kb = K + ((int64_t)b * Hkv + h) * n_max * d;
+        const uint16_t *Vb = V + ((int64_t)b * Hkv + h) * n_max * d;
+        double qd[256];
+        for (int j = 0; j < d; ++j)
+            qd[j] = oracle_half_to_double(q[(int64_t)p * d + j]);
+        double *z = (double *)malloc(sizeof(double) * (size_t)n);
+        double m = -INFINITY;
+        for (int64_t t = 0; t < n; ++t) {
+            double acc = 0.0;
+            for (int j = 0; j < d; ++j)
+                acc += qd[j] * oracle_half_to_double(Kb[t * d + j]);
+            z[t] = alpha * acc;
+            if (z[t] > m) m = z[t];
+        }
+        double den = 0.0;
+        for (int64_t t = 0; t < n; ++t) {
+            double w = exp(z[t] - m);
+            den += w;
+            for (int j = 0; j < d; ++j)
+                o[j] += w * oracle_half_to_double(Vb[t * d + j]);
+        }
+        for (int j = 0; j < d; ++j)
+            o[j] /= den;
+        free(z);
+    }
+    return 0;
 }
 
 /* ---------------------------------------------------------------- append */

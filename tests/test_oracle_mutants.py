@@ -22,6 +22,7 @@ import oracle
 from tests import test_oracle_append as TA
 from tests import test_oracle_decode as TD
 from tests import test_oracle_encoder_order as TO
+from tests import test_oracle_dense as TN
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(os.path.dirname(HERE), "oracle", "oracle.c")
@@ -49,6 +50,13 @@ APPEND_PINS = [
     lambda: TO.test_encoder_steps_match_exact_fma_chain(2, 64),
 ]
 
+DENSE_PINS = [
+    TN.test_materialize_matches_numpy_einsum,
+    TN.test_materialize_identity_basis_is_exact,
+    lambda: TN.test_dense_decode_equals_sdpa(0),
+    TN.test_dense_decode_closed_forms,
+]
+
 _STEP1 = ("        float acc = 0.0f;                                         /* step 1 */\n"
           "        for (int j = 0; j < d; ++j)\n"
           "            acc = fmaf(h2f(basis[(int64_t)i * d + j]), h2f(x[j]), acc);\n")
@@ -59,7 +67,9 @@ _STEP2 = ("        float acc = 0.0f;                                         /* 
 MUTANTS = {
     "drop_residual": ("x[idx[u]] += g * (double)val[u];", "(void)g;", DECODE_PINS),
     "residual_sign": ("x[idx[u]] += g * (double)val[u];", "x[idx[u]] -= g * (double)val[u];", DECODE_PINS),
-    "kv_basis_swap": ("reconstruct(sh, bV,", "reconstruct(sh, bK,", DECODE_PINS),
+    "kv_basis_swap": ("reconstruct(sh, bV, coefV + tt * R, idxV + tt * S, valV + tt * S, scaleV[tt], k, x);",
+                      "reconstruct(sh, bK, coefV + tt * R, idxV + tt * S, valV + tt * S, scaleV[tt], k, x);",
+                      DECODE_PINS),
     "head_map": ("q[((int64_t)b * Hq + h * gq + g) * d + j]", "q[((int64_t)b * Hq + g * Hkv + h) * d + j]",
                  DECODE_PINS),
     "no_softmax_scale": ("z[g * n + t] = alpha * acc;", "z[g * n + t] = acc;", DECODE_PINS),
@@ -73,6 +83,15 @@ MUTANTS = {
     "unrounded_coef": ("c[i] = h2f(c16[i]);", "c[i] = acc;", APPEND_PINS),
     "wrong_code_range": ("amax / (float)qmax", "amax / (float)(qmax + 1)", APPEND_PINS),
     "residual_flipped": ("e[j] = h2f(x[j]) - acc;", "e[j] = acc - h2f(x[j]);", APPEND_PINS),
+    "materialize_v_with_k_basis": ("reconstruct(sh, bV, coefV + tt * R, idxV + tt * S, valV + tt * S, scaleV[tt], k, xv);",
+                                   "reconstruct(sh, bK, coefV + tt * R, idxV + tt * S, valV + tt * S, scaleV[tt], k, xv);",
+                                   DENSE_PINS),
+    "materialize_ragged_ignored": ("            if (t >= n_tokens[b]) {", "            if (t >= NM) {", DENSE_PINS),
+    "dense_no_scale": ("            z[t] = alpha * acc;", "            z[t] = acc;", DENSE_PINS),
+    "dense_head_map": ("int b = p / Hq, g = p % Hq, h = g / gq;", "int b = p / Hq, g = p % Hq, h = g % Hkv;",
+                       DENSE_PINS),
+    "dense_no_normalisation": ("            o[j] /= den;\n        free(z);", "            o[j] /= 1.0;\n        free(z);",
+                               DENSE_PINS),
     "step1_descending": (_STEP1, _STEP1.replace("for (int j = 0; j < d; ++j)", "for (int j = d - 1; j >= 0; --j)"),
                          APPEND_PINS),
     "step2_descending": (_STEP2, _STEP2.replace("for (int i = 0; i < r; ++i)", "for (int i = r - 1; i >= 0; --i)"),
