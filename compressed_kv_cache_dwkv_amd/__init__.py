@@ -88,6 +88,10 @@ _SIGS = {
     "dwkv_append": [_P, _I, _P, _P, _P, _P, _P, _I, _P],
     "dwkv_decode_step": [_P, _I, _P, _I, ctypes.c_float, _P, _P, ctypes.c_size_t, _P, _P, _P, _P, _P, _P],
     "dwkv_decode_step_noalloc": [_P, _I, _P, _I, ctypes.c_float, _P, _P, _P, _P, _P, _P, _P],
+    "dwkv_materialize_layer": [_P, _I, _I, _P, _P, ctypes.c_int64, _P, _P],
+    "dwkv_dense_workspace_bytes": [_I, _I, _I, _I, _I, ctypes.POINTER(ctypes.c_size_t)],
+    "dwkv_dense_decode": [_P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_int64, _I, ctypes.c_float, _P, _P,
+                          ctypes.c_size_t, _P],
     "dwkv_check_errors": [_P, _P, ctypes.POINTER(ctypes.c_uint32)],
     "dwkv_clear_errors": [_P, _P],
 }
@@ -318,6 +322,43 @@ def dwkv_decode_step_noalloc(h, layer: int, q, out, k, v, tier, gateK=None, gate
                                          _ptr(gateK, torch.float16, (B, H), name="gateK"),
                                          _ptr(gateV, torch.float16, (B, H), name="gateV"), _stream(stream)),
            "dwkv_decode_step_noalloc")
+
+
+def dwkv_materialize_layer(h, layer: int, k_out, v_out, n_out=None, stream=None) -> None:
+    """k_out: fp16 [B][H_kv][n_cap][d]; v_out: fp16 [B][H_kv][n_cap/16][d][16];
+    n_out: int32 [B][H_kv] or None."""
+    import torch
+    B, H, n_cap, d = k_out.shape
+    _check(_lib.dwkv_materialize_layer(h, layer, B, _ptr(k_out, torch.float16, name="k_out"),
+                                       _ptr(v_out, torch.float16, (B, H, n_cap // 16, d, 16), name="v_out"),
+                                       n_cap, _ptr(n_out, torch.int32, (B, H), name="n_out"), _stream(stream)),
+           "dwkv_materialize_layer")
+
+
+def dwkv_dense_workspace_bytes(batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                               splits: int) -> int:
+    n = ctypes.c_size_t()
+    _check(_lib.dwkv_dense_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim, splits, ctypes.byref(n)),
+           "dwkv_dense_workspace_bytes")
+    return n.value
+
+
+def dwkv_dense_decode(q, k, v, n_tokens, out, workspace, splits: int, softmax_scale: Optional[float] = None,
+                      stream=None) -> None:
+    """q fp16 [B][H_q][d]; k fp16 [B][H_kv][n_cap][d]; v fp16
+    [B][H_kv][n_cap/16][d][16]; n_tokens int32 [B][H_kv]; out fp32 [B][H_q][d]."""
+    import torch
+    B, Hq, d = q.shape
+    _, Hkv, n_cap, _ = k.shape
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    ws = workspace.numel() * workspace.element_size()
+    _check(_lib.dwkv_dense_decode(_ptr(q, torch.float16, name="q"), _ptr(k, torch.float16, name="k"),
+                                  _ptr(v, torch.float16, (B, Hkv, n_cap // 16, d, 16), name="v"),
+                                  _ptr(n_tokens, torch.int32, (B, Hkv), name="n_tokens"), B, Hq, Hkv, d, n_cap,
+                                  splits, float(softmax_scale), _ptr(out, torch.float32, (B, Hq, d), name="out"),
+                                  _ptr(workspace, name="workspace"), ws, _stream(stream)),
+           "dwkv_dense_decode")
 
 
 def dwkv_check_errors(h, stream=None) -> int:

@@ -454,6 +454,77 @@ int dwkv_decode_step_noalloc(dwkv_handle *h, int layer, const void *q, int batch
         dwkv::launch_decode(ly, h->arena, layer, q, batch, softmax_scale, out, ws, h->splits, &ap, s));
 }
 
+int dwkv_materialize_layer(dwkv_handle *h, int layer, int batch, void *k_out, void *v_out, int64_t n_cap,
+                           int32_t *n_out, void *stream)
+{
+    if (!valid_handle(h) || !k_out || !v_out) return DWKV_ERR_INVALID_ARG;
+    const Layout &ly = h->ly;
+    if (layer < 0 || layer >= ly.L || batch <= 0 || batch > ly.Bmax) return DWKV_ERR_INVALID_ARG;
+    if (n_cap <= 0 || n_cap % 64 != 0 || n_cap < ly.max_tokens || n_cap / 64 > INT32_MAX) return DWKV_ERR_INVALID_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return hip_status(dwkv::launch_materialize(ly, h->arena, layer, batch, static_cast<uint16_t *>(k_out),
+                                               static_cast<uint16_t *>(v_out), n_cap, n_out, s));
+}
+
+static bool dense_shape_ok(int batch, int num_q_heads, int num_kv_heads, int head_dim, int splits)
+{
+    if (batch <= 0 || num_kv_heads <= 0 || num_q_heads <= 0 || num_q_heads % num_kv_heads != 0) return false;
+    const int gq = num_q_heads / num_kv_heads;
+    if (gq != 1 && gq != 2 && gq != 4 && gq != 8) return false;
+    if (head_dim != 64 && head_dim != 128) return false;
+    return splits >= 1 && splits <= dwkv::kMaxSplits;
+}
+
+static size_t dense_ws_bytes(int batch, int num_q_heads, int num_kv_heads, int head_dim, int splits)
+{
+    const int64_t B = batch;
+    int64_t off = dwkv::align_up(B * num_kv_heads * dwkv::kArriveStride * 4, 256);
+    off += dwkv::align_up(B * num_kv_heads * splits * dwkv::kMlStride * 4, 256);
+    off += dwkv::align_up(B * num_q_heads * (int64_t)splits * head_dim * 4, 256);
+    return (size_t)off;
+}
+
+int dwkv_dense_workspace_bytes(int batch, int num_q_heads, int num_kv_heads, int head_dim, int splits,
+                               size_t *bytes)
+{
+    if (!bytes || !dense_shape_ok(batch, num_q_heads, num_kv_heads, head_dim, splits)) return DWKV_ERR_INVALID_ARG;
+    *bytes = dense_ws_bytes(batch, num_q_heads, num_kv_heads, head_dim, splits);
+    return DWKV_OK;
+}
+
+int dwkv_dense_decode(const void *q, const void *k, const void *v, const int32_t *n_tokens, int batch,
+                      int num_q_heads, int num_kv_heads, int head_dim, int64_t n_cap, int splits,
+                      float softmax_scale, float *out, void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!q || !k || !v || !n_tokens || !out || !workspace) return DWKV_ERR_INVALID_ARG;
+    if (!dense_shape_ok(batch, num_q_heads, num_kv_heads, head_dim, splits)) return DWKV_ERR_INVALID_ARG;
+    if (n_cap <= 0 || n_cap % 64 != 0 || n_cap >= (int64_t(1) << 31)) return DWKV_ERR_INVALID_ARG;
+    if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale)) return DWKV_ERR_INVALID_ARG;
+    if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return DWKV_ERR_INVALID_ARG;
+    if (workspace_bytes < dense_ws_bytes(batch, num_q_heads, num_kv_heads, head_dim, splits))
+        return DWKV_ERR_WORKSPACE;
+    uint8_t *p = static_cast<uint8_t *>(workspace);
+    dwkv::DenseArgs a;
+    a.ws.arrive = reinterpret_cast<uint32_t *>(p);
+    p += dwkv::align_up((int64_t)batch * num_kv_heads * dwkv::kArriveStride * 4, 256);
+    a.ws.pm = reinterpret_cast<float *>(p);
+    a.ws.pl = a.ws.pm + dwkv::kMlNorm;
+    p += dwkv::align_up((int64_t)batch * num_kv_heads * splits * dwkv::kMlStride * 4, 256);
+    a.ws.po = reinterpret_cast<float *>(p);
+    a.q = static_cast<const uint16_t *>(q);
+    a.k = static_cast<const uint16_t *>(k);
+    a.v = static_cast<const uint16_t *>(v);
+    a.n = n_tokens;
+    a.out = out;
+    a.B = batch;
+    a.Hq = num_q_heads;
+    a.Hkv = num_kv_heads;
+    a.d = head_dim;
+    a.n_cap = n_cap;
+    a.scale = softmax_scale;
+    return hip_status(dwkv::launch_dense_decode(a, splits, static_cast<hipStream_t>(stream)));
+}
+
 int dwkv_append(dwkv_handle *h, int layer, const void *k, const void *v, const void *tier,
                 const void *gateK, const void *gateV, int batch, void *stream)
 {

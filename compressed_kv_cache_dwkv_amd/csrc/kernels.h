@@ -42,6 +42,26 @@ hipError_t launch_decode(const Layout &ly, uint8_t *arena, int layer, const void
                          float softmax_scale, float *out, const DecodeWorkspace &ws, int splits,
                          const AppendArgs *ap, hipStream_t stream);
 
+// Dense fp16 decode (the uncompressed comparator): q fp16 [B][Hq][d]; k fp16
+// [B][Hkv][n_cap][d] token rows; v fp16 [B][Hkv][n_cap/16][d][16]; n int32
+// [B][Hkv] tokens per (sequence, KV head); out fp32 [B][Hq][d].
+struct DenseArgs {
+    const uint16_t *q, *k, *v;
+    const int32_t *n;
+    float *out;
+    DecodeWorkspace ws;
+    int B, Hq, Hkv, d;
+    int64_t n_cap;
+    float scale;
+};
+hipError_t launch_dense_decode(const DenseArgs &a, int splits, hipStream_t stream);
+
+// Writes the Eq. (1) reconstruction of every cached token of `layer` (batch
+// sequences) into the dense layout above, in position order, and the tokens
+// per (sequence, KV head) into n_out (int32 [batch][Hkv], may be null).
+hipError_t launch_materialize(const Layout &ly, uint8_t *arena, int layer, int batch, uint16_t *kout,
+                              uint16_t *vout, int64_t n_cap, int32_t *n_out, hipStream_t stream);
+
 hipError_t launch_append(const Layout &ly, uint8_t *arena, int layer, const void *k,
                          const void *v, const void *tier, const void *gateK, const void *gateV,
                          int batch, hipStream_t stream);

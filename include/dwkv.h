@@ -257,6 +257,47 @@ int dwkv_decode_step_noalloc(dwkv_handle *h, int layer, const void *q, int batch
                              float *out, const void *k, const void *v, const void *tier,
                              const void *gateK, const void *gateV, void *stream);
 
+/*
+ * The explicit reconstruction an unfused decode performs before attention
+ * (paper §3 Eq. (1); the zhichai.net summary's Ch. 3.3 names base lookup and
+ * residual dequantisation as separate launches, and the paper's §5 ablation
+ * measures decode without the fused kernel): every cached token of `layer`
+ * for sequences b < batch, written as dense fp16 K^ and V^ in position order.
+ *   k_out: device fp16 [batch][H_kv][n_cap][head_dim] (token rows)
+ *   v_out: device fp16 [batch][H_kv][n_cap/16][head_dim][16] (16-token blocks,
+ *          channel-major inside a block)
+ *   n_cap: a multiple of 64, >= the config's max_tokens; positions past a
+ *          sequence's length up to the next multiple of 64 are written 0,
+ *          later ones are not written
+ *   n_out: device int32 [batch][H_kv] (tokens per sequence and KV head), or NULL
+ * Each element is the fp32 sum of the exact fp16 products plus the residual
+ * channels, rounded once to fp16.
+ */
+int dwkv_materialize_layer(dwkv_handle *h, int layer, int batch, void *k_out, void *v_out, int64_t n_cap,
+                           int32_t *n_out, void *stream);
+
+/* Device workspace of dwkv_dense_decode (host only).  Zero-fill it once
+ * before its first use; every call leaves it ready for the next. */
+int dwkv_dense_workspace_bytes(int batch, int num_q_heads, int num_kv_heads, int head_dim, int splits,
+                               size_t *bytes);
+
+/*
+ * Decode attention over a dense (uncompressed) fp16 K/V cache, the baseline
+ * the compressed cache is measured against (paper §4) and the attention
+ * launch of an unfused decode:
+ *   out[b][g][:] = sum_{t < n_tokens[b][h]} softmax_t(softmax_scale q[b][g] . K_t) V_t
+ * with h = g / (num_q_heads / num_kv_heads).
+ *   q: device fp16 [batch][num_q_heads][head_dim]
+ *   k, v: device, the layouts of dwkv_materialize_layer's k_out and v_out
+ *   n_tokens: device int32 [batch][num_kv_heads], each <= n_cap
+ *   splits: workgroups per (sequence, KV head), 1..256
+ *   out: device fp32 [batch][num_q_heads][head_dim]; zero for an empty context
+ * head_dim 64 or 128; 1, 2, 4 or 8 query heads per KV head.
+ */
+int dwkv_dense_decode(const void *q, const void *k, const void *v, const int32_t *n_tokens, int batch,
+                      int num_q_heads, int num_kv_heads, int head_dim, int64_t n_cap, int splits,
+                      float softmax_scale, float *out, void *workspace, size_t workspace_bytes, void *stream);
+
 /* Synchronises the stream; returns DWKV_ERR_DEVICE if the device error word
  * is set (its bits in *bits if non-NULL), else DWKV_OK. */
 int dwkv_check_errors(dwkv_handle *h, void *stream, uint32_t *bits);

@@ -190,6 +190,42 @@ def test_noalloc_step_rejects_what_its_scratch_cannot_hold():
         L.dwkv_destroy(h)
 
 
+def test_dense_comparator_host_checks():
+    """dwkv_dense_decode / dwkv_materialize_layer reject bad shapes before
+    any HIP call."""
+    L = d._lib
+    kk = ctypes.c_void_p(1 << 44)
+    ws = d.dwkv_dense_workspace_bytes(2, 32, 8, 128, 16)
+    assert ws >= 2 * 32 * 16 * 128 * 4
+    n = ctypes.c_size_t()
+    assert L.dwkv_dense_workspace_bytes(2, 24, 8, 128, 16, ctypes.byref(n)) == d.DWKV_ERR_INVALID_ARG
+    assert L.dwkv_dense_workspace_bytes(2, 32, 8, 96, 16, ctypes.byref(n)) == d.DWKV_ERR_INVALID_ARG
+    assert L.dwkv_dense_workspace_bytes(2, 32, 8, 128, 0, ctypes.byref(n)) == d.DWKV_ERR_INVALID_ARG
+    wsp = ctypes.c_void_p(1 << 43)
+    args = dict(q=kk, k=kk, v=kk, n=kk, B=2, Hq=32, Hkv=8, d=128, n_cap=4096, S=16, sc=0.1, out=kk)
+    def call(**kw):
+        a = dict(args, **kw)
+        return L.dwkv_dense_decode(a["q"], a["k"], a["v"], a["n"], a["B"], a["Hq"], a["Hkv"], a["d"], a["n_cap"],
+                                   a["S"], a["sc"], a["out"], kw.get("wsp", wsp), kw.get("ws", ws), None)
+    assert call(q=None) == d.DWKV_ERR_INVALID_ARG
+    assert call(n_cap=4000) == d.DWKV_ERR_INVALID_ARG          # not a multiple of 64
+    assert call(sc=0.0) == d.DWKV_ERR_INVALID_ARG
+    assert call(S=257) == d.DWKV_ERR_INVALID_ARG
+    assert call(ws=ws - 1) == d.DWKV_ERR_WORKSPACE
+    assert call(wsp=ctypes.c_void_p((1 << 43) + 8)) == d.DWKV_ERR_INVALID_ARG
+    cfg = _cfg()
+    h = ctypes.c_void_p()
+    assert L.dwkv_create(ctypes.byref(cfg), ctypes.c_void_p(1 << 40), d.dwkv_arena_bytes(cfg), ctypes.byref(h)) == d.DWKV_OK
+    try:
+        assert L.dwkv_materialize_layer(h, 0, 1, kk, None, 256, None, None) == d.DWKV_ERR_INVALID_ARG
+        assert L.dwkv_materialize_layer(h, 32, 1, kk, kk, 256, None, None) == d.DWKV_ERR_INVALID_ARG
+        assert L.dwkv_materialize_layer(h, 0, 3, kk, kk, 256, None, None) == d.DWKV_ERR_INVALID_ARG
+        assert L.dwkv_materialize_layer(h, 0, 1, kk, kk, 128, None, None) == d.DWKV_ERR_INVALID_ARG   # < max_tokens
+        assert L.dwkv_materialize_layer(h, 0, 1, kk, kk, 200, None, None) == d.DWKV_ERR_INVALID_ARG   # not /64
+    finally:
+        L.dwkv_destroy(h)
+
+
 def test_workspace_scales_with_batch_and_splits():
     a = d.dwkv_workspace_bytes(_cfg(decode_splits=4), 1)
     b = d.dwkv_workspace_bytes(_cfg(decode_splits=8), 1)
