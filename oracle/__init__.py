@@ -202,6 +202,52 @@ def dense_decode(K: np.ndarray, V: np.ndarray, n_tokens, q: np.ndarray, alpha: O
     return out
 
 
+# ------------------------------------------------------------------ probe (Eq. (3))
+def probe_error(cfg, lay: Dict[str, np.ndarray], basisK: np.ndarray, basisV: np.ndarray,
+                K_ref: np.ndarray, V_ref: np.ndarray, n_ref, qs: Sequence[np.ndarray],
+                eps: float = 1e-6, alpha: Optional[float] = None) -> np.ndarray:
+    """The paper's Eq. (3) (§3 Method, attention-output probes) per (sequence,
+    KV head): || Attn(Q, K, V) - Attn(Q, K^, V^) ||_2 / (|| Attn(Q, K, V) ||_2 + eps),
+    where K, V is the higher-fidelity dense fp16 cache (K_ref, V_ref
+    [B][H_kv][n_max][d] token rows, n_ref tokens per sequence), K^, V^ the
+    compressed cache (lay), and Q the recent query vectors qs (each fp16
+    [B][H_q][d]) of the KV head's query heads; the norms run over every
+    query position, query head and channel.  Returns fp64 [B][H_kv]."""
+    B, Hkv = lay["coefK"].shape[:2]
+    gq = cfg.num_q_heads // Hkv
+    num = np.zeros((B, Hkv))
+    den = np.zeros((B, Hkv))
+    for q in qs:
+        oc = decode(cfg, lay, basisK, basisV, q, alpha=alpha)
+        oe = dense_decode(K_ref, V_ref, n_ref, q, alpha=alpha)
+        dd = ((oe - oc) ** 2).reshape(B, Hkv, gq, -1).sum(axis=(2, 3))
+        ee = (oe ** 2).reshape(B, Hkv, gq, -1).sum(axis=(2, 3))
+        num += dd
+        den += ee
+    return np.sqrt(num) / (np.sqrt(den) + eps)
+
+
+def probe_controller(tau: float, below: int, err: float, tol: float, step: float, patience: int,
+                     tau_min: float, tau_max: float):
+    """One probe interval of a depth window's router threshold (§3, the
+    paragraph after Eq. (3)): an error above the window's tolerance lowers
+    tau_m, so more of the window's tokens take higher residual rank; errors
+    below it for `patience` probe intervals in a row raise tau_m, reducing
+    residual storage.  tau moves by `step` in fp32 and stays in [tau_min,
+    tau_max].  Returns (tau, below-tolerance run length)."""
+    t = np.float32(tau)
+    if err > tol:
+        t = np.float32(t - np.float32(step))
+        below = 0
+    else:
+        below += 1
+        if below >= patience:
+            t = np.float32(t + np.float32(step))
+            below = 0
+    t = np.float32(min(max(t, np.float32(tau_min)), np.float32(tau_max)))
+    return float(t), below
+
+
 # ------------------------------------------------------------------ append
 def append_vector(basis: np.ndarray, x: np.ndarray, r: int, s: int, qmax: int,
                   gate: Optional[np.float16] = None):
