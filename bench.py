@@ -49,6 +49,11 @@ def parse_args():
     p.add_argument("--kernel-reps", type=int, default=10)
     p.add_argument("--separate", action="store_true",
                    help="two launches per layer (dwkv_decode_attn, dwkv_append) instead of dwkv_decode_step")
+    p.add_argument("--comparator", choices=["dense", "unfused"], default=None,
+                   help="time a comparator instead of the fused step: 'dense' = flash-decode over a dense fp16 "
+                        "cache of the same shape; 'unfused' = per layer, materialise K^/V^ to HBM, dense "
+                        "flash-decode over it, then the append")
+    p.add_argument("--dense-splits", type=int, default=0, help="dense decode workgroups per KV head (0 = auto)")
     p.add_argument("--copy-probe", action="store_true",
                    help="also run a plain 512 MiB device copy (counter calibration)")
     p.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -314,6 +319,101 @@ def cpu_baseline(cfg, bases, appends, budget_s: float):
     }
 
 
+def _time_graph_steps(step, W: int, K: int, chunk: int):
+    """W eager warm-up steps, then K steps replayed from graphs of `chunk`
+    steps; returns the elapsed milliseconds of the K steps."""
+    import torch
+    for s in range(W):
+        step(s)
+    torch.cuda.synchronize()
+    graphs = []
+    for c0 in range(W, W + K, chunk):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for s in range(c0, min(c0 + chunk, W + K)):
+                step(s)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for g in graphs:
+        g.replay()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end)
+
+
+def _graph_launch_ms(launches, reps: int):
+    """Mean milliseconds of one launch: the launches in one graph, replayed."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        launches()
+    g.replay()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
+        a.record()
+        g.replay()
+        b.record()
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+
+def _dense_splits(args, cfg) -> int:
+    if args.dense_splits > 0:
+        return args.dense_splits
+    return max(1, min(256, 1024 // (cfg.batch * cfg.num_kv_heads)))
+
+
+def run_dense(args, cfg, K: int, W: int):
+    """Flash-decode over a dense fp16 cache of the workload's shape (every
+    layer, the workload's context), the uncompressed baseline."""
+    import torch
+    from compressed_kv_cache_dwkv_amd import dwkv_dense_decode, dwkv_dense_workspace_bytes
+    torch.cuda.set_device(0)
+    L, B, H, Hq, d, n = cfg.num_layers, cfg.batch, cfg.num_kv_heads, cfg.num_q_heads, cfg.head_dim, cfg.n_tokens
+    n_cap = (n + 63) // 64 * 64
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(cfg.seed)
+    Kd = torch.randn((L, B, H, n_cap, d), generator=gen, dtype=torch.float16, device="cuda")
+    Vd = torch.randn((L, B, H, n_cap // 16, d, 16), generator=gen, dtype=torch.float16, device="cuda")
+    q = torch.from_numpy(np.stack([gen_query(cfg, l) for l in range(L)])).cuda()
+    out = torch.empty((L, B, Hq, d), dtype=torch.float32, device="cuda")
+    S = _dense_splits(args, cfg)
+    ws = torch.zeros(dwkv_dense_workspace_bytes(B, Hq, H, d, S), dtype=torch.uint8, device="cuda")
+    n_dev = torch.full((B, H), n, dtype=torch.int32, device="cuda")
+    scale = 1.0 / math.sqrt(d)
+    print(f"bench: dense cache resident ({(Kd.numel() + Vd.numel()) * 2 / 1e9:.2f} GB), splits {S}",
+          file=sys.stderr, flush=True)
+
+    def step(s):
+        for l in range(L):
+            dwkv_dense_decode(q[l], Kd[l], Vd[l], n_dev, out[l], ws, S, scale)
+
+    elapsed_ms = _time_graph_steps(step, W, K, args.chunk)
+    launch_ms = elapsed_ms / (K * L)
+    one_step_ms = _graph_launch_ms(lambda: step(0), args.kernel_reps) / L
+    layer_bytes = B * H * n * d * 2 * 2
+    achieved = layer_bytes / (launch_ms * 1e-3) / 1e9
+    return {
+        "metric": METRIC + " [comparator: dense fp16 cache]",
+        "value": B * K / (elapsed_ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": elapsed_ms / K, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp16 MFMA operands, fp32 accumulate", "data": "synthetic",
+        "config": {"workload": cfg.name, "comparator": "dense", "batch": B, "context": n, "layers": L,
+                   "q_heads": Hq, "kv_heads": H, "head_dim": d, "dense_splits": S,
+                   "storage": "fp16 K rows and fp16 V in 16-token blocks, no compression",
+                   "note": "attention only; the dense cache's append (one 512-byte K and V row per KV head) "
+                           "is not launched"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBPS, "traffic": None, "kernel": "dense_decode_kernel",
+                     "algorithmic_bytes_per_launch": layer_bytes, "mean_launch_us": launch_ms * 1e3,
+                     "launch_time_from": "timed region", "one_step_graph_launch_us": one_step_ms * 1e3},
+        "cpu_baseline": None,
+    }
+
+
 def main():
     args = parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -330,6 +430,9 @@ def main():
     K = args.steps if args.steps is not None else cfg.bench_steps
     W = args.warmup
     L, B, H = cfg.num_layers, cfg.batch, cfg.num_kv_heads
+    if args.comparator == "dense":
+        print(json.dumps(run_dense(args, cfg, K, W)), flush=True)
+        return
 
     # ---- synthetic inputs (host): the layer generators start before the
     #      GPU is touched; each layer is imported as it arrives and dropped
@@ -375,8 +478,24 @@ def main():
     scale = 1.0 / math.sqrt(cfg.head_dim)
     print(f"bench: cache resident ({cache.arena.numel() / 1e9:.2f} GB arena)", file=sys.stderr, flush=True)
 
+    unfused = args.comparator == "unfused"
+    if unfused:
+        from compressed_kv_cache_dwkv_amd import (dwkv_dense_decode, dwkv_dense_workspace_bytes,
+                                                 dwkv_materialize_layer)
+        n_cap = (int(cache.cfg.max_tokens) + 63) // 64 * 64
+        Kd = torch.empty((B, H, n_cap, cfg.head_dim), dtype=torch.float16, device="cuda")
+        Vd = torch.empty((B, H, n_cap // 16, cfg.head_dim, 16), dtype=torch.float16, device="cuda")
+        n_dev = torch.empty((B, H), dtype=torch.int32, device="cuda")
+        S_dense = _dense_splits(args, cfg)
+        ws_dense = torch.zeros(dwkv_dense_workspace_bytes(B, cfg.num_q_heads, H, cfg.head_dim, S_dense),
+                               dtype=torch.uint8, device="cuda")
+
     def layer_step(l, s):
-        if args.separate:
+        if unfused:
+            dwkv_materialize_layer(h, l, Kd, Vd, n_dev)
+            dwkv_dense_decode(q_dev[l], Kd, Vd, n_dev, out_dev[l], ws_dense, S_dense, scale)
+            dwkv_append(h, l, k_dev[s, l], v_dev[s, l], t_dev[s, l])
+        elif args.separate:
             dwkv_decode_attn(h, l, q_dev[l], out_dev[l], ws, scale)
             dwkv_append(h, l, k_dev[s, l], v_dev[s, l], t_dev[s, l])
         else:
@@ -428,10 +547,23 @@ def main():
     layer_bytes = [algorithmic_layer_bytes(cfg, counts[l], None if args.separate else last[l]["tier"])
                    for l in range(L)]
     step_bytes = sum(algorithmic_layer_bytes(cfg, counts[l], last[l]["tier"]) for l in range(L))
+    breakdown = None
+    if unfused:
+        mat_ms = _graph_launch_ms(lambda: [dwkv_materialize_layer(h, l, Kd, Vd, n_dev) for l in range(L)],
+                                  args.kernel_reps) / L
+        dec_ms = _graph_launch_ms(lambda: [dwkv_dense_decode(q_dev[l], Kd, Vd, n_dev, out_dev[l], ws_dense, S_dense,
+                                                             scale) for l in range(L)], args.kernel_reps) / L
+        app_ms = _graph_launch_ms(lambda: [dwkv_append(h, l, k_dev[W + K - 1, l], v_dev[W + K - 1, l],
+                                                       t_dev[W + K - 1, l]) for l in range(L)], 2) / L
+        breakdown = {"materialize_us": mat_ms * 1e3, "dense_decode_us": dec_ms * 1e3, "append_us": app_ms * 1e3,
+                     "dense_splits": S_dense, "note": "per layer, from replays of a graph of one step's launches "
+                                                      "of each kernel (appends add tokens to the cache)"}
     kg = torch.cuda.CUDAGraph()
     with torch.cuda.graph(kg):
         for l in range(L):
-            if args.separate:
+            if unfused:
+                dwkv_dense_decode(q_dev[l], Kd, Vd, n_dev, out_dev[l], ws_dense, S_dense, scale)
+            elif args.separate:
                 dwkv_decode_attn(h, l, q_dev[l], out_dev[l], ws, scale)
             else:
                 layer_step(l, W + K - 1)
@@ -459,12 +591,20 @@ def main():
         mean_launch_ms = graph_launch_ms
         launch_source = "replays of one step's decode launches"
     bytes_per_launch = float(np.mean(layer_bytes))
-    achieved = bytes_per_launch / (mean_launch_ms * 1e-3) / 1e9
+    kernel_name = "decode_kernel"
     traffic = stored_traffic(cfg.name)
+    if unfused:
+        # the dense decode over the materialised layer: its dense bytes
+        mean_launch_ms = breakdown["dense_decode_us"] * 1e-3
+        launch_source = "replays of one step's dense decode launches"
+        bytes_per_launch = float(B * H * (cfg.n_tokens + W + K) * cfg.head_dim * 2 * 2)
+        kernel_name = "dense_decode_kernel"
+        traffic = None
+    achieved = bytes_per_launch / (mean_launch_ms * 1e-3) / 1e9
 
     dense = w.dense_kv_bytes(L, H, cfg.head_dim, cfg.n_tokens + W + K, batch=B)
     res = {
-        "metric": METRIC,
+        "metric": METRIC + (" [comparator: unfused decode]" if unfused else ""),
         "value": tok_s,
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -484,7 +624,8 @@ def main():
             "resid_channels": cfg.resid_channels, "resid_bits": cfg.resid_bits,
             "storage": "fp16 coefficients, uint8 channel indices, packed codes, fp16 scales",
             "graph_replay": bool(graphs), "decode_splits": cache.splits,
-            "launches_per_layer": 2 if args.separate else 1,
+            "launches_per_layer": 3 if unfused else 2 if args.separate else 1,
+            **({"comparator": "unfused"} if unfused else {}),
         },
         "step_GBps": step_bytes / (ms_per_step * 1e-3) / 1e9,
         "step_frac_of_peak": step_bytes / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBPS,
@@ -492,10 +633,11 @@ def main():
             "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
             "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
             "traffic_GBps": None if traffic is None else traffic / (mean_launch_ms * 1e-3) / 1e9,
-            "kernel": "decode_kernel", "algorithmic_bytes_per_launch": bytes_per_launch,
+            "kernel": kernel_name, "algorithmic_bytes_per_launch": bytes_per_launch,
             "mean_launch_us": mean_launch_ms * 1e3, "launch_time_from": launch_source,
             "one_step_graph_launch_us": graph_launch_ms * 1e3,
         },
+        **({"breakdown": breakdown} if breakdown else {}),
         "memory": {
             "compressed_bytes": step_bytes, "dense_fp16_bytes": dense,
             "reduction_vs_fp16": dense / step_bytes,

@@ -133,6 +133,7 @@ int build_layout(const dwkv_config *c, Layout *ly)
     ly->basis_elems = (int64_t)ly->Hkv * ly->R * ly->d;
     ly->off_basis = off;    off = align_up(off + (int64_t)ly->num_groups * 2 * ly->basis_elems * 2, 256);
     ly->off_basisvt = off;  off = align_up(off + (int64_t)ly->num_groups * ly->basis_elems * 2, 256);
+    ly->off_basiskt = off;  off = align_up(off + (int64_t)ly->num_groups * ly->basis_elems * 2, 256);
     ly->off_seg = off;      off = off + heads * ly->head_block;
     // spare tail: the decode kernel's fixed-shape tile loads may read up to
     // a few KiB past the last token of the last head block

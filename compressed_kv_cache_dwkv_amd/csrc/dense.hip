@@ -66,8 +66,101 @@ __device__ __forceinline__ float ld_agent(const float *p)
 }
 
 // ------------------------------------------------------------ dense decode
+// Operands of one 32-token tile in flight (see dense_decode_kernel).
+template <int D>
+struct DTile {
+    half8_t k[2][D / 32];
+    half8_t v[D / 16];
+};
+
+template <int D>
+__device__ __forceinline__ void dense_load(DTile<D> &T, const uint16_t *Kb, const uint16_t *Vb, int tok0, int c16,
+                                           int g)
+{
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+        const int tok = tok0 + 16 * mb + c16;
+#pragma unroll
+        for (int c = 0; c < D / 32; ++c)
+            T.k[mb][c] = *reinterpret_cast<const half8_t *>(Kb + (int64_t)tok * D + 32 * c + 8 * g);
+    }
+    const uint16_t *vb = Vb + ((int64_t)(tok0 / 16) * D) * 16 + 4 * g;
+#pragma unroll
+    for (int cb = 0; cb < D / 16; ++cb) {
+        const half4_t lo = *reinterpret_cast<const half4_t *>(vb + (16 * cb + c16) * 16);
+        const half4_t hi = *reinterpret_cast<const half4_t *>(vb + (D + 16 * cb + c16) * 16);
+        T.v[cb] = cat(lo, hi);
+    }
+}
+
+// One tile: scores on the matrix cores, online softmax (base 2, lazy max),
+// probabilities times V on the matrix cores.  Lane (c16, g) holds head c16's
+// scores of tokens 16 mb + 4 g + j and accumulator rows 4 g + j (heads).
 template <int GQ, int D>
-__global__ __launch_bounds__(kDBlock) void dense_decode_kernel(DenseArgs a)
+__device__ __forceinline__ void dense_tile(DTile<D> &T, const half8_t (&qop)[D / 32], float4_t (&O)[D / 16],
+                                           float &m, float &l, int left, float zs, int c16, int g)
+{
+    constexpr int NC = D / 32, NB = D / 16;
+    // operands of tokens past the context are zeroed (whatever the buffer
+    // holds there must not meet a zero probability)
+    if (left < kDTile) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+            if (16 * mb + c16 >= left) {
+#pragma unroll
+                for (int c = 0; c < NC; ++c) T.k[mb][c] = half8_t{0, 0, 0, 0, 0, 0, 0, 0};
+            }
+#pragma unroll
+        for (int cb = 0; cb < NB; ++cb)
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                if (16 * (i >> 2) + 4 * g + (i & 3) >= left) T.v[cb][i] = (_Float16)0.0f;
+    }
+    float4_t s0 = float4_t{0.0f, 0.0f, 0.0f, 0.0f}, s1 = s0;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        s0 = mma32(T.k[0][c], qop[c], s0);
+        s1 = mma32(T.k[1][c], qop[c], s1);
+    }
+    float z[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        z[j] = 4 * g + j < left ? s0[j] * zs : -INFINITY;
+        z[4 + j] = 16 + 4 * g + j < left ? s1[j] * zs : -INFINITY;
+    }
+    float tm = z[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) tm = fmaxf(tm, z[i]);
+    tm = fmaxf(tm, shfl_xor(tm, 16));
+    tm = fmaxf(tm, shfl_xor(tm, 32));
+    // lazy running max: moved (and the sums rescaled) only when a logit
+    // passes it by more than the lag
+    if (__builtin_amdgcn_ballot_w64(tm > m + kLag)) {
+        const float nm = tm > m + kLag ? tm : m;
+        const float f = m == -INFINITY ? 0.0f : exp2f(m - nm);
+        m = nm;
+        l *= f;
+        // accumulator row 4 g + j is head 4 g + j: its factor from that head's lane
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float fr = __shfl(f, 4 * g + j, kWave);
+#pragma unroll
+            for (int cb = 0; cb < NB; ++cb) O[cb][j] *= fr;
+        }
+    }
+    half8_t P;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const _Float16 p = (_Float16)exp2f(z[i] - m);
+        P[i] = p;
+        l += (float)p;
+    }
+#pragma unroll
+    for (int cb = 0; cb < NB; ++cb) O[cb] = mma32(P, T.v[cb], O[cb]);
+}
+
+template <int GQ, int D>
+__global__ __launch_bounds__(kDBlock, 2) void dense_decode_kernel(DenseArgs a)
 {
     constexpr int NC = D / 32;                 // 32-channel chunks of the scores
     constexpr int NB = D / 16;                 // 16-channel blocks of the output
@@ -99,90 +192,28 @@ __global__ __launch_bounds__(kDBlock) void dense_decode_kernel(DenseArgs a)
     float m = -INFINITY;                      // running max of head c16 (base-2 logits)
     float l = 0.0f;                           // this lane's share of head c16's normaliser
 
-    for (int t = t0 + wave; t < t1; t += kDWaves) {
-        const int tok0 = t * kDTile;
-        // K operand of 16-token block mb: token tok0 + 16 mb + c16, channels
-        // 32 c + 8 g ..; V operand of output block cb: channel 16 cb + c16,
-        // tokens 4 g .. 4 g + 3 of both blocks (the same token order as the
-        // probabilities' operand below)
-        half8_t kop[2][NC];
-        half8_t vop[NB];
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-            const int tok = tok0 + 16 * mb + c16;
-#pragma unroll
-            for (int c = 0; c < NC; ++c) kop[mb][c] = *reinterpret_cast<const half8_t *>(Kb + (int64_t)tok * D + 32 * c + 8 * g);
+    // two-deep pipeline over tiles t0 + wave, + 4, ...: the next tile's
+    // loads are in flight while the current one is computed
+    {
+        DTile<D> TA, TB;
+        int t = t0 + wave;
+        if (t < t1) dense_load<D>(TA, Kb, Vb, t * kDTile, c16, g);
+        while (t < t1) {
+            int tn = t + kDWaves;
+            if (tn < t1) dense_load<D>(TB, Kb, Vb, tn * kDTile, c16, g);
+            dense_tile<GQ, D>(TA, qop, O, m, l, n - t * kDTile, zs, c16, g);
+            t = tn;
+            if (t >= t1) break;
+            tn = t + kDWaves;
+            if (tn < t1) dense_load<D>(TA, Kb, Vb, tn * kDTile, c16, g);
+            dense_tile<GQ, D>(TB, qop, O, m, l, n - t * kDTile, zs, c16, g);
+            t = tn;
         }
-        const uint16_t *vb = Vb + ((int64_t)(tok0 / 16) * D) * 16 + 4 * g;
-#pragma unroll
-        for (int cb = 0; cb < NB; ++cb) {
-            const half4_t lo = *reinterpret_cast<const half4_t *>(vb + (16 * cb + c16) * 16);
-            const half4_t hi = *reinterpret_cast<const half4_t *>(vb + (D + 16 * cb + c16) * 16);
-            vop[cb] = cat(lo, hi);
-        }
-        // tokens of the tile that exist; operands of the others are zeroed
-        // (whatever the buffer holds there must not meet a zero probability)
-        const int left = n - tok0;
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-            if (16 * mb + c16 >= left) {
-#pragma unroll
-                for (int c = 0; c < NC; ++c) kop[mb][c] = half8_t{0, 0, 0, 0, 0, 0, 0, 0};
-            }
-        if (left < kDTile) {
-#pragma unroll
-            for (int cb = 0; cb < NB; ++cb)
-#pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    if (16 * (i >> 2) + 4 * g + (i & 3) >= left) vop[cb][i] = (_Float16)0.0f;
-        }
-        // scores: lane holds tokens 16 mb + 4 g + j of the tile for head c16
-        float4_t s0 = float4_t{0.0f, 0.0f, 0.0f, 0.0f}, s1 = s0;
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            s0 = mma32(kop[0][c], qop[c], s0);
-            s1 = mma32(kop[1][c], qop[c], s1);
-        }
-        float z[8];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            z[j] = 4 * g + j < left ? s0[j] * zs : -INFINITY;
-            z[4 + j] = 16 + 4 * g + j < left ? s1[j] * zs : -INFINITY;
-        }
-        float tm = z[0];
-#pragma unroll
-        for (int i = 1; i < 8; ++i) tm = fmaxf(tm, z[i]);
-        tm = fmaxf(tm, shfl_xor(tm, 16));
-        tm = fmaxf(tm, shfl_xor(tm, 32));
-        // lazy running max: moved (and the sums rescaled) only when a logit
-        // passes it by more than the lag
-        if (__builtin_amdgcn_ballot_w64(tm > m + kLag)) {
-            const float nm = tm > m + kLag ? tm : m;
-            const float f = m == -INFINITY ? 0.0f : exp2f(m - nm);
-            m = nm;
-            l *= f;
-            // accumulator row 4 g + j is head 4 g + j: its factor from that head's lane
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float fr = __shfl(f, 4 * g + j, kWave);
-#pragma unroll
-                for (int cb = 0; cb < NB; ++cb) O[cb][j] *= fr;
-            }
-        }
-        half8_t P;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const _Float16 p = (_Float16)exp2f(z[i] - m);
-            P[i] = p;
-            l += (float)p;
-        }
-#pragma unroll
-        for (int cb = 0; cb < NB; ++cb) O[cb] = mma32(P, vop[cb], O[cb]);
     }
 
     // ---- this workgroup's waves merged through LDS
     __shared__ float s_m[kDWaves][GQ], s_l[kDWaves][GQ];
-    __shared__ float s_o[kDWaves][GQ][D];
+    __shared__ __attribute__((aligned(16))) float s_o[kDWaves][GQ][D];
     __shared__ int s_last;
     l += shfl_xor(l, 16);
     l += shfl_xor(l, 32);
@@ -231,19 +262,48 @@ __global__ __launch_bounds__(kDBlock) void dense_decode_kernel(DenseArgs a)
     }
     __syncthreads();
     if (!s_last) return;
+    // every split's maxima and normalisers into LDS at once, then the
+    // weights 2^(m_s - M) per head (wave w reduces heads w, w + 4)
+    __shared__ float s_w[GQ][kMaxSplits];              // maxima, then weights
+    __shared__ float s_pl[GQ][kMaxSplits];             // normalisers
+    __shared__ float s_L[GQ];
+    for (int i = tid; i < GQ * S; i += kDBlock) {
+        const int hd = i / S, sp = i % S;
+        const int64_t ml = (((int64_t)b * a.Hkv + h) * S + sp) * kMlStride + hd;
+        s_w[hd][sp] = ld_agent(pm + ml);
+        s_pl[hd][sp] = ld_agent(pm + ml + kMlNorm);
+    }
+    __syncthreads();
+    for (int hd = wave; hd < GQ; hd += kDWaves) {
+        float M = -INFINITY;
+        for (int sp = lane; sp < S; sp += kWave) M = fmaxf(M, s_w[hd][sp]);
+        M = wave_max(M);
+        float L = 0.0f;
+        for (int sp = lane; sp < S; sp += kWave) {
+            const float wgt = M == -INFINITY ? 0.0f : exp2f(s_w[hd][sp] - M);
+            s_w[hd][sp] = wgt;
+            L += wgt * s_pl[hd][sp];
+        }
+        L = wave_sum(L);
+        if (lane == 0) s_L[hd] = L;
+    }
+    __syncthreads();
+    // outputs: each thread one channel of one head, its splits' partials
+    // requested eight at a time
     for (int e = tid; e < GQ * D; e += kDBlock) {
         const int hd = e / D, ch = e % D;
-        const int64_t ml0 = (((int64_t)b * a.Hkv + h) * S) * kMlStride + hd;
-        float M = -INFINITY;
-        for (int sp = 0; sp < S; ++sp) M = fmaxf(M, ld_agent(pm + ml0 + (int64_t)sp * kMlStride));
-        float o = 0.0f, L = 0.0f;
         const float *pb = po + ((int64_t)b * a.Hq + h * GQ + hd) * S * D + ch;
-        for (int sp = 0; sp < S; ++sp) {
-            const float ms = ld_agent(pm + ml0 + (int64_t)sp * kMlStride);
-            const float f = M == -INFINITY ? 0.0f : exp2f(ms - M);
-            o += f * ld_agent(pb + (int64_t)sp * D);
-            L += f * ld_agent(pm + ml0 + (int64_t)sp * kMlStride + kMlNorm);
+        float o = 0.0f;
+        int sp = 0;
+        for (; sp + 8 <= S; sp += 8) {
+            float x[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) x[u] = ld_agent(pb + (int64_t)(sp + u) * D);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) o += s_w[hd][sp + u] * x[u];
         }
+        for (; sp < S; ++sp) o += s_w[hd][sp] * ld_agent(pb + (int64_t)sp * D);
+        const float L = s_L[hd];
         a.out[((int64_t)b * a.Hq + h * GQ + hd) * D + ch] = L > 0.0f ? o / L : 0.0f;
     }
     if (tid == 0)
@@ -254,9 +314,10 @@ __global__ __launch_bounds__(kDBlock) void dense_decode_kernel(DenseArgs a)
 // --------------------------------------------------------- materialisation
 // One workgroup per 64 positions of one (sequence, KV head): each position's
 // (tier, slot) from the position map, its coefficients gathered into LDS,
-// the basis products on the matrix cores (coefficients times the transposed
-// basis, 16 tokens x 16 channels per product, fp32 sums of exact fp16
-// products), the residual channels added in fp32, one rounding to fp16.
+// the basis products on the matrix cores (coefficients times the arena's
+// transposed basis, 16 tokens x 16 channels per product, fp32 sums of
+// exact fp16 products), the residual channels added in fp32, one rounding
+// to fp16.
 constexpr int kMTok = 64;
 constexpr int kMBlock = 256;
 
@@ -265,14 +326,13 @@ __global__ __launch_bounds__(kMBlock) void materialize_kernel(Layout ly, uint8_t
                                                               uint16_t *kout, uint16_t *vout, int64_t n_cap,
                                                               int32_t *n_out)
 {
-    constexpr int BS = RM + 8;                 // fp16 per transposed-basis row (padded)
     constexpr int CS = RM + 8;                 // fp16 per coefficient row
     constexpr int OS = D + 4;                  // fp32 per output row
-    __shared__ __attribute__((aligned(16))) uint16_t s_bt[D * BS];      // basis^T [channel][rank]
     __shared__ __attribute__((aligned(16))) uint16_t s_c[kMTok * CS];    // coefficients [token][rank]
     __shared__ __attribute__((aligned(16))) float s_out[kMTok * OS];     // reconstruction [token][channel]
     __shared__ int s_tier[kMTok], s_slot[kMTok];
-    const int p0 = blockIdx.x * kMTok, h = blockIdx.y, b = blockIdx.z;
+    const int64_t p0 = (int64_t)blockIdx.x * kMTok;
+    const int h = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
     const int c16 = lane & 15, g = lane >> 4;
     const int32_t *cnt = counts_ptr(ly, arena, layer, b, h);
@@ -281,49 +341,61 @@ __global__ __launch_bounds__(kMBlock) void materialize_kernel(Layout ly, uint8_t
     if (p0 == 0 && tid == 0 && n_out) n_out[b * ly.Hkv + h] = n;
     if (p0 >= n) return;
     const int32_t *pm = posmap_ptr(ly, arena, layer, b, h);
+    const uint8_t *blk = head_block_ptr(ly, arena, layer, b, h);
+    const int R = ly.R, m = layer / ly.G;
     if (tid < kMTok) {
-        const int p = p0 + tid;
+        const int64_t p = p0 + tid;
         const int e = p < n ? pm[p] : -1;
         s_tier[tid] = e < 0 ? -1 : (e >> 28);
         s_slot[tid] = e < 0 ? 0 : (e & 0x0FFFFFFF);
     }
-    const uint8_t *blk = head_block_ptr(ly, arena, layer, b, h);
-    const int R = ly.R;
     for (int z = 0; z < 2; ++z) {
         __syncthreads();
-        // transposed basis of this Z (zero past R)
-        const uint16_t *Bz = basis_ptr(ly, arena, layer / ly.G, z, h);
-        for (int e = tid; e < RM * D; e += kMBlock) {
-            const int i = e / D, j = e % D;
-            s_bt[j * BS + i] = i < R ? Bz[(int64_t)i * D + j] : (uint16_t)0;
-        }
-        // coefficients of the 64 positions (zero past each token's rank)
-        for (int e = tid; e < kMTok * RM; e += kMBlock) {
-            const int t = e / RM, i = e % RM;
-            const int k = s_tier[t];
-            uint16_t c = 0;
-            if (k >= 0 && k < ly.T) {
-                const int r = ly.rank[k];
-                const int64_t slot = s_slot[t];
-                if (i < r) {
-                    const uint16_t *src = reinterpret_cast<const uint16_t *>(blk + (z ? ly.f_coefV[k] : ly.f_coefK[k]));
-                    c = z ? src[coefV_index(r, slot, i)] : src[slot * r + i];
+        // coefficients of the 64 positions (zero past each token's rank):
+        // K rows in 4-element pieces, V (16-token blocks) element by element
+        if (z == 0) {
+            for (int e = tid; e < kMTok * (RM / 4); e += kMBlock) {
+                const int t = e / (RM / 4), i4 = 4 * (e % (RM / 4));
+                const int k = s_tier[t];
+                uint2 c = make_uint2(0u, 0u);
+                if (k >= 0 && k < ly.T && i4 < ly.rank[k]) {
+                    const int r = ly.rank[k];
+                    const uint16_t *src = reinterpret_cast<const uint16_t *>(blk + ly.f_coefK[k]);
+                    c = *reinterpret_cast<const uint2 *>(src + (int64_t)s_slot[t] * r + i4);
                 }
+                *reinterpret_cast<uint2 *>(&s_c[t * CS + i4]) = c;
             }
-            s_c[t * CS + i] = c;
+        } else {
+            for (int e = tid; e < kMTok * RM; e += kMBlock) {
+                const int t = e / RM, i = e % RM;
+                const int k = s_tier[t];
+                uint16_t c = 0;
+                if (k >= 0 && k < ly.T && i < ly.rank[k]) {
+                    const uint16_t *src = reinterpret_cast<const uint16_t *>(blk + ly.f_coefV[k]);
+                    c = src[coefV_index(ly.rank[k], s_slot[t], i)];
+                }
+                s_c[t * CS + i] = c;
+            }
         }
         __syncthreads();
-        // wave w: tokens 16 w .. 16 w + 15, every 16-channel block
+        // wave w: tokens 16 w .. 16 w + 15, every 16-channel block; the B
+        // operand (8 ranks of one channel) straight from the transposed
+        // basis, in 4-rank pieces (zero past R)
         {
+            const uint16_t *bt = z ? basis_vt_ptr(ly, arena, m, h) : basis_kt_ptr(ly, arena, m, h);
             const int tok = 16 * wave + c16;
-#pragma unroll
+#pragma unroll 2
             for (int cb = 0; cb < D / 16; ++cb) {
                 float4_t acc = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+                const uint16_t *row = bt + (int64_t)(16 * cb + c16) * R;
 #pragma unroll
                 for (int k0 = 0; k0 < RM; k0 += 32) {
                     const half8_t av = *reinterpret_cast<const half8_t *>(&s_c[tok * CS + k0 + 8 * g]);
-                    const half8_t bv = *reinterpret_cast<const half8_t *>(&s_bt[(16 * cb + c16) * BS + k0 + 8 * g]);
-                    acc = mma32(av, bv, acc);
+                    const int i0 = k0 + 8 * g;
+                    half4_t lo = half4_t{0, 0, 0, 0}, hi = half4_t{0, 0, 0, 0};
+                    if (i0 < R) lo = *reinterpret_cast<const half4_t *>(row + i0);
+                    if (i0 + 4 < R) hi = *reinterpret_cast<const half4_t *>(row + i0 + 4);
+                    acc = mma32(av, cat(lo, hi), acc);
                 }
 #pragma unroll
                 for (int j = 0; j < 4; ++j) s_out[(16 * wave + 4 * g + j) * OS + 16 * cb + c16] = acc[j];
@@ -334,13 +406,14 @@ __global__ __launch_bounds__(kMBlock) void materialize_kernel(Layout ly, uint8_t
         if (tid < kMTok) {
             const int k = s_tier[tid];
             if (k >= 0 && k < ly.T) {
-                const int s = ly.resid[k];
+                const int sres = ly.resid[k];
                 const int64_t slot = s_slot[tid];
-                if (s > 0) {
+                if (sres > 0) {
                     const uint8_t *idx = blk + (z ? ly.f_idxV[k] : ly.f_idxK[k]) + slot * ly.istride[k];
                     const uint8_t *val = blk + (z ? ly.f_valV[k] : ly.f_valK[k]) + slot * ly.vstride[k];
-                    const float sc = h2f(reinterpret_cast<const uint16_t *>(blk + (z ? ly.f_scaleV[k] : ly.f_scaleK[k]))[slot]);
-                    for (int u = 0; u < s; ++u) {
+                    const float sc =
+                        h2f(reinterpret_cast<const uint16_t *>(blk + (z ? ly.f_scaleV[k] : ly.f_scaleK[k]))[slot]);
+                    for (int u = 0; u < sres; ++u) {
                         const int j = idx[u] < D ? idx[u] : D - 1;
                         s_out[tid * OS + j] += sc * (float)unpack_code(val, u, ly.bits);
                     }
@@ -348,25 +421,32 @@ __global__ __launch_bounds__(kMBlock) void materialize_kernel(Layout ly, uint8_t
             }
         }
         __syncthreads();
-        // fp16 out: K rows, V 16-token blocks (channel-major); positions past
-        // the context are written as zeros
+        // fp16 out, 8 values per 16-byte store: K rows; V 16-token blocks
+        // (8 tokens of one channel per store).  Positions past the context
+        // within these 64 are written as zeros.
         uint16_t *dst = (z ? vout : kout) + ((int64_t)b * ly.Hkv + h) * n_cap * D;
-        for (int e = tid; e < kMTok * D; e += kMBlock) {
-            int t, j;
+        for (int e = tid; e < kMTok * D / 8; e += kMBlock) {
+            uint16_t v8[8];
+            int64_t off;
             if (z == 0) {
-                t = e / D;
-                j = e % D;
+                const int t = e / (D / 8), j8 = 8 * (e % (D / 8));
+#pragma unroll
+                for (int u = 0; u < 8; ++u) v8[u] = p0 + t < n ? f2h(s_out[t * OS + j8 + u]) : (uint16_t)0;
+                off = (p0 + t) * D + j8;
             } else {
-                // element order of the blocked layout: [block][channel][token]
-                const int blk16 = e / (16 * D), rem = e % (16 * D);
-                j = rem / 16;
-                t = 16 * blk16 + rem % 16;
+                const int blk16 = e / (2 * D), rem = e % (2 * D);
+                const int ch = rem / 2, t8 = 16 * blk16 + 8 * (rem % 2);
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    v8[u] = p0 + t8 + u < n ? f2h(s_out[(t8 + u) * OS + ch]) : (uint16_t)0;
+                off = ((p0 / 16 + blk16) * D + ch) * 16 + 8 * (rem % 2);
             }
-            const uint16_t v = p0 + t < n ? f2h(s_out[t * OS + j]) : (uint16_t)0;
-            if (z == 0)
-                dst[(int64_t)(p0 + t) * D + j] = v;
-            else
-                dst[((int64_t)(p0 + t) / 16 * D + j) * 16 + (p0 + t) % 16] = v;
+            uint4 w;
+            w.x = v8[0] | ((uint32_t)v8[1] << 16);
+            w.y = v8[2] | ((uint32_t)v8[3] << 16);
+            w.z = v8[4] | ((uint32_t)v8[5] << 16);
+            w.w = v8[6] | ((uint32_t)v8[7] << 16);
+            *reinterpret_cast<uint4 *>(dst + off) = w;
         }
     }
 }

@@ -199,6 +199,7 @@ __global__ void transpose_basis_kernel(Layout ly, uint8_t *arena, int m)
         const int64_t rem = e - (int64_t)h * ly.R * ly.d;
         const int j = (int)(rem / ly.R), i = (int)(rem % ly.R);
         basis_vt_ptr(ly, arena, m, h)[(int64_t)j * ly.R + i] = basis_ptr(ly, arena, m, 1, h)[(int64_t)i * ly.d + j];
+        basis_kt_ptr(ly, arena, m, h)[(int64_t)j * ly.R + i] = basis_ptr(ly, arena, m, 0, h)[(int64_t)i * ly.d + j];
     }
 }
 

@@ -74,7 +74,7 @@ hipError_t launch_export(const Layout &ly, uint8_t *arena, int layer,
                          const dwkv_logical_layer &dst, int32_t *counts, int32_t *slots,
                          int batch, hipStream_t stream);
 
-// Writes the transposed V basis of window m (basis_vt_ptr) from the arena's copy.
+// Writes the transposed bases of window m (basis_vt_ptr, basis_kt_ptr) from the arena's copies.
 hipError_t launch_transpose_basis(const Layout &ly, uint8_t *arena, int m, hipStream_t stream);
 
 hipError_t launch_fill_u32(uint32_t *p, uint32_t value, int64_t count, hipStream_t stream);

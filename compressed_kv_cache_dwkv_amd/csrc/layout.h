@@ -70,7 +70,7 @@ struct Layout {
     double inv_cblk[kMaxTiers];  // 1 / (16 * cost): reciprocal of a 16-token block's cost
     int64_t cap[kMaxTiers];
     int64_t max_tokens;
-    int64_t off_err, off_counts, off_posmap, off_basis, off_basisvt, off_seg;
+    int64_t off_err, off_counts, off_posmap, off_basis, off_basisvt, off_basiskt, off_seg;
     int64_t basis_elems;         // Hkv * R * d  (one Z of one window)
     int64_t head_block;          // bytes of one (layer, b, h) block
     int64_t f_coefK[kMaxTiers], f_coefV[kMaxTiers];
@@ -118,6 +118,14 @@ DWKV_HD uint16_t *basis_ptr(const Layout &ly, uint8_t *arena, int m, int z, int 
 DWKV_HD uint16_t *basis_vt_ptr(const Layout &ly, uint8_t *arena, int m, int h)
 {
     return reinterpret_cast<uint16_t *>(arena + ly.off_basisvt) + (int64_t)m * ly.basis_elems +
+           (int64_t)h * ly.R * ly.d;
+}
+
+// Transposed K basis of window m, KV head h: d rows of R fp16 (the
+// explicit reconstruction's matrix-core operand).
+DWKV_HD uint16_t *basis_kt_ptr(const Layout &ly, uint8_t *arena, int m, int h)
+{
+    return reinterpret_cast<uint16_t *>(arena + ly.off_basiskt) + (int64_t)m * ly.basis_elems +
            (int64_t)h * ly.R * ly.d;
 }
 

@@ -65,7 +65,7 @@ def test_arena_holds_every_algorithmic_byte_with_small_overhead():
     total = d.dwkv_arena_bytes(cfg)
     per_head = sum(k * w.compressed_bytes_per_token(r, 8, 4) for k, r in zip(cap, c.tier_rank))
     heads = 32 * 8
-    bases = 8 * 3 * 8 * 64 * 128 * 2       # K and V bases, and a transposed copy of V
+    bases = 8 * 4 * 8 * 64 * 128 * 2       # K and V bases, and transposed copies of both
     posmap = heads * 70000 * 4
     assert total >= heads * per_head + bases + posmap
     assert total <= heads * per_head * 1.001 + bases + posmap + heads * 4 * 4 + 65536
