@@ -92,6 +92,10 @@ _SIGS = {
     "dwkv_dense_workspace_bytes": [_I, _I, _I, _I, _I, ctypes.POINTER(ctypes.c_size_t)],
     "dwkv_dense_decode": [_P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_int64, _I, ctypes.c_float, _P, _P,
                           ctypes.c_size_t, _P],
+    "dwkv_probe_workspace_bytes": [ctypes.POINTER(dwkv_config), _I, _I, _I, ctypes.POINTER(ctypes.c_size_t)],
+    "dwkv_probe_error": [_P, _I, _P, _I, _I, _P, _P, _P, ctypes.c_int64, _I, ctypes.c_float, ctypes.c_float, _P, _P,
+                         ctypes.c_size_t, _P],
+    "dwkv_probe_update": [_P, _P, _I, _P, ctypes.c_float, ctypes.c_float, _I, ctypes.c_float, ctypes.c_float],
     "dwkv_check_errors": [_P, _P, ctypes.POINTER(ctypes.c_uint32)],
     "dwkv_clear_errors": [_P, _P],
 }
@@ -359,6 +363,43 @@ def dwkv_dense_decode(q, k, v, n_tokens, out, workspace, splits: int, softmax_sc
                                   splits, float(softmax_scale), _ptr(out, torch.float32, (B, Hq, d), name="out"),
                                   _ptr(workspace, name="workspace"), ws, _stream(stream)),
            "dwkv_dense_decode")
+
+
+def dwkv_probe_workspace_bytes(cfg: dwkv_config, batch: int, n_queries: int, dense_splits: int) -> int:
+    n = ctypes.c_size_t()
+    _check(_lib.dwkv_probe_workspace_bytes(ctypes.byref(cfg), batch, n_queries, dense_splits, ctypes.byref(n)),
+           "dwkv_probe_workspace_bytes")
+    return n.value
+
+
+def dwkv_probe_error(h, layer: int, q, k_ref, v_ref, n_ref, err, workspace, dense_splits: int,
+                     softmax_scale: Optional[float] = None, eps: float = 1e-6, stream=None) -> None:
+    """q fp16 [n_queries][B][H_q][d]; k_ref, v_ref, n_ref as dwkv_dense_decode;
+    err fp32 [B][H_kv]."""
+    import torch
+    nq, B, Hq, d = q.shape
+    _, Hkv, n_cap, _ = k_ref.shape
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    ws = workspace.numel() * workspace.element_size()
+    _check(_lib.dwkv_probe_error(h, layer, _ptr(q, torch.float16, name="q"), nq, B,
+                                 _ptr(k_ref, torch.float16, name="k_ref"),
+                                 _ptr(v_ref, torch.float16, (B, Hkv, n_cap // 16, d, 16), name="v_ref"),
+                                 _ptr(n_ref, torch.int32, (B, Hkv), name="n_ref"), n_cap, dense_splits,
+                                 float(softmax_scale), float(eps), _ptr(err, torch.float32, (B, Hkv), name="err"),
+                                 _ptr(workspace, name="workspace"), ws, _stream(stream)),
+           "dwkv_probe_error")
+
+
+def dwkv_probe_update(tau: np.ndarray, below: np.ndarray, err: np.ndarray, tol: float, step: float,
+                      patience: int, tau_min: float, tau_max: float) -> None:
+    """Host arrays, updated in place: tau float32 [W], below int32 [W], err float32 [W]."""
+    assert tau.dtype == np.float32 and below.dtype == np.int32 and err.dtype == np.float32
+    assert tau.flags["C_CONTIGUOUS"] and below.flags["C_CONTIGUOUS"] and err.flags["C_CONTIGUOUS"]
+    _check(_lib.dwkv_probe_update(tau.ctypes.data_as(ctypes.c_void_p), below.ctypes.data_as(ctypes.c_void_p),
+                                  tau.size, np.ascontiguousarray(err).ctypes.data_as(ctypes.c_void_p),
+                                  float(tol), float(step), int(patience), float(tau_min), float(tau_max)),
+           "dwkv_probe_update")
 
 
 def dwkv_check_errors(h, stream=None) -> int:

@@ -526,6 +526,101 @@ int dwkv_dense_decode(const void *q, const void *k, const void *v, const int32_t
     return hip_status(dwkv::launch_dense_decode(a, splits, static_cast<hipStream_t>(stream)));
 }
 
+// Probe workspace: the compressed decode's, the dense decode's, then the
+// two attention outputs of every probed query.
+static size_t probe_ws_bytes(const Layout &ly, int splits, int batch, int n_queries, int dense_splits)
+{
+    const size_t a = dwkv::align_up((int64_t)dwkv::decode_workspace_bytes(ly, batch, splits), 256);
+    const size_t b = dwkv::align_up((int64_t)dense_ws_bytes(batch, ly.Hq, ly.Hkv, ly.d, dense_splits), 256);
+    const size_t o = dwkv::align_up((int64_t)n_queries * batch * ly.Hq * ly.d * 4, 256);
+    return a + b + 2 * o;
+}
+
+int dwkv_probe_workspace_bytes(const dwkv_config *cfg, int batch, int n_queries, int dense_splits, size_t *bytes)
+{
+    if (!cfg || !bytes) return DWKV_ERR_INVALID_ARG;
+    Layout ly;
+    int rc = dwkv::build_layout(cfg, &ly);
+    if (rc != DWKV_OK) return rc;
+    if (batch <= 0 || batch > ly.Bmax || n_queries <= 0 || dense_splits < 1 || dense_splits > dwkv::kMaxSplits)
+        return DWKV_ERR_INVALID_ARG;
+    *bytes = probe_ws_bytes(ly, dwkv::plan_splits(*cfg, ly), batch, n_queries, dense_splits);
+    return DWKV_OK;
+}
+
+int dwkv_probe_error(dwkv_handle *h, int layer, const void *q, int n_queries, int batch, const void *k_ref,
+                     const void *v_ref, const int32_t *n_ref, int64_t n_cap, int dense_splits, float softmax_scale,
+                     float eps, float *err, void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!valid_handle(h) || !q || !k_ref || !v_ref || !n_ref || !err || !workspace) return DWKV_ERR_INVALID_ARG;
+    const Layout &ly = h->ly;
+    if (layer < 0 || layer >= ly.L || batch <= 0 || batch > ly.Bmax || n_queries <= 0) return DWKV_ERR_INVALID_ARG;
+    if (dense_splits < 1 || dense_splits > dwkv::kMaxSplits) return DWKV_ERR_INVALID_ARG;
+    if (n_cap <= 0 || n_cap % 64 != 0 || n_cap >= (int64_t(1) << 31)) return DWKV_ERR_INVALID_ARG;
+    if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale) || !(eps >= 0.0f)) return DWKV_ERR_INVALID_ARG;
+    if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return DWKV_ERR_INVALID_ARG;
+    if (workspace_bytes < probe_ws_bytes(ly, h->splits, batch, n_queries, dense_splits)) return DWKV_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint8_t *p = static_cast<uint8_t *>(workspace);
+    const dwkv::DecodeWorkspace wc = dwkv::carve_workspace(ly, p, batch, h->splits);
+    p += dwkv::align_up((int64_t)dwkv::decode_workspace_bytes(ly, batch, h->splits), 256);
+    uint8_t *pd = p;
+    p += dwkv::align_up((int64_t)dense_ws_bytes(batch, ly.Hq, ly.Hkv, ly.d, dense_splits), 256);
+    const int64_t out_elems = (int64_t)batch * ly.Hq * ly.d;
+    float *o_cmp = reinterpret_cast<float *>(p);
+    float *o_ref = reinterpret_cast<float *>(p + dwkv::align_up((int64_t)n_queries * out_elems * 4, 256));
+    dwkv::DenseArgs a;
+    a.ws.arrive = reinterpret_cast<uint32_t *>(pd);
+    pd += dwkv::align_up((int64_t)batch * ly.Hkv * dwkv::kArriveStride * 4, 256);
+    a.ws.pm = reinterpret_cast<float *>(pd);
+    a.ws.pl = a.ws.pm + dwkv::kMlNorm;
+    pd += dwkv::align_up((int64_t)batch * ly.Hkv * dense_splits * dwkv::kMlStride * 4, 256);
+    a.ws.po = reinterpret_cast<float *>(pd);
+    a.k = static_cast<const uint16_t *>(k_ref);
+    a.v = static_cast<const uint16_t *>(v_ref);
+    a.n = n_ref;
+    a.B = batch;
+    a.Hq = ly.Hq;
+    a.Hkv = ly.Hkv;
+    a.d = ly.d;
+    a.n_cap = n_cap;
+    a.scale = softmax_scale;
+    const uint16_t *qq = static_cast<const uint16_t *>(q);
+    for (int i = 0; i < n_queries; ++i) {
+        const uint16_t *qi = qq + i * out_elems;
+        hipError_t e = dwkv::launch_decode(ly, h->arena, layer, qi, batch, softmax_scale, o_cmp + i * out_elems, wc,
+                                           h->splits, nullptr, s);
+        if (e != hipSuccess) return hip_status(e);
+        a.q = qi;
+        a.out = o_ref + i * out_elems;
+        e = dwkv::launch_dense_decode(a, dense_splits, s);
+        if (e != hipSuccess) return hip_status(e);
+    }
+    return hip_status(dwkv::launch_probe_error(o_ref, o_cmp, n_queries, batch, ly.Hq, ly.Hkv, ly.d, eps, err, s));
+}
+
+int dwkv_probe_update(float *tau, int32_t *below, int n_windows, const float *err, float tol, float step,
+                      int patience, float tau_min, float tau_max)
+{
+    if (!tau || !below || !err || n_windows <= 0 || patience <= 0 || !(tau_min <= tau_max) || !(step >= 0.0f))
+        return DWKV_ERR_INVALID_ARG;
+    for (int m = 0; m < n_windows; ++m) {
+        float t = tau[m];
+        if (err[m] > tol) {
+            t = t - step;
+            below[m] = 0;
+        } else {
+            below[m] += 1;
+            if (below[m] >= patience) {
+                t = t + step;
+                below[m] = 0;
+            }
+        }
+        tau[m] = t < tau_min ? tau_min : (t > tau_max ? tau_max : t);
+    }
+    return DWKV_OK;
+}
+
 int dwkv_append(dwkv_handle *h, int layer, const void *k, const void *v, const void *tier,
                 const void *gateK, const void *gateV, int batch, void *stream)
 {

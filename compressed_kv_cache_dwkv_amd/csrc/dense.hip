@@ -451,6 +451,43 @@ __global__ __launch_bounds__(kMBlock) void materialize_kernel(Layout ly, uint8_t
     }
 }
 
+// Eq. (3) of the paper (§3, attention-output probes): per (sequence, KV
+// head), || o_ref - o_cmp ||_2 / (|| o_ref ||_2 + eps) over every probed query
+// position, query head of the group and channel.  o_ref, o_cmp: fp32
+// [nq][B][Hq][d].  One workgroup per (KV head, sequence), fp32 sums.
+constexpr int kPBlock = 256;
+__global__ __launch_bounds__(kPBlock) void probe_error_kernel(const float *o_ref, const float *o_cmp, int nq, int B,
+                                                              int Hq, int Hkv, int d, float eps, float *err)
+{
+    const int h = blockIdx.x, b = blockIdx.y;
+    const int gq = Hq / Hkv, per_q = gq * d;
+    float num = 0.0f, den = 0.0f;
+    for (int i = 0; i < nq; ++i) {
+        const int64_t base = (((int64_t)i * B + b) * Hq + (int64_t)h * gq) * d;
+        for (int e = threadIdx.x; e < per_q; e += kPBlock) {
+            const float r = o_ref[base + e], c = o_cmp[base + e];
+            num += (r - c) * (r - c);
+            den += r * r;
+        }
+    }
+    __shared__ float s_n[kPBlock / kWave], s_d[kPBlock / kWave];
+    num = wave_sum(num);
+    den = wave_sum(den);
+    if (lane_id() == 0) {
+        s_n[threadIdx.x / kWave] = num;
+        s_d[threadIdx.x / kWave] = den;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float tn = 0.0f, td = 0.0f;
+        for (int w = 0; w < kPBlock / kWave; ++w) {
+            tn += s_n[w];
+            td += s_d[w];
+        }
+        err[b * Hkv + h] = sqrtf(tn) / (sqrtf(td) + eps);
+    }
+}
+
 template <int GQ, int D>
 hipError_t launch_dense_gq(const DenseArgs &a, int splits, hipStream_t stream)
 {
@@ -478,6 +515,15 @@ hipError_t launch_dense_decode(const DenseArgs &a, int splits, hipStream_t strea
     if (a.d == 64) return launch_dense_d<64>(a, splits, stream);
     if (a.d == 128) return launch_dense_d<128>(a, splits, stream);
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_probe_error(const float *o_ref, const float *o_cmp, int nq, int B, int Hq, int Hkv, int d, float eps,
+                              float *err, hipStream_t stream)
+{
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(probe_error_kernel, dim3(Hkv, B), dim3(kPBlock), 0, stream, o_ref, o_cmp, nq, B, Hq, Hkv, d,
+                       eps, err);
+    return hipGetLastError();
 }
 
 hipError_t launch_materialize(const Layout &ly, uint8_t *arena, int layer, int batch, uint16_t *kout,

@@ -62,6 +62,12 @@ hipError_t launch_dense_decode(const DenseArgs &a, int splits, hipStream_t strea
 hipError_t launch_materialize(const Layout &ly, uint8_t *arena, int layer, int batch, uint16_t *kout,
                               uint16_t *vout, int64_t n_cap, int32_t *n_out, hipStream_t stream);
 
+// Eq. (3) relative L2 error per (sequence, KV head) from the reference and
+// compressed attention outputs o_ref, o_cmp (fp32 [nq][B][Hq][d]) into err
+// (fp32 [B][Hkv]).
+hipError_t launch_probe_error(const float *o_ref, const float *o_cmp, int nq, int B, int Hq, int Hkv, int d, float eps,
+                              float *err, hipStream_t stream);
+
 hipError_t launch_append(const Layout &ly, uint8_t *arena, int layer, const void *k,
                          const void *v, const void *tier, const void *gateK, const void *gateV,
                          int batch, hipStream_t stream);

@@ -298,6 +298,44 @@ int dwkv_dense_decode(const void *q, const void *k, const void *v, const int32_t
                       int num_q_heads, int num_kv_heads, int head_dim, int64_t n_cap, int splits,
                       float softmax_scale, float *out, void *workspace, size_t workspace_bytes, void *stream);
 
+/* Device workspace of dwkv_probe_error for batch sequences and n_queries
+ * probed query positions (host only).  Zero-fill it once before its first
+ * use; every call leaves it ready for the next. */
+int dwkv_probe_workspace_bytes(const dwkv_config *cfg, int batch, int n_queries, int dense_splits, size_t *bytes);
+
+/*
+ * The attention-output probe of the paper's §3 (Eq. (3)): for each
+ * (sequence b, KV head h) of `layer`,
+ *   err[b][h] = || Attn(Q, K, V) - Attn(Q, K^, V^) ||_2 / (|| Attn(Q, K, V) ||_2 + eps)
+ * where K^, V^ is the compressed cache (dwkv_decode_attn over it), K, V a
+ * higher-fidelity dense fp16 copy of the same tokens (dwkv_dense_decode over
+ * it) and Q the n_queries recent query vectors; the norms run over every
+ * query position, every query head of the KV head and every channel.
+ *   q: device fp16 [n_queries][batch][num_q_heads][head_dim]
+ *   k_ref, v_ref, n_ref, n_cap, dense_splits: the dense cache as for
+ *          dwkv_dense_decode
+ *   err: device fp32 [batch][num_kv_heads]
+ * The reference cache is the caller's: the paper materialises it
+ * temporarily for the probed window.  Which heads and positions to probe,
+ * and how often, is the caller's schedule.
+ */
+int dwkv_probe_error(dwkv_handle *h, int layer, const void *q, int n_queries, int batch, const void *k_ref,
+                     const void *v_ref, const int32_t *n_ref, int64_t n_cap, int dense_splits, float softmax_scale,
+                     float eps, float *err, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * One probe interval of the router thresholds tau_m of n_windows depth
+ * windows (the paper's §3, the paragraph after Eq. (3)), host memory only:
+ * for window m, an error err[m] above tol lowers tau[m] by step (more tokens
+ * of the window take higher residual rank) and resets below[m]; otherwise
+ * below[m] counts the intervals in a row under tolerance and, when it
+ * reaches patience, tau[m] rises by step (less residual storage) and
+ * below[m] restarts.  tau stays in [tau_min, tau_max].  The pages give no
+ * values for the tolerance, step or patience: they are the caller's.
+ */
+int dwkv_probe_update(float *tau, int32_t *below, int n_windows, const float *err, float tol, float step,
+                      int patience, float tau_min, float tau_max);
+
 /* Synchronises the stream; returns DWKV_ERR_DEVICE if the device error word
  * is set (its bits in *bits if non-NULL), else DWKV_OK. */
 int dwkv_check_errors(dwkv_handle *h, void *stream, uint32_t *bits);
