@@ -58,7 +58,8 @@ int build_layout(const dwkv_config *c, Layout *ly)
     for (int k = 0; k < c->num_tiers; ++k) {
         int r = c->tier_rank[k], s = c->tier_resid[k];
         if (r <= 0 || r > c->r_max || r % 4 != 0) return DWKV_ERR_UNSUPPORTED;
-        if (r <= prev) return DWKV_ERR_INVALID_ARG;  // ranks strictly ascending
+        if (r < prev) return DWKV_ERR_INVALID_ARG;   // ranks non-decreasing (equal ranks: tiers that
+                                                     // differ only in their residual channels)
         prev = r;
         if (s < 0 || s > kMaxResid || s > c->head_dim) return DWKV_ERR_UNSUPPORTED;
         if (c->tier_capacity[k] < 0 || c->tier_capacity[k] >= (int64_t(1) << 28))

@@ -69,7 +69,9 @@ extern "C" {
 
 /*
  * Static shape of one cache.  Supported: head_dim 64 or 128; r_max a multiple
- * of 4 in [4, 128]; 1..8 tiers with ranks ascending, each a multiple of 4 and
+ * of 4 in [4, 128]; 1..8 tiers with ranks non-decreasing (tiers of one rank
+ * that differ in tier_resid give the paper's fixed coefficient width with
+ * router-chosen residual channels), each a multiple of 4 and
  * <= r_max; tier_resid[k] (channels kept per token) in [0, 8]; resid_bits 4
  * or 8; num_q_heads a multiple of num_kv_heads with at most 8 query heads per
  * KV head.  tier_capacity[k] is the number of token slots per (layer,

@@ -48,7 +48,8 @@ def test_config_validation(field, value, code):
 
 
 def test_tier_table_validation():
-    assert _rc_arena(_cfg(tier_rank=(8, 8, 32, 64))) == d.DWKV_ERR_INVALID_ARG      # not ascending
+    assert _rc_arena(_cfg(tier_rank=(16, 8, 32, 64))) == d.DWKV_ERR_INVALID_ARG     # descending
+    assert _rc_arena(_cfg(tier_rank=(16, 16, 16, 16), tier_resid=(0, 2, 4, 8))) == d.DWKV_OK   # fixed r_b, routed s
     assert _rc_arena(_cfg(tier_rank=(8, 16, 32, 72))) == d.DWKV_ERR_UNSUPPORTED     # above r_max
     assert _rc_arena(_cfg(tier_rank=(6, 16, 32, 64))) == d.DWKV_ERR_UNSUPPORTED     # not /4
     assert _rc_arena(_cfg(tier_resid=(8, 8, 8, 9))) == d.DWKV_ERR_UNSUPPORTED

@@ -130,6 +130,18 @@ def test_group_sizes_and_head_dims(G, gq, d, bits):
     _run(G, cfg, layers=(0, 1), splits=9, peak=4.0)
 
 
+@pytest.mark.parametrize("rb,bits", [(16, 4), (32, 8), (64, 4)])
+def test_paper_literal_tiers_fixed_rank_routed_residuals(G, rb, bits):
+    """The paper's storage reading (§3: coefficients of one fixed width r_b,
+    the router choosing how many residual channels a token keeps, levels
+    0/2, 4 and 8): four tiers of rank r_b with s = 0, 2, 4, 8."""
+    cfg = tiny_config(batch=2, num_kv_heads=2, num_q_heads=8, head_dim=128, r_max=64,
+                      tier_rank=(rb,) * 4, tier_prob=(0.4, 0.3, 0.2, 0.1), tier_resid=(0, 2, 4, 8),
+                      resid_channels=8, resid_bits=bits, n_tokens=2500)
+    _run(G, cfg, layers=(0, 1), splits=6, peak=4.0)
+    _run(G, cfg, layers=(1,), splits=0, needle=True)
+
+
 def test_wide_basis_identity_d128(G):
     """B = I with r_max = d = 128: the cache stores K and V directly."""
     cfg = tiny_config(batch=1, num_kv_heads=2, num_q_heads=8, head_dim=128, r_max=128,

@@ -139,6 +139,16 @@ def test_step_full_size_as_benchmarked(G, ci, layer):
     _steps(G, cfg, cfg.n_tokens, steps=2, layer=layer, expect_splits=32)
 
 
+def test_step_paper_literal_tiers(G):
+    """Fixed coefficient width r_b = 32 with routed residual channels 0/2/4/8:
+    the one-launch step against the two calls and the oracle."""
+    from tests.helpers import tiny_config
+    cfg = tiny_config(batch=2, num_layers=4, layers_per_group=2, num_kv_heads=4, num_q_heads=16, head_dim=128,
+                      r_max=32, tier_rank=(32,) * 4, tier_prob=(0.4, 0.3, 0.2, 0.1), tier_resid=(0, 2, 4, 8),
+                      resid_channels=8, resid_bits=4, n_tokens=1800)
+    _steps(G, cfg, 1800, steps=3, layer=3, splits=4)
+
+
 def test_step_on_empty_cache(G):
     """An empty cache: zero output, and the step's token becomes the first."""
     cfg = w.get_config(0)
