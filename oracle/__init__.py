@@ -32,6 +32,7 @@ class _Shape(ctypes.Structure):
         ("r_max", ctypes.c_int32), ("s_max", ctypes.c_int32),
         ("n_max", ctypes.c_int64), ("num_tiers", ctypes.c_int32),
         ("tier_rank", ctypes.c_int32 * 8), ("tier_resid", ctypes.c_int32 * 8),
+        ("coef_bits", ctypes.c_int32),
     ]
 
 
@@ -46,19 +47,24 @@ def _load(path: str):
     L.oracle_half_to_double_array.argtypes = [P, P, ctypes.c_int64]
     L.oracle_float_to_half_array.argtypes = [P, P, ctypes.c_int64]
     L.oracle_decode.restype = ctypes.c_int
-    L.oracle_decode.argtypes = [ctypes.POINTER(_Shape), P, P, P, P, P, P, P, P, P, P, P, P,
+    L.oracle_decode.argtypes = [ctypes.POINTER(_Shape), P, P, P, P, P, P, P, P, P, P, P, P, P, P,
                                 P, ctypes.c_double, P, P, ctypes.c_int, ctypes.c_int]
     L.oracle_materialize.restype = ctypes.c_int
-    L.oracle_materialize.argtypes = [ctypes.POINTER(_Shape), P, P, P, P, P, P, P, P, P, P, P, P, P, P,
+    L.oracle_materialize.argtypes = [ctypes.POINTER(_Shape), P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P,
                                      ctypes.c_int]
     L.oracle_dense_decode.restype = ctypes.c_int
     L.oracle_dense_decode.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int64,
                                       P, P, P, P, ctypes.c_double, P, ctypes.c_int]
+    L.oracle_append_ex.restype = ctypes.c_int
+    L.oracle_append_ex.argtypes = [ctypes.c_int, ctypes.c_int, P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_uint16, ctypes.c_int, P, P, P, P, P]
     L.oracle_append.restype = ctypes.c_int
     L.oracle_append.argtypes = [ctypes.c_int, ctypes.c_int, P, P, ctypes.c_int, ctypes.c_int,
                                 ctypes.c_int, ctypes.c_uint16, P, P, P, P]
     L.oracle_append_residual.restype = ctypes.c_int
     L.oracle_append_residual.argtypes = [ctypes.c_int, ctypes.c_int, P, P, ctypes.c_int, P]
+    L.oracle_append_residual_ex.restype = ctypes.c_int
+    L.oracle_append_residual_ex.argtypes = [ctypes.c_int, ctypes.c_int, P, P, ctypes.c_int, ctypes.c_int, P]
     L.oracle_append_projection.restype = ctypes.c_int
     L.oracle_append_projection.argtypes = [ctypes.c_int, ctypes.c_int, P, P, ctypes.c_int, P]
     L.oracle_max_threads.restype = ctypes.c_int
@@ -126,6 +132,7 @@ def decode(cfg, lay: Dict[str, np.ndarray], basisK: np.ndarray, basisV: np.ndarr
     sh.batch, sh.num_q_heads, sh.num_kv_heads, sh.head_dim = B, Hq, Hkv, d
     sh.r_max, sh.s_max, sh.n_max = R, S, n_max
     sh.num_tiers = cfg.num_tiers
+    sh.coef_bits = _coef_bits(cfg)
     res = tuple(tier_resid) if tier_resid is not None else cfg.resid_per_tier
     for k in range(cfg.num_tiers):
         sh.tier_rank[k] = cfg.tier_rank[k]
@@ -141,13 +148,31 @@ def decode(cfg, lay: Dict[str, np.ndarray], basisK: np.ndarray, basisV: np.ndarr
     c = {k: np.ascontiguousarray(v) for k, v in lay.items()}
     rc = lib().oracle_decode(
         ctypes.byref(sh), _p(np.ascontiguousarray(c["n_tokens"], np.int64)), _p(c["tier"]),
-        _p(_u16(basisK)), _p(_u16(basisV)), _p(_u16(c["coefK"])), _p(_u16(c["coefV"])),
+        _p(_u16(basisK)), _p(_u16(basisV)), _p(_coef(c["coefK"])), _p(_coef(c["coefV"])),
         _p(c["idxK"]), _p(c["idxV"]), _p(c["valK"]), _p(c["valV"]),
-        _p(_u16(c["scaleK"])), _p(_u16(c["scaleV"])), _p(_u16(q)), float(alpha), _p(out),
+        _p(_u16(c["scaleK"])), _p(_u16(c["scaleV"])), *_cscales(c), _p(_u16(q)), float(alpha), _p(out),
         pa, npairs, int(threads))
     if rc != 0:
         raise ValueError("oracle_decode rejected its arguments")
     return out
+
+
+def _coef_bits(cfg) -> int:
+    return int(getattr(cfg, "coef_bits", 16) or 16)
+
+
+def _coef(a: np.ndarray) -> np.ndarray:
+    """Coefficient array as the oracle reads it: fp16 bits, or int8 codes."""
+    a = np.ascontiguousarray(a)
+    return a if a.dtype == np.int8 else _u16(a)
+
+
+def _cscales(c):
+    """Pointers to the per-token coefficient block scales (8-bit form), or
+    NULL for fp16 coefficients."""
+    if "cscaleK" in c:
+        return _p(_u16(c["cscaleK"])), _p(_u16(c["cscaleV"]))
+    return None, None
 
 
 def _shape(cfg, lay, tier_resid=None):
@@ -157,6 +182,7 @@ def _shape(cfg, lay, tier_resid=None):
     sh.num_q_heads = cfg.num_q_heads
     sh.r_max, sh.s_max, sh.n_max = R, lay["idxK"].shape[3], n_max
     sh.num_tiers = cfg.num_tiers
+    sh.coef_bits = _coef_bits(cfg)
     res = tuple(tier_resid) if tier_resid is not None else cfg.resid_per_tier
     for k in range(cfg.num_tiers):
         sh.tier_rank[k] = cfg.tier_rank[k]
@@ -176,9 +202,9 @@ def materialize(cfg, lay: Dict[str, np.ndarray], basisK: np.ndarray, basisV: np.
     c = {k: np.ascontiguousarray(v) for k, v in lay.items()}
     rc = lib().oracle_materialize(
         ctypes.byref(sh), _p(np.ascontiguousarray(c["n_tokens"], np.int64)), _p(c["tier"]),
-        _p(_u16(basisK)), _p(_u16(basisV)), _p(_u16(c["coefK"])), _p(_u16(c["coefV"])),
+        _p(_u16(basisK)), _p(_u16(basisV)), _p(_coef(c["coefK"])), _p(_coef(c["coefV"])),
         _p(c["idxK"]), _p(c["idxV"]), _p(c["valK"]), _p(c["valV"]),
-        _p(_u16(c["scaleK"])), _p(_u16(c["scaleV"])), _p(K), _p(V), int(threads))
+        _p(_u16(c["scaleK"])), _p(_u16(c["scaleV"])), *_cscales(c), _p(K), _p(V), int(threads))
     if rc != 0:
         raise ValueError("oracle_materialize rejected its arguments")
     return K, V
@@ -250,30 +276,36 @@ def probe_controller(tau: float, below: int, err: float, tol: float, step: float
 
 # ------------------------------------------------------------------ append
 def append_vector(basis: np.ndarray, x: np.ndarray, r: int, s: int, qmax: int,
-                  gate: Optional[np.float16] = None):
+                  gate: Optional[np.float16] = None, coef_bits: int = 16):
     """Encode one fp16 vector.  basis: fp16 [r_max][d]; x: fp16 [d].
-    Returns (c fp16[r], idx uint8[s], val int8[s], scale fp16)."""
+    Returns (c, idx uint8[s], val int8[s], scale fp16) with c fp16[r]; with
+    coef_bits 8, (c int8[r], idx, val, scale, coefficient block scale fp16)."""
     b = _u16(basis)
     xv = _u16(x)
     r_max, d = b.shape
-    c = np.zeros(max(r, 1), np.uint16)
+    c = np.zeros(max(r, 1), np.uint16 if coef_bits == 16 else np.int8)
     idx = np.zeros(max(s, 1), np.uint8)
     val = np.zeros(max(s, 1), np.int8)
     sc = np.zeros(1, np.uint16)
+    cs = np.zeros(1, np.uint16)
     g = 0x3C00 if gate is None else int(np.asarray(gate, np.float16).view(np.uint16))
-    rc = lib().oracle_append(d, r_max, _p(b), _p(xv), r, s, qmax, g, _p(c), _p(idx), _p(val), _p(sc))
+    rc = lib().oracle_append_ex(d, r_max, _p(b), _p(xv), r, s, qmax, g, coef_bits, _p(c), _p(cs), _p(idx),
+                                _p(val), _p(sc))
     if rc != 0:
         raise ValueError("oracle_append rejected its arguments")
+    if coef_bits == 8:
+        return c[:r], idx[:s], val[:s], sc.view(np.float16)[0], cs.view(np.float16)[0]
     return c[:r].view(np.float16), idx[:s], val[:s], sc.view(np.float16)[0]
 
 
-def append_residual(basis: np.ndarray, x: np.ndarray, r: int) -> np.ndarray:
-    """fp32 residual e = x - B^T fp16(B x) of the encoder (step 2)."""
+def append_residual(basis: np.ndarray, x: np.ndarray, r: int, coef_bits: int = 16) -> np.ndarray:
+    """fp32 residual e = x - B^T c of the encoder (step 2), c the stored
+    coefficients (fp16, or int8 codes times their block scale)."""
     b = _u16(basis)
     xv = _u16(x)
     r_max, d = b.shape
     e = np.zeros(d, np.float32)
-    if lib().oracle_append_residual(d, r_max, _p(b), _p(xv), r, _p(e)) != 0:
+    if lib().oracle_append_residual_ex(d, r_max, _p(b), _p(xv), r, coef_bits, _p(e)) != 0:
         raise ValueError("oracle_append_residual rejected its arguments")
     return e
 
@@ -301,9 +333,11 @@ def append_layer(cfg, basisK: np.ndarray, basisV: np.ndarray, k: np.ndarray, v: 
     B, H, d = k.shape
     R, S = cfg.r_max, cfg.s_max
     res = cfg.resid_per_tier
+    cb = _coef_bits(cfg)
     out = {}
     for z, x, bas, gate in (("K", k, basisK, gateK), ("V", v, basisV, gateV)):
-        coef = np.zeros((B, H, R), np.float16)
+        coef = np.zeros((B, H, R), np.float16 if cb == 16 else np.int8)
+        cscale = np.zeros((B, H), np.float16)
         idx = np.zeros((B, H, S), np.uint8)
         val = np.zeros((B, H, S), np.int8)
         sc = np.zeros((B, H), np.float16)
@@ -312,10 +346,14 @@ def append_layer(cfg, basisK: np.ndarray, basisV: np.ndarray, k: np.ndarray, v: 
                 t = int(tier[b, h])
                 r, s = cfg.tier_rank[t], res[t]
                 g = None if gate is None else gate[b, h]
-                c, i, vv, scale = append_vector(bas[h], x[b, h], r, s, cfg.qmax, g)
-                coef[b, h, :r] = c
-                idx[b, h, :s] = i
-                val[b, h, :s] = vv
-                sc[b, h] = scale
+                enc = append_vector(bas[h], x[b, h], r, s, cfg.qmax, g, coef_bits=cb)
+                coef[b, h, :r] = enc[0]
+                idx[b, h, :s] = enc[1]
+                val[b, h, :s] = enc[2]
+                sc[b, h] = enc[3]
+                if cb == 8:
+                    cscale[b, h] = enc[4]
         out["coef" + z], out["idx" + z], out["val" + z], out["scale" + z] = coef, idx, val, sc
+        if cb == 8:
+            out["cscale" + z] = cscale
     return out

@@ -121,13 +121,24 @@ typedef struct oracle_shape {
     int32_t num_tiers;
     int32_t tier_rank[8];
     int32_t tier_resid[8];
+    int32_t coef_bits;               /* 16: fp16 coefficients; 8: int8 codes times a per-token fp16 scale */
 } oracle_shape;
 
-/* Rebuild one cached vector (K or V) of token t in fp64 (Eq. (1)).
+/* Coefficient i of the token whose row starts at element tt * r_max of the
+ * coefficient array: fp16, or (8-bit blockwise form, paper §3 second
+ * paragraph) the token's fp16 block scale times an int8 code. */
+static double coef_at(const oracle_shape *sh, const void *coef, const uint16_t *cscale, int64_t tt, int i)
+{
+    if (sh->coef_bits == 8)
+        return oracle_half_to_double(cscale[tt]) * (double)((const int8_t *)coef)[tt * sh->r_max + i];
+    return oracle_half_to_double(((const uint16_t *)coef)[tt * sh->r_max + i]);
+}
+
+/* Rebuild one cached vector (K or V) of token tt in fp64 (Eq. (1)).
  * basis: the window's basis already decoded to fp64, [r_max][d]. */
 static void reconstruct(const oracle_shape *sh, const double *basis /* [r_max][d] */,
-                        const uint16_t *coef /* [r_max] */, const uint8_t *idx, const int8_t *val,
-                        uint16_t scale, int tier, double *x /* [d] */)
+                        const void *coef, const uint16_t *cscale, int64_t tt, const uint8_t *idx,
+                        const int8_t *val, uint16_t scale, int tier, double *x /* [d] */)
 {
     int d = sh->head_dim;
     int r = sh->tier_rank[tier];
@@ -135,7 +146,7 @@ static void reconstruct(const oracle_shape *sh, const double *basis /* [r_max][d
     for (int j = 0; j < d; ++j)
         x[j] = 0.0;
     for (int i = 0; i < r; ++i) {
-        double c = oracle_half_to_double(coef[i]);
+        double c = coef_at(sh, coef, cscale, tt, i);
         const double *bi = basis + (int64_t)i * d;
         for (int j = 0; j < d; ++j)
             x[j] += c * bi[j];
@@ -153,10 +164,11 @@ static void reconstruct(const oracle_shape *sh, const double *basis /* [r_max][d
  */
 int oracle_decode(const oracle_shape *sh, const int64_t *n_tokens, const uint8_t *tier,
                   const uint16_t *basisK, const uint16_t *basisV,
-                  const uint16_t *coefK, const uint16_t *coefV,
+                  const void *coefK, const void *coefV,
                   const uint8_t *idxK, const uint8_t *idxV,
                   const int8_t *valK, const int8_t *valV,
                   const uint16_t *scaleK, const uint16_t *scaleV,
+                  const uint16_t *cscaleK, const uint16_t *cscaleV,
                   const uint16_t *q, double alpha, double *out,
                   const int32_t *pairs, int n_pairs, int nthreads)
 {
@@ -205,7 +217,7 @@ int oracle_decode(const oracle_shape *sh, const int64_t *n_tokens, const uint8_t
             int64_t tt = base + t;
             int k = tier[tt];
             if (k >= sh->num_tiers) { bad = 1; k = 0; }
-            reconstruct(sh, bK, coefK + tt * R, idxK + tt * S, valK + tt * S, scaleK[tt], k, x);
+            reconstruct(sh, bK, coefK, cscaleK, tt, idxK + tt * S, valK + tt * S, scaleK[tt], k, x);
             for (int g = 0; g < gq; ++g) {
                 double acc = 0.0;
                 for (int j = 0; j < d; ++j)
@@ -227,7 +239,7 @@ int oracle_decode(const oracle_shape *sh, const int64_t *n_tokens, const uint8_t
             int64_t tt = base + t;
             int k = tier[tt];
             if (k >= sh->num_tiers) k = 0;
-            reconstruct(sh, bV, coefV + tt * R, idxV + tt * S, valV + tt * S, scaleV[tt], k, x);
+            reconstruct(sh, bV, coefV, cscaleV, tt, idxV + tt * S, valV + tt * S, scaleV[tt], k, x);
             for (int g = 0; g < gq; ++g) {
                 double w = exp(z[g * n + t] - mx[g]);
                 den[g] += w;
@@ -255,10 +267,11 @@ int oracle_decode(const oracle_shape *sh, const int64_t *n_tokens, const uint8_t
  */
 int oracle_materialize(const oracle_shape *sh, const int64_t *n_tokens, const uint8_t *tier,
                        const uint16_t *basisK, const uint16_t *basisV,
-                       const uint16_t *coefK, const uint16_t *coefV,
+                       const void *coefK, const void *coefV,
                        const uint8_t *idxK, const uint8_t *idxV,
                        const int8_t *valK, const int8_t *valV,
                        const uint16_t *scaleK, const uint16_t *scaleV,
+                       const uint16_t *cscaleK, const uint16_t *cscaleV,
                        double *Kout, double *Vout, int nthreads)
 {
     const int B = sh->batch, Hkv = sh->num_kv_heads;
@@ -289,8 +302,8 @@ int oracle_materialize(const oracle_shape *sh, const int64_t *n_tokens, const ui
             int64_t tt = base + t;
             int k = tier[tt];
             if (k >= sh->num_tiers) { bad = 1; k = 0; }
-            reconstruct(sh, bK, coefK + tt * R, idxK + tt * S, valK + tt * S, scaleK[tt], k, xk);
-            reconstruct(sh, bV, coefV + tt * R, idxV + tt * S, valV + tt * S, scaleV[tt], k, xv);
+            reconstruct(sh, bK, coefK, cscaleK, tt, idxK + tt * S, valK + tt * S, scaleK[tt], k, xk);
+            reconstruct(sh, bV, coefV, cscaleV, tt, idxV + tt * S, valV + tt * S, scaleV[tt], k, xv);
         }
         free(bK); free(bV);
     }
@@ -364,20 +377,46 @@ int oracle_dense_decode(int B, int Hq, int Hkv, int d, int64_t n_max, const int6
  * Outputs: c_out[r] fp16 bits, idx_out[s] ascending, val_out[s], *scale_out
  * fp16 bits (0 when s == 0).  Returns 0, or -1 on an invalid argument.
  */
-/* Steps 1-2: fp16 coefficients c[r] (and, if sum is not NULL, the fp32
- * projection sums they are rounded from) and the fp32 residual e[d]. */
-static void project(int d, const uint16_t *basis, const uint16_t *x, int r, uint16_t *c16,
-                    float *sum, float *e)
+/* Steps 1-2: the coefficients (fp16 when coef_bits is 16; else int8 codes
+ * in c8 with one fp16 block scale *cs16) -- and, if sum is not NULL, the
+ * fp32 projection sums they come from -- and the fp32 residual e[d] against
+ * the stored coefficients. */
+static void project(int d, const uint16_t *basis, const uint16_t *x, int r, int coef_bits, uint16_t *c16,
+                    int8_t *c8, uint16_t *cs16, float *sum, float *e)
 {
-    float c[256];
+    float c[256], acc1[256];
     for (int i = 0; i < r; ++i) {
         float acc = 0.0f;                                         /* step 1 */
         for (int j = 0; j < d; ++j)
             acc = fmaf(h2f(basis[(int64_t)i * d + j]), h2f(x[j]), acc);
         if (sum)
             sum[i] = acc;
-        c16[i] = oracle_float_to_half(acc);
-        c[i] = h2f(c16[i]);
+        acc1[i] = acc;
+    }
+    if (coef_bits == 8) {
+        /* 8-bit blockwise form: one block per token; scale = fp16(max |sum| /
+         * 127), codes rint(sum / scale) in [-127, 127] (0 for a zero scale);
+         * the stored coefficient is code * scale, exact in fp32 */
+        float amax = 0.0f;
+        for (int i = 0; i < r; ++i)
+            if (fabsf(acc1[i]) > amax) amax = fabsf(acc1[i]);
+        *cs16 = oracle_float_to_half(amax / 127.0f);
+        float sf = h2f(*cs16);
+        for (int i = 0; i < r; ++i) {
+            float q = 0.0f;
+            if (sf != 0.0f) {
+                q = rintf(acc1[i] / sf);
+                if (q > 127.0f) q = 127.0f;
+                if (q < -127.0f) q = -127.0f;
+            }
+            c8[i] = (int8_t)q;
+            c[i] = q * sf;
+        }
+    } else {
+        for (int i = 0; i < r; ++i) {
+            c16[i] = oracle_float_to_half(acc1[i]);
+            c[i] = h2f(c16[i]);
+        }
     }
     for (int j = 0; j < d; ++j) {
         float acc = 0.0f;                                         /* step 2 */
@@ -394,14 +433,18 @@ static void project(int d, const uint16_t *basis, const uint16_t *x, int r, uint
  * Outputs: c_out[r] fp16 bits, idx_out[s] ascending, val_out[s], *scale_out
  * fp16 bits (0 when s == 0).  Returns 0, or -1 on an invalid argument.
  */
-int oracle_append(int d, int r_max, const uint16_t *basis, const uint16_t *x, int r, int s,
-                  int qmax, uint16_t gate, uint16_t *c_out, uint8_t *idx_out, int8_t *val_out,
-                  uint16_t *scale_out)
+int oracle_append_ex(int d, int r_max, const uint16_t *basis, const uint16_t *x, int r, int s,
+                     int qmax, uint16_t gate, int coef_bits, void *c_out, uint16_t *cscale_out,
+                     uint8_t *idx_out, int8_t *val_out, uint16_t *scale_out)
 {
-    if (d <= 0 || d > 256 || r < 0 || r > r_max || s < 0 || s > d || qmax <= 0)
+    if (d <= 0 || d > 256 || r < 0 || r > r_max || s < 0 || s > d || qmax <= 0 ||
+        (coef_bits != 8 && coef_bits != 16))
         return -1;
     float e[256];
-    project(d, basis, x, r, c_out, NULL, e);
+    uint16_t cs = 0;
+    project(d, basis, x, r, coef_bits, (uint16_t *)c_out, (int8_t *)c_out, &cs, NULL, e);
+    if (cscale_out)
+        *cscale_out = cs;
     *scale_out = 0;
     if (s == 0)
         return 0;
@@ -445,6 +488,14 @@ int oracle_append(int d, int r_max, const uint16_t *basis, const uint16_t *x, in
     return 0;
 }
 
+int oracle_append(int d, int r_max, const uint16_t *basis, const uint16_t *x, int r, int s,
+                  int qmax, uint16_t gate, uint16_t *c_out, uint8_t *idx_out, int8_t *val_out,
+                  uint16_t *scale_out)
+{
+    return oracle_append_ex(d, r_max, basis, x, r, s, qmax, gate, 16, c_out, NULL, idx_out, val_out,
+                            scale_out);
+}
+
 /* Residual vector e of step 2 (for the quantisation-bound checks). */
 int oracle_append_residual(int d, int r_max, const uint16_t *basis, const uint16_t *x, int r,
                            float *e_out)
@@ -452,7 +503,19 @@ int oracle_append_residual(int d, int r_max, const uint16_t *basis, const uint16
     if (d <= 0 || d > 256 || r < 0 || r > r_max)
         return -1;
     uint16_t c16[256];
-    project(d, basis, x, r, c16, NULL, e_out);
+    project(d, basis, x, r, 16, c16, NULL, NULL, NULL, e_out);
+    return 0;
+}
+
+/* Residual e of step 2 for either coefficient form (coef_bits 16 or 8). */
+int oracle_append_residual_ex(int d, int r_max, const uint16_t *basis, const uint16_t *x, int r, int coef_bits,
+                              float *e_out)
+{
+    if (d <= 0 || d > 256 || r < 0 || r > r_max || (coef_bits != 8 && coef_bits != 16))
+        return -1;
+    uint16_t c16[256], cs;
+    int8_t c8[256];
+    project(d, basis, x, r, coef_bits, c16, c8, &cs, NULL, e_out);
     return 0;
 }
 
@@ -465,7 +528,7 @@ int oracle_append_projection(int d, int r_max, const uint16_t *basis, const uint
         return -1;
     uint16_t c16[256];
     float e[256];
-    project(d, basis, x, r, c16, sum_out, e);
+    project(d, basis, x, r, 16, c16, NULL, NULL, sum_out, e);
     return 0;
 }
 

@@ -30,6 +30,8 @@ def dense_from_logical(cfg: Config, lay: dict, basis: np.ndarray, z: str) -> np.
     """Textbook materialisation [B][H][n][d] in fp64: coefficients times basis
     vectors (NumPy matmul) plus the sparse residual written into its channels."""
     coef = lay["coef" + z].astype(np.float64)                 # [B][H][n][R]
+    if "cscale" + z in lay:                                   # 8-bit codes times their block scale
+        coef = coef * lay["cscale" + z].astype(np.float64)[..., None]
     B, H, n, R = coef.shape
     bas = basis.astype(np.float64)                            # [H][R][d]
     x = np.einsum("bhnr,hrd->bhnd", coef, bas)
@@ -89,4 +91,6 @@ def extend_layer(lay: dict, enc: dict, tier: np.ndarray, n: int) -> dict:
         out["idx" + z][:, :, n] = enc["idx" + z]
         out["val" + z][:, :, n] = enc["val" + z]
         out["scale" + z][:, :, n] = enc["scale" + z]
+        if "cscale" + z in enc:
+            out["cscale" + z][:, :, n] = enc["cscale" + z]
     return out

@@ -23,6 +23,7 @@ from tests import test_oracle_append as TA
 from tests import test_oracle_decode as TD
 from tests import test_oracle_encoder_order as TO
 from tests import test_oracle_dense as TN
+from tests import test_oracle_coef8 as TC
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(os.path.dirname(HERE), "oracle", "oracle.c")
@@ -57,6 +58,14 @@ DENSE_PINS = [
     TN.test_dense_decode_closed_forms,
 ]
 
+COEF8_PINS = [
+    TC.test_decode_with_8bit_coefficients_equals_sdpa_on_materialised_cache,
+    TC.test_identity_basis_encoding_by_hand,
+    lambda: TC.test_step2_against_exact_chain_with_dequantised_coefficients(16),
+    TC.test_coefficient_quantisation_bound,
+    TC.test_coefficient_codes_round_half_to_even,
+]
+
 _STEP1 = ("        float acc = 0.0f;                                         /* step 1 */\n"
           "        for (int j = 0; j < d; ++j)\n"
           "            acc = fmaf(h2f(basis[(int64_t)i * d + j]), h2f(x[j]), acc);\n")
@@ -67,8 +76,8 @@ _STEP2 = ("        float acc = 0.0f;                                         /* 
 MUTANTS = {
     "drop_residual": ("x[idx[u]] += g * (double)val[u];", "(void)g;", DECODE_PINS),
     "residual_sign": ("x[idx[u]] += g * (double)val[u];", "x[idx[u]] -= g * (double)val[u];", DECODE_PINS),
-    "kv_basis_swap": ("reconstruct(sh, bV, coefV + tt * R, idxV + tt * S, valV + tt * S, scaleV[tt], k, x);",
-                      "reconstruct(sh, bK, coefV + tt * R, idxV + tt * S, valV + tt * S, scaleV[tt], k, x);",
+    "kv_basis_swap": ("reconstruct(sh, bV, coefV, cscaleV, tt, idxV + tt * S, valV + tt * S, scaleV[tt], k, x);",
+                      "reconstruct(sh, bK, coefV, cscaleV, tt, idxV + tt * S, valV + tt * S, scaleV[tt], k, x);",
                       DECODE_PINS),
     "head_map": ("q[((int64_t)b * Hq + h * gq + g) * d + j]", "q[((int64_t)b * Hq + g * Hkv + h) * d + j]",
                  DECODE_PINS),
@@ -80,11 +89,11 @@ MUTANTS = {
                      DECODE_PINS),
     "tie_to_larger": ("fabsf(e[j]) > fabsf(e[best])", "fabsf(e[j]) >= fabsf(e[best])", APPEND_PINS),
     "round_half_away": ("v = rintf(e[j] / sf);", "v = roundf(e[j] / sf);", APPEND_PINS),
-    "unrounded_coef": ("c[i] = h2f(c16[i]);", "c[i] = acc;", APPEND_PINS),
+    "unrounded_coef": ("c[i] = h2f(c16[i]);", "c[i] = acc1[i];", APPEND_PINS),
     "wrong_code_range": ("amax / (float)qmax", "amax / (float)(qmax + 1)", APPEND_PINS),
     "residual_flipped": ("e[j] = h2f(x[j]) - acc;", "e[j] = acc - h2f(x[j]);", APPEND_PINS),
-    "materialize_v_with_k_basis": ("reconstruct(sh, bV, coefV + tt * R, idxV + tt * S, valV + tt * S, scaleV[tt], k, xv);",
-                                   "reconstruct(sh, bK, coefV + tt * R, idxV + tt * S, valV + tt * S, scaleV[tt], k, xv);",
+    "materialize_v_with_k_basis": ("reconstruct(sh, bV, coefV, cscaleV, tt, idxV + tt * S, valV + tt * S, scaleV[tt], k, xv);",
+                                   "reconstruct(sh, bK, coefV, cscaleV, tt, idxV + tt * S, valV + tt * S, scaleV[tt], k, xv);",
                                    DENSE_PINS),
     "materialize_ragged_ignored": ("            if (t >= n_tokens[b]) {", "            if (t >= NM) {", DENSE_PINS),
     "dense_no_scale": ("            z[t] = alpha * acc;", "            z[t] = acc;", DENSE_PINS),
@@ -92,6 +101,13 @@ MUTANTS = {
                        DENSE_PINS),
     "dense_no_normalisation": ("            o[j] /= den;\n        free(z);", "            o[j] /= 1.0;\n        free(z);",
                                DENSE_PINS),
+    "coef8_scale_range": ("*cs16 = oracle_float_to_half(amax / 127.0f);", "*cs16 = oracle_float_to_half(amax / 128.0f);",
+                          COEF8_PINS),
+    "coef8_residual_unquantised": ("            c[i] = q * sf;", "            c[i] = acc1[i];", COEF8_PINS),
+    "coef8_round_away": ("                q = rintf(acc1[i] / sf);", "                q = roundf(acc1[i] / sf);",
+                         COEF8_PINS),
+    "coef8_scale_ignored": ("return oracle_half_to_double(cscale[tt]) * (double)((const int8_t *)coef)[tt * sh->r_max + i];",
+                            "return (double)((const int8_t *)coef)[tt * sh->r_max + i];", COEF8_PINS),
     "step1_descending": (_STEP1, _STEP1.replace("for (int j = 0; j < d; ++j)", "for (int j = d - 1; j >= 0; --j)"),
                          APPEND_PINS),
     "step2_descending": (_STEP2, _STEP2.replace("for (int i = 0; i < r; ++i)", "for (int i = r - 1; i >= 0; --i)"),

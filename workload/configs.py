@@ -33,6 +33,7 @@ class Config:
     skew_frac: float = 0.0
     bench_steps: int = 1
     tier_resid: Tuple[int, ...] = field(default=())   # per-tier s; () = all s
+    coef_bits: int = 16            # 16: fp16 coefficients; 8: int8 codes with a per-token fp16 block scale
 
     @property
     def group_q(self) -> int:

@@ -11,7 +11,11 @@ Distributions (per workload configuration):
     the routed rank by window, head and token).  Optional router skew forces
     a prefix and a random 2% of positions to the top tier.
   * coefficients c_i ~ N(0, 1/(1+i)) (variance), i < r_tier, rounded to fp16;
-    entries at i >= r_tier are zero (never stored by the cache).
+    entries at i >= r_tier are zero (never stored by the cache).  In the
+    8-bit blockwise form the codes and block scales are drawn directly:
+    codes rint(N(0,1) * 127 / (3 sqrt(1+i))) clipped to [-127, 127], and a
+    per-token scale fp16(3/127 * exp(0.1 N(0,1))), so that code * scale has
+    about the fp16 form's variance.
   * residual: s distinct uniform channels (ascending), integer values uniform
     on [-qmax, qmax], scale = fp16(0.01 |N(0,1)|).
   * queries: fp16 N(0,1).
@@ -27,7 +31,7 @@ from .configs import Config
 _FIELDS = {
     "basis": 1, "tier": 2, "skewpos": 3, "coef": 4, "idx": 5, "val": 6, "scale": 7,
     "query": 8, "app_tier": 9, "app_coef": 10, "app_idx": 11, "app_val": 12,
-    "app_scale": 13, "needle": 14,
+    "app_scale": 13, "needle": 14, "cscale": 15,
 }
 
 
@@ -116,7 +120,9 @@ def empty_layer(cfg: Config, n: int = 0) -> Dict[str, np.ndarray]:
         "tier": np.zeros((B, H, n), np.uint8),
     }
     for z in "KV":
-        lay["coef" + z] = np.zeros((B, H, n, R), np.float16)
+        lay["coef" + z] = np.zeros((B, H, n, R), np.float16 if cfg.coef_bits == 16 else np.int8)
+        if cfg.coef_bits == 8:
+            lay["cscale" + z] = np.zeros((B, H, n), np.float16)
         lay["idx" + z] = np.zeros((B, H, n, S), np.uint8)
         lay["val" + z] = np.zeros((B, H, n, S), np.int8)
         lay["scale" + z] = np.zeros((B, H, n), np.float16)
@@ -154,7 +160,13 @@ def gen_layer(cfg: Config, layer: int, n: Optional[int] = None, all_top: bool = 
                     continue
                 r = int(ranks[k])
                 c = rc.standard_normal((cnt, r), dtype=np.float32) * std_all[:r].astype(np.float32)
-                coef[b][sel[0], sel[1], :r] = c.astype(np.float16)
+                if cfg.coef_bits == 8:
+                    codes = np.clip(np.rint(c * np.float32(127.0 / 3.0)), -127, 127).astype(np.int8)
+                    coef[b][sel[0], sel[1], :r] = codes
+                    u = _rng(seed, "cscale", layer, zi, b, k).standard_normal(cnt)
+                    lay["cscale" + z][b][sel[0], sel[1]] = (3.0 / 127.0 * np.exp(0.1 * u)).astype(np.float16)
+                else:
+                    coef[b][sel[0], sel[1], :r] = c.astype(np.float16)
                 s = int(svec[k])
                 if s == 0:
                     continue
@@ -234,7 +246,14 @@ def plant_needles(cfg: Config, lay: Dict[str, np.ndarray], basisK16: np.ndarray,
             for t in positions:
                 lay["tier"][b, h, t] = top
                 lay["coefK"][b, h, t, :] = 0
-                lay["coefK"][b, h, t, :r] = (lam * proj).astype(np.float16)
+                if cfg.coef_bits == 8:
+                    # the needle's coefficients as codes and a block scale
+                    v = (lam * proj).astype(np.float32)
+                    cs = (np.abs(v).max() / np.float32(127)).astype(np.float16)
+                    lay["cscaleK"][b, h, t] = cs
+                    lay["coefK"][b, h, t, :r] = np.clip(np.rint(v / np.float32(cs)), -127, 127).astype(np.int8)
+                else:
+                    lay["coefK"][b, h, t, :r] = (lam * proj).astype(np.float16)
                 for z in "KV":
                     lay["idx" + z][b, h, t] = 0
                     lay["val" + z][b, h, t] = 0
