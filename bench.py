@@ -32,7 +32,20 @@ from workload.gen import gen_append_inputs, gen_layer, gen_query, make_bases, ma
 METRIC = "decode tokens/s + achieved HBM GB/s (% of peak), compressed-KV attn at 64K"
 PEAK_HBM_GBPS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
-DECODE_SRC = os.path.join(ROOT, "compressed_kv_cache_dwkv_amd", "csrc", "decode.hip")
+DECODE_SRCS = [os.path.join(ROOT, "compressed_kv_cache_dwkv_amd", "csrc", f)
+               for f in ("decode_impl.h", "decode.hip", "decode8.hip")]
+
+
+def decode_source_sha() -> str:
+    """sha256 of the decode kernel's sources (the kernel and its instances)."""
+    h = hashlib.sha256()
+    for f in DECODE_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
+def workload_name(cfg) -> str:
+    return cfg.name if cfg.coef_bits == 16 else cfg.name + "-int8coef"
 
 
 def parse_args():
@@ -53,6 +66,8 @@ def parse_args():
                    help="time a comparator instead of the fused step: 'dense' = flash-decode over a dense fp16 "
                         "cache of the same shape; 'unfused' = per layer, materialise K^/V^ to HBM, dense "
                         "flash-decode over it, then the append")
+    p.add_argument("--coef-bits", type=int, choices=[8, 16], default=16,
+                   help="coefficient form: 16 = fp16, 8 = the 8-bit blockwise form (int8 codes, fp16 block scales)")
     p.add_argument("--dense-splits", type=int, default=0, help="dense decode workgroups per KV head (0 = auto)")
     p.add_argument("--copy-probe", action="store_true",
                    help="also run a plain 512 MiB device copy (counter calibration)")
@@ -118,14 +133,16 @@ def pmc_summary(workload: str, fetch_dir: str, write_dir: str, bench_json: Optio
                         "scale": scale, "bytes_per_launch": float(np.mean(dec)) * 1024 * scale}
     total = res["FETCH_SIZE"]["bytes_per_launch"] + res["WRITE_SIZE"]["bytes_per_launch"]
     rec = {"workload": workload, "kernel": "decode_kernel",
-           "decode_source_sha256": hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest(),
+           "decode_source_sha256": decode_source_sha(),
            "hbm_bytes_per_launch": total, "counters": res,
            "copy_probe_bytes": COPY_PROBE_BYTES}
     os.makedirs(PROFILES, exist_ok=True)
     path = os.path.join(PROFILES, f"decode_{workload}_traffic.json")
     json.dump(rec, open(path, "w"), indent=1)
-    cfg = next(c for c in w.CONFIGS if c.name == workload)
+    base = workload[:-len("-int8coef")] if workload.endswith("-int8coef") else workload
+    cfg = next(c for c in w.CONFIGS if c.name == base)
     ci = w.CONFIGS.index(cfg)
+    cflag = " --coef-bits 8" if workload != base else ""
     alg = None
     if bench_json:     # the JSON line the counter run itself printed
         alg = _json_line(bench_json)["roofline"]["algorithmic_bytes_per_launch"]
@@ -142,10 +159,10 @@ def pmc_summary(workload: str, fetch_dir: str, write_dir: str, bench_json: Optio
         "",
         "```",
         f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d <fetch> -o run -- python3 <repo>/bench.py "
-        f"--config {ci} {PMC_RUN_ARGS}",
+        f"--config {ci}{cflag} {PMC_RUN_ARGS}",
         f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d <write> -o run -- python3 <repo>/bench.py "
-        f"--config {ci} {PMC_RUN_ARGS}",
-        f"python3 <repo>/bench.py --config {ci} --pmc-summary <fetch> <write> --bench-json <fetch run's JSON line>",
+        f"--config {ci}{cflag} {PMC_RUN_ARGS}",
+        f"python3 <repo>/bench.py --config {ci}{cflag} --pmc-summary <fetch> <write> --bench-json <fetch run's JSON line>",
         "```",
         "",
         "`--copy-probe` adds a plain 512 MiB device-to-device copy to the same process; each counter is",
@@ -189,7 +206,7 @@ def trace_summary(cfg, ci: int, trace_dir: str, bench_json: Optional[str]):
         raise SystemExit("no decode_kernel in the trace")
     bj = _json_line(bench_json) if bench_json else None
     lines = [
-        f"# decode_kernel, {cfg.name} (batch {cfg.batch}, {cfg.num_layers} layers, {cfg.num_q_heads} q / "
+        f"# decode_kernel, {workload_name(cfg)} (batch {cfg.batch}, {cfg.num_layers} layers, {cfg.num_q_heads} q / "
         f"{cfg.num_kv_heads} KV heads, d {cfg.head_dim}, {cfg.n_tokens} tokens)",
         "",
         "The kernel is the one-launch decode step (`dwkv_decode_step`: decode attention plus the append of the new",
@@ -199,8 +216,9 @@ def trace_summary(cfg, ci: int, trace_dir: str, bench_json: Optional[str]):
         "",
         "```",
         f"rocprofv3 --kernel-trace --stats --output-format csv -d <out> -o bench -- python3 <repo>/bench.py "
-        f"--config {ci} {TRACE_RUN_ARGS}",
-        f"python3 <repo>/bench.py --config {ci} --trace-summary <out> [--bench-json <default run's line>]",
+        f"--config {ci}{' --coef-bits 8' if cfg.coef_bits == 8 else ''} {TRACE_RUN_ARGS}",
+        f"python3 <repo>/bench.py --config {ci}{' --coef-bits 8' if cfg.coef_bits == 8 else ''} --trace-summary <out> "
+        f"[--bench-json <default run's line>]",
         "```",
         "",
         "Kernel statistics (durations in ns; graph replays of the warm-up and timed steps plus the replays of",
@@ -227,13 +245,13 @@ def trace_summary(cfg, ci: int, trace_dir: str, bench_json: Optional[str]):
             "of one step's launches.  The trace's start-to-end durations of back-to-back kernels include each",
             "kernel's end, which overlaps the next kernel's start.",
         ]
-    open(os.path.join(PROFILES, f"decode_{cfg.name}_kernel_trace.md"), "w").write("\n".join(lines) + "\n")
+    open(os.path.join(PROFILES, f"decode_{workload_name(cfg)}_kernel_trace.md"), "w").write("\n".join(lines) + "\n")
     print("\n".join(lines), flush=True)
 
 
 def _gen_layer_job(args):
-    ci, layer = args
-    return gen_layer(w.get_config(ci), layer)
+    ci, layer, coef_bits = args
+    return gen_layer(w.get_config(ci).with_(coef_bits=coef_bits), layer)
 
 
 def algorithmic_layer_bytes(cfg, counts: np.ndarray, app_tier: Optional[np.ndarray] = None) -> int:
@@ -244,7 +262,7 @@ def algorithmic_layer_bytes(cfg, counts: np.ndarray, app_tier: Optional[np.ndarr
     sequence shares them), and -- with an append -- the appended token of each
     (sequence, KV head) at its tier's size.  Queries, outputs, split partials
     and padding are not counted."""
-    per_tok = np.array([w.compressed_bytes_per_token(r, s, cfg.resid_bits)
+    per_tok = np.array([w.compressed_bytes_per_token(r, s, cfg.resid_bits, cfg.coef_bits)
                         for r, s in zip(cfg.tier_rank, cfg.resid_per_tier)])
     tok = float((counts.reshape(-1, cfg.num_tiers) * per_tok[None, :]).sum())
     bases = 2 * cfg.num_kv_heads * cfg.r_max * cfg.head_dim * 2
@@ -259,7 +277,7 @@ def stored_traffic(workload: str):
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    sha = hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()
+    sha = decode_source_sha()
     if rec.get("decode_source_sha256") != sha:
         return None
     return rec.get("hbm_bytes_per_launch")
@@ -420,9 +438,9 @@ def main():
     if args.gpus != 1 or world != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}), flush=True)
         sys.exit(2)
-    cfg = w.get_config(args.config)
+    cfg = w.get_config(args.config).with_(coef_bits=args.coef_bits)
     if args.pmc_summary:
-        pmc_summary(cfg.name, *args.pmc_summary, bench_json=args.bench_json)
+        pmc_summary(workload_name(cfg), *args.pmc_summary, bench_json=args.bench_json)
         return
     if args.trace_summary:
         trace_summary(cfg, args.config, args.trace_summary, args.bench_json)
@@ -439,7 +457,7 @@ def main():
     t0 = time.perf_counter()
     workers = min(16, len(os.sched_getaffinity(0)))
     ex = ProcessPoolExecutor(max_workers=workers)
-    layer_iter = ex.map(_gen_layer_job, [(args.config, l) for l in range(L)])
+    layer_iter = ex.map(_gen_layer_job, [(args.config, l, cfg.coef_bits) for l in range(L)])
     bases = make_bases(cfg)
     appends = [[gen_append_inputs(cfg, l, s, bases) for l in range(L)] for s in range(W + K)]
     queries = np.stack([gen_query(cfg, l) for l in range(L)])
@@ -453,7 +471,7 @@ def main():
     cap = [int(c) + extra for c in max_tier_counts(cfg)]
     cache = CompressedKVCache(L, cfg.layers_per_group, cfg.num_q_heads, H, cfg.head_dim, cfg.r_max,
                               cfg.tier_rank, cfg.resid_per_tier, cfg.resid_bits, B, cap,
-                              cfg.n_tokens + extra, decode_splits=args.splits)
+                              cfg.n_tokens + extra, decode_splits=args.splits, coef_bits=cfg.coef_bits)
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
     for m in range(cfg.num_groups):
         cache.set_basis(m, dev(bases["K"][m]), dev(bases["V"][m]))
@@ -592,7 +610,7 @@ def main():
         launch_source = "replays of one step's decode launches"
     bytes_per_launch = float(np.mean(layer_bytes))
     kernel_name = "decode_kernel"
-    traffic = stored_traffic(cfg.name)
+    traffic = stored_traffic(workload_name(cfg))
     if unfused:
         # the dense decode over the materialised layer: its dense bytes
         mean_launch_ms = breakdown["dense_decode_us"] * 1e-3
@@ -617,12 +635,15 @@ def main():
         "dtype": "fp16 MFMA operands, fp32 accumulate",
         "data": "synthetic",
         "config": {
-            "workload": cfg.name, "batch": B, "context": cfg.n_tokens, "layers": L,
+            "workload": workload_name(cfg), "batch": B, "context": cfg.n_tokens, "layers": L,
             "q_heads": cfg.num_q_heads, "kv_heads": H, "head_dim": cfg.head_dim,
             "layers_per_basis": cfg.layers_per_group, "r_max": cfg.r_max,
             "tier_rank": list(cfg.tier_rank), "tier_mix": list(cfg.tier_prob),
             "resid_channels": cfg.resid_channels, "resid_bits": cfg.resid_bits,
-            "storage": "fp16 coefficients, uint8 channel indices, packed codes, fp16 scales",
+            "storage": ("fp16 coefficients" if cfg.coef_bits == 16 else
+                        "8-bit blockwise coefficients (int8 codes, fp16 block scale per token)")
+                       + ", uint8 channel indices, packed codes, fp16 scales",
+            "coef_bits": cfg.coef_bits,
             "graph_replay": bool(graphs), "decode_splits": cache.splits,
             "launches_per_layer": 3 if unfused else 2 if args.separate else 1,
             **({"comparator": "unfused"} if unfused else {}),

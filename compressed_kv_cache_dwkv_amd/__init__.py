@@ -58,6 +58,7 @@ class dwkv_config(ctypes.Structure):
         ("resid_bits", ctypes.c_int32), ("max_batch", ctypes.c_int32),
         ("decode_splits", ctypes.c_int32),
         ("tier_capacity", ctypes.c_int64 * MAX_TIERS), ("max_tokens", ctypes.c_int64),
+        ("coef_bits", ctypes.c_int32),
     ]
 
 
@@ -68,6 +69,7 @@ class dwkv_logical_layer(ctypes.Structure):
         ("idxK", ctypes.c_void_p), ("idxV", ctypes.c_void_p),
         ("valK", ctypes.c_void_p), ("valV", ctypes.c_void_p),
         ("scaleK", ctypes.c_void_p), ("scaleV", ctypes.c_void_p),
+        ("cscaleK", ctypes.c_void_p), ("cscaleV", ctypes.c_void_p),
     ]
 
 
@@ -160,7 +162,7 @@ def _ptr(t, dtype=None, shape=None, name="tensor") -> int:
 def make_config(num_layers: int, layers_per_group: int, num_q_heads: int, num_kv_heads: int,
                 head_dim: int, r_max: int, tier_rank: Sequence[int], tier_resid: Sequence[int],
                 resid_bits: int, max_batch: int, tier_capacity: Sequence[int], max_tokens: int,
-                decode_splits: int = 0) -> dwkv_config:
+                decode_splits: int = 0, coef_bits: int = 16) -> dwkv_config:
     c = dwkv_config()
     c.num_layers, c.layers_per_group = num_layers, layers_per_group
     c.num_q_heads, c.num_kv_heads, c.head_dim, c.r_max = num_q_heads, num_kv_heads, head_dim, r_max
@@ -173,6 +175,7 @@ def make_config(num_layers: int, layers_per_group: int, num_q_heads: int, num_kv
         c.tier_capacity[k] = int(tier_capacity[k])
     c.resid_bits, c.max_batch, c.decode_splits = resid_bits, max_batch, decode_splits
     c.max_tokens = int(max_tokens)
+    c.coef_bits = int(coef_bits)
     return c
 
 
@@ -213,7 +216,10 @@ def _logical(lay: Dict[str, object]) -> dwkv_logical_layer:
     L.n_max = int(lay["tier"].shape[-1])
     L.tier = _ptr(lay["tier"], torch.uint8, name="tier")
     for z in "KV":
-        setattr(L, "coef" + z, _ptr(lay["coef" + z], torch.float16, name="coef" + z))
+        ct = lay["coef" + z]
+        setattr(L, "coef" + z, _ptr(ct, torch.int8 if ct.dtype == torch.int8 else torch.float16, name="coef" + z))
+        if "cscale" + z in lay:
+            setattr(L, "cscale" + z, _ptr(lay["cscale" + z], torch.float16, name="cscale" + z))
         setattr(L, "idx" + z, _ptr(lay["idx" + z], torch.uint8, name="idx" + z))
         setattr(L, "val" + z, _ptr(lay["val" + z], torch.int8, name="val" + z))
         setattr(L, "scale" + z, _ptr(lay["scale" + z], torch.float16, name="scale" + z))

@@ -21,10 +21,11 @@ class CompressedKVCache:
     def __init__(self, num_layers: int, layers_per_group: int, num_q_heads: int, num_kv_heads: int,
                  head_dim: int, r_max: int, tier_rank: Sequence[int], tier_resid: Sequence[int],
                  resid_bits: int, max_batch: int, tier_capacity: Sequence[int], max_tokens: int,
-                 decode_splits: int = 0, device: str = "cuda"):
+                 decode_splits: int = 0, device: str = "cuda", coef_bits: int = 16):
         self.cfg = make_config(num_layers, layers_per_group, num_q_heads, num_kv_heads, head_dim,
                                r_max, tier_rank, tier_resid, resid_bits, max_batch, tier_capacity,
-                               max_tokens, decode_splits)
+                               max_tokens, decode_splits, coef_bits)
+        self.coef_bits = coef_bits
         self.device = torch.device(device)
         self.num_layers, self.num_q_heads, self.num_kv_heads = num_layers, num_q_heads, num_kv_heads
         self.head_dim, self.r_max, self.num_tiers = head_dim, r_max, len(tier_rank)
@@ -59,7 +60,10 @@ class CompressedKVCache:
         dev = self.device
         dst = {"tier": torch.zeros((B, H, n_max), dtype=torch.uint8, device=dev)}
         for z in "KV":
-            dst["coef" + z] = torch.zeros((B, H, n_max, R), dtype=torch.float16, device=dev)
+            dst["coef" + z] = torch.zeros((B, H, n_max, R), dtype=torch.float16 if self.coef_bits == 16 else torch.int8,
+                                          device=dev)
+            if self.coef_bits == 8:
+                dst["cscale" + z] = torch.zeros((B, H, n_max), dtype=torch.float16, device=dev)
             dst["idx" + z] = torch.zeros((B, H, n_max, S), dtype=torch.uint8, device=dev)
             dst["val" + z] = torch.zeros((B, H, n_max, S), dtype=torch.int8, device=dev)
             dst["scale" + z] = torch.zeros((B, H, n_max), dtype=torch.float16, device=dev)

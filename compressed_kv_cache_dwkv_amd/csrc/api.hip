@@ -54,6 +54,8 @@ int build_layout(const dwkv_config *c, Layout *ly)
     if (c->resid_bits != 4 && c->resid_bits != 8) return DWKV_ERR_UNSUPPORTED;
     if (c->max_tokens >= (int64_t(1) << 31)) return DWKV_ERR_UNSUPPORTED;
     if (c->decode_splits > kMaxSplits) return DWKV_ERR_UNSUPPORTED;
+    if (c->coef_bits != 0 && c->coef_bits != 8 && c->coef_bits != 16) return DWKV_ERR_UNSUPPORTED;
+    if (c->coef_bits == 8 && c->r_max > 64) return DWKV_ERR_UNSUPPORTED;
     int prev = 0, smax = 0;
     for (int k = 0; k < c->num_tiers; ++k) {
         int r = c->tier_rank[k], s = c->tier_resid[k];
@@ -79,6 +81,8 @@ int build_layout(const dwkv_config *c, Layout *ly)
     ly->s_max = smax;
     ly->qmax = c->resid_bits == 4 ? 7 : 127;
     ly->num_groups = (c->num_layers + c->layers_per_group - 1) / c->layers_per_group;
+    ly->cb = c->coef_bits == 8 ? 1 : 2;
+    const int cb = ly->cb;
     ly->max_tokens = c->max_tokens;
 
     int64_t blk = 0;
@@ -93,18 +97,20 @@ int build_layout(const dwkv_config *c, Layout *ly)
         ly->istride[k] = is;
         ly->vstride[k] = vs;
         ly->cap[k] = c->tier_capacity[k];
-        ly->weight[k] = 4 * r + (s > 0 ? 2 * (is + vs + 2) : 0);
+        ly->weight[k] = 2 * cb * r + (cb == 1 ? 4 : 0) + (s > 0 ? 2 * (is + vs + 2) : 0);
         ly->cost[k] = token_cost(r, c->r_max);
         ly->inv_cblk[k] = 1.0 / (16.0 * ly->cost[k]);
         blk = align_up(blk, 256);
-        ly->f_coefK[k] = blk; blk = align_up(blk + cap * r * 2, 16);
-        ly->f_coefV[k] = blk; blk = align_up(blk + cap * r * 2, 16);
+        ly->f_coefK[k] = blk; blk = align_up(blk + cap * r * cb, 16);
+        ly->f_coefV[k] = blk; blk = align_up(blk + cap * r * cb, 16);
         ly->f_idxK[k] = blk;  blk = align_up(blk + cap * is, 16);
         ly->f_idxV[k] = blk;  blk = align_up(blk + cap * is, 16);
         ly->f_valK[k] = blk;  blk = align_up(blk + cap * vs, 16);
         ly->f_valV[k] = blk;  blk = align_up(blk + cap * vs, 16);
         ly->f_scaleK[k] = blk; blk = align_up(blk + (s > 0 ? cap * 2 : 0), 16);
         ly->f_scaleV[k] = blk; blk = align_up(blk + (s > 0 ? cap * 2 : 0), 16);
+        ly->f_cscK[k] = blk; blk = align_up(blk + (cb == 1 ? cap * 2 : 0), 16);
+        ly->f_cscV[k] = blk; blk = align_up(blk + (cb == 1 ? cap * 2 : 0), 16);
     }
     // 16 spare bytes: fixed-width residual reads may run past the last token
     ly->head_block = align_up(blk + 16, 256);
@@ -124,7 +130,9 @@ int build_layout(const dwkv_config *c, Layout *ly)
         t.istride = ly->istride[k];
         t.vstride = ly->vstride[k];
         t.weight = ly->weight[k];
-        t.pad0 = t.pad1 = t.pad2 = 0;
+        t.cscK = (int32_t)ly->f_cscK[k];
+        t.cscV = (int32_t)ly->f_cscV[k];
+        t.pad2 = 0;
     }
     const int64_t heads = (int64_t)ly->L * ly->Bmax * ly->Hkv;
     int64_t off = 0;
@@ -326,12 +334,13 @@ int dwkv_set_basis(dwkv_handle *h, int group, const void *basisK, const void *ba
     return hip_status(e);
 }
 
-static bool logical_ok(const dwkv_logical_layer *L, int s_max)
+static bool logical_ok(const dwkv_logical_layer *L, int s_max, int cb)
 {
     if (!L || L->n_max < 0) return false;
     if (!L->tier || !L->coefK || !L->coefV) return false;
     if (s_max > 0 && (!L->idxK || !L->idxV || !L->valK || !L->valV || !L->scaleK || !L->scaleV))
         return false;
+    if (cb == 1 && (!L->cscaleK || !L->cscaleV)) return false;
     return true;
 }
 
@@ -341,7 +350,7 @@ int dwkv_import_layer(dwkv_handle *h, int layer, const dwkv_logical_layer *src,
     if (!valid_handle(h) || !n_tokens) return DWKV_ERR_INVALID_ARG;
     const Layout &ly = h->ly;
     if (layer < 0 || layer >= ly.L || batch <= 0 || batch > ly.Bmax) return DWKV_ERR_INVALID_ARG;
-    if (!logical_ok(src, ly.s_max)) return DWKV_ERR_INVALID_ARG;
+    if (!logical_ok(src, ly.s_max, ly.cb)) return DWKV_ERR_INVALID_ARG;
     for (int b = 0; b < batch; ++b) {
         if (n_tokens[b] < 0 || n_tokens[b] > src->n_max) return DWKV_ERR_INVALID_ARG;
         if (n_tokens[b] > ly.max_tokens) return DWKV_ERR_CAPACITY;
@@ -360,7 +369,7 @@ int dwkv_export_layer(dwkv_handle *h, int layer, const dwkv_logical_layer *dst, 
     if (!valid_handle(h) || !counts) return DWKV_ERR_INVALID_ARG;
     const Layout &ly = h->ly;
     if (layer < 0 || layer >= ly.L || batch <= 0 || batch > ly.Bmax) return DWKV_ERR_INVALID_ARG;
-    if (!logical_ok(dst, ly.s_max)) return DWKV_ERR_INVALID_ARG;
+    if (!logical_ok(dst, ly.s_max, ly.cb)) return DWKV_ERR_INVALID_ARG;
     hipStream_t s = static_cast<hipStream_t>(stream);
     return hip_status(dwkv::launch_export(ly, h->arena, layer, *dst, counts, slots, batch, s));
 }

@@ -174,22 +174,56 @@ __device__ __forceinline__ int append_encode(const AppendRegs<D> &st, const Layo
     for (int q = 0; q < NJ; ++q) sx[lane + q * kWave] = st.xv[q];
     wave_fence();
 
-    // 1. coefficients c_i = fp16(sum_j B[i][j] x_j), sequential in j (x read
-    //    from LDS, the same address in every lane)
-    uint16_t *cdst = reinterpret_cast<uint16_t *>(blk + (z ? ly.f_coefV[k] : ly.f_coefK[k]));
+    // 1. coefficient sums sum_j B[i][j] x_j, sequential in j (x read from
+    //    LDS, the same address in every lane), then stored as fp16, or in the
+    //    8-bit blockwise form: block scale fp16(max |sum| / 127), codes
+    //    rint(sum / scale) in [-127, 127] (0 for a zero scale); step 2 then
+    //    uses the stored values (code * scale is exact in fp32)
+    float acc1[2] = {0.0f, 0.0f};
 #pragma unroll
     for (int rr = 0; rr < 2; ++rr) {
         if (rr * kWave < r) {
             float acc = 0.0f;
 #pragma unroll
             for (int j = 0; j < D; ++j) acc = __builtin_fmaf(half_at<D>(st.brow[rr], j), sx[j], acc);
+            acc1[rr] = as_fp32(acc);
+        }
+    }
+    const int64_t coff = z ? ly.f_coefV[k] : ly.f_coefK[k];
+    if (ly.cb == 2) {
+        uint16_t *cdst = reinterpret_cast<uint16_t *>(blk + coff);
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr) {
             const int i = lane + rr * kWave;
-            const uint16_t c16 = f2h(as_fp32(acc));
             if (i < r) {
+                const uint16_t c16 = f2h(acc1[rr]);
                 cdst[z ? coefV_index(r, slot, i) : (int64_t)slot * r + i] = c16;
                 sc[i] = h2f(c16);
             }
         }
+    } else {
+        int8_t *cdst = reinterpret_cast<int8_t *>(blk + coff);
+        float a = 0.0f;
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr)
+            if (lane + rr * kWave < r) a = fmaxf(a, fabsf(acc1[rr]));
+        a = wave_max(a);
+        const uint16_t cs16 = f2h(__fdiv_rn(a, 127.0f));
+        const float sf = h2f(cs16);
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr) {
+            const int i = lane + rr * kWave;
+            if (i < r) {
+                float qv = 0.0f;
+                if (sf != 0.0f) {
+                    qv = rintf(__fdiv_rn(acc1[rr], sf));
+                    qv = fminf(fmaxf(qv, -127.0f), 127.0f);
+                }
+                cdst[z ? coefV_index(r, slot, i) : (int64_t)slot * r + i] = static_cast<int8_t>(qv);
+                sc[i] = qv * sf;
+            }
+        }
+        if (lane == 0) reinterpret_cast<uint16_t *>(blk + (z ? ly.f_cscV[k] : ly.f_cscK[k]))[slot] = cs16;
     }
     wave_fence();
 

@@ -331,6 +331,7 @@ __global__ __launch_bounds__(kMBlock) void materialize_kernel(Layout ly, uint8_t
     __shared__ __attribute__((aligned(16))) uint16_t s_c[kMTok * CS];    // coefficients [token][rank]
     __shared__ __attribute__((aligned(16))) float s_out[kMTok * OS];     // reconstruction [token][channel]
     __shared__ int s_tier[kMTok], s_slot[kMTok];
+    __shared__ float s_cs[kMTok];                                        // 8-bit form: block scales
     const int64_t p0 = (int64_t)blockIdx.x * kMTok;
     const int h = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
@@ -352,8 +353,28 @@ __global__ __launch_bounds__(kMBlock) void materialize_kernel(Layout ly, uint8_t
     for (int z = 0; z < 2; ++z) {
         __syncthreads();
         // coefficients of the 64 positions (zero past each token's rank):
-        // K rows in 4-element pieces, V (16-token blocks) element by element
-        if (z == 0) {
+        // K rows in 4-element pieces, V (16-token blocks) element by element;
+        // 8-bit codes go in as exact fp16 values and their block scales
+        // multiply the products' rows
+        if (ly.cb == 1) {
+            if (tid < kMTok) {
+                const int k = s_tier[tid];
+                s_cs[tid] = k >= 0 && k < ly.T
+                                ? h2f(reinterpret_cast<const uint16_t *>(blk + (z ? ly.f_cscV[k] : ly.f_cscK[k]))[s_slot[tid]])
+                                : 0.0f;
+            }
+            for (int e = tid; e < kMTok * RM; e += kMBlock) {
+                const int t = e / RM, i = e % RM;
+                const int k = s_tier[t];
+                _Float16 c = (_Float16)0.0f;
+                if (k >= 0 && k < ly.T && i < ly.rank[k]) {
+                    const int8_t *src = reinterpret_cast<const int8_t *>(blk + (z ? ly.f_coefV[k] : ly.f_coefK[k]));
+                    const int r = ly.rank[k];
+                    c = (_Float16)(float)(z ? src[coefV_index(r, s_slot[t], i)] : src[(int64_t)s_slot[t] * r + i]);
+                }
+                s_c[t * CS + i] = __builtin_bit_cast(uint16_t, c);
+            }
+        } else if (z == 0) {
             for (int e = tid; e < kMTok * (RM / 4); e += kMBlock) {
                 const int t = e / (RM / 4), i4 = 4 * (e % (RM / 4));
                 const int k = s_tier[t];
@@ -398,7 +419,10 @@ __global__ __launch_bounds__(kMBlock) void materialize_kernel(Layout ly, uint8_t
                     acc = mma32(av, cat(lo, hi), acc);
                 }
 #pragma unroll
-                for (int j = 0; j < 4; ++j) s_out[(16 * wave + 4 * g + j) * OS + 16 * cb + c16] = acc[j];
+                for (int j = 0; j < 4; ++j) {
+                    const int tr = 16 * wave + 4 * g + j;
+                    s_out[tr * OS + 16 * cb + c16] = ly.cb == 1 ? acc[j] * s_cs[tr] : acc[j];
+                }
             }
         }
         __syncthreads();

@@ -57,13 +57,26 @@ __global__ __launch_bounds__(kBlock) void import_kernel(Layout ly, uint8_t *aren
                 const int r = ly.rank[k], s = ly.resid[k], vb = ly.vbytes[k];
                 const int is = ly.istride[k], vs = ly.vstride[k];
                 const int64_t tr = row0 + t;
-                const uint16_t *ck = static_cast<const uint16_t *>(src.coefK) + tr * ly.R;
-                const uint16_t *cv = static_cast<const uint16_t *>(src.coefV) + tr * ly.R;
-                uint16_t *dk = reinterpret_cast<uint16_t *>(blk + ly.f_coefK[k]) + (int64_t)slot * r;
-                uint16_t *dv = reinterpret_cast<uint16_t *>(blk + ly.f_coefV[k]);
-                for (int i = 0; i < r; ++i) {
-                    dk[i] = ck[i];
-                    dv[coefV_index(r, slot, i)] = cv[i];
+                if (ly.cb == 2) {
+                    const uint16_t *ck = static_cast<const uint16_t *>(src.coefK) + tr * ly.R;
+                    const uint16_t *cv = static_cast<const uint16_t *>(src.coefV) + tr * ly.R;
+                    uint16_t *dk = reinterpret_cast<uint16_t *>(blk + ly.f_coefK[k]) + (int64_t)slot * r;
+                    uint16_t *dv = reinterpret_cast<uint16_t *>(blk + ly.f_coefV[k]);
+                    for (int i = 0; i < r; ++i) {
+                        dk[i] = ck[i];
+                        dv[coefV_index(r, slot, i)] = cv[i];
+                    }
+                } else {
+                    const int8_t *ck = static_cast<const int8_t *>(src.coefK) + tr * ly.R;
+                    const int8_t *cv = static_cast<const int8_t *>(src.coefV) + tr * ly.R;
+                    int8_t *dk = reinterpret_cast<int8_t *>(blk + ly.f_coefK[k]) + (int64_t)slot * r;
+                    int8_t *dv = reinterpret_cast<int8_t *>(blk + ly.f_coefV[k]);
+                    for (int i = 0; i < r; ++i) {
+                        dk[i] = ck[i];
+                        dv[coefV_index(r, slot, i)] = cv[i];
+                    }
+                    reinterpret_cast<uint16_t *>(blk + ly.f_cscK[k])[slot] = static_cast<const uint16_t *>(src.cscaleK)[tr];
+                    reinterpret_cast<uint16_t *>(blk + ly.f_cscV[k])[slot] = static_cast<const uint16_t *>(src.cscaleV)[tr];
                 }
                 if (s > 0) {
                     for (int z = 0; z < 2; ++z) {
@@ -136,13 +149,26 @@ __global__ __launch_bounds__(kBlock) void export_kernel(Layout ly, uint8_t *aren
         const int64_t tr = row0 + t;
         static_cast<uint8_t *>(dst.tier)[tr] = static_cast<uint8_t>(k);
         if (slots) slots[tr] = slot;
-        const uint16_t *sk = reinterpret_cast<const uint16_t *>(blk + ly.f_coefK[k]) + (int64_t)slot * r;
-        const uint16_t *sv = reinterpret_cast<const uint16_t *>(blk + ly.f_coefV[k]);
-        uint16_t *ck = static_cast<uint16_t *>(dst.coefK) + tr * ly.R;
-        uint16_t *cv = static_cast<uint16_t *>(dst.coefV) + tr * ly.R;
-        for (int i = 0; i < ly.R; ++i) {
-            ck[i] = i < r ? sk[i] : 0;
-            cv[i] = i < r ? sv[coefV_index(r, slot, i)] : 0;
+        if (ly.cb == 2) {
+            const uint16_t *sk = reinterpret_cast<const uint16_t *>(blk + ly.f_coefK[k]) + (int64_t)slot * r;
+            const uint16_t *sv = reinterpret_cast<const uint16_t *>(blk + ly.f_coefV[k]);
+            uint16_t *ck = static_cast<uint16_t *>(dst.coefK) + tr * ly.R;
+            uint16_t *cv = static_cast<uint16_t *>(dst.coefV) + tr * ly.R;
+            for (int i = 0; i < ly.R; ++i) {
+                ck[i] = i < r ? sk[i] : 0;
+                cv[i] = i < r ? sv[coefV_index(r, slot, i)] : 0;
+            }
+        } else {
+            const int8_t *sk = reinterpret_cast<const int8_t *>(blk + ly.f_coefK[k]) + (int64_t)slot * r;
+            const int8_t *sv = reinterpret_cast<const int8_t *>(blk + ly.f_coefV[k]);
+            int8_t *ck = static_cast<int8_t *>(dst.coefK) + tr * ly.R;
+            int8_t *cv = static_cast<int8_t *>(dst.coefV) + tr * ly.R;
+            for (int i = 0; i < ly.R; ++i) {
+                ck[i] = i < r ? sk[i] : 0;
+                cv[i] = i < r ? sv[coefV_index(r, slot, i)] : 0;
+            }
+            static_cast<uint16_t *>(dst.cscaleK)[tr] = reinterpret_cast<const uint16_t *>(blk + ly.f_cscK[k])[slot];
+            static_cast<uint16_t *>(dst.cscaleV)[tr] = reinterpret_cast<const uint16_t *>(blk + ly.f_cscV[k])[slot];
         }
         if (ly.s_max == 0) continue;
         for (int z = 0; z < 2; ++z) {

@@ -68,6 +68,12 @@ hipError_t launch_materialize(const Layout &ly, uint8_t *arena, int layer, int b
 hipError_t launch_probe_error(const float *o_ref, const float *o_cmp, int nq, int B, int Hq, int Hkv, int d, float eps,
                               float *err, hipStream_t stream);
 
+// The decode kernel's instances for 8-bit blockwise coefficients (ly.cb == 1);
+// qscale is softmax_scale * log2(e).
+hipError_t launch_decode8(const Layout &ly, uint8_t *arena, int layer, const uint16_t *q, int batch, float qscale,
+                          float *out, const DecodeWorkspace &ws, int splits, const AppendArgs &ap,
+                          hipStream_t stream);
+
 hipError_t launch_append(const Layout &ly, uint8_t *arena, int layer, const void *k,
                          const void *v, const void *tier, const void *gateK, const void *gateV,
                          int batch, hipStream_t stream);

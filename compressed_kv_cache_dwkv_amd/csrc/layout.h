@@ -16,7 +16,11 @@
 //                                                      per byte, element 2u in
 //                                                      the low nibble of byte u)
 //   scaleK [cap] fp16       scaleV [cap] fp16         (absent when s_k == 0)
+//   cscaleK [cap] fp16      cscaleV [cap] fp16        (8-bit coefficients only:
+//                                                      each token's block scale)
 //
+// With 8-bit blockwise coefficients coefK and coefV hold int8 codes in the
+// same arrangement (one byte per coefficient).
 // where is_k and vs_k are the s_k index bytes and s_k * bits / 8 code bytes
 // of a token rounded up to whole 4-byte words (no rounding for the usual
 // s_k = 4 or 8 with 8-bit, s_k = 8 with 4-bit codes), so a run of tokens of
@@ -55,11 +59,12 @@ constexpr int kMaxSplits = 256;   // decode workgroups per (sequence, KV head)
 // start of a (layer, sequence, KV head) block, and the tier's shape.
 struct TierDesc {
     int32_t coefK, coefV, idxK, idxV, valK, valV, scaleK, scaleV;
-    int32_t rank, resid, istride, vstride, weight, pad0, pad1, pad2;
+    int32_t rank, resid, istride, vstride, weight, cscK, cscV, pad2;
 };
 
 struct Layout {
     int32_t L, G, Hq, Hkv, d, R, T, bits, Bmax, gq, s_max, qmax, num_groups;
+    int32_t cb;                  // bytes per stored coefficient: 2 (fp16) or 1 (8-bit codes)
     int32_t rank[kMaxTiers];
     int32_t resid[kMaxTiers];
     int32_t vbytes[kMaxTiers];   // packed code bytes per token
@@ -77,6 +82,7 @@ struct Layout {
     int64_t f_idxK[kMaxTiers], f_idxV[kMaxTiers];
     int64_t f_valK[kMaxTiers], f_valV[kMaxTiers];
     int64_t f_scaleK[kMaxTiers], f_scaleV[kMaxTiers];
+    int64_t f_cscK[kMaxTiers], f_cscV[kMaxTiers];
     int64_t total;
     TierDesc tier[kMaxTiers];    // the same tiers, packed per tier (head blocks < 2 GiB)
 };

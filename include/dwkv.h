@@ -78,6 +78,9 @@ extern "C" {
  * sequence, KV head) reserved for tier k; max_tokens bounds the total tokens
  * per (layer, sequence, KV head).  decode_splits: workgroups per (sequence,
  * KV head) for dwkv_decode_attn, 0 = chosen from the capacities.
+ * coef_bits selects the coefficient form (paper §3, second paragraph:
+ * coefficients are stored in 8-bit blockwise quantised form; one block is
+ * one token's r_k coefficients).
  */
 typedef struct dwkv_config {
     int32_t num_layers;
@@ -94,6 +97,8 @@ typedef struct dwkv_config {
     int32_t decode_splits;
     int64_t tier_capacity[DWKV_MAX_TIERS];
     int64_t max_tokens;
+    int32_t coef_bits;   /* 16 (or 0): fp16 coefficients; 8: the paper's 8-bit blockwise form
+                            (int8 codes in [-127, 127] and one fp16 scale per token and Z) */
 } dwkv_config;
 
 typedef struct dwkv_handle dwkv_handle;
@@ -111,6 +116,10 @@ typedef struct dwkv_handle dwkv_handle;
  *   valV
  *   scaleK fp16  [B][H_kv][n_max]
  *   scaleV
+ * With coef_bits 8, coefK/coefV hold int8 codes [B][H_kv][n_max][r_max] and
+ *   cscaleK fp16  [B][H_kv][n_max]   each token's coefficient block scale
+ *   cscaleV
+ * (unused, may be NULL, with fp16 coefficients).
  */
 typedef struct dwkv_logical_layer {
     int64_t n_max;
@@ -119,6 +128,7 @@ typedef struct dwkv_logical_layer {
     void *idxK, *idxV;
     void *valK, *valV;
     void *scaleK, *scaleV;
+    void *cscaleK, *cscaleV;
 } dwkv_logical_layer;
 
 /* Bytes of device memory one cache needs (host only, no GPU call). */

@@ -28,7 +28,7 @@ def make_cache(cfg: Config, capacity=None, extra: int = 16, splits: int = 0,
     return CompressedKVCache(
         cfg.num_layers, cfg.layers_per_group, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim,
         cfg.r_max, cfg.tier_rank, cfg.resid_per_tier, cfg.resid_bits, cfg.batch, capacity,
-        max_tokens if max_tokens is not None else n + extra, splits)
+        max_tokens if max_tokens is not None else n + extra, splits, coef_bits=cfg.coef_bits)
 
 
 def load_bases(cache, bases: Dict[str, np.ndarray], groups: Optional[Iterable[int]] = None):

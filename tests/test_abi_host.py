@@ -47,6 +47,18 @@ def test_config_validation(field, value, code):
     assert _rc_arena(cfg) == code
 
 
+def test_coefficient_form_validation_and_size():
+    """coef_bits 16 (or 0) and 8; 8-bit codes only with bases of at most 64
+    vectors; the 8-bit arena holds r + 2 bytes per token and Z instead of 2 r."""
+    assert _rc_arena(_cfg(coef_bits=7)) == d.DWKV_ERR_UNSUPPORTED
+    assert _rc_arena(_cfg(coef_bits=8, r_max=128, tier_rank=(8, 16, 32, 128))) == d.DWKV_ERR_UNSUPPORTED
+    cap = (40000, 20000, 10000, 7000)
+    a16 = d.dwkv_arena_bytes(_cfg(tier_capacity=cap, max_tokens=1, max_batch=1))
+    a8 = d.dwkv_arena_bytes(_cfg(tier_capacity=cap, max_tokens=1, max_batch=1, coef_bits=8))
+    saved = 32 * 8 * sum(c * (2 * 2 * r - (2 * r + 4)) for c, r in zip(cap, (8, 16, 32, 64)))
+    assert abs((a16 - a8) - saved) <= 32 * 8 * 2048        # per-array alignment of the head blocks
+
+
 def test_tier_table_validation():
     assert _rc_arena(_cfg(tier_rank=(16, 8, 32, 64))) == d.DWKV_ERR_INVALID_ARG     # descending
     assert _rc_arena(_cfg(tier_rank=(16, 16, 16, 16), tier_resid=(0, 2, 4, 8))) == d.DWKV_OK   # fixed r_b, routed s

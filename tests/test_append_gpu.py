@@ -32,10 +32,15 @@ def _compare_token(cfg, exported, slots, counts_before, pos, enc, tier):
             assert slots[b, h, pos] == counts_before[b, h, k], "slot must be the tier's old count"
             r, s = cfg.tier_rank[k], cfg.resid_per_tier[k]
             for z in "KV":
-                got_c = exported["coef" + z][b, h, pos].view(np.uint16)
-                ref_c = enc["coef" + z][b, h].view(np.uint16)
+                got_c = exported["coef" + z][b, h, pos]
+                ref_c = enc["coef" + z][b, h]
+                got_c = got_c.view(np.uint16) if got_c.dtype == np.float16 else got_c.view(np.uint8)
+                ref_c = ref_c.view(np.uint16) if ref_c.dtype == np.float16 else ref_c.view(np.uint8)
                 assert np.array_equal(got_c[:r], ref_c[:r]), f"coef{z} (b={b},h={h})"
                 assert not got_c[r:].any()
+                if "cscale" + z in enc:
+                    assert exported["cscale" + z][b, h, pos].view(np.uint16) == \
+                        enc["cscale" + z][b, h].view(np.uint16), f"cscale{z}"
                 assert np.array_equal(exported["idx" + z][b, h, pos, :s], enc["idx" + z][b, h, :s])
                 assert np.array_equal(exported["val" + z][b, h, pos, :s], enc["val" + z][b, h, :s])
                 if s > 0:
@@ -128,6 +133,35 @@ def test_append_paper_literal_tiers(G):
                       tier_resid=(0, 2, 4, 8), resid_channels=8, resid_bits=4, n_tokens=64)
     cache, _, _ = _append_steps(G, cfg, steps=5, n0=64)
     cache.close()
+
+
+@pytest.mark.parametrize("ci", [0, 1])
+def test_append_bit_exact_8bit_coefficients(G, ci):
+    """The 8-bit blockwise coefficient form: codes, block scale, kept
+    channels, residual codes and scale, bit for bit."""
+    cfg = w.get_config(ci).with_(coef_bits=8)
+    cfg = cfg.with_(batch=16) if ci == 1 else cfg
+    cache, _, _ = _append_steps(G, cfg, steps=6, n0=200, gates=ci == 1)
+    cache.close()
+
+
+def test_import_export_round_trip_8bit_coefficients(G):
+    cfg = w.get_config(1).with_(batch=2, coef_bits=8)
+    bases = make_bases(cfg)
+    cache = G.make_cache(cfg, n=3000)
+    try:
+        G.load_bases(cache, bases, groups=[0])
+        lay = gen_layer(cfg, 1, n=3000)
+        lay["n_tokens"][:] = [3000, 1111]
+        G.load_layer(cache, 1, lay)
+        ex, counts, slots = G.export_np(cache, 1, 2, 3000)
+        for b, n in ((0, 3000), (1, 1111)):
+            for key in ("tier", "coefK", "coefV", "cscaleK", "cscaleV", "idxK", "idxV", "valK", "valV", "scaleK",
+                        "scaleV"):
+                assert np.array_equal(ex[key][b, :, :n].view(np.uint8), lay[key][b, :, :n].view(np.uint8)), key
+        assert cache.check_errors() == 0
+    finally:
+        cache.close()
 
 
 def test_append_many_random_vectors(G):

@@ -142,6 +142,21 @@ def test_paper_literal_tiers_fixed_rank_routed_residuals(G, rb, bits):
     _run(G, cfg, layers=(1,), splits=0, needle=True)
 
 
+@pytest.mark.parametrize("ci,variant", [(0, "plain"), (1, "plain"), (4, "plain"), (1, "peaked"), (1, "needle"),
+                                        (2, "full")])
+def test_8bit_blockwise_coefficients(G, ci, variant):
+    """The paper's 8-bit blockwise coefficient form (int8 codes, one fp16
+    block scale per token and Z) in the launch configuration the benchmark
+    would use."""
+    cfg = w.get_config(ci).with_(coef_bits=8)
+    if variant == "full":
+        _run(G, cfg, layers=(5,))
+        return
+    n = cfg.n_tokens if ci == 0 else 5000
+    kw = {"peak": 16.0} if variant == "peaked" else {"needle": True} if variant == "needle" else {}
+    _run(G, cfg, layers=(1, 2) if ci else (0, 1), n=n, **kw)
+
+
 def test_wide_basis_identity_d128(G):
     """B = I with r_max = d = 128: the cache stores K and V directly."""
     cfg = tiny_config(batch=1, num_kv_heads=2, num_q_heads=8, head_dim=128, r_max=128,

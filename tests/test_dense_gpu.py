@@ -57,9 +57,10 @@ def _materialize(G, cache, layer, batch, cfg, n_cap):
     return ko, vo, no
 
 
-@pytest.mark.parametrize("ci,n,ragged", [(0, None, None), (1, 3000, [3000, 1777]), (4, 2000, None)])
-def test_materialize_matches_oracle_within_one_ulp(G, ci, n, ragged):
-    cfg = w.get_config(ci)
+@pytest.mark.parametrize("ci,n,ragged,cb", [(0, None, None, 16), (1, 3000, [3000, 1777], 16), (4, 2000, None, 16),
+                                           (1, 3000, [3000, 1777], 8), (0, None, None, 8)])
+def test_materialize_matches_oracle_within_one_ulp(G, ci, n, ragged, cb):
+    cfg = w.get_config(ci).with_(coef_bits=cb)
     if ragged:
         cfg = cfg.with_(batch=len(ragged))
     n = cfg.n_tokens if n is None else n

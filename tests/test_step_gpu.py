@@ -149,6 +149,14 @@ def test_step_paper_literal_tiers(G):
     _steps(G, cfg, 1800, steps=3, layer=3, splits=4)
 
 
+@pytest.mark.parametrize("ci,n0,splits", [(0, 1024, 3), (1, 1500, 8), (2, 65536, 0)])
+def test_step_8bit_coefficients(G, ci, n0, splits):
+    """The one-launch step with 8-bit blockwise coefficients (the encoder
+    quantises the new token's coefficients in the same launch)."""
+    cfg = w.get_config(ci).with_(coef_bits=8)
+    _steps(G, cfg, n0, steps=2, layer=1, splits=splits)
+
+
 def test_step_on_empty_cache(G):
     """An empty cache: zero output, and the step's token becomes the first."""
     cfg = w.get_config(0)

@@ -99,10 +99,12 @@ def dense_kv_bytes(num_layers: int, num_kv_heads: int, head_dim: int, n_tokens: 
     return 2 * num_layers * num_kv_heads * head_dim * n_tokens * batch * elem_bytes
 
 
-def compressed_bytes_per_token(rank: int, s: int, bits: int) -> float:
+def compressed_bytes_per_token(rank: int, s: int, bits: int, coef_bits: int = 16) -> float:
     """Algorithmic bytes one token occupies per (layer, KV head), K and V
-    together: fp16 coefficients at the routed rank, and per Z a residual block
-    of s uint8 channel indices, s packed values and one fp16 scale (no block
-    at all for a tier that keeps no residual channel)."""
+    together: the coefficients at the routed rank (fp16, or int8 codes plus
+    one fp16 block scale), and per Z a residual block of s uint8 channel
+    indices, s packed values and one fp16 scale (no block at all for a tier
+    that keeps no residual channel)."""
     block = 0 if s == 0 else s + s * bits / 8 + 2
-    return 2 * (2 * rank) + 2 * block
+    coef = 2 * rank if coef_bits == 16 else rank + 2
+    return 2 * coef + 2 * block
