@@ -67,6 +67,9 @@ def _load(path: str):
     L.oracle_append_residual_ex.argtypes = [ctypes.c_int, ctypes.c_int, P, P, ctypes.c_int, ctypes.c_int, P]
     L.oracle_append_projection.restype = ctypes.c_int
     L.oracle_append_projection.argtypes = [ctypes.c_int, ctypes.c_int, P, P, ctypes.c_int, P]
+    L.oracle_encode_tokens.restype = ctypes.c_int
+    L.oracle_encode_tokens.argtypes = [ctypes.c_int, ctypes.c_int, P, ctypes.c_int64, P, P, P, P, ctypes.c_int,
+                                       ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, P, P, P, ctypes.c_int]
     L.oracle_max_threads.restype = ctypes.c_int
     return L
 
@@ -357,3 +360,7 @@ def append_layer(cfg, basisK: np.ndarray, basisV: np.ndarray, k: np.ndarray, v: 
         if cb == 8:
             out["cscale" + z] = cscale
     return out
+
+
+# ------------------------------------------------------------------ prefill
+from .prefill import orth, prefill_bases, prefill_encode, range_finder, window_gram  # noqa: E402,F401

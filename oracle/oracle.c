@@ -27,6 +27,9 @@
  *  oracle_dense_decode -- textbook decode attention over a dense fp16 K/V
  *    cache (the uncompressed baseline).
  *
+ *  oracle_encode_tokens -- the prefill's bulk encoding: each token exactly
+ *    as one oracle_append (below), tokens independent of one another.
+ *
  *  oracle_append -- encoding one new K or V vector into the compressed form
  *    (paper §3 Method, second paragraph: coefficients by projection onto the
  *    current basis; residual kept only on the routed channels, with low-bit
@@ -530,6 +533,45 @@ int oracle_append_projection(int d, int r_max, const uint16_t *basis, const uint
     float e[256];
     project(d, basis, x, r, 16, c16, NULL, NULL, sum_out, e);
     return 0;
+}
+
+/*
+ * Bulk encoding of prefill tokens (paper §3 Method, the data-path paragraph
+ * with Fig. 2: during prefill every cached vector is projected onto its
+ * window's basis and its residual quantised at the routed channel count).
+ * The prefill holds no arithmetic of its own: token u of the count vectors
+ * x[u][d] is encoded exactly as one append (oracle_append_ex) at rank
+ * ranks[u], resid[u] kept channels and gate gates[u] (NULL: a gate of 1).
+ * Outputs per token, at strides r_stride / s_stride: c_out (fp16 bits, or
+ * int8 codes with coef_bits 8), cs_out (block scales, 8-bit form only),
+ * idx_out, val_out, scale_out.  Returns 0, or -1 if any token's arguments
+ * are invalid.
+ */
+int oracle_encode_tokens(int d, int r_max, const uint16_t *basis, int64_t count, const uint16_t *x,
+                         const int32_t *ranks, const int32_t *resid, const uint16_t *gates, int qmax,
+                         int coef_bits, int r_stride, int s_stride, void *c_out, uint16_t *cs_out,
+                         uint8_t *idx_out, int8_t *val_out, uint16_t *scale_out, int nthreads)
+{
+    if (coef_bits != 8 && coef_bits != 16)
+        return -1;
+    const int eb = coef_bits / 8;
+    int bad = 0;
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static) num_threads(nthreads > 0 ? nthreads : 1) reduction(| : bad)
+#endif
+    for (int64_t u = 0; u < count; ++u) {
+        if (ranks[u] > r_stride || resid[u] > s_stride) {
+            bad |= 1;
+            continue;
+        }
+        uint8_t *c = (uint8_t *)c_out + u * r_stride * eb;
+        const int rc = oracle_append_ex(d, r_max, basis, x + u * d, ranks[u], resid[u], qmax,
+                                        gates ? gates[u] : (uint16_t)0x3c00, coef_bits, c,
+                                        cs_out ? cs_out + u : NULL, idx_out + u * s_stride,
+                                        val_out + u * s_stride, scale_out + u);
+        bad |= rc != 0;
+    }
+    return bad ? -1 : 0;
 }
 
 int oracle_max_threads(void)

@@ -23,9 +23,14 @@ from .gen import (
     gen_append_inputs,
     layer_bases,
     empty_layer,
+    gen_prefill,
+    gen_sketch,
+    gen_tiers,
+    gen_gates,
 )
 
 __all__ = [
     "Config", "CONFIGS", "get_config", "dense_kv_bytes", "compressed_bytes_per_token",
     "make_bases", "gen_layer", "gen_query", "gen_append_inputs", "layer_bases", "empty_layer",
+    "gen_prefill", "gen_sketch", "gen_tiers", "gen_gates",
 ]

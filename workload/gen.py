@@ -19,6 +19,18 @@ Distributions (per workload configuration):
   * residual: s distinct uniform channels (ascending), integer values uniform
     on [-qmax, qmax], scale = fp16(0.01 |N(0,1)|).
   * queries: fp16 N(0,1).
+  * prefill keys and values (the input of the prefill compression): per
+    (depth group m, KV head h, Z) a random orthogonal d x d matrix U (QR of a
+    Gaussian, diag(R) > 0) and a geometric spectrum sigma_i = decay^i (decay
+    0.93 for K, 0.96 for V); each layer of the group scales it by its own
+    exp(0.1 N(0,1)) per channel, and token t is U (sigma_l * g_t) plus an
+    isotropic N(0, noise^2) floor (noise 0.02), g_t ~ N(0, I), rounded to
+    fp16.  Neighbouring layers thus share a dominant channel subspace with
+    layer-specific deviations.  Positions at or beyond a sequence's length
+    hold the `tail` value.
+  * the range finder's Gaussian sketch: N(0,1) fp32 [d][k] per (m, Z, h).
+  * prefill gates: per token fp16, 1.0 with probability 0.3, else uniform
+    on [0.25, 1).
 """
 from __future__ import annotations
 
@@ -31,7 +43,8 @@ from .configs import Config
 _FIELDS = {
     "basis": 1, "tier": 2, "skewpos": 3, "coef": 4, "idx": 5, "val": 6, "scale": 7,
     "query": 8, "app_tier": 9, "app_coef": 10, "app_idx": 11, "app_val": 12,
-    "app_scale": 13, "needle": 14, "cscale": 15,
+    "app_scale": 13, "needle": 14, "cscale": 15, "pf_rot": 16, "pf_spec": 17, "pf_x": 18,
+    "pf_noise": 19, "pf_omega": 20, "pf_gate": 21,
 }
 
 
@@ -273,3 +286,65 @@ def max_tier_counts(cfg: Config, n: Optional[int] = None, all_top: bool = False,
         for k in range(cfg.num_tiers):
             mx[k] = max(mx[k], int((tier == k).sum(axis=-1).max()) if n > 0 else 0)
     return mx
+
+
+# --------------------------------------------------------------------------- prefill
+def gen_prefill(cfg: Config, layer: int, n: Optional[int] = None, lengths: Optional[Sequence[int]] = None,
+                tail: float = 0.0, noise: float = 0.02, variant_seed: int = 0):
+    """Prefill keys and values of one layer: (K, V) fp16 [B][H_kv][n][d] with
+    n = max(lengths) (default: every sequence cfg.n_tokens long)."""
+    n = cfg.n_tokens if n is None else int(n)
+    lengths = [n] * cfg.batch if lengths is None else [int(x) for x in lengths]
+    n_cap = max(lengths) if lengths else 0
+    seed = _seed_of(cfg, variant_seed)
+    m = layer // cfg.layers_per_group
+    d, H = cfg.head_dim, cfg.num_kv_heads
+    out = []
+    for zi, decay in enumerate((0.93, 0.96)):
+        X = np.full((cfg.batch, H, n_cap, d), tail, np.float16)
+        for h in range(H):
+            g = _rng(seed, "pf_rot", m, zi, h).standard_normal((d, d))
+            U, rr = np.linalg.qr(g)
+            U = (U * np.sign(np.diag(rr))[None, :]).astype(np.float32)
+            sig = decay ** np.arange(d) * np.exp(0.1 * _rng(seed, "pf_spec", m, zi, h, layer).standard_normal(d))
+            A = (sig[:, None] * U.T).astype(np.float32)          # x = g @ A = U (sig * g)
+            for b in range(cfg.batch):
+                nb = lengths[b]
+                if nb == 0:
+                    continue
+                gx = _rng(seed, "pf_x", layer, zi, b, h).standard_normal((nb, d), dtype=np.float32)
+                e = _rng(seed, "pf_noise", layer, zi, b, h).standard_normal((nb, d), dtype=np.float32)
+                X[b, h, :nb] = (gx @ A + np.float32(noise) * e).astype(np.float16)
+        out.append(X)
+    return out[0], out[1]
+
+
+def gen_sketch(cfg: Config, k: int, variant_seed: int = 0) -> np.ndarray:
+    """Gaussian sketches: fp32 [num_groups][2][H_kv][d][k]."""
+    seed = _seed_of(cfg, variant_seed)
+    om = np.zeros((cfg.num_groups, 2, cfg.num_kv_heads, cfg.head_dim, k), np.float32)
+    for m in range(cfg.num_groups):
+        for zi in range(2):
+            for h in range(cfg.num_kv_heads):
+                om[m, zi, h] = _rng(seed, "pf_omega", m, zi, h).standard_normal((cfg.head_dim, k), dtype=np.float32)
+    return om
+
+
+def gen_tiers(cfg: Config, layer: int, n: Optional[int] = None, variant_seed: int = 0) -> np.ndarray:
+    """The router's tier per (b, KV head, position): uint8 [B][H_kv][n], shared
+    by the layers of a depth group (the mix of the cached layers)."""
+    n = cfg.n_tokens if n is None else int(n)
+    return _tiers(cfg, layer, n, _seed_of(cfg, variant_seed), False)
+
+
+def gen_gates(cfg: Config, layer: int, n: Optional[int] = None, variant_seed: int = 0):
+    """Per-token residual gates (gateK, gateV): fp16 [B][H_kv][n]."""
+    n = cfg.n_tokens if n is None else int(n)
+    seed = _seed_of(cfg, variant_seed)
+    out = []
+    for zi in range(2):
+        r = _rng(seed, "pf_gate", layer, zi)
+        u = r.random((cfg.batch, cfg.num_kv_heads, n))
+        g = 0.25 + 0.75 * r.random((cfg.batch, cfg.num_kv_heads, n))
+        out.append(np.where(u < 0.3, 1.0, g).astype(np.float16))
+    return out[0], out[1]
