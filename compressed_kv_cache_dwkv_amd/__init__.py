@@ -81,6 +81,7 @@ _SIGS = {
     "dwkv_destroy": [_P],
     "dwkv_reset": [_P, _P],
     "dwkv_set_basis": [_P, _I, _P, _P, _P],
+    "dwkv_get_basis": [_P, _I, _P, _P, _P],
     "dwkv_import_layer": [_P, _I, ctypes.POINTER(dwkv_logical_layer), ctypes.POINTER(ctypes.c_int64), _I, _P],
     "dwkv_export_layer": [_P, _I, ctypes.POINTER(dwkv_logical_layer), _P, _P, _I, _P],
     "dwkv_read_counts": [_P, _I, _I, _P, _P],
@@ -98,6 +99,10 @@ _SIGS = {
     "dwkv_probe_error": [_P, _I, _P, _I, _I, _P, _P, _P, ctypes.c_int64, _I, ctypes.c_float, ctypes.c_float, _P, _P,
                          ctypes.c_size_t, _P],
     "dwkv_probe_update": [_P, _P, _I, _P, ctypes.c_float, ctypes.c_float, _I, ctypes.c_float, ctypes.c_float],
+    "dwkv_prefill_workspace_bytes": [ctypes.POINTER(dwkv_config), ctypes.POINTER(ctypes.c_size_t)],
+    "dwkv_prefill_gram": [_P, _I, _P, _P, _P, _I, ctypes.c_int64, _I, _P, ctypes.c_size_t, _P],
+    "dwkv_prefill_bases": [_P, _I, _I, _P, _I, _I, _P, _P, ctypes.c_size_t, _P],
+    "dwkv_prefill_encode": [_P, _I, _P, _P, _P, _I, ctypes.c_int64, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "dwkv_check_errors": [_P, _P, ctypes.POINTER(ctypes.c_uint32)],
     "dwkv_clear_errors": [_P, _P],
 }
@@ -208,6 +213,14 @@ def dwkv_set_basis(h, group: int, basisK, basisV, stream=None) -> None:
     _check(_lib.dwkv_set_basis(h, group, _ptr(basisK, torch.float16, name="basisK"),
                                _ptr(basisV, torch.float16, name="basisV"), _stream(stream)),
            "dwkv_set_basis")
+
+
+def dwkv_get_basis(h, group: int, basisK, basisV, stream=None) -> None:
+    """basisK, basisV: fp16 [H_kv][r_max][d] GPU tensors, filled from the arena."""
+    import torch
+    _check(_lib.dwkv_get_basis(h, group, _ptr(basisK, torch.float16, name="basisK"),
+                               _ptr(basisV, torch.float16, tuple(basisK.shape), name="basisV"), _stream(stream)),
+           "dwkv_get_basis")
 
 
 def _logical(lay: Dict[str, object]) -> dwkv_logical_layer:
@@ -406,6 +419,52 @@ def dwkv_probe_update(tau: np.ndarray, below: np.ndarray, err: np.ndarray, tol: 
                                   tau.size, np.ascontiguousarray(err).ctypes.data_as(ctypes.c_void_p),
                                   float(tol), float(step), int(patience), float(tau_min), float(tau_max)),
            "dwkv_probe_update")
+
+
+def dwkv_prefill_workspace_bytes(cfg: dwkv_config) -> int:
+    out = ctypes.c_size_t(0)
+    _check(_lib.dwkv_prefill_workspace_bytes(ctypes.byref(cfg), ctypes.byref(out)), "dwkv_prefill_workspace_bytes")
+    return int(out.value)
+
+
+def dwkv_prefill_gram(h, layer: int, k, v, n_tokens, workspace, first: bool, stream=None) -> None:
+    """k, v fp16 [B][H_kv][n_cap][d]; n_tokens int32 [B] (all on the GPU)."""
+    import torch
+    B, H, n_cap, d = k.shape
+    _check(_lib.dwkv_prefill_gram(h, layer, _ptr(k, torch.float16, name="k"),
+                                  _ptr(v, torch.float16, (B, H, n_cap, d), name="v"),
+                                  _ptr(n_tokens, torch.int32, (B,), name="n_tokens"), B, n_cap, 1 if first else 0,
+                                  _ptr(workspace, name="workspace"), workspace.numel() * workspace.element_size(),
+                                  _stream(stream)),
+           "dwkv_prefill_gram")
+
+
+def dwkv_prefill_bases(h, group0: int, omega, workspace, power_iters: int = 2, ritz=None, stream=None) -> None:
+    """omega fp32 [n_groups][2][H_kv][d][k]; ritz fp64 [n_groups][2][H_kv][k] or None."""
+    import torch
+    G, _, H, d, k = omega.shape
+    _check(_lib.dwkv_prefill_bases(h, group0, G, _ptr(omega, torch.float32, name="omega"), k, power_iters,
+                                   _ptr(ritz, torch.float64, (G, 2, H, k), name="ritz"),
+                                   _ptr(workspace, name="workspace"), workspace.numel() * workspace.element_size(),
+                                   _stream(stream)),
+           "dwkv_prefill_bases")
+
+
+def dwkv_prefill_encode(h, layer: int, k, v, n_tokens, tier, workspace, gateK=None, gateV=None,
+                        stream=None) -> None:
+    """k, v fp16 [B][H_kv][n_cap][d]; n_tokens int32 [B]; tier uint8 [B][H_kv][n_cap];
+    gateK, gateV fp16 [B][H_kv][n_cap] or None."""
+    import torch
+    B, H, n_cap, d = k.shape
+    _check(_lib.dwkv_prefill_encode(h, layer, _ptr(k, torch.float16, name="k"),
+                                    _ptr(v, torch.float16, (B, H, n_cap, d), name="v"),
+                                    _ptr(n_tokens, torch.int32, (B,), name="n_tokens"), B, n_cap,
+                                    _ptr(tier, torch.uint8, (B, H, n_cap), name="tier"),
+                                    _ptr(gateK, torch.float16, (B, H, n_cap), name="gateK"),
+                                    _ptr(gateV, torch.float16, (B, H, n_cap), name="gateV"),
+                                    _ptr(workspace, name="workspace"), workspace.numel() * workspace.element_size(),
+                                    _stream(stream)),
+           "dwkv_prefill_encode")
 
 
 def dwkv_check_errors(h, stream=None) -> int:

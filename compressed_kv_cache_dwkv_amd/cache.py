@@ -9,7 +9,9 @@ import torch
 
 from . import (dwkv_append, dwkv_arena_bytes, dwkv_check_errors, dwkv_clear_errors, dwkv_create,
                dwkv_decode_attn, dwkv_decode_splits, dwkv_decode_step, dwkv_destroy, dwkv_export_layer, dwkv_import_layer,
-               dwkv_read_counts, dwkv_reset, dwkv_set_basis, dwkv_workspace_bytes, make_config)
+               dwkv_get_basis, dwkv_prefill_bases, dwkv_prefill_encode, dwkv_prefill_gram,
+               dwkv_prefill_workspace_bytes, dwkv_read_counts, dwkv_reset, dwkv_set_basis, dwkv_workspace_bytes,
+               make_config)
 
 
 class CompressedKVCache:
@@ -34,6 +36,7 @@ class CompressedKVCache:
         self.arena = torch.empty(dwkv_arena_bytes(self.cfg), dtype=torch.uint8, device=self.device)
         self.handle = dwkv_create(self.cfg, self.arena)
         self._ws: Dict[int, torch.Tensor] = {}
+        self._pws: Optional[torch.Tensor] = None
         dwkv_reset(self.handle)
 
     # ------------------------------------------------------------------ setup
@@ -71,6 +74,39 @@ class CompressedKVCache:
         slots = torch.zeros((B, H, n_max), dtype=torch.int32, device=dev)
         dwkv_export_layer(self.handle, layer, dst, counts, slots)
         return dst, counts, slots
+
+    def get_basis(self, group: int):
+        """The window's bases (basisK, basisV), fp16 [H_kv][r_max][d] GPU tensors."""
+        bk = torch.empty((self.num_kv_heads, self.r_max, self.head_dim), dtype=torch.float16, device=self.device)
+        bv = torch.empty_like(bk)
+        dwkv_get_basis(self.handle, group, bk, bv)
+        return bk, bv
+
+    # ------------------------------------------------------------------ prefill
+    def prefill_workspace(self) -> torch.Tensor:
+        if self._pws is None:
+            self._pws = torch.zeros(dwkv_prefill_workspace_bytes(self.cfg), dtype=torch.uint8, device=self.device)
+        return self._pws
+
+    def prefill_gram(self, layer: int, k: torch.Tensor, v: torch.Tensor, n_tokens: torch.Tensor, first: bool) -> None:
+        dwkv_prefill_gram(self.handle, layer, k, v, n_tokens, self.prefill_workspace(), first)
+
+    def prefill_bases(self, group0: int, omega: torch.Tensor, power_iters: int = 2,
+                      ritz: Optional[torch.Tensor] = None) -> None:
+        if omega.dim() != 5 or tuple(omega.shape[1:4]) != (2, self.num_kv_heads, self.head_dim):
+            raise ValueError("omega must be [n_groups][2][H_kv][head_dim][k]")
+        dwkv_prefill_bases(self.handle, group0, omega, self.prefill_workspace(), power_iters, ritz)
+
+    def prefill_encode(self, layer: int, k: torch.Tensor, v: torch.Tensor, n_tokens: torch.Tensor,
+                       tier: torch.Tensor, gateK: Optional[torch.Tensor] = None,
+                       gateV: Optional[torch.Tensor] = None) -> None:
+        dwkv_prefill_encode(self.handle, layer, k, v, n_tokens, tier, self.prefill_workspace(), gateK, gateV)
+
+    def gram(self, group: int) -> torch.Tensor:
+        """The window's accumulated Gram sums, fp64 [2][H_kv][d][d] (a view of the workspace)."""
+        H, d = self.num_kv_heads, self.head_dim
+        n = 2 * H * d * d
+        return self.prefill_workspace()[: (group + 1) * n * 8].view(torch.float64)[group * n:].view(2, H, d, d)
 
     def read_counts(self, layer: int, batch: int):
         return dwkv_read_counts(self.handle, layer, batch, self.num_kv_heads, self.num_tiers)

@@ -334,6 +334,20 @@ int dwkv_set_basis(dwkv_handle *h, int group, const void *basisK, const void *ba
     return hip_status(e);
 }
 
+int dwkv_get_basis(dwkv_handle *h, int group, void *basisK, void *basisV, void *stream)
+{
+    if (!valid_handle(h) || !basisK || !basisV) return DWKV_ERR_INVALID_ARG;
+    const Layout &ly = h->ly;
+    if (group < 0 || group >= ly.num_groups) return DWKV_ERR_INVALID_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const size_t bytes = (size_t)ly.basis_elems * 2;
+    hipError_t e = hipMemcpyAsync(basisK, dwkv::basis_ptr(ly, h->arena, group, 0, 0), bytes,
+                                  hipMemcpyDeviceToDevice, s);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(basisV, dwkv::basis_ptr(ly, h->arena, group, 1, 0), bytes, hipMemcpyDeviceToDevice, s);
+    return hip_status(e);
+}
+
 static bool logical_ok(const dwkv_logical_layer *L, int s_max, int cb)
 {
     if (!L || L->n_max < 0) return false;
@@ -629,6 +643,137 @@ int dwkv_probe_update(float *tau, int32_t *below, int n_windows, const float *er
         tau[m] = t < tau_min ? tau_min : (t > tau_max ? tau_max : t);
     }
     return DWKV_OK;
+}
+
+// ------------------------------------------------------------------ prefill
+
+// Gram workgroups per (Z, KV head): about 512 workgroups per call.
+static int gram_splits(const Layout &ly)
+{
+    int s = (512 + 2 * ly.Hkv - 1) / (2 * ly.Hkv);
+    return s < 1 ? 1 : (s > dwkv::kGramMaxSplits ? dwkv::kGramMaxSplits : s);
+}
+
+// Prefill workspace: the Gram sums of every window (fp64, first, so that
+// their offset is 0), the Gram partials, the arrival counters, then the
+// encoder's per-(sequence, KV head) status and tier counts.
+struct PrefillWs {
+    double *acc;
+    float *part;
+    uint32_t *arrive;
+    int32_t *status, *newcnt;
+    size_t bytes;
+};
+
+static PrefillWs carve_prefill(const Layout &ly, void *base)
+{
+    PrefillWs w;
+    uint8_t *p = static_cast<uint8_t *>(base);
+    size_t off = 0;
+    auto take = [&](int64_t bytes) {
+        uint8_t *q = p ? p + off : nullptr;
+        off += (size_t)dwkv::align_up(bytes, 256);
+        return q;
+    };
+    const int64_t dd = (int64_t)ly.d * ly.d;
+    w.acc = reinterpret_cast<double *>(take((int64_t)ly.num_groups * 2 * ly.Hkv * dd * 8));
+    w.part = reinterpret_cast<float *>(take((int64_t)2 * ly.Hkv * gram_splits(ly) * dwkv::gram_pairs(ly.d) * 256 * 4));
+    w.arrive = reinterpret_cast<uint32_t *>(take((int64_t)2 * ly.Hkv * dwkv::kArriveStride * 4));
+    w.status = reinterpret_cast<int32_t *>(take((int64_t)ly.Bmax * ly.Hkv * 4));
+    w.newcnt = reinterpret_cast<int32_t *>(take((int64_t)ly.Bmax * ly.Hkv * dwkv::kMaxTiers * 4));
+    w.bytes = off;
+    return w;
+}
+
+int dwkv_prefill_workspace_bytes(const dwkv_config *cfg, size_t *bytes)
+{
+    if (!cfg || !bytes) return DWKV_ERR_INVALID_ARG;
+    Layout ly;
+    const int rc = dwkv::build_layout(cfg, &ly);
+    if (rc != DWKV_OK) return rc;
+    *bytes = carve_prefill(ly, nullptr).bytes;
+    return DWKV_OK;
+}
+
+static int prefill_common(const dwkv_handle *h, int layer, const void *k, const void *v, const int32_t *n_tokens,
+                          int batch, int64_t n_cap, void *ws, size_t ws_bytes)
+{
+    if (!valid_handle(h) || !k || !v || !n_tokens || !ws) return DWKV_ERR_INVALID_ARG;
+    const Layout &ly = h->ly;
+    if (layer < 0 || layer >= ly.L || batch <= 0 || batch > ly.Bmax || batch > dwkv::kGramMaxBatch)
+        return DWKV_ERR_INVALID_ARG;
+    if (n_cap <= 0 || n_cap >= (int64_t(1) << 31)) return DWKV_ERR_INVALID_ARG;
+    if (reinterpret_cast<uintptr_t>(ws) % 256 != 0) return DWKV_ERR_INVALID_ARG;
+    if (reinterpret_cast<uintptr_t>(k) % 16 != 0 || reinterpret_cast<uintptr_t>(v) % 16 != 0)
+        return DWKV_ERR_INVALID_ARG;
+    if (ws_bytes < carve_prefill(ly, nullptr).bytes) return DWKV_ERR_WORKSPACE;
+    return DWKV_OK;
+}
+
+int dwkv_prefill_gram(dwkv_handle *h, int layer, const void *k, const void *v, const int32_t *n_tokens, int batch,
+                      int64_t n_cap, int first, void *workspace, size_t workspace_bytes, void *stream)
+{
+    const int rc = prefill_common(h, layer, k, v, n_tokens, batch, n_cap, workspace, workspace_bytes);
+    if (rc != DWKV_OK) return rc;
+    const Layout &ly = h->ly;
+    const PrefillWs w = carve_prefill(ly, workspace);
+    dwkv::GramArgs a;
+    a.k = static_cast<const uint16_t *>(k);
+    a.v = static_cast<const uint16_t *>(v);
+    a.n_tokens = n_tokens;
+    a.B = batch;
+    a.Hkv = ly.Hkv;
+    a.n_cap = n_cap;
+    a.S = gram_splits(ly);
+    a.first = first ? 1 : 0;
+    a.part = w.part;
+    a.acc = w.acc + (int64_t)(layer / ly.G) * 2 * ly.Hkv * ly.d * ly.d;
+    a.arrive = w.arrive;
+    return hip_status(dwkv::launch_gram(ly, h->arena, a, static_cast<hipStream_t>(stream)));
+}
+
+int dwkv_prefill_bases(dwkv_handle *h, int group0, int n_groups, const float *omega, int sketch, int power_iters,
+                       double *ritz, void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!valid_handle(h) || !omega || !workspace) return DWKV_ERR_INVALID_ARG;
+    const Layout &ly = h->ly;
+    if (group0 < 0 || n_groups <= 0 || group0 + n_groups > ly.num_groups) return DWKV_ERR_INVALID_ARG;
+    if (sketch < ly.R || sketch > ly.d || power_iters < 0 || power_iters > 16) return DWKV_ERR_INVALID_ARG;
+    if (sketch > dwkv::kMaxSketch) return DWKV_ERR_UNSUPPORTED;
+    if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return DWKV_ERR_INVALID_ARG;
+    if (workspace_bytes < carve_prefill(ly, nullptr).bytes) return DWKV_ERR_WORKSPACE;
+    const PrefillWs w = carve_prefill(ly, workspace);
+    dwkv::BasesArgs a;
+    a.acc = w.acc + (int64_t)group0 * 2 * ly.Hkv * ly.d * ly.d;
+    a.omega = omega;
+    a.ritz = ritz;
+    a.k = sketch;
+    a.power_iters = power_iters;
+    a.group0 = group0;
+    return hip_status(dwkv::launch_bases(ly, h->arena, a, n_groups, static_cast<hipStream_t>(stream)));
+}
+
+int dwkv_prefill_encode(dwkv_handle *h, int layer, const void *k, const void *v, const int32_t *n_tokens, int batch,
+                        int64_t n_cap, const void *tier, const void *gate_k, const void *gate_v, void *workspace,
+                        size_t workspace_bytes, void *stream)
+{
+    const int rc = prefill_common(h, layer, k, v, n_tokens, batch, n_cap, workspace, workspace_bytes);
+    if (rc != DWKV_OK) return rc;
+    if (!tier) return DWKV_ERR_INVALID_ARG;
+    const Layout &ly = h->ly;
+    const PrefillWs w = carve_prefill(ly, workspace);
+    dwkv::EncodeArgs a;
+    a.layer = layer;
+    a.k = static_cast<const uint16_t *>(k);
+    a.v = static_cast<const uint16_t *>(v);
+    a.n_tokens = n_tokens;
+    a.n_cap = n_cap;
+    a.tier = static_cast<const uint8_t *>(tier);
+    a.gateK = static_cast<const uint16_t *>(gate_k);
+    a.gateV = static_cast<const uint16_t *>(gate_v);
+    a.status = w.status;
+    a.newcnt = w.newcnt;
+    return hip_status(dwkv::launch_prefill_encode(ly, h->arena, a, batch, static_cast<hipStream_t>(stream)));
 }
 
 int dwkv_append(dwkv_handle *h, int layer, const void *k, const void *v, const void *tier,

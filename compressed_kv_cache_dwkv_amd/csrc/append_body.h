@@ -124,54 +124,47 @@ __device__ __forceinline__ uint32_t append_admit(const Layout &ly, int k, int cn
     return err;
 }
 
-// Encodes Z = z and stores the token's coefficients, residual record and
-// scale at its slot, past the tier's counted tokens (so readers of the
-// cache never use it before it is published).  Returns 1 if the token is
-// admitted (the same answer in both waves), with its tier slot and
-// position; the token is published by append_commit once both waves are
-// done.
+// Copies wave z's basis rows (held in registers by append_fetch or its
+// bulk counterpart) into the LDS rows sB, for the column reads of step 2.
 template <int D>
-__device__ __forceinline__ int append_encode(const AppendRegs<D> &st, const Layout &ly, uint8_t *arena,
-                                             int layer, int b, int h, int z, int lane,
-                                             const AppendArgs &ap, const AppendLds &L, int &slot_out,
-                                             int &n_out)
+__device__ __forceinline__ void encode_stage_basis(const uint4 (&brow)[2][D / 8], uint16_t *sB, int R, int lane)
 {
-#pragma clang fp contract(off)
-    constexpr int NJ = D / kWave;             // channels per lane
     constexpr int RW = D / 8;                 // 16-byte pieces of a basis row
-    const int bh = b * ly.Hkv + h;
-    const int R = ly.R, k = st.k;
-
-    // admission (decided identically by both waves; wave 0 reports)
-    int slot, n;
-    const uint32_t err = append_admit(ly, k, st.cnt_l, slot, n);
-    slot_out = slot;
-    n_out = n;
-    if (err) {
-        if (z == 0 && lane == 0) atomicOr(err_ptr(ly, arena), err);
-        return 0;
-    }
-    const int r = ly.rank[k], s = ly.resid[k];
-    uint8_t *blk = head_block_ptr(ly, arena, layer, b, h);
-
-    // the rows into LDS for column reads
-    uint16_t *sB = L.B + z * (kMaxRank * kAppendBStride);
-    float *sx = L.x + z * kMaxHeadDim, *sc = L.c + z * kMaxRank;
 #pragma unroll
     for (int rr = 0; rr < 2; ++rr) {
         if (lane + rr * kWave < R) {
             uint32_t *dst = reinterpret_cast<uint32_t *>(sB + (lane + rr * kWave) * kAppendBStride);
 #pragma unroll
             for (int c = 0; c < RW; ++c) {
-                dst[4 * c + 0] = st.brow[rr][c].x;
-                dst[4 * c + 1] = st.brow[rr][c].y;
-                dst[4 * c + 2] = st.brow[rr][c].z;
-                dst[4 * c + 3] = st.brow[rr][c].w;
+                dst[4 * c + 0] = brow[rr][c].x;
+                dst[4 * c + 1] = brow[rr][c].y;
+                dst[4 * c + 2] = brow[rr][c].z;
+                dst[4 * c + 3] = brow[rr][c].w;
             }
         }
     }
+}
+
+// Encodes one vector (lane j holding channels j, j + 64 in xv) at tier k and
+// stores its coefficients, residual record and scale at `slot` of the tier
+// region in blk (the (layer, sequence, KV head) block).  brow: basis rows
+// lane and lane + 64; sB: the same rows in LDS; sx, sc, scode, sidx: this
+// wave's LDS scratch.  gate16: the fp16 gate (0x3C00 for a gate of 1).
+// Every append and every bulk prefill encoding runs this one body, so both
+// give the same bits for the same vector.
+template <int D>
+__device__ __forceinline__ void encode_store(const uint4 (&brow)[2][D / 8], const float (&xv)[D / kWave],
+                                             const uint16_t *sB, float *sx, float *sc, int8_t *scode,
+                                             uint8_t *sidx, const Layout &ly, uint8_t *blk, int k, int slot,
+                                             int z, int lane, uint16_t gate16)
+{
+#pragma clang fp contract(off)
+    constexpr int NJ = D / kWave;             // channels per lane
+    const int r = ly.rank[k], s = ly.resid[k];
+
+    wave_fence();                             // the previous vector's reads of sx, sc are issued
 #pragma unroll
-    for (int q = 0; q < NJ; ++q) sx[lane + q * kWave] = st.xv[q];
+    for (int q = 0; q < NJ; ++q) sx[lane + q * kWave] = xv[q];
     wave_fence();
 
     // 1. coefficient sums sum_j B[i][j] x_j, sequential in j (x read from
@@ -185,7 +178,7 @@ __device__ __forceinline__ int append_encode(const AppendRegs<D> &st, const Layo
         if (rr * kWave < r) {
             float acc = 0.0f;
 #pragma unroll
-            for (int j = 0; j < D; ++j) acc = __builtin_fmaf(half_at<D>(st.brow[rr], j), sx[j], acc);
+            for (int j = 0; j < D; ++j) acc = __builtin_fmaf(half_at<D>(brow[rr], j), sx[j], acc);
             acc1[rr] = as_fp32(acc);
         }
     }
@@ -235,7 +228,7 @@ __device__ __forceinline__ int append_encode(const AppendRegs<D> &st, const Layo
         float acc = 0.0f;
 #pragma unroll 8
         for (int i = 0; i < r; ++i) acc = __builtin_fmaf(h2f(sB[i * kAppendBStride + j]), sc[i], acc);
-        e[q] = st.xv[q] - acc;
+        e[q] = xv[q] - acc;
     }
 
     if (s > 0) {
@@ -269,8 +262,6 @@ __device__ __forceinline__ int append_encode(const AppendRegs<D> &st, const Layo
         const uint16_t s16 = f2h(__fdiv_rn(amax, (float)ly.qmax));
         const float sf = h2f(s16);
         // 5. codes, placed in ascending channel order
-        int8_t *scode = L.code + z * kMaxResid;
-        uint8_t *sidx = L.idx + z * kMaxResid;
 #pragma unroll
         for (int q = 0; q < NJ; ++q) {
             if (!keep[q]) continue;
@@ -299,12 +290,40 @@ __device__ __forceinline__ int append_encode(const AppendRegs<D> &st, const Layo
         }
         // 6. the gate folds into the stored scale
         if (lane == 0) {
-            const uint16_t *gp = z ? ap.gateV : ap.gateK;
-            const uint16_t g = gp ? gp[bh] : uint16_t(0x3C00);
-            const uint16_t stored = (g == 0x3C00) ? s16 : f2h(h2f(g) * sf);
+            const uint16_t stored = (gate16 == 0x3C00) ? s16 : f2h(h2f(gate16) * sf);
             reinterpret_cast<uint16_t *>(blk + (z ? ly.f_scaleV[k] : ly.f_scaleK[k]))[slot] = stored;
         }
     }
+}
+
+// Encodes Z = z and stores the token's coefficients, residual record and
+// scale at its slot, past the tier's counted tokens (so readers of the
+// cache never use it before it is published).  Returns 1 if the token is
+// admitted (the same answer in both waves), with its tier slot and
+// position; the token is published by append_commit once both waves are
+// done.
+template <int D>
+__device__ __forceinline__ int append_encode(const AppendRegs<D> &st, const Layout &ly, uint8_t *arena,
+                                             int layer, int b, int h, int z, int lane,
+                                             const AppendArgs &ap, const AppendLds &L, int &slot_out,
+                                             int &n_out)
+{
+    const int bh = b * ly.Hkv + h;
+    // admission (decided identically by both waves; wave 0 reports)
+    int slot, n;
+    const uint32_t err = append_admit(ly, st.k, st.cnt_l, slot, n);
+    slot_out = slot;
+    n_out = n;
+    if (err) {
+        if (z == 0 && lane == 0) atomicOr(err_ptr(ly, arena), err);
+        return 0;
+    }
+    uint16_t *sB = L.B + z * (kMaxRank * kAppendBStride);
+    encode_stage_basis<D>(st.brow, sB, ly.R, lane);
+    const uint16_t *gp = z ? ap.gateV : ap.gateK;
+    const uint16_t g = gp ? gp[bh] : uint16_t(0x3C00);
+    encode_store<D>(st.brow, st.xv, sB, L.x + z * kMaxHeadDim, L.c + z * kMaxRank, L.code + z * kMaxResid,
+                    L.idx + z * kMaxResid, ly, head_block_ptr(ly, arena, layer, b, h), st.k, slot, z, lane, g);
     return 1;
 }
 

@@ -89,6 +89,51 @@ hipError_t launch_export(const Layout &ly, uint8_t *arena, int layer,
 // Writes the transposed bases of window m (basis_vt_ptr, basis_kt_ptr) from the arena's copies.
 hipError_t launch_transpose_basis(const Layout &ly, uint8_t *arena, int m, hipStream_t stream);
 
+// Prefill compression (prefill.hip).
+constexpr int kGramMaxBatch = 1024;   // sequences per Gram call
+constexpr int kGramMaxSplits = 128;   // workgroups per (Z, KV head) of a Gram call
+constexpr int kMaxSketch = 72;        // sketch width k (LDS: two head_dim x k fp64 matrices)
+constexpr int kJacobiMaxSweeps = 40;
+
+// Number of 16x16 blocks on and above the diagonal of a head_dim^2 matrix.
+constexpr int gram_pairs(int d) { return (d / 16) * (d / 16 + 1) / 2; }
+
+struct GramArgs {
+    const uint16_t *k, *v;        // fp16 [B][Hkv][n_cap][d]
+    const int32_t *n_tokens;      // [B] prefill length per sequence
+    int B, Hkv;
+    int64_t n_cap;
+    int S;                        // workgroups per (Z, KV head)
+    int first;                    // 1: the window's sums start here
+    float *part;                  // [2 Hkv][S][gram_pairs(d) * 256] partial sums
+    double *acc;                  // the window's [2][Hkv][d][d] sums
+    uint32_t *arrive;             // [2 Hkv][kArriveStride]
+};
+hipError_t launch_gram(const Layout &ly, uint8_t *arena, const GramArgs &a, hipStream_t stream);
+
+struct BasesArgs {
+    const double *acc;            // [n_groups][2][Hkv][d][d] Gram sums of windows group0, ...
+    const float *omega;           // [n_groups][2][Hkv][d][k] Gaussian sketches
+    double *ritz;                 // [n_groups][2][Hkv][k] Ritz values in decreasing order, or null
+    int k, power_iters, group0;
+};
+// Forms the bases of windows group0 .. group0 + n_groups - 1 and their
+// transposed copies.
+hipError_t launch_bases(const Layout &ly, uint8_t *arena, const BasesArgs &a, int n_groups, hipStream_t stream);
+
+struct EncodeArgs {
+    int layer;
+    const uint16_t *k, *v;        // fp16 [B][Hkv][n_cap][d]
+    const int32_t *n_tokens;      // [B]
+    int64_t n_cap;
+    const uint8_t *tier;          // [B][Hkv][n_cap]
+    const uint16_t *gateK, *gateV;  // fp16 [B][Hkv][n_cap], or null
+    int32_t *status;              // [B][Hkv] first position, or -1 if refused
+    int32_t *newcnt;              // [B][Hkv][kMaxTiers]
+};
+hipError_t launch_prefill_encode(const Layout &ly, uint8_t *arena, const EncodeArgs &a, int batch,
+                                 hipStream_t stream);
+
 hipError_t launch_fill_u32(uint32_t *p, uint32_t value, int64_t count, hipStream_t stream);
 
 }  // namespace dwkv

@@ -66,6 +66,7 @@ extern "C" {
 #define DWKV_DEVERR_BAD_TIER 4u   /* a tier index >= num_tiers in device input    */
 #define DWKV_DEVERR_BAD_INDEX 8u  /* a residual channel index >= head_dim on import
                                      (stored as head_dim - 1)                     */
+#define DWKV_DEVERR_BAD_LENGTH 16u /* a prefill length outside [0, n_cap]           */
 
 /*
  * Static shape of one cache.  Supported: head_dim 64 or 128; r_max a multiple
@@ -154,6 +155,10 @@ int dwkv_reset(dwkv_handle *h, void *stream);
  */
 int dwkv_set_basis(dwkv_handle *h, int group, const void *basisK, const void *basisV,
                    void *stream);
+
+/* Copies the shared bases of window `group` out of the arena, in
+ * dwkv_set_basis's layout (device fp16 [H_kv][r_max][head_dim] each). */
+int dwkv_get_basis(dwkv_handle *h, int group, void *basisK, void *basisV, void *stream);
 
 /*
  * Replaces the content of `layer` by the logical cache `src` (device arrays,
@@ -347,6 +352,80 @@ int dwkv_probe_error(dwkv_handle *h, int layer, const void *q, int n_queries, in
  */
 int dwkv_probe_update(float *tau, int32_t *below, int n_windows, const float *err, float tol, float step,
                       int patience, float tau_min, float tau_max);
+
+/*
+ * Prefill compression (the paper's §3 Method: the shared bases are
+ * initialised after prefill from a randomized low-rank sketch of the cached
+ * keys and values, per depth window, KV head and Z; every prefill token is
+ * then projected onto its window's basis and its residual quantised at the
+ * router's channel count -- the data path of Fig. 2).  Three calls, in this
+ * order for each window m (layers m * layers_per_group ...):
+ *
+ *   dwkv_prefill_gram   once per layer of the window (first != 0 for the
+ *                       first one): adds the layer's prefill vectors to the
+ *                       window's Gram matrices C^Z_h = sum x x^T;
+ *   dwkv_prefill_bases  forms the bases of one or more windows from their
+ *                       Gram matrices and writes them into the cache (as
+ *                       dwkv_set_basis would);
+ *   dwkv_prefill_encode once per layer: appends its prefill tokens.
+ *
+ * Prefill keys and values k, v: device fp16 [batch][num_kv_heads][n_cap]
+ * [head_dim] (16-byte aligned), the first n_tokens[b] positions of sequence
+ * b valid; n_tokens: device int32 [batch] (a length outside [0, n_cap] sets
+ * DWKV_DEVERR_BAD_LENGTH and counts as 0).  Every window's Gram sums pool
+ * all layers of the window, all sequences of the batch and every valid
+ * position (the bases are shared by the batch).
+ *
+ * Workspace: device memory of dwkv_prefill_workspace_bytes(cfg) bytes,
+ * 256-byte aligned, zero-filled by the caller before its first use and left
+ * ready for the next call; one workspace per stream of concurrent prefill
+ * work.  Its first num_groups * 2 * num_kv_heads * head_dim^2 * 8 bytes hold
+ * the Gram sums, fp64 [window][Z][KV head][head_dim][head_dim] (row-major,
+ * exactly symmetric), for inspection.
+ */
+int dwkv_prefill_workspace_bytes(const dwkv_config *cfg, size_t *bytes);
+
+/* The window of `layer` gets layer's contribution.  The matrix-core partial
+ * sums are fp32 per workgroup (a fixed share of the 64-token tiles of the
+ * layer), added in fp64 in workgroup order: the result is deterministic. */
+int dwkv_prefill_gram(dwkv_handle *h, int layer, const void *k, const void *v, const int32_t *n_tokens, int batch,
+                      int64_t n_cap, int first, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Bases of windows group0 .. group0 + n_groups - 1 (one workgroup per
+ * window, Z and KV head, fp64), by the randomized range finder with power
+ * iterations and a Rayleigh-Ritz step (Halko, Martinsson and Tropp, SIAM
+ * Review 2011, §4.5 and §5.3) on the window's Gram matrix C:
+ *   1. Y = C Omega            (Omega: the caller's Gaussian sketch)
+ *   2. Q = orth(Y)            (Gram-Schmidt twice per column over [Y | I],
+ *                              a column skipped when its norm falls to
+ *                              2^-40 of its norm before; the first k kept)
+ *   3. power_iters times Q = orth(C Q)
+ *   4. T = Q^T C Q = U diag(theta) U^T (cyclic Jacobi)
+ *   5. the Ritz vectors Q U in decreasing theta (ties: lower index first),
+ *      each with its first largest-magnitude entry made positive
+ *   6. the first r_max of them, rounded once to fp16, as the basis rows.
+ * omega: device fp32 [n_groups][2][num_kv_heads][head_dim][sketch] (Z = K,
+ * V); sketch in [r_max, min(head_dim, 72)]; power_iters in [0, 16].  ritz:
+ * device fp64 [n_groups][2][num_kv_heads][sketch] (theta in decreasing
+ * order), or NULL.
+ */
+int dwkv_prefill_bases(dwkv_handle *h, int group0, int n_groups, const float *omega, int sketch, int power_iters,
+                       double *ritz, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Appends layer's prefill tokens, in position order after the tokens it
+ * already holds: token t of sequence b, KV head h is encoded exactly as
+ * dwkv_append would encode it (same bits) at tier tier[b][h][t] with gates
+ * gate_k/gate_v[b][h][t].  tier: device uint8 [batch][num_kv_heads][n_cap];
+ * gate_k, gate_v: device fp16 [batch][num_kv_heads][n_cap] or NULL (a gate
+ * of 1).  Admission is per (sequence, KV head), all or nothing: a tier >=
+ * num_tiers, a full tier region or a full position map sets the device
+ * error word and leaves that (sequence, KV head) unchanged.
+ */
+int dwkv_prefill_encode(dwkv_handle *h, int layer, const void *k, const void *v, const int32_t *n_tokens, int batch,
+                        int64_t n_cap, const void *tier, const void *gate_k, const void *gate_v, void *workspace,
+                        size_t workspace_bytes, void *stream);
 
 /* Synchronises the stream; returns DWKV_ERR_DEVICE if the device error word
  * is set (its bits in *bits if non-NULL), else DWKV_OK. */

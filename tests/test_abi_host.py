@@ -239,6 +239,45 @@ def test_dense_comparator_host_checks():
         L.dwkv_destroy(h)
 
 
+def test_prefill_host_checks():
+    """The prefill entry points reject bad arguments before any HIP call; the
+    workspace starts with the fp64 Gram sums of every window."""
+    L = d._lib
+    cfg = _cfg()
+    ws = d.dwkv_prefill_workspace_bytes(cfg)
+    assert ws >= 8 * 2 * 8 * 128 * 128 * 8
+    h = ctypes.c_void_p()
+    assert L.dwkv_create(ctypes.byref(cfg), ctypes.c_void_p(1 << 40), d.dwkv_arena_bytes(cfg), ctypes.byref(h)) == d.DWKV_OK
+    kk = ctypes.c_void_p(1 << 44)
+    wsp = ctypes.c_void_p(1 << 43)
+    try:
+        g = lambda layer=0, k=kk, v=kk, n=kk, B=1, cap=4096, p=wsp, sz=ws: L.dwkv_prefill_gram(
+            h, layer, k, v, n, B, cap, 1, p, sz, None)
+        assert g(k=None) == d.DWKV_ERR_INVALID_ARG
+        assert g(n=None) == d.DWKV_ERR_INVALID_ARG
+        assert g(layer=32) == d.DWKV_ERR_INVALID_ARG
+        assert g(B=0) == d.DWKV_ERR_INVALID_ARG
+        assert g(B=3) == d.DWKV_ERR_INVALID_ARG                     # more than max_batch
+        assert g(cap=0) == d.DWKV_ERR_INVALID_ARG
+        assert g(k=ctypes.c_void_p((1 << 44) + 8)) == d.DWKV_ERR_INVALID_ARG
+        assert g(p=ctypes.c_void_p((1 << 43) + 64)) == d.DWKV_ERR_INVALID_ARG
+        assert g(sz=ws - 1) == d.DWKV_ERR_WORKSPACE
+        b = lambda g0=0, ng=1, om=kk, k=72, q=2, sz=ws: L.dwkv_prefill_bases(h, g0, ng, om, k, q, None, wsp, sz, None)
+        assert b(om=None) == d.DWKV_ERR_INVALID_ARG
+        assert b(g0=7, ng=2) == d.DWKV_ERR_INVALID_ARG
+        assert b(ng=0) == d.DWKV_ERR_INVALID_ARG
+        assert b(k=60) == d.DWKV_ERR_INVALID_ARG                   # narrower than r_max
+        assert b(k=129) == d.DWKV_ERR_INVALID_ARG                  # wider than head_dim
+        assert b(k=80) == d.DWKV_ERR_UNSUPPORTED                   # beyond the LDS-resident sketch
+        assert b(q=-1) == d.DWKV_ERR_INVALID_ARG
+        assert b(sz=ws - 1) == d.DWKV_ERR_WORKSPACE
+        assert L.dwkv_prefill_encode(h, 0, kk, kk, kk, 1, 4096, None, None, None, wsp, ws, None) == d.DWKV_ERR_INVALID_ARG
+        assert L.dwkv_prefill_encode(h, 0, kk, kk, kk, 1, 4096, kk, None, None, wsp, ws - 1,
+                                     None) == d.DWKV_ERR_WORKSPACE
+    finally:
+        L.dwkv_destroy(h)
+
+
 def test_workspace_scales_with_batch_and_splits():
     a = d.dwkv_workspace_bytes(_cfg(decode_splits=4), 1)
     b = d.dwkv_workspace_bytes(_cfg(decode_splits=8), 1)

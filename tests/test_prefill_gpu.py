@@ -1,0 +1,425 @@
+"""Prefill compression through the C ABI against the oracle (needs an MI355X).
+
+  * Gram sums: bit-exact on integer-valued prefill data (every product and
+    partial sum is an integer below 2^24, exact in fp32 in any order), and
+    within the fp32 summation bound |dC_ij| <= m 2^-24 sum_t |x_ti x_tj|
+    (m: vectors one workgroup sums, at most a layer's) on Gaussian data,
+    whose tail positions hold NaN (they must not count).
+  * Bases: on identical Gram matrices (the integer data) the Ritz values
+    agree to 1e-10 of the largest, and each basis row whose Ritz value is
+    separated from its neighbours by 1e-6 of the largest is the oracle's fp64
+    row rounded once to fp16 (within half an fp16 unit plus 1e-9).  On
+    Gaussian data the difference of the two Gram matrices dC enters
+    (Weyl: Ritz values within 2 ||dC||_2; Davis-Kahan: converged rows within
+    2 sqrt(2) ||dC||_2 / gap).
+  * Bulk encode: bit-exact against the oracle (every token exactly one
+    append) given the same seeded bases, for fp16 and 8-bit coefficients,
+    head_dim 64 and 128, gates, ragged lengths, paper-literal tiers, and in
+    two chunks; refusals leave a (sequence, KV head) unchanged.
+  * The three steps in a chain, and the full 64K-token Llama-3-8B shape.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workload as w
+from workload.gen import gen_gates, gen_prefill, gen_query, gen_sketch, gen_tiers, make_bases
+from tests.helpers import tiny_config
+
+pytestmark = pytest.mark.gpu
+
+DEVERR_BAD_TIER, DEVERR_TIER_FULL, DEVERR_BAD_LENGTH = 4, 1, 16
+
+
+@pytest.fixture(scope="module")
+def G():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from tests import gpu_util
+    return gpu_util
+
+
+def _cfg8k(**kw):
+    return w.get_config(1).with_(**kw)
+
+
+def _window(cfg, lengths, m=0, integer=False, tail=np.nan, variant_seed=0):
+    Ks, Vs = [], []
+    for layer in range(m * cfg.layers_per_group, (m + 1) * cfg.layers_per_group):
+        K, V = gen_prefill(cfg, layer, lengths=lengths, tail=0.0, variant_seed=variant_seed)
+        if integer:
+            K = np.clip(np.rint(K.astype(np.float32) * 4), -16, 16).astype(np.float16)
+            V = np.clip(np.rint(V.astype(np.float32) * 4), -16, 16).astype(np.float16)
+        for X in (K, V):
+            for b, n in enumerate(lengths):
+                X[b, :, n:] = tail
+        Ks.append(K)
+        Vs.append(V)
+    return Ks, Vs
+
+
+def _grams(G, cache, cfg, Ks, Vs, lengths, m=0):
+    n_dev = G.dev(np.asarray(lengths, np.int32))
+    for i, (K, V) in enumerate(zip(Ks, Vs)):
+        cache.prefill_gram(m * cfg.layers_per_group + i, G.dev(K), G.dev(V), n_dev, first=(i == 0))
+    import torch
+    torch.cuda.synchronize()
+    return cache.gram(m).cpu().numpy()
+
+
+def _cache(G, cfg, n):
+    return G.make_cache(cfg, n=n, extra=64)
+
+
+def _oracle_gram(cfg, Ks, Vs, lengths, z, h):
+    L = Ks if z == 0 else Vs
+    return oracle.window_gram([x for X in L for x in oracle.prefill.window_vectors(X, lengths, h)])
+
+
+def _abs_gram(cfg, Ks, Vs, lengths, z, h):
+    L = Ks if z == 0 else Vs
+    return oracle.window_gram([np.abs(x.astype(np.float64)) for X in L
+                               for x in oracle.prefill.window_vectors(X, lengths, h)])
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_gram_exact_on_integer_data(G, d):
+    cfg = _cfg8k(batch=3) if d == 128 else tiny_config(batch=3, num_kv_heads=2, num_q_heads=4, head_dim=64,
+                                                        r_max=32, tier_rank=(8, 16, 32), tier_prob=(0.5, 0.3, 0.2),
+                                                        n_tokens=3000)
+    lengths = [3000, 1777, 0]
+    Ks, Vs = _window(cfg, lengths, integer=True)
+    cache = _cache(G, cfg, 3000)
+    try:
+        print(f"gram exact: d={d} lengths={lengths}", flush=True)
+        got = _grams(G, cache, cfg, Ks, Vs, lengths)
+        for z in range(2):
+            for h in range(cfg.num_kv_heads):
+                assert np.array_equal(got[z, h], _oracle_gram(cfg, Ks, Vs, lengths, z, h)), (z, h)
+        assert cache.check_errors() == 0
+        # a second window call sequence starts afresh (first = True)
+        got2 = _grams(G, cache, cfg, Ks, Vs, lengths)
+        assert np.array_equal(got, got2)
+    finally:
+        cache.close()
+
+
+def test_gram_within_fp32_bound_and_ignores_tails(G):
+    cfg = _cfg8k(batch=2)
+    lengths = [5000, 2345]
+    Ks, Vs = _window(cfg, lengths)
+    cache = _cache(G, cfg, 5000)
+    try:
+        got = _grams(G, cache, cfg, Ks, Vs, lengths)
+        m = sum(lengths)
+        worst = 0.0
+        for z in range(2):
+            for h in range(cfg.num_kv_heads):
+                ref = _oracle_gram(cfg, Ks, Vs, lengths, z, h)
+                bound = m * 2.0 ** -24 * _abs_gram(cfg, Ks, Vs, lengths, z, h)
+                err = np.abs(got[z, h] - ref)
+                assert np.all(np.isfinite(got[z, h]))
+                assert np.all(err <= bound), (z, h, (err / np.maximum(bound, 1e-300)).max())
+                assert np.array_equal(got[z, h], got[z, h].T)
+                worst = max(worst, (err / np.maximum(bound, 1e-300)).max())
+        print(f"gram error / bound: {worst:.2e}")
+    finally:
+        cache.close()
+
+
+def _ritz_order_gaps(theta):
+    th = np.asarray(theta, np.float64)
+    gaps = np.full(th.shape, np.inf)
+    gaps[:-1] = np.minimum(gaps[:-1], th[:-1] - th[1:])
+    gaps[1:] = np.minimum(gaps[1:], th[:-1] - th[1:])
+    return gaps
+
+
+def _bases(G, cache, cfg, omega, q, m=0):
+    import torch
+    k = omega.shape[-1]
+    ritz = torch.zeros((1, 2, cfg.num_kv_heads, k), dtype=torch.float64, device="cuda")
+    cache.prefill_bases(m, G.dev(omega[m:m + 1]), q, ritz)
+    bk, bv = cache.get_basis(m)
+    torch.cuda.synchronize()
+    return bk.cpu().numpy(), bv.cpu().numpy(), ritz.cpu().numpy()[0]
+
+
+@pytest.mark.parametrize("d,k,q", [(128, 72, 2), (128, 72, 0), (64, 40, 1), (64, 64, 3)])
+def test_bases_match_oracle_on_identical_gram(G, d, k, q):
+    cfg = _cfg8k(batch=2) if d == 128 else tiny_config(batch=2, num_kv_heads=2, num_q_heads=4, head_dim=64,
+                                                        r_max=32, tier_rank=(8, 16, 32), tier_prob=(0.5, 0.3, 0.2),
+                                                        n_tokens=3000)
+    lengths = [3000, 1500]
+    Ks, Vs = _window(cfg, lengths, integer=True)
+    omega = gen_sketch(cfg, k)
+    cache = _cache(G, cfg, 3000)
+    try:
+        print(f"bases exact-gram: d={d} k={k} q={q}", flush=True)
+        _grams(G, cache, cfg, Ks, Vs, lengths)
+        bk, bv, ritz = _bases(G, cache, cfg, omega, q)
+        ref = oracle.prefill_bases(cfg, Ks, Vs, lengths, omega[0], q)
+        strict = 0
+        for zi, (z, got) in enumerate((("K", bk), ("V", bv))):
+            for h in range(cfg.num_kv_heads):
+                th = ref["theta" + z][h]
+                assert np.abs(ritz[zi, h] - th).max() <= 1e-10 * th[0], (z, h)
+                gaps = _ritz_order_gaps(th)
+                B64 = ref[z + "64"][h]
+                for i in range(cfg.r_max):
+                    if gaps[i] < 1e-6 * th[0]:
+                        continue
+                    ulp = np.spacing(np.abs(B64[i]).astype(np.float16)).astype(np.float64)
+                    diff = np.abs(got[h, i].astype(np.float64) - B64[i])
+                    assert np.all(diff <= 0.5 * ulp + 1e-9), (z, h, i, (diff - 0.5 * ulp).max())
+                    strict += 1
+        assert strict >= cfg.r_max        # most rows are separated
+        assert cache.check_errors() == 0
+    finally:
+        cache.close()
+
+
+def test_bases_match_oracle_on_gaussian_data(G):
+    cfg = _cfg8k(batch=2)
+    lengths = [4000, 2100]
+    Ks, Vs = _window(cfg, lengths)
+    k, q = cfg.r_max + 8, 2
+    omega = gen_sketch(cfg, k)
+    cache = _cache(G, cfg, 4000)
+    try:
+        grams = _grams(G, cache, cfg, Ks, Vs, lengths)
+        bk, bv, ritz = _bases(G, cache, cfg, omega, q)
+        ref = oracle.prefill_bases(cfg, Ks, Vs, lengths, omega[0], q)
+        for zi, (z, got) in enumerate((("K", bk), ("V", bv))):
+            for h in range(cfg.num_kv_heads):
+                C = ref["gram" + z][h]
+                dC = np.linalg.norm(grams[zi, h] - C, 2)
+                th = ref["theta" + z][h]
+                assert np.abs(ritz[zi, h] - th).max() <= 2 * dC + 1e-10 * th[0], (z, h)
+                gaps = _ritz_order_gaps(th)
+                B64 = ref[z + "64"][h]
+                for i in range(cfg.r_max):
+                    v = B64[i]
+                    res = np.linalg.norm(C @ v - th[i] * v) / th[0]
+                    if res > 1e-9 or gaps[i] < 100 * dC:
+                        continue
+                    ulp = np.spacing(np.abs(v).astype(np.float16)).astype(np.float64)
+                    tol = 0.5 * ulp + 2 * np.sqrt(2) * dC / gaps[i] + 1e-9
+                    assert np.all(np.abs(got[h, i].astype(np.float64) - v) <= tol), (z, h, i)
+    finally:
+        cache.close()
+
+
+def _encode(G, cache, cfg, layer, K, V, lengths, tier, gK=None, gV=None):
+    cache.prefill_encode(layer, G.dev(K), G.dev(V), G.dev(np.asarray(lengths, np.int32)), G.dev(tier),
+                         None if gK is None else G.dev(gK), None if gV is None else G.dev(gV))
+
+
+def _compare_layer(cfg, got, ref, lengths):
+    cb = cfg.coef_bits
+    fields = ["tier"] + [f + z for z in "KV" for f in ("coef", "idx", "val", "scale")]
+    if cb == 8:
+        fields += ["cscaleK", "cscaleV"]
+    for b, n in enumerate(lengths):
+        for f in fields:
+            g = got[f][b, :, :n]
+            r = ref[f][b, :, :n]
+            if f.startswith(("idx", "val")):
+                # only each token's own s_k entries are defined
+                res = np.asarray(cfg.resid_per_tier)[ref["tier"][b, :, :n]]
+                mask = np.arange(cfg.s_max)[None, None, :] < res[..., None]
+                g, r = np.where(mask, g[..., :cfg.s_max], 0), np.where(mask, r, 0)
+            if f.startswith("scale"):
+                res = np.asarray(cfg.resid_per_tier)[ref["tier"][b, :, :n]]
+                g, r = np.where(res > 0, g.view(np.uint16), 0), np.where(res > 0, r.view(np.uint16), 0)
+            gv = g.view(np.uint16) if g.dtype == np.float16 else g
+            rv = r.view(np.uint16) if r.dtype == np.float16 else r
+            bad = np.argwhere(gv != rv)
+            assert bad.size == 0, f"b={b} {f}: {len(bad)} mismatches, first {bad[:3].tolist()}"
+
+
+CASES = {
+    "fp16": dict(cfg=lambda: _cfg8k(batch=3), gates=True),
+    "int8coef": dict(cfg=lambda: _cfg8k(batch=3, coef_bits=8), gates=True),
+    "d64_8bit_resid": dict(cfg=lambda: tiny_config(batch=3, num_kv_heads=2, num_q_heads=8, head_dim=64, r_max=32,
+                                                   tier_rank=(4, 8, 16, 32), tier_prob=(0.4, 0.3, 0.2, 0.1),
+                                                   resid_channels=4, resid_bits=8, n_tokens=3000), gates=False),
+    "paper_literal": dict(cfg=lambda: _cfg8k(batch=3, r_max=32, tier_rank=(32,) * 4, tier_prob=(0.4, 0.3, 0.2, 0.1),
+                                             tier_resid=(0, 2, 4, 8)), gates=True),
+}
+
+
+@pytest.mark.parametrize("case", sorted(CASES))
+def test_prefill_encode_bit_exact(G, case):
+    cfg = CASES[case]["cfg"]()
+    lengths = [3000, 1777, 0]
+    layer = cfg.layers_per_group + 1 if cfg.num_layers > cfg.layers_per_group else 0
+    m = layer // cfg.layers_per_group
+    bases = make_bases(cfg)
+    K, V = gen_prefill(cfg, layer, lengths=lengths, tail=np.nan)
+    tier = gen_tiers(cfg, layer, 3000)
+    gK, gV = gen_gates(cfg, layer, 3000) if CASES[case]["gates"] else (None, None)
+    cache = _cache(G, cfg, 3000)
+    try:
+        G.load_bases(cache, bases, groups=[m])
+        print(f"prefill encode: {case} lengths={lengths}", flush=True)
+        _encode(G, cache, cfg, layer, K, V, lengths, tier, gK, gV)
+        assert cache.check_errors() == 0
+        got, counts, _ = G.export_np(cache, layer, cfg.batch, 3000)
+        ref = oracle.prefill_encode(cfg, bases["K"][m], bases["V"][m], K, V, lengths, tier, gK, gV)
+        _compare_layer(cfg, got, ref, lengths)
+        for b, n in enumerate(lengths):
+            for h in range(cfg.num_kv_heads):
+                assert list(counts[b, h]) == [int((tier[b, h, :n] == k).sum()) for k in range(cfg.num_tiers)]
+    finally:
+        cache.close()
+
+
+def test_prefill_encode_in_two_chunks_equals_one(G):
+    """1000 positions, then the remaining 2000 in a second call: the layer is
+    the oracle's encoding of all 3000 (positions continue)."""
+    cfg = _cfg8k(batch=2)
+    layer, n, cut = 2, 3000, 1000
+    bases = make_bases(cfg)
+    K, V = gen_prefill(cfg, layer, lengths=[n, n])
+    tier = gen_tiers(cfg, layer, n)
+    gK, gV = gen_gates(cfg, layer, n)
+    cache = _cache(G, cfg, n)
+    try:
+        G.load_bases(cache, bases, groups=[0])
+        _encode(G, cache, cfg, layer, K[:, :, :cut].copy(), V[:, :, :cut].copy(), [cut, cut],
+                tier[:, :, :cut].copy(), gK[:, :, :cut].copy(), gV[:, :, :cut].copy())
+        _encode(G, cache, cfg, layer, K[:, :, cut:].copy(), V[:, :, cut:].copy(), [n - cut, n - cut],
+                tier[:, :, cut:].copy(), gK[:, :, cut:].copy(), gV[:, :, cut:].copy())
+        assert cache.check_errors() == 0
+        got, _, _ = G.export_np(cache, layer, cfg.batch, n)
+        ref = oracle.prefill_encode(cfg, bases["K"][0], bases["V"][0], K, V, [n, n], tier, gK, gV)
+        _compare_layer(cfg, got, ref, [n, n])
+    finally:
+        cache.close()
+
+
+def test_prefill_encode_refusals(G):
+    """A tier beyond the table refuses its (sequence, KV head) as a whole;
+    the others are encoded.  A tier region that would overflow does the
+    same."""
+    cfg = _cfg8k(batch=2)
+    layer, n = 0, 1000
+    bases = make_bases(cfg)
+    K, V = gen_prefill(cfg, layer, lengths=[n, n])
+    tier = gen_tiers(cfg, layer, n)
+    tier[1, 3, 500] = cfg.num_tiers            # one bad token
+    cache = _cache(G, cfg, n)
+    try:
+        G.load_bases(cache, bases, groups=[0])
+        _encode(G, cache, cfg, layer, K, V, [n, n], tier)
+        assert cache.check_errors() & DEVERR_BAD_TIER
+        counts = cache.read_counts(layer, cfg.batch)
+        assert counts[1, 3].sum() == 0
+        assert counts[0].sum() == cfg.num_kv_heads * n and counts[1].sum() == (cfg.num_kv_heads - 1) * n
+        cache.clear_errors()
+        got, _, _ = G.export_np(cache, layer, cfg.batch, n)
+        ref = oracle.prefill_encode(cfg, bases["K"][0], bases["V"][0], K[:1], V[:1], [n], tier[:1])
+        for f in ("coefK", "scaleV", "idxK"):
+            assert np.array_equal(got[f][0].view(np.uint8), ref[f][0].view(np.uint8))
+    finally:
+        cache.close()
+    # a tier region too small for the prefill
+    small = G.make_cache(cfg, capacity=[n // 4, n, n, n], max_tokens=n + 16, n=n)
+    try:
+        G.load_bases(small, bases, groups=[0])
+        tier = gen_tiers(cfg, layer, n)
+        _encode(G, small, cfg, layer, K, V, [n, n], tier)
+        assert small.check_errors() & DEVERR_TIER_FULL
+        assert small.read_counts(layer, cfg.batch).sum() == 0
+    finally:
+        small.close()
+
+
+def test_prefill_chain_decodes_like_the_oracle_chain(G):
+    """Gram, bases and encode for a window, then decode attention: the GPU
+    chain's error against dense attention over the original keys and
+    values is that of the oracle's own chain."""
+    import torch
+    cfg = _cfg8k(batch=2)
+    lengths = [4000, 2500]
+    Ks, Vs = _window(cfg, lengths, tail=0.0)
+    k, q = cfg.r_max + 8, 2
+    omega = gen_sketch(cfg, k)
+    cache = _cache(G, cfg, 4000)
+    try:
+        _grams(G, cache, cfg, Ks, Vs, lengths)
+        cache.prefill_bases(0, G.dev(omega[0:1]), q)
+        for i in range(cfg.layers_per_group):
+            tier = gen_tiers(cfg, i, 4000)
+            _encode(G, cache, cfg, i, Ks[i], Vs[i], lengths, tier)
+        assert cache.check_errors() == 0
+        ref = oracle.prefill_bases(cfg, Ks, Vs, lengths, omega[0], q)
+        for i in (0, cfg.layers_per_group - 1):
+            qv = gen_query(cfg, i)
+            got = G.decode_np(cache, i, qv)
+            dense = oracle.dense_decode(Ks[i], Vs[i], lengths, qv)
+            lay = oracle.prefill_encode(cfg, ref["K"], ref["V"], Ks[i], Vs[i], lengths, gen_tiers(cfg, i, 4000))
+            chain = oracle.decode(cfg, lay, ref["K"], ref["V"], qv)
+            e_gpu = G.norm_err(got, dense).max()
+            e_or = G.norm_err(chain, dense).max()
+            print(f"layer {i}: gpu chain {e_gpu:.3e}, oracle chain {e_or:.3e}")
+            assert e_gpu <= 1.5 * e_or + 2e-3
+    finally:
+        cache.close()
+
+
+def test_prefill_full_size_64k(G):
+    """The 64K-token Llama-3-8B shape of the benchmark (one window: 4
+    layers, 8 KV heads): the Gram sums within the fp32 bound, the Ritz
+    values within Weyl's bound, and 4096 sampled tokens of each layer
+    encoded bit-exactly."""
+    import torch
+    cfg = w.get_config(2)
+    n = cfg.n_tokens
+    lengths = [n]
+    print("prefill 64K: generating", flush=True)
+    Ks, Vs = _window(cfg, lengths, tail=0.0)
+    k, q = cfg.r_max + 8, 2
+    omega = gen_sketch(cfg, k)
+    cache = _cache(G, cfg, n)
+    try:
+        print("prefill 64K: gram", flush=True)
+        grams = _grams(G, cache, cfg, Ks, Vs, lengths)
+        bk, bv, ritz = _bases(G, cache, cfg, omega, q)
+        tiers = [gen_tiers(cfg, i, n) for i in range(cfg.layers_per_group)]
+        for i in range(cfg.layers_per_group):
+            _encode(G, cache, cfg, i, Ks[i], Vs[i], lengths, tiers[i])
+        assert cache.check_errors() == 0
+        print("prefill 64K: oracle", flush=True)
+        ref = oracle.prefill_bases(cfg, Ks, Vs, lengths, omega[0], q)
+        for zi, z in enumerate("KV"):
+            for h in range(cfg.num_kv_heads):
+                C = ref["gram" + z][h]
+                bound = n * cfg.layers_per_group * 2.0 ** -24 * _abs_gram(cfg, Ks, Vs, lengths, zi, h)
+                assert np.all(np.abs(grams[zi, h] - C) <= bound)
+                dC = np.linalg.norm(grams[zi, h] - C, 2)
+                th = ref["theta" + z][h]
+                assert np.abs(ritz[zi, h] - th).max() <= 2 * dC + 1e-10 * th[0]
+        # the encoder at this shape, on the oracle's bases (an oracle input
+        # never comes from the GPU), against the oracle on a token sample
+        bases = {"K": ref["K"][None], "V": ref["V"][None]}
+        rng = np.random.default_rng(7)
+        sample = np.sort(rng.choice(n, 4096, replace=False))
+        for i in (0, cfg.layers_per_group - 1):
+            fresh = _cache(G, cfg, n)
+            try:
+                G.load_bases(fresh, bases, groups=[0])
+                _encode(G, fresh, cfg, i, Ks[i], Vs[i], lengths, tiers[i])
+                assert fresh.check_errors() == 0
+                got, _, _ = G.export_np(fresh, i, 1, n)
+            finally:
+                fresh.close()
+            sub = {k2: np.ascontiguousarray(v[:, :, sample]) for k2, v in got.items()}
+            ref_lay = oracle.prefill_encode(cfg, ref["K"], ref["V"], np.ascontiguousarray(Ks[i][:, :, sample]),
+                                            np.ascontiguousarray(Vs[i][:, :, sample]), [len(sample)],
+                                            np.ascontiguousarray(tiers[i][:, :, sample]))
+            _compare_layer(cfg, sub, ref_lay, [len(sample)])
+    finally:
+        cache.close()
