@@ -77,6 +77,10 @@ def parse_args():
     p.add_argument("--trace-summary", metavar="TRACE_DIR",
                    help="summarise a rocprofv3 --kernel-trace --stats run of this script into "
                         "profiles/ and exit")
+    p.add_argument("--mode", choices=["decode", "prefill"], default="decode",
+                   help="decode: the decode step (the headline); prefill: compression of the workload's "
+                        "prompt into the cache (Gram sums, bases, bulk encode for every layer)")
+    p.add_argument("--power-iters", type=int, default=2, help="prefill: range-finder power iterations")
     p.add_argument("--bench-json", metavar="FILE",
                    help="with --trace-summary: the JSON line of a default run of the same build, "
                         "quoted beside the trace; with --pmc-summary: the counter run's own JSON line "
@@ -432,6 +436,172 @@ def run_dense(args, cfg, K: int, W: int):
     }
 
 
+PREFILL_METRIC = "prefill compression tokens/s (prompt tokens, all layers: Gram sums, bases, bulk encode)"
+
+
+def prefill_step_bytes(cfg, tiers) -> dict:
+    """Algorithmic bytes of one prefill compression of the whole model, per
+    kernel family: the Gram pass reads every prefill key and value once;
+    the bases read each window's Gram matrices once and write the bases;
+    the encoder reads every key and value and its tier once and writes each
+    token at its tier's size plus its position-map entry.  tiers: the
+    per-layer tier arrays of one window (they stand for every window)."""
+    L, B, H, d, n, lpg = cfg.num_layers, cfg.batch, cfg.num_kv_heads, cfg.head_dim, cfg.n_tokens, cfg.layers_per_group
+    kv = B * H * n * d * 2 * 2
+    per_tok = np.array([w.compressed_bytes_per_token(r, s, cfg.resid_bits, cfg.coef_bits)
+                        for r, s in zip(cfg.tier_rank, cfg.resid_per_tier)])
+    enc = []
+    for l in range(L):
+        t = tiers[l % lpg]
+        enc.append(kv + B * H * n + float(per_tok[t.reshape(-1).astype(np.int64)].sum()) + B * H * n * 4)
+    bases = cfg.num_groups * (2 * H * d * d * 8 + 2 * H * cfg.r_max * d * 2 * 3)
+    return {"gram_per_layer": kv, "encode_per_layer": float(np.mean(enc)), "bases_total": bases,
+            "total": kv * L + sum(enc) + bases}
+
+
+def _gen_prefill_job(args):
+    ci, layer = args
+    from workload.gen import gen_prefill
+    return gen_prefill(w.get_config(ci), layer)
+
+
+def run_prefill(args, cfg, K: int, W: int):
+    """Prefill compression of the workload's prompt for every layer: Gram
+    sums of every layer, the bases of every window in one launch, then the
+    bulk encode of every layer.  One window's prefill keys, values and tiers
+    (seeded, the generator's distributions) stand in for every window's."""
+    import torch
+    from workload.gen import gen_sketch, gen_tiers
+    from compressed_kv_cache_dwkv_amd import dwkv_reset
+    from compressed_kv_cache_dwkv_amd.cache import CompressedKVCache
+    L, B, H, d, n, lpg = cfg.num_layers, cfg.batch, cfg.num_kv_heads, cfg.head_dim, cfg.n_tokens, cfg.layers_per_group
+    t0 = time.perf_counter()
+    with ProcessPoolExecutor(max_workers=min(lpg, len(os.sched_getaffinity(0)))) as ex:
+        kvs = list(ex.map(_gen_prefill_job, [(args.config, l) for l in range(lpg)]))
+    tiers = [gen_tiers(cfg, l, n) for l in range(lpg)]
+    sketch = min(cfg.r_max + 8, cfg.head_dim)
+    omega = gen_sketch(cfg, sketch)
+    print(f"bench: prefill inputs generated ({time.perf_counter() - t0:.1f} s)", file=sys.stderr, flush=True)
+    torch.cuda.set_device(0)
+    cap = [int(c) + 16 for c in max_tier_counts(cfg)]
+    cache = CompressedKVCache(L, lpg, cfg.num_q_heads, H, d, cfg.r_max, cfg.tier_rank, cfg.resid_per_tier,
+                              cfg.resid_bits, B, cap, n + 16, coef_bits=cfg.coef_bits)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    k_dev = [dev(kv[0]) for kv in kvs]
+    v_dev = [dev(kv[1]) for kv in kvs]
+    del kvs
+    t_dev = [dev(t) for t in tiers]
+    om_dev = dev(omega)
+    n_dev = torch.full((B,), n, dtype=torch.int32, device="cuda")
+    cache.prefill_workspace()
+    h = cache.handle
+    q = args.power_iters
+
+    def grams():
+        for l in range(L):
+            cache.prefill_gram(l, k_dev[l % lpg], v_dev[l % lpg], n_dev, first=(l % lpg == 0))
+
+    def bases():
+        cache.prefill_bases(0, om_dev, q)
+
+    def encodes():
+        dwkv_reset(h)
+        for l in range(L):
+            cache.prefill_encode(l, k_dev[l % lpg], v_dev[l % lpg], n_dev, t_dev[l % lpg])
+
+    def step(s):
+        grams()
+        bases()
+        encodes()
+
+    elapsed_ms = _time_graph_steps(step, W, K, 1)
+    assert cache.check_errors() == 0, "prefill overflowed the cache"
+    gram_ms = _graph_launch_ms(grams, args.kernel_reps)
+    bases_ms = _graph_launch_ms(bases, args.kernel_reps)
+    enc_ms = _graph_launch_ms(encodes, args.kernel_reps)
+    assert cache.check_errors() == 0
+    by = prefill_step_bytes(cfg, tiers)
+    ms_per_step = elapsed_ms / K
+    gram_launch_ms = gram_ms / L
+    enc_layer_ms = enc_ms / L
+    fam = {"gram": gram_ms, "bases": bases_ms, "encode": enc_ms}
+    dominant = max(fam, key=fam.get)
+    # the encoder's arithmetic: per vector r d fp32 FMAs for the projection
+    # and r d for the residual (2 flops each), K and V of every token
+    r_tok = np.asarray(cfg.tier_rank)[np.concatenate([t.reshape(-1) for t in tiers]).astype(np.int64)]
+    enc_flop_layer = float(r_tok.sum()) / lpg * d * 2 * 2 * 2
+    if dominant == "gram":
+        roof = {"bound": "hbm", "kernel": "gram_kernel", "achieved": by["gram_per_layer"] / (gram_launch_ms * 1e-3) / 1e9,
+                "peak": PEAK_HBM_GBPS, "unit": "GB/s", "algorithmic_bytes_per_launch": by["gram_per_layer"],
+                "mean_launch_us": gram_launch_ms * 1e3}
+    else:
+        roof = {"bound": "alu", "kernel": "encode_kernel (+ slot and publish passes)",
+                "achieved": enc_flop_layer / (enc_layer_ms * 1e-3) / 1e12, "peak": 157.3, "unit": "TFLOP/s",
+                "algorithmic_flop_per_launch": enc_flop_layer, "mean_launch_us": enc_layer_ms * 1e3,
+                "hbm_GBps": by["encode_per_layer"] / (enc_layer_ms * 1e-3) / 1e9}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["launch_time_from"] = "replays of a graph of one step's launches of that kernel family"
+    res = {
+        "metric": PREFILL_METRIC, "value": B * n * K / (elapsed_ms / 1e3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": K, "warmup": W, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp16 inputs; fp16 MFMA + fp32 (Gram), fp64 (bases), fp32 (encoder)",
+        "data": "synthetic",
+        "config": {"workload": cfg.name + "-prefill", "batch": B, "context": n, "layers": L, "kv_heads": H,
+                   "head_dim": d, "layers_per_basis": lpg, "r_max": cfg.r_max, "sketch": sketch,
+                   "power_iters": q, "tier_rank": list(cfg.tier_rank), "tier_mix": list(cfg.tier_prob),
+                   "resid_channels": cfg.resid_channels, "resid_bits": cfg.resid_bits, "coef_bits": cfg.coef_bits,
+                   "inputs": "one window's prefill K/V and tiers stand in for every window's"},
+        "step_GBps": by["total"] / (ms_per_step * 1e-3) / 1e9,
+        "step_frac_of_peak": by["total"] / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+        "breakdown": {"gram_ms": gram_ms, "bases_ms": bases_ms, "encode_ms": enc_ms, "reset_in_encode": True,
+                      "gram_GBps": by["gram_per_layer"] / (gram_launch_ms * 1e-3) / 1e9,
+                      "encode_GBps": by["encode_per_layer"] / (enc_layer_ms * 1e-3) / 1e9,
+                      "algorithmic_bytes": by},
+        "roofline": roof,
+        "cpu_baseline": None if args.no_cpu_baseline else prefill_cpu_baseline(cfg, args.cpu_seconds),
+    }
+    cache.close()
+    return res
+
+
+def prefill_cpu_baseline(cfg, budget_s: float):
+    """The oracle's prefill compression on a bounded sample: one window's
+    Gram sums and bases over the first n_s tokens, and the bulk encode of
+    those tokens for every layer of the window, n_s doubled until the
+    budget is spent; scaled to prompt tokens per second over all layers."""
+    import oracle
+    from workload.gen import gen_prefill, gen_sketch, gen_tiers
+    lpg = cfg.layers_per_group
+    sketch = min(cfg.r_max + 8, cfg.head_dim)
+    omega = gen_sketch(cfg, sketch)[0]
+    host = len(os.sched_getaffinity(0))
+    threads = min(oracle.max_threads(), host)
+    ns, best = 256, None
+    total = 0.0
+    while total < budget_s and ns <= cfg.n_tokens:
+        Ks, Vs, ts = [], [], []
+        for l in range(lpg):
+            K, V = gen_prefill(cfg, l, n=ns)
+            Ks.append(K)
+            Vs.append(V)
+            ts.append(gen_tiers(cfg, l, ns))
+        t0 = time.perf_counter()
+        bs = oracle.prefill_bases(cfg, Ks, Vs, [ns] * cfg.batch, omega, 2)
+        for l in range(lpg):
+            oracle.prefill_encode(cfg, bs["K"], bs["V"], Ks[l], Vs[l], [ns] * cfg.batch, ts[l], nthreads=threads)
+        dt = time.perf_counter() - t0
+        total += dt
+        best = (ns, dt)
+        ns *= 2
+    ns, dt = best
+    return {"value": cfg.batch * ns / (dt * cfg.num_layers / lpg), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle", "host_cores": host, "cpu_model": _cpu_model(),
+            "sample": f"one window ({lpg} layers) of a {ns}-token prompt: Gram sums and bases (fp64 NumPy), "
+                      f"then the bulk encode of every token (C, {threads} threads), {dt:.2f} s, "
+                      f"scaled to {cfg.num_layers} layers"}
+
+
 def main():
     args = parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -450,6 +620,11 @@ def main():
     L, B, H = cfg.num_layers, cfg.batch, cfg.num_kv_heads
     if args.comparator == "dense":
         print(json.dumps(run_dense(args, cfg, K, W)), flush=True)
+        return
+    if args.mode == "prefill":
+        K = args.steps if args.steps is not None else 10
+        W = min(W, 2)
+        print(json.dumps(run_prefill(args, cfg, K, W)), flush=True)
         return
 
     # ---- synthetic inputs (host): the layer generators start before the

@@ -655,13 +655,15 @@ static int gram_splits(const Layout &ly)
 }
 
 // Prefill workspace: the Gram sums of every window (fp64, first, so that
-// their offset is 0), the Gram partials, the arrival counters, then the
-// encoder's per-(sequence, KV head) status and tier counts.
+// their offset is 0), the Gram partials, then the encoder's per-(sequence,
+// KV head) status, tier counts and tier-ordered token lists, and the
+// window's bases in fp32.
 struct PrefillWs {
     double *acc;
     float *part;
-    uint32_t *arrive;
-    int32_t *status, *newcnt;
+    int32_t *status, *cnt0, *tot, *inv, *cntc;
+    int n_chunks;
+    float *brows, *bcols;
     size_t bytes;
 };
 
@@ -678,9 +680,14 @@ static PrefillWs carve_prefill(const Layout &ly, void *base)
     const int64_t dd = (int64_t)ly.d * ly.d;
     w.acc = reinterpret_cast<double *>(take((int64_t)ly.num_groups * 2 * ly.Hkv * dd * 8));
     w.part = reinterpret_cast<float *>(take((int64_t)2 * ly.Hkv * gram_splits(ly) * dwkv::gram_pairs(ly.d) * 256 * 4));
-    w.arrive = reinterpret_cast<uint32_t *>(take((int64_t)2 * ly.Hkv * dwkv::kArriveStride * 4));
     w.status = reinterpret_cast<int32_t *>(take((int64_t)ly.Bmax * ly.Hkv * 4));
-    w.newcnt = reinterpret_cast<int32_t *>(take((int64_t)ly.Bmax * ly.Hkv * dwkv::kMaxTiers * 4));
+    w.cnt0 = reinterpret_cast<int32_t *>(take((int64_t)ly.Bmax * ly.Hkv * dwkv::kMaxTiers * 4));
+    w.tot = reinterpret_cast<int32_t *>(take((int64_t)ly.Bmax * ly.Hkv * dwkv::kMaxTiers * 4));
+    w.inv = reinterpret_cast<int32_t *>(take((int64_t)ly.Bmax * ly.Hkv * ly.max_tokens * 4));
+    w.n_chunks = (int)((ly.max_tokens + dwkv::kSlotChunk - 1) / dwkv::kSlotChunk) + 1;
+    w.cntc = reinterpret_cast<int32_t *>(take((int64_t)ly.Bmax * ly.Hkv * w.n_chunks * dwkv::kChunkStride * 4));
+    w.brows = reinterpret_cast<float *>(take((int64_t)2 * ly.basis_elems * 4));
+    w.bcols = reinterpret_cast<float *>(take((int64_t)2 * ly.Hkv * ly.d * dwkv::kMaxRank * 4));
     w.bytes = off;
     return w;
 }
@@ -728,7 +735,6 @@ int dwkv_prefill_gram(dwkv_handle *h, int layer, const void *k, const void *v, c
     a.first = first ? 1 : 0;
     a.part = w.part;
     a.acc = w.acc + (int64_t)(layer / ly.G) * 2 * ly.Hkv * ly.d * ly.d;
-    a.arrive = w.arrive;
     return hip_status(dwkv::launch_gram(ly, h->arena, a, static_cast<hipStream_t>(stream)));
 }
 
@@ -772,7 +778,16 @@ int dwkv_prefill_encode(dwkv_handle *h, int layer, const void *k, const void *v,
     a.gateK = static_cast<const uint16_t *>(gate_k);
     a.gateV = static_cast<const uint16_t *>(gate_v);
     a.status = w.status;
-    a.newcnt = w.newcnt;
+    a.cnt0 = w.cnt0;
+    a.tot = w.tot;
+    a.inv = w.inv;
+    a.basis_rows = w.brows;
+    a.basis_cols = w.bcols;
+    a.cntc = w.cntc;
+    {
+        const int64_t need = (n_cap + dwkv::kSlotChunk - 1) / dwkv::kSlotChunk;
+        a.n_chunks = (int)(need < w.n_chunks ? (need < 1 ? 1 : need) : w.n_chunks);
+    }
     return hip_status(dwkv::launch_prefill_encode(ly, h->arena, a, batch, static_cast<hipStream_t>(stream)));
 }
 

@@ -94,6 +94,8 @@ constexpr int kGramMaxBatch = 1024;   // sequences per Gram call
 constexpr int kGramMaxSplits = 128;   // workgroups per (Z, KV head) of a Gram call
 constexpr int kMaxSketch = 72;        // sketch width k (LDS: two head_dim x k fp64 matrices)
 constexpr int kJacobiMaxSweeps = 40;
+constexpr int kSlotChunk = 1024;      // positions per chunk of the encoder's count and place passes
+constexpr int kChunkStride = 16;      // ints per chunk record (tier counts, then the bad-tier flag)
 
 // Number of 16x16 blocks on and above the diagonal of a head_dim^2 matrix.
 constexpr int gram_pairs(int d) { return (d / 16) * (d / 16 + 1) / 2; }
@@ -107,7 +109,6 @@ struct GramArgs {
     int first;                    // 1: the window's sums start here
     float *part;                  // [2 Hkv][S][gram_pairs(d) * 256] partial sums
     double *acc;                  // the window's [2][Hkv][d][d] sums
-    uint32_t *arrive;             // [2 Hkv][kArriveStride]
 };
 hipError_t launch_gram(const Layout &ly, uint8_t *arena, const GramArgs &a, hipStream_t stream);
 
@@ -129,7 +130,11 @@ struct EncodeArgs {
     const uint8_t *tier;          // [B][Hkv][n_cap]
     const uint16_t *gateK, *gateV;  // fp16 [B][Hkv][n_cap], or null
     int32_t *status;              // [B][Hkv] first position, or -1 if refused
-    int32_t *newcnt;              // [B][Hkv][kMaxTiers]
+    int32_t *cnt0, *tot;          // [B][Hkv][kMaxTiers] tier counts before the call, tokens added
+    int32_t *inv;                 // [B][Hkv][max_tokens] the call's tokens listed by tier
+    int32_t *cntc;                // [B][Hkv][n_chunks][kChunkStride] tier counts per chunk (+ a bad-tier flag)
+    int n_chunks;                 // chunks of kSlotChunk positions the call's counts cover
+    float *basis_rows, *basis_cols;  // the window's bases in fp32, [2][Hkv][r_max][d] and [2][Hkv][d][kMaxRank]
 };
 hipError_t launch_prefill_encode(const Layout &ly, uint8_t *arena, const EncodeArgs &a, int batch,
                                  hipStream_t stream);

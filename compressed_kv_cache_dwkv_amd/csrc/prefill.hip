@@ -10,8 +10,8 @@
 //             C^Z_h = sum over sequences b and positions t < n_b of x x^T:
 //             64-token tiles staged through LDS in a transposed, swizzled
 //             layout and contracted over tokens on the matrix cores (fp16
-//             operands, exact products, fp32 sums per workgroup); the last
-//             workgroup of a (Z, h) adds the fp32 partials in fp64, in split
+//             operands, exact products, fp32 sums per workgroup); a second
+//             kernel adds each element's fp32 partials in fp64, in split
 //             order, into the window's fp64 accumulator in the workspace.
 //   bases  -- one workgroup per (window, Z, h), in fp64: the randomized
 //             range finder with power iterations and a Rayleigh-Ritz step
@@ -20,15 +20,15 @@
 //             parallel cyclic Jacobi eigensolver (round-robin pairs); the
 //             Ritz vectors in decreasing Ritz value, sign-normalised, become
 //             the basis rows in fp16 (rounded once from fp64).
-//   encode -- a slot pass gives every prefill token its tier slot and
+//   encode -- count and place passes give every prefill token its tier slot and
 //             position-map entry (an append's admission, for all tokens of a
-//             (sequence, KV head) at once); the encoder runs the append's
-//             own body (append_body.h) over the tokens, several per wave with
-//             the basis rows kept in registers; a publish pass sets the tier
-//             counts.
+//             (sequence, KV head) at once) and lists the tokens by tier; the
+//             encoder takes 64 tokens of one tier per wave, one per lane, and
+//             follows the append's order of operations exactly (so it gives
+//             the append's bits), the basis values reaching every lane
+//             through scalar loads; a publish pass sets the tier counts.
 #include <hip/hip_runtime.h>
 
-#include "append_body.h"
 #include "device.h"
 #include "kernels.h"
 #include "layout.h"
@@ -87,15 +87,16 @@ __device__ __forceinline__ float4_t mfma32(half8_t a, half8_t b, float4_t c)
 }
 
 // The products of wave W's blocks (pairs W, W + 4, ...) for one 32-token
-// step: f[c] is the fragment of channel block c.
-template <int D, int W>
+// step: f[c] is the fragment of channel block c.  The block indices are
+// template arguments, so every operand is a fixed register.
+template <int D, int W, int IDX>
 __device__ __forceinline__ void gram_mma(const half8_t (&f)[D / 16], float4_t (&acc)[(D / 16 * (D / 16 + 1) / 2 + 3) / 4])
 {
-    constexpr int NB = D / 16, NP = NB * (NB + 1) / 2, PW = (NP + 3) / 4;
-#pragma unroll
-    for (int i = 0; i < PW; ++i) {
-        const int p = W + 4 * i;
-        if (p < NP) acc[i] = mfma32(f[pair_i(p, NB)], f[pair_j(p, NB)], acc[i]);
+    constexpr int NB = D / 16, NP = NB * (NB + 1) / 2, P = W + 4 * IDX;
+    if constexpr (P < NP) {
+        constexpr int I = pair_i(P, NB), J = pair_j(P, NB);
+        acc[IDX] = mfma32(f[I], f[J], acc[IDX]);
+        gram_mma<D, W, IDX + 1>(f, acc);
     }
 }
 
@@ -106,7 +107,6 @@ __global__ __launch_bounds__(kGramThreads) void gram_kernel(Layout ly, uint8_t *
     constexpr int CPR = D / 8;                  // 16-byte pieces of a token row
     __shared__ __attribute__((aligned(16))) uint16_t sT[2][D * kGramTile];
     __shared__ int s_tile0[kGramMaxBatch + 1];  // first flat tile of each sequence
-    __shared__ int s_last;
 
     const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
     const int s = blockIdx.x, zh = blockIdx.y;
@@ -178,10 +178,10 @@ __global__ __launch_bounds__(kGramThreads) void gram_kernel(Layout ly, uint8_t *
                 fr[c] = *reinterpret_cast<const half8_t *>(&sT[buf][ch * kGramTile + 8 * (g ^ gram_swz(ch))]);
             }
             switch (wave) {
-            case 0: gram_mma<D, 0>(fr, acc); break;
-            case 1: gram_mma<D, 1>(fr, acc); break;
-            case 2: gram_mma<D, 2>(fr, acc); break;
-            default: gram_mma<D, 3>(fr, acc); break;
+            case 0: gram_mma<D, 0, 0>(fr, acc); break;
+            case 1: gram_mma<D, 1, 0>(fr, acc); break;
+            case 2: gram_mma<D, 2, 0>(fr, acc); break;
+            default: gram_mma<D, 3, 0>(fr, acc); break;
             }
         }
     }
@@ -197,32 +197,35 @@ __global__ __launch_bounds__(kGramThreads) void gram_kernel(Layout ly, uint8_t *
             for (int j = 0; j < 4; ++j) part[(p * 4 + j) * kWave + lane] = acc[i][j];
         }
     }
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-        const uint32_t old = __hip_atomic_fetch_add(a.arrive + zh * kArriveStride, 1u, __ATOMIC_ACQ_REL,
-                                                    __HIP_MEMORY_SCOPE_AGENT);
-        s_last = old == (uint32_t)(a.S - 1);
-    }
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
+}
 
-    // the last workgroup: sum the partials in split order, in fp64
-    double *C = a.acc + (int64_t)zh * D * D;
-    const float *P = a.part + (int64_t)zh * a.S * NP * 256;
-    for (int e = tid; e < NP * 256; e += kGramThreads) {
-        const int p = e >> 8, j = (e >> 6) & 3, l = e & 63;
-        const int row = 16 * pair_i(p, NB) + 4 * (l >> 4) + j, col = 16 * pair_j(p, NB) + (l & 15);
-        if (row > col) continue;                   // a diagonal block's lower half mirrors its upper half
-        double sum = 0.0;
-        for (int q = 0; q < a.S; ++q) sum += (double)__builtin_nontemporal_load(P + (int64_t)q * NP * 256 + e);
-        const double v = a.first ? sum : C[row * D + col] + sum;
-        C[row * D + col] = v;
-        C[col * D + row] = v;
+// Sums the S partials of each Gram element in split order, in fp64, into
+// the window's accumulator (or over it with a.first), and mirrors it: one
+// thread per element of the blocks on and above the diagonal.
+template <int D>
+__global__ __launch_bounds__(256) void gram_reduce_kernel(GramArgs a)
+{
+    constexpr int NB = D / 16, NP = NB * (NB + 1) / 2;
+    const int zh = blockIdx.y, e = blockIdx.x * 256 + threadIdx.x;
+    if (e >= NP * 256) return;
+    const int p = e >> 8, j = (e >> 6) & 3, l = e & 63;
+    const int row = 16 * pair_i(p, NB) + 4 * (l >> 4) + j, col = 16 * pair_j(p, NB) + (l & 15);
+    if (row > col) return;                        // a diagonal block's lower half mirrors its upper half
+    const float *P = a.part + (int64_t)zh * a.S * NP * 256 + e;
+    double sum = 0.0;
+    int q = 0;
+    for (; q + 8 <= a.S; q += 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = P[(int64_t)(q + u) * NP * 256];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) sum += (double)v[u];
     }
-    if (tid == 0)
-        __hip_atomic_store(a.arrive + zh * kArriveStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (; q < a.S; ++q) sum += (double)P[(int64_t)q * NP * 256];
+    double *C = a.acc + (int64_t)zh * D * D;
+    const double v = a.first ? sum : C[row * D + col] + sum;
+    C[row * D + col] = v;
+    C[col * D + row] = v;
 }
 
 // ------------------------------------------------------------------ bases
@@ -312,37 +315,49 @@ __device__ void gemm_cq(const double *C, const double *src, double *dst, int k)
 // Q (LDS [D][k]) = k orthonormal columns spanning W's: classical
 // Gram-Schmidt twice per column over the columns of [W | I], a column kept
 // unless its norm after the two passes is at most 2^-40 of its norm before.
+// The projections' sums are split over the workgroup's four quarters
+// (partials in sp, [4][max(D, k)]) and added in quarter order.
 template <int D>
-__device__ void orth(const double *W, double *Q, int k, double *sv, double *sr, double *sred)
+__device__ void orth(const double *W, double *Q, int k, double *sv, double *sr, double *sp, double *sred)
 {
-    const int tid = threadIdx.x;
+    constexpr int QT = kBasesThreads / 4;          // threads per quarter (128)
+    const int tid = threadIdx.x, qi = tid / QT, qt = tid % QT;
     int kept = 0;
     for (int cand = 0; kept < k && cand < k + D; ++cand) {
         if (tid < D) sv[tid] = cand < k ? W[tid * k + cand] : (tid == cand - k ? 1.0 : 0.0);
         double mine = tid < D ? sv[tid] : 0.0;
         const double n0 = sqrt(block_sum(mine * mine, sred));
         for (int pass = 0; pass < 2 && kept > 0; ++pass) {
-            if (tid < kept) {
-                double p0 = 0.0, p1 = 0.0, p2 = 0.0, p3 = 0.0;
-                for (int i = 0; i < D; i += 4) {
-                    p0 = fma(Q[i * k + tid], sv[i], p0);
-                    p1 = fma(Q[(i + 1) * k + tid], sv[i + 1], p1);
-                    p2 = fma(Q[(i + 2) * k + tid], sv[i + 2], p2);
-                    p3 = fma(Q[(i + 3) * k + tid], sv[i + 3], p3);
+            // r = Q[:, :kept]^T v: quarter qi sums rows [qi D/4, (qi+1) D/4)
+            if (qt < kept) {
+                double p0 = 0.0, p1 = 0.0;
+                const int i0 = qi * (D / 4);
+#pragma unroll 4
+                for (int i = i0; i < i0 + D / 4; i += 2) {
+                    p0 = fma(Q[i * k + qt], sv[i], p0);
+                    p1 = fma(Q[(i + 1) * k + qt], sv[i + 1], p1);
                 }
-                sr[tid] = (p0 + p1) + (p2 + p3);
+                sp[qi * kMaxSketch + qt] = p0 + p1;
             }
             __syncthreads();
-            if (tid < D) {
+            if (tid < kept)
+                sr[tid] = ((sp[tid] + sp[kMaxSketch + tid]) + sp[2 * kMaxSketch + tid]) + sp[3 * kMaxSketch + tid];
+            __syncthreads();
+            // v -= Q[:, :kept] r: quarter qi sums columns [c0, c1)
+            if (qt < D) {
+                const int per = (kept + 3) / 4, c0 = qi * per, c1 = min(kept, c0 + per);
                 double p0 = 0.0, p1 = 0.0;
-                int cc = 0;
-                for (; cc + 1 < kept; cc += 2) {
-                    p0 = fma(Q[tid * k + cc], sr[cc], p0);
-                    p1 = fma(Q[tid * k + cc + 1], sr[cc + 1], p1);
+                int cc = c0;
+                for (; cc + 1 < c1; cc += 2) {
+                    p0 = fma(Q[qt * k + cc], sr[cc], p0);
+                    p1 = fma(Q[qt * k + cc + 1], sr[cc + 1], p1);
                 }
-                if (cc < kept) p0 = fma(Q[tid * k + cc], sr[cc], p0);
-                sv[tid] -= p0 + p1;
+                if (cc < c1) p0 = fma(Q[qt * k + cc], sr[cc], p0);
+                sp[qi * kMaxHeadDim + qt] = p0 + p1;
             }
+            __syncthreads();
+            if (tid < D)
+                sv[tid] -= ((sp[tid] + sp[kMaxHeadDim + tid]) + sp[2 * kMaxHeadDim + tid]) + sp[3 * kMaxHeadDim + tid];
             __syncthreads();
         }
         mine = tid < D ? sv[tid] : 0.0;
@@ -367,6 +382,7 @@ __global__ __launch_bounds__(kBasesThreads) void bases_kernel(Layout ly, uint8_t
     __shared__ double sW[kMaxHeadDim * kMaxSketch];
     __shared__ double sv[kMaxHeadDim];
     __shared__ double sr[kMaxSketch + 1];
+    __shared__ double sp[4 * kMaxHeadDim];
     __shared__ double sred[kBasesWaves];
     __shared__ double s_c[kMaxSketch / 2 + 1], s_s[kMaxSketch / 2 + 1];
     __shared__ int s_a[kMaxSketch / 2 + 1], s_b[kMaxSketch / 2 + 1];
@@ -384,11 +400,11 @@ __global__ __launch_bounds__(kBasesThreads) void bases_kernel(Layout ly, uint8_t
     for (int e = tid; e < D * k; e += kBasesThreads) sQ[e] = (double)om[e];
     __syncthreads();
     gemm_cq<D>(C, sQ, sW, k);
-    orth<D>(sW, sQ, k, sv, sr, sred);
+    orth<D>(sW, sQ, k, sv, sr, sp, sred);
     // 3. power iterations
     for (int it = 0; it < a.power_iters; ++it) {
         gemm_cq<D>(C, sQ, sW, k);
-        orth<D>(sW, sQ, k, sv, sr, sred);
+        orth<D>(sW, sQ, k, sv, sr, sp, sred);
     }
     // 4. T = Q^T C Q, symmetrised, into sW
     gemm_cq<D>(C, sQ, sW, k);
@@ -458,7 +474,10 @@ __global__ __launch_bounds__(kBasesThreads) void bases_kernel(Layout ly, uint8_t
                         s = t * c;
                     }
                 } else {
-                    pa = pb = -1;
+                    // the index paired with the absent one (k odd) sits out
+                    // this step: a pair of one, never rotated
+                    pa = pa < k ? pa : pb;
+                    pb = -1;
                 }
                 s_a[tid] = pa;
                 s_b[tid] = pb;
@@ -466,29 +485,39 @@ __global__ __launch_bounds__(kBasesThreads) void bases_kernel(Layout ly, uint8_t
                 s_s[tid] = s;
             }
             __syncthreads();
-            // rows: T <- J^T T
-            for (int e = tid; e < P * k; e += kBasesThreads) {
-                const int p = e / k, j = e % k, pa = s_a[p], pb = s_b[p];
-                if (pa < 0 || s_s[p] == 0.0) continue;
-                const double c = s_c[p], s = s_s[p];
-                const double ta = T[pa * k + j], tb = T[pb * k + j];
-                T[pa * k + j] = c * ta - s * tb;
-                T[pb * k + j] = s * ta + c * tb;
+            // T <- J^T T J one 2x2 block (pairs p, p2) per item, from the
+            // block's old values; Q <- Q J one (row, pair) per item
+            for (int e = tid; e < P * P; e += kBasesThreads) {
+                const int p = e / P, p2 = e - p * P;
+                const int a0 = s_a[p], b0 = s_b[p], a1 = s_a[p2], b1 = s_b[p2];
+                const double c0 = s_c[p], s0 = s_s[p], c1 = s_c[p2], s1 = s_s[p2];
+                if (s0 == 0.0 && s1 == 0.0) continue;
+                const bool hb0 = b0 >= 0, hb1 = b1 >= 0;   // false: a pair of one (s = 0)
+                const double taa = T[a0 * k + a1], tab = hb1 ? T[a0 * k + b1] : 0.0;
+                const double tba = hb0 ? T[b0 * k + a1] : 0.0, tbb = hb0 && hb1 ? T[b0 * k + b1] : 0.0;
+                // rows: J_p^T
+                const double raa = c0 * taa - s0 * tba, rab = c0 * tab - s0 * tbb;
+                const double rba = s0 * taa + c0 * tba, rbb = s0 * tab + c0 * tbb;
+                // columns: J_p2
+                double naa = c1 * raa - s1 * rab, nab = s1 * raa + c1 * rab;
+                double nba = c1 * rba - s1 * rbb, nbb = s1 * rba + c1 * rbb;
+                if (p == p2) {                      // the rotated pair's off-diagonal entries
+                    nab = 0.0;
+                    nba = 0.0;
+                }
+                T[a0 * k + a1] = naa;
+                if (hb1) T[a0 * k + b1] = nab;
+                if (hb0) T[b0 * k + a1] = nba;
+                if (hb0 && hb1) T[b0 * k + b1] = nbb;
             }
-            __syncthreads();
-            // columns: T <- T J, Q <- Q J
-            for (int e = tid; e < P * (k + D); e += kBasesThreads) {
-                const int p = e / (k + D), i = e % (k + D), pa = s_a[p], pb = s_b[p];
-                if (pa < 0 || s_s[p] == 0.0) continue;
-                const double c = s_c[p], s = s_s[p];
-                double *M = i < k ? T : sQ;
-                const int r = i < k ? i : i - k;
-                const double ta = M[r * k + pa], tb = M[r * k + pb];
-                double na = c * ta - s * tb, nb = s * ta + c * tb;
-                if (i < k && r == pa) nb = 0.0;        // the rotated pair's off-diagonal entries
-                if (i < k && r == pb) na = 0.0;
-                M[r * k + pa] = na;
-                M[r * k + pb] = nb;
+            for (int e = tid; e < P * D; e += kBasesThreads) {
+                const int p = e / D, i = e % D;
+                const int a0 = s_a[p], b0 = s_b[p];
+                if (s_s[p] == 0.0) continue;
+                const double c0 = s_c[p], s0 = s_s[p];
+                const double qa = sQ[i * k + a0], qb = sQ[i * k + b0];
+                sQ[i * k + a0] = c0 * qa - s0 * qb;
+                sQ[i * k + b0] = s0 * qa + c0 * qb;
             }
             __syncthreads();
         }
@@ -526,63 +555,103 @@ __global__ __launch_bounds__(kBasesThreads) void bases_kernel(Layout ly, uint8_t
 
 // ------------------------------------------------------------------ encode
 
-constexpr int kEncodeThreads = 256;
-constexpr int kEncodeTokens = 256;   // tokens per workgroup (each wave: half of them, one Z)
+constexpr int kSlotThreads = 256;
 
-// Tier slots of one (sequence, KV head)'s prefill tokens: admission of all
-// of them at once (tiers valid, every tier region and the position map with
-// room), then position n0 + t gets (tier << 28 | slot) with slots in
-// position order after the tier's counted tokens.  status[b][h] = n0, or -1
-// when refused (nothing is written then); newcnt gets the tier counts to
-// publish.
-__global__ __launch_bounds__(kEncodeThreads) void slots_kernel(Layout ly, uint8_t *arena, EncodeArgs a)
+// Tier counts of one chunk (kSlotChunk positions) of one (sequence, KV
+// head)'s prefill tokens, and whether any tier is out of range:
+// cntc[bh][c][0..T) and cntc[bh][c][kMaxTiers].
+__global__ __launch_bounds__(kSlotThreads) void count_kernel(Layout ly, EncodeArgs a)
 {
-    __shared__ int s_tot[kMaxTiers], s_run[kMaxTiers], s_wc[kEncodeThreads / kWave][kMaxTiers];
-    __shared__ int s_bad;
-    const int bh = blockIdx.x, b = bh / ly.Hkv, h = bh % ly.Hkv;
-    const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
-    const int32_t *cnt = counts_ptr(ly, arena, a.layer, b, h);
-    if (tid < kMaxTiers) {
-        s_tot[tid] = 0;
-        s_run[tid] = 0;
-    }
-    if (tid == 0) s_bad = 0;
+    __shared__ int s_cnt[kMaxTiers + 1];
+    const int c = blockIdx.x, bh = blockIdx.y, b = bh / ly.Hkv;
+    const int tid = threadIdx.x;
+    if (tid <= kMaxTiers) s_cnt[tid] = 0;
     __syncthreads();
     int n = a.n_tokens[b];
-    const bool bad_len = n < 0 || n > a.n_cap;
-    if (bad_len) n = 0;
+    n = (n < 0 || n > a.n_cap) ? 0 : n;
     const uint8_t *tier = a.tier + (int64_t)bh * a.n_cap;
     int loc[kMaxTiers] = {0, 0, 0, 0, 0, 0, 0, 0};
     int bad = 0;
-    for (int t = tid; t < n; t += kEncodeThreads) {
+    const int t1 = min(n, (c + 1) * kSlotChunk);
+    for (int t = c * kSlotChunk + tid; t < t1; t += kSlotThreads) {
         const int k = tier[t];
-        if (k >= ly.T) bad = 1;
+        bad |= k >= ly.T;
 #pragma unroll
         for (int kk = 0; kk < kMaxTiers; ++kk) loc[kk] += k == kk;
     }
 #pragma unroll
     for (int kk = 0; kk < kMaxTiers; ++kk)
-        if (kk < ly.T && loc[kk]) atomicAdd(&s_tot[kk], loc[kk]);
-    if (bad) atomicOr(&s_bad, 1);
+        if (loc[kk]) atomicAdd(&s_cnt[kk], loc[kk]);
+    if (bad) atomicOr(&s_cnt[kMaxTiers], 1);
     __syncthreads();
+    if (tid <= kMaxTiers) a.cntc[((int64_t)bh * a.n_chunks + c) * kChunkStride + tid] = s_cnt[tid];
+}
+
+// Places one chunk of one (sequence, KV head)'s prefill tokens: admission
+// of the whole call for that (sequence, KV head) from every chunk's counts
+// (tiers valid, every tier region and the position map with room), then
+// position n0 + t gets (tier << 28 | slot) with slots in position order
+// after the tier's counted tokens, and the tokens are listed by tier (in
+// position order within a tier) for the encoder: inv[base_k + u] is the
+// u-th token of tier k.  status = n0, or -1 when refused (nothing is
+// written then).
+__global__ __launch_bounds__(kSlotThreads) void place_kernel(Layout ly, uint8_t *arena, EncodeArgs a)
+{
+    __shared__ int s_tot[kMaxTiers], s_off[kMaxTiers], s_run[kMaxTiers], s_wc[kSlotThreads / kWave][kMaxTiers];
+    __shared__ int s_bad;
+    const int c = blockIdx.x, bh = blockIdx.y, b = bh / ly.Hkv, h = bh % ly.Hkv;
+    const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
+    const int32_t *cnt = counts_ptr(ly, arena, a.layer, b, h);
+    if (tid < kMaxTiers) {
+        int tot = 0, off = 0;
+        for (int cc = 0; cc < a.n_chunks; ++cc) {
+            const int v = a.cntc[((int64_t)bh * a.n_chunks + cc) * kChunkStride + tid];
+            off += cc < c ? v : 0;
+            tot += v;
+        }
+        s_tot[tid] = tot;
+        s_off[tid] = off;
+        s_run[tid] = 0;
+    }
+    if (tid == 0) {
+        int bad = 0;
+        for (int cc = 0; cc < a.n_chunks; ++cc) bad |= a.cntc[((int64_t)bh * a.n_chunks + cc) * kChunkStride + kMaxTiers];
+        s_bad = bad;
+    }
+    __syncthreads();
+    int n = a.n_tokens[b];
+    const bool bad_len = n < 0 || n > a.n_cap;
+    if (bad_len) n = 0;
     int n0 = 0;
     for (int kk = 0; kk < ly.T; ++kk) n0 += cnt[kk];
     uint32_t err = bad_len ? DWKV_DEVERR_BAD_LENGTH : 0u;
     if (s_bad) err |= DWKV_DEVERR_BAD_TIER;
     for (int kk = 0; kk < ly.T; ++kk)
         if (cnt[kk] + s_tot[kk] > ly.cap[kk]) err |= DWKV_DEVERR_TIER_FULL;
-    if ((int64_t)n0 + n > ly.max_tokens) err |= DWKV_DEVERR_POS_FULL;
+    if ((int64_t)n0 + n > ly.max_tokens || n > (int64_t)a.n_chunks * kSlotChunk) err |= DWKV_DEVERR_POS_FULL;
     if (err) {
-        if (tid == 0) {
+        if (tid == 0 && c == 0) {
             atomicOr(err_ptr(ly, arena), err);
             a.status[bh] = -1;
         }
         return;
     }
+    int base[kMaxTiers];
+    {
+        int acc = 0;
+#pragma unroll
+        for (int kk = 0; kk < kMaxTiers; ++kk) {
+            base[kk] = acc;
+            acc += kk < ly.T ? s_tot[kk] : 0;
+        }
+    }
+    const uint8_t *tier = a.tier + (int64_t)bh * a.n_cap;
     int32_t *pm = posmap_ptr(ly, arena, a.layer, b, h) + n0;
-    for (int base = 0; base < n; base += kEncodeThreads) {
-        const int t = base + tid;
-        const int k = t < n ? tier[t] : -1;
+    int32_t *inv = a.inv + (int64_t)bh * ly.max_tokens;
+    const int t1 = min(n, (c + 1) * kSlotChunk);
+    for (int t0 = c * kSlotChunk; t0 < t1; t0 += kSlotThreads) {
+        const int t = t0 + tid;
+        const int k = t < t1 ? tier[t] : -1;
         int rank = 0;
 #pragma unroll
         for (int kk = 0; kk < kMaxTiers; ++kk) {
@@ -593,65 +662,277 @@ __global__ __launch_bounds__(kEncodeThreads) void slots_kernel(Layout ly, uint8_
         }
         __syncthreads();
         if (k >= 0) {
-            int off = s_run[k];
+            int off = s_off[k] + s_run[k];
             for (int ww = 0; ww < w; ++ww) off += s_wc[ww][k];
-            pm[t] = (k << 28) | (cnt[k] + off + rank);
+            off += rank;
+            pm[t] = (k << 28) | (cnt[k] + off);
+            int bk = 0;
+#pragma unroll
+            for (int kk = 0; kk < kMaxTiers; ++kk) bk = kk == k ? base[kk] : bk;
+            inv[bk + off] = t;
         }
         __syncthreads();
         if (tid < ly.T)
-            for (int ww = 0; ww < kEncodeThreads / kWave; ++ww) s_run[tid] += s_wc[ww][tid];
+            for (int ww = 0; ww < kSlotThreads / kWave; ++ww) s_run[tid] += s_wc[ww][tid];
         __syncthreads();
     }
-    if (tid == 0) a.status[bh] = n0;
-    if (tid < ly.T) a.newcnt[bh * kMaxTiers + tid] = cnt[tid] + s_tot[tid];
+    if (c == 0) {
+        if (tid == 0) a.status[bh] = n0;
+        if (tid < kMaxTiers) {
+            a.cnt0[bh * kMaxTiers + tid] = tid < ly.T ? cnt[tid] : 0;
+            a.tot[bh * kMaxTiers + tid] = tid < ly.T ? s_tot[tid] : 0;
+        }
+    }
 }
 
-// Encodes the tokens [blockIdx.x * kEncodeTokens, +kEncodeTokens) of one
-// (sequence, KV head): wave w encodes Z = w % 2 for every other token of
-// the range, starting at w / 2, each token exactly as an append would.
-template <int D>
-__global__ __launch_bounds__(kEncodeThreads) void encode_kernel(Layout ly, uint8_t *arena, EncodeArgs a)
+// The window's bases in fp32 for the encoder's scalar loads: rows [z][h][i][j]
+// and transposed [z][h][j][i] (row stride kMaxRank, so that the encoder's
+// loads of one coefficient block sit at fixed offsets from one address).
+__global__ void basis_f32_kernel(Layout ly, uint8_t *arena, int m, float *rows, float *cols)
 {
-    constexpr int NJ = D / kWave;
-    constexpr int NW = kEncodeThreads / kWave;
-    __shared__ __attribute__((aligned(16))) uint16_t sB[2][kMaxRank * kAppendBStride];
-    __shared__ float sx[NW][kMaxHeadDim], sc[NW][kMaxRank];
-    __shared__ int8_t scode[NW][kMaxResid];
-    __shared__ uint8_t sidx[NW][kMaxResid];
+    const int64_t n = 2 * ly.basis_elems;
+    for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < n; e += (int64_t)gridDim.x * blockDim.x) {
+        const int z = (int)(e / ly.basis_elems);
+        const int64_t rem = e - (int64_t)z * ly.basis_elems;
+        const int h = (int)(rem / ((int64_t)ly.R * ly.d));
+        const int64_t r2 = rem - (int64_t)h * ly.R * ly.d;
+        const int i = (int)(r2 / ly.d), j = (int)(r2 % ly.d);
+        const float v = h2f(basis_ptr(ly, arena, m, z, h)[(int64_t)i * ly.d + j]);
+        rows[e] = v;
+        cols[(((int64_t)z * ly.Hkv + h) * ly.d + j) * kMaxRank + i] = v;
+    }
+}
 
-    const int h = blockIdx.y, b = blockIdx.z, bh = b * ly.Hkv + h;
+// An fp32 value kept as such (the later fp16 conversion rounds this fp32
+// value, not the exact sum), without the memory side effects of a volatile
+// statement, so the basis loads around it stay scalar.
+__device__ __forceinline__ float keep_fp32(float v)
+{
+    asm("" : "+v"(v));
+    return v;
+}
+
+template <int N>
+__device__ __forceinline__ void sload(const float *__restrict__ p, float (&v)[N])
+{
+#pragma unroll
+    for (int u = 0; u < N; ++u) v[u] = p[u];
+}
+
+// Encodes up to 64 tokens of one tier of one (sequence, KV head) and one Z,
+// one token per lane, in exactly the append's order of operations: step 1
+// sums sum_j B[i][j] x_j for every coefficient i sequentially in j (eight
+// coefficients' sums interleaved), step 2 sums sum_i B[i][j] c_i for every
+// channel j sequentially in i, the top-s channels come from an insertion
+// pass over j (ascending, so an equal |e| never displaces a lower channel),
+// and the scale, codes and gate follow as in the append.  The basis values
+// are wave-uniform: they come through scalar loads.
+template <int D>
+__global__ __launch_bounds__(kWave) void encode_kernel(Layout ly, uint8_t *__restrict__ arena, EncodeArgs a,
+                                                       const float *__restrict__ brows,
+                                                       const float *__restrict__ bcols)
+{
+#pragma clang fp contract(off)
+    extern __shared__ float s_c[];                 // [r][64]: this wave's coefficients, lane-minor
+    const int zh = blockIdx.y, z = zh / ly.Hkv, h = zh % ly.Hkv, b = blockIdx.z;
+    const int bh = b * ly.Hkv + h;
+    const int lane = threadIdx.x;
     const int n0 = a.status[bh];
     if (n0 < 0) return;
-    const int n = a.n_tokens[b];
-    const int t_begin = blockIdx.x * kEncodeTokens;
-    if (t_begin >= n) return;
-    const int t_end = min(n, t_begin + kEncodeTokens);
-    const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave, z = w & 1;
-
-    uint4 brow[2][D / 8];
-    const uint16_t *Bg = basis_ptr(ly, arena, a.layer / ly.G, z, h);
+    // the chunk's tier: chunks of 64 list entries, tier by tier
+    const int chunk = blockIdx.x;
+    int k = -1, first = 0, c0 = 0;
 #pragma unroll
-    for (int rr = 0; rr < 2; ++rr) {
-        const int row = lane + rr * kWave < ly.R ? lane + rr * kWave : 0;
-#pragma unroll
-        for (int c = 0; c < D / 8; ++c) brow[rr][c] = reinterpret_cast<const uint4 *>(Bg + (int64_t)row * D)[c];
+    for (int kk = 0; kk < kMaxTiers; ++kk) {
+        if (kk >= ly.T) break;
+        const int tot = a.tot[bh * kMaxTiers + kk];
+        const int nc = (tot + kWave - 1) / kWave;
+        if (k < 0 && chunk < c0 + nc) {
+            k = kk;
+            first = (chunk - c0) * kWave;
+        }
+        c0 += nc;
     }
-    if (w < 2) encode_stage_basis<D>(brow, sB[z], ly.R, lane);
-    __syncthreads();
-
-    const uint16_t *X = (z ? a.v : a.k) + (int64_t)bh * a.n_cap * D;
-    const uint16_t *G = z ? a.gateV : a.gateK;
-    const int32_t *pm = posmap_ptr(ly, arena, a.layer, b, h) + n0;
+    if (k < 0) return;
+    int base = 0;
+    for (int kk = 0; kk < k; ++kk) base += a.tot[bh * kMaxTiers + kk];
+    const int tot = a.tot[bh * kMaxTiers + k];
+    const int u = first + lane;
+    const bool live = u < tot;
+    const int t = live ? a.inv[(int64_t)bh * ly.max_tokens + base + u] : a.inv[(int64_t)bh * ly.max_tokens + base + first];
+    const int slot = a.cnt0[bh * kMaxTiers + k] + (live ? u : first);
+    const int r = ly.rank[k], s = ly.resid[k];
     uint8_t *blk = head_block_ptr(ly, arena, a.layer, b, h);
-    for (int t = t_begin + (w >> 1); t < t_end; t += 2) {
-        float xv[NJ];
+    const float *__restrict__ Brow = brows + (int64_t)zh * ly.R * D;      // [i][j]
+    const float *__restrict__ Bcol = bcols + (int64_t)zh * D * kMaxRank;  // [j][i], stride kMaxRank
+    const uint16_t *X = (z ? a.v : a.k) + ((int64_t)bh * a.n_cap + t) * D;
+
+    // 1. the coefficient sums, eight at a time
+    {
+        float x[D];
 #pragma unroll
-        for (int q = 0; q < NJ; ++q) xv[q] = h2f(X[(int64_t)t * D + lane + q * kWave]);
-        const int e = __builtin_amdgcn_readfirstlane(pm[t]);
-        const uint16_t g = G ? G[(int64_t)bh * a.n_cap + t] : uint16_t(0x3C00);
-        encode_store<D>(brow, xv, sB[z], sx[w], sc[w], scode[w], sidx[w], ly, blk, e >> 28, e & 0x0FFFFFFF, z,
-                        lane, g);
+        for (int q = 0; q < D / 8; ++q) {
+            const uint4 v = reinterpret_cast<const uint4 *>(X)[q];
+            const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                x[8 * q + 2 * m] = h2f((uint16_t)(wv[m] & 0xFFFF));
+                x[8 * q + 2 * m + 1] = h2f((uint16_t)(wv[m] >> 16));
+            }
+        }
+        for (int i0 = 0; i0 < r; i0 += 8) {
+            float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            const float *__restrict__ bc = Bcol + i0;
+            if (i0 + 8 <= r) {
+#pragma unroll
+                for (int j = 0; j < D; ++j) {
+                    float bv[8];
+                    sload<8>(bc + j * kMaxRank, bv);
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) acc[q] = __builtin_fmaf(bv[q], x[j], acc[q]);
+                }
+#pragma unroll
+                for (int q = 0; q < 8; ++q) s_c[(i0 + q) * kWave + lane] = keep_fp32(acc[q]);
+            } else {
+#pragma unroll
+                for (int j = 0; j < D; ++j) {
+                    float bv[4];
+                    sload<4>(bc + j * kMaxRank, bv);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) acc[q] = __builtin_fmaf(bv[q], x[j], acc[q]);
+                }
+#pragma unroll
+                for (int q = 0; q < 4; ++q) s_c[(i0 + q) * kWave + lane] = keep_fp32(acc[q]);
+            }
+        }
     }
+    // the coefficients' rounding (fp16, or 8-bit codes with a block scale):
+    // s_c holds the values step 2 uses, s_q what is stored
+    float cs_f = 0.0f;
+    uint16_t cs16 = 0;
+    if (ly.cb != 2) {
+        float amax = 0.0f;
+        for (int i = 0; i < r; ++i) amax = fmaxf(amax, fabsf(s_c[i * kWave + lane]));
+        cs16 = f2h(__fdiv_rn(amax, 127.0f));
+        cs_f = h2f(cs16);
+    }
+    for (int i = 0; i < r; ++i) {
+        const float sum = s_c[i * kWave + lane];
+        if (ly.cb == 2) {
+            const uint16_t c16 = f2h(sum);
+            s_c[i * kWave + lane] = h2f(c16);
+        } else {
+            float qv = 0.0f;
+            if (cs_f != 0.0f) {
+                qv = rintf(__fdiv_rn(sum, cs_f));
+                qv = fminf(fmaxf(qv, -127.0f), 127.0f);
+            }
+            s_c[i * kWave + lane] = qv * cs_f;
+        }
+    }
+
+    // 2. the residual sums, sequential in i for every channel
+    float e[D];
+    if (s > 0) {
+#pragma unroll
+        for (int j = 0; j < D; ++j) e[j] = 0.0f;
+        for (int i = 0; i < r; ++i) {
+            const float ci = s_c[i * kWave + lane];
+            const float *__restrict__ br = Brow + (int64_t)i * D;
+#pragma unroll
+            for (int j0 = 0; j0 < D; j0 += 8) {
+                float bv[8];
+                sload<8>(br + j0, bv);
+#pragma unroll
+                for (int q = 0; q < 8; ++q) e[j0 + q] = __builtin_fmaf(bv[q], ci, e[j0 + q]);
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < D / 8; ++q) {
+            const uint4 v = reinterpret_cast<const uint4 *>(X)[q];
+            const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                e[8 * q + 2 * m] = h2f((uint16_t)(wv[m] & 0xFFFF)) - e[8 * q + 2 * m];
+                e[8 * q + 2 * m + 1] = h2f((uint16_t)(wv[m] >> 16)) - e[8 * q + 2 * m + 1];
+            }
+        }
+    }
+
+    // the coefficients into the tier region
+    const int64_t coff = z ? ly.f_coefV[k] : ly.f_coefK[k];
+    if (live) {
+        if (ly.cb == 2) {
+            uint16_t *cdst = reinterpret_cast<uint16_t *>(blk + coff);
+            for (int i = 0; i < r; ++i)
+                cdst[z ? coefV_index(r, slot, i) : (int64_t)slot * r + i] = f2h(s_c[i * kWave + lane]);
+        } else {
+            int8_t *cdst = reinterpret_cast<int8_t *>(blk + coff);
+            for (int i = 0; i < r; ++i) {
+                const float c = s_c[i * kWave + lane];
+                cdst[z ? coefV_index(r, slot, i) : (int64_t)slot * r + i] =
+                    static_cast<int8_t>(cs_f != 0.0f ? (int)__fdiv_rn(c, cs_f) : 0);
+            }
+            reinterpret_cast<uint16_t *>(blk + (z ? ly.f_cscV[k] : ly.f_cscK[k]))[slot] = cs16;
+        }
+    }
+    if (s == 0) return;
+
+    // 3. the s largest keys |e| bits << 9 | (255 - j) << 1 | sign, kept
+    //    sorted (largest first) while j ascends
+    uint64_t top[kMaxResid];
+#pragma unroll
+    for (int q = 0; q < kMaxResid; ++q) top[q] = 0;
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+        const uint32_t bits = __float_as_uint(e[j]);
+        uint64_t key = ((uint64_t)(bits & 0x7FFFFFFFu) << 9) | ((uint64_t)(255 - j) << 1) | (bits >> 31);
+#pragma unroll
+        for (int q = 0; q < kMaxResid; ++q) {
+            if (q < s) {
+                const uint64_t hi = key > top[q] ? key : top[q];
+                key = key > top[q] ? top[q] : key;
+                top[q] = hi;
+            }
+        }
+    }
+    // 4. the scale from the largest kept |e|
+    const float amax = __uint_as_float((uint32_t)(top[0] >> 9));
+    const uint16_t s16 = f2h(__fdiv_rn(amax, (float)ly.qmax));
+    const float sf = h2f(s16);
+    // 5. codes, placed in ascending channel order
+    uint64_t idxw = 0, valw = 0;
+#pragma unroll
+    for (int q = 0; q < kMaxResid; ++q) {
+        if (q < s) {
+            const int jq = 255 - (int)((top[q] >> 1) & 0xFF);
+            const float eq = __uint_as_float((uint32_t)(top[q] >> 9) | ((uint32_t)(top[q] & 1) << 31));
+            int pos = 0;
+#pragma unroll
+            for (int q2 = 0; q2 < kMaxResid; ++q2)
+                if (q2 < s) pos += (255 - (int)((top[q2] >> 1) & 0xFF)) < jq;
+            float v = 0.0f;
+            if (sf != 0.0f) {
+                v = rintf(__fdiv_rn(eq, sf));
+                v = fminf(fmaxf(v, -(float)ly.qmax), (float)ly.qmax);
+            }
+            const int code = (int)v;
+            idxw |= (uint64_t)jq << (8 * pos);
+            valw |= ly.bits == 8 ? (uint64_t)(code & 0xFF) << (8 * pos) : (uint64_t)(code & 0xF) << (4 * pos);
+        }
+    }
+    if (!live) return;
+    uint32_t *idst = reinterpret_cast<uint32_t *>(blk + (z ? ly.f_idxV[k] : ly.f_idxK[k]) + (int64_t)slot * ly.istride[k]);
+    uint32_t *vdst = reinterpret_cast<uint32_t *>(blk + (z ? ly.f_valV[k] : ly.f_valK[k]) + (int64_t)slot * ly.vstride[k]);
+    idst[0] = (uint32_t)idxw;
+    if (ly.istride[k] > 4) idst[1] = (uint32_t)(idxw >> 32);
+    vdst[0] = (uint32_t)valw;
+    if (ly.vstride[k] > 4) vdst[1] = (uint32_t)(valw >> 32);
+    // 6. the gate folds into the stored scale
+    const uint16_t *G = z ? a.gateV : a.gateK;
+    const uint16_t g = G ? G[(int64_t)bh * a.n_cap + t] : uint16_t(0x3C00);
+    reinterpret_cast<uint16_t *>(blk + (z ? ly.f_scaleV[k] : ly.f_scaleK[k]))[slot] =
+        (g == 0x3C00) ? s16 : f2h(h2f(g) * sf);
 }
 
 // Publishes the encoded tokens: the tier counts of every admitted
@@ -662,7 +943,8 @@ __global__ void publish_kernel(Layout ly, uint8_t *arena, EncodeArgs a, int n_bh
     if (e >= n_bh * ly.T) return;
     const int bh = e / ly.T, k = e % ly.T;
     if (a.status[bh] < 0) return;
-    counts_ptr(ly, arena, a.layer, bh / ly.Hkv, bh % ly.Hkv)[k] = a.newcnt[bh * kMaxTiers + k];
+    counts_ptr(ly, arena, a.layer, bh / ly.Hkv, bh % ly.Hkv)[k] =
+        a.cnt0[bh * kMaxTiers + k] + a.tot[bh * kMaxTiers + k];
 }
 
 }  // namespace
@@ -672,6 +954,10 @@ hipError_t launch_gram(const Layout &ly, uint8_t *arena, const GramArgs &a, hipS
     (void)hipGetLastError();  // drop errors left by earlier, unrelated calls
     const auto kern = ly.d == 64 ? gram_kernel<64> : gram_kernel<128>;
     hipLaunchKernelGGL(kern, dim3(a.S, 2 * a.Hkv), dim3(kGramThreads), 0, stream, ly, arena, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const auto red = ly.d == 64 ? gram_reduce_kernel<64> : gram_reduce_kernel<128>;
+    hipLaunchKernelGGL(red, dim3(gram_pairs(ly.d), 2 * a.Hkv), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -689,16 +975,23 @@ hipError_t launch_prefill_encode(const Layout &ly, uint8_t *arena, const EncodeA
                                  hipStream_t stream)
 {
     (void)hipGetLastError();  // drop errors left by earlier, unrelated calls
-    hipLaunchKernelGGL(slots_kernel, dim3(batch * ly.Hkv), dim3(kEncodeThreads), 0, stream, ly, arena, a);
+    const int64_t be = 2 * ly.basis_elems;
+    hipLaunchKernelGGL(basis_f32_kernel, dim3((unsigned)((be + 255) / 256 < 1024 ? (be + 255) / 256 : 1024)),
+                       dim3(256), 0, stream, ly, arena, a.layer / ly.G, a.basis_rows, a.basis_cols);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(count_kernel, dim3(a.n_chunks, batch * ly.Hkv), dim3(kSlotThreads), 0, stream, ly, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(place_kernel, dim3(a.n_chunks, batch * ly.Hkv), dim3(kSlotThreads), 0, stream, ly, arena, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
     const auto kern = ly.d == 64 ? encode_kernel<64> : encode_kernel<128>;
-    const unsigned chunks = (unsigned)((a.n_cap + kEncodeTokens - 1) / kEncodeTokens);
-    if (chunks > 0) {
-        hipLaunchKernelGGL(kern, dim3(chunks, ly.Hkv, batch), dim3(kEncodeThreads), 0, stream, ly, arena, a);
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
+    const unsigned chunks = (unsigned)((a.n_cap + kWave - 1) / kWave + ly.T);
+    hipLaunchKernelGGL(kern, dim3(chunks, 2 * ly.Hkv, batch), dim3(kWave), (size_t)ly.R * kWave * 4, stream, ly,
+                       arena, a, a.basis_rows, a.basis_cols);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
     const int n = batch * ly.Hkv * ly.T;
     hipLaunchKernelGGL(publish_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, ly, arena, a, batch * ly.Hkv);
     return hipGetLastError();

@@ -146,7 +146,7 @@ def _bases(G, cache, cfg, omega, q, m=0):
     return bk.cpu().numpy(), bv.cpu().numpy(), ritz.cpu().numpy()[0]
 
 
-@pytest.mark.parametrize("d,k,q", [(128, 72, 2), (128, 72, 0), (64, 40, 1), (64, 64, 3)])
+@pytest.mark.parametrize("d,k,q", [(128, 72, 2), (128, 72, 0), (64, 40, 1), (64, 64, 3), (64, 41, 2)])
 def test_bases_match_oracle_on_identical_gram(G, d, k, q):
     cfg = _cfg8k(batch=2) if d == 128 else tiny_config(batch=2, num_kv_heads=2, num_q_heads=4, head_dim=64,
                                                         r_max=32, tier_rank=(8, 16, 32), tier_prob=(0.5, 0.3, 0.2),
