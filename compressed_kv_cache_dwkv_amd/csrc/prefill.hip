@@ -723,9 +723,9 @@ __device__ __forceinline__ void sload(const float *__restrict__ p, float (&v)[N]
 // one token per lane, in exactly the append's order of operations: step 1
 // sums sum_j B[i][j] x_j for every coefficient i sequentially in j (eight
 // coefficients' sums interleaved), step 2 sums sum_i B[i][j] c_i for every
-// channel j sequentially in i, the top-s channels come from an insertion
-// pass over j (ascending, so an equal |e| never displaces a lower channel),
-// and the scale, codes and gate follow as in the append.  The basis values
+// channel j sequentially in i, the kept channels are the s largest |e|
+// (ties to the lower channel, as in the append), and the scale, codes and
+// gate follow as in the append.  The basis values
 // are wave-uniform: they come through scalar loads.
 template <int D>
 __global__ __launch_bounds__(kWave) void encode_kernel(Layout ly, uint8_t *__restrict__ arena, EncodeArgs a,
@@ -878,48 +878,68 @@ __global__ __launch_bounds__(kWave) void encode_kernel(Layout ly, uint8_t *__res
     }
     if (s == 0) return;
 
-    // 3. the s largest keys |e| bits << 9 | (255 - j) << 1 | sign, kept
-    //    sorted (largest first) while j ascends
-    uint64_t top[kMaxResid];
+    // 3. the s kept channels: the s largest |e| with ties to the lower
+    //    channel.  First the largest kMaxResid |e| by a max/min insertion
+    //    (thr: the s-th of them), then, in ascending channel order, every
+    //    channel above thr and the first (s - #above) channels at thr,
+    //    queued in that order: each kept channel shifts a queue of
+    //    kMaxResid values and the index word, so the last s entries hold
+    //    the kept channels in ascending order.
+    float top[kMaxResid];
 #pragma unroll
-    for (int q = 0; q < kMaxResid; ++q) top[q] = 0;
+    for (int q = 0; q < kMaxResid; ++q) top[q] = 0.0f;
 #pragma unroll
     for (int j = 0; j < D; ++j) {
-        const uint32_t bits = __float_as_uint(e[j]);
-        uint64_t key = ((uint64_t)(bits & 0x7FFFFFFFu) << 9) | ((uint64_t)(255 - j) << 1) | (bits >> 31);
+        float v = fabsf(e[j]);
 #pragma unroll
         for (int q = 0; q < kMaxResid; ++q) {
-            if (q < s) {
-                const uint64_t hi = key > top[q] ? key : top[q];
-                key = key > top[q] ? top[q] : key;
-                top[q] = hi;
-            }
+            const float hi = fmaxf(top[q], v);
+            v = fminf(top[q], v);
+            top[q] = hi;
         }
     }
+    float thr = top[0];
+    int above = 0;
+#pragma unroll
+    for (int q = 0; q < kMaxResid; ++q) thr = q == s - 1 ? top[q] : thr;
+#pragma unroll
+    for (int q = 0; q < kMaxResid; ++q) above += (q < s && top[q] > thr) ? 1 : 0;
+    const int need = s - above;
+    float ev[kMaxResid];
+#pragma unroll
+    for (int q = 0; q < kMaxResid; ++q) ev[q] = 0.0f;
+    uint64_t idxw = 0;
+    int ties = 0;
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+        const float v = fabsf(e[j]);
+        const int at = v == thr;
+        const int keep = (v > thr) | (at & (ties < need));
+        ties += at & keep;
+#pragma unroll
+        for (int q = 0; q + 1 < kMaxResid; ++q) ev[q] = keep ? ev[q + 1] : ev[q];
+        ev[kMaxResid - 1] = keep ? e[j] : ev[kMaxResid - 1];
+        idxw = keep ? (idxw >> 8) | ((uint64_t)j << (8 * (kMaxResid - 1))) : idxw;
+    }
+    idxw >>= 8 * (kMaxResid - s);
     // 4. the scale from the largest kept |e|
-    const float amax = __uint_as_float((uint32_t)(top[0] >> 9));
+    const float amax = top[0];
     const uint16_t s16 = f2h(__fdiv_rn(amax, (float)ly.qmax));
     const float sf = h2f(s16);
-    // 5. codes, placed in ascending channel order
-    uint64_t idxw = 0, valw = 0;
+    // 5. codes, in ascending channel order (queue entry kMaxResid - s + u
+    //    is the u-th kept channel)
+    uint64_t valw = 0;
+    const int skip = kMaxResid - s;
 #pragma unroll
     for (int q = 0; q < kMaxResid; ++q) {
-        if (q < s) {
-            const int jq = 255 - (int)((top[q] >> 1) & 0xFF);
-            const float eq = __uint_as_float((uint32_t)(top[q] >> 9) | ((uint32_t)(top[q] & 1) << 31));
-            int pos = 0;
-#pragma unroll
-            for (int q2 = 0; q2 < kMaxResid; ++q2)
-                if (q2 < s) pos += (255 - (int)((top[q2] >> 1) & 0xFF)) < jq;
-            float v = 0.0f;
-            if (sf != 0.0f) {
-                v = rintf(__fdiv_rn(eq, sf));
-                v = fminf(fmaxf(v, -(float)ly.qmax), (float)ly.qmax);
-            }
-            const int code = (int)v;
-            idxw |= (uint64_t)jq << (8 * pos);
-            valw |= ly.bits == 8 ? (uint64_t)(code & 0xFF) << (8 * pos) : (uint64_t)(code & 0xF) << (4 * pos);
+        float v = 0.0f;
+        if (sf != 0.0f) {
+            v = rintf(__fdiv_rn(ev[q], sf));
+            v = fminf(fmaxf(v, -(float)ly.qmax), (float)ly.qmax);
         }
+        const int code = (int)v, u = q - skip;
+        if (u >= 0)
+            valw |= ly.bits == 8 ? (uint64_t)(code & 0xFF) << (8 * u) : (uint64_t)(code & 0xF) << (4 * u);
     }
     if (!live) return;
     uint32_t *idst = reinterpret_cast<uint32_t *>(blk + (z ? ly.f_idxV[k] : ly.f_idxK[k]) + (int64_t)slot * ly.istride[k]);
