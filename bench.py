@@ -439,6 +439,119 @@ def run_dense(args, cfg, K: int, W: int):
 PREFILL_METRIC = "prefill compression tokens/s (prompt tokens, all layers: Gram sums, bases, bulk encode)"
 
 
+PREFILL_SRCS = [os.path.join(ROOT, "compressed_kv_cache_dwkv_amd", "csrc", "prefill.hip")]
+PREFILL_RUN_ARGS = "--mode prefill --steps 1 --warmup 1 --no-cpu-baseline --copy-probe --kernel-reps 1"
+PREFILL_TRACE_ARGS = "--mode prefill --steps 3 --warmup 1 --no-cpu-baseline --kernel-reps 2"
+PREFILL_KERNELS = ("gram_kernel", "gram_reduce_kernel", "bases_kernel", "transpose_basis_kernel", "basis_f32_kernel",
+                   "count_kernel", "place_kernel", "encode_kernel", "publish_kernel")
+
+
+def prefill_source_sha() -> str:
+    h = hashlib.sha256()
+    for f in PREFILL_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
+def _prefill_name(name: str) -> Optional[str]:
+    for k in PREFILL_KERNELS:
+        if "::" + k in name or name.startswith(k) or (" " + k) in name or (k + "<") in name:
+            return k
+    return None
+
+
+def prefill_pmc_summary(cfg, ci: int, fetch_dir: str, write_dir: str, bench_json: Optional[str]):
+    """HBM bytes per launch of the prefill kernels from FETCH_SIZE /
+    WRITE_SIZE, scaled as for the decode kernel by a plain copy's reading."""
+    res = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        per = _pmc_per_dispatch(d, counter)
+        cpy = [v for k, vs in per.items() if "copyBuffer" in k for v in vs]
+        cpy = [v for v in cpy if v * 1024 > COPY_PROBE_BYTES / 4]
+        if not cpy:
+            raise SystemExit(f"{counter}: no copy-probe dispatch")
+        scale = COPY_PROBE_BYTES / (float(np.mean(cpy)) * 1024)
+        for name, vs in per.items():
+            k = _prefill_name(name)
+            if k in ("gram_kernel", "encode_kernel", "bases_kernel", "place_kernel", "count_kernel"):
+                res.setdefault(k, {})[counter] = {"kib_mean": float(np.mean(vs)), "dispatches": len(vs),
+                                                   "bytes_per_launch": float(np.mean(vs)) * 1024 * scale,
+                                                   "scale": scale}
+    bj = _json_line(bench_json) if bench_json else None
+    alg = {"gram_kernel": bj["breakdown"]["algorithmic_bytes"]["gram_per_layer"],
+           "encode_kernel": bj["breakdown"]["algorithmic_bytes"]["encode_per_layer"]} if bj else {}
+    rec = {"workload": cfg.name + "-prefill", "prefill_source_sha256": prefill_source_sha(), "kernels": {}}
+    lines = [f"# Prefill kernels' HBM traffic, {cfg.name} prompt ({cfg.n_tokens} tokens, {cfg.num_layers} layers)", "",
+             "Commands (run from /tmp with TMPDIR=/tmp on one MI355X), then the summary on any host:", "", "```",
+             f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d <fetch> -o run -- python3 <repo>/bench.py "
+             f"--config {ci} {PREFILL_RUN_ARGS}",
+             f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d <write> -o run -- python3 <repo>/bench.py "
+             f"--config {ci} {PREFILL_RUN_ARGS}",
+             f"python3 <repo>/bench.py --config {ci} --mode prefill --pmc-summary <fetch> <write> "
+             f"--bench-json <fetch run's JSON line>", "```", "",
+             "Each counter is scaled by (512 MiB) / (its reading for a plain 512 MiB device copy in the same process).",
+             "", "| kernel | dispatches | FETCH bytes / launch | WRITE bytes / launch | algorithmic bytes | ratio |",
+             "|---|---|---|---|---|---|"]
+    for k, v in sorted(res.items()):
+        f = v.get("FETCH_SIZE", {}).get("bytes_per_launch", 0.0)
+        wr = v.get("WRITE_SIZE", {}).get("bytes_per_launch", 0.0)
+        a = alg.get(k)
+        rec["kernels"][k] = {"fetch_bytes": f, "write_bytes": wr, "hbm_bytes_per_launch": f + wr,
+                             "algorithmic_bytes_per_launch": a, "counters": v}
+        lines.append(f"| {k} | {v.get('FETCH_SIZE', {}).get('dispatches', 0)} | {f:.0f} | {wr:.0f} | "
+                     f"{'' if a is None else f'{a:.0f}'} | {'' if a is None else f'{(f + wr) / a:.3f}'} |")
+    lines += ["", f"Prefill source sha256: `{rec['prefill_source_sha256']}` (bench.py reports `traffic` only while "
+                  "prefill.hip matches it)."]
+    os.makedirs(PROFILES, exist_ok=True)
+    json.dump(rec, open(os.path.join(PROFILES, f"prefill_{cfg.name}_traffic.json"), "w"), indent=1)
+    open(os.path.join(PROFILES, f"prefill_{cfg.name}_traffic.md"), "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines), flush=True)
+
+
+def prefill_stored_traffic(cfg, kernel: str):
+    path = os.path.join(PROFILES, f"prefill_{cfg.name}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("prefill_source_sha256") != prefill_source_sha():
+        return None
+    return rec["kernels"].get(kernel, {}).get("hbm_bytes_per_launch")
+
+
+def prefill_trace_summary(cfg, ci: int, trace_dir: str, bench_json: Optional[str]):
+    """profiles/prefill_<workload>_kernel_trace.md from a rocprofv3
+    --kernel-trace --stats run of the prefill mode."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_stats.csv under {trace_dir}")
+    rows = [r for f in files for r in csv.DictReader(open(f)) if _prefill_name(r["Name"])]
+    bj = _json_line(bench_json) if bench_json else None
+    lines = [f"# Prefill compression kernels, {cfg.name} prompt (batch {cfg.batch}, {cfg.n_tokens} tokens, "
+             f"{cfg.num_layers} layers, {cfg.num_kv_heads} KV heads, d {cfg.head_dim}, r_max {cfg.r_max})", "",
+             "Command (run from /tmp with TMPDIR=/tmp on one MI355X), then the summary on any host:", "", "```",
+             f"rocprofv3 --kernel-trace --stats --output-format csv -d <out> -o run -- python3 <repo>/bench.py "
+             f"--config {ci} {PREFILL_TRACE_ARGS}",
+             f"python3 <repo>/bench.py --config {ci} --mode prefill --trace-summary <out> [--bench-json <line>]",
+             "```", "",
+             "Per prompt: one Gram launch (+ reduction) and one encode family (count, place, fp32 basis copy, encode,",
+             "publish) per layer, one bases launch for all windows (+ a transpose per window).", "",
+             "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        lines.append(f"| {_prefill_name(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} |")
+    if bj:
+        b, rf = bj["breakdown"], bj["roofline"]
+        lines += ["", f"The same build's default `bench.py --config {ci} --mode prefill` run: {bj['value']:.0f} prompt "
+                      f"tokens/s ({bj['ms_per_step']:.2f} ms per prompt of {cfg.n_tokens} tokens, {cfg.num_layers} "
+                      f"layers); Gram {b['gram_ms']:.2f} ms ({b['gram_GBps']:.0f} GB/s), bases {b['bases_ms']:.2f} ms, "
+                      f"encode {b['encode_ms']:.2f} ms ({b['encode_GBps']:.0f} GB/s); dominant kernel "
+                      f"{rf['kernel']}: {rf['achieved']:.2f} {rf['unit']} ({rf['frac'] * 100:.1f}% of {rf['peak']})."]
+    open(os.path.join(PROFILES, f"prefill_{cfg.name}_kernel_trace.md"), "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines), flush=True)
+
+
 def prefill_step_bytes(cfg, tiers) -> dict:
     """Algorithmic bytes of one prefill compression of the whole model, per
     kernel family: the Gram pass reads every prefill key and value once;
@@ -540,7 +653,10 @@ def run_prefill(args, cfg, K: int, W: int):
                 "algorithmic_flop_per_launch": enc_flop_layer, "mean_launch_us": enc_layer_ms * 1e3,
                 "hbm_GBps": by["encode_per_layer"] / (enc_layer_ms * 1e-3) / 1e9}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    kname = "gram_kernel" if dominant == "gram" else "encode_kernel"
+    roof["traffic"] = prefill_stored_traffic(cfg, kname)
+    if roof["traffic"] is not None:
+        roof["traffic_GBps"] = roof["traffic"] / (roof["mean_launch_us"] * 1e-6) / 1e9
     roof["launch_time_from"] = "replays of a graph of one step's launches of that kernel family"
     res = {
         "metric": PREFILL_METRIC, "value": B * n * K / (elapsed_ms / 1e3), "unit": "tokens/s", "n_gpus": 1,
@@ -561,6 +677,13 @@ def run_prefill(args, cfg, K: int, W: int):
         "roofline": roof,
         "cpu_baseline": None if args.no_cpu_baseline else prefill_cpu_baseline(cfg, args.cpu_seconds),
     }
+    if args.copy_probe:
+        src = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     cache.close()
     return res
 
@@ -610,10 +733,16 @@ def main():
         sys.exit(2)
     cfg = w.get_config(args.config).with_(coef_bits=args.coef_bits)
     if args.pmc_summary:
-        pmc_summary(workload_name(cfg), *args.pmc_summary, bench_json=args.bench_json)
+        if args.mode == "prefill":
+            prefill_pmc_summary(cfg, args.config, *args.pmc_summary, bench_json=args.bench_json)
+        else:
+            pmc_summary(workload_name(cfg), *args.pmc_summary, bench_json=args.bench_json)
         return
     if args.trace_summary:
-        trace_summary(cfg, args.config, args.trace_summary, args.bench_json)
+        if args.mode == "prefill":
+            prefill_trace_summary(cfg, args.config, args.trace_summary, args.bench_json)
+        else:
+            trace_summary(cfg, args.config, args.trace_summary, args.bench_json)
         return
     K = args.steps if args.steps is not None else cfg.bench_steps
     W = args.warmup
