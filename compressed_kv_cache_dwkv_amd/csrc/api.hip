@@ -152,15 +152,34 @@ int build_layout(const dwkv_config *c, Layout *ly)
 
 // Workgroups per (sequence, KV head) for decode.  A decode workgroup fills
 // one compute unit (8 waves, more than half the LDS), so the grid aims at
-// one workgroup per compute unit of the 256, while leaving each workgroup at
-// least 1024 token slots (16 tiles of 64) of its head.
+// Compute units of the current device (read once per process; 256, the
+// MI355X's, when no device answers, as in host-only use).
+static int device_cus()
+{
+    static int cus = 0;
+    static std::once_flag once;
+    std::call_once(once, [] {
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+            cus = n;
+        else
+            cus = 256;
+        (void)hipGetLastError();
+    });
+    return cus;
+}
+
+// one workgroup per compute unit of the device, while leaving each
+// workgroup at least 1024 token slots (16 tiles of 64) of its head.
 static int plan_splits(const dwkv_config &c, const Layout &ly)
 {
     if (c.decode_splits > 0) return c.decode_splits;
     int64_t slots = 0;
     for (int k = 0; k < ly.T; ++k) slots += ly.cap[k];
     const int64_t heads = (int64_t)ly.Bmax * ly.Hkv;
-    int64_t s = (256 + heads - 1) / heads;
+    const int64_t cus = device_cus();
+    int64_t s = (cus + heads - 1) / heads;
     const int64_t by_tokens = slots / 1024;
     if (s > by_tokens) s = by_tokens;
     if (s < 1) s = 1;
@@ -647,10 +666,11 @@ int dwkv_probe_update(float *tau, int32_t *below, int n_windows, const float *er
 
 // ------------------------------------------------------------------ prefill
 
-// Gram workgroups per (Z, KV head): about 512 workgroups per call.
+// Gram workgroups per (Z, KV head): about two workgroups per compute unit.
 static int gram_splits(const Layout &ly)
 {
-    int s = (512 + 2 * ly.Hkv - 1) / (2 * ly.Hkv);
+    const int want = 2 * dwkv::device_cus();
+    int s = (want + 2 * ly.Hkv - 1) / (2 * ly.Hkv);
     return s < 1 ? 1 : (s > dwkv::kGramMaxSplits ? dwkv::kGramMaxSplits : s);
 }
 

@@ -280,7 +280,7 @@ __device__ __forceinline__ uint16_t d2h_rne(double x)
 // Reads row j of C (equal to column j) so that the lanes' loads are
 // contiguous.  Writes W into dst after every thread's reads of src.
 template <int D>
-__device__ void gemm_cq(const double *C, const double *src, double *dst, int k)
+__device__ void gemm_cq(const double *C, const double *src, double *dst, int k, int ks)
 {
     constexpr int RI = D / kWave;
     const int lane = lane_id(), w = threadIdx.x / kWave;
@@ -297,7 +297,7 @@ __device__ void gemm_cq(const double *C, const double *src, double *dst, int k)
 #pragma unroll
         for (int cc = 0; cc < kColsPerWave; ++cc) {
             if (c0 + cc < k) {
-                const double qv = src[j * k + c0 + cc];
+                const double qv = src[j * ks + c0 + cc];
 #pragma unroll
                 for (int ri = 0; ri < RI; ++ri) acc[ri][cc] = fma(cj[ri], qv, acc[ri][cc]);
             }
@@ -308,7 +308,7 @@ __device__ void gemm_cq(const double *C, const double *src, double *dst, int k)
     for (int ri = 0; ri < RI; ++ri)
 #pragma unroll
         for (int cc = 0; cc < kColsPerWave; ++cc)
-            if (c0 + cc < k) dst[(lane + kWave * ri) * k + c0 + cc] = acc[ri][cc];
+            if (c0 + cc < k) dst[(lane + kWave * ri) * ks + c0 + cc] = acc[ri][cc];
     __syncthreads();
 }
 
@@ -318,13 +318,13 @@ __device__ void gemm_cq(const double *C, const double *src, double *dst, int k)
 // The projections' sums are split over the workgroup's four quarters
 // (partials in sp, [4][max(D, k)]) and added in quarter order.
 template <int D>
-__device__ void orth(const double *W, double *Q, int k, double *sv, double *sr, double *sp, double *sred)
+__device__ void orth(const double *W, double *Q, int k, int ks, double *sv, double *sr, double *sp, double *sred)
 {
     constexpr int QT = kBasesThreads / 4;          // threads per quarter (128)
     const int tid = threadIdx.x, qi = tid / QT, qt = tid % QT;
     int kept = 0;
     for (int cand = 0; kept < k && cand < k + D; ++cand) {
-        if (tid < D) sv[tid] = cand < k ? W[tid * k + cand] : (tid == cand - k ? 1.0 : 0.0);
+        if (tid < D) sv[tid] = cand < k ? W[tid * ks + cand] : (tid == cand - k ? 1.0 : 0.0);
         double mine = tid < D ? sv[tid] : 0.0;
         const double n0 = sqrt(block_sum(mine * mine, sred));
         for (int pass = 0; pass < 2 && kept > 0; ++pass) {
@@ -334,8 +334,8 @@ __device__ void orth(const double *W, double *Q, int k, double *sv, double *sr, 
                 const int i0 = qi * (D / 4);
 #pragma unroll 4
                 for (int i = i0; i < i0 + D / 4; i += 2) {
-                    p0 = fma(Q[i * k + qt], sv[i], p0);
-                    p1 = fma(Q[(i + 1) * k + qt], sv[i + 1], p1);
+                    p0 = fma(Q[i * ks + qt], sv[i], p0);
+                    p1 = fma(Q[(i + 1) * ks + qt], sv[i + 1], p1);
                 }
                 sp[qi * kMaxSketch + qt] = p0 + p1;
             }
@@ -349,10 +349,10 @@ __device__ void orth(const double *W, double *Q, int k, double *sv, double *sr, 
                 double p0 = 0.0, p1 = 0.0;
                 int cc = c0;
                 for (; cc + 1 < c1; cc += 2) {
-                    p0 = fma(Q[qt * k + cc], sr[cc], p0);
-                    p1 = fma(Q[qt * k + cc + 1], sr[cc + 1], p1);
+                    p0 = fma(Q[qt * ks + cc], sr[cc], p0);
+                    p1 = fma(Q[qt * ks + cc + 1], sr[cc + 1], p1);
                 }
-                if (cc < c1) p0 = fma(Q[qt * k + cc], sr[cc], p0);
+                if (cc < c1) p0 = fma(Q[qt * ks + cc], sr[cc], p0);
                 sp[qi * kMaxHeadDim + qt] = p0 + p1;
             }
             __syncthreads();
@@ -363,7 +363,7 @@ __device__ void orth(const double *W, double *Q, int k, double *sv, double *sr, 
         mine = tid < D ? sv[tid] : 0.0;
         const double n1 = sqrt(block_sum(mine * mine, sred));
         if (n0 != 0.0 && n1 > 0x1p-40 * n0) {
-            if (tid < D) Q[tid * k + kept] = sv[tid] / n1;
+            if (tid < D) Q[tid * ks + kept] = sv[tid] / n1;
             ++kept;
         }
         __syncthreads();
@@ -378,8 +378,10 @@ __device__ __forceinline__ int rr_index(int pos, int step, int kp)
 template <int D>
 __global__ __launch_bounds__(kBasesThreads) void bases_kernel(Layout ly, uint8_t *arena, BasesArgs a)
 {
-    __shared__ double sQ[kMaxHeadDim * kMaxSketch];
-    __shared__ double sW[kMaxHeadDim * kMaxSketch];
+    // Q and W rows padded to an odd number of doubles (ks = k | 1), so that
+    // lanes walking consecutive rows of one column hit different banks
+    __shared__ double sQ[kMaxHeadDim * (kMaxSketch + 1)];
+    __shared__ double sW[kMaxHeadDim * (kMaxSketch + 1)];
     __shared__ double sv[kMaxHeadDim];
     __shared__ double sr[kMaxSketch + 1];
     __shared__ double sp[4 * kMaxHeadDim];
@@ -389,7 +391,7 @@ __global__ __launch_bounds__(kBasesThreads) void bases_kernel(Layout ly, uint8_t
     __shared__ int s_perm[kMaxSketch];
     __shared__ double s_sgn[kMaxSketch];
 
-    const int tid = threadIdx.x, k = a.k;
+    const int tid = threadIdx.x, k = a.k, ks = k | 1;
     const int zh = blockIdx.x, gi = blockIdx.y;
     const int z = zh / ly.Hkv, h = zh % ly.Hkv;
     const int m = a.group0 + gi;
@@ -397,17 +399,17 @@ __global__ __launch_bounds__(kBasesThreads) void bases_kernel(Layout ly, uint8_t
     const float *om = a.omega + ((int64_t)gi * 2 * ly.Hkv + zh) * D * k;
 
     // 1. Y = C Omega;  2. Q = orth(Y)
-    for (int e = tid; e < D * k; e += kBasesThreads) sQ[e] = (double)om[e];
+    for (int e = tid; e < D * k; e += kBasesThreads) sQ[(e / k) * ks + e % k] = (double)om[e];
     __syncthreads();
-    gemm_cq<D>(C, sQ, sW, k);
-    orth<D>(sW, sQ, k, sv, sr, sp, sred);
+    gemm_cq<D>(C, sQ, sW, k, ks);
+    orth<D>(sW, sQ, k, ks, sv, sr, sp, sred);
     // 3. power iterations
     for (int it = 0; it < a.power_iters; ++it) {
-        gemm_cq<D>(C, sQ, sW, k);
-        orth<D>(sW, sQ, k, sv, sr, sp, sred);
+        gemm_cq<D>(C, sQ, sW, k, ks);
+        orth<D>(sW, sQ, k, ks, sv, sr, sp, sred);
     }
     // 4. T = Q^T C Q, symmetrised, into sW
-    gemm_cq<D>(C, sQ, sW, k);
+    gemm_cq<D>(C, sQ, sW, k, ks);
     {
         constexpr int kPer = (kMaxSketch * kMaxSketch + kBasesThreads - 1) / kBasesThreads;
         double t[kPer];
@@ -419,8 +421,8 @@ __global__ __launch_bounds__(kBasesThreads) void bases_kernel(Layout ly, uint8_t
                 const int ra = e / k, cb = e % k;
                 double p0 = 0.0, p1 = 0.0;
                 for (int i = 0; i < D; i += 2) {
-                    p0 = fma(sQ[i * k + ra], sW[i * k + cb], p0);
-                    p1 = fma(sQ[(i + 1) * k + ra], sW[(i + 1) * k + cb], p1);
+                    p0 = fma(sQ[i * ks + ra], sW[i * ks + cb], p0);
+                    p1 = fma(sQ[(i + 1) * ks + ra], sW[(i + 1) * ks + cb], p1);
                 }
                 t[u] = p0 + p1;
             }
@@ -485,10 +487,12 @@ __global__ __launch_bounds__(kBasesThreads) void bases_kernel(Layout ly, uint8_t
                 s_s[tid] = s;
             }
             __syncthreads();
-            // T <- J^T T J one 2x2 block (pairs p, p2) per item, from the
-            // block's old values; Q <- Q J one (row, pair) per item
+            // T <- J^T T J one 2x2 block (pairs p <= p2) per item, from the
+            // block's old values, written with its mirror (T stays exactly
+            // symmetric); Q <- Q J one (row, pair) per item
             for (int e = tid; e < P * P; e += kBasesThreads) {
                 const int p = e / P, p2 = e - p * P;
+                if (p > p2) continue;
                 const int a0 = s_a[p], b0 = s_b[p], a1 = s_a[p2], b1 = s_b[p2];
                 const double c0 = s_c[p], s0 = s_s[p], c1 = s_c[p2], s1 = s_s[p2];
                 if (s0 == 0.0 && s1 == 0.0) continue;
@@ -509,15 +513,21 @@ __global__ __launch_bounds__(kBasesThreads) void bases_kernel(Layout ly, uint8_t
                 if (hb1) T[a0 * k + b1] = nab;
                 if (hb0) T[b0 * k + a1] = nba;
                 if (hb0 && hb1) T[b0 * k + b1] = nbb;
+                if (p != p2) {
+                    T[a1 * k + a0] = naa;
+                    if (hb1) T[b1 * k + a0] = nab;
+                    if (hb0) T[a1 * k + b0] = nba;
+                    if (hb0 && hb1) T[b1 * k + b0] = nbb;
+                }
             }
             for (int e = tid; e < P * D; e += kBasesThreads) {
                 const int p = e / D, i = e % D;
                 const int a0 = s_a[p], b0 = s_b[p];
                 if (s_s[p] == 0.0) continue;
                 const double c0 = s_c[p], s0 = s_s[p];
-                const double qa = sQ[i * k + a0], qb = sQ[i * k + b0];
-                sQ[i * k + a0] = c0 * qa - s0 * qb;
-                sQ[i * k + b0] = s0 * qa + c0 * qb;
+                const double qa = sQ[i * ks + a0], qb = sQ[i * ks + b0];
+                sQ[i * ks + a0] = c0 * qa - s0 * qb;
+                sQ[i * ks + b0] = s0 * qa + c0 * qb;
             }
             __syncthreads();
         }
@@ -535,20 +545,20 @@ __global__ __launch_bounds__(kBasesThreads) void bases_kernel(Layout ly, uint8_t
         int best = 0;
         double bv = fabs(sQ[tid]);
         for (int i = 1; i < D; ++i) {
-            const double v = fabs(sQ[i * k + tid]);
+            const double v = fabs(sQ[i * ks + tid]);
             if (v > bv) {
                 bv = v;
                 best = i;
             }
         }
-        s_sgn[tid] = sQ[best * k + tid] < 0.0 ? -1.0 : 1.0;
+        s_sgn[tid] = sQ[best * ks + tid] < 0.0 ? -1.0 : 1.0;
     }
     __syncthreads();
     // 6. the first r_max Ritz vectors as the basis rows, in fp16
     uint16_t *Bz = basis_ptr(ly, arena, m, z, h);
     for (int e = tid; e < ly.R * D; e += kBasesThreads) {
         const int rho = e / D, i = e % D, col = s_perm[rho];
-        Bz[e] = d2h_rne(s_sgn[col] * sQ[i * k + col]);
+        Bz[e] = d2h_rne(s_sgn[col] * sQ[i * ks + col]);
     }
     if (a.ritz && tid < k) a.ritz[((int64_t)gi * 2 * ly.Hkv + zh) * k + tid] = T[s_perm[tid] * k + s_perm[tid]];
 }
