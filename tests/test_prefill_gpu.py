@@ -180,6 +180,45 @@ def test_bases_match_oracle_on_identical_gram(G, d, k, q):
         cache.close()
 
 
+def test_bases_of_several_windows_in_one_launch(G):
+    """One bases call over windows 0..2 (the benchmark's launch shape: every
+    window of the model at once), each window with its own Gram sums and
+    sketch, against the oracle window by window."""
+    import torch
+    cfg = _cfg8k(batch=2, num_layers=12)
+    lengths = [2000, 1300]
+    k, q = cfg.r_max + 8, 2
+    omega = gen_sketch(cfg, k)
+    cache = _cache(G, cfg, 2000)
+    try:
+        wins = []
+        for m in range(3):
+            Ks, Vs = _window(cfg, lengths, m=m, integer=True)
+            _grams(G, cache, cfg, Ks, Vs, lengths, m=m)
+            wins.append((Ks, Vs))
+        ritz = torch.zeros((3, 2, cfg.num_kv_heads, k), dtype=torch.float64, device="cuda")
+        cache.prefill_bases(0, G.dev(omega[0:3]), q, ritz)
+        torch.cuda.synchronize()
+        rz = ritz.cpu().numpy()
+        for m, (Ks, Vs) in enumerate(wins):
+            bk, bv = (t.cpu().numpy() for t in cache.get_basis(m))
+            ref = oracle.prefill_bases(cfg, Ks, Vs, lengths, omega[m], q)
+            for zi, (z, got) in enumerate((("K", bk), ("V", bv))):
+                for h in range(cfg.num_kv_heads):
+                    th = ref["theta" + z][h]
+                    assert np.abs(rz[m, zi, h] - th).max() <= 1e-10 * th[0], (m, z, h)
+                    gaps = _ritz_order_gaps(th)
+                    for i in range(cfg.r_max):
+                        if gaps[i] < 1e-6 * th[0]:
+                            continue
+                        B64 = ref[z + "64"][h][i]
+                        ulp = np.spacing(np.abs(B64).astype(np.float16)).astype(np.float64)
+                        assert np.all(np.abs(got[h, i].astype(np.float64) - B64) <= 0.5 * ulp + 1e-9), (m, z, h, i)
+        assert cache.check_errors() == 0
+    finally:
+        cache.close()
+
+
 def test_bases_match_oracle_on_gaussian_data(G):
     cfg = _cfg8k(batch=2)
     lengths = [4000, 2100]
