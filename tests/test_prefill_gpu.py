@@ -376,6 +376,69 @@ def test_prefill_encode_refusals(G):
         small.close()
 
 
+def test_appends_after_prefill_continue_the_layer(G):
+    """Prefill encode, then three one-token appends (dwkv_append) and one
+    one-launch decode step: the position map and tier slots the prefill
+    leaves are the ones the append path continues; the exported layer is the
+    oracle's prefill encoding followed by the oracle's appends."""
+    import torch
+    cfg = _cfg8k(batch=2)
+    layer, lengths = 3, [900, 555]
+    bases = make_bases(cfg)
+    K, V = gen_prefill(cfg, layer, lengths=lengths)
+    tier = gen_tiers(cfg, layer, 900)
+    gK, gV = gen_gates(cfg, layer, 900)
+    cache = _cache(G, cfg, 1000)
+    try:
+        G.load_bases(cache, bases, groups=[0])
+        _encode(G, cache, cfg, layer, K, V, lengths, tier, gK, gV)
+        apps = [w.gen_append_inputs(cfg, layer, st, bases) for st in range(4)]
+        for a in apps[:3]:
+            cache.append(layer, G.dev(a["k"]), G.dev(a["v"]), G.dev(a["tier"]))
+        q = gen_query(cfg, layer)
+        cache.decode_step(layer, G.dev(q), G.dev(apps[3]["k"]), G.dev(apps[3]["v"]), G.dev(apps[3]["tier"]))
+        torch.cuda.synchronize()
+        assert cache.check_errors() == 0
+        n_after = [n + 4 for n in lengths]
+        got, counts, _ = G.export_np(cache, layer, cfg.batch, max(n_after))
+        ref = oracle.prefill_encode(cfg, bases["K"][0], bases["V"][0], K, V, lengths, tier, gK, gV)
+        for b, n in enumerate(lengths):
+            for h in range(cfg.num_kv_heads):
+                for st, a in enumerate(apps):
+                    t = n + st
+                    k = int(a["tier"][b, h])
+                    assert got["tier"][b, h, t] == k
+                    r, s_ = cfg.tier_rank[k], cfg.resid_per_tier[k]
+                    for z in "KV":
+                        enc = oracle.append_vector(bases[z][0][h], a[z.lower()][b, h], r, s_, cfg.qmax)
+                        assert np.array_equal(got["coef" + z][b, h, t, :r].view(np.uint16), enc[0].view(np.uint16))
+                        assert np.array_equal(got["idx" + z][b, h, t, :s_], enc[1])
+                        assert np.array_equal(got["val" + z][b, h, t, :s_], enc[2])
+                        assert got["scale" + z][b, h, t].view(np.uint16) == enc[3].view(np.uint16)
+        _compare_layer(cfg, {kk: np.ascontiguousarray(v[:, :, :900]) for kk, v in got.items()}, ref, lengths)
+    finally:
+        cache.close()
+
+
+def test_prefill_length_beyond_the_buffer_is_refused(G):
+    """n_tokens > n_cap sets the bad-length bit and leaves that sequence's
+    heads empty; the other sequence is encoded."""
+    cfg = _cfg8k(batch=2)
+    layer = 1
+    bases = make_bases(cfg)
+    K, V = gen_prefill(cfg, layer, lengths=[300, 300])
+    tier = gen_tiers(cfg, layer, 300)
+    cache = _cache(G, cfg, 1000)
+    try:
+        G.load_bases(cache, bases, groups=[0])
+        cache.prefill_encode(layer, G.dev(K), G.dev(V), G.dev(np.asarray([300, 301], np.int32)), G.dev(tier))
+        assert cache.check_errors() & DEVERR_BAD_LENGTH
+        counts = cache.read_counts(layer, cfg.batch)
+        assert counts[1].sum() == 0 and counts[0].sum() == cfg.num_kv_heads * 300
+    finally:
+        cache.close()
+
+
 def test_prefill_chain_decodes_like_the_oracle_chain(G):
     """Gram, bases and encode for a window, then decode attention: the GPU
     chain's error against dense attention over the original keys and
