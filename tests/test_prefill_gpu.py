@@ -315,6 +315,43 @@ def test_prefill_encode_bit_exact(G, case):
         cache.close()
 
 
+def test_prefill_batch16_ragged(G):
+    """Sixteen sequences of different lengths (the batch of the 32K x 16
+    workload, shorter), including empty ones: Gram sums exact on integer
+    data, bases and the bulk encode against the oracle."""
+    cfg = _cfg8k(batch=16)
+    rng = np.random.default_rng(16)
+    lengths = [int(x) for x in rng.integers(0, 1200, 16)]
+    lengths[3] = 0
+    lengths[7] = 1199
+    n = max(lengths)
+    Ks, Vs = _window(cfg, lengths, integer=True)
+    omega = gen_sketch(cfg, cfg.r_max + 8)
+    cache = _cache(G, cfg, n)
+    try:
+        got = _grams(G, cache, cfg, Ks, Vs, lengths)
+        for z in range(2):
+            for h in range(cfg.num_kv_heads):
+                assert np.array_equal(got[z, h], _oracle_gram(cfg, Ks, Vs, lengths, z, h)), (z, h)
+        bk, bv, ritz = _bases(G, cache, cfg, omega, 2)
+        ref = oracle.prefill_bases(cfg, Ks, Vs, lengths, omega[0], 2)
+        for zi, z in enumerate("KV"):
+            for h in range(cfg.num_kv_heads):
+                th = ref["theta" + z][h]
+                assert np.abs(ritz[zi, h] - th).max() <= 1e-10 * th[0], (z, h)
+        layer = 2
+        tier = gen_tiers(cfg, layer, n)
+        bases = {"K": ref["K"][None], "V": ref["V"][None]}
+        G.load_bases(cache, bases, groups=[0])
+        _encode(G, cache, cfg, layer, Ks[layer], Vs[layer], lengths, tier)
+        assert cache.check_errors() == 0
+        out, _, _ = G.export_np(cache, layer, cfg.batch, n)
+        ref_lay = oracle.prefill_encode(cfg, ref["K"], ref["V"], Ks[layer], Vs[layer], lengths, tier)
+        _compare_layer(cfg, out, ref_lay, lengths)
+    finally:
+        cache.close()
+
+
 def test_prefill_encode_in_two_chunks_equals_one(G):
     """1000 positions, then the remaining 2000 in a second call: the layer is
     the oracle's encoding of all 3000 (positions continue)."""
