@@ -696,8 +696,9 @@ __global__ __launch_bounds__(kSlotThreads) void place_kernel(Layout ly, uint8_t 
 }
 
 // The window's bases in fp32 for the encoder's scalar loads: rows [z][h][i][j]
-// and transposed [z][h][j][i] (row stride kMaxRank, so that the encoder's
-// loads of one coefficient block sit at fixed offsets from one address).
+// and, for the coefficient sums, blocks of 8 coefficients [z][h][i / 8][j][i % 8]
+// (a (z, h) spans d * kMaxRank floats): one block's loads sit at fixed offsets
+// from one address and fill whole cache lines.
 __global__ void basis_f32_kernel(Layout ly, uint8_t *arena, int m, float *rows, float *cols)
 {
     const int64_t n = 2 * ly.basis_elems;
@@ -709,7 +710,7 @@ __global__ void basis_f32_kernel(Layout ly, uint8_t *arena, int m, float *rows, 
         const int i = (int)(r2 / ly.d), j = (int)(r2 % ly.d);
         const float v = h2f(basis_ptr(ly, arena, m, z, h)[(int64_t)i * ly.d + j]);
         rows[e] = v;
-        cols[(((int64_t)z * ly.Hkv + h) * ly.d + j) * kMaxRank + i] = v;
+        cols[((int64_t)z * ly.Hkv + h) * ly.d * kMaxRank + ((int64_t)(i >> 3) * ly.d + j) * 8 + (i & 7)] = v;
     }
 }
 
@@ -737,24 +738,29 @@ __device__ __forceinline__ void sload(const float *__restrict__ p, float (&v)[N]
 // (ties to the lower channel, as in the append), and the scale, codes and
 // gate follow as in the append.  The basis values
 // are wave-uniform: they come through scalar loads.
-template <int D>
+template <int D, int CB>  // CB: bytes per stored coefficient (2: fp16, 1: 8-bit codes)
 __global__ __launch_bounds__(kWave) void encode_kernel(Layout ly, uint8_t *__restrict__ arena, EncodeArgs a,
                                                        const float *__restrict__ brows,
                                                        const float *__restrict__ bcols)
 {
 #pragma clang fp contract(off)
-    extern __shared__ float s_c[];                 // [r][64]: this wave's coefficients, lane-minor
+    // [r][64]: this wave's coefficients, lane-minor (fp16 when they are
+    // stored as fp16, else fp32 sums and then the values step 2 uses); then
+    // the kept channels
+    extern __shared__ float s_c[];
+    uint16_t *s_h = reinterpret_cast<uint16_t *>(s_c);
     const int zh = blockIdx.y, z = zh / ly.Hkv, h = zh % ly.Hkv, b = blockIdx.z;
     const int bh = b * ly.Hkv + h;
     const int lane = threadIdx.x;
     const int n0 = a.status[bh];
     if (n0 < 0) return;
-    // the chunk's tier: chunks of 64 list entries, tier by tier
+    // the chunk's tier: chunks of 64 list entries, tier by tier from the
+    // highest rank (the longest chunks are dispatched first)
     const int chunk = blockIdx.x;
     int k = -1, first = 0, c0 = 0;
 #pragma unroll
-    for (int kk = 0; kk < kMaxTiers; ++kk) {
-        if (kk >= ly.T) break;
+    for (int kk = kMaxTiers - 1; kk >= 0; --kk) {
+        if (kk >= ly.T) continue;
         const int tot = a.tot[bh * kMaxTiers + kk];
         const int nc = (tot + kWave - 1) / kWave;
         if (k < 0 && chunk < c0 + nc) {
@@ -774,7 +780,7 @@ __global__ __launch_bounds__(kWave) void encode_kernel(Layout ly, uint8_t *__res
     const int r = ly.rank[k], s = ly.resid[k];
     uint8_t *blk = head_block_ptr(ly, arena, a.layer, b, h);
     const float *__restrict__ Brow = brows + (int64_t)zh * ly.R * D;      // [i][j]
-    const float *__restrict__ Bcol = bcols + (int64_t)zh * D * kMaxRank;  // [j][i], stride kMaxRank
+    const float *__restrict__ Bcol = bcols + (int64_t)zh * D * kMaxRank;  // [i / 8][j][i % 8]
     const uint16_t *X = (z ? a.v : a.k) + ((int64_t)bh * a.n_cap + t) * D;
 
     // 1. the coefficient sums, eight at a time
@@ -792,46 +798,52 @@ __global__ __launch_bounds__(kWave) void encode_kernel(Layout ly, uint8_t *__res
         }
         for (int i0 = 0; i0 < r; i0 += 8) {
             float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-            const float *__restrict__ bc = Bcol + i0;
+            const float *__restrict__ bc = Bcol + (int64_t)i0 * D;
             if (i0 + 8 <= r) {
 #pragma unroll
                 for (int j = 0; j < D; ++j) {
                     float bv[8];
-                    sload<8>(bc + j * kMaxRank, bv);
+                    sload<8>(bc + j * 8, bv);
 #pragma unroll
                     for (int q = 0; q < 8; ++q) acc[q] = __builtin_fmaf(bv[q], x[j], acc[q]);
                 }
 #pragma unroll
-                for (int q = 0; q < 8; ++q) s_c[(i0 + q) * kWave + lane] = keep_fp32(acc[q]);
+                for (int q = 0; q < 8; ++q) {
+                    if (CB == 2)
+                        s_h[(i0 + q) * kWave + lane] = f2h(keep_fp32(acc[q]));
+                    else
+                        s_c[(i0 + q) * kWave + lane] = keep_fp32(acc[q]);
+                }
             } else {
 #pragma unroll
                 for (int j = 0; j < D; ++j) {
                     float bv[4];
-                    sload<4>(bc + j * kMaxRank, bv);
+                    sload<4>(bc + j * 8, bv);
 #pragma unroll
                     for (int q = 0; q < 4; ++q) acc[q] = __builtin_fmaf(bv[q], x[j], acc[q]);
                 }
 #pragma unroll
-                for (int q = 0; q < 4; ++q) s_c[(i0 + q) * kWave + lane] = keep_fp32(acc[q]);
+                for (int q = 0; q < 4; ++q) {
+                    if (CB == 2)
+                        s_h[(i0 + q) * kWave + lane] = f2h(keep_fp32(acc[q]));
+                    else
+                        s_c[(i0 + q) * kWave + lane] = keep_fp32(acc[q]);
+                }
             }
         }
     }
-    // the coefficients' rounding (fp16, or 8-bit codes with a block scale):
-    // s_c holds the values step 2 uses, s_q what is stored
+    // the 8-bit form's rounding: codes with a block scale, and s_c then
+    // holds code x scale, the values step 2 uses (the fp16 form was rounded
+    // as it was written)
     float cs_f = 0.0f;
     uint16_t cs16 = 0;
-    if (ly.cb != 2) {
+    if (CB != 2) {
         float amax = 0.0f;
         for (int i = 0; i < r; ++i) amax = fmaxf(amax, fabsf(s_c[i * kWave + lane]));
         cs16 = f2h(__fdiv_rn(amax, 127.0f));
         cs_f = h2f(cs16);
-    }
-    for (int i = 0; i < r; ++i) {
-        const float sum = s_c[i * kWave + lane];
-        if (ly.cb == 2) {
-            const uint16_t c16 = f2h(sum);
-            s_c[i * kWave + lane] = h2f(c16);
-        } else {
+        for (int i = 0; i < r; ++i) {
+            const float sum = s_c[i * kWave + lane];
             float qv = 0.0f;
             if (cs_f != 0.0f) {
                 qv = rintf(__fdiv_rn(sum, cs_f));
@@ -847,7 +859,7 @@ __global__ __launch_bounds__(kWave) void encode_kernel(Layout ly, uint8_t *__res
 #pragma unroll
         for (int j = 0; j < D; ++j) e[j] = 0.0f;
         for (int i = 0; i < r; ++i) {
-            const float ci = s_c[i * kWave + lane];
+            const float ci = CB == 2 ? h2f(s_h[i * kWave + lane]) : s_c[i * kWave + lane];
             const float *__restrict__ br = Brow + (int64_t)i * D;
 #pragma unroll
             for (int j0 = 0; j0 < D; j0 += 8) {
@@ -872,10 +884,10 @@ __global__ __launch_bounds__(kWave) void encode_kernel(Layout ly, uint8_t *__res
     // the coefficients into the tier region
     const int64_t coff = z ? ly.f_coefV[k] : ly.f_coefK[k];
     if (live) {
-        if (ly.cb == 2) {
+        if (CB == 2) {
             uint16_t *cdst = reinterpret_cast<uint16_t *>(blk + coff);
             for (int i = 0; i < r; ++i)
-                cdst[z ? coefV_index(r, slot, i) : (int64_t)slot * r + i] = f2h(s_c[i * kWave + lane]);
+                cdst[z ? coefV_index(r, slot, i) : (int64_t)slot * r + i] = s_h[i * kWave + lane];
         } else {
             int8_t *cdst = reinterpret_cast<int8_t *>(blk + coff);
             for (int i = 0; i < r; ++i) {
@@ -889,24 +901,21 @@ __global__ __launch_bounds__(kWave) void encode_kernel(Layout ly, uint8_t *__res
     if (s == 0) return;
 
     // 3. the s kept channels: the s largest |e| with ties to the lower
-    //    channel.  First the largest kMaxResid |e| by a max/min insertion
-    //    (thr: the s-th of them), then, in ascending channel order, every
-    //    channel above thr and the first (s - #above) channels at thr,
-    //    queued in that order: each kept channel shifts a queue of
-    //    kMaxResid values and the index word, so the last s entries hold
-    //    the kept channels in ascending order.
+    //    channel.  First the largest kMaxResid |e|, in decreasing order, by
+    //    an insertion in which entry q becomes the median of its old value,
+    //    the old entry q - 1 and the new value (thr: the s-th of them); then,
+    //    in ascending channel order, every channel above thr and the first
+    //    (s - #above) channels at thr go to the next of this lane's s LDS
+    //    slots (the others to a spare slot), value and channel together.
     float top[kMaxResid];
 #pragma unroll
     for (int q = 0; q < kMaxResid; ++q) top[q] = 0.0f;
 #pragma unroll
     for (int j = 0; j < D; ++j) {
-        float v = fabsf(e[j]);
+        const float v = fabsf(e[j]);
 #pragma unroll
-        for (int q = 0; q < kMaxResid; ++q) {
-            const float hi = fmaxf(top[q], v);
-            v = fminf(top[q], v);
-            top[q] = hi;
-        }
+        for (int q = kMaxResid - 1; q > 0; --q) top[q] = __builtin_amdgcn_fmed3f(top[q - 1], top[q], v);
+        top[0] = fmaxf(top[0], v);
     }
     float thr = top[0];
     int above = 0;
@@ -915,41 +924,39 @@ __global__ __launch_bounds__(kWave) void encode_kernel(Layout ly, uint8_t *__res
 #pragma unroll
     for (int q = 0; q < kMaxResid; ++q) above += (q < s && top[q] > thr) ? 1 : 0;
     const int need = s - above;
-    float ev[kMaxResid];
-#pragma unroll
-    for (int q = 0; q < kMaxResid; ++q) ev[q] = 0.0f;
-    uint64_t idxw = 0;
-    int ties = 0;
+    float *s_ev = s_c;                                                     // [kMaxResid + 1][64]
+    int *s_ej = reinterpret_cast<int *>(s_c) + (kMaxResid + 1) * kWave;    // the same, channels
+    int ties = 0, cnt = 0;
 #pragma unroll
     for (int j = 0; j < D; ++j) {
         const float v = fabsf(e[j]);
-        const int at = v == thr;
-        const int keep = (v > thr) | (at & (ties < need));
-        ties += at & keep;
-#pragma unroll
-        for (int q = 0; q + 1 < kMaxResid; ++q) ev[q] = keep ? ev[q + 1] : ev[q];
-        ev[kMaxResid - 1] = keep ? e[j] : ev[kMaxResid - 1];
-        idxw = keep ? (idxw >> 8) | ((uint64_t)j << (8 * (kMaxResid - 1))) : idxw;
+        const int at = (v == thr) & (ties < need);
+        const int keep = (v > thr) | at;
+        ties += at;
+        const int slot = (keep ? cnt : kMaxResid) * kWave + lane;
+        s_ev[slot] = e[j];
+        s_ej[slot] = j;
+        cnt += keep;
     }
-    idxw >>= 8 * (kMaxResid - s);
     // 4. the scale from the largest kept |e|
     const float amax = top[0];
     const uint16_t s16 = f2h(__fdiv_rn(amax, (float)ly.qmax));
     const float sf = h2f(s16);
-    // 5. codes, in ascending channel order (queue entry kMaxResid - s + u
-    //    is the u-th kept channel)
-    uint64_t valw = 0;
-    const int skip = kMaxResid - s;
+    // 5. codes and channel bytes, in ascending channel order (slot u is the
+    //    u-th kept channel)
+    uint64_t valw = 0, idxw = 0;
 #pragma unroll
-    for (int q = 0; q < kMaxResid; ++q) {
+    for (int u = 0; u < kMaxResid; ++u) {
+        if (u >= s) break;
+        const float ev = s_ev[u * kWave + lane];
         float v = 0.0f;
         if (sf != 0.0f) {
-            v = rintf(__fdiv_rn(ev[q], sf));
+            v = rintf(__fdiv_rn(ev, sf));
             v = fminf(fmaxf(v, -(float)ly.qmax), (float)ly.qmax);
         }
-        const int code = (int)v, u = q - skip;
-        if (u >= 0)
-            valw |= ly.bits == 8 ? (uint64_t)(code & 0xFF) << (8 * u) : (uint64_t)(code & 0xF) << (4 * u);
+        const int code = (int)v;
+        idxw |= (uint64_t)(uint32_t)s_ej[u * kWave + lane] << (8 * u);
+        valw |= ly.bits == 8 ? (uint64_t)(code & 0xFF) << (8 * u) : (uint64_t)(code & 0xF) << (4 * u);
     }
     if (!live) return;
     uint32_t *idst = reinterpret_cast<uint32_t *>(blk + (z ? ly.f_idxV[k] : ly.f_idxK[k]) + (int64_t)slot * ly.istride[k]);
@@ -1016,10 +1023,14 @@ hipError_t launch_prefill_encode(const Layout &ly, uint8_t *arena, const EncodeA
     hipLaunchKernelGGL(place_kernel, dim3(a.n_chunks, batch * ly.Hkv), dim3(kSlotThreads), 0, stream, ly, arena, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const auto kern = ly.d == 64 ? encode_kernel<64> : encode_kernel<128>;
+    const auto kern = ly.cb == 2 ? (ly.d == 64 ? encode_kernel<64, 2> : encode_kernel<128, 2>)
+                                 : (ly.d == 64 ? encode_kernel<64, 1> : encode_kernel<128, 1>);
     const unsigned chunks = (unsigned)((a.n_cap + kWave - 1) / kWave + ly.T);
-    hipLaunchKernelGGL(kern, dim3(chunks, 2 * ly.Hkv, batch), dim3(kWave), (size_t)ly.R * kWave * 4, stream, ly,
-                       arena, a, a.basis_rows, a.basis_cols);
+    const size_t coef_lds = (size_t)ly.R * kWave * (ly.cb == 2 ? 2 : 4);
+    const size_t sel_lds = (size_t)2 * (kMaxResid + 1) * kWave * 4;
+    const size_t lds = coef_lds > sel_lds ? coef_lds : sel_lds;
+    hipLaunchKernelGGL(kern, dim3(chunks, 2 * ly.Hkv, batch), dim3(kWave), lds, stream, ly, arena, a, a.basis_rows,
+                       a.basis_cols);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int n = batch * ly.Hkv * ly.T;
