@@ -901,42 +901,63 @@ __global__ __launch_bounds__(kWave) void encode_kernel(Layout ly, uint8_t *__res
     if (s == 0) return;
 
     // 3. the s kept channels: the s largest |e| with ties to the lower
-    //    channel.  First the largest kMaxResid |e|, in decreasing order, by
-    //    an insertion in which entry q becomes the median of its old value,
-    //    the old entry q - 1 and the new value (thr: the s-th of them); then,
-    //    in ascending channel order, every channel above thr and the first
-    //    (s - #above) channels at thr go to the next of this lane's s LDS
-    //    slots (the others to a spare slot), value and channel together.
-    float top[kMaxResid];
+    //    channel.  First the largest kMaxResid + 1 |e|, in decreasing order,
+    //    by an insertion in which entry q becomes the median of its old
+    //    value, the old entry q - 1 and the new value (thr: the s-th of
+    //    them); then, in ascending channel order, every channel above thr
+    //    and the first (s - #above) channels at thr go to the next of this
+    //    lane's s LDS slots (the others to a spare slot), value and channel
+    //    together.  Where the (s + 1)-th largest is below thr in every lane
+    //    (no tie at the threshold to break), the kept channels are those at
+    //    or above thr.
+    constexpr int kTop = kMaxResid + 1;
+    float top[kTop];
 #pragma unroll
-    for (int q = 0; q < kMaxResid; ++q) top[q] = 0.0f;
+    for (int q = 0; q < kTop; ++q) top[q] = 0.0f;
 #pragma unroll
     for (int j = 0; j < D; ++j) {
         const float v = fabsf(e[j]);
 #pragma unroll
-        for (int q = kMaxResid - 1; q > 0; --q) top[q] = __builtin_amdgcn_fmed3f(top[q - 1], top[q], v);
+        for (int q = kTop - 1; q > 0; --q) top[q] = __builtin_amdgcn_fmed3f(top[q - 1], top[q], v);
         top[0] = fmaxf(top[0], v);
     }
-    float thr = top[0];
+    float thr = top[0], nxt = top[1];
     int above = 0;
 #pragma unroll
-    for (int q = 0; q < kMaxResid; ++q) thr = q == s - 1 ? top[q] : thr;
+    for (int q = 0; q < kMaxResid; ++q) {
+        thr = q == s - 1 ? top[q] : thr;
+        nxt = q == s - 1 ? top[q + 1] : nxt;
+    }
 #pragma unroll
     for (int q = 0; q < kMaxResid; ++q) above += (q < s && top[q] > thr) ? 1 : 0;
     const int need = s - above;
     float *s_ev = s_c;                                                     // [kMaxResid + 1][64]
     int *s_ej = reinterpret_cast<int *>(s_c) + (kMaxResid + 1) * kWave;    // the same, channels
-    int ties = 0, cnt = 0;
+    int cnt = 0;
+    if (__all(nxt < thr)) {
+        float *const spare = s_ev + kMaxResid * kWave + lane;
+        float *next = s_ev + lane;
 #pragma unroll
-    for (int j = 0; j < D; ++j) {
-        const float v = fabsf(e[j]);
-        const int at = (v == thr) & (ties < need);
-        const int keep = (v > thr) | at;
-        ties += at;
-        const int slot = (keep ? cnt : kMaxResid) * kWave + lane;
-        s_ev[slot] = e[j];
-        s_ej[slot] = j;
-        cnt += keep;
+        for (int j = 0; j < D; ++j) {
+            const bool keep = fabsf(e[j]) >= thr;
+            float *const p = keep ? next : spare;
+            p[0] = e[j];
+            reinterpret_cast<int *>(p)[(kMaxResid + 1) * kWave] = j;
+            next += keep ? kWave : 0;
+        }
+    } else {
+        int ties = 0;
+#pragma unroll
+        for (int j = 0; j < D; ++j) {
+            const float v = fabsf(e[j]);
+            const int at = (v == thr) & (ties < need);
+            const int keep = (v > thr) | at;
+            ties += at;
+            const int slot = (keep ? cnt : kMaxResid) * kWave + lane;
+            s_ev[slot] = e[j];
+            s_ej[slot] = j;
+            cnt += keep;
+        }
     }
     // 4. the scale from the largest kept |e|
     const float amax = top[0];

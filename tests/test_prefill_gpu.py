@@ -352,6 +352,65 @@ def test_prefill_batch16_ragged(G):
         cache.close()
 
 
+def _permutation_bases(cfg, seed):
+    """Signed permutation rows (fp16-exact): every coefficient is a signed
+    input channel and every residual channel is an input value or exactly 0."""
+    rng = np.random.default_rng(seed)
+    out = {}
+    for z in "KV":
+        B = np.zeros((cfg.num_groups, cfg.num_kv_heads, cfg.r_max, cfg.head_dim), np.float16)
+        for m in range(cfg.num_groups):
+            for h in range(cfg.num_kv_heads):
+                cols = rng.permutation(cfg.head_dim)[: cfg.r_max]
+                B[m, h, np.arange(cfg.r_max), cols] = rng.choice([-1.0, 1.0], cfg.r_max)
+        out[z] = B
+    return out
+
+
+@pytest.mark.parametrize("coef_bits", [16, 8])
+def test_prefill_encode_planted_ties(G, coef_bits):
+    """Residuals with many equal |e| at the kept-channel threshold (values
+    from {0, +-0.25, +-0.5, +-1}) and all-zero residuals, after a run of
+    generic tokens, in one call: the tie rule (the lower channel first) and
+    the tie-free channel selection against the oracle, bit-exact."""
+    cfg = _cfg8k(batch=2, coef_bits=coef_bits)
+    lengths = [2400, 1500]
+    n = max(lengths)
+    layer = 1
+    bases = _permutation_bases(cfg, 7)
+    K, V = gen_prefill(cfg, layer, lengths=lengths, tail=np.nan)
+    rng = np.random.default_rng(11)
+    for X in (K, V):
+        planted = rng.choice([0.0, 0.25, -0.25, 0.5, -0.5, 1.0, -1.0], (cfg.batch, cfg.num_kv_heads, n, cfg.head_dim))
+        X[:, :, 800:n] = planted[:, :, 800:n].astype(np.float16)
+        X[:, :, 1200:1300] = 0.0
+        for b, nb in enumerate(lengths):
+            X[b, :, nb:] = np.nan
+    tier = gen_tiers(cfg, layer, n)
+    cache = _cache(G, cfg, n)
+    try:
+        G.load_bases(cache, bases, groups=[0])
+        print(f"prefill encode with planted ties: coef_bits={coef_bits}", flush=True)
+        _encode(G, cache, cfg, layer, K, V, lengths, tier)
+        assert cache.check_errors() == 0
+        got, _, _ = G.export_np(cache, layer, cfg.batch, n)
+        ref = oracle.prefill_encode(cfg, bases["K"][0], bases["V"][0], K, V, lengths, tier)
+        _compare_layer(cfg, got, ref, lengths)
+        # the all-zero rows have a zero scale, and (fp16 coefficients: each
+        # residual channel is the input channel or 0) the planted rows put
+        # more channels at the threshold than are kept
+        assert (ref["scaleK"][0, :, 1200:1300].view(np.uint16) == 0).all()
+        if coef_bits == 16:
+            s = cfg.resid_per_tier[0]
+            B = bases["K"][0, 0].astype(np.float64)
+            x = K[0, 0, 800:1200].astype(np.float64)
+            e = np.abs(x - (x @ B.T) @ B)
+            top = -np.sort(-e, axis=1)
+            assert (top[:, s] == top[:, s - 1]).sum() > 100
+    finally:
+        cache.close()
+
+
 def test_prefill_encode_in_two_chunks_equals_one(G):
     """1000 positions, then the remaining 2000 in a second call: the layer is
     the oracle's encoding of all 3000 (positions continue)."""
