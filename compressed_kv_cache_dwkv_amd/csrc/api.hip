@@ -743,6 +743,8 @@ int dwkv_prefill_gram(dwkv_handle *h, int layer, const void *k, const void *v, c
     const int rc = prefill_common(h, layer, k, v, n_tokens, batch, n_cap, workspace, workspace_bytes);
     if (rc != DWKV_OK) return rc;
     const Layout &ly = h->ly;
+    // the Gram kernel addresses a sequence's rows with 32-bit byte offsets
+    if ((n_cap + 256) * ly.d * 2 > (int64_t)UINT32_MAX) return DWKV_ERR_UNSUPPORTED;
     const PrefillWs w = carve_prefill(ly, workspace);
     dwkv::GramArgs a;
     a.k = static_cast<const uint16_t *>(k);

@@ -267,16 +267,6 @@ __device__ __forceinline__ Tile locate(const Ranges &rg, Cursor &cur, const Layo
     return t;
 }
 
-// Buffer resource over `bytes` bytes at p (a wave-uniform address).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const uint8_t *p, int64_t bytes)
-{
-    const uint64_t a = reinterpret_cast<uint64_t>(p);
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
-    void *u = reinterpret_cast<void *>(((uint64_t)hi << 32) | lo);
-    return __builtin_amdgcn_make_buffer_rsrc(u, (short)0, __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000);
-}
-
 // Issues every load of a tile: always the same number of load instructions,
 // so the compiler's wait counts stay exact and the next tile's loads are
 // never waited for while the current tile is computed.  The loads are

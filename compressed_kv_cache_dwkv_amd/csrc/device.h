@@ -8,6 +8,17 @@ namespace dwkv {
 
 constexpr int kWave = 64;
 
+// Buffer resource over `bytes` bytes at p (a wave-uniform address, bytes
+// below 2^32): buffer loads past its end return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const void *p, int64_t bytes)
+{
+    const uint64_t a = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    void *u = reinterpret_cast<void *>(((uint64_t)hi << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(u, (short)0, __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000);
+}
+
 __device__ __forceinline__ float h2f(uint16_t h)
 {
     return static_cast<float>(__builtin_bit_cast(_Float16, h));

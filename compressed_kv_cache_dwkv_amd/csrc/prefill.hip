@@ -107,6 +107,7 @@ __global__ __launch_bounds__(kGramThreads) void gram_kernel(Layout ly, uint8_t *
     constexpr int CPR = D / 8;                  // 16-byte pieces of a token row
     __shared__ __attribute__((aligned(16))) uint16_t sT[2][D * kGramTile];
     __shared__ int s_tile0[kGramMaxBatch + 1];  // first flat tile of each sequence
+    __shared__ int s_len[kGramMaxBatch];        // its length, clamped to [0, n_cap]
 
     const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
     const int s = blockIdx.x, zh = blockIdx.y;
@@ -123,6 +124,7 @@ __global__ __launch_bounds__(kGramThreads) void gram_kernel(Layout ly, uint8_t *
                 bad = DWKV_DEVERR_BAD_LENGTH;
                 n = n < 0 ? 0 : (int)a.n_cap;
             }
+            s_len[b] = n;
             f += (n + kGramTile - 1) / kGramTile;
         }
         s_tile0[a.B] = f;
@@ -132,29 +134,38 @@ __global__ __launch_bounds__(kGramThreads) void gram_kernel(Layout ly, uint8_t *
     const int F = s_tile0[a.B];
     const int f0 = (int)((int64_t)F * s / a.S), f1 = (int)((int64_t)F * (s + 1) / a.S);
 
-    // this thread's share of a tile: 4 consecutive tokens x 8 channels
+    // this thread's share of a tile: 4 consecutive tokens x 8 channels; two
+    // tiles are in flight (the loads of tiles f + 1 and f + 2 while tile f
+    // is contracted)
     const bool loader = tid < 2 * D;
     const int col8 = tid % CPR, rowq = tid / CPR;
-    uint4 x[4];
+    uint4 xa[4], xb[4];
     int b = 0;
-    auto load = [&](int f) {
+    auto load = [&](int f, uint4 (&x)[4]) {
+        // (the length from LDS: a global load here would make the tile
+        // loads wait for every load in flight)
         while (f >= s_tile0[b + 1]) ++b;
-        int n = a.n_tokens[b];
-        n = n < 0 ? 0 : (n > a.n_cap ? (int)a.n_cap : n);
+        const int n = s_len[b];
         const int t0 = (f - s_tile0[b]) * kGramTile + 4 * rowq;
-        const uint16_t *src = X + ((int64_t)(b * a.Hkv + h) * a.n_cap) * D + 8 * col8;
+        // buffer loads over the sequence's first n rows: rows past them read
+        // as zeros, and every load is issued, so the waits count the loads
+        // in flight exactly
+        const __amdgpu_buffer_rsrc_t rs = block_rsrc(X + (int64_t)(b * a.Hkv + h) * a.n_cap * D, (int64_t)n * D * 2);
+        const uint32_t off = (uint32_t)t0 * (D * 2) + 16u * col8;
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-            x[u] = (loader && t0 + u < n) ? *reinterpret_cast<const uint4 *>(src + (int64_t)(t0 + u) * D)
-                                          : make_uint4(0, 0, 0, 0);
+        for (int u = 0; u < 4; ++u) {
+            const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, off + (uint32_t)(u * D * 2), 0, 0);
+            x[u] = make_uint4(v[0], v[1], v[2], v[3]);
+        }
     };
 
     float4_t acc[PW];
 #pragma unroll
     for (int i = 0; i < PW; ++i) acc[i] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-    if (f0 < f1) load(f0);
-    for (int f = f0, buf = 0; f < f1; ++f, buf ^= 1) {
+    // tile f (registers x) into LDS buffer buf, then its products; the loads
+    // of tile f + 2 go into x once it is stored
+    auto step = [&](int f, int buf, uint4 (&x)[4]) {
         // the loaded pieces into the tile, 4 tokens of one channel per store
         if (loader) {
 #pragma unroll
@@ -167,7 +178,7 @@ __global__ __launch_bounds__(kGramThreads) void gram_kernel(Layout ly, uint8_t *
             }
         }
         __syncthreads();
-        if (f + 1 < f1) load(f + 1);
+        load(f + 2 < f1 ? f + 2 : f1 - 1, x);  // past the last tile: a load of it, unused
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             half8_t fr[NB];
@@ -184,6 +195,18 @@ __global__ __launch_bounds__(kGramThreads) void gram_kernel(Layout ly, uint8_t *
             default: gram_mma<D, 3, 0>(fr, acc); break;
             }
         }
+    };
+    if (f0 < f1) {
+        load(f0, xa);
+        load(f0 + 1 < f1 ? f0 + 1 : f1 - 1, xb);
+        // whole pairs, then an odd last tile (so that every pass through the
+        // loop issues its loads in the same order)
+        int f = f0;
+        for (; f + 1 < f1; f += 2) {
+            step(f, 0, xa);
+            step(f + 1, 1, xb);
+        }
+        if (f < f1) step(f, 0, xa);
     }
 
     // the partial sums, lane-major: element (p, j, lane) of block p is

@@ -387,7 +387,9 @@ int dwkv_prefill_workspace_bytes(const dwkv_config *cfg, size_t *bytes);
 
 /* The window of `layer` gets layer's contribution.  The matrix-core partial
  * sums are fp32 per workgroup (a fixed share of the 64-token tiles of the
- * layer), added in fp64 in workgroup order: the result is deterministic. */
+ * layer), added in fp64 in workgroup order: the result is deterministic.
+ * DWKV_ERR_UNSUPPORTED when (n_cap + 256) * head_dim * 2 exceeds 2^32 - 1
+ * (a sequence's rows are addressed with 32-bit byte offsets). */
 int dwkv_prefill_gram(dwkv_handle *h, int layer, const void *k, const void *v, const int32_t *n_tokens, int batch,
                       int64_t n_cap, int first, void *workspace, size_t workspace_bytes, void *stream);
 
