@@ -262,6 +262,7 @@ def test_prefill_host_checks():
         assert g(k=ctypes.c_void_p((1 << 44) + 8)) == d.DWKV_ERR_INVALID_ARG
         assert g(p=ctypes.c_void_p((1 << 43) + 64)) == d.DWKV_ERR_INVALID_ARG
         assert g(sz=ws - 1) == d.DWKV_ERR_WORKSPACE
+        assert g(cap=(1 << 24)) == d.DWKV_ERR_UNSUPPORTED              # rows beyond 32-bit byte offsets
         b = lambda g0=0, ng=1, om=kk, k=72, q=2, sz=ws: L.dwkv_prefill_bases(h, g0, ng, om, k, q, None, wsp, sz, None)
         assert b(om=None) == d.DWKV_ERR_INVALID_ARG
         assert b(g0=7, ng=2) == d.DWKV_ERR_INVALID_ARG
