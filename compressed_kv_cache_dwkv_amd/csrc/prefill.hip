@@ -25,8 +25,9 @@
 //             (sequence, KV head) at once) and lists the tokens by tier; the
 //             encoder takes 64 tokens of one tier per wave, one per lane, and
 //             follows the append's order of operations exactly (so it gives
-//             the append's bits), the basis values reaching every lane
-//             through scalar loads; a publish pass sets the tier counts.
+//             the append's bits), the fp16 basis values reaching every
+//             lane through scalar loads as operands of mixed-precision
+//             FMAs; a publish pass sets the tier counts.
 #include <hip/hip_runtime.h>
 
 #include "device.h"
@@ -718,11 +719,12 @@ __global__ __launch_bounds__(kSlotThreads) void place_kernel(Layout ly, uint8_t 
     }
 }
 
-// The window's bases in fp32 for the encoder's scalar loads: rows [z][h][i][j]
-// and, for the coefficient sums, blocks of 8 coefficients [z][h][i / 8][j][i % 8]
-// (a (z, h) spans d * kMaxRank floats): one block's loads sit at fixed offsets
+// The window's bases for the encoder's scalar loads, fp16 as in the cache:
+// rows [z][h][i][j] (a (z, h) spans r_max * d values) and, for the
+// coefficient sums, blocks of 8 coefficients [z][h][i / 8][j][i % 8] (a
+// (z, h) spans d * kMaxRank values): one block's loads sit at fixed offsets
 // from one address and fill whole cache lines.
-__global__ void basis_f32_kernel(Layout ly, uint8_t *arena, int m, float *rows, float *cols)
+__global__ void basis_copy_kernel(Layout ly, uint8_t *arena, int m, uint16_t *rows, uint16_t *blocks)
 {
     const int64_t n = 2 * ly.basis_elems;
     for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < n; e += (int64_t)gridDim.x * blockDim.x) {
@@ -731,9 +733,9 @@ __global__ void basis_f32_kernel(Layout ly, uint8_t *arena, int m, float *rows, 
         const int h = (int)(rem / ((int64_t)ly.R * ly.d));
         const int64_t r2 = rem - (int64_t)h * ly.R * ly.d;
         const int i = (int)(r2 / ly.d), j = (int)(r2 % ly.d);
-        const float v = h2f(basis_ptr(ly, arena, m, z, h)[(int64_t)i * ly.d + j]);
+        const uint16_t v = basis_ptr(ly, arena, m, z, h)[(int64_t)i * ly.d + j];
         rows[e] = v;
-        cols[((int64_t)z * ly.Hkv + h) * ly.d * kMaxRank + ((int64_t)(i >> 3) * ly.d + j) * 8 + (i & 7)] = v;
+        blocks[((int64_t)z * ly.Hkv + h) * ly.d * kMaxRank + ((int64_t)(i >> 3) * ly.d + j) * 8 + (i & 7)] = v;
     }
 }
 
@@ -747,11 +749,16 @@ __device__ __forceinline__ float keep_fp32(float v)
 }
 
 template <int N>
-__device__ __forceinline__ void sload(const float *__restrict__ p, float (&v)[N])
+__device__ __forceinline__ void sload(const uint32_t *__restrict__ p, uint32_t (&v)[N])
 {
 #pragma unroll
     for (int u = 0; u < N; ++u) v[u] = p[u];
 }
+
+// fp16 halves of a 32-bit word, exactly in fp32 (the multiply-adds take them
+// as fp16 operands of a mixed-precision FMA)
+__device__ __forceinline__ float lo_h(uint32_t w) { return h2f((uint16_t)(w & 0xFFFFu)); }
+__device__ __forceinline__ float hi_h(uint32_t w) { return h2f((uint16_t)(w >> 16)); }
 
 // Encodes up to 64 tokens of one tier of one (sequence, KV head) and one Z,
 // one token per lane, in exactly the append's order of operations: step 1
@@ -763,8 +770,8 @@ __device__ __forceinline__ void sload(const float *__restrict__ p, float (&v)[N]
 // are wave-uniform: they come through scalar loads.
 template <int D, int CB>  // CB: bytes per stored coefficient (2: fp16, 1: 8-bit codes)
 __global__ __launch_bounds__(kWave) void encode_kernel(Layout ly, uint8_t *__restrict__ arena, EncodeArgs a,
-                                                       const float *__restrict__ brows,
-                                                       const float *__restrict__ bcols)
+                                                       const uint16_t *__restrict__ brows,
+                                                       const uint16_t *__restrict__ bblocks)
 {
 #pragma clang fp contract(off)
     // [r][64]: this wave's coefficients, lane-minor (fp16 when they are
@@ -802,33 +809,36 @@ __global__ __launch_bounds__(kWave) void encode_kernel(Layout ly, uint8_t *__res
     const int slot = a.cnt0[bh * kMaxTiers + k] + (live ? u : first);
     const int r = ly.rank[k], s = ly.resid[k];
     uint8_t *blk = head_block_ptr(ly, arena, a.layer, b, h);
-    const float *__restrict__ Brow = brows + (int64_t)zh * ly.R * D;      // [i][j]
-    const float *__restrict__ Bcol = bcols + (int64_t)zh * D * kMaxRank;  // [i / 8][j][i % 8]
+    // fp16 basis words: rows [i][j / 2], blocks [i / 8][j][(i % 8) / 2]
+    const uint32_t *__restrict__ Brow = reinterpret_cast<const uint32_t *>(brows + (int64_t)zh * ly.R * D);
+    const uint32_t *__restrict__ Bblk = reinterpret_cast<const uint32_t *>(bblocks + (int64_t)zh * D * kMaxRank);
     const uint16_t *X = (z ? a.v : a.k) + ((int64_t)bh * a.n_cap + t) * D;
 
-    // 1. the coefficient sums, eight at a time
+    // 1. the coefficient sums, eight at a time (x as fp16 pairs)
     {
-        float x[D];
+        uint32_t xw[D / 2];
 #pragma unroll
         for (int q = 0; q < D / 8; ++q) {
             const uint4 v = reinterpret_cast<const uint4 *>(X)[q];
-            const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                x[8 * q + 2 * m] = h2f((uint16_t)(wv[m] & 0xFFFF));
-                x[8 * q + 2 * m + 1] = h2f((uint16_t)(wv[m] >> 16));
-            }
+            xw[4 * q] = v.x;
+            xw[4 * q + 1] = v.y;
+            xw[4 * q + 2] = v.z;
+            xw[4 * q + 3] = v.w;
         }
         for (int i0 = 0; i0 < r; i0 += 8) {
             float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-            const float *__restrict__ bc = Bcol + (int64_t)i0 * D;
+            const uint32_t *__restrict__ bb = Bblk + (int64_t)i0 * D / 2;
             if (i0 + 8 <= r) {
 #pragma unroll
                 for (int j = 0; j < D; ++j) {
-                    float bv[8];
-                    sload<8>(bc + j * 8, bv);
+                    uint32_t bw[4];
+                    sload<4>(bb + j * 4, bw);
+                    const float xj = (j & 1) ? hi_h(xw[j / 2]) : lo_h(xw[j / 2]);
 #pragma unroll
-                    for (int q = 0; q < 8; ++q) acc[q] = __builtin_fmaf(bv[q], x[j], acc[q]);
+                    for (int q = 0; q < 4; ++q) {
+                        acc[2 * q] = __builtin_fmaf(lo_h(bw[q]), xj, acc[2 * q]);
+                        acc[2 * q + 1] = __builtin_fmaf(hi_h(bw[q]), xj, acc[2 * q + 1]);
+                    }
                 }
 #pragma unroll
                 for (int q = 0; q < 8; ++q) {
@@ -840,10 +850,14 @@ __global__ __launch_bounds__(kWave) void encode_kernel(Layout ly, uint8_t *__res
             } else {
 #pragma unroll
                 for (int j = 0; j < D; ++j) {
-                    float bv[4];
-                    sload<4>(bc + j * 8, bv);
+                    uint32_t bw[2];
+                    sload<2>(bb + j * 4, bw);
+                    const float xj = (j & 1) ? hi_h(xw[j / 2]) : lo_h(xw[j / 2]);
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) acc[q] = __builtin_fmaf(bv[q], x[j], acc[q]);
+                    for (int q = 0; q < 2; ++q) {
+                        acc[2 * q] = __builtin_fmaf(lo_h(bw[q]), xj, acc[2 * q]);
+                        acc[2 * q + 1] = __builtin_fmaf(hi_h(bw[q]), xj, acc[2 * q + 1]);
+                    }
                 }
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
@@ -883,13 +897,16 @@ __global__ __launch_bounds__(kWave) void encode_kernel(Layout ly, uint8_t *__res
         for (int j = 0; j < D; ++j) e[j] = 0.0f;
         for (int i = 0; i < r; ++i) {
             const float ci = CB == 2 ? h2f(s_h[i * kWave + lane]) : s_c[i * kWave + lane];
-            const float *__restrict__ br = Brow + (int64_t)i * D;
+            const uint32_t *__restrict__ br = Brow + (int64_t)i * D / 2;
 #pragma unroll
             for (int j0 = 0; j0 < D; j0 += 8) {
-                float bv[8];
-                sload<8>(br + j0, bv);
+                uint32_t bw[4];
+                sload<4>(br + j0 / 2, bw);
 #pragma unroll
-                for (int q = 0; q < 8; ++q) e[j0 + q] = __builtin_fmaf(bv[q], ci, e[j0 + q]);
+                for (int q = 0; q < 4; ++q) {
+                    e[j0 + 2 * q] = __builtin_fmaf(lo_h(bw[q]), ci, e[j0 + 2 * q]);
+                    e[j0 + 2 * q + 1] = __builtin_fmaf(hi_h(bw[q]), ci, e[j0 + 2 * q + 1]);
+                }
             }
         }
 #pragma unroll
@@ -1057,8 +1074,8 @@ hipError_t launch_prefill_encode(const Layout &ly, uint8_t *arena, const EncodeA
 {
     (void)hipGetLastError();  // drop errors left by earlier, unrelated calls
     const int64_t be = 2 * ly.basis_elems;
-    hipLaunchKernelGGL(basis_f32_kernel, dim3((unsigned)((be + 255) / 256 < 1024 ? (be + 255) / 256 : 1024)),
-                       dim3(256), 0, stream, ly, arena, a.layer / ly.G, a.basis_rows, a.basis_cols);
+    hipLaunchKernelGGL(basis_copy_kernel, dim3((unsigned)((be + 255) / 256 < 1024 ? (be + 255) / 256 : 1024)),
+                       dim3(256), 0, stream, ly, arena, a.layer / ly.G, a.basis_rows, a.basis_blocks);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(count_kernel, dim3(a.n_chunks, batch * ly.Hkv), dim3(kSlotThreads), 0, stream, ly, a);
@@ -1074,7 +1091,7 @@ hipError_t launch_prefill_encode(const Layout &ly, uint8_t *arena, const EncodeA
     const size_t sel_lds = (size_t)2 * (kMaxResid + 1) * kWave * 4;
     const size_t lds = coef_lds > sel_lds ? coef_lds : sel_lds;
     hipLaunchKernelGGL(kern, dim3(chunks, 2 * ly.Hkv, batch), dim3(kWave), lds, stream, ly, arena, a, a.basis_rows,
-                       a.basis_cols);
+                       a.basis_blocks);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int n = batch * ly.Hkv * ly.T;
