@@ -683,7 +683,7 @@ struct PrefillWs {
     float *part;
     int32_t *status, *cnt0, *tot, *inv, *cntc;
     int n_chunks;
-    uint16_t *brows, *bblocks;
+    uint16_t *bblocks;
     size_t bytes;
 };
 
@@ -706,7 +706,6 @@ static PrefillWs carve_prefill(const Layout &ly, void *base)
     w.inv = reinterpret_cast<int32_t *>(take((int64_t)ly.Bmax * ly.Hkv * ly.max_tokens * 4));
     w.n_chunks = (int)((ly.max_tokens + dwkv::kSlotChunk - 1) / dwkv::kSlotChunk) + 1;
     w.cntc = reinterpret_cast<int32_t *>(take((int64_t)ly.Bmax * ly.Hkv * w.n_chunks * dwkv::kChunkStride * 4));
-    w.brows = reinterpret_cast<uint16_t *>(take((int64_t)2 * ly.basis_elems * 2));
     w.bblocks = reinterpret_cast<uint16_t *>(take((int64_t)2 * ly.Hkv * ly.d * dwkv::kMaxRank * 2));
     w.bytes = off;
     return w;
@@ -803,7 +802,6 @@ int dwkv_prefill_encode(dwkv_handle *h, int layer, const void *k, const void *v,
     a.cnt0 = w.cnt0;
     a.tot = w.tot;
     a.inv = w.inv;
-    a.basis_rows = w.brows;
     a.basis_blocks = w.bblocks;
     a.cntc = w.cntc;
     {

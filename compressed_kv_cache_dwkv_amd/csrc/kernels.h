@@ -134,8 +134,7 @@ struct EncodeArgs {
     int32_t *inv;                 // [B][Hkv][max_tokens] the call's tokens listed by tier
     int32_t *cntc;                // [B][Hkv][n_chunks][kChunkStride] tier counts per chunk (+ a bad-tier flag)
     int n_chunks;                 // chunks of kSlotChunk positions the call's counts cover
-    uint16_t *basis_rows;         // the window's bases, fp16 [2][Hkv][r_max][d]
-    uint16_t *basis_blocks;       // and in blocks of 8 rows, fp16 [2][Hkv][kMaxRank / 8][d][8]
+    uint16_t *basis_blocks;       // the window's bases in blocks of 8 rows, fp16 [2][Hkv][kMaxRank / 8][d][8]
 };
 hipError_t launch_prefill_encode(const Layout &ly, uint8_t *arena, const EncodeArgs &a, int batch,
                                  hipStream_t stream);

@@ -719,12 +719,11 @@ __global__ __launch_bounds__(kSlotThreads) void place_kernel(Layout ly, uint8_t 
     }
 }
 
-// The window's bases for the encoder's scalar loads, fp16 as in the cache:
-// rows [z][h][i][j] (a (z, h) spans r_max * d values) and, for the
-// coefficient sums, blocks of 8 coefficients [z][h][i / 8][j][i % 8] (a
-// (z, h) spans d * kMaxRank values): one block's loads sit at fixed offsets
-// from one address and fill whole cache lines.
-__global__ void basis_copy_kernel(Layout ly, uint8_t *arena, int m, uint16_t *rows, uint16_t *blocks)
+// The window's bases for the encoder's scalar loads, fp16 as in the cache,
+// in blocks of 8 rows [z][h][i / 8][j][i % 8] (a (z, h) spans d * kMaxRank
+// values): the loads of one block sit at fixed offsets from one address and
+// fill whole cache lines, and both encoder steps read them.
+__global__ void basis_copy_kernel(Layout ly, uint8_t *arena, int m, uint16_t *blocks)
 {
     const int64_t n = 2 * ly.basis_elems;
     for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < n; e += (int64_t)gridDim.x * blockDim.x) {
@@ -733,9 +732,8 @@ __global__ void basis_copy_kernel(Layout ly, uint8_t *arena, int m, uint16_t *ro
         const int h = (int)(rem / ((int64_t)ly.R * ly.d));
         const int64_t r2 = rem - (int64_t)h * ly.R * ly.d;
         const int i = (int)(r2 / ly.d), j = (int)(r2 % ly.d);
-        const uint16_t v = basis_ptr(ly, arena, m, z, h)[(int64_t)i * ly.d + j];
-        rows[e] = v;
-        blocks[((int64_t)z * ly.Hkv + h) * ly.d * kMaxRank + ((int64_t)(i >> 3) * ly.d + j) * 8 + (i & 7)] = v;
+        blocks[((int64_t)z * ly.Hkv + h) * ly.d * kMaxRank + ((int64_t)(i >> 3) * ly.d + j) * 8 + (i & 7)] =
+            basis_ptr(ly, arena, m, z, h)[(int64_t)i * ly.d + j];
     }
 }
 
@@ -770,7 +768,6 @@ __device__ __forceinline__ float hi_h(uint32_t w) { return h2f((uint16_t)(w >> 1
 // are wave-uniform: they come through scalar loads.
 template <int D, int CB>  // CB: bytes per stored coefficient (2: fp16, 1: 8-bit codes)
 __global__ __launch_bounds__(kWave) void encode_kernel(Layout ly, uint8_t *__restrict__ arena, EncodeArgs a,
-                                                       const uint16_t *__restrict__ brows,
                                                        const uint16_t *__restrict__ bblocks)
 {
 #pragma clang fp contract(off)
@@ -809,8 +806,7 @@ __global__ __launch_bounds__(kWave) void encode_kernel(Layout ly, uint8_t *__res
     const int slot = a.cnt0[bh * kMaxTiers + k] + (live ? u : first);
     const int r = ly.rank[k], s = ly.resid[k];
     uint8_t *blk = head_block_ptr(ly, arena, a.layer, b, h);
-    // fp16 basis words: rows [i][j / 2], blocks [i / 8][j][(i % 8) / 2]
-    const uint32_t *__restrict__ Brow = reinterpret_cast<const uint32_t *>(brows + (int64_t)zh * ly.R * D);
+    // fp16 basis words in blocks of 8 rows: [i / 8][j][(i % 8) / 2]
     const uint32_t *__restrict__ Bblk = reinterpret_cast<const uint32_t *>(bblocks + (int64_t)zh * D * kMaxRank);
     const uint16_t *X = (z ? a.v : a.k) + ((int64_t)bh * a.n_cap + t) * D;
 
@@ -895,18 +891,46 @@ __global__ __launch_bounds__(kWave) void encode_kernel(Layout ly, uint8_t *__res
     if (s > 0) {
 #pragma unroll
         for (int j = 0; j < D; ++j) e[j] = 0.0f;
-        for (int i = 0; i < r; ++i) {
-            const float ci = CB == 2 ? h2f(s_h[i * kWave + lane]) : s_c[i * kWave + lane];
-            const uint32_t *__restrict__ br = Brow + (int64_t)i * D / 2;
+        // eight coefficients at a time from the same basis blocks as step 1
+        // (then a last block of four): each channel's chain still runs over
+        // i in ascending order
+        int i0 = 0;
+        for (; i0 + 8 <= r; i0 += 8) {
+            const uint32_t *__restrict__ bb = Bblk + (int64_t)i0 * D / 2;
+            float c[8];
 #pragma unroll
-            for (int j0 = 0; j0 < D; j0 += 8) {
-                uint32_t bw[4];
-                sload<4>(br + j0 / 2, bw);
+            for (int q = 0; q < 8; ++q) c[q] = CB == 2 ? h2f(s_h[(i0 + q) * kWave + lane]) : s_c[(i0 + q) * kWave + lane];
+            // four channels per 64-byte load, their chains interleaved
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    e[j0 + 2 * q] = __builtin_fmaf(lo_h(bw[q]), ci, e[j0 + 2 * q]);
-                    e[j0 + 2 * q + 1] = __builtin_fmaf(hi_h(bw[q]), ci, e[j0 + 2 * q + 1]);
+            for (int j0 = 0; j0 < D; j0 += 4) {
+                uint32_t bw[16];
+                sload<16>(bb + j0 * 4, bw);
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const uint32_t w = bw[4 * u + q / 2];
+                        e[j0 + u] = __builtin_fmaf((q & 1) ? hi_h(w) : lo_h(w), c[q], e[j0 + u]);
+                    }
                 }
+            }
+        }
+        if (i0 < r) {
+            const uint32_t *__restrict__ bb = Bblk + (int64_t)i0 * D / 2;
+            float c[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) c[q] = CB == 2 ? h2f(s_h[(i0 + q) * kWave + lane]) : s_c[(i0 + q) * kWave + lane];
+#pragma unroll
+            for (int j = 0; j < D; ++j) {
+                uint32_t bw[2];
+                sload<2>(bb + j * 4, bw);
+                float v = e[j];
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    v = __builtin_fmaf(lo_h(bw[q]), c[2 * q], v);
+                    v = __builtin_fmaf(hi_h(bw[q]), c[2 * q + 1], v);
+                }
+                e[j] = v;
             }
         }
 #pragma unroll
@@ -1075,7 +1099,7 @@ hipError_t launch_prefill_encode(const Layout &ly, uint8_t *arena, const EncodeA
     (void)hipGetLastError();  // drop errors left by earlier, unrelated calls
     const int64_t be = 2 * ly.basis_elems;
     hipLaunchKernelGGL(basis_copy_kernel, dim3((unsigned)((be + 255) / 256 < 1024 ? (be + 255) / 256 : 1024)),
-                       dim3(256), 0, stream, ly, arena, a.layer / ly.G, a.basis_rows, a.basis_blocks);
+                       dim3(256), 0, stream, ly, arena, a.layer / ly.G, a.basis_blocks);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(count_kernel, dim3(a.n_chunks, batch * ly.Hkv), dim3(kSlotThreads), 0, stream, ly, a);
@@ -1090,8 +1114,7 @@ hipError_t launch_prefill_encode(const Layout &ly, uint8_t *arena, const EncodeA
     const size_t coef_lds = (size_t)ly.R * kWave * (ly.cb == 2 ? 2 : 4);
     const size_t sel_lds = (size_t)2 * (kMaxResid + 1) * kWave * 4;
     const size_t lds = coef_lds > sel_lds ? coef_lds : sel_lds;
-    hipLaunchKernelGGL(kern, dim3(chunks, 2 * ly.Hkv, batch), dim3(kWave), lds, stream, ly, arena, a, a.basis_rows,
-                       a.basis_blocks);
+    hipLaunchKernelGGL(kern, dim3(chunks, 2 * ly.Hkv, batch), dim3(kWave), lds, stream, ly, arena, a, a.basis_blocks);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int n = batch * ly.Hkv * ly.T;
