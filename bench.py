@@ -442,7 +442,7 @@ PREFILL_METRIC = "prefill compression tokens/s (prompt tokens, all layers: Gram 
 PREFILL_SRCS = [os.path.join(ROOT, "compressed_kv_cache_dwkv_amd", "csrc", "prefill.hip")]
 PREFILL_RUN_ARGS = "--mode prefill --steps 1 --warmup 1 --no-cpu-baseline --copy-probe --kernel-reps 1"
 PREFILL_TRACE_ARGS = "--mode prefill --steps 3 --warmup 1 --no-cpu-baseline --kernel-reps 2"
-PREFILL_KERNELS = ("gram_kernel", "gram_reduce_kernel", "bases_kernel", "transpose_basis_kernel", "basis_f32_kernel",
+PREFILL_KERNELS = ("gram_kernel", "gram_reduce_kernel", "bases_kernel", "transpose_basis_kernel", "basis_copy_kernel",
                    "count_kernel", "place_kernel", "encode_kernel", "publish_kernel")
 
 
@@ -535,7 +535,7 @@ def prefill_trace_summary(cfg, ci: int, trace_dir: str, bench_json: Optional[str
              f"--config {ci} {PREFILL_TRACE_ARGS}",
              f"python3 <repo>/bench.py --config {ci} --mode prefill --trace-summary <out> [--bench-json <line>]",
              "```", "",
-             "Per prompt: one Gram launch (+ reduction) and one encode family (count, place, fp32 basis copy, encode,",
+             "Per prompt: one Gram launch (+ reduction) and one encode family (count, place, fp16 basis block copy, encode,",
              "publish) per layer, one bases launch for all windows (+ a transpose per window).", "",
              "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
     for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
@@ -650,9 +650,14 @@ def run_prefill(args, cfg, K: int, W: int):
     else:
         roof = {"bound": "alu", "kernel": "encode_kernel (+ slot and publish passes)",
                 "achieved": enc_flop_layer / (enc_layer_ms * 1e-3) / 1e12, "peak": 157.3, "unit": "TFLOP/s",
+                # 157.3 counts two fp32 FMAs per lane and cycle (packed); one per
+                # lane and cycle: 256 CUs x 64 lanes x 2 flops x 2.4 GHz
+                "peak_unpacked": 78.6,
                 "algorithmic_flop_per_launch": enc_flop_layer, "mean_launch_us": enc_layer_ms * 1e3,
                 "hbm_GBps": by["encode_per_layer"] / (enc_layer_ms * 1e-3) / 1e9}
     roof["frac"] = roof["achieved"] / roof["peak"]
+    if "peak_unpacked" in roof:
+        roof["frac_unpacked"] = roof["achieved"] / roof["peak_unpacked"]
     kname = "gram_kernel" if dominant == "gram" else "encode_kernel"
     roof["traffic"] = prefill_stored_traffic(cfg, kname)
     if roof["traffic"] is not None:
