@@ -779,17 +779,24 @@ __global__ __launch_bounds__(kWave) void encode_kernel(Layout ly, uint8_t *__res
     const int zh = blockIdx.y, z = zh / ly.Hkv, h = zh % ly.Hkv, b = blockIdx.z;
     const int bh = b * ly.Hkv + h;
     const int lane = threadIdx.x;
+    // the (sequence, KV head)'s status, tier totals and first slots in one
+    // round trip (every load issued before any is used)
     const int n0 = a.status[bh];
-    if (n0 < 0) return;
+    int totv[kMaxTiers], c0v[kMaxTiers];
+#pragma unroll
+    for (int kk = 0; kk < kMaxTiers; ++kk) {
+        const int tv = a.tot[bh * kMaxTiers + kk], cv = a.cnt0[bh * kMaxTiers + kk];
+        totv[kk] = kk < ly.T ? tv : 0;
+        c0v[kk] = cv;
+    }
     // the chunk's tier: chunks of 64 list entries, tier by tier from the
-    // highest rank (the longest chunks are dispatched first)
-    const int chunk = blockIdx.x;
+    // highest rank (the longest chunks are dispatched first); none for a
+    // refused (sequence, KV head)
+    const int chunk = n0 < 0 ? 0x7FFFFFFF : (int)blockIdx.x;
     int k = -1, first = 0, c0 = 0;
 #pragma unroll
     for (int kk = kMaxTiers - 1; kk >= 0; --kk) {
-        if (kk >= ly.T) continue;
-        const int tot = a.tot[bh * kMaxTiers + kk];
-        const int nc = (tot + kWave - 1) / kWave;
+        const int nc = (totv[kk] + kWave - 1) / kWave;
         if (k < 0 && chunk < c0 + nc) {
             k = kk;
             first = (chunk - c0) * kWave;
@@ -797,13 +804,17 @@ __global__ __launch_bounds__(kWave) void encode_kernel(Layout ly, uint8_t *__res
         c0 += nc;
     }
     if (k < 0) return;
-    int base = 0;
-    for (int kk = 0; kk < k; ++kk) base += a.tot[bh * kMaxTiers + kk];
-    const int tot = a.tot[bh * kMaxTiers + k];
+    int base = 0, tot = 0, cnt0 = 0;
+#pragma unroll
+    for (int kk = 0; kk < kMaxTiers; ++kk) {
+        base += kk < k ? totv[kk] : 0;
+        tot = kk == k ? totv[kk] : tot;
+        cnt0 = kk == k ? c0v[kk] : cnt0;
+    }
     const int u = first + lane;
     const bool live = u < tot;
     const int t = live ? a.inv[(int64_t)bh * ly.max_tokens + base + u] : a.inv[(int64_t)bh * ly.max_tokens + base + first];
-    const int slot = a.cnt0[bh * kMaxTiers + k] + (live ? u : first);
+    const int slot = cnt0 + (live ? u : first);
     const int r = ly.rank[k], s = ly.resid[k];
     uint8_t *blk = head_block_ptr(ly, arena, a.layer, b, h);
     // fp16 basis words in blocks of 8 rows: [i / 8][j][(i % 8) / 2]
