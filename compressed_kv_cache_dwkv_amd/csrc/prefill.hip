@@ -254,7 +254,7 @@ __global__ __launch_bounds__(256) void gram_reduce_kernel(GramArgs a)
 
 // ------------------------------------------------------------------ bases
 
-constexpr int kBasesThreads = 512;
+constexpr int kBasesThreads = 1024;
 constexpr int kBasesWaves = kBasesThreads / kWave;
 constexpr int kColsPerWave = (kMaxSketch + kBasesWaves - 1) / kBasesWaves;
 
@@ -344,7 +344,7 @@ __device__ void gemm_cq(const double *C, const double *src, double *dst, int k, 
 template <int D>
 __device__ void orth(const double *W, double *Q, int k, int ks, double *sv, double *sr, double *sp, double *sred)
 {
-    constexpr int QT = kBasesThreads / 4;          // threads per quarter (128)
+    constexpr int QT = kBasesThreads / 4;          // threads per quarter
     const int tid = threadIdx.x, qi = tid / QT, qt = tid % QT;
     int kept = 0;
     for (int cand = 0; kept < k && cand < k + D; ++cand) {
