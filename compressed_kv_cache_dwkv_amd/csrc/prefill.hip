@@ -30,6 +30,8 @@
 //             FMAs; a publish pass sets the tier counts.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "device.h"
 #include "kernels.h"
 #include "layout.h"
@@ -145,8 +147,8 @@ __global__ __launch_bounds__(kGramThreads) void gram_kernel(Layout ly, uint8_t *
     auto load = [&](int f, uint4 (&x)[4]) {
         // (the length from LDS: a global load here would make the tile
         // loads wait for every load in flight)
-        while (f >= s_tile0[b + 1]) ++b;
-        const int n = s_len[b];
+        while (b < a.B - 1 && f >= s_tile0[b + 1]) ++b;
+        const int n = f < f1 ? s_len[b] : 0;    // past this workgroup's share: zeros
         const int t0 = (f - s_tile0[b]) * kGramTile + 4 * rowq;
         // buffer loads over the sequence's first n rows: rows past them read
         // as zeros, and every load is issued, so the waits count the loads
@@ -164,9 +166,10 @@ __global__ __launch_bounds__(kGramThreads) void gram_kernel(Layout ly, uint8_t *
 #pragma unroll
     for (int i = 0; i < PW; ++i) acc[i] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-    // tile f (registers x) into LDS buffer buf, then its products; the loads
-    // of tile f + 2 go into x once it is stored
-    auto step = [&](int f, int buf, uint4 (&x)[4]) {
+    // tile f (registers x) into LDS buffer buf, then wave W's products; the
+    // loads of tile f + 2 go into x once it is stored
+    auto step = [&](auto wtag, int f, int buf, uint4 (&x)[4]) {
+        constexpr int W = decltype(wtag)::value;
         // the loaded pieces into the tile, 4 tokens of one channel per store
         if (loader) {
 #pragma unroll
@@ -179,7 +182,7 @@ __global__ __launch_bounds__(kGramThreads) void gram_kernel(Layout ly, uint8_t *
             }
         }
         __syncthreads();
-        load(f + 2 < f1 ? f + 2 : f1 - 1, x);  // past the last tile: a load of it, unused
+        load(f + 2 < f1 ? f + 2 : f1, x);       // past the share: zeros
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             half8_t fr[NB];
@@ -189,25 +192,28 @@ __global__ __launch_bounds__(kGramThreads) void gram_kernel(Layout ly, uint8_t *
                 const int ch = 16 * c + (lane & 15);
                 fr[c] = *reinterpret_cast<const half8_t *>(&sT[buf][ch * kGramTile + 8 * (g ^ gram_swz(ch))]);
             }
-            switch (wave) {
-            case 0: gram_mma<D, 0, 0>(fr, acc); break;
-            case 1: gram_mma<D, 1, 0>(fr, acc); break;
-            case 2: gram_mma<D, 2, 0>(fr, acc); break;
-            default: gram_mma<D, 3, 0>(fr, acc); break;
+            gram_mma<D, W, 0>(fr, acc);
+        }
+    };
+    // whole pairs of tiles (an odd count ends with a tile of zeros: index
+    // f1, whose loads all read past the rows), so that every pass through
+    // the loop issues its loads in the same order; one copy of the loop per
+    // wave, so that each wave's block list is fixed in its code
+    auto run = [&](auto wtag) {
+        if (f0 < f1) {
+            load(f0, xa);
+            load(f0 + 1, xb);
+            for (int f = f0; f < f1; f += 2) {
+                step(wtag, f, 0, xa);
+                step(wtag, f + 1, 1, xb);
             }
         }
     };
-    if (f0 < f1) {
-        load(f0, xa);
-        load(f0 + 1 < f1 ? f0 + 1 : f1 - 1, xb);
-        // whole pairs, then an odd last tile (so that every pass through the
-        // loop issues its loads in the same order)
-        int f = f0;
-        for (; f + 1 < f1; f += 2) {
-            step(f, 0, xa);
-            step(f + 1, 1, xb);
-        }
-        if (f < f1) step(f, 0, xa);
+    switch (wave) {
+    case 0: run(std::integral_constant<int, 0>{}); break;
+    case 1: run(std::integral_constant<int, 1>{}); break;
+    case 2: run(std::integral_constant<int, 2>{}); break;
+    default: run(std::integral_constant<int, 3>{}); break;
     }
 
     // the partial sums, lane-major: element (p, j, lane) of block p is
