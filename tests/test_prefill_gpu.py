@@ -286,6 +286,12 @@ CASES = {
                                                    resid_channels=4, resid_bits=8, n_tokens=3000), gates=False),
     "paper_literal": dict(cfg=lambda: _cfg8k(batch=3, r_max=32, tier_rank=(32,) * 4, tier_prob=(0.4, 0.3, 0.2, 0.1),
                                              tier_resid=(0, 2, 4, 8)), gates=True),
+    # ranks 4 mod 8: the encoder's 4-row remainder block in both steps, with
+    # 8-bit and fp16 coefficients
+    "ranks_4mod8_int8coef": dict(cfg=lambda: _cfg8k(batch=3, r_max=44, tier_rank=(4, 12, 20, 44),
+                                                    tier_prob=(0.4, 0.3, 0.2, 0.1), coef_bits=8), gates=True),
+    "ranks_4mod8_fp16": dict(cfg=lambda: _cfg8k(batch=3, r_max=44, tier_rank=(4, 12, 20, 44),
+                                                tier_prob=(0.4, 0.3, 0.2, 0.1)), gates=False),
 }
 
 
