@@ -622,10 +622,31 @@ def run_prefill(args, cfg, K: int, W: int):
         for l in range(L):
             cache.prefill_encode(l, k_dev[l % lpg], v_dev[l % lpg], n_dev, t_dev[l % lpg])
 
+    # The step as a pipeline: each window's bases start on a second stream
+    # (default priority) as soon as its Gram sums are complete, while the
+    # remaining Gram sums run; the encodes of a window wait for its bases
+    # only.  The bases read only their window's Gram sums, so they share the
+    # workspace with the other calls.
+    G = L // lpg
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    ev_gram = [torch.cuda.Event() for _ in range(G)]
+    ev_bases = [torch.cuda.Event() for _ in range(G)]
+
     def step(s):
-        grams()
-        bases()
-        encodes()
+        dwkv_reset(h)
+        for m in range(G):
+            for l in range(m * lpg, (m + 1) * lpg):
+                cache.prefill_gram(l, k_dev[l % lpg], v_dev[l % lpg], n_dev, first=(l % lpg == 0))
+            ev_gram[m].record(main)
+            with torch.cuda.stream(side):
+                side.wait_event(ev_gram[m])
+                cache.prefill_bases(m, om_dev[m:m + 1], q)
+                ev_bases[m].record(side)
+        for m in range(G):
+            main.wait_event(ev_bases[m])
+            for l in range(m * lpg, (m + 1) * lpg):
+                cache.prefill_encode(l, k_dev[l % lpg], v_dev[l % lpg], n_dev, t_dev[l % lpg])
 
     elapsed_ms = _time_graph_steps(step, W, K, 1)
     assert cache.check_errors() == 0, "prefill overflowed the cache"

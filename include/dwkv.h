@@ -379,7 +379,12 @@ int dwkv_probe_update(float *tau, int32_t *below, int n_windows, const float *er
  * Workspace: device memory of dwkv_prefill_workspace_bytes(cfg) bytes,
  * 256-byte aligned, zero-filled by the caller before its first use and left
  * ready for the next call; one workspace per stream of concurrent prefill
- * work.  Its first num_groups * 2 * num_kv_heads * head_dim^2 * 8 bytes hold
+ * work, with one exception: dwkv_prefill_bases reads only its windows' Gram
+ * sums and writes only their bases, so it may run on another stream, with
+ * the same workspace, concurrently with Gram calls of other windows and
+ * encode calls of layers of other windows (the caller orders each window's
+ * Gram calls before its bases and its bases before its encodes, for
+ * instance with events).  Its first num_groups * 2 * num_kv_heads * head_dim^2 * 8 bytes hold
  * the Gram sums, fp64 [window][Z][KV head][head_dim][head_dim] (row-major,
  * exactly symmetric), for inspection.
  */

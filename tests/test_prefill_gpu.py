@@ -522,6 +522,62 @@ def test_appends_after_prefill_continue_the_layer(G):
         cache.close()
 
 
+def test_prefill_pipelined_on_two_streams(G):
+    """Each window's bases on a second stream as soon as its Gram sums are
+    complete, overlapping the next windows' Gram sums, and each window's
+    encodes waiting for its bases only, all on one workspace: the bases and
+    every encoded layer equal those of the sequential order, bit for bit."""
+    import torch
+    cfg = _cfg8k(batch=2)
+    lengths, n, nw = [1500, 900], 1500, 3
+    lpg = cfg.layers_per_group
+    layers = range(nw * lpg)
+    data = {l: gen_prefill(cfg, l, lengths=lengths, tail=0.0) for l in layers}
+    tiers = {l: G.dev(gen_tiers(cfg, l, n)) for l in layers}
+    dev = {l: (G.dev(data[l][0]), G.dev(data[l][1])) for l in layers}
+    omega = G.dev(gen_sketch(cfg, cfg.r_max + 8)[:nw])
+    nd = G.dev(np.asarray(lengths, np.int32))
+    seq, pipe = _cache(G, cfg, n), _cache(G, cfg, n)
+    try:
+        print("prefill: sequential order", flush=True)
+        for l in layers:
+            seq.prefill_gram(l, *dev[l], nd, first=(l % lpg == 0))
+        seq.prefill_bases(0, omega, 2)
+        for l in layers:
+            seq.prefill_encode(l, *dev[l], nd, tiers[l])
+        torch.cuda.synchronize()
+        print("prefill: pipelined on two streams", flush=True)
+        main, side = torch.cuda.current_stream(), torch.cuda.Stream()
+        ev_gram = [torch.cuda.Event() for _ in range(nw)]
+        ev_bases = [torch.cuda.Event() for _ in range(nw)]
+        for m in range(nw):
+            for l in range(m * lpg, (m + 1) * lpg):
+                pipe.prefill_gram(l, *dev[l], nd, first=(l % lpg == 0))
+            ev_gram[m].record(main)
+            with torch.cuda.stream(side):
+                side.wait_event(ev_gram[m])
+                pipe.prefill_bases(m, omega[m:m + 1], 2)
+                ev_bases[m].record(side)
+        for m in range(nw):
+            main.wait_event(ev_bases[m])
+            for l in range(m * lpg, (m + 1) * lpg):
+                pipe.prefill_encode(l, *dev[l], nd, tiers[l])
+        torch.cuda.synchronize()
+        assert seq.check_errors() == 0 and pipe.check_errors() == 0
+        for m in range(nw):
+            for a, b in zip(seq.get_basis(m), pipe.get_basis(m)):
+                assert torch.equal(a.view(torch.int16), b.view(torch.int16)), m
+        for l in layers:
+            ga, ca, _ = G.export_np(seq, l, cfg.batch, n)
+            gb, cb, _ = G.export_np(pipe, l, cfg.batch, n)
+            assert np.array_equal(ca, cb), l
+            for f in ga:
+                assert np.array_equal(ga[f].view(np.uint8), gb[f].view(np.uint8)), (l, f)
+    finally:
+        seq.close()
+        pipe.close()
+
+
 def test_prefill_length_beyond_the_buffer_is_refused(G):
     """n_tokens > n_cap sets the bad-length bit and leaves that sequence's
     heads empty; the other sequence is encoded."""
