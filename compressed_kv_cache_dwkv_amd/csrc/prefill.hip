@@ -400,6 +400,77 @@ __device__ void orth(const double *W, double *Q, int k, int ks, double *sv, doub
     }
 }
 
+// One CholeskyQR pass over the k columns of X (LDS [D][ks], in place):
+// G = X^T X (upper triangle, in g [k][k | 1]), G = R^T R, X = X R^{-1} (row by
+// row, forward substitution).  Returns false, with X unchanged, when a
+// pivot's remainder falls to 1e-5 of its column's norm or below (the
+// columns are then too close to dependent for this path).  scratch: 2 k.
+template <int D>
+__device__ __forceinline__ bool cholqr_pass(double *X, double *g, int k, int ks, double *scratch)
+{
+    const int tid = threadIdx.x, kg = k | 1;
+    double *norm2 = scratch, *rdiag = scratch + kMaxSketch;
+    for (int e = tid; e < k * k; e += kBasesThreads) {
+        const int a = e / k, b = e - a * k;
+        if (a > b) continue;
+        double p0 = 0.0, p1 = 0.0;
+        for (int i = 0; i < D; i += 2) {
+            p0 = fma(X[i * ks + a], X[i * ks + b], p0);
+            p1 = fma(X[(i + 1) * ks + a], X[(i + 1) * ks + b], p1);
+        }
+        g[a * kg + b] = p0 + p1;
+    }
+    __syncthreads();
+    if (tid < k) norm2[tid] = g[tid * kg + tid];
+    for (int j = 0; j < k; ++j) {
+        __syncthreads();
+        // every thread reads the same pivot: the branch is uniform
+        const double d = g[j * kg + j];
+        if (!(d > 1e-10 * norm2[j])) return false;
+        const double r = sqrt(d);
+        if (tid == j) rdiag[j] = r;
+        if (tid > j && tid < k) g[j * kg + tid] /= r;
+        __syncthreads();
+        const int w = k - j - 1;
+        for (int e = tid; e < w * w; e += kBasesThreads) {
+            const int a = j + 1 + e / w, b = j + 1 + e % w;
+            if (a <= b) g[a * kg + b] = fma(-g[j * kg + a], g[j * kg + b], g[a * kg + b]);
+        }
+    }
+    __syncthreads();
+    if (tid < D) {
+        double *x = X + tid * ks;
+        for (int b = 0; b < k; ++b) {
+            double p0 = x[b], p1 = 0.0;
+            int a = 0;
+            for (; a + 1 < b; a += 2) {
+                p0 = fma(-x[a], g[a * kg + b], p0);
+                p1 = fma(-x[a + 1], g[(a + 1) * kg + b], p1);
+            }
+            if (a < b) p0 = fma(-x[a], g[a * kg + b], p0);
+            x[b] = (p0 + p1) / rdiag[b];
+        }
+    }
+    __syncthreads();
+    return true;
+}
+
+// Q (LDS [D][k]) = k orthonormal columns spanning W's.  Where two CholeskyQR
+// passes hold (no column's remainder below 1e-5 of its norm, so that
+// Gram-Schmidt over [W | I] would keep exactly W's columns), their result,
+// which spans the same space (W is left holding it); else Gram-Schmidt as
+// defined above (orth), on W or on the first pass's columns.
+template <int D>
+__device__ __forceinline__ void orth_fast(double *W, double *Q, int k, int ks, double *sv, double *sr, double *sp, double *sred)
+{
+    if (cholqr_pass<D>(W, Q, k, ks, sp) && cholqr_pass<D>(W, Q, k, ks, sp)) {
+        for (int e = threadIdx.x; e < D * ks; e += kBasesThreads) Q[e] = W[e];
+        __syncthreads();
+        return;
+    }
+    orth<D>(W, Q, k, ks, sv, sr, sp, sred);
+}
+
 __device__ __forceinline__ int rr_index(int pos, int step, int kp)
 {
     return pos == 0 ? 0 : 1 + (pos - 1 + step) % (kp - 1);
@@ -432,11 +503,11 @@ __global__ __launch_bounds__(kBasesThreads) void bases_kernel(Layout ly, uint8_t
     for (int e = tid; e < D * k; e += kBasesThreads) sQ[(e / k) * ks + e % k] = (double)om[e];
     __syncthreads();
     gemm_cq<D>(C, sQ, sW, k, ks);
-    orth<D>(sW, sQ, k, ks, sv, sr, sp, sred);
+    orth_fast<D>(sW, sQ, k, ks, sv, sr, sp, sred);
     // 3. power iterations
     for (int it = 0; it < a.power_iters; ++it) {
         gemm_cq<D>(C, sQ, sW, k, ks);
-        orth<D>(sW, sQ, k, ks, sv, sr, sp, sred);
+        orth_fast<D>(sW, sQ, k, ks, sv, sr, sp, sred);
     }
     // 4. T = Q^T C Q, symmetrised, into sW
     gemm_cq<D>(C, sQ, sW, k, ks);

@@ -180,6 +180,43 @@ def test_bases_match_oracle_on_identical_gram(G, d, k, q):
         cache.close()
 
 
+def test_bases_rank_deficient_window(G):
+    """A window of 32 vectors per KV head (rank < k = 72): the CholeskyQR
+    fast path must decline (a pivot falls to zero) and Gram-Schmidt over
+    [Y | I] completes the basis as the oracle does.  Ritz values within
+    1e-10 of the largest; every row whose Ritz value is separated (the
+    nonzero ones) is the oracle's fp64 row rounded once to fp16."""
+    cfg = _cfg8k(batch=2)
+    lengths = [5, 3]
+    Ks, Vs = _window(cfg, lengths, integer=True)
+    omega = gen_sketch(cfg, cfg.r_max + 8)
+    cache = _cache(G, cfg, 64)
+    try:
+        print("bases: rank-deficient window", flush=True)
+        _grams(G, cache, cfg, Ks, Vs, lengths)
+        bk, bv, ritz = _bases(G, cache, cfg, omega, 2)
+        ref = oracle.prefill_bases(cfg, Ks, Vs, lengths, omega[0], 2)
+        strict = 0
+        for zi, (z, got) in enumerate((("K", bk), ("V", bv))):
+            for h in range(cfg.num_kv_heads):
+                th = ref["theta" + z][h]
+                assert np.abs(ritz[zi, h] - th).max() <= 1e-10 * th[0], (z, h)
+                assert (th > 1e-9 * th[0]).sum() <= 32
+                gaps = _ritz_order_gaps(th)
+                B64 = ref[z + "64"][h]
+                for i in range(cfg.r_max):
+                    if gaps[i] < 1e-6 * th[0]:
+                        continue
+                    ulp = np.spacing(np.abs(B64[i]).astype(np.float16)).astype(np.float64)
+                    diff = np.abs(got[h, i].astype(np.float64) - B64[i])
+                    assert np.all(diff <= 0.5 * ulp + 1e-9), (z, h, i, (diff - 0.5 * ulp).max())
+                    strict += 1
+        assert strict >= 2 * cfg.num_kv_heads * 16
+        assert cache.check_errors() == 0
+    finally:
+        cache.close()
+
+
 def test_bases_of_several_windows_in_one_launch(G):
     """One bases call over windows 0..2 (the benchmark's launch shape: every
     window of the model at once), each window with its own Gram sums and
