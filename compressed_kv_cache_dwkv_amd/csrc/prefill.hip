@@ -401,24 +401,50 @@ __device__ void orth(const double *W, double *Q, int k, int ks, double *sv, doub
 }
 
 // One CholeskyQR pass over the k columns of X (LDS [D][ks], in place):
-// G = X^T X (upper triangle, in g [k][k | 1]), G = R^T R, X = X R^{-1} (row by
-// row, forward substitution).  Returns false, with X unchanged, when a
-// pivot's remainder falls to 1e-5 of its column's norm or below (the
-// columns are then too close to dependent for this path).  scratch: 2 k.
+// G = X^T X (upper triangle, in g [k][k | 1]; a thread per 4x4 tile), G =
+// R^T R (right-looking, the trailing update spread over the workgroup),
+// X = X R^{-1} (a thread per row, forward substitution).
+// Returns false, with X unchanged, when a pivot's remainder falls to 1e-5
+// of its column's norm or below (the columns are then too close to
+// dependent for this path).  scratch: 2 kMaxSketch doubles.
 template <int D>
 __device__ __forceinline__ bool cholqr_pass(double *X, double *g, int k, int ks, double *scratch)
 {
-    const int tid = threadIdx.x, kg = k | 1;
+    const int tid = threadIdx.x, kg = k | 1, nb = (k + 3) / 4;
     double *norm2 = scratch, *rdiag = scratch + kMaxSketch;
-    for (int e = tid; e < k * k; e += kBasesThreads) {
-        const int a = e / k, b = e - a * k;
-        if (a > b) continue;
-        double p0 = 0.0, p1 = 0.0;
-        for (int i = 0; i < D; i += 2) {
-            p0 = fma(X[i * ks + a], X[i * ks + b], p0);
-            p1 = fma(X[(i + 1) * ks + a], X[(i + 1) * ks + b], p1);
+    if (tid < nb * (nb + 1) / 2) {
+        // tile (A, B), A <= B, in row order
+        int A = 0, t = tid;
+        while (t >= nb - A) {
+            t -= nb - A;
+            ++A;
         }
-        g[a * kg + b] = p0 + p1;
+        const int B = A + t;
+        double acc[4][4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[u][v] = 0.0;
+        for (int i = 0; i < D; ++i) {
+            // (columns past k read other LDS values; their products are dropped)
+            double xa[4], xb[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                xa[u] = X[i * ks + 4 * A + u];
+                xb[u] = X[i * ks + 4 * B + u];
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) acc[u][v] = fma(xa[u], xb[v], acc[u][v]);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int a = 4 * A + u, b = 4 * B + v;
+                if (a <= b && b < k) g[a * kg + b] = acc[u][v];
+            }
     }
     __syncthreads();
     if (tid < k) norm2[tid] = g[tid * kg + tid];
