@@ -740,20 +740,25 @@ __global__ __launch_bounds__(kSlotThreads) void place_kernel(Layout ly, uint8_t 
     const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
     const int32_t *cnt = counts_ptr(ly, arena, a.layer, b, h);
     if (tid < kMaxTiers) {
-        int tot = 0, off = 0;
-        for (int cc = 0; cc < a.n_chunks; ++cc) {
-            const int v = a.cntc[((int64_t)bh * a.n_chunks + cc) * kChunkStride + tid];
-            off += cc < c ? v : 0;
-            tot += v;
-        }
-        s_tot[tid] = tot;
-        s_off[tid] = off;
+        s_tot[tid] = 0;
+        s_off[tid] = 0;
         s_run[tid] = 0;
     }
-    if (tid == 0) {
-        int bad = 0;
-        for (int cc = 0; cc < a.n_chunks; ++cc) bad |= a.cntc[((int64_t)bh * a.n_chunks + cc) * kChunkStride + kMaxTiers];
-        s_bad = bad;
+    if (tid == 0) s_bad = 0;
+    __syncthreads();
+    // every chunk's counts and bad-tier flag, one load per (chunk, field),
+    // all in flight at once (integer sums: the order does not matter)
+    for (int e = tid; e < a.n_chunks * (kMaxTiers + 1); e += kSlotThreads) {
+        const int cc = e / (kMaxTiers + 1), f = e - cc * (kMaxTiers + 1);
+        const int v = a.cntc[((int64_t)bh * a.n_chunks + cc) * kChunkStride + f];
+        if (v != 0) {
+            if (f == kMaxTiers) {
+                atomicOr(&s_bad, 1);
+            } else {
+                atomicAdd(&s_tot[f], v);
+                if (cc < c) atomicAdd(&s_off[f], v);
+            }
+        }
     }
     __syncthreads();
     int n = a.n_tokens[b];
