@@ -6,6 +6,7 @@
 #include <cstring>
 #include <mutex>
 #include <new>
+#include <vector>
 
 #include "dwkv.h"
 #include "kernels.h"
@@ -16,6 +17,14 @@ struct dwkv_handle {
     dwkv::Layout ly;
     uint8_t *arena;
     int splits;
+    // bases written per window so far (dwkv_set_basis, dwkv_prefill_bases),
+    // and the window, version and workspace of the last block copy of a
+    // window's bases that a prefill encode made: the next encode of a layer
+    // of that window, on that workspace, reuses it
+    std::vector<uint64_t> basis_version;
+    int copied_group = -1;
+    uint64_t copied_version = 0;
+    const void *copied_ws = nullptr;
 };
 
 namespace dwkv {
@@ -315,6 +324,12 @@ int dwkv_create(const dwkv_config *cfg, void *arena, size_t arena_bytes, dwkv_ha
     h->ly = ly;
     h->arena = static_cast<uint8_t *>(arena);
     h->splits = dwkv::plan_splits(*cfg, ly);
+    try {
+        h->basis_version.assign((size_t)ly.num_groups, 0);
+    } catch (...) {
+        delete h;
+        return DWKV_ERR_INVALID_ARG;
+    }
     *out = h;
     return DWKV_OK;
 }
@@ -343,6 +358,7 @@ int dwkv_set_basis(dwkv_handle *h, int group, const void *basisK, const void *ba
     const Layout &ly = h->ly;
     if (group < 0 || group >= ly.num_groups) return DWKV_ERR_INVALID_ARG;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    ++h->basis_version[group];
     size_t bytes = (size_t)ly.basis_elems * 2;
     hipError_t e = hipMemcpyAsync(dwkv::basis_ptr(ly, h->arena, group, 0, 0), basisK, bytes,
                                   hipMemcpyDeviceToDevice, s);
@@ -777,6 +793,7 @@ int dwkv_prefill_bases(dwkv_handle *h, int group0, int n_groups, const float *om
     a.k = sketch;
     a.power_iters = power_iters;
     a.group0 = group0;
+    for (int g = group0; g < group0 + n_groups; ++g) ++h->basis_version[g];
     return hip_status(dwkv::launch_bases(ly, h->arena, a, n_groups, static_cast<hipStream_t>(stream)));
 }
 
@@ -808,7 +825,17 @@ int dwkv_prefill_encode(dwkv_handle *h, int layer, const void *k, const void *v,
         const int64_t need = (n_cap + dwkv::kSlotChunk - 1) / dwkv::kSlotChunk;
         a.n_chunks = (int)(need < w.n_chunks ? (need < 1 ? 1 : need) : w.n_chunks);
     }
-    return hip_status(dwkv::launch_prefill_encode(ly, h->arena, a, batch, static_cast<hipStream_t>(stream)));
+    // the window's block copy of its bases is made once per basis version
+    const int m = layer / ly.G;
+    a.copy_basis = !(h->copied_group == m && h->copied_version == h->basis_version[m] && h->copied_ws == workspace);
+    h->copied_group = -1;
+    const int rc2 = hip_status(dwkv::launch_prefill_encode(ly, h->arena, a, batch, static_cast<hipStream_t>(stream)));
+    if (rc2 == DWKV_OK) {
+        h->copied_group = m;
+        h->copied_version = h->basis_version[m];
+        h->copied_ws = workspace;
+    }
+    return rc2;
 }
 
 int dwkv_append(dwkv_handle *h, int layer, const void *k, const void *v, const void *tier,

@@ -135,6 +135,7 @@ struct EncodeArgs {
     int32_t *cntc;                // [B][Hkv][n_chunks][kChunkStride] tier counts per chunk (+ a bad-tier flag)
     int n_chunks;                 // chunks of kSlotChunk positions the call's counts cover
     uint16_t *basis_blocks;       // the window's bases in blocks of 8 rows, fp16 [2][Hkv][kMaxRank / 8][d][8]
+    bool copy_basis;              // (re)make basis_blocks from the arena first
 };
 hipError_t launch_prefill_encode(const Layout &ly, uint8_t *arena, const EncodeArgs &a, int batch,
                                  hipStream_t stream);

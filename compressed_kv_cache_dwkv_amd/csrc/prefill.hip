@@ -710,8 +710,16 @@ __global__ __launch_bounds__(kSlotThreads) void count_kernel(Layout ly, EncodeAr
     int loc[kMaxTiers] = {0, 0, 0, 0, 0, 0, 0, 0};
     int bad = 0;
     const int t1 = min(n, (c + 1) * kSlotChunk);
-    for (int t = c * kSlotChunk + tid; t < t1; t += kSlotThreads) {
-        const int k = tier[t];
+    // the chunk's tiers, every load issued before any is used
+    int kt[kSlotChunk / kSlotThreads];
+#pragma unroll
+    for (int u = 0; u < kSlotChunk / kSlotThreads; ++u) {
+        const int t = c * kSlotChunk + u * kSlotThreads + tid;
+        kt[u] = t < t1 ? tier[t] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kSlotChunk / kSlotThreads; ++u) {
+        const int k = kt[u];
         bad |= k >= ly.T;
 #pragma unroll
         for (int kk = 0; kk < kMaxTiers; ++kk) loc[kk] += k == kk;
@@ -1216,11 +1224,14 @@ hipError_t launch_prefill_encode(const Layout &ly, uint8_t *arena, const EncodeA
                                  hipStream_t stream)
 {
     (void)hipGetLastError();  // drop errors left by earlier, unrelated calls
-    const int64_t be = 2 * ly.basis_elems;
-    hipLaunchKernelGGL(basis_copy_kernel, dim3((unsigned)((be + 255) / 256 < 1024 ? (be + 255) / 256 : 1024)),
-                       dim3(256), 0, stream, ly, arena, a.layer / ly.G, a.basis_blocks);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    hipError_t e = hipSuccess;
+    if (a.copy_basis) {
+        const int64_t be = 2 * ly.basis_elems;
+        hipLaunchKernelGGL(basis_copy_kernel, dim3((unsigned)((be + 255) / 256 < 1024 ? (be + 255) / 256 : 1024)),
+                           dim3(256), 0, stream, ly, arena, a.layer / ly.G, a.basis_blocks);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     hipLaunchKernelGGL(count_kernel, dim3(a.n_chunks, batch * ly.Hkv), dim3(kSlotThreads), 0, stream, ly, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;

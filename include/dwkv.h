@@ -428,7 +428,11 @@ int dwkv_prefill_bases(dwkv_handle *h, int group0, int n_groups, const float *om
  * gate_k, gate_v: device fp16 [batch][num_kv_heads][n_cap] or NULL (a gate
  * of 1).  Admission is per (sequence, KV head), all or nothing: a tier >=
  * num_tiers, a full tier region or a full position map sets the device
- * error word and leaves that (sequence, KV head) unchanged.
+ * error word and leaves that (sequence, KV head) unchanged.  The encoder
+ * reads the window's bases from a copy in the workspace, made by the first
+ * call for a layer of that window after each dwkv_set_basis or
+ * dwkv_prefill_bases of it (bases written into the arena by other means
+ * are not seen by a later call for the same window).
  */
 int dwkv_prefill_encode(dwkv_handle *h, int layer, const void *k, const void *v, const int32_t *n_tokens, int batch,
                         int64_t n_cap, const void *tier, const void *gate_k, const void *gate_v, void *workspace,

@@ -615,6 +615,31 @@ def test_prefill_pipelined_on_two_streams(G):
         pipe.close()
 
 
+def test_prefill_encode_follows_new_bases(G):
+    """The encoder's copy of a window's bases is reused by the next layers of
+    that window and remade after dwkv_set_basis: layer 0 with bases A, layer
+    1 with A again, then layer 2 after the window's bases become B; each
+    against the oracle with the bases it was encoded with."""
+    cfg = _cfg8k(batch=2)
+    lengths, n = [700, 450], 700
+    A, B = make_bases(cfg), make_bases(cfg, variant_seed=1)
+    cache = _cache(G, cfg, n)
+    try:
+        for layer, bases in ((0, A), (1, A), (2, B)):
+            if layer != 1:
+                G.load_bases(cache, bases, groups=[0])
+            K, V = gen_prefill(cfg, layer, lengths=lengths)
+            tier = gen_tiers(cfg, layer, n)
+            print(f"prefill encode after bases change: layer {layer}", flush=True)
+            _encode(G, cache, cfg, layer, K, V, lengths, tier)
+            assert cache.check_errors() == 0
+            got, _, _ = G.export_np(cache, layer, cfg.batch, n)
+            ref = oracle.prefill_encode(cfg, bases["K"][0], bases["V"][0], K, V, lengths, tier)
+            _compare_layer(cfg, got, ref, lengths)
+    finally:
+        cache.close()
+
+
 def test_prefill_length_beyond_the_buffer_is_refused(G):
     """n_tokens > n_cap sets the bad-length bit and leaves that sequence's
     heads empty; the other sequence is encoded."""
