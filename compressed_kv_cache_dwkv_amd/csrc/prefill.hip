@@ -8,16 +8,18 @@
 // Three launch families:
 //   gram   -- one layer's contribution to its window's Gram matrices
 //             C^Z_h = sum over sequences b and positions t < n_b of x x^T:
-//             64-token tiles staged through LDS in a transposed, swizzled
-//             layout and contracted over tokens on the matrix cores (fp16
+//             64-token tiles, two in flight per workgroup, staged through
+//             LDS in a transposed, swizzled layout and contracted over
+//             tokens on the matrix cores (fp16
 //             operands, exact products, fp32 sums per workgroup); a second
 //             kernel adds each element's fp32 partials in fp64, in split
 //             order, into the window's fp64 accumulator in the workspace.
 //   bases  -- one workgroup per (window, Z, h), in fp64: the randomized
 //             range finder with power iterations and a Rayleigh-Ritz step
 //             (Halko, Martinsson and Tropp, SIAM Review 2011, §4.5 and §5.3)
-//             on C, with Gram-Schmidt twice per column over [Y | I] and a
-//             parallel cyclic Jacobi eigensolver (round-robin pairs); the
+//             on C, with Gram-Schmidt twice per column over [Y | I] (or
+//             two CholeskyQR passes where they keep exactly Y's columns) and
+//             a parallel cyclic Jacobi eigensolver (round-robin pairs); the
 //             Ritz vectors in decreasing Ritz value, sign-normalised, become
 //             the basis rows in fp16 (rounded once from fp64).
 //   encode -- count and place passes give every prefill token its tier slot and
@@ -880,8 +882,10 @@ __device__ __forceinline__ float hi_h(uint32_t w) { return h2f((uint16_t)(w >> 1
 // coefficients' sums interleaved), step 2 sums sum_i B[i][j] c_i for every
 // channel j sequentially in i, the kept channels are the s largest |e|
 // (ties to the lower channel, as in the append), and the scale, codes and
-// gate follow as in the append.  The basis values
-// are wave-uniform: they come through scalar loads.
+// gate follow as in the append.  The basis values are wave-uniform: they
+// come through scalar loads of the window's fp16 block copy, as the fp16
+// operand of mixed-precision FMAs (an exact conversion, so each is the
+// append's fp32 FMA).
 template <int D, int CB>  // CB: bytes per stored coefficient (2: fp16, 1: 8-bit codes)
 __global__ __launch_bounds__(kWave) void encode_kernel(Layout ly, uint8_t *__restrict__ arena, EncodeArgs a,
                                                        const uint16_t *__restrict__ bblocks)
