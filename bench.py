@@ -535,8 +535,10 @@ def prefill_trace_summary(cfg, ci: int, trace_dir: str, bench_json: Optional[str
              f"--config {ci} {PREFILL_TRACE_ARGS}",
              f"python3 <repo>/bench.py --config {ci} --mode prefill --trace-summary <out> [--bench-json <line>]",
              "```", "",
-             "Per prompt: one Gram launch (+ reduction) and one encode family (count, place, fp16 basis block copy, encode,",
-             "publish) per layer, one bases launch for all windows (+ a transpose per window).", "",
+             "Per prompt: one Gram launch (+ reduction) and one encode family (count, place, encode, publish; the fp16",
+             "basis block copy once per window) per layer, and one bases launch (+ a transpose) per window on a second",
+             "stream.  The trace also holds the breakdown's replays: the bases of all windows in one launch (128",
+             "workgroups), so the bases row averages launches of 16 and of 128 workgroups.", "",
              "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
     for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
         lines.append(f"| {_prefill_name(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
