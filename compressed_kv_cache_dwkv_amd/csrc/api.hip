@@ -4,8 +4,10 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <atomic>
 #include <mutex>
 #include <new>
+#include <unordered_map>
 #include <vector>
 
 #include "dwkv.h"
@@ -17,15 +19,29 @@ struct dwkv_handle {
     dwkv::Layout ly;
     uint8_t *arena;
     int splits;
-    // bases written per window so far (dwkv_set_basis, dwkv_prefill_bases),
-    // and the window, version and workspace of the last block copy of a
-    // window's bases that a prefill encode made: the next encode of a layer
-    // of that window, on that workspace, reuses it
+    uint64_t serial;                       // unique in the process
+    // bases written per window so far (dwkv_set_basis, dwkv_prefill_bases)
     std::vector<uint64_t> basis_version;
-    int copied_group = -1;
-    uint64_t copied_version = 0;
-    const void *copied_ws = nullptr;
 };
+
+namespace {
+
+// The window bases a prefill workspace's block copy holds: made by handle
+// `serial` for window `group` at basis version `version`, in the stream
+// capture `capture` (0: not captured).  An encode reuses the copy only with
+// every field equal, so a captured graph never relies on a copy made outside
+// it, nor an eager call on one made inside a graph.
+struct CopyTag {
+    uint64_t serial;
+    int group;
+    uint64_t version;
+    unsigned long long capture;
+};
+std::mutex g_copy_mu;
+std::unordered_map<const void *, CopyTag> g_copy_tags;
+std::atomic<uint64_t> g_next_serial{1};
+
+}  // namespace
 
 namespace dwkv {
 
@@ -324,6 +340,7 @@ int dwkv_create(const dwkv_config *cfg, void *arena, size_t arena_bytes, dwkv_ha
     h->ly = ly;
     h->arena = static_cast<uint8_t *>(arena);
     h->splits = dwkv::plan_splits(*cfg, ly);
+    h->serial = g_next_serial.fetch_add(1);
     try {
         h->basis_version.assign((size_t)ly.num_groups, 0);
     } catch (...) {
@@ -826,14 +843,28 @@ int dwkv_prefill_encode(dwkv_handle *h, int layer, const void *k, const void *v,
         a.n_chunks = (int)(need < w.n_chunks ? (need < 1 ? 1 : need) : w.n_chunks);
     }
     // the window's block copy of its bases is made once per basis version
+    // (and per stream capture)
+    hipStream_t s = static_cast<hipStream_t>(stream);
     const int m = layer / ly.G;
-    a.copy_basis = !(h->copied_group == m && h->copied_version == h->basis_version[m] && h->copied_ws == workspace);
-    h->copied_group = -1;
-    const int rc2 = hip_status(dwkv::launch_prefill_encode(ly, h->arena, a, batch, static_cast<hipStream_t>(stream)));
+    unsigned long long capture = 0;
+    hipStreamCaptureStatus cst = hipStreamCaptureStatusNone;
+    if (hipStreamGetCaptureInfo(s, &cst, &capture) != hipSuccess) {
+        (void)hipGetLastError();
+        cst = hipStreamCaptureStatusNone;
+    }
+    if (cst != hipStreamCaptureStatusActive) capture = 0;
+    const CopyTag want{h->serial, m, h->basis_version[m], capture};
+    {
+        std::lock_guard<std::mutex> lock(g_copy_mu);
+        auto it = g_copy_tags.find(workspace);
+        a.copy_basis = !(it != g_copy_tags.end() && it->second.serial == want.serial && it->second.group == want.group &&
+                         it->second.version == want.version && it->second.capture == want.capture);
+        if (it != g_copy_tags.end()) g_copy_tags.erase(it);
+    }
+    const int rc2 = hip_status(dwkv::launch_prefill_encode(ly, h->arena, a, batch, s));
     if (rc2 == DWKV_OK) {
-        h->copied_group = m;
-        h->copied_version = h->basis_version[m];
-        h->copied_ws = workspace;
+        std::lock_guard<std::mutex> lock(g_copy_mu);
+        g_copy_tags[workspace] = want;
     }
     return rc2;
 }

@@ -429,10 +429,12 @@ int dwkv_prefill_bases(dwkv_handle *h, int group0, int n_groups, const float *om
  * of 1).  Admission is per (sequence, KV head), all or nothing: a tier >=
  * num_tiers, a full tier region or a full position map sets the device
  * error word and leaves that (sequence, KV head) unchanged.  The encoder
- * reads the window's bases from a copy in the workspace, made by the first
- * call for a layer of that window after each dwkv_set_basis or
- * dwkv_prefill_bases of it (bases written into the arena by other means
- * are not seen by a later call for the same window).
+ * reads the window's bases from a copy in the workspace, which a call
+ * makes unless the workspace's last copy was made by this handle, for this
+ * window, since its last dwkv_set_basis or dwkv_prefill_bases, and in the
+ * same stream capture (or outside any capture, as this call is): a captured
+ * graph never relies on a copy made outside it.  Bases written into the
+ * arena by other means are not seen by such a reusing call.
  */
 int dwkv_prefill_encode(dwkv_handle *h, int layer, const void *k, const void *v, const int32_t *n_tokens, int batch,
                         int64_t n_cap, const void *tier, const void *gate_k, const void *gate_v, void *workspace,

@@ -640,6 +640,72 @@ def test_prefill_encode_follows_new_bases(G):
         cache.close()
 
 
+def test_prefill_basis_copy_shared_workspace_and_graphs(G):
+    """The encoder's block copy of a window's bases lives in the workspace:
+    (1) two caches sharing one workspace each encode with their own bases;
+    (2) an encode captured in a graph makes its own copy, so replaying the
+    graph after another window's encode overwrote the copy still uses the
+    right bases.  Every layer against the oracle with its bases."""
+    import torch
+    from compressed_kv_cache_dwkv_amd import dwkv_prefill_encode
+    cfg = _cfg8k(batch=2)
+    lengths, n = [500, 320], 500
+    lpg = cfg.layers_per_group
+    A, B = make_bases(cfg), make_bases(cfg, variant_seed=1)
+    ca, cb = _cache(G, cfg, n), _cache(G, cfg, n)
+    nd = G.dev(np.asarray(lengths, np.int32))
+    inputs = {}
+
+    def prepare(cache, layer):
+        K, V = gen_prefill(cfg, layer, lengths=lengths)
+        tier = gen_tiers(cfg, layer, n)
+        inputs[(id(cache), layer)] = (K, V, tier, G.dev(K), G.dev(V), G.dev(tier))
+
+    def enc(cache, layer, ws):
+        if (id(cache), layer) not in inputs:
+            prepare(cache, layer)
+        dk, dv, dt = inputs[(id(cache), layer)][3:]
+        dwkv_prefill_encode(cache.handle, layer, dk, dv, nd, dt, ws)
+
+    def check(cache, layer, bases, m):
+        K, V, tier = inputs[(id(cache), layer)][:3]
+        got, _, _ = G.export_np(cache, layer, cfg.batch, n)
+        ref = oracle.prefill_encode(cfg, bases["K"][m], bases["V"][m], K, V, lengths, tier)
+        _compare_layer(cfg, got, ref, lengths)
+
+    try:
+        ws = ca.prefill_workspace()
+        G.load_bases(ca, A, groups=[0, 1])
+        G.load_bases(cb, B, groups=[0])
+        print("shared workspace: cache A, cache B, cache A", flush=True)
+        enc(ca, 0, ws)
+        enc(cb, 0, ws)
+        enc(ca, 1, ws)
+        torch.cuda.synchronize()
+        assert ca.check_errors() == 0 and cb.check_errors() == 0
+        check(ca, 0, A, 0)
+        check(cb, 0, B, 0)
+        check(ca, 1, A, 0)
+        print("graph: capture an encode of window 0, then an eager encode of window 1, then replay", flush=True)
+        enc(ca, 2, ws)                       # eager copy of window 0's bases
+        prepare(ca, 3)                       # (no uploads inside the capture)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            enc(ca, 3, ws)                   # window 0 again, inside the capture
+        enc(ca, lpg, ws)                     # window 1: its copy replaces window 0's
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert ca.check_errors() == 0
+        check(ca, 2, A, 0)
+        check(ca, 3, A, 0)
+        check(ca, lpg, A, 1)
+    finally:
+        ca.close()
+        cb.close()
+
+
 def test_prefill_length_beyond_the_buffer_is_refused(G):
     """n_tokens > n_cap sets the bad-length bit and leaves that sequence's
     heads empty; the other sequence is encoded."""
