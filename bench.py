@@ -69,6 +69,9 @@ def parse_args():
     p.add_argument("--coef-bits", type=int, choices=[8, 16], default=16,
                    help="coefficient form: 16 = fp16, 8 = the 8-bit blockwise form (int8 codes, fp16 block scales)")
     p.add_argument("--dense-splits", type=int, default=0, help="dense decode workgroups per KV head (0 = auto)")
+    p.add_argument("--stream-probe", action="store_true",
+                   help="time a plain streaming read of one decode launch's algorithmic bytes per layer, "
+                        "launched like the decode (graph replays over the layers), at several grids")
     p.add_argument("--copy-probe", action="store_true",
                    help="also run a plain 512 MiB device copy (counter calibration)")
     p.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -436,6 +439,54 @@ def run_dense(args, cfg, K: int, W: int):
     }
 
 
+def run_stream_probe(args, cfg, K: int, W: int):
+    """The bandwidth a single launch that only reads one decode launch's
+    algorithmic bytes reaches: one buffer of that size per layer, read by
+    dwkv_stream_probe with the decode's grid and with wider ones, the
+    launches replayed from graphs exactly as the decode steps are."""
+    import torch
+    from compressed_kv_cache_dwkv_amd import dwkv_stream_probe
+    torch.cuda.set_device(0)
+    lay = gen_layer(cfg, 0)
+    # layer 0's tier counts, with an appended token of tier 0 per (sequence, KV head)
+    tiers, n_tok = np.asarray(lay["tier"]), np.asarray(lay["n_tokens"])
+    counts = np.zeros((cfg.batch, cfg.num_kv_heads, cfg.num_tiers), np.int64)
+    for b in range(cfg.batch):
+        for h in range(cfg.num_kv_heads):
+            counts[b, h] = np.bincount(tiers[b, h, :int(n_tok[b])], minlength=cfg.num_tiers)[:cfg.num_tiers]
+    per_layer = algorithmic_layer_bytes(cfg, counts, np.zeros((cfg.batch, cfg.num_kv_heads), np.int64))
+    nbytes = (per_layer + 15) // 16 * 16
+    L = cfg.num_layers
+    slab = torch.empty((L, nbytes), dtype=torch.uint8, device="cuda")
+    slab.view(torch.int32).random_()             # arbitrary contents, written once
+    sink = torch.zeros(64, dtype=torch.int32, device="cuda")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    splits = max(1, min(256, -(-cus // (cfg.batch * cfg.num_kv_heads))))   # the decode's plan
+    grids = [(splits * cfg.batch * cfg.num_kv_heads, 512), (1024, 256), (2048, 256), (4096, 256)]
+    rows = []
+    for wg, th in grids:
+        def step(s, wg=wg, th=th):
+            for l in range(L):
+                dwkv_stream_probe(slab[l], nbytes, wg, th, 0x9E3779B9, sink)
+        elapsed_ms = _time_graph_steps(step, W, K, args.chunk)
+        launch_us = elapsed_ms / (K * L) * 1e3
+        gbps = nbytes / (launch_us * 1e-6) / 1e9
+        rows.append({"workgroups": wg, "threads": th, "mean_launch_us": launch_us, "achieved": gbps,
+                     "frac": gbps / PEAK_HBM_GBPS})
+        print(f"bench: stream probe {wg} x {th}: {launch_us:.2f} us per launch, {gbps:.0f} GB/s",
+              file=sys.stderr, flush=True)
+    best = max(rows, key=lambda r: r["achieved"])
+    return {
+        "metric": "streaming read of one decode launch's algorithmic bytes per layer (measurement aid)",
+        "value": best["achieved"], "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "higher_is_better": True, "data": "synthetic",
+        "config": {"workload": cfg.name, "bytes_per_launch": nbytes, "layers": L,
+                   "decode_grid": [grids[0][0], grids[0][1]], "launch": "graph replays, one launch per layer"},
+        "grids": rows,
+        "peak": PEAK_HBM_GBPS,
+    }
+
+
 PREFILL_METRIC = "prefill compression tokens/s (prompt tokens, all layers: Gram sums, bases, bulk encode)"
 
 
@@ -775,6 +826,9 @@ def main():
     K = args.steps if args.steps is not None else cfg.bench_steps
     W = args.warmup
     L, B, H = cfg.num_layers, cfg.batch, cfg.num_kv_heads
+    if args.stream_probe:
+        print(json.dumps(run_stream_probe(args, cfg, K, W)), flush=True)
+        return
     if args.comparator == "dense":
         print(json.dumps(run_dense(args, cfg, K, W)), flush=True)
         return

@@ -95,6 +95,7 @@ _SIGS = {
     "dwkv_dense_workspace_bytes": [_I, _I, _I, _I, _I, ctypes.POINTER(ctypes.c_size_t)],
     "dwkv_dense_decode": [_P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_int64, _I, ctypes.c_float, _P, _P,
                           ctypes.c_size_t, _P],
+    "dwkv_stream_probe": [_P, ctypes.c_int64, _I, _I, ctypes.c_uint32, _P, _P],
     "dwkv_probe_workspace_bytes": [ctypes.POINTER(dwkv_config), _I, _I, _I, ctypes.POINTER(ctypes.c_size_t)],
     "dwkv_probe_error": [_P, _I, _P, _I, _I, _P, _P, _P, ctypes.c_int64, _I, ctypes.c_float, ctypes.c_float, _P, _P,
                          ctypes.c_size_t, _P],
@@ -382,6 +383,14 @@ def dwkv_dense_decode(q, k, v, n_tokens, out, workspace, splits: int, softmax_sc
                                   splits, float(softmax_scale), _ptr(out, torch.float32, (B, Hq, d), name="out"),
                                   _ptr(workspace, name="workspace"), ws, _stream(stream)),
            "dwkv_dense_decode")
+
+
+def dwkv_stream_probe(src, nbytes: int, workgroups: int, threads: int, magic: int, sink, stream=None) -> None:
+    """A plain streaming read of nbytes of src (a measurement aid: the
+    bandwidth one launch of that size and grid reaches)."""
+    _check(_lib.dwkv_stream_probe(_ptr(src, name="src"), int(nbytes), int(workgroups), int(threads),
+                                  int(magic) & 0xFFFFFFFF, _ptr(sink, torch.int32, name="sink"), _stream(stream)),
+           "dwkv_stream_probe")
 
 
 def dwkv_probe_workspace_bytes(cfg: dwkv_config, batch: int, n_queries: int, dense_splits: int) -> int:

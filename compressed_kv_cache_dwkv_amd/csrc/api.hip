@@ -569,6 +569,19 @@ int dwkv_dense_workspace_bytes(int batch, int num_q_heads, int num_kv_heads, int
     return DWKV_OK;
 }
 
+int dwkv_stream_probe(const void *src, int64_t bytes, int workgroups, int threads, uint32_t magic, uint32_t *sink,
+                      void *stream)
+{
+    if (!src || !sink) return DWKV_ERR_INVALID_ARG;
+    if (reinterpret_cast<uintptr_t>(src) % 16 != 0 || reinterpret_cast<uintptr_t>(sink) % 4 != 0)
+        return DWKV_ERR_INVALID_ARG;
+    if (bytes <= 0 || bytes % 16 != 0) return DWKV_ERR_INVALID_ARG;
+    if (workgroups < 1 || workgroups > 65535 || threads < 64 || threads > 1024 || threads % 64 != 0)
+        return DWKV_ERR_INVALID_ARG;
+    return hip_status(dwkv::launch_stream_read(src, bytes, workgroups, threads, magic, sink,
+                                               static_cast<hipStream_t>(stream)));
+}
+
 int dwkv_dense_decode(const void *q, const void *k, const void *v, const int32_t *n_tokens, int batch,
                       int num_q_heads, int num_kv_heads, int head_dim, int64_t n_cap, int splits,
                       float softmax_scale, float *out, void *workspace, size_t workspace_bytes, void *stream)

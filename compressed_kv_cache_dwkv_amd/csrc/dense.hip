@@ -531,7 +531,42 @@ hipError_t launch_dense_d(const DenseArgs &a, int splits, hipStream_t stream)
     }
 }
 
+// A plain streaming read, the measured ceiling for one launch that moves a
+// given number of bytes with a given grid (a measurement aid beside the
+// comparators, not part of any decode path): workgroup w reads the w-th
+// contiguous share of the buffer in 16-byte pieces, four loads in flight
+// per thread, and folds them into one word that is stored only if it
+// equals `magic` (so the loads cannot be dropped, and nothing is written).
+__global__ void stream_read_kernel(const uint4 *src, int64_t n16, uint32_t magic, uint32_t *sink)
+{
+    const int64_t per = (n16 + gridDim.x - 1) / gridDim.x;
+    const int64_t lo = (int64_t)blockIdx.x * per;
+    const int64_t hi = lo + per < n16 ? lo + per : n16;
+    const int64_t nt = blockDim.x;
+    int64_t i = lo + threadIdx.x;
+    uint32_t acc = 0;
+    for (; i + 3 * nt < hi; i += 4 * nt) {
+        const uint4 a = src[i], b = src[i + nt], c = src[i + 2 * nt], d = src[i + 3 * nt];
+        acc ^= (a.x ^ a.y ^ a.z ^ a.w) + (b.x ^ b.y ^ b.z ^ b.w) + (c.x ^ c.y ^ c.z ^ c.w) + (d.x ^ d.y ^ d.z ^ d.w);
+    }
+    for (; i < hi; i += nt) {
+        const uint4 a = src[i];
+        acc ^= a.x ^ a.y ^ a.z ^ a.w;
+    }
+    if (acc == magic) sink[0] = acc;
+}
+
 }  // namespace
+
+hipError_t launch_stream_read(const void *src, int64_t bytes, int workgroups, int threads, uint32_t magic,
+                              uint32_t *sink, hipStream_t stream)
+{
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)workgroups), dim3((unsigned)threads), 0, stream,
+                       static_cast<const uint4 *>(src), bytes / 16, magic, sink);
+    return hipGetLastError();
+}
+
 
 hipError_t launch_dense_decode(const DenseArgs &a, int splits, hipStream_t stream)
 {

@@ -56,6 +56,11 @@ struct DenseArgs {
 };
 hipError_t launch_dense_decode(const DenseArgs &a, int splits, hipStream_t stream);
 
+// A plain streaming read of `bytes` (a multiple of 16) with the given grid;
+// a measurement aid.
+hipError_t launch_stream_read(const void *src, int64_t bytes, int workgroups, int threads, uint32_t magic,
+                              uint32_t *sink, hipStream_t stream);
+
 // Writes the Eq. (1) reconstruction of every cached token of `layer` (batch
 // sequences) into the dense layout above, in position order, and the tokens
 // per (sequence, KV head) into n_out (int32 [batch][Hkv], may be null).

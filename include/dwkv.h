@@ -315,6 +315,24 @@ int dwkv_dense_decode(const void *q, const void *k, const void *v, const int32_t
                       int num_q_heads, int num_kv_heads, int head_dim, int64_t n_cap, int splits,
                       float softmax_scale, float *out, void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * Measurement aid, not a step of the method: a plain streaming read of
+ * `bytes` of device memory at src by `workgroups` workgroups of `threads`
+ * threads (workgroup w reads the w-th contiguous share, 16 bytes per load,
+ * four loads in flight per thread).  It computes nothing the method needs;
+ * timed like a decode launch of the same size and grid, it gives the
+ * bandwidth a single launch of that shape can reach on this device.
+ *   src: device, 16-byte aligned; bytes: a positive multiple of 16
+ *   workgroups: 1..65535; threads: a multiple of 64 in 64..1024
+ *   magic, sink: the folded word of the loaded data is stored to sink[0]
+ *          (device, 4 bytes) only if it equals magic; sink may be
+ *          written, nothing else is
+ * Returns DWKV_ERR_INVALID_ARG for a null or misaligned pointer or a size
+ * or grid outside these ranges.
+ */
+int dwkv_stream_probe(const void *src, int64_t bytes, int workgroups, int threads, uint32_t magic, uint32_t *sink,
+                      void *stream);
+
 /* Device workspace of dwkv_probe_error for batch sequences and n_queries
  * probed query positions (host only).  Zero-fill it once before its first
  * use; every call leaves it ready for the next. */

@@ -299,3 +299,19 @@ def test_single_hip_runtime_in_process():
     maps = open("/proc/self/maps").read()
     libs = {l.split()[-1] for l in maps.splitlines() if "libamdhip64" in l}
     assert len(libs) == 1, libs
+
+
+def test_stream_probe_validation_without_gpu():
+    """The streaming-read probe refuses bad pointers, sizes and grids before
+    any device call (fake, aligned device addresses: nothing is launched)."""
+    L = d._lib
+    src, sink = ctypes.c_void_p(1 << 20), ctypes.c_void_p(1 << 21)
+    ok = dict(bytes=1 << 16, wg=256, th=512)
+    assert L.dwkv_stream_probe(None, ok["bytes"], ok["wg"], ok["th"], 0, sink, None) == d.DWKV_ERR_INVALID_ARG
+    assert L.dwkv_stream_probe(src, ok["bytes"], ok["wg"], ok["th"], 0, None, None) == d.DWKV_ERR_INVALID_ARG
+    assert L.dwkv_stream_probe(ctypes.c_void_p((1 << 20) + 8), ok["bytes"], ok["wg"], ok["th"], 0, sink,
+                               None) == d.DWKV_ERR_INVALID_ARG
+    for nbytes in (0, -16, 24):
+        assert L.dwkv_stream_probe(src, nbytes, ok["wg"], ok["th"], 0, sink, None) == d.DWKV_ERR_INVALID_ARG
+    for wg, th in ((0, 512), (65536, 512), (256, 0), (256, 96), (256, 2048)):
+        assert L.dwkv_stream_probe(src, ok["bytes"], wg, th, 0, sink, None) == d.DWKV_ERR_INVALID_ARG
