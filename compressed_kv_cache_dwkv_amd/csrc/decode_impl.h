@@ -1060,83 +1060,86 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
     }
     __syncthreads();
     if (!s_last) return;
-    // The appended token is published by a wave with no head of its own to
-    // reduce (the last one, while the others reduce), else by wave 0 after
-    // the merge.  Its tier is requested with the partials, so publishing
-    // waits for no memory of its own.
-    constexpr int kPubWave = GQ < kWaves ? kWaves - 1 : 0;
+    // The appended token is published by the last wave once its share of
+    // the merge is done, before the barrier.  Its tier is requested with the
+    // partials, so publishing waits for no memory of its own.
+    constexpr int kPubWave = kWaves - 1;
     const int app_tier_v = appending && wave == kPubWave ? ap.tier[b * ly.Hkv + h] : 0;
     // Each thread owns 4 adjacent outputs of one head and an interleaved
-    // subset of the splits.  Its partial vectors of the first 32 splits (at
-    // least 8) are requested together with every split's max and
-    // normaliser, so the merge waits for memory once up to 32 splits;
-    // weights 2^(m_s - M) then come from LDS (the V-residual tiles: [GQ][S]
-    // weights, [GQ][S] normalisers, reduction area).
+    // subset of the splits (part, part + parts, ...).  The partial vectors,
+    // maxima and normalisers of its first splits are requested together, so
+    // the merge waits for memory once up to 32 splits; the thread combines
+    // its splits against their own largest max, and the parts are combined
+    // through LDS after one barrier (fixed orders: bitwise reproducible).
     constexpr int quads = GQ * D / 4;
     constexpr int parts = kBlock / quads;
     constexpr int kFirst = 32 / parts > 8 ? 32 / parts : 8;
     static_assert(kBlock % quads == 0, "merge layout");
-    static_assert((2 * kMaxSplits * 8 + kBlock * 4) * 4 <= sizeof(s_ev), "merge scratch");
+    static_assert(kBlock * (16 + 8) <= sizeof(s_ev), "merge scratch");
     const int qd = tid % quads, part = tid / quads;
     const int hq = (4 * qd) / D, j4 = (4 * qd) % D;
     const float *pob = ws.po + ((int64_t)b * ly.Hq + g0 + hq) * S * D + j4;
+    const float *pmb = ws.pm + ((int64_t)b * ly.Hkv + h) * S * kMlStride + hq;
     float4_t pc[kFirst];
+    float mc[kFirst], lc[kFirst];
 #pragma unroll
     for (int c = 0; c < kFirst; ++c) {
         const int sp = part + c * parts;
-        pc[c] = sp < S ? ld_agent4(pob + (int64_t)sp * D) : float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        const bool on = sp < S;
+        const int sq = on ? sp : 0;
+        pc[c] = ld_agent4(pob + (int64_t)sq * D);
+        mc[c] = __hip_atomic_load(pmb + (int64_t)sq * kMlStride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        lc[c] = __hip_atomic_load(pmb + (int64_t)sq * kMlStride + kMlNorm, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
+        if (!on) mc[c] = -INFINITY;
     }
-    float *s_w = reinterpret_cast<float *>(s_ev);
-    float *s_pl = s_w + GQ * S;
-    for (int i = tid; i < GQ * S; i += kBlock) {
-        const int g = i / S, sp = i % S;
-        const int64_t ml = (((int64_t)b * ly.Hkv + h) * S + sp) * kMlStride + g;
-        s_w[i] = __hip_atomic_load(ws.pm + ml, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-        s_pl[i] = __hip_atomic_load(ws.pl + ml, __ATOMIC_RELAXED,
-                                    __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __syncthreads();
-    // wave g reduces head g: max, weights, normaliser
-    if (wave < GQ) {
-        const int g = wave;
-        float M = -INFINITY;
-        for (int sp = lane; sp < S; sp += kWave) M = fmaxf(M, s_w[g * S + sp]);
-        M = wave_max(M);
-        float L = 0.0f;
-        for (int sp = lane; sp < S; sp += kWave) {
-            const float wgt = M == -INFINITY ? 0.0f : fast_exp2(s_w[g * S + sp] - M);
-            s_w[g * S + sp] = wgt;
-            L += wgt * s_pl[g * S + sp];
-        }
-        L = wave_sum(L);
-        if (lane == 0) s_L[g] = L;
-    } else if (appending && wave == kPubWave) {
-        publish_token(ly, arena, layer, b, h, app_tier_v, rg.cnt, lane);
-    }
-    __syncthreads();
+    float Mp = -INFINITY;
+#pragma unroll
+    for (int c = 0; c < kFirst; ++c) Mp = fmaxf(Mp, mc[c]);
+    float Lp = 0.0f;
     float4_t accm = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int c = 0; c < kFirst; ++c) {
-        const int sp = part + c * parts;
-        if (sp < S) accm += s_w[hq * S + sp] * pc[c];
+        const float wgt = mc[c] == -INFINITY ? 0.0f : fast_exp2(mc[c] - Mp);
+        accm += wgt * pc[c];
+        Lp += wgt * lc[c];
     }
+    // splits past the first batch (more than 32 splits): one at a time
     for (int sp = part + kFirst * parts; sp < S; sp += parts) {
-        accm += s_w[hq * S + sp] * ld_agent4(pob + (int64_t)sp * D);
+        const float4_t o = ld_agent4(pob + (int64_t)sp * D);
+        const float m = __hip_atomic_load(pmb + (int64_t)sp * kMlStride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const float l = __hip_atomic_load(pmb + (int64_t)sp * kMlStride + kMlNorm, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT);
+        const float nm = fmaxf(Mp, m);
+        const float fa = Mp == -INFINITY ? 0.0f : fast_exp2(Mp - nm);
+        const float fb = m == -INFINITY ? 0.0f : fast_exp2(m - nm);
+        accm = fa * accm + fb * o;
+        Lp = fa * Lp + fb * l;
+        Mp = nm;
     }
-    __syncthreads();
-    float4_t *s_red = reinterpret_cast<float4_t *>(s_ev) + kMaxSplits * 2 * 8 / 4;   // [parts][quads]
-    s_red[part * quads + qd] = accm;
+    if (appending && wave == kPubWave) publish_token(ly, arena, layer, b, h, app_tier_v, rg.cnt, lane);
+    float4_t *s_red = reinterpret_cast<float4_t *>(s_ev);                      // [parts][quads]
+    float *s_mp = reinterpret_cast<float *>(s_red + kBlock);                    // [parts][quads] max, then normaliser
+    s_red[tid] = accm;
+    s_mp[tid] = Mp;
+    s_mp[kBlock + tid] = Lp;
     __syncthreads();
     if (tid < quads) {
-        float4_t o = s_red[tid];
-        for (int p2 = 1; p2 < parts; ++p2) o += s_red[p2 * quads + tid];
-        const float L = s_L[hq];
+        float M = -INFINITY;
+#pragma unroll
+        for (int p2 = 0; p2 < parts; ++p2) M = fmaxf(M, s_mp[p2 * quads + tid]);
+        float4_t o = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        float L = 0.0f;
+#pragma unroll
+        for (int p2 = 0; p2 < parts; ++p2) {
+            const float mp = s_mp[p2 * quads + tid];
+            const float wgt = mp == -INFINITY ? 0.0f : fast_exp2(mp - M);
+            o += wgt * s_red[p2 * quads + tid];
+            L += wgt * s_mp[kBlock + p2 * quads + tid];
+        }
         const float inv = L > 0.0f ? 1.0f / L : 0.0f;
         *reinterpret_cast<float4_t *>(out + ((int64_t)b * ly.Hq + g0 + hq) * D + j4) = o * inv;
     }
-    if (GQ == kWaves && appending && wave == kPubWave)
-        publish_token(ly, arena, layer, b, h, app_tier_v, rg.cnt, lane);
     if (tid == 0) __hip_atomic_store(&ws.arrive[(b * ly.Hkv + h) * kArriveStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
