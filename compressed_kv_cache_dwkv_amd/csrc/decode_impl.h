@@ -1084,14 +1084,17 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
     float mc[kFirst], lc[kFirst];
 #pragma unroll
     for (int c = 0; c < kFirst; ++c) {
+        // (sp is the same in every lane of a wave: splits past S cost no load)
         const int sp = part + c * parts;
-        const bool on = sp < S;
-        const int sq = on ? sp : 0;
-        pc[c] = ld_agent4(pob + (int64_t)sq * D);
-        mc[c] = __hip_atomic_load(pmb + (int64_t)sq * kMlStride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        lc[c] = __hip_atomic_load(pmb + (int64_t)sq * kMlStride + kMlNorm, __ATOMIC_RELAXED,
-                                  __HIP_MEMORY_SCOPE_AGENT);
-        if (!on) mc[c] = -INFINITY;
+        pc[c] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        mc[c] = -INFINITY;
+        lc[c] = 0.0f;
+        if (sp < S) {
+            pc[c] = ld_agent4(pob + (int64_t)sp * D);
+            mc[c] = __hip_atomic_load(pmb + (int64_t)sp * kMlStride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            lc[c] = __hip_atomic_load(pmb + (int64_t)sp * kMlStride + kMlNorm, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
     float Mp = -INFINITY;
 #pragma unroll
