@@ -46,6 +46,23 @@ hipError_t launch_d(const Layout &ly, uint8_t *arena, int layer, const uint16_t 
 
 }  // namespace
 
+// The append's encoding, done by the first workgroup of each (sequence, KV
+// head) before its share of the tiles, in the units of the work balance
+// (9216 per tile), from kernel-trace sweeps of the share on each workload
+// shape: 250000 (about 27 tiles) with at most 4 query heads per KV head and
+// many splits per head (the 64K workload); 30% less with 8 query heads per
+// KV head, whose tiles take longer (the 128K 70B-shaped workload: 175000
+// best); 40% more with at most 4 splits per head, where every encoder of the
+// batch runs at once and each takes longer (the 32K x 16 workload: 350000
+// best).
+static float encode_units(const Layout &ly, int splits)
+{
+    float e = 250000.0f;
+    if (ly.gq > 4) e *= 0.7f;
+    if (splits <= 4) e *= 1.4f;
+    return e;
+}
+
 hipError_t launch_decode(const Layout &ly, uint8_t *arena, int layer, const void *q, int batch,
                          float softmax_scale, float *out, const DecodeWorkspace &ws, int splits,
                          const AppendArgs *ap, hipStream_t stream)
@@ -53,7 +70,8 @@ hipError_t launch_decode(const Layout &ly, uint8_t *arena, int layer, const void
     const float qs = softmax_scale * kLog2e;
     const uint16_t *qq = static_cast<const uint16_t *>(q);
     const AppendArgs none{nullptr, nullptr, nullptr, nullptr, nullptr};
-    const AppendArgs &a = ap ? *ap : none;
+    AppendArgs a = ap ? *ap : none;
+    if (ap) a.enc_units = encode_units(ly, splits);
     (void)hipGetLastError();  // drop errors left by earlier, unrelated calls
     if (ly.cb == 1) return launch_decode8(ly, arena, layer, qq, batch, qs, out, ws, splits, a, stream);
     if (ly.d == 64) return launch_d<64>(ly, arena, layer, qq, batch, qs, out, ws, splits, a, stream);

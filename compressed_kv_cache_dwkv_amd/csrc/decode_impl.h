@@ -67,10 +67,6 @@ constexpr int ev_stride(int gq) { return gq > 4 ? kTile + 4 : kTile + 8; }
 constexpr int ev_wave(int gq) { return (kEvRows * ev_stride(gq) + 7) / 8 * 8; }   // fp16, 16-byte multiple
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kMaxLag = 8.0f;           // log2 units the running max may trail
-// The append's encoding, done by the first workgroup of each (sequence, KV
-// head) before its share of the tiles, in the units of the work balance
-// (9216 per tile; measured: a share about 27 tiles smaller hides it).
-constexpr int64_t kEncodeUnits = 250000;
 
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
@@ -803,7 +799,7 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
         }
         // the encoding workgroup starts its share later: its boundaries
         // move down by the encoding's cost in balance units
-        const float E = appending ? (float)kEncodeUnits : 0.0f;
+        const float E = appending ? ap.enc_units : 0.0f;
         const float step = (W + E) * (float)invS;
         const float icb = (float)icb_l;
         const float x0 = fmaxf(floorf(step * (float)split) - E, 0.0f) - wk_l;

@@ -29,6 +29,10 @@ struct AppendArgs {
     const uint16_t *k, *v;          // fp16 [B][Hkv][d]
     const uint8_t *tier;            // [B][Hkv], the router's rank tier
     const uint16_t *gateK, *gateV;  // fp16 [B][Hkv], or null for a gate of 1
+    // one-launch decode step only: how much less of the tile work the
+    // encoding workgroup of each (sequence, KV head) takes, in the units the
+    // splits are balanced on (set by launch_decode)
+    float enc_units = 0.0f;
 };
 
 size_t decode_workspace_bytes(const Layout &ly, int batch, int splits);
