@@ -158,6 +158,20 @@ int build_layout(const dwkv_config *c, Layout *ly)
         t.cscK = (int32_t)ly->f_cscK[k];
         t.cscV = (int32_t)ly->f_cscV[k];
         t.pad2 = 0;
+        // operand slots of a decode tile (the rank's 16-channel blocks, at
+        // most 8 slots) and the residual record masks
+        const int r = ly->rank[k], sk = ly->resid[k];
+        const int lkbr = (r > 16) + (r > 32) + (r > 64);
+        for (int i = 0; i < 8; ++i) {
+            const int mb = i >> lkbr, kb = i & ((1 << lkbr) - 1);
+            t.koff[i] = (16 * mb * r + 16 * kb) * ly->cb;
+            t.voff[i] = (mb * r + 16 * kb) * 16 * ly->cb;
+        }
+        auto low_bits = [](int n) -> uint32_t { return n >= 32 ? 0xFFFFFFFFu : n <= 0 ? 0u : (1u << n) - 1u; };
+        t.im0 = low_bits(8 * sk);
+        t.im1 = low_bits(8 * sk - 32);
+        t.cm0 = low_bits(ly->bits * sk);
+        t.cm1 = low_bits(ly->bits * sk - 32);
     }
     const int64_t heads = (int64_t)ly->L * ly->Bmax * ly->Hkv;
     int64_t off = 0;

@@ -281,7 +281,7 @@ __device__ __forceinline__ void issue_tile(const Tile &t, TileData<NS> &D, __amd
 {
     const int c16 = lane & 15, grp = lane >> 4;
     const TierDesc &td = ly.tier[t.k];
-    const int r = t.r, kbr = t.kbr;
+    const int r = t.r;
     const uint32_t tok0 = (uint32_t)t.blk0 * 16u;
     if constexpr (CB == 1) {
         // 8-bit codes: one byte per coefficient, the same arrangement; the
@@ -292,9 +292,8 @@ __device__ __forceinline__ void issue_tile(const Tile &t, TileData<NS> &D, __amd
         const uint32_t kl = (uint32_t)(c16 * r + 4 * grp), vl = (uint32_t)(c16 * 16 + 4 * grp);
 #pragma unroll
         for (int i = 0; i < NS; ++i) {
-            const int mb = i >> t.lkbr, kb = i & (kbr - 1);
-            D.ka8[i] = __builtin_amdgcn_raw_buffer_load_b32(rb, kl, sK + (uint32_t)(16 * mb * r + 16 * kb), 0);
-            D.va8[i] = __builtin_amdgcn_raw_buffer_load_b32(rb, vl, sV + (uint32_t)(mb * r + 16 * kb) * 16u, 0);
+            D.ka8[i] = __builtin_amdgcn_raw_buffer_load_b32(rb, kl, sK + (uint32_t)td.koff[i], 0);
+            D.va8[i] = __builtin_amdgcn_raw_buffer_load_b32(rb, vl, sV + (uint32_t)td.voff[i], 0);
             D.ka[i] = __builtin_bit_cast(half4_t, __builtin_amdgcn_raw_buffer_load_b64(rbv, kbv, (uint32_t)i * 32u, 0));
         }
         // block scales: the lane's token's (K), tokens 4 grp .. of each 16-token block (V)
@@ -316,11 +315,9 @@ __device__ __forceinline__ void issue_tile(const Tile &t, TileData<NS> &D, __amd
     const uint32_t kl = v ? (uint32_t)(c16 * r + 4 * grp) * 2u : kbv;   // token c16, channels 4grp..
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
-        const int mb = i >> t.lkbr, kb = i & (kbr - 1);
-        const uint32_t ko = v ? sK + (uint32_t)(16 * mb * r + 16 * kb) * 2u : (uint32_t)i * 32u;
+        const uint32_t ko = v ? sK + (uint32_t)td.koff[i] : (uint32_t)i * 32u;
         D.ka[i] = __builtin_bit_cast(half4_t, __builtin_amdgcn_raw_buffer_load_b64(rk, kl, ko, 0));
-        D.va[i] = __builtin_bit_cast(
-            half4_t, __builtin_amdgcn_raw_buffer_load_b64(rb, vl, sV + (uint32_t)(mb * r + 16 * kb) * 32u, 0));
+        D.va[i] = __builtin_bit_cast(half4_t, __builtin_amdgcn_raw_buffer_load_b64(rb, vl, sV + (uint32_t)td.voff[i], 0));
     }
     }
     // residual records of token `lane` (token 0's for lanes past the tile:
@@ -356,13 +353,6 @@ struct WaveAcc {
     float m[GQ];                         // running max per head (the same in every lane)
 };
 
-// Bit masks keeping the first s entries of a token's record words (index
-// bytes; `bits`-bit codes), uniform over the wave.
-__device__ __forceinline__ uint32_t low_bits(int n)
-{
-    return n >= 32 ? 0xFFFFFFFFu : n <= 0 ? 0u : (1u << n) - 1u;
-}
-
 // fp16 probabilities of a wave's tile in LDS, [head][token] with the tokens
 // of each 32-token chunk ordered as the lanes of a 32-deep operand hold
 // them: token 16 h + 4 g + i of the chunk (h < 2, g < 4, i < 4) sits at
@@ -388,7 +378,7 @@ template <int GQ, int KB, int D, int BITS, int CB>
 __device__ __forceinline__ void process_tile(const Tile &t, const TileData<kSlots * (KB / 4)> &Dt,
                                              const half4_t *s_qb, WaveAcc<GQ, KB, D> &A,
                                              const float (*s_qt)[GQ < 4 ? 4 : GQ], _Float16 *sP,
-                                             _Float16 *ev, int lane)
+                                             _Float16 *ev, const TierDesc *tiers, int lane)
 {
     constexpr int bits = BITS;                      // code width: fields at fixed positions
     constexpr int NS = kSlots * (KB / 4);
@@ -459,8 +449,8 @@ __device__ __forceinline__ void process_tile(const Tile &t, const TileData<kSlot
 #pragma unroll
         for (int g = 0; g < GP; ++g) z[g] *= kcs;
     }
-    const uint32_t im0 = low_bits(8 * s), im1 = low_bits(8 * s - 32);
-    const uint32_t cm0 = low_bits(bits * s), cm1 = low_bits(bits * s - 32);
+    const TierDesc &td = tiers[t.k];
+    const uint32_t im0 = td.im0, im1 = td.im1, cm0 = td.cm0, cm1 = td.cm1;
     {
         const uint32_t ki0 = (Dt.ki0 & im0) | (0x80808080u & ~im0);
         const uint32_t ki1 = (Dt.ki1 & im1) | (0x80808080u & ~im1);
@@ -909,7 +899,7 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
     // (the tile past a wave's last holds the B_V operand: copied out at the
     // loop's exits, not selected between the buffers after it)
     half4_t bvt[NS];
-    if (ta.nv > 0) process_tile<GQ, KB, D, BITS, CB>(ta, DA, s_qb, A, s_qt, sP, ev, lane);
+    if (ta.nv > 0) process_tile<GQ, KB, D, BITS, CB>(ta, DA, s_qb, A, s_qt, sP, ev, ly.tier, lane);
     while (true) {
         if (!tb.valid) {
 #pragma unroll
@@ -919,7 +909,7 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
         cur.rem += kWaves;
         ta = locate<NS>(rg, cur, ly);
         issue_tile<NS, CB>(ta, DA, rb, rbv, kbv, ly, lane);
-        process_tile<GQ, KB, D, BITS, CB>(tb, DB, s_qb, A, s_qt, sP, ev, lane);
+        process_tile<GQ, KB, D, BITS, CB>(tb, DB, s_qb, A, s_qt, sP, ev, ly.tier, lane);
         if (!ta.valid) {
 #pragma unroll
             for (int i = 0; i < NS; ++i) bvt[i] = DA.ka[i];
@@ -928,7 +918,7 @@ __global__ __launch_bounds__(kBlock, 1) void decode_kernel(Layout ly, uint8_t *a
         cur.rem += kWaves;
         tb = locate<NS>(rg, cur, ly);
         issue_tile<NS, CB>(tb, DB, rb, rbv, kbv, ly, lane);
-        process_tile<GQ, KB, D, BITS, CB>(ta, DA, s_qb, A, s_qt, sP, ev, lane);
+        process_tile<GQ, KB, D, BITS, CB>(ta, DA, s_qb, A, s_qt, sP, ev, ly.tier, lane);
     }
 
     // ---- merge the waves of this workgroup: each wave leaves its unscaled

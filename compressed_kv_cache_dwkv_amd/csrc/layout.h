@@ -60,6 +60,14 @@ constexpr int kMaxSplits = 256;   // decode workgroups per (sequence, KV head)
 struct TierDesc {
     int32_t coefK, coefV, idxK, idxV, valK, valV, scaleK, scaleV;
     int32_t rank, resid, istride, vstride, weight, cscK, cscV, pad2;
+    // A decode tile's operand slot i (16-token block i >> log2(kb), 16-channel
+    // block i & (kb - 1), kb the rank's 16-channel blocks): its byte offset
+    // from the tile's first K (koff) and V (voff) coefficient, for the
+    // layout's coefficient width.
+    int32_t koff[8], voff[8];
+    // Masks keeping the first `resid` entries of a token's residual record
+    // words: index bytes (im0, im1) and packed codes (cm0, cm1).
+    uint32_t im0, im1, cm0, cm1;
 };
 
 struct Layout {
