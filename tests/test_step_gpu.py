@@ -115,13 +115,15 @@ def test_step_llama8b_shape_batched(G, splits):
     _steps(G, cfg, 1500, steps=3, layer=5, splits=splits)
 
 
-@pytest.mark.parametrize("splits", [0, 8, 32])
+# (2 and 3 splits: the encoding share of a launch with at most 4 splits
+# per head, the full-size 32K x 16 workload's case)
+@pytest.mark.parametrize("splits", [0, 2, 3, 8, 32])
 def test_step_batch16_router_skew(G, splits):
     cfg = w.get_config(3)
     _steps(G, cfg, 600, steps=2, layer=2, splits=splits)
 
 
-@pytest.mark.parametrize("splits", [0, 8, 32])
+@pytest.mark.parametrize("splits", [0, 3, 8, 32])
 def test_step_llama70b_shape(G, splits):
     cfg = w.get_config(4)
     _steps(G, cfg, 900, steps=2, layer=7, splits=splits)
