@@ -95,6 +95,10 @@ struct Layout {
     TierDesc tier[kMaxTiers];    // the same tiers, packed per tier (head blocks < 2 GiB)
 };
 
+// Kernels take the layout by value, beside a few hundred bytes of other
+// arguments, within the 4 KiB a launch's arguments may occupy.
+static_assert(sizeof(Layout) <= 3072, "layout too large for a kernel argument");
+
 DWKV_HD int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
 DWKV_HD uint8_t *head_block_ptr(const Layout &ly, uint8_t *arena, int layer, int b, int h)
