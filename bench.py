@@ -33,11 +33,13 @@ METRIC = "decode tokens/s + achieved HBM GB/s (% of peak), compressed-KV attn at
 PEAK_HBM_GBPS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
 DECODE_SRCS = [os.path.join(ROOT, "compressed_kv_cache_dwkv_amd", "csrc", f)
-               for f in ("decode_impl.h", "decode.hip", "decode8.hip")]
+               for f in ("decode_impl.h", "decode.hip", "decode8.hip", "layout.h")] + \
+              [os.path.join(ROOT, "compressed_kv_cache_dwkv_amd", "build.py")]
 
 
 def decode_source_sha() -> str:
-    """sha256 of the decode kernel's sources (the kernel and its instances)."""
+    """sha256 of the decode kernel's sources (the kernel, its instances, the
+    layout it reads and the build flags it is compiled with)."""
     h = hashlib.sha256()
     for f in DECODE_SRCS:
         h.update(open(f, "rb").read())
@@ -187,7 +189,7 @@ def pmc_summary(workload: str, fetch_dir: str, write_dir: str, bench_json: Optio
            if alg else "."),
         "",
         f"Decode source sha256: `{rec['decode_source_sha256']}` (bench.py reports `traffic` only while "
-        "decode.hip matches it).",
+        "the decode sources and build flags match it).",
     ]
     open(os.path.join(PROFILES, f"decode_{workload}_traffic.md"), "w").write("\n".join(lines) + "\n")
     print(json.dumps(rec), flush=True)
