@@ -85,3 +85,70 @@ def _one_call(G, cfg, n0, layer, splits, ragged=None):
 def test_noalloc_step_matches_workspace_step_on_two_calls(G):
     _one_call(G, w.get_config(4), 20000, layer=9, splits=32)
     _one_call(G, w.get_config(1).with_(batch=2), 1500, layer=6, splits=4, ragged=[1500, 700])
+
+
+def test_noalloc_step_replayed_from_a_graph(G):
+    """The callers this entry point is for capture it in graphs.  One eager
+    call sets the scratch up, then the captured call is replayed for three
+    more steps, each step's query and token written into the graph's input
+    buffers between replays: every replay's output bitwise equal to
+    dwkv_decode_step's on a twin cache, and the layers byte for byte the
+    same at the end (the split merge leaves the scratch's counters at zero
+    for the next replay)."""
+    import torch
+    import compressed_kv_cache_dwkv_amd as d
+    cfg = w.get_config(1)
+    layer, n0, steps = 5, 8192, 4
+    bases = make_bases(cfg)
+    m = layer // cfg.layers_per_group
+    caches = [G.make_cache(cfg, n=n0, extra=steps + 4, splits=32) for _ in range(2)]
+    ref_cache, na_cache = caches
+    try:
+        print(f"no-alloc graph test: {cfg.name} n0={n0} layer={layer} splits={na_cache.splits}", flush=True)
+        lay = gen_layer(cfg, layer, n=n0)
+        for c in caches:
+            G.load_bases(c, bases, groups=[m])
+            G.load_layer(c, layer, lay)
+        B, Hq, Hkv, dh = cfg.batch, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim
+        sq = torch.zeros((B, Hq, dh), dtype=torch.float16, device="cuda")
+        sk = torch.zeros((B, Hkv, dh), dtype=torch.float16, device="cuda")
+        sv = torch.zeros_like(sk)
+        st = torch.zeros((B, Hkv), dtype=torch.uint8, device="cuda")
+        so = torch.zeros((B, Hq, dh), dtype=torch.float32, device="cuda")
+        g = None
+        for step in range(steps):
+            q = gen_query(cfg, layer, step=step)
+            a = gen_append_inputs(cfg, layer, step, bases)
+            want = ref_cache.decode_step(layer, G.dev(q), G.dev(a["k"]), G.dev(a["v"]), G.dev(a["tier"]))
+            sq.copy_(G.dev(q))
+            sk.copy_(G.dev(a["k"]))
+            sv.copy_(G.dev(a["v"]))
+            st.copy_(G.dev(a["tier"]))
+            if g is None:       # the first call is eager; the graph is captured after it
+                d.dwkv_decode_step_noalloc(na_cache.handle, layer, sq, so, sk, sv, st)
+                torch.cuda.synchronize()
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    d.dwkv_decode_step_noalloc(na_cache.handle, layer, sq, so, sk, sv, st)
+            else:
+                g.replay()
+            torch.cuda.synchronize()
+            assert np.array_equal(so.cpu().numpy().view(np.uint32), want.cpu().numpy().view(np.uint32)), \
+                f"step {step}: differs from dwkv_decode_step"
+            if step == 0:
+                ref = oracle.decode(cfg, lay, bases["K"][m], bases["V"][m], q)
+                err = G.norm_err(so.cpu().numpy().astype(np.float64), ref)
+                assert err.max() <= TOL, f"max normalised error {err.max():.3e}"
+            print(f"  step {step}: {'eager' if step == 0 else 'replay'} equal to dwkv_decode_step", flush=True)
+        ex_r, cnt_r, sl_r = G.export_np(ref_cache, layer, B, n0 + steps)
+        ex_n, cnt_n, sl_n = G.export_np(na_cache, layer, B, n0 + steps)
+        assert np.array_equal(cnt_r, cnt_n) and np.array_equal(sl_r, sl_n)
+        assert int(cnt_n.sum()) == B * Hkv * (n0 + steps)
+        for key in ex_r:
+            assert np.array_equal(ex_r[key].view(np.uint8), ex_n[key].view(np.uint8)), key
+        for c in caches:
+            assert c.check_errors() == 0
+        del g
+    finally:
+        for c in caches:
+            c.close()
