@@ -810,7 +810,7 @@ def main():
     args = parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}), flush=True)
+        print(json.dumps({"error": "the benchmark runs on one GPU only; --gpus must be 1"}), flush=True)
         sys.exit(2)
     cfg = w.get_config(args.config).with_(coef_bits=args.coef_bits)
     if args.pmc_summary:
