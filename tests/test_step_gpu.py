@@ -194,3 +194,89 @@ def test_step_full_tier_sets_error_and_keeps_output(G):
         assert G.norm_err(out.cpu().numpy().astype(np.float64), ref).max() <= TOL
     finally:
         cache.close()
+
+
+def _extend_ragged(lay: dict, enc: dict, tier: np.ndarray) -> dict:
+    """`lay` with the oracle's encoding of one token per (b, KV head) put at
+    each sequence's own next position (sequences of different lengths)."""
+    ns = lay["n_tokens"].astype(np.int64)
+    need = int(ns.max()) + 1
+    out = {}
+    for key, v in lay.items():
+        if key == "n_tokens":
+            out[key] = ns + 1
+            continue
+        shape = list(v.shape)
+        shape[2] = max(shape[2], need)
+        nv = np.zeros(shape, v.dtype)
+        nv[:, :, :v.shape[2]] = v
+        out[key] = nv
+    for b, n in enumerate(ns):
+        out["tier"][b, :, n] = tier[b]
+        for z in "KV":
+            for f in ("coef", "idx", "val", "scale", "cscale"):
+                if f + z in enc:
+                    out[f + z][b, :, n] = enc[f + z][b]
+    return out
+
+
+def test_step_ragged_batch_with_empty_and_one_token_sequences(G):
+    """One-launch steps on a batch whose sequences hold 0, 1 and 3000 tokens,
+    at 32 splits per KV head: most workgroups of the short sequences have no
+    tile (their splits publish empty partials), the empty sequence's first
+    output is exactly zero, and every sequence's token goes to its own next
+    position.  Three steps, each against the oracle over the cache before it
+    and against decode + append on a twin cache (outputs within the bound,
+    the layer byte for byte); the appended tokens bit for bit."""
+    import torch
+    cfg = w.get_config(1).with_(batch=3)
+    layer, steps, ns0 = 6, 3, [0, 1, 3000]
+    bases = make_bases(cfg)
+    m = layer // cfg.layers_per_group
+    caches = [G.make_cache(cfg, n=max(ns0), extra=steps + 4, splits=32) for _ in range(2)]
+    sep, fused = caches
+    try:
+        print(f"ragged step test: {cfg.name} lengths={ns0} splits={fused.splits}", flush=True)
+        assert fused.splits == 32
+        lay = gen_layer(cfg, layer, n=max(ns0))
+        lay["n_tokens"][:] = ns0
+        for c in caches:
+            G.load_bases(c, bases, groups=[m])
+            G.load_layer(c, layer, lay)
+        for step in range(steps):
+            ns = [int(x) for x in lay["n_tokens"]]
+            q = gen_query(cfg, layer, step=step)
+            a = gen_append_inputs(cfg, layer, step, bases)
+            before = fused.read_counts(layer, cfg.batch)
+            assert np.array_equal(before.sum(axis=-1), np.array(ns)[:, None].repeat(cfg.num_kv_heads, 1))
+            out_sep = sep.decode(layer, G.dev(q))
+            sep.append(layer, G.dev(a["k"]), G.dev(a["v"]), G.dev(a["tier"]))
+            out_fused = fused.decode_step(layer, G.dev(q), G.dev(a["k"]), G.dev(a["v"]), G.dev(a["tier"]))
+            torch.cuda.synchronize()
+            got, two = out_fused.cpu().numpy(), out_sep.cpu().numpy()
+            ref = oracle.decode(cfg, lay, bases["K"][m], bases["V"][m], q)
+            live = np.array(ns) > 0
+            for b in np.nonzero(~live)[0]:
+                assert not got[b].any() and not two[b].any(), f"step {step}: empty sequence {b} must give 0"
+            err = G.norm_err(got.astype(np.float64), ref)[live]
+            err_sep = G.norm_err(two.astype(np.float64), ref)[live]
+            same = G.norm_err(got.astype(np.float64), two.astype(np.float64))[live]
+            assert err.max() <= TOL, f"step {step}: max normalised error {err.max():.3e}"
+            assert err_sep.max() <= TOL and same.max() <= SAME
+            print(f"  step {step} lengths {ns}: error {err.max():.2e}, two calls {err_sep.max():.2e}", flush=True)
+            n_max = max(ns) + 1
+            ex_s, cnt_s, sl_s = G.export_np(sep, layer, cfg.batch, n_max)
+            ex_f, cnt_f, sl_f = G.export_np(fused, layer, cfg.batch, n_max)
+            assert np.array_equal(cnt_s, cnt_f) and np.array_equal(sl_s, sl_f)
+            for key in ex_s:
+                assert np.array_equal(ex_s[key].view(np.uint8), ex_f[key].view(np.uint8)), key
+            enc = oracle.append_layer(cfg, bases["K"][m], bases["V"][m], a["k"], a["v"], a["tier"])
+            for b in range(cfg.batch):
+                _compare_token(cfg.with_(batch=1), {k: v[b:b + 1] for k, v in ex_f.items()}, sl_f[b:b + 1],
+                               before[b:b + 1], ns[b], {k: v[b:b + 1] for k, v in enc.items()}, a["tier"][b:b + 1])
+            lay = _extend_ragged(lay, enc, a["tier"])
+        for c in caches:
+            assert c.check_errors() == 0
+    finally:
+        for c in caches:
+            c.close()
