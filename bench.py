@@ -32,14 +32,20 @@ from workload.gen import gen_append_inputs, gen_layer, gen_query, make_bases, ma
 METRIC = "decode tokens/s + achieved HBM GB/s (% of peak), compressed-KV attn at 64K"
 PEAK_HBM_GBPS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
-DECODE_SRCS = [os.path.join(ROOT, "compressed_kv_cache_dwkv_amd", "csrc", f)
-               for f in ("decode_impl.h", "decode.hip", "decode8.hip", "layout.h")] + \
-              [os.path.join(ROOT, "compressed_kv_cache_dwkv_amd", "build.py")]
+# every file the decode kernel's translation units read (the kernel, its
+# instances, the append encoder compiled into the one-launch step, the shared
+# device helpers and declarations, the layout, the C header) and the build
+# flags it is compiled with
+_CSRC = os.path.join(ROOT, "compressed_kv_cache_dwkv_amd", "csrc")
+_SHARED_SRCS = [os.path.join(_CSRC, f) for f in ("device.h", "kernels.h", "layout.h")] + \
+               [os.path.join(ROOT, "include", "dwkv.h"), os.path.join(ROOT, "compressed_kv_cache_dwkv_amd", "build.py")]
+DECODE_SRCS = [os.path.join(_CSRC, f) for f in ("decode_impl.h", "decode.hip", "decode8.hip", "append_body.h")] + \
+              _SHARED_SRCS
 
 
 def decode_source_sha() -> str:
-    """sha256 of the decode kernel's sources (the kernel, its instances, the
-    layout it reads and the build flags it is compiled with)."""
+    """sha256 of the decode kernel's sources: every file its translation
+    units include and the build flags it is compiled with."""
     h = hashlib.sha256()
     for f in DECODE_SRCS:
         h.update(open(f, "rb").read())
@@ -87,9 +93,9 @@ def parse_args():
                         "prompt into the cache (Gram sums, bases, bulk encode for every layer)")
     p.add_argument("--power-iters", type=int, default=2, help="prefill: range-finder power iterations")
     p.add_argument("--bench-json", metavar="FILE",
-                   help="with --trace-summary: the JSON line of a default run of the same build, "
-                        "quoted beside the trace; with --pmc-summary: the counter run's own JSON line "
-                        "(its algorithmic bytes per launch)")
+                   help="a run's saved stdout, whose last JSON line is used: with --trace-summary, a default "
+                        "run of the same build, quoted beside the trace; with --pmc-summary, the counter run's "
+                        "own output (its algorithmic bytes per launch)")
     return p.parse_args()
 
 
@@ -171,7 +177,7 @@ def pmc_summary(workload: str, fetch_dir: str, write_dir: str, bench_json: Optio
         f"--config {ci}{cflag} {PMC_RUN_ARGS}",
         f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d <write> -o run -- python3 <repo>/bench.py "
         f"--config {ci}{cflag} {PMC_RUN_ARGS}",
-        f"python3 <repo>/bench.py --config {ci}{cflag} --pmc-summary <fetch> <write> --bench-json <fetch run's JSON line>",
+        f"python3 <repo>/bench.py --config {ci}{cflag} --pmc-summary <fetch> <write> --bench-json <fetch run's stdout file>",
         "```",
         "",
         "`--copy-probe` adds a plain 512 MiB device-to-device copy to the same process; each counter is",
@@ -227,7 +233,7 @@ def trace_summary(cfg, ci: int, trace_dir: str, bench_json: Optional[str]):
         f"rocprofv3 --kernel-trace --stats --output-format csv -d <out> -o bench -- python3 <repo>/bench.py "
         f"--config {ci}{' --coef-bits 8' if cfg.coef_bits == 8 else ''} {TRACE_RUN_ARGS}",
         f"python3 <repo>/bench.py --config {ci}{' --coef-bits 8' if cfg.coef_bits == 8 else ''} --trace-summary <out> "
-        f"[--bench-json <default run's line>]",
+        f"[--bench-json <default run's stdout file>]",
         "```",
         "",
         "Kernel statistics (durations in ns; graph replays of the warm-up and timed steps plus the replays of",
@@ -492,7 +498,7 @@ def run_stream_probe(args, cfg, K: int, W: int):
 PREFILL_METRIC = "prefill compression tokens/s (prompt tokens, all layers: Gram sums, bases, bulk encode)"
 
 
-PREFILL_SRCS = [os.path.join(ROOT, "compressed_kv_cache_dwkv_amd", "csrc", "prefill.hip")]
+PREFILL_SRCS = [os.path.join(_CSRC, "prefill.hip")] + _SHARED_SRCS   # its includes and build flags too
 PREFILL_RUN_ARGS = "--mode prefill --steps 1 --warmup 1 --no-cpu-baseline --copy-probe --kernel-reps 1"
 PREFILL_TRACE_ARGS = "--mode prefill --steps 3 --warmup 1 --no-cpu-baseline --kernel-reps 2"
 PREFILL_KERNELS = ("gram_kernel", "gram_reduce_kernel", "bases_kernel", "transpose_basis_kernel", "basis_copy_kernel",
@@ -541,7 +547,7 @@ def prefill_pmc_summary(cfg, ci: int, fetch_dir: str, write_dir: str, bench_json
              f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d <write> -o run -- python3 <repo>/bench.py "
              f"--config {ci} {PREFILL_RUN_ARGS}",
              f"python3 <repo>/bench.py --config {ci} --mode prefill --pmc-summary <fetch> <write> "
-             f"--bench-json <fetch run's JSON line>", "```", "",
+             f"--bench-json <fetch run's stdout file>", "```", "",
              "Each counter is scaled by (512 MiB) / (its reading for a plain 512 MiB device copy in the same process).",
              "", "| kernel | dispatches | FETCH bytes / launch | WRITE bytes / launch | algorithmic bytes | ratio |",
              "|---|---|---|---|---|---|"]
@@ -554,7 +560,7 @@ def prefill_pmc_summary(cfg, ci: int, fetch_dir: str, write_dir: str, bench_json
         lines.append(f"| {k} | {v.get('FETCH_SIZE', {}).get('dispatches', 0)} | {f:.0f} | {wr:.0f} | "
                      f"{'' if a is None else f'{a:.0f}'} | {'' if a is None else f'{(f + wr) / a:.3f}'} |")
     lines += ["", f"Prefill source sha256: `{rec['prefill_source_sha256']}` (bench.py reports `traffic` only while "
-                  "prefill.hip matches it)."]
+                  "the prefill sources and build flags match it)."]
     os.makedirs(PROFILES, exist_ok=True)
     json.dump(rec, open(os.path.join(PROFILES, f"prefill_{cfg.name}_traffic.json"), "w"), indent=1)
     open(os.path.join(PROFILES, f"prefill_{cfg.name}_traffic.md"), "w").write("\n".join(lines) + "\n")
@@ -586,7 +592,7 @@ def prefill_trace_summary(cfg, ci: int, trace_dir: str, bench_json: Optional[str
              "Command (run from /tmp with TMPDIR=/tmp on one MI355X), then the summary on any host:", "", "```",
              f"rocprofv3 --kernel-trace --stats --output-format csv -d <out> -o run -- python3 <repo>/bench.py "
              f"--config {ci} {PREFILL_TRACE_ARGS}",
-             f"python3 <repo>/bench.py --config {ci} --mode prefill --trace-summary <out> [--bench-json <line>]",
+             f"python3 <repo>/bench.py --config {ci} --mode prefill --trace-summary <out> [--bench-json <default run's stdout file>]",
              "```", "",
              "Per prompt: one Gram launch (+ reduction) and one encode family (count, place, encode, publish; the fp16",
              "basis block copy once per window) per layer, and one bases launch (+ a transpose) per window on a second",
