@@ -2,7 +2,9 @@
 divides by, checked against a count token by token from the storage format
 (K and V coefficients at the token's routed rank, and per K and V a
 residual block of s index bytes, s codes of `bits` bits and one fp16
-scale), plus hand values; and the refusal of more than one GPU."""
+scale), plus hand values; the refusal of more than one GPU; and that the
+source hashes tying recorded counter traffic to a build cover every file
+the profiled kernels include."""
 import json
 import os
 import subprocess
@@ -70,3 +72,36 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2
     msg = json.loads(r.stdout.strip().splitlines()[-1])
     assert "one GPU" in msg["error"]
+
+
+def _local_includes(path, seen):
+    """`path` and every file it reaches through #include "..." (transitively),
+    looked up beside the including file, then in include/."""
+    import re
+    path = os.path.realpath(path)
+    if path in seen:
+        return seen
+    seen.add(path)
+    for line in open(path):
+        m = re.match(r'\s*#\s*include\s+"([^"]+)"', line)
+        if m:
+            for d in (os.path.dirname(path), os.path.join(ROOT, "include")):
+                cand = os.path.join(d, m.group(1))
+                if os.path.exists(cand):
+                    _local_includes(cand, seen)
+                    break
+            else:
+                raise AssertionError(f"{path}: include {m.group(1)} not found")
+    return seen
+
+
+@pytest.mark.parametrize("kind,units", [("decode", ("decode.hip", "decode8.hip")), ("prefill", ("prefill.hip",))])
+def test_source_hash_covers_every_included_file(bench, kind, units):
+    csrc = os.path.join(ROOT, "compressed_kv_cache_dwkv_amd", "csrc")
+    reached = set()
+    for u in units:
+        _local_includes(os.path.join(csrc, u), reached)
+    hashed = {os.path.realpath(f) for f in (bench.DECODE_SRCS if kind == "decode" else bench.PREFILL_SRCS)}
+    missing = sorted(os.path.relpath(f, ROOT) for f in reached - hashed)
+    assert not missing, f"{kind} hash misses {missing}"
+    assert os.path.realpath(os.path.join(ROOT, "compressed_kv_cache_dwkv_amd", "build.py")) in hashed
