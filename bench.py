@@ -64,6 +64,12 @@ def parse_args():
     p.add_argument("--config", type=int, default=2, help="workload index 0-4 (2 = 64K headline)")
     p.add_argument("--chunk", type=int, default=16, help="steps per captured graph")
     p.add_argument("--splits", type=int, default=0, help="decode workgroups per KV head (0 = auto)")
+    p.add_argument("--context", type=int, default=0,
+                   help="tokens already cached per sequence in place of the workload's (0 = the workload's); "
+                        "the workload is then named with the context, so no recorded counter traffic applies")
+    p.add_argument("--batch", type=int, default=0,
+                   help="sequences per step in place of the workload's (0 = the workload's); the workload is "
+                        "then named with the batch, so no recorded counter traffic applies to it")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample budget")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-graph", action="store_true", help="launch eagerly instead of graph replay")
@@ -265,8 +271,8 @@ def trace_summary(cfg, ci: int, trace_dir: str, bench_json: Optional[str]):
 
 
 def _gen_layer_job(args):
-    ci, layer, coef_bits = args
-    return gen_layer(w.get_config(ci).with_(coef_bits=coef_bits), layer)
+    ci, layer, coef_bits, batch, n = args
+    return gen_layer(w.get_config(ci).with_(coef_bits=coef_bits, batch=batch, n_tokens=n), layer)
 
 
 def algorithmic_layer_bytes(cfg, counts: np.ndarray, app_tier: Optional[np.ndarray] = None) -> int:
@@ -634,9 +640,9 @@ def prefill_step_bytes(cfg, tiers) -> dict:
 
 
 def _gen_prefill_job(args):
-    ci, layer = args
+    ci, layer, batch, n = args
     from workload.gen import gen_prefill
-    return gen_prefill(w.get_config(ci), layer)
+    return gen_prefill(w.get_config(ci).with_(batch=batch, n_tokens=n), layer)
 
 
 def run_prefill(args, cfg, K: int, W: int):
@@ -651,7 +657,7 @@ def run_prefill(args, cfg, K: int, W: int):
     L, B, H, d, n, lpg = cfg.num_layers, cfg.batch, cfg.num_kv_heads, cfg.head_dim, cfg.n_tokens, cfg.layers_per_group
     t0 = time.perf_counter()
     with ProcessPoolExecutor(max_workers=min(lpg, len(os.sched_getaffinity(0)))) as ex:
-        kvs = list(ex.map(_gen_prefill_job, [(args.config, l) for l in range(lpg)]))
+        kvs = list(ex.map(_gen_prefill_job, [(args.config, l, cfg.batch, cfg.n_tokens) for l in range(lpg)]))
     tiers = [gen_tiers(cfg, l, n) for l in range(lpg)]
     sketch = min(cfg.r_max + 8, cfg.head_dim)
     omega = gen_sketch(cfg, sketch)
@@ -819,6 +825,10 @@ def main():
         print(json.dumps({"error": "the benchmark runs on one GPU only; --gpus must be 1"}), flush=True)
         sys.exit(2)
     cfg = w.get_config(args.config).with_(coef_bits=args.coef_bits)
+    if args.batch and args.batch != cfg.batch:
+        cfg = cfg.with_(batch=args.batch, name=f"{cfg.name}-batch{args.batch}")
+    if args.context and args.context != cfg.n_tokens:
+        cfg = cfg.with_(n_tokens=args.context, name=f"{cfg.name}-ctx{args.context}")
     if args.pmc_summary:
         if args.mode == "prefill":
             prefill_pmc_summary(cfg, args.config, *args.pmc_summary, bench_json=args.bench_json)
@@ -851,7 +861,7 @@ def main():
     t0 = time.perf_counter()
     workers = min(16, len(os.sched_getaffinity(0)))
     ex = ProcessPoolExecutor(max_workers=workers)
-    layer_iter = ex.map(_gen_layer_job, [(args.config, l, cfg.coef_bits) for l in range(L)])
+    layer_iter = ex.map(_gen_layer_job, [(args.config, l, cfg.coef_bits, cfg.batch, cfg.n_tokens) for l in range(L)])
     bases = make_bases(cfg)
     appends = [[gen_append_inputs(cfg, l, s, bases) for l in range(L)] for s in range(W + K)]
     queries = np.stack([gen_query(cfg, l) for l in range(L)])
