@@ -818,17 +818,25 @@ def prefill_cpu_baseline(cfg, budget_s: float):
                       f"scaled to {cfg.num_layers} layers"}
 
 
+def resolve_config(args):
+    """The workload of `--config` with `--coef-bits`, and any `--batch` or
+    `--context` override; an overridden workload carries the override in its
+    name, so profiles recorded for the workload itself never apply to it."""
+    cfg = w.get_config(args.config).with_(coef_bits=args.coef_bits)
+    if args.batch and args.batch != cfg.batch:
+        cfg = cfg.with_(batch=args.batch, name=f"{cfg.name}-batch{args.batch}")
+    if args.context and args.context != cfg.n_tokens:
+        cfg = cfg.with_(n_tokens=args.context, name=f"{cfg.name}-ctx{args.context}")
+    return cfg
+
+
 def main():
     args = parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(json.dumps({"error": "the benchmark runs on one GPU only; --gpus must be 1"}), flush=True)
         sys.exit(2)
-    cfg = w.get_config(args.config).with_(coef_bits=args.coef_bits)
-    if args.batch and args.batch != cfg.batch:
-        cfg = cfg.with_(batch=args.batch, name=f"{cfg.name}-batch{args.batch}")
-    if args.context and args.context != cfg.n_tokens:
-        cfg = cfg.with_(n_tokens=args.context, name=f"{cfg.name}-ctx{args.context}")
+    cfg = resolve_config(args)
     if args.pmc_summary:
         if args.mode == "prefill":
             prefill_pmc_summary(cfg, args.config, *args.pmc_summary, bench_json=args.bench_json)

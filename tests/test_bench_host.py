@@ -105,3 +105,20 @@ def test_source_hash_covers_every_included_file(bench, kind, units):
     missing = sorted(os.path.relpath(f, ROOT) for f in reached - hashed)
     assert not missing, f"{kind} hash misses {missing}"
     assert os.path.realpath(os.path.join(ROOT, "compressed_kv_cache_dwkv_amd", "build.py")) in hashed
+
+
+def test_overridden_workloads_take_no_recorded_traffic(bench, monkeypatch):
+    def cfg_of(*argv):
+        monkeypatch.setattr(sys, "argv", ["bench.py", *argv])
+        return bench.resolve_config(bench.parse_args())
+    base = cfg_of()
+    assert base.name == "llama3-8b-64k" and base.batch == 1 and base.n_tokens == 65536
+    assert bench.stored_traffic(bench.workload_name(base)) is not None
+    for argv, field, value, name in ((("--context", "8192"), "n_tokens", 8192, "llama3-8b-64k-ctx8192"),
+                                     (("--batch", "4"), "batch", 4, "llama3-8b-64k-batch4"),
+                                     (("--config", "3", "--batch", "2"), "batch", 2, "llama3-8b-32k-b16-batch2")):
+        cfg = cfg_of(*argv)
+        assert getattr(cfg, field) == value and cfg.name == name
+        assert bench.stored_traffic(bench.workload_name(cfg)) is None
+    same = cfg_of("--context", "65536", "--batch", "1")       # the workload's own values: not an override
+    assert same.name == base.name
