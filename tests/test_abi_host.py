@@ -315,3 +315,26 @@ def test_stream_probe_validation_without_gpu():
         assert L.dwkv_stream_probe(src, nbytes, ok["wg"], ok["th"], 0, sink, None) == d.DWKV_ERR_INVALID_ARG
     for wg, th in ((0, 512), (65536, 512), (256, 0), (256, 96), (256, 2048)):
         assert L.dwkv_stream_probe(src, ok["bytes"], wg, th, 0, sink, None) == d.DWKV_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("n,expect", [(8192, 8), (16384, 16), (32768, 32), (131072, 32)])
+def test_split_plan_over_context(n, expect):
+    """The Llama-3-8B shape at batch 1 and other contexts, with the spare
+    slots of `bench.py --context n --steps 64` (8 warm-up steps, 64 timed,
+    10 kernel repetitions, 8 more): one split per 1024 token slots until
+    every compute unit has a workgroup (32 splits of 8 KV heads), as the
+    context sweep ran them."""
+    from workload.gen import max_tier_counts
+    c = w.get_config(2).with_(n_tokens=n)
+    extra = 8 + 64 + 10 + 8
+    cap = [int(x) + extra for x in max_tier_counts(c)]
+    cfg = d.make_config(c.num_layers, c.layers_per_group, c.num_q_heads, c.num_kv_heads, c.head_dim,
+                        c.r_max, c.tier_rank, c.resid_per_tier, c.resid_bits, c.batch, cap,
+                        c.n_tokens + extra, 0)
+    h = ctypes.c_void_p()
+    need = d.dwkv_arena_bytes(cfg)
+    assert d._lib.dwkv_create(ctypes.byref(cfg), ctypes.c_void_p(1 << 40), need, ctypes.byref(h)) == d.DWKV_OK
+    try:
+        assert d.dwkv_decode_splits(h) == expect
+    finally:
+        d._lib.dwkv_destroy(h)
